@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Throughput of one tensor-parallel rank's MLP shard on one MI355X (simulated ranks in one HBM).
+
+One step = the whole hot path for rank 0 of t = 8 at the Llama-3-70B shape (hidden 8192,
+intermediate 28672, 3584 per rank), over one batch of tokens:
+  1. shard_linear_col   gate_up column GEMM with the fused SiLU(gate)·up epilogue -> act [b, 3584]
+  2. shard_linear_row   down_proj row GEMM -> rank 0's partial [b, 8192] inside P[8, b, 8192]
+  3. reduce_partials_rmsnorm   sum of the 8 partials + residual, RMSNorm -> residual_out, y
+The other seven ranks' partials are computed once before timing (their work is identical in
+shape to rank 0's and would run on the other GPUs).
+
+Inputs are synthetic and seeded (X, R ~ N(0,1); W ~ N(0,0.02); gamma ~ N(1,0.1); bf16), drawn on the
+device and resident in HBM before the timed region.  The JSON line reports whole-step throughput as
+algorithmic GEMM TFLOP/s (2·b·k·n per GEMM), each kernel's own time from HIP events recorded on the
+stream the kernels run on, the dominant kernel against its roofline, and the CPU oracle timed on a
+bounded sample of the same work.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (2.5 PFLOP/s)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (8 TB/s)
+
+
+def gemm_flops(b, k, n):
+    return 2.0 * b * k * n
+
+
+def col_silu_bytes(b, k, n_act):
+    # X read once, the rank's gate and up weight columns read once, act written once (bf16)
+    return 2.0 * (b * k + k * 2 * n_act + b * n_act)
+
+
+def row_bytes(b, k_r, n):
+    return 2.0 * (b * k_r + k_r * n + b * n)
+
+
+def reduce_bytes(t, b, n, residual=True):
+    # t partials + residual read, gamma read, residual_out and y written (bf16)
+    return 2.0 * (t * b * n + (b * n if residual else 0) + n + 2 * b * n)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--batch", type=int, default=4096, help="tokens per step (4096 prefill; 64 decode)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the secondary 64-token decode line")
+    ap.add_argument("--cpu-rows", type=int, default=32, help="token rows in the CPU oracle sample")
+    return ap.parse_args()
+
+
+def run_mlp(ttl, torch, w, b, steps, warmup, seed):
+    from tensor_transformer_linear_amd import workloads as wl
+    dev = "cuda"
+    inp = wl.mlp_inputs(w, b, seed=seed, device=dev)
+    X, R, gamma, Wgu, Wd = inp["X"], inp["R"], inp["gamma"], inp["Wgu"], inp["Wd"]
+    t, H, I = w.t, w.hidden, w.intermediate
+    Ir = I // t
+    sp = ttl.merged_gate_up_split(I, t)
+    act = torch.empty((b, Ir), dtype=torch.bfloat16, device=dev)
+    P = torch.empty((t, b, H), dtype=torch.bfloat16, device=dev)
+    rout = torch.empty((b, H), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((b, H), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    # every simulated rank's partial, once
+    for r in range(t):
+        ttl.shard_linear_col(X, Wgu, t, r, sp, ttl.EPI_SILU_MUL, Y=act, stream=stream)
+        ttl.shard_linear_row(act, Wd, t, r, True, P=P[r], stream=stream)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ttl.shard_linear_col(X, Wgu, t, 0, sp, ttl.EPI_SILU_MUL, Y=act, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        ttl.shard_linear_row(act, Wd, t, 0, True, P=P[0], stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        ttl.reduce_partials_rmsnorm(P, gamma, w.eps, R, residual_out=rout, Y=y, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # whole-step timing: nothing but the launches between the two events
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    # per-kernel timing: events between the launches, over the same number of steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    k_ms = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j in range(3)]
+
+    f_col = gemm_flops(b, H, 2 * Ir)
+    f_row = gemm_flops(b, Ir, H)
+    by_col = col_silu_bytes(b, H, Ir)
+    by_row = row_bytes(b, Ir, H)
+    by_red = reduce_bytes(t, b, H)
+    kern = {
+        "shard_linear_col_silu_mul": {"avg_us": k_ms[0] * 1e3, "gflop": f_col / 1e9, "mbytes": by_col / 1e6,
+                                      "tflops": f_col / (k_ms[0] * 1e9), "gbs": by_col / (k_ms[0] * 1e6)},
+        "shard_linear_row": {"avg_us": k_ms[1] * 1e3, "gflop": f_row / 1e9, "mbytes": by_row / 1e6,
+                             "tflops": f_row / (k_ms[1] * 1e9), "gbs": by_row / (k_ms[1] * 1e6)},
+        "reduce_partials_rmsnorm": {"avg_us": k_ms[2] * 1e3, "mbytes": by_red / 1e6,
+                                    "gbs": by_red / (k_ms[2] * 1e6)},
+    }
+    for name, d in kern.items():
+        d["frac_mfma_peak"] = d.get("tflops", 0.0) / PEAK_BF16_TFLOPS
+        d["frac_hbm_peak"] = d["gbs"] / PEAK_HBM_GBS
+    return {"ms_per_step": ms_step, "flops": f_col + f_row, "kernels": kern,
+            "tensors": (X, Wgu, Wd, R, gamma)}
+
+
+def cpu_baseline(torch, w, tensors, rows):
+    """The oracle as it stands, on rank 0's work for `rows` token rows (rows are independent)."""
+    import numpy as np
+    import oracle
+    from tensor_transformer_linear_amd import workloads as wl
+    X, Wgu, Wd, R, gamma = tensors
+    t, H, I = w.t, w.hidden, w.intermediate
+    Ir = I // t
+    # inputs to host memory and the oracle's decoding (not timed: input preparation)
+    Xs = oracle.bf16_bits_to_f64(wl.bf16_bits(X[:rows].cpu()))
+    Rs = oracle.bf16_bits_to_f64(wl.bf16_bits(R[:rows].cpu()))
+    gs = oracle.bf16_bits_to_f64(wl.bf16_bits(gamma.cpu()))
+    Wgu64 = oracle.bf16_bits_to_f64(wl.bf16_bits(Wgu.cpu()))
+    Wd64 = oracle.bf16_bits_to_f64(wl.bf16_bits(Wd.cpu()))
+    other = np.zeros((t - 1, rows, H))  # the other ranks' partials: same shape, values irrelevant to time
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    split = oracle.merged_gate_up_split(I, t)
+    t0 = time.perf_counter()
+    act = oracle.round_bf16(oracle.silu_mul(oracle.col_shard(Xs, Wgu64, split, t, 0)))
+    p0 = oracle.round_bf16(oracle.row_shard(act, Wd64, t, 0, x_is_parallel=True))
+    h, y = oracle.reduce_partials_rmsnorm(np.concatenate([p0[None], other]), Rs, gs, w.eps)
+    dt = time.perf_counter() - t0
+    flops = gemm_flops(rows, H, 2 * Ir) + gemm_flops(rows, Ir, H)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": dt,
+            "sample": f"rank 0 of t={t}: gate_up+SiLU*up, down partial and reduce+RMSNorm for {rows} of "
+                      f"the token rows (float64 numpy oracle; rows are independent, so throughput "
+                      f"scales to the full batch)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the tensor-parallel work (ranks are simulated in one "
+              "HBM); runs on more than one GPU are not part of this benchmark.", file=sys.stderr)
+        return 2
+    import torch
+    from tensor_transformer_linear_amd import ttl
+    from tensor_transformer_linear_amd import workloads as wl
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    w = wl.LLAMA3_70B_MLP_TP8
+    b = args.batch
+    res = run_mlp(ttl, torch, w, b, args.steps, args.warmup, seed=0)
+    ms = res["ms_per_step"]
+    value = res["flops"] / (ms * 1e9)
+    kcol = res["kernels"]["shard_linear_col_silu_mul"]
+    dominant_bound = "mfma" if b >= 512 else "hbm"
+    if dominant_bound == "mfma":
+        roof = {"kernel": "shard_linear_col_silu_mul", "bound": "mfma", "achieved": kcol["tflops"],
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": kcol["tflops"] / PEAK_BF16_TFLOPS,
+                "traffic": None}
+    else:
+        roof = {"kernel": "shard_linear_col_silu_mul", "bound": "hbm", "achieved": kcol["gbs"],
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": kcol["gbs"] / PEAK_HBM_GBS, "traffic": None}
+    out = {
+        "metric": "TFLOP/s and % bf16 MFMA peak, 1-rank shard of Llama-3-70B MLP at TP=8 shape",
+        "value": value,
+        "unit": "TFLOP/s",
+        "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"llama3_70b_mlp_tp8_rank0_b{b}", "hidden": w.hidden,
+                   "intermediate": w.intermediate, "t": w.t, "tokens": b,
+                   "step": "gate_up+SiLU*up (col) -> down (row partial) -> reduce 8 partials + residual + RMSNorm"},
+        "roofline": roof,
+        "kernels": res["kernels"],
+    }
+    if not args.no_decode and b != 64:
+        dec = run_mlp(ttl, torch, w, 64, args.steps, args.warmup, seed=1)
+        out["decode64"] = {"ms_per_step": dec["ms_per_step"],
+                           "tflops": dec["flops"] / (dec["ms_per_step"] * 1e9),
+                           "kernels": dec["kernels"]}
+        del dec
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(torch, w, res["tensors"], args.cpu_rows)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,160 @@
+/*
+ * ttl.h — tensor-parallel sharded linear layers, one rank's share on one MI355X (gfx950).
+ *
+ * The library runs the data-parallel hot path of Megatron-style tensor parallelism for a
+ * Llama-style decoder with t tensor-parallel ranks simulated inside one GPU's HBM:
+ *
+ *   column-parallel GEMM   Y_r = X · W[:, C_r]              (gate_up_proj, head-sliced qkv_proj)
+ *   fused SiLU·up          act_r = silu(gate_r) · up_r     (epilogue of the gate_up column GEMM)
+ *   row-parallel GEMM      P_r = X_r · W[r·k/t:(r+1)·k/t, :]  (down_proj, o_proj: a partial sum)
+ *   reduce + norm          h = Σ_r P_r + residual;  y = h / sqrt(mean(h²) + eps) · gamma
+ *
+ * The statement of the problem follows the vLLM tensor-parallel walkthrough
+ * "vLLM 源码完全拆解（十一）：模型并行与 Worker 层" (pinghaoyang.com.cn), section
+ * "一个矩阵乘法如何被切开": a dense layer computes Y = X·W with X[b,k] (b tokens, k input features),
+ * W[k,n] and Y[b,n]; t ranks either cut W along n (column split, input replicated, outputs
+ * concatenate) or cut W along k and X along its last dimension (row split, partial outputs that
+ * must be summed).  Llama's projections carry no bias, so none is taken here.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are bf16 (raw bits in uint16_t), row-major, dense: X[b,k] has row stride k, W[k,n]
+ *     has row stride n, partials are [t,b,n].  Every tensor pointer is a DEVICE pointer.
+ *   - W is always the full, unsharded weight; the rank's slice is addressed in place by offsets
+ *     (the analogue of weight_loader's narrow() in section "ColumnParallelLinear"), never copied.
+ *   - Arithmetic: bf16 × bf16 products accumulated in fp32 on the matrix cores; elementwise math in
+ *     fp32; every output is rounded to bf16, nearest-even.
+ *   - Ownership: the caller allocates and owns every buffer; the library keeps no pointer after a
+ *     call returns and frees nothing of the caller's.  Calls are asynchronous: they validate, then
+ *     enqueue kernels on `stream` (a hipStream_t; NULL = the default stream) and return.  Buffers
+ *     must stay alive until the stream has run the work.
+ *   - Errors: every call returns a ttl_status.  Arguments are validated synchronously before any
+ *     launch; on a non-OK status nothing has been enqueued and ttl_last_error() returns a message
+ *     (thread-local).  A launch failure reported by the runtime is TTL_ERR_HIP.  A fault inside a
+ *     kernel surfaces at the caller's next synchronisation, as with any HIP kernel.
+ *   - Alignment: every pointer 16-byte aligned and every row stride and every slice width a
+ *     multiple of 8 elements (16 bytes), else TTL_ERR_ALIGN.
+ */
+#ifndef TTL_H
+#define TTL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t ttl_status;
+#define TTL_OK 0
+#define TTL_ERR_NULL 1          /* a required pointer is NULL */
+#define TTL_ERR_SHAPE 2         /* a size is <= 0 or out of the supported range */
+#define TTL_ERR_NOT_DIVISIBLE 3 /* a shard width is not an exact division (vLLM's divide() asserts) */
+#define TTL_ERR_RANK 4          /* t < 1 or rank outside [0, t) */
+#define TTL_ERR_ALIGN 5         /* pointer not 16-byte aligned or stride/width not a multiple of 8 */
+#define TTL_ERR_UNSUPPORTED 6   /* a combination the library does not implement */
+#define TTL_ERR_HIP 7           /* the HIP runtime reported an error */
+
+typedef int32_t ttl_epilogue;
+#define TTL_EPI_NONE 0
+#define TTL_EPI_SILU_MUL 1
+
+#define TTL_MAX_SEGMENTS 3
+
+/*
+ * Column split of the full W[k,n] ("MergedColumnParallelLinear / QkvParallelLinear" on the vLLM
+ * walkthrough): W is nseg segments packed side by side along n — one for a plain layer, two for
+ * gate_up (output_sizes = [I, I]), three for qkv (q | k | v).  seg_n[i] is segment i's width in the
+ * full W (the widths sum to n); seg_parts[i] is how many distinct slices segment i is cut into:
+ * t for a plain, gate, up or q segment and for k/v when t <= n_kv_heads; n_kv_heads for k/v when
+ * t > n_kv_heads (each kv head then replicated on t / n_kv_heads ranks).  Rank r takes slice
+ * floor(r · seg_parts[i] / t) of each segment; its output concatenates the slices in segment order.
+ */
+typedef struct {
+  int32_t nseg;
+  int64_t seg_n[TTL_MAX_SEGMENTS];
+  int32_t seg_parts[TTL_MAX_SEGMENTS];
+} ttl_col_split;
+
+/*
+ * shard_linear_col — ColumnParallelLinear forward of rank `rank` of `t`, with gather_output=False
+ * (vLLM walkthrough, section "ColumnParallelLinear": the rank keeps its own n/t columns).
+ *
+ *   X      [b, k]  bf16, the full (replicated) input.
+ *   W      [k, n]  bf16, the full weight; only the rank's columns are read.
+ *   split  column split (see ttl_col_split); NULL means one segment cut into t slices.
+ *   epi    TTL_EPI_NONE: Y[b, n_r] = X · W[:, C_r], n_r = Σ_i seg_n[i] / seg_parts[i].
+ *          TTL_EPI_SILU_MUL: the split must have two equal segments (gate | up) with equal part
+ *          counts; Y[b, n_r/2] = silu(X·W_gate_r) · (X·W_up_r) with silu(x) = x / (1 + e^-x),
+ *          computed in fp32 from the fp32 accumulators — the activation "on the local shard" of
+ *          section 14 of "vLLM Code Reading (Section 5)" (jeremyguo.space).  gate and up never
+ *          reach memory.
+ *   Y      output, row stride n_r (or n_r/2), caller-allocated.
+ * Errors: NULL X/W/Y -> NULL; b,k,n <= 0 -> SHAPE; bad t/rank -> RANK; a segment width not
+ * divisible by its part count, part count neither t nor a divisor of t, or widths not summing to n
+ * -> NOT_DIVISIBLE; misalignment -> ALIGN; SILU_MUL with an unsuitable split or nseg outside 1..3
+ * -> UNSUPPORTED.
+ */
+ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k,
+                            const uint16_t* W, int64_t n,
+                            int32_t t, int32_t rank,
+                            const ttl_col_split* split,
+                            ttl_epilogue epi,
+                            uint16_t* Y,
+                            void* stream);
+
+/*
+ * shard_linear_row — RowParallelLinear forward of rank `rank` of `t` with reduce_results=False:
+ * the rank's partial sum, which a later reduction adds up (vLLM walkthrough, section
+ * "RowParallelLinear"; section 12 of "vLLM Code Reading (Section 5)": Y_i = X_i A_i, Y = Σ_i Y_i).
+ *
+ *   X      x_is_parallel != 0: the rank's input slice [b, k/t] (input_is_parallel=True, e.g. the
+ *          act of shard_linear_col);  x_is_parallel == 0: the full input [b, k], whose columns
+ *          [r·k/t, (r+1)·k/t) are used (split along the last dimension).
+ *   k      the FULL input dimension of W.
+ *   W      [k, n] bf16, full weight; rows [r·k/t, (r+1)·k/t) are read.
+ *   P      [b, n] bf16 partial for this rank (for simulated ranks, the caller passes P + r·b·n of
+ *          a [t, b, n] buffer).
+ * Errors: as above; k not divisible by t -> NOT_DIVISIBLE.
+ */
+ttl_status shard_linear_row(const uint16_t* X, int64_t b, int64_t k,
+                            int32_t x_is_parallel,
+                            const uint16_t* W, int64_t n,
+                            int32_t t, int32_t rank,
+                            uint16_t* P,
+                            void* stream);
+
+/*
+ * reduce_partials_rmsnorm — the row-parallel reduction of t rank partials held in one HBM,
+ * followed by the residual add and RMSNorm of post_attention_layernorm(hidden, residual)
+ * ("Tensor & pipeline parallelism", Undercurrent docs, sections "Row-parallel layers all-reduce
+ * inside forward()", "residual_stream" and "final_norm": the norm is over the full, unsharded
+ * hidden dimension).
+ *
+ *   P         [t, b, n] bf16 partials.
+ *   residual  [b, n] bf16 or NULL (then h = Σ_r P_r).
+ *   gamma     [n] bf16 RMSNorm gain (replicated on every rank).
+ *   eps       added to the mean square inside the square root.
+ *   residual_out [b, n] bf16: the updated residual stream h = Σ_r P_r + residual (the sum in fp32,
+ *             ascending r, then the residual); may alias `residual`.
+ *   Y         [b, n] bf16: h / sqrt(mean_j h_j² + eps) · gamma, from the fp32 h.
+ * The summation order is fixed, so results are bitwise reproducible run to run.
+ * Errors: NULL P/gamma/residual_out/Y -> NULL; t < 1 -> RANK; b, n <= 0 or n > 65536 -> SHAPE;
+ * misalignment -> ALIGN; Y aliasing an input -> UNSUPPORTED.
+ */
+ttl_status reduce_partials_rmsnorm(const uint16_t* P, int32_t t, int64_t b, int64_t n,
+                                   const uint16_t* residual,
+                                   const uint16_t* gamma, float eps,
+                                   uint16_t* residual_out,
+                                   uint16_t* Y,
+                                   void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* ttl_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t ttl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTL_H */

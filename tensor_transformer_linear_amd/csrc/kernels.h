@@ -1,0 +1,42 @@
+// Internal declarations shared by the HIP sources of libttl (not part of the public C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttl {
+
+// Parameters of one tiled bf16 GEMM launch: C[M, N] = A[M, K] · B_map[K, N].
+// A rows have stride lda (elements); A already points at the first column the rank uses.
+// B is the weight, row stride ldb, already pointing at the first row the rank uses; output column
+// j reads weight column wcol(j) given by the column map below.
+struct GemmParams {
+  const uint16_t* A;
+  const uint16_t* B;
+  uint16_t* C;
+  int64_t lda, ldb, ldc;
+  int32_t M, N, K;        // N = output columns (act columns in SiLU·up mode)
+  int32_t mode;           // 0: plain / segmented columns, 1: SiLU(gate)·up
+  int32_t nseg;           // mode 0: 1..3 segments
+  int32_t seg_out0[4];    // mode 0: first output column of segment s; seg_out0[nseg] = N
+  int64_t seg_w0[3];      // mode 0: weight column of segment s's first output column
+  int64_t gate_w0, up_w0; // mode 1: weight columns of act column 0's gate and up inputs
+  int32_t tiles_m, tiles_n;
+};
+
+hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t stream);
+
+struct ReduceNormParams {
+  const uint16_t* P;
+  const uint16_t* residual;  // may be null
+  const uint16_t* gamma;
+  uint16_t* residual_out;
+  uint16_t* Y;
+  int64_t b, n;
+  int32_t t;
+  float eps;
+};
+
+hipError_t launch_reduce_rmsnorm(const ReduceNormParams& p, hipStream_t stream);
+
+}  // namespace ttl

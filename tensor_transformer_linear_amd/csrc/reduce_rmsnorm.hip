@@ -1,0 +1,125 @@
+// Sum of t simulated-rank partials + residual add + RMSNorm, one pass over HBM.
+//
+// One workgroup per token row.  Each thread owns CPT pieces of 8 consecutive bf16 columns
+// (piece c = tid + THREADS*j), read with 16-byte loads so that a wave covers 1 KiB of a row per
+// load instruction.  The row's fp32 sum h stays in registers from the partial-sum pass to the
+// normalisation pass, so every byte is read once and written once:
+//   s = P_0 + P_1 + ... + P_{t-1}   (fp32, ascending rank: fixed order, bitwise reproducible)
+//   h = s + residual                 (fp32); residual_out = bf16(h)
+//   y = bf16(h * rsqrt(mean(h^2) + eps) * gamma)
+// The mean square is reduced within each wave by butterfly shuffles and across waves through LDS
+// in wave order, again a fixed order.
+#include "kernels.h"
+
+namespace ttl {
+namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ inline float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+__device__ inline void add_piece(float* h, u32x4_t v) {
+  h[0] += lo_bf16(v.x); h[1] += hi_bf16(v.x);
+  h[2] += lo_bf16(v.y); h[3] += hi_bf16(v.y);
+  h[4] += lo_bf16(v.z); h[5] += hi_bf16(v.z);
+  h[6] += lo_bf16(v.w); h[7] += hi_bf16(v.w);
+}
+
+template <int CPT, int THREADS>
+__global__ __launch_bounds__(THREADS) void reduce_rmsnorm_kernel(const ReduceNormParams p) {
+  constexpr int kWaves = THREADS / 64;
+  __shared__ float wave_sums[kWaves];
+
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int64_t n = p.n;
+  const int pieces = (int)(n >> 3);
+  const int64_t plane = p.b * n;  // elements of one rank's partial
+
+  float h[CPT][8];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[j][e] = 0.0f;
+
+  const uint16_t* prow = p.P + row * n;
+  for (int r = 0; r < p.t; ++r) {
+    const uint16_t* src = prow + (int64_t)r * plane;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = tid + THREADS * j;
+      if (c < pieces) add_piece(h[j], *reinterpret_cast<const u32x4_t*>(src + (int64_t)c * 8));
+    }
+  }
+  if (p.residual != nullptr) {
+    const uint16_t* rrow = p.residual + row * n;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int c = tid + THREADS * j;
+      if (c < pieces) add_piece(h[j], *reinterpret_cast<const u32x4_t*>(rrow + (int64_t)c * 8));
+    }
+  }
+
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < CPT; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += h[j][e] * h[j][e];  // pieces past n hold zeros
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  if ((tid & 63) == 0) wave_sums[tid >> 6] = ss;
+  __syncthreads();
+  float total = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) total += wave_sums[w];
+  const float inv = __frsqrt_rn(total / (float)n + p.eps);
+
+  uint16_t* rout = p.residual_out + row * n;
+  uint16_t* yrow = p.Y + row * n;
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int c = tid + THREADS * j;
+    if (c < pieces) {
+      const u32x4_t g = *reinterpret_cast<const u32x4_t*>(p.gamma + (int64_t)c * 8);
+      u32x4_t ro, yo;
+      ro.x = pack_bf16x2(h[j][0], h[j][1]);
+      ro.y = pack_bf16x2(h[j][2], h[j][3]);
+      ro.z = pack_bf16x2(h[j][4], h[j][5]);
+      ro.w = pack_bf16x2(h[j][6], h[j][7]);
+      yo.x = pack_bf16x2(h[j][0] * inv * lo_bf16(g.x), h[j][1] * inv * hi_bf16(g.x));
+      yo.y = pack_bf16x2(h[j][2] * inv * lo_bf16(g.y), h[j][3] * inv * hi_bf16(g.y));
+      yo.z = pack_bf16x2(h[j][4] * inv * lo_bf16(g.z), h[j][5] * inv * hi_bf16(g.z));
+      yo.w = pack_bf16x2(h[j][6] * inv * lo_bf16(g.w), h[j][7] * inv * hi_bf16(g.w));
+      *reinterpret_cast<u32x4_t*>(rout + (int64_t)c * 8) = ro;
+      *reinterpret_cast<u32x4_t*>(yrow + (int64_t)c * 8) = yo;
+    }
+  }
+}
+
+template <int CPT, int THREADS>
+hipError_t launch(const ReduceNormParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((reduce_rmsnorm_kernel<CPT, THREADS>), dim3((unsigned)p.b), dim3(THREADS), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_reduce_rmsnorm(const ReduceNormParams& p, hipStream_t stream) {
+  const int64_t pieces = p.n / 8;
+  if (pieces <= 256) return launch<1, 256>(p, stream);
+  if (pieces <= 512) return launch<2, 256>(p, stream);
+  if (pieces <= 1024) return launch<4, 256>(p, stream);
+  if (pieces <= 2048) return launch<8, 256>(p, stream);
+  return launch<8, 1024>(p, stream);  // n <= 65536, checked by the caller
+}
+
+}  // namespace ttl

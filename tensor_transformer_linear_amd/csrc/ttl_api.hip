@@ -1,0 +1,232 @@
+// C ABI of libttl: argument validation, shard addressing and kernel launch.
+//
+// Every entry point validates synchronously and returns a status before anything is enqueued; on
+// success it enqueues its kernel on the caller's stream and returns without waiting.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kernels.h"
+#include "ttl.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ttl_status fail(ttl_status status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte ranges [a, a+na) and [b, b+nb) overlap.
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+constexpr int64_t kMaxDim = 0x7FFFFFFF;
+// Per-tile buffer offsets are 32-bit: 256 input rows and 65 weight rows of pitch must stay < 2^31 B.
+constexpr int64_t kMaxLda = (int64_t)1 << 21;
+constexpr int64_t kMaxLdb = (int64_t)1 << 23;
+
+ttl_status launch_status(hipError_t e, const char* who) {
+  if (e != hipSuccess) return fail(TTL_ERR_HIP, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
+  return TTL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ttl_last_error(void) { return g_last_error.c_str(); }
+
+int32_t ttl_version(void) { return 100; }  // 0.1.0
+
+ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k, const uint16_t* W, int64_t n,
+                            int32_t t, int32_t rank, const ttl_col_split* split, ttl_epilogue epi,
+                            uint16_t* Y, void* stream) {
+  static const char* who = "shard_linear_col";
+  if (X == nullptr || W == nullptr || Y == nullptr)
+    return fail(TTL_ERR_NULL, "%s: X, W and Y must be non-NULL", who);
+  if (b <= 0 || k <= 0 || n <= 0 || b > kMaxDim || k > kMaxDim || n > kMaxDim)
+    return fail(TTL_ERR_SHAPE, "%s: b=%lld k=%lld n=%lld must be in [1, 2^31)", who, (long long)b,
+                (long long)k, (long long)n);
+  if (t < 1 || rank < 0 || rank >= t)
+    return fail(TTL_ERR_RANK, "%s: need t >= 1 and 0 <= rank < t (t=%d rank=%d)", who, t, rank);
+  if (epi != TTL_EPI_NONE && epi != TTL_EPI_SILU_MUL)
+    return fail(TTL_ERR_UNSUPPORTED, "%s: unknown epilogue %d", who, epi);
+
+  ttl_col_split sp;
+  if (split != nullptr) {
+    sp = *split;
+  } else {
+    sp.nseg = 1;
+    sp.seg_n[0] = n;
+    sp.seg_parts[0] = t;
+  }
+  if (sp.nseg < 1 || sp.nseg > TTL_MAX_SEGMENTS)
+    return fail(TTL_ERR_UNSUPPORTED, "%s: nseg=%d must be 1..%d", who, sp.nseg, TTL_MAX_SEGMENTS);
+
+  ttl::GemmParams p = {};
+  int64_t sum = 0, n_r = 0, wcol0[TTL_MAX_SEGMENTS], width[TTL_MAX_SEGMENTS];
+  for (int s = 0; s < sp.nseg; ++s) {
+    const int64_t ns = sp.seg_n[s];
+    const int32_t parts = sp.seg_parts[s];
+    if (ns <= 0) return fail(TTL_ERR_SHAPE, "%s: segment %d has width %lld", who, s, (long long)ns);
+    if (parts < 1 || parts > t || t % parts != 0)
+      return fail(TTL_ERR_NOT_DIVISIBLE, "%s: segment %d is cut into %d parts; need a divisor of t=%d",
+                  who, s, parts, t);
+    if (ns % parts != 0)
+      return fail(TTL_ERR_NOT_DIVISIBLE, "%s: segment %d width %lld is not divisible by %d", who, s,
+                  (long long)ns, parts);
+    width[s] = ns / parts;
+    const int64_t q = (int64_t)rank * parts / t;  // which slice of the segment this rank owns
+    wcol0[s] = sum + q * width[s];
+    sum += ns;
+    n_r += width[s];
+  }
+  if (sum != n)
+    return fail(TTL_ERR_NOT_DIVISIBLE, "%s: segment widths sum to %lld but W has n=%lld columns", who,
+                (long long)sum, (long long)n);
+  if (!aligned16(X) || !aligned16(W) || !aligned16(Y))
+    return fail(TTL_ERR_ALIGN, "%s: X, W and Y must be 16-byte aligned", who);
+  if (k % 8 != 0 || n % 8 != 0)
+    return fail(TTL_ERR_ALIGN, "%s: k=%lld and n=%lld must be multiples of 8", who, (long long)k,
+                (long long)n);
+  for (int s = 0; s < sp.nseg; ++s)
+    if (width[s] % 8 != 0)
+      return fail(TTL_ERR_ALIGN, "%s: slice width %lld of segment %d is not a multiple of 8", who,
+                  (long long)width[s], s);
+  if (k > kMaxLda || n > kMaxLdb)
+    return fail(TTL_ERR_SHAPE, "%s: k=%lld or n=%lld exceeds the supported row pitch", who,
+                (long long)k, (long long)n);
+
+  p.A = X;
+  p.lda = k;
+  p.B = W;
+  p.ldb = n;
+  p.C = Y;
+  p.M = (int32_t)b;
+  p.K = (int32_t)k;
+  if (epi == TTL_EPI_SILU_MUL) {
+    if (sp.nseg != 2 || sp.seg_n[0] != sp.seg_n[1] || sp.seg_parts[0] != sp.seg_parts[1])
+      return fail(TTL_ERR_UNSUPPORTED,
+                  "%s: SiLU*up needs two equal segments (gate | up) with equal part counts", who);
+    p.mode = 1;
+    p.N = (int32_t)width[0];
+    p.ldc = width[0];
+    p.gate_w0 = wcol0[0];
+    p.up_w0 = wcol0[1];
+    p.tiles_n = (p.N + 127) / 128;
+  } else {
+    p.mode = 0;
+    p.N = (int32_t)n_r;
+    p.ldc = n_r;
+    p.nseg = sp.nseg;
+    int64_t out0 = 0;
+    for (int s = 0; s < sp.nseg; ++s) {
+      p.seg_out0[s] = (int32_t)out0;
+      p.seg_w0[s] = wcol0[s];
+      out0 += width[s];
+    }
+    p.seg_out0[sp.nseg] = (int32_t)out0;
+    p.tiles_n = (p.N + 255) / 256;
+  }
+  p.tiles_m = (p.M + 255) / 256;
+  if ((int64_t)p.tiles_m * p.tiles_n > kMaxDim)
+    return fail(TTL_ERR_SHAPE, "%s: too many tiles", who);
+  return launch_status(ttl::launch_gemm_bf16(p, static_cast<hipStream_t>(stream)), who);
+}
+
+ttl_status shard_linear_row(const uint16_t* X, int64_t b, int64_t k, int32_t x_is_parallel,
+                            const uint16_t* W, int64_t n, int32_t t, int32_t rank, uint16_t* P,
+                            void* stream) {
+  static const char* who = "shard_linear_row";
+  if (X == nullptr || W == nullptr || P == nullptr)
+    return fail(TTL_ERR_NULL, "%s: X, W and P must be non-NULL", who);
+  if (b <= 0 || k <= 0 || n <= 0 || b > kMaxDim || k > kMaxDim || n > kMaxDim)
+    return fail(TTL_ERR_SHAPE, "%s: b=%lld k=%lld n=%lld must be in [1, 2^31)", who, (long long)b,
+                (long long)k, (long long)n);
+  if (t < 1 || rank < 0 || rank >= t)
+    return fail(TTL_ERR_RANK, "%s: need t >= 1 and 0 <= rank < t (t=%d rank=%d)", who, t, rank);
+  if (k % t != 0)
+    return fail(TTL_ERR_NOT_DIVISIBLE, "%s: k=%lld is not divisible by t=%d", who, (long long)k, t);
+  const int64_t kr = k / t;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(P))
+    return fail(TTL_ERR_ALIGN, "%s: X, W and P must be 16-byte aligned", who);
+  if (kr % 8 != 0 || n % 8 != 0 || k % 8 != 0)
+    return fail(TTL_ERR_ALIGN, "%s: k/t=%lld and n=%lld must be multiples of 8", who,
+                (long long)kr, (long long)n);
+  const int64_t lda = x_is_parallel ? kr : k;
+  if (lda > kMaxLda || n > kMaxLdb)
+    return fail(TTL_ERR_SHAPE, "%s: row pitch of X or W exceeds the supported range", who);
+
+  ttl::GemmParams p = {};
+  p.A = x_is_parallel ? X : X + (int64_t)rank * kr;
+  p.lda = lda;
+  p.B = W + (int64_t)rank * kr * n;
+  p.ldb = n;
+  p.C = P;
+  p.ldc = n;
+  p.M = (int32_t)b;
+  p.N = (int32_t)n;
+  p.K = (int32_t)kr;
+  p.mode = 0;
+  p.nseg = 1;
+  p.seg_out0[0] = 0;
+  p.seg_out0[1] = (int32_t)n;
+  p.seg_w0[0] = 0;
+  p.tiles_m = (p.M + 255) / 256;
+  p.tiles_n = (p.N + 255) / 256;
+  if ((int64_t)p.tiles_m * p.tiles_n > kMaxDim)
+    return fail(TTL_ERR_SHAPE, "%s: too many tiles", who);
+  return launch_status(ttl::launch_gemm_bf16(p, static_cast<hipStream_t>(stream)), who);
+}
+
+ttl_status reduce_partials_rmsnorm(const uint16_t* P, int32_t t, int64_t b, int64_t n,
+                                   const uint16_t* residual, const uint16_t* gamma, float eps,
+                                   uint16_t* residual_out, uint16_t* Y, void* stream) {
+  static const char* who = "reduce_partials_rmsnorm";
+  if (P == nullptr || gamma == nullptr || residual_out == nullptr || Y == nullptr)
+    return fail(TTL_ERR_NULL, "%s: P, gamma, residual_out and Y must be non-NULL", who);
+  if (t < 1) return fail(TTL_ERR_RANK, "%s: t=%d must be >= 1", who, t);
+  if (b <= 0 || n <= 0 || b > kMaxDim || n > 65536)
+    return fail(TTL_ERR_SHAPE, "%s: need 1 <= b < 2^31 and 1 <= n <= 65536 (b=%lld n=%lld)", who,
+                (long long)b, (long long)n);
+  if (!(eps >= 0.0f)) return fail(TTL_ERR_SHAPE, "%s: eps must be >= 0", who);
+  if (n % 8 != 0) return fail(TTL_ERR_ALIGN, "%s: n=%lld must be a multiple of 8", who, (long long)n);
+  if (!aligned16(P) || !aligned16(gamma) || !aligned16(residual_out) || !aligned16(Y) ||
+      (residual != nullptr && !aligned16(residual)))
+    return fail(TTL_ERR_ALIGN, "%s: all tensors must be 16-byte aligned", who);
+  const int64_t row_bytes = b * n * 2;
+  const int64_t p_bytes = row_bytes * t;
+  if (overlaps(Y, row_bytes, P, p_bytes) || overlaps(Y, row_bytes, gamma, n * 2) ||
+      overlaps(Y, row_bytes, residual_out, row_bytes) ||
+      (residual != nullptr && overlaps(Y, row_bytes, residual, row_bytes)))
+    return fail(TTL_ERR_UNSUPPORTED, "%s: Y must not overlap any other tensor", who);
+  if (overlaps(residual_out, row_bytes, P, p_bytes) || overlaps(residual_out, row_bytes, gamma, n * 2) ||
+      (residual != nullptr && residual != residual_out && overlaps(residual_out, row_bytes, residual, row_bytes)))
+    return fail(TTL_ERR_UNSUPPORTED,
+                "%s: residual_out may alias residual exactly but must not overlap anything else", who);
+
+  ttl::ReduceNormParams p;
+  p.P = P;
+  p.residual = residual;
+  p.gamma = gamma;
+  p.residual_out = residual_out;
+  p.Y = Y;
+  p.b = b;
+  p.n = n;
+  p.t = t;
+  p.eps = eps;
+  return launch_status(ttl::launch_reduce_rmsnorm(p, static_cast<hipStream_t>(stream)), who);
+}
+
+}  // extern "C"

@@ -1,0 +1,183 @@
+"""ctypes binding of libttl (argument marshalling only: every step runs in the HIP library).
+
+The names mirror the C ABI in include/ttl.h.  Tensors are torch bf16 tensors on the GPU; torch is
+used for device memory and streams only.  Importing this module loads libttl.so and raises
+ImportError if it has not been built, so the compute path can never silently fall back to anything
+else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libttl.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m tensor_transformer_linear_amd.build` "
+                      "(or __graft_entry__.build()) before using the HIP path")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+OK = 0
+ERR_NULL, ERR_SHAPE, ERR_NOT_DIVISIBLE, ERR_RANK, ERR_ALIGN, ERR_UNSUPPORTED, ERR_HIP = range(1, 8)
+EPI_NONE = 0
+EPI_SILU_MUL = 1
+MAX_SEGMENTS = 3
+EXPORTED = ("shard_linear_col", "shard_linear_row", "reduce_partials_rmsnorm", "ttl_last_error",
+            "ttl_version")
+
+
+class ColSplit(ctypes.Structure):
+    _fields_ = [("nseg", ctypes.c_int32),
+                ("seg_n", ctypes.c_int64 * MAX_SEGMENTS),
+                ("seg_parts", ctypes.c_int32 * MAX_SEGMENTS)]
+
+
+_c_u16p = ctypes.c_void_p
+_lib.shard_linear_col.restype = ctypes.c_int32
+_lib.shard_linear_col.argtypes = [_c_u16p, ctypes.c_int64, ctypes.c_int64, _c_u16p, ctypes.c_int64,
+                                  ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ColSplit),
+                                  ctypes.c_int32, _c_u16p, ctypes.c_void_p]
+_lib.shard_linear_row.restype = ctypes.c_int32
+_lib.shard_linear_row.argtypes = [_c_u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, _c_u16p,
+                                  ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _c_u16p,
+                                  ctypes.c_void_p]
+_lib.reduce_partials_rmsnorm.restype = ctypes.c_int32
+_lib.reduce_partials_rmsnorm.argtypes = [_c_u16p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                         _c_u16p, _c_u16p, ctypes.c_float, _c_u16p, _c_u16p,
+                                         ctypes.c_void_p]
+_lib.ttl_last_error.restype = ctypes.c_char_p
+_lib.ttl_last_error.argtypes = []
+_lib.ttl_version.restype = ctypes.c_int32
+_lib.ttl_version.argtypes = []
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raw C entry points, for callers that marshal pointers themselves)."""
+    return _lib
+
+
+class TTLError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def last_error() -> str:
+    return (_lib.ttl_last_error() or b"").decode()
+
+
+def _check(status: int):
+    if status != OK:
+        raise TTLError(status, last_error())
+
+
+def make_split(seg_n: Sequence[int], seg_parts: Sequence[int]) -> ColSplit:
+    if not 1 <= len(seg_n) <= MAX_SEGMENTS or len(seg_n) != len(seg_parts):
+        raise ValueError("1..3 segments with one part count each")
+    s = ColSplit()
+    s.nseg = len(seg_n)
+    for i, (w, q) in enumerate(zip(seg_n, seg_parts)):
+        s.seg_n[i] = int(w)
+        s.seg_parts[i] = int(q)
+    return s
+
+
+def merged_gate_up_split(intermediate: int, t: int) -> ColSplit:
+    """gate_up with output_sizes=[I, I]: gate and up are separate segments, each cut into t slices."""
+    return make_split((intermediate, intermediate), (t, t))
+
+
+def qkv_split(n_q_heads: int, n_kv_heads: int, head_dim: int, t: int) -> ColSplit:
+    """q | k | v segments; k and v have min(t, n_kv) distinct slices (replicated when t > n_kv)."""
+    kv_parts = n_kv_heads if t >= n_kv_heads else t
+    return make_split((n_q_heads * head_dim, n_kv_heads * head_dim, n_kv_heads * head_dim),
+                      (t, kv_parts, kv_parts))
+
+
+def split_width(split: Optional[ColSplit], n: int, t: int) -> int:
+    """Output columns of one rank under `split` (None: n / t)."""
+    if split is None:
+        return n // t
+    return sum(split.seg_n[i] // split.seg_parts[i] for i in range(split.nseg))
+
+
+def _dev_ptr(x: Optional[torch.Tensor], name: str) -> Optional[int]:
+    if x is None:
+        return None
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if x.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {x.dtype}")
+    if not x.is_cuda:
+        raise ValueError(f"{name} must live on the GPU (the library has no host path)")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major, dense)")
+    return x.data_ptr()
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def shard_linear_col(X: torch.Tensor, W: torch.Tensor, t: int, rank: int,
+                     split: Optional[ColSplit] = None, epi: int = EPI_NONE,
+                     Y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Column-parallel output of `rank`: X[b,k] · W[:, C_rank] (optionally SiLU(gate)·up)."""
+    b, k = X.shape
+    n = W.shape[1]
+    if W.shape[0] != k:
+        raise ValueError(f"X is [{b},{k}] but W is {tuple(W.shape)}")
+    width = split_width(split, n, t) if t >= 1 else 0
+    ncols = width // 2 if epi == EPI_SILU_MUL else width
+    if Y is None:
+        Y = torch.empty((b, max(ncols, 0)), dtype=torch.bfloat16, device=X.device)
+    _check(_lib.shard_linear_col(_dev_ptr(X, "X"), b, k, _dev_ptr(W, "W"), n, t, rank,
+                                 ctypes.byref(split) if split is not None else None, epi,
+                                 _dev_ptr(Y, "Y"), _stream_handle(stream)))
+    return Y
+
+
+def shard_linear_row(X: torch.Tensor, W: torch.Tensor, t: int, rank: int,
+                     x_is_parallel: bool = True, P: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """Row-parallel partial of `rank`: X_rank · W[rank*k/t:(rank+1)*k/t, :]."""
+    k, n = W.shape
+    b = X.shape[0]
+    if P is None:
+        P = torch.empty((b, n), dtype=torch.bfloat16, device=X.device)
+    _check(_lib.shard_linear_row(_dev_ptr(X, "X"), b, k, 1 if x_is_parallel else 0,
+                                 _dev_ptr(W, "W"), n, t, rank, _dev_ptr(P, "P"),
+                                 _stream_handle(stream)))
+    return P
+
+
+def reduce_partials_rmsnorm(P: torch.Tensor, gamma: torch.Tensor, eps: float,
+                            residual: Optional[torch.Tensor] = None,
+                            residual_out: Optional[torch.Tensor] = None,
+                            Y: Optional[torch.Tensor] = None,
+                            stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Sum of the t partials P[t,b,n] + residual, then RMSNorm; returns (residual_out, Y)."""
+    t, b, n = P.shape
+    if residual_out is None:
+        residual_out = torch.empty((b, n), dtype=torch.bfloat16, device=P.device)
+    if Y is None:
+        Y = torch.empty((b, n), dtype=torch.bfloat16, device=P.device)
+    _check(_lib.reduce_partials_rmsnorm(_dev_ptr(P, "P"), t, b, n, _dev_ptr(residual, "residual"),
+                                        _dev_ptr(gamma, "gamma"), float(eps),
+                                        _dev_ptr(residual_out, "residual_out"), _dev_ptr(Y, "Y"),
+                                        _stream_handle(stream)))
+    return residual_out, Y
+
+
+def version() -> int:
+    return int(_lib.ttl_version())

@@ -1,0 +1,126 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the header declares, and
+rejects bad arguments with the documented status before touching the device.
+
+Every call below fails validation, so no kernel is launched and no HIP call is made.  Pointers are
+fake, suitably aligned integers that are never dereferenced.
+"""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+from tensor_transformer_linear_amd import ttl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ttl.h")
+
+A, B, C, D = 0x10000, 0x20000, 0x30000, 0x40000  # fake 16-byte-aligned device addresses
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:ttl_status|const char\*|int32_t)\s+(\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(ttl.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", ttl.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(ttl.lib(), name)
+
+
+def test_status_codes_match_header():
+    text = open(HEADER).read()
+    codes = dict((m[0], int(m[1])) for m in re.findall(r"#define (TTL_\w+) (\d+)", text))
+    assert codes["TTL_OK"] == ttl.OK
+    assert codes["TTL_ERR_NULL"] == ttl.ERR_NULL
+    assert codes["TTL_ERR_SHAPE"] == ttl.ERR_SHAPE
+    assert codes["TTL_ERR_NOT_DIVISIBLE"] == ttl.ERR_NOT_DIVISIBLE
+    assert codes["TTL_ERR_RANK"] == ttl.ERR_RANK
+    assert codes["TTL_ERR_ALIGN"] == ttl.ERR_ALIGN
+    assert codes["TTL_ERR_UNSUPPORTED"] == ttl.ERR_UNSUPPORTED
+    assert codes["TTL_ERR_HIP"] == ttl.ERR_HIP
+    assert codes["TTL_EPI_SILU_MUL"] == ttl.EPI_SILU_MUL
+    assert codes["TTL_MAX_SEGMENTS"] == ttl.MAX_SEGMENTS
+    assert ttl.version() >= 100
+
+
+def _col(X=A, b=16, k=256, W=B, n=1376, t=2, rank=0, split=None, epi=0, Y=C):
+    sp = None if split is None else ttl.ctypes.byref(split)
+    return ttl.lib().shard_linear_col(X, b, k, W, n, t, rank, sp, epi, Y, None)
+
+
+def _row(X=A, b=16, k=688, par=1, W=B, n=256, t=2, rank=0, P=C):
+    return ttl.lib().shard_linear_row(X, b, k, par, W, n, t, rank, P, None)
+
+
+def _red(P=A, t=2, b=16, n=256, R=B, gamma=D, eps=1e-5, Rout=B, Y=C):
+    return ttl.lib().reduce_partials_rmsnorm(P, t, b, n, R, gamma, eps, Rout, Y, None)
+
+
+@pytest.mark.parametrize("call,status,needle", [
+    (lambda: _col(X=None), ttl.ERR_NULL, "non-NULL"),
+    (lambda: _col(Y=None), ttl.ERR_NULL, "non-NULL"),
+    (lambda: _col(b=0), ttl.ERR_SHAPE, "b=0"),
+    (lambda: _col(k=-8), ttl.ERR_SHAPE, ""),
+    (lambda: _col(t=0), ttl.ERR_RANK, "t=0"),
+    (lambda: _col(rank=2), ttl.ERR_RANK, "rank=2"),
+    (lambda: _col(rank=-1), ttl.ERR_RANK, ""),
+    (lambda: _col(n=1370, t=4), ttl.ERR_NOT_DIVISIBLE, "not divisible"),
+    (lambda: _col(split=ttl.make_split((688, 680), (2, 2))), ttl.ERR_NOT_DIVISIBLE, "sum to 1368"),
+    (lambda: _col(split=ttl.make_split((688, 688), (2, 3)), t=6), ttl.ERR_NOT_DIVISIBLE, "divisible by 3"),
+    (lambda: _col(split=ttl.make_split((688, 688), (4, 4)), t=2), ttl.ERR_NOT_DIVISIBLE, "divisor"),
+    (lambda: _col(X=A + 8), ttl.ERR_ALIGN, "aligned"),
+    (lambda: _col(k=252), ttl.ERR_ALIGN, "multiples of 8"),
+    (lambda: _col(n=1376, t=4, split=ttl.make_split((688, 688), (4, 4))), ttl.ERR_ALIGN, "slice width 172"),
+    (lambda: _col(epi=1), ttl.ERR_UNSUPPORTED, "two equal segments"),
+    (lambda: _col(epi=1, split=ttl.make_split((704, 672), (2, 2))), ttl.ERR_UNSUPPORTED, "two equal"),
+    (lambda: _col(epi=7), ttl.ERR_UNSUPPORTED, "epilogue"),
+    (lambda: _row(P=None), ttl.ERR_NULL, "non-NULL"),
+    (lambda: _row(n=0), ttl.ERR_SHAPE, ""),
+    (lambda: _row(rank=5), ttl.ERR_RANK, ""),
+    (lambda: _row(k=689), ttl.ERR_NOT_DIVISIBLE, "not divisible"),
+    (lambda: _row(k=680, t=4), ttl.ERR_ALIGN, "k/t=170"),
+    (lambda: _row(W=B + 2), ttl.ERR_ALIGN, "aligned"),
+    (lambda: _red(P=None), ttl.ERR_NULL, ""),
+    (lambda: _red(gamma=None), ttl.ERR_NULL, ""),
+    (lambda: _red(t=0), ttl.ERR_RANK, ""),
+    (lambda: _red(n=65544), ttl.ERR_SHAPE, "65536"),
+    (lambda: _red(b=0), ttl.ERR_SHAPE, ""),
+    (lambda: _red(eps=-1.0), ttl.ERR_SHAPE, "eps"),
+    (lambda: _red(n=252), ttl.ERR_ALIGN, "multiple of 8"),
+    (lambda: _red(Y=C + 4), ttl.ERR_ALIGN, "aligned"),
+    (lambda: _red(Y=A + 16), ttl.ERR_UNSUPPORTED, "overlap"),
+    (lambda: _red(Rout=A), ttl.ERR_UNSUPPORTED, "alias"),
+    (lambda: _red(R=B, Rout=B + 16), ttl.ERR_UNSUPPORTED, "alias"),
+], ids=lambda v: v if isinstance(v, (int, str)) else "")
+def test_validation_rejects_before_launch(call, status, needle):
+    got = call()
+    assert got == status, (got, ttl.last_error())
+    assert needle in ttl.last_error()
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    X = torch.zeros(16, 256, dtype=torch.bfloat16)
+    W = torch.zeros(256, 1376, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        ttl.shard_linear_col(X, W, 2, 0, ttl.merged_gate_up_split(688, 2), ttl.EPI_SILU_MUL)
+    with pytest.raises(TypeError, match="bfloat16"):
+        ttl.shard_linear_row(X.float(), W, 2, 0)
+
+
+def test_split_helpers_match_header_rule():
+    sp = ttl.qkv_split(64, 8, 128, 8)
+    assert ttl.split_width(sp, 10240, 8) == 1280
+    sp = ttl.qkv_split(32, 4, 128, 8)
+    assert [sp.seg_parts[i] for i in range(3)] == [8, 4, 4]
+    assert ttl.split_width(ttl.merged_gate_up_split(28672, 8), 57344, 8) == 7168

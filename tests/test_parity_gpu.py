@@ -1,0 +1,174 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on seeded synthetic inputs.
+
+Small cases compare every element; they span several 256-wide tiles and ragged tails in all three
+GEMM dimensions.  Tolerance: max |gpu - ref| <= 2e-2 * rms(ref) per output tensor, the reference
+being the oracle's float64 value (bf16 inputs, so the only device-side error is fp32 accumulation,
+fp32 elementwise math and the final bf16 rounding).  Integer-exact special cases (identity and
+one-hot operands) are compared bit for bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tensor_transformer_linear_amd import workloads as wl
+from tests.util import assert_close, f64, from_gpu, gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ttl():
+    from tensor_transformer_linear_amd import ttl as lib
+    assert torch.cuda.is_available()
+    return lib
+
+
+def _col_case(ttl, b, k, split_np, split_c, t, seed, epi=0):
+    n = sum(split_np[0])
+    X = wl.random_bf16((b, k), seed)
+    W = wl.random_bf16((k, n), seed + 1, std=0.05)
+    Xd, Wd = gpu(X), gpu(W)
+    Xo, Wo = f64(X), f64(W)
+    for r in range(t):
+        Y = ttl.shard_linear_col(Xd, Wd, t, r, split_c, epi)
+        ref = oracle.col_shard(Xo, Wo, split_np, t, r)
+        if epi == ttl.EPI_SILU_MUL:
+            ref = oracle.silu_mul(ref)
+        assert_close(from_gpu(Y), ref, f"col b={b} k={k} n={n} t={t} r={r} epi={epi}")
+
+
+@pytest.mark.parametrize("b,k,I,t", [
+    (16, 256, 688, 2),      # the tiny workload's gate_up shape
+    (1, 64, 128, 2),        # single row, one k-tile
+    (300, 200, 344, 1),     # ragged in M (300), K (200) and N (344 act columns)
+    (257, 512, 1024, 4),    # one row past a 256 tile
+    (513, 1024, 2048, 8),   # several tiles in every dimension
+])
+def test_col_silu_mul(ttl, b, k, I, t):
+    _col_case(ttl, b, k, oracle.merged_gate_up_split(I, t), ttl.merged_gate_up_split(I, t), t,
+              seed=10 + b, epi=ttl.EPI_SILU_MUL)
+
+
+@pytest.mark.parametrize("b,k,n,t", [(16, 256, 1376, 2), (300, 136, 520, 1), (260, 512, 2048, 4)])
+def test_col_plain(ttl, b, k, n, t):
+    _col_case(ttl, b, k, oracle.plain_split(n, t), None, t, seed=20 + b)
+
+
+@pytest.mark.parametrize("b,k,nq,nkv,hd,t", [
+    (70, 256, 8, 4, 32, 4),    # t == n_kv
+    (70, 256, 16, 8, 16, 4),   # t < n_kv: 2 kv heads per rank
+    (33, 128, 8, 2, 32, 4),    # t > n_kv: one kv head per rank, replicated twice
+    (300, 512, 32, 8, 128, 4), # the 8B attention head layout at a small batch
+])
+def test_col_qkv(ttl, b, k, nq, nkv, hd, t):
+    _col_case(ttl, b, k, oracle.qkv_split(nq, nkv, hd, t), ttl.qkv_split(nq, nkv, hd, t), t, seed=30 + b)
+
+
+@pytest.mark.parametrize("b,k,n,t", [(16, 688, 256, 2), (300, 344, 520, 1), (257, 1024, 768, 4),
+                                     (5, 2048, 264, 8)])
+@pytest.mark.parametrize("x_is_parallel", [True, False])
+def test_row(ttl, b, k, n, t, x_is_parallel):
+    w = k // t
+    X = wl.random_bf16((b, k), 40 + b)
+    W = wl.random_bf16((k, n), 41 + b, std=0.05)
+    Xd, Wd = gpu(X), gpu(W)
+    Xo, Wo = f64(X), f64(W)
+    for r in range(t):
+        xin = Xd[:, r * w:(r + 1) * w].contiguous() if x_is_parallel else Xd
+        P = ttl.shard_linear_row(xin, Wd, t, r, x_is_parallel)
+        ref = oracle.row_shard(Xo, Wo, t, r, x_is_parallel=False)
+        assert_close(from_gpu(P), ref, f"row b={b} k={k} n={n} t={t} r={r} par={x_is_parallel}")
+
+
+@pytest.mark.parametrize("t,b,n,with_residual", [(2, 16, 256, True), (8, 5, 4096, True),
+                                                  (1, 3, 8, True), (4, 33, 8192, False),
+                                                  (3, 7, 4104, True), (2, 4, 16384, True),
+                                                  (2, 2, 65536, True)])
+def test_reduce_rmsnorm(ttl, t, b, n, with_residual):
+    P = wl.random_bf16((t, b, n), 50 + n)
+    R = wl.random_bf16((b, n), 51 + n) if with_residual else None
+    gamma = wl.random_bf16((n,), 52 + n, mean=1.0, std=0.1)
+    Rd = gpu(R) if with_residual else None
+    rout, y = ttl.reduce_partials_rmsnorm(gpu(P), gpu(gamma), 1e-5, Rd)
+    h, yref = oracle.reduce_partials_rmsnorm(f64(P), f64(R) if with_residual else None, f64(gamma), 1e-5)
+    assert_close(from_gpu(rout), h, f"reduce residual_out t={t} b={b} n={n}")
+    assert_close(from_gpu(y), yref, f"reduce y t={t} b={b} n={n}")
+
+
+def test_reduce_residual_in_place(ttl):
+    t, b, n = 4, 9, 1024
+    P, R = wl.random_bf16((t, b, n), 60), wl.random_bf16((b, n), 61)
+    gamma = wl.random_bf16((n,), 62, mean=1.0, std=0.1)
+    Rd = gpu(R)
+    rout, y = ttl.reduce_partials_rmsnorm(gpu(P), gpu(gamma), 1e-5, Rd, residual_out=Rd)
+    assert rout.data_ptr() == Rd.data_ptr()
+    h, yref = oracle.reduce_partials_rmsnorm(f64(P), f64(R), f64(gamma), 1e-5)
+    assert_close(from_gpu(Rd), h, "in-place residual")
+    assert_close(from_gpu(y), yref, "in-place y")
+
+
+def test_identity_and_one_hot_are_exact(ttl):
+    # W = identity: every column of the output is one column of X, exactly.
+    b, k, t = 40, 256, 2
+    X = wl.random_bf16((b, k), 70)
+    W = torch.eye(k, dtype=torch.bfloat16)
+    Y0 = ttl.shard_linear_col(gpu(X), gpu(W), t, 1)
+    assert torch.equal(Y0.cpu(), X[:, k // t:])
+    # one-hot rows of X: each output row is a row of W, exactly (row split: of the rank's rows).
+    n = 264
+    Wr = wl.random_bf16((k, n), 71)
+    Xo = torch.zeros((b, k), dtype=torch.bfloat16)
+    idx = torch.arange(b) * 7 % k
+    Xo[torch.arange(b), idx] = 1.0
+    P = ttl.shard_linear_row(gpu(Xo), gpu(Wr), 1, 0, x_is_parallel=True)
+    assert torch.equal(P.cpu(), Wr[idx])
+
+
+def test_bitwise_deterministic(ttl):
+    b, k, I, t = 300, 512, 1024, 2
+    X, Wgu = gpu(wl.random_bf16((b, k), 80)), gpu(wl.random_bf16((k, 2 * I), 81, std=0.05))
+    Wd = gpu(wl.random_bf16((I, k), 82, std=0.05))
+    sp = ttl.merged_gate_up_split(I, t)
+    outs = []
+    for _ in range(2):
+        act = ttl.shard_linear_col(X, Wgu, t, 1, sp, ttl.EPI_SILU_MUL)
+        P = torch.stack([ttl.shard_linear_row(act, Wd, t, 1) for _ in range(2)])
+        r, y = ttl.reduce_partials_rmsnorm(P, gpu(torch.ones(k, dtype=torch.bfloat16)), 1e-5)
+        torch.cuda.synchronize()
+        outs.append((act.cpu(), P.cpu(), r.cpu(), y.cpu()))
+    for a, c in zip(*outs):
+        assert torch.equal(a, c)
+
+
+def test_tiny_mlp_chain_all_ranks(ttl):
+    """The tiny Llama-style MLP (hidden 256, intermediate 688, t = 2, 16 tokens) end to end."""
+    w = wl.TINY_MLP_T2
+    b = w.batches[0]
+    inp = wl.mlp_inputs(w, b, seed=0)
+    d = {k: gpu(v) for k, v in inp.items()}
+    o = {k: f64(v) for k, v in inp.items()}
+    sp = ttl.merged_gate_up_split(w.intermediate, w.t)
+    P = torch.empty((w.t, b, w.hidden), dtype=torch.bfloat16, device="cuda")
+    acts = []
+    for r in range(w.t):
+        act = ttl.shard_linear_col(d["X"], d["Wgu"], w.t, r, sp, ttl.EPI_SILU_MUL)
+        ttl.shard_linear_row(act, d["Wd"], w.t, r, True, P=P[r])
+        acts.append(act)
+    rout, y = ttl.reduce_partials_rmsnorm(P, d["gamma"], w.eps, d["R"])
+    ref_acts, ref_P = oracle.mlp_rank_chain(o["X"], o["Wgu"], o["Wd"], w.t, w.intermediate)
+    h, yref = oracle.reduce_partials_rmsnorm(ref_P, o["R"], o["gamma"], w.eps)
+    for r in range(w.t):
+        assert_close(from_gpu(acts[r]), ref_acts[r], f"tiny act r={r}")
+        assert_close(from_gpu(P[r]), ref_P[r], f"tiny partial r={r}")
+    assert_close(from_gpu(rout), h, "tiny residual_out")
+    assert_close(from_gpu(y), yref, "tiny y")
+    # the unrounded float64 chain (no bf16 storage between steps) is within tolerance too
+    _, P64 = oracle.mlp_rank_chain(o["X"], o["Wgu"], o["Wd"], w.t, w.intermediate, store_bf16=False)
+    h64, y64 = oracle.reduce_partials_rmsnorm(P64, o["R"], o["gamma"], w.eps)
+    assert_close(from_gpu(y), y64, "tiny y vs unrounded chain")
+    # the sum of the rank partials equals the unsharded gated MLP (row-split invariant)
+    full = (oracle.silu(o["X"] @ o["Wgu"][:, :w.intermediate]) * (o["X"] @ o["Wgu"][:, w.intermediate:])) @ o["Wd"]
+    psum = from_gpu(P).sum(0)
+    assert_close(psum, full, "tiny sum of partials vs unsharded MLP")
