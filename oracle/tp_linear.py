@@ -241,20 +241,23 @@ def reduce_partials_rmsnorm(P, residual, gamma, eps: float):
 
 
 def mlp_rank_chain(X, Wgu, Wd, t: int, intermediate: int, store_bf16: bool = True):
-    """gate_up (column, merged) -> silu*up -> down (row) for every rank; returns (acts, P).
+    """gate_up (column, merged) -> silu*up -> down (row) for every rank.
 
-    With store_bf16 the per-rank activation and partial are rounded to bf16 where the library
-    boundary stores them in bf16 (the rank's act tensor and its partial); the next step reads those.
+    Returns (acts, P, acts_stored, P_stored).  acts[r] and P[r] are each step's exact value given
+    the inputs that step reads; with store_bf16 those inputs are the bf16 values the library
+    boundary stores between steps (the rank's act tensor, its partial), i.e. acts_stored[r] =
+    round_bf16(acts[r]) feeds the down projection and P_stored = round_bf16(P) feeds the reduction.
+    Without store_bf16 the stored values equal the exact ones.
     """
     split = merged_gate_up_split(intermediate, t)
-    acts, parts = [], []
+    acts, parts, acts_s, parts_s = [], [], [], []
     for r in range(t):
         act = silu_mul(col_shard(X, Wgu, split, t, r))
-        if store_bf16:
-            act = round_bf16(act)
-        p = row_shard(act, Wd, t, r, x_is_parallel=True)
-        if store_bf16:
-            p = round_bf16(p)
+        act_s = round_bf16(act) if store_bf16 else act
+        p = row_shard(act_s, Wd, t, r, x_is_parallel=True)
+        p_s = round_bf16(p) if store_bf16 else p
         acts.append(act)
+        acts_s.append(act_s)
         parts.append(p)
-    return acts, np.stack(parts)
+        parts_s.append(p_s)
+    return acts, np.stack(parts), acts_s, np.stack(parts_s)

