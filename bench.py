@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the secondary 64-token decode line")
     ap.add_argument("--cpu-rows", type=int, default=32, help="token rows in the CPU oracle sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (5 times) and exit: the "
+                         "reference for scaling HBM traffic counters")
     return ap.parse_args()
 
 
@@ -174,11 +177,20 @@ def main():
               "HBM); runs on more than one GPU are not part of this benchmark.", file=sys.stderr)
         return 2
     import torch
-    from tensor_transformer_linear_amd import ttl
-    from tensor_transformer_linear_amd import workloads as wl
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
+        return 0
+    from tensor_transformer_linear_amd import ttl
+    from tensor_transformer_linear_amd import workloads as wl
     w = wl.LLAMA3_70B_MLP_TP8
     b = args.batch
     res = run_mlp(ttl, torch, w, b, args.steps, args.warmup, seed=0)
