@@ -57,6 +57,15 @@ typedef int32_t ttl_epilogue;
 #define TTL_EPI_NONE 0
 #define TTL_EPI_SILU_MUL 1
 
+/* Storage of the weight W[k,n] (the logical operand is always W[k,n]):
+ *   TTL_W_KN: row-major [k][n], row stride n — the statement's own layout;
+ *   TTL_W_NK: the transpose stored row-major, [n][k], row stride k — how PyTorch-style Linear
+ *             weights ([out_features, in_features]) are kept; the matrix cores read it without a
+ *             transpose.  Its byte extent must stay below 2 GiB. */
+typedef int32_t ttl_weight_layout;
+#define TTL_W_KN 0
+#define TTL_W_NK 1
+
 #define TTL_MAX_SEGMENTS 3
 
 /*
@@ -79,7 +88,7 @@ typedef struct {
  * (vLLM walkthrough, section "ColumnParallelLinear": the rank keeps its own n/t columns).
  *
  *   X      [b, k]  bf16, the full (replicated) input.
- *   W      [k, n]  bf16, the full weight; only the rank's columns are read.
+ *   W      the full weight W[k, n] stored as `w_layout` says; only the rank's columns are read.
  *   split  column split (see ttl_col_split); NULL means one segment cut into t slices.
  *   epi    TTL_EPI_NONE: Y[b, n_r] = X · W[:, C_r], n_r = Σ_i seg_n[i] / seg_parts[i].
  *          TTL_EPI_SILU_MUL: the split must have two equal segments (gate | up) with equal part
@@ -90,11 +99,11 @@ typedef struct {
  *   Y      output, row stride n_r (or n_r/2), caller-allocated.
  * Errors: NULL X/W/Y -> NULL; b,k,n <= 0 -> SHAPE; bad t/rank -> RANK; a segment width not
  * divisible by its part count, part count neither t nor a divisor of t, or widths not summing to n
- * -> NOT_DIVISIBLE; misalignment -> ALIGN; SILU_MUL with an unsuitable split or nseg outside 1..3
- * -> UNSUPPORTED.
+ * -> NOT_DIVISIBLE; misalignment -> ALIGN; SILU_MUL with an unsuitable split, nseg outside 1..3, an
+ * unknown w_layout or a TTL_W_NK weight of 2 GiB or more -> UNSUPPORTED.
  */
 ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k,
-                            const uint16_t* W, int64_t n,
+                            const uint16_t* W, int64_t n, ttl_weight_layout w_layout,
                             int32_t t, int32_t rank,
                             const ttl_col_split* split,
                             ttl_epilogue epi,
@@ -110,14 +119,14 @@ ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k,
  *          act of shard_linear_col);  x_is_parallel == 0: the full input [b, k], whose columns
  *          [r·k/t, (r+1)·k/t) are used (split along the last dimension).
  *   k      the FULL input dimension of W.
- *   W      [k, n] bf16, full weight; rows [r·k/t, (r+1)·k/t) are read.
+ *   W      the full weight W[k, n] stored as `w_layout` says; W's rows [r·k/t, (r+1)·k/t) are read.
  *   P      [b, n] bf16 partial for this rank (for simulated ranks, the caller passes P + r·b·n of
  *          a [t, b, n] buffer).
  * Errors: as above; k not divisible by t -> NOT_DIVISIBLE.
  */
 ttl_status shard_linear_row(const uint16_t* X, int64_t b, int64_t k,
                             int32_t x_is_parallel,
-                            const uint16_t* W, int64_t n,
+                            const uint16_t* W, int64_t n, ttl_weight_layout w_layout,
                             int32_t t, int32_t rank,
                             uint16_t* P,
                             void* stream);

@@ -1,37 +1,47 @@
 // Tiled bf16 GEMM on the CDNA4 matrix cores for the column- and row-parallel shards.
 //
-// C[M, N] = A[M, K] · B[K, map(N)] with A = the rank's input rows (k contiguous) and B = the
-// unsharded weight W[k, n] (n contiguous), addressed in place: the rank's columns are chosen by a
-// column map (plain slice, up to three q|k|v segments, or paired gate|up columns for the fused
-// SiLU·up epilogue) and the rank's rows by the B base pointer.
+// C[M, N] = A[M, K] · B[K, map(N)]: A = the rank's input rows (k contiguous), B = the unsharded
+// weight, addressed in place.  The weight is stored either as W[k][n] (n contiguous, the layout of
+// the statement Y = X·W) or transposed as W^T[n][k] (k contiguous, the layout PyTorch-style Linear
+// weights are kept in).  The rank's columns are chosen by a column map (plain slice, up to three
+// q|k|v segments, or paired gate|up columns for the fused SiLU·up epilogue) and the rank's rows by
+// the B base pointer.
 //
-// Workgroup tile 256 x 256 x 64, 256 threads = 4 wave64s in a 2 x 2 grid, each wave owning a
-// 128 x 128 block as 4 x 4 v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per lane, held in the
-// accumulation registers).
+// Workgroup tile 256 x 256 weight columns, k-tiles of 64 (each A row and W^T row then contributes
+// one whole 128-B line per k-tile).  Eight wave64s (two per SIMD, so one
+// wave's LDS reads, waits and barrier overlap the other's matrix work) in a 2 x 4 grid, each owning
+// 128 x 64 outputs as 4 x 2 v_mfma_f32_32x32x16_bf16 accumulators.
 //
 // Data movement (gfx950):
-//  * Global -> LDS without passing through registers: buffer_load_dwordx4 ... lds, 64 lanes x 16 B
-//    = 1 KiB of LDS per instruction, lane i landing at byte 16*i of the instruction's block.  Each
-//    lane picks the global piece that must land there, which is how the LDS layouts below get their
-//    XOR swizzles.
-//  * Two LDS stages (distinct __shared__ objects, so the compiler can tell the stage being read from
-//    the one being filled): the copy of k-tile kt+1 is in flight while the matrix cores consume
-//    k-tile kt; one wait + barrier per k-tile.
-//  * A (X rows) is staged as [256 m][64 k]: 8 chunks of 16 B per 128-B row, chunk c stored at slot
-//    c ^ (m % 8), so the 32 rows a 32 x 32 block reads at one k-chunk spread over all banks.
-//  * B (W rows) is staged as loaded, [64 k][256 n]: 32 chunks per 512-B row, chunk c stored at slot
-//    c ^ (2 * (k % 4)).  The matrix cores want 8 consecutive k of one n per lane; ds_read_b64_tr_b16
-//    returns, in each 16-lane group, the transpose of a 4 (k) x 16 (n) block — lane j of the group
-//    addresses row k0 + j/4 at n0 + 4*(j%4) and receives k0..k0+3 at n0 + j — so two such reads
-//    build one operand with no transpose in registers.  The swizzle puts the 4 rows x 32 B of one
-//    group read on distinct banks.
+//  * Global -> LDS without registers: buffer_load_dwordx4 ... lds moves 64 lanes x 16 B = 1 KiB per
+//    instruction, lane i landing at byte 16*i of the instruction's block.  Each lane picks the global
+//    piece that must land there, which is how the LDS layouts below get their XOR swizzles.
+//  * A ring of kStages k-tiles in LDS (two 64-KiB stages): tiles kt+1 .. kt+kStages-1 are in flight
+//    while tile kt is read; one wait + barrier per k-tile.
+//  * LDS has 64 banks of 4 B; 16 lanes reading 16 B each (or 32 lanes reading 8 B each) are
+//    conflict-free when they cover 256 distinct bytes modulo 256.
+//  * A (and B when stored [n][k]) is staged as [256 rows][64 k]: eight 16-B chunks per 128-B row,
+//    chunk c of row m at slot c ^ ((m / 2) % 8), so the 16 rows one ds_read_b128 touches at one
+//    k-chunk fall on distinct banks.
+//  * B stored [k][n] is staged as loaded, [64 k][256 n]: 32 chunks per 512-B row, chunk c of row k at
+//    slot c ^ (4 * (k % 4)).  The matrix cores want 8 consecutive k of one n per lane;
+//    ds_read_b64_tr_b16 returns, in each 16-lane group, the transpose of a 4 (k) x 16 (n) block —
+//    lane j of the group addresses row k0 + j/4 at n0 + 4*(j%4) and receives k0..k0+3 at n0 + j — so
+//    two such reads build one operand without a transpose in registers.
 //  * Tiles are ordered for the L2 of each XCD: consecutive workgroups go to different XCDs, so the
-//    block index is remapped so that each XCD works on a compact group of tiles (4 row-tiles wide)
-//    that share A rows and W columns in its L2.
+//    block index is remapped so that each XCD works on a compact group of tiles (4 row-tiles tall)
+//    that share A rows and weight columns in its L2.
 //
-// Tails in M, N and K: buffer loads whose offsets are pushed past the record count return zeros, so
-// the k-tail contributes exact zeros and no branch sits in the main loop; stores are masked.
+// Tails in M, N and K: copies whose offsets are pushed past the buffer's record count read zeros, so
+// the k-tail contributes exact zeros and the steady-state loop has no bounds logic; stores are masked.
 #include "kernels.h"
+
+#ifndef TTL_GEMM_BK
+#define TTL_GEMM_BK 64
+#endif
+#ifndef TTL_GEMM_STAGES
+#define TTL_GEMM_STAGES (TTL_GEMM_BK == 64 ? 2 : 4)
+#endif
 
 namespace ttl {
 namespace {
@@ -39,32 +49,43 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 
-constexpr int kBM = 256;
-constexpr int kBN = 256;                  // weight columns per tile
-constexpr int kBK = 64;
-constexpr int kThreads = 256;
-constexpr int kTileElems = kBM * kBK;     // A or B stage, bf16 elements (32 KiB)
-constexpr int kLoadsPerOperand = kTileElems * 2 / (kThreads * 16);  // 16-B pieces per thread = 8
-constexpr int kXcds = 8;                  // MI355X: 8 XCDs, workgroups dealt round-robin
-constexpr int kGroupM = 4;                // row-tiles per L2 group
-constexpr uint32_t kOob = 0x80000000u;    // beyond every record count used below
+constexpr int kBM = 256;                   // output rows per tile
+constexpr int kBN = 256;                   // weight columns per tile
+constexpr int kBK = TTL_GEMM_BK;           // k per stage (64: 128-B global row pieces)
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStages = TTL_GEMM_STAGES;
+constexpr int kWN = 64;                    // weight columns per wave (2 x 4 wave grid)
+constexpr int kNI = kWN / 32;              // 32-wide accumulator blocks per wave along n
+constexpr int kAElems = kBM * kBK;         // A stage (bf16 elements)
+constexpr int kBElems = kBK * kBN;         // B stage
+constexpr int kStageElems = kAElems + kBElems;
+constexpr int kACopies = kAElems * 2 / 1024 / kWaves;   // 1-KiB copies per wave per tile
+constexpr int kBCopies = kBElems * 2 / 1024 / kWaves;
+constexpr int kLoads = kACopies + kBCopies;             // vmcnt increments per wave per tile
+constexpr int kXcds = 8;                   // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr int kGroupM = 4;                 // row-tiles per L2 group
+constexpr uint32_t kOob = 0x80000000u;     // beyond every record count used below
 constexpr int32_t kMaxRecords = 0x7FFFFFF0;
 
-enum { kPlain = 0, kSiluMul = 1 };
+constexpr int kChunks = kBK / 8;           // 16-B chunks per [rows][k] staged row
+constexpr int kRowsPer256 = 256 / (2 * kBK);  // staged rows per 256 B of LDS
+constexpr int kRowsPerCopy = 1024 / (2 * kBK);
+constexpr int kKK = kBK / 16;              // k16 slices per stage
 
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int32_t rec = bytes <= 0 ? 0 : (bytes > kMaxRecords ? kMaxRecords : (int32_t)bytes);
-  // dword3 = 0x00020000: 32-bit data format, the raw (untyped) buffer setting for gfx9 parts.
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, rec, 0x00020000);
-}
+static_assert(kBK == 32 || kBK == 64, "stage depth");
+static_assert(kStages >= 2 && kStages <= 5 && kStages * kStageElems * 2 <= 160 * 1024, "LDS ring");
+static_assert(kBCopies % 2 == 0, "[k][n] copies come in k-row-parity pairs");
+
+enum { kPlain = 0, kSiluMul = 1 };
 
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2_t f = {lo, hi};
@@ -76,15 +97,41 @@ __device__ inline float silu_mul(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
-// The LDS stages: one distinct object per (stage, operand).
-template <int S> __device__ inline uint16_t* stage_a() {
-  __shared__ __attribute__((aligned(1024))) uint16_t buf[kTileElems];
-  return buf;
+// Raw buffer descriptor (gfx9): 48-bit base, stride 0, record count in bytes, dword3 = 0x00020000
+// (32-bit data format, the raw untyped setting).  Accesses at offsets >= the record count read 0.
+__device__ inline i32x4_t buffer_desc(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const int32_t rec = bytes <= 0 ? 0 : (bytes > kMaxRecords ? kMaxRecords : (int32_t)bytes);
+  i32x4_t d;
+  d.x = (int32_t)(uint32_t)a;
+  d.y = (int32_t)((uint32_t)(a >> 32) & 0xFFFFu);
+  d.z = rec;
+  d.w = 0x00020000;
+  return d;
 }
-template <int S> __device__ inline uint16_t* stage_b() {
-  __shared__ __attribute__((aligned(1024))) uint16_t buf[kTileElems];
-  return buf;
+
+// One 16-byte-per-lane copy from global memory straight into LDS (buffer_load_dwordx4 ... lds):
+// lane i's 16 bytes land at lds_base + 16*i.  Written as asm so that the compiler's wait insertion,
+// which cannot follow the ring's stage ownership across the loop, does not drain the ring; every
+// wait for these copies is explicit (wait_vmcnt).  M0 holds the LDS base; one wait state must
+// separate its write from the copy.
+__device__ inline void copy16_to_lds(i32x4_t desc, uint32_t voffset, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voffset), "s"(desc), "s"(lds_base) : "memory");
 }
+
+// Wait until at most N of this wave's vector-memory operations are outstanding.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// Workgroup barrier for the ring.  __syncthreads() carries a release fence, which would make the
+// compiler drain every outstanding copy (vmcnt(0)) before it; the waits this kernel needs are
+// explicit (wait_vmcnt for this wave's copies, lgkmcnt(0) for its LDS reads), and the memory clobber
+// keeps the compiler from moving LDS accesses across the barrier.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Remap the block index so that the tiles one XCD runs form compact groups, then walk tiles in
 // groups of kGroupM row-tiles.  Both maps are bijections on [0, tiles).
@@ -102,187 +149,236 @@ __device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, i
   tn = inner / gsize;
 }
 
+// Weight column of tile column c (the first of 8 consecutive ones), and whether it is in range.
 template <int MODE>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+__device__ inline int64_t weight_column(const GemmParams& p, int n0, int c, bool& ok) {
+  if (MODE == kSiluMul) {
+    // Tile column c = w*64 + nb*32 + j: block nb = 0 of a wave holds gate columns and nb = 1 the up
+    // columns of the same act columns, so gate and up of one output meet in one lane.
+    const int w = c / kWN, nb = (c % kWN) / 32, j = c % 32;
+    const int act = n0 + w * (kWN / 2) + j;
+    ok = act < p.N;
+    return (nb == 0 ? p.gate_w0 : p.up_w0) + act;
+  }
+  const int oc = n0 + c;
+  ok = oc < p.N;
+  int64_t w0 = p.seg_w0[0];
+  int s0 = p.seg_out0[0];
+  if (p.nseg > 1 && oc >= p.seg_out0[1]) { w0 = p.seg_w0[1]; s0 = p.seg_out0[1]; }
+  if (p.nseg > 2 && oc >= p.seg_out0[2]) { w0 = p.seg_w0[2]; s0 = p.seg_out0[2]; }
+  return w0 + (oc - s0);
+}
+
+template <int MODE, bool WNK>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_kernel(const GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages * kStageElems];
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2;  // rows wm*128 .. +127
+  const int wn = wave & 3;   // weight columns wn*64 .. +63
 
   int tile_m, tile_n;
   tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tile_m, tile_n);
   const int m0 = tile_m * kBM;
   const int n0 = tile_n * (MODE == kSiluMul ? kBN / 2 : kBN);  // first output column of the tile
+  const int nk = (p.K + kBK - 1) / kBK;
+  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds);
 
-  // ---- A copy: piece i of this thread is instruction q = wave*8 + i, rows 8q + lane/8, and the
-  // slot lane%8 of the row holds k-chunk (lane%8) ^ (row%8) = (lane%8) ^ (lane/8).
-  const int a_row0 = wave * 64 + (lane >> 3);               // + 8*i
-  const int a_chunk = (lane & 7) ^ (lane >> 3);
-  uint32_t a_rowmask = 0;
+  // ---- Copy offsets, fixed for the whole k loop (the descriptors move with k0).
+  // [rows][kBK] staging (A, and B when WNK): copy i of the wave is block q = kACopies*wave + i of
+  // kRowsPerCopy rows; lane l lands in row q*kRowsPerCopy + l/kChunks at slot l%kChunks, which holds
+  // k-chunk slot ^ ((row / kRowsPer256) % kChunks).
+  uint32_t a_off[kACopies];
+  int a_kc[kACopies];  // first k of the chunk each copy lane moves, for the k-tail test
 #pragma unroll
-  for (int i = 0; i < kLoadsPerOperand; ++i)
-    if (m0 + a_row0 + 8 * i < p.M) a_rowmask |= 1u << i;
-
-  // ---- B copy: instruction q = wave*8 + i covers k rows 2q, 2q+1; lane -> row 2q + lane/32,
-  // slot lane%32, which holds chunk (lane%32) ^ (2*(row%4)).  row%4 = 2*(i%2) + lane/32.
-  int64_t b_wcol[2];
-  uint32_t b_colok = 0;
+  for (int i = 0; i < kACopies; ++i) {
+    const int row = (kACopies * wave + i) * kRowsPerCopy + lane / kChunks;
+    const int chunk = (lane % kChunks) ^ ((row / kRowsPer256) % kChunks);
+    a_kc[i] = chunk * 8;
+    a_off[i] = (m0 + row < p.M) ? (uint32_t)(((int64_t)row * p.lda + chunk * 8) * 2) : kOob;
+  }
+  uint32_t b_off[kBCopies];
+  int b_kc[kBCopies];  // k of each copy lane (first k of its chunk, or its k row), for the k-tail test
 #pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    const int krow4 = 2 * par + (lane >> 5);
-    const int chunk = (lane & 31) ^ (2 * krow4);
-    const int c = chunk * 8;  // tile column of the chunk's first element
-    int64_t wcol;
+  for (int i = 0; i < kBCopies; ++i) {
+    const int q = kBCopies * wave + i;
     bool ok;
-    if (MODE == kSiluMul) {
-      // Tile column c = w*128 + nb*32 + j: blocks nb = 0,1 are gate columns and nb = 2,3 the up
-      // columns of the same act columns, so gate and up of one output meet in one lane.
-      const int w = c >> 7, nb = (c & 127) >> 5, j = c & 31;
-      const int act = n0 + w * 64 + (nb & 1) * 32 + j;
-      ok = act < p.N;
-      wcol = (nb < 2 ? p.gate_w0 : p.up_w0) + act;
+    if (WNK) {
+      const int n = q * kRowsPerCopy + lane / kChunks;  // tile column = staged row
+      const int chunk = (lane % kChunks) ^ ((n / kRowsPer256) % kChunks);
+      const int64_t wrow = weight_column<MODE>(p, n0, n & ~7, ok) + (n & 7);
+      b_off[i] = ok ? (uint32_t)((wrow * p.ldb + chunk * 8) * 2) : kOob;
+      b_kc[i] = chunk * 8;
     } else {
-      const int oc = n0 + c;
-      ok = oc < p.N;
-      int64_t w0 = p.seg_w0[0];
-      int s0 = p.seg_out0[0];
-      if (p.nseg > 1 && oc >= p.seg_out0[1]) { w0 = p.seg_w0[1]; s0 = p.seg_out0[1]; }
-      if (p.nseg > 2 && oc >= p.seg_out0[2]) { w0 = p.seg_w0[2]; s0 = p.seg_out0[2]; }
-      wcol = w0 + (oc - s0);
+      // copy q covers k rows 2q, 2q+1: lane l lands in row 2q + l/32 at slot l%32, holding chunk
+      // (l%32) ^ (4*(row%4)), row%4 = 2*(q%2) + l/32 = 2*(i%2) + l/32.
+      const int krow = 2 * q + (lane >> 5);
+      const int chunk = (lane & 31) ^ (4 * (2 * (i & 1) + (lane >> 5)));
+      const int64_t wcol = weight_column<MODE>(p, n0, chunk * 8, ok);
+      b_off[i] = ok ? (uint32_t)(((int64_t)krow * p.ldb + wcol) * 2) : kOob;
+      b_kc[i] = krow;
     }
-    b_wcol[par] = wcol;
-    if (ok) b_colok |= 1u << par;
   }
 
-  const int nk = (p.K + kBK - 1) / kBK;
-
-  auto copy_tile = [&](int kt, uint16_t* sa, uint16_t* sb) {
-    const int k0 = kt * kBK;
-    const __amdgpu_buffer_rsrc_t ar =
-        make_rsrc(p.A + (int64_t)m0 * p.lda + k0, ((int64_t)(p.M - m0 - 1) * p.lda + (p.K - k0)) * 2);
-    const bool a_kok = k0 + a_chunk * 8 < p.K;
+  auto copy_tile = [&](int t, bool ktail) {
+    const int k0 = t * kBK;
+    const uint32_t st = lds0 + (uint32_t)((t % kStages) * kStageElems * 2);
+    const i32x4_t ad =
+        buffer_desc(p.A + (int64_t)m0 * p.lda + k0, ((int64_t)(p.M - m0 - 1) * p.lda + (p.K - k0)) * 2);
 #pragma unroll
-    for (int i = 0; i < kLoadsPerOperand; ++i) {
-      const uint32_t off = (uint32_t)(((int64_t)(a_row0 + 8 * i) * p.lda + a_chunk * 8) * 2);
-      const uint32_t ok = (uint32_t)a_kok & (a_rowmask >> i);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void*)(sa + (wave * 8 + i) * 512), 16,
-                                               off | (((ok & 1u) - 1u) & kOob), 0, 0, 0);
+    for (int i = 0; i < kACopies; ++i) {
+      const uint32_t off = (ktail && k0 + a_kc[i] >= p.K) ? kOob : a_off[i];
+      copy16_to_lds(ad, off, st + (kACopies * wave + i) * 1024);
     }
-    const __amdgpu_buffer_rsrc_t br =
-        make_rsrc(p.B + (int64_t)k0 * p.ldb, (int64_t)(p.K - k0) * p.ldb * 2);
+    // B: the rows of W^T (b_rows of them, pitch ldb) from column k0, or k rows k0.. of W.
+    const i32x4_t bd =
+        WNK ? buffer_desc(p.B + k0, ((int64_t)(p.b_rows - 1) * p.ldb + (p.K - k0)) * 2)
+            : buffer_desc(p.B + (int64_t)k0 * p.ldb, (int64_t)(p.K - k0) * p.ldb * 2);
 #pragma unroll
-    for (int i = 0; i < kLoadsPerOperand; ++i) {
-      const int q = wave * 8 + i;
-      const int krow = 2 * q + (lane >> 5);
-      const int par = i & 1;
-      const uint32_t off = (uint32_t)(((int64_t)krow * p.ldb + b_wcol[par]) * 2);
-      const uint32_t ok = ((b_colok >> par) & 1u) & (uint32_t)(k0 + krow < p.K);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void*)(sb + q * 512), 16,
-                                               off | ((ok - 1u) & kOob), 0, 0, 0);
+    for (int i = 0; i < kBCopies; ++i) {
+      const uint32_t off = (ktail && k0 + b_kc[i] >= p.K) ? kOob : b_off[i];
+      copy16_to_lds(bd, off, st + kAElems * 2 + (kBCopies * wave + i) * 1024);
     }
   };
 
-  f32x16_t acc[4][4];
+  // ---- Fragment reads (element offsets within a stage).
+  // [rows][kBK] staging: row r, k-chunk kk*2 + lane/32 at slot chunk ^ ((r / kRowsPer256) % kChunks);
+  // for the rows a wave reads, the swizzle term is ((lane%32) / kRowsPer256) % kChunks.
+  const int a_r = lane & 31;
+  const int a_half = lane >> 5;
+  const int rs = (a_r / kRowsPer256) % kChunks;
+  int ra_off[kKK], rb_off[kKK];
+#pragma unroll
+  for (int kk = 0; kk < kKK; ++kk) {
+    const int slot = (kk * 2 + a_half) ^ rs;
+    ra_off[kk] = (wm * 128 + a_r) * kBK + slot * 8;
+    rb_off[kk] = kAElems + (wn * kWN + a_r) * kBK + slot * 8;  // WNK: B rows are weight columns
+  }
+  // [k][n] staging: 16-lane group g = lane/16 reads k row kk*16 + 8*(g/2) + 4*h + (lane%16)/4 at
+  // n = wn*64 + ni*32 + 16*(g%2) + 4*(lane%4): chunk 8*wn + 4*ni + c with c = 2*(g%2) + (lane%4)/2,
+  // stored at slot chunk ^ (4*(k%4)) where k%4 = (lane%16)/4.
+  int rt_off[kNI];
+  {
+    const int krow = 8 * (lane >> 5) + ((lane & 15) >> 2);
+    const int x = 4 * ((lane & 15) >> 2);
+    const int c = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni)
+      rt_off[ni] = kAElems + krow * kBN + ((8 * wn + 4 * ni + c) ^ x) * 8 + 4 * (lane & 1);
+  }
+
+  bf16x8_t af[2][4], bv[2][kNI];
+  auto read_frags = [&](int t, int kk, int buf) {
+    const uint16_t* st = lds + (t % kStages) * kStageElems;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+      af[buf][mi] = *reinterpret_cast<const bf16x8_t*>(st + ra_off[kk] + mi * 32 * kBK);
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) {
+      if (WNK) {
+        bv[buf][ni] = *reinterpret_cast<const bf16x8_t*>(st + rb_off[kk] + ni * 32 * kBK);
+      } else {
+        const uint16_t* b = st + rt_off[ni] + kk * 16 * kBN;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b));
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b + 4 * kBN));
+        bv[buf][ni] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
+  };
+
+  f32x16_t acc[4][kNI];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
-  // Per-lane LDS read offsets (elements), split into a per-lane part and compile-time constants.
-  // A: row wm*128 + mi*32 + lane%32, k-chunk kk*2 + lane/32, stored at slot chunk ^ (row % 8);
-  //    row % 8 = lane % 8, so slot = ((kk ^ s1) << 1) | (lane/32 ^ s0) with s = lane % 8.
-  // B: 16-lane group g = lane/16 reads k row kk*16 + 8*(g/2) + 4*h + (lane%16)/4 at
-  //    n = wn*128 + ni*32 + 16*(g%2) + 4*(lane%4); its chunk n/8 = 16*wn + 4*ni + c with
-  //    c = 2*(g%2) + (lane%4)/2 is stored at slot chunk ^ (2*(k%4)), k%4 = (lane%16)/4, and only
-  //    the parity of ni reaches the XOR.
-  const int a_r = lane & 31;
-  const int a_half = lane >> 5;
-  int a_off[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int slot = (((kk ^ ((a_r & 7) >> 1)) << 1) | (a_half ^ (a_r & 1)));
-    a_off[kk] = (wm * 128 + a_r) * kBK + slot * 8;
-  }
-  int b_off[2];
-  {
-    const int krow = 8 * (lane >> 5) + ((lane & 15) >> 2);
-    const int x = 2 * ((lane & 15) >> 2);
-    const int c = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-#pragma unroll
-    for (int par = 0; par < 2; ++par) {
-      const int slot = (16 * wn + 4 * par + c) ^ x;
-      b_off[par] = krow * kBN + slot * 8 + 4 * (lane & 1);
-    }
-  }
-
-  auto read_frags = [&](const uint16_t* sa, const uint16_t* sb, int kk, bf16x8_t* af, bf16x8_t* bv) {
+  auto mfma_block = [&](int buf) {
+    // Weight block as the first operand: lane l then holds output row (l & 31) and, in
+    // accumulator register r, output column 8*(r/4) + 4*(l/32) + r%4 of the 32 x 32 block.
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
-      af[mi] = *reinterpret_cast<const bf16x8_t*>(sa + a_off[kk] + mi * 32 * kBK);
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const uint16_t* base = sb + b_off[ni & 1] + kk * 16 * kBN + (ni >> 1) * 64;
-      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
-      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 4 * kBN));
-      bv[ni] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int ni = 0; ni < kNI; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[buf][ni], af[buf][mi], acc[mi][ni], 0, 0, 0);
+  };
+  auto interleave_hint = [&]() {
+    // The MFMAs of a slice with the next slice's fragment reads placed one after each MFMA.
+    constexpr int kReads = 4 + (WNK ? 1 : 2) * kNI, kMfma = 4 * kNI;
+#pragma unroll
+    for (int i = 0; i < kReads; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
+    if (kMfma > kReads) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
   };
 
-  auto compute = [&](const uint16_t* sa, const uint16_t* sb) {
-    bf16x8_t af[2][4], bv[2][4];
-    read_frags(sa, sb, 0, af[0], bv[0]);
+  // One k-tile: the MFMAs of each k16 slice overlap the reads of the next; the barrier that
+  // publishes tile kt+1 sits before the MFMAs of the last slice, which overlap the first reads of
+  // tile kt+1.
+  auto compute_tile = [&](int kt, auto wait) {
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int cur = kk & 1;
-      if (kk + 1 < kBK / 16) read_frags(sa, sb, kk + 1, af[cur ^ 1], bv[cur ^ 1]);
-      // Weight block as the first operand: lane l then holds output row (l & 31) and, in
-      // accumulator register r, output column 8*(r/4) + 4*(l/32) + r%4 of the 32 x 32 block.
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[cur][ni], af[cur][mi], acc[mi][ni], 0, 0, 0);
+    for (int kk = 0; kk + 1 < kKK; ++kk) {
+      read_frags(kt, kk + 1, (kk + 1) & 1);
+      mfma_block(kk & 1);
+      interleave_hint();
+      __builtin_amdgcn_sched_barrier(0);
     }
+    wait();
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nk) read_frags(kt + 1, 0, 0);
+    mfma_block((kKK - 1) & 1);
+    interleave_hint();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Two-stage pipeline, unrolled by two so that every access names its stage object statically;
-  // an odd last k-tile is peeled so that the loop has a single exit.
-  copy_tile(0, stage_a<0>(), stage_b<0>());
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  const bool ktail = (p.K % kBK) != 0;
+  // Prologue: tiles 0 .. kStages-2 in flight, tile 0 landed and its first fragments read.
+  for (int t = 0; t < kStages - 1 && t < nk; ++t) copy_tile(t, ktail && t == nk - 1);
+  if (nk >= kStages - 1) wait_vmcnt<(kStages - 2) * kLoads>();
+  else wait_vmcnt<0>();
+  lds_barrier();
+  read_frags(0, 0, 0);
+
   int kt = 0;
-  for (; kt + 2 <= nk; kt += 2) {
-    copy_tile(kt + 1, stage_a<1>(), stage_b<1>());
+  // Steady state: the copy of tile kt + kStages - 1 refills the stage of tile kt - 1, which every
+  // wave left behind at the barrier inside step kt - 1; before the barrier of step kt, tile kt+1
+  // must have landed, i.e. at most the kStages - 2 newer tiles' copies may still be in flight.
+  for (; kt + kStages - 1 < nk; ++kt) {
+    copy_tile(kt + kStages - 1, ktail && kt + kStages - 1 == nk - 1);
     __builtin_amdgcn_sched_barrier(0);
-    compute(stage_a<0>(), stage_b<0>());
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (kt + 2 < nk) copy_tile(kt + 2, stage_a<0>(), stage_b<0>());
-    __builtin_amdgcn_sched_barrier(0);
-    compute(stage_a<1>(), stage_b<1>());
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    compute_tile(kt, [] { wait_vmcnt<(kStages - 2) * kLoads>(); });
   }
-  if (kt < nk) compute(stage_a<0>(), stage_b<0>());
+  // Drain: no more copies; before each barrier only the tiles after kt+1 may still be in flight.
+  for (; kt < nk; ++kt) {
+    const int newer = nk - 1 - (kt + 1);
+    compute_tile(kt, [&] {
+      if (newer >= 3) wait_vmcnt<(kStages >= 5 ? 3 * kLoads : 0)>();
+      else if (newer == 2) wait_vmcnt<(kStages >= 4 ? 2 * kLoads : 0)>();
+      else if (newer == 1) wait_vmcnt<kLoads>();
+      else wait_vmcnt<0>();
+    });
+  }
 
   // Epilogue straight from the accumulators: each lane owns 4 consecutive columns of one row per
   // register group, stored as one 8-byte piece.
   const int row_base = m0 + wm * 128 + a_r;
-  if (MODE == kPlain) {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const int row = row_base + mi * 32;
-      if (row >= p.M) continue;
-      uint16_t* crow = p.C + (int64_t)row * p.ldc;
+  for (int mi = 0; mi < 4; ++mi) {
+    const int row = row_base + mi * 32;
+    if (row >= p.M) continue;
+    uint16_t* crow = p.C + (int64_t)row * p.ldc;
+    if (MODE == kPlain) {
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
+      for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int col = n0 + wn * 128 + ni * 32 + g * 8 + a_half * 4;
+          const int col = n0 + wn * kWN + ni * 32 + g * 8 + a_half * 4;
           if (col < p.N) {
             u32x2_t v;
             v.x = pack_bf16x2(acc[mi][ni][4 * g + 0], acc[mi][ni][4 * g + 1]);
@@ -290,41 +386,40 @@ void gemm_bf16_kernel(const GemmParams p) {
             *reinterpret_cast<u32x2_t*>(crow + col) = v;
           }
         }
-    }
-  } else {
+    } else {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const int row = row_base + mi * 32;
-      if (row >= p.M) continue;
-      uint16_t* crow = p.C + (int64_t)row * p.ldc;
+      for (int g = 0; g < 4; ++g) {
+        const int col = n0 + wn * (kWN / 2) + g * 8 + a_half * 4;
+        if (col < p.N) {
+          float a[4];
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = n0 + wn * 64 + ni * 32 + g * 8 + a_half * 4;
-          if (col < p.N) {
-            float a[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) a[e] = silu_mul(acc[mi][ni][4 * g + e], acc[mi][ni + 2][4 * g + e]);
-            u32x2_t v;
-            v.x = pack_bf16x2(a[0], a[1]);
-            v.y = pack_bf16x2(a[2], a[3]);
-            *reinterpret_cast<u32x2_t*>(crow + col) = v;
-          }
+          for (int e = 0; e < 4; ++e) a[e] = silu_mul(acc[mi][0][4 * g + e], acc[mi][1][4 * g + e]);
+          u32x2_t v;
+          v.x = pack_bf16x2(a[0], a[1]);
+          v.y = pack_bf16x2(a[2], a[3]);
+          *reinterpret_cast<u32x2_t*>(crow + col) = v;
         }
+      }
     }
   }
 }
 
+template <int MODE, bool WNK>
+void launch_one(const GemmParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_bf16_kernel<MODE, WNK>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
+                     dim3(kThreads), 0, stream, p);
+}
+
 }  // namespace
 
+int gemm_tile_rows() { return kBM; }
+int gemm_tile_cols(int mode) { return mode == kSiluMul ? kBN / 2 : kBN; }
+
 hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
-  const dim3 block(kThreads);
   if (p.mode == kSiluMul)
-    hipLaunchKernelGGL(gemm_bf16_kernel<kSiluMul>, grid, block, 0, stream, p);
+    p.w_nk ? launch_one<kSiluMul, true>(p, stream) : launch_one<kSiluMul, false>(p, stream);
   else
-    hipLaunchKernelGGL(gemm_bf16_kernel<kPlain>, grid, block, 0, stream, p);
+    p.w_nk ? launch_one<kPlain, true>(p, stream) : launch_one<kPlain, false>(p, stream);
   return hipGetLastError();
 }
 

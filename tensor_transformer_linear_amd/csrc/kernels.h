@@ -8,8 +8,9 @@ namespace ttl {
 
 // Parameters of one tiled bf16 GEMM launch: C[M, N] = A[M, K] · B_map[K, N].
 // A rows have stride lda (elements); A already points at the first column the rank uses.
-// B is the weight, row stride ldb, already pointing at the first row the rank uses; output column
-// j reads weight column wcol(j) given by the column map below.
+// B is the weight: w_nk = 0 stores it as W[k][n] (row stride ldb, B at the first k row the rank
+// uses); w_nk = 1 stores W^T[n][k] (row stride ldb, b_rows rows, B at the first k column the rank
+// uses).  Output column j reads weight column wcol(j) given by the column map below.
 struct GemmParams {
   const uint16_t* A;
   const uint16_t* B;
@@ -22,7 +23,13 @@ struct GemmParams {
   int64_t seg_w0[3];      // mode 0: weight column of segment s's first output column
   int64_t gate_w0, up_w0; // mode 1: weight columns of act column 0's gate and up inputs
   int32_t tiles_m, tiles_n;
+  int32_t w_nk;           // weight stored transposed ([n][k])
+  int64_t b_rows;         // w_nk: rows of W^T reachable from B
 };
+
+// Output tile of one workgroup: rows, and output columns for a mode (0 plain, 1 SiLU·up).
+int gemm_tile_rows();
+int gemm_tile_cols(int mode);
 
 hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t stream);
 

@@ -35,6 +35,8 @@ constexpr int64_t kMaxDim = 0x7FFFFFFF;
 // Per-tile buffer offsets are 32-bit: 256 input rows and 65 weight rows of pitch must stay < 2^31 B.
 constexpr int64_t kMaxLda = (int64_t)1 << 21;
 constexpr int64_t kMaxLdb = (int64_t)1 << 23;
+// A [n][k] weight is addressed with 32-bit byte offsets from its base.
+constexpr int64_t kMaxNkBytes = (int64_t)0x7FFFFFF0 - 16;
 
 ttl_status launch_status(hipError_t e, const char* who) {
   if (e != hipSuccess) return fail(TTL_ERR_HIP, "%s: kernel launch failed: %s", who, hipGetErrorString(e));
@@ -50,8 +52,8 @@ const char* ttl_last_error(void) { return g_last_error.c_str(); }
 int32_t ttl_version(void) { return 100; }  // 0.1.0
 
 ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k, const uint16_t* W, int64_t n,
-                            int32_t t, int32_t rank, const ttl_col_split* split, ttl_epilogue epi,
-                            uint16_t* Y, void* stream) {
+                            ttl_weight_layout w_layout, int32_t t, int32_t rank,
+                            const ttl_col_split* split, ttl_epilogue epi, uint16_t* Y, void* stream) {
   static const char* who = "shard_linear_col";
   if (X == nullptr || W == nullptr || Y == nullptr)
     return fail(TTL_ERR_NULL, "%s: X, W and Y must be non-NULL", who);
@@ -62,6 +64,8 @@ ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k, const uint1
     return fail(TTL_ERR_RANK, "%s: need t >= 1 and 0 <= rank < t (t=%d rank=%d)", who, t, rank);
   if (epi != TTL_EPI_NONE && epi != TTL_EPI_SILU_MUL)
     return fail(TTL_ERR_UNSUPPORTED, "%s: unknown epilogue %d", who, epi);
+  if (w_layout != TTL_W_KN && w_layout != TTL_W_NK)
+    return fail(TTL_ERR_UNSUPPORTED, "%s: unknown weight layout %d", who, w_layout);
 
   ttl_col_split sp;
   if (split != nullptr) {
@@ -107,11 +111,15 @@ ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k, const uint1
   if (k > kMaxLda || n > kMaxLdb)
     return fail(TTL_ERR_SHAPE, "%s: k=%lld or n=%lld exceeds the supported row pitch", who,
                 (long long)k, (long long)n);
+  if (w_layout == TTL_W_NK && n * k * 2 >= kMaxNkBytes)
+    return fail(TTL_ERR_UNSUPPORTED, "%s: a [n][k] weight must stay below 2 GiB", who);
 
   p.A = X;
   p.lda = k;
   p.B = W;
-  p.ldb = n;
+  p.w_nk = w_layout == TTL_W_NK;
+  p.ldb = p.w_nk ? k : n;
+  p.b_rows = n;
   p.C = Y;
   p.M = (int32_t)b;
   p.K = (int32_t)k;
@@ -124,7 +132,7 @@ ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k, const uint1
     p.ldc = width[0];
     p.gate_w0 = wcol0[0];
     p.up_w0 = wcol0[1];
-    p.tiles_n = (p.N + 127) / 128;
+    p.tiles_n = (p.N + ttl::gemm_tile_cols(1) - 1) / ttl::gemm_tile_cols(1);
   } else {
     p.mode = 0;
     p.N = (int32_t)n_r;
@@ -137,17 +145,17 @@ ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k, const uint1
       out0 += width[s];
     }
     p.seg_out0[sp.nseg] = (int32_t)out0;
-    p.tiles_n = (p.N + 255) / 256;
+    p.tiles_n = (p.N + ttl::gemm_tile_cols(0) - 1) / ttl::gemm_tile_cols(0);
   }
-  p.tiles_m = (p.M + 255) / 256;
+  p.tiles_m = (p.M + ttl::gemm_tile_rows() - 1) / ttl::gemm_tile_rows();
   if ((int64_t)p.tiles_m * p.tiles_n > kMaxDim)
     return fail(TTL_ERR_SHAPE, "%s: too many tiles", who);
   return launch_status(ttl::launch_gemm_bf16(p, static_cast<hipStream_t>(stream)), who);
 }
 
 ttl_status shard_linear_row(const uint16_t* X, int64_t b, int64_t k, int32_t x_is_parallel,
-                            const uint16_t* W, int64_t n, int32_t t, int32_t rank, uint16_t* P,
-                            void* stream) {
+                            const uint16_t* W, int64_t n, ttl_weight_layout w_layout, int32_t t,
+                            int32_t rank, uint16_t* P, void* stream) {
   static const char* who = "shard_linear_row";
   if (X == nullptr || W == nullptr || P == nullptr)
     return fail(TTL_ERR_NULL, "%s: X, W and P must be non-NULL", who);
@@ -156,6 +164,8 @@ ttl_status shard_linear_row(const uint16_t* X, int64_t b, int64_t k, int32_t x_i
                 (long long)k, (long long)n);
   if (t < 1 || rank < 0 || rank >= t)
     return fail(TTL_ERR_RANK, "%s: need t >= 1 and 0 <= rank < t (t=%d rank=%d)", who, t, rank);
+  if (w_layout != TTL_W_KN && w_layout != TTL_W_NK)
+    return fail(TTL_ERR_UNSUPPORTED, "%s: unknown weight layout %d", who, w_layout);
   if (k % t != 0)
     return fail(TTL_ERR_NOT_DIVISIBLE, "%s: k=%lld is not divisible by t=%d", who, (long long)k, t);
   const int64_t kr = k / t;
@@ -165,14 +175,19 @@ ttl_status shard_linear_row(const uint16_t* X, int64_t b, int64_t k, int32_t x_i
     return fail(TTL_ERR_ALIGN, "%s: k/t=%lld and n=%lld must be multiples of 8", who,
                 (long long)kr, (long long)n);
   const int64_t lda = x_is_parallel ? kr : k;
-  if (lda > kMaxLda || n > kMaxLdb)
+  if (lda > kMaxLda || n > kMaxLdb || k > kMaxLdb)
     return fail(TTL_ERR_SHAPE, "%s: row pitch of X or W exceeds the supported range", who);
+  if (w_layout == TTL_W_NK && n * k * 2 >= kMaxNkBytes)
+    return fail(TTL_ERR_UNSUPPORTED, "%s: a [n][k] weight must stay below 2 GiB", who);
 
   ttl::GemmParams p = {};
   p.A = x_is_parallel ? X : X + (int64_t)rank * kr;
   p.lda = lda;
-  p.B = W + (int64_t)rank * kr * n;
-  p.ldb = n;
+  p.w_nk = w_layout == TTL_W_NK;
+  // W[k][n]: the rank's k rows start at row r*k/t.  W^T[n][k]: they are columns r*k/t.. of each row.
+  p.B = p.w_nk ? W + (int64_t)rank * kr : W + (int64_t)rank * kr * n;
+  p.ldb = p.w_nk ? k : n;
+  p.b_rows = n;
   p.C = P;
   p.ldc = n;
   p.M = (int32_t)b;
@@ -183,8 +198,8 @@ ttl_status shard_linear_row(const uint16_t* X, int64_t b, int64_t k, int32_t x_i
   p.seg_out0[0] = 0;
   p.seg_out0[1] = (int32_t)n;
   p.seg_w0[0] = 0;
-  p.tiles_m = (p.M + 255) / 256;
-  p.tiles_n = (p.N + 255) / 256;
+  p.tiles_m = (p.M + ttl::gemm_tile_rows() - 1) / ttl::gemm_tile_rows();
+  p.tiles_n = (p.N + ttl::gemm_tile_cols(0) - 1) / ttl::gemm_tile_cols(0);
   if ((int64_t)p.tiles_m * p.tiles_n > kMaxDim)
     return fail(TTL_ERR_SHAPE, "%s: too many tiles", who);
   return launch_status(ttl::launch_gemm_bf16(p, static_cast<hipStream_t>(stream)), who);

@@ -27,6 +27,8 @@ OK = 0
 ERR_NULL, ERR_SHAPE, ERR_NOT_DIVISIBLE, ERR_RANK, ERR_ALIGN, ERR_UNSUPPORTED, ERR_HIP = range(1, 8)
 EPI_NONE = 0
 EPI_SILU_MUL = 1
+W_KN = 0  # weight stored [k][n] (row stride n)
+W_NK = 1  # weight stored transposed, [n][k] (row stride k), as PyTorch-style Linear weights are
 MAX_SEGMENTS = 3
 EXPORTED = ("shard_linear_col", "shard_linear_row", "reduce_partials_rmsnorm", "ttl_last_error",
             "ttl_version")
@@ -41,12 +43,12 @@ class ColSplit(ctypes.Structure):
 _c_u16p = ctypes.c_void_p
 _lib.shard_linear_col.restype = ctypes.c_int32
 _lib.shard_linear_col.argtypes = [_c_u16p, ctypes.c_int64, ctypes.c_int64, _c_u16p, ctypes.c_int64,
-                                  ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ColSplit),
-                                  ctypes.c_int32, _c_u16p, ctypes.c_void_p]
+                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.POINTER(ColSplit), ctypes.c_int32, _c_u16p, ctypes.c_void_p]
 _lib.shard_linear_row.restype = ctypes.c_int32
 _lib.shard_linear_row.argtypes = [_c_u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, _c_u16p,
-                                  ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _c_u16p,
-                                  ctypes.c_void_p]
+                                  ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                  _c_u16p, ctypes.c_void_p]
 _lib.reduce_partials_rmsnorm.restype = ctypes.c_int32
 _lib.reduce_partials_rmsnorm.argtypes = [_c_u16p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                          _c_u16p, _c_u16p, ctypes.c_float, _c_u16p, _c_u16p,
@@ -129,19 +131,32 @@ def _stream_handle(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
+def _weight_dims(W: torch.Tensor, w_layout: int):
+    """(k, n) of the logical W[k, n] given its storage."""
+    if w_layout == W_NK:
+        n, k = W.shape
+    else:
+        k, n = W.shape
+    return k, n
+
+
 def shard_linear_col(X: torch.Tensor, W: torch.Tensor, t: int, rank: int,
                      split: Optional[ColSplit] = None, epi: int = EPI_NONE,
-                     Y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Column-parallel output of `rank`: X[b,k] · W[:, C_rank] (optionally SiLU(gate)·up)."""
+                     Y: Optional[torch.Tensor] = None, stream=None,
+                     w_layout: int = W_KN) -> torch.Tensor:
+    """Column-parallel output of `rank`: X[b,k] · W[:, C_rank] (optionally SiLU(gate)·up).
+
+    W is the logical [k, n] weight stored as `w_layout` says: a [k, n] tensor (W_KN) or its
+    transpose as an [n, k] tensor (W_NK)."""
     b, k = X.shape
-    n = W.shape[1]
-    if W.shape[0] != k:
-        raise ValueError(f"X is [{b},{k}] but W is {tuple(W.shape)}")
+    kw, n = _weight_dims(W, w_layout)
+    if kw != k:
+        raise ValueError(f"X is [{b},{k}] but W is {tuple(W.shape)} (layout {w_layout})")
     width = split_width(split, n, t) if t >= 1 else 0
     ncols = width // 2 if epi == EPI_SILU_MUL else width
     if Y is None:
         Y = torch.empty((b, max(ncols, 0)), dtype=torch.bfloat16, device=X.device)
-    _check(_lib.shard_linear_col(_dev_ptr(X, "X"), b, k, _dev_ptr(W, "W"), n, t, rank,
+    _check(_lib.shard_linear_col(_dev_ptr(X, "X"), b, k, _dev_ptr(W, "W"), n, w_layout, t, rank,
                                  ctypes.byref(split) if split is not None else None, epi,
                                  _dev_ptr(Y, "Y"), _stream_handle(stream)))
     return Y
@@ -149,14 +164,14 @@ def shard_linear_col(X: torch.Tensor, W: torch.Tensor, t: int, rank: int,
 
 def shard_linear_row(X: torch.Tensor, W: torch.Tensor, t: int, rank: int,
                      x_is_parallel: bool = True, P: Optional[torch.Tensor] = None,
-                     stream=None) -> torch.Tensor:
-    """Row-parallel partial of `rank`: X_rank · W[rank*k/t:(rank+1)*k/t, :]."""
-    k, n = W.shape
+                     stream=None, w_layout: int = W_KN) -> torch.Tensor:
+    """Row-parallel partial of `rank`: X_rank · W[rank*k/t:(rank+1)*k/t, :] (W stored per w_layout)."""
+    k, n = _weight_dims(W, w_layout)
     b = X.shape[0]
     if P is None:
         P = torch.empty((b, n), dtype=torch.bfloat16, device=X.device)
     _check(_lib.shard_linear_row(_dev_ptr(X, "X"), b, k, 1 if x_is_parallel else 0,
-                                 _dev_ptr(W, "W"), n, t, rank, _dev_ptr(P, "P"),
+                                 _dev_ptr(W, "W"), n, w_layout, t, rank, _dev_ptr(P, "P"),
                                  _stream_handle(stream)))
     return P
 

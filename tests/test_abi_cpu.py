@@ -49,17 +49,18 @@ def test_status_codes_match_header():
     assert codes["TTL_ERR_UNSUPPORTED"] == ttl.ERR_UNSUPPORTED
     assert codes["TTL_ERR_HIP"] == ttl.ERR_HIP
     assert codes["TTL_EPI_SILU_MUL"] == ttl.EPI_SILU_MUL
+    assert codes["TTL_W_KN"] == ttl.W_KN and codes["TTL_W_NK"] == ttl.W_NK
     assert codes["TTL_MAX_SEGMENTS"] == ttl.MAX_SEGMENTS
     assert ttl.version() >= 100
 
 
-def _col(X=A, b=16, k=256, W=B, n=1376, t=2, rank=0, split=None, epi=0, Y=C):
+def _col(X=A, b=16, k=256, W=B, n=1376, t=2, rank=0, split=None, epi=0, Y=C, lay=0):
     sp = None if split is None else ttl.ctypes.byref(split)
-    return ttl.lib().shard_linear_col(X, b, k, W, n, t, rank, sp, epi, Y, None)
+    return ttl.lib().shard_linear_col(X, b, k, W, n, lay, t, rank, sp, epi, Y, None)
 
 
-def _row(X=A, b=16, k=688, par=1, W=B, n=256, t=2, rank=0, P=C):
-    return ttl.lib().shard_linear_row(X, b, k, par, W, n, t, rank, P, None)
+def _row(X=A, b=16, k=688, par=1, W=B, n=256, t=2, rank=0, P=C, lay=0):
+    return ttl.lib().shard_linear_row(X, b, k, par, W, n, lay, t, rank, P, None)
 
 
 def _red(P=A, t=2, b=16, n=256, R=B, gamma=D, eps=1e-5, Rout=B, Y=C):
@@ -84,6 +85,9 @@ def _red(P=A, t=2, b=16, n=256, R=B, gamma=D, eps=1e-5, Rout=B, Y=C):
     (lambda: _col(epi=1), ttl.ERR_UNSUPPORTED, "two equal segments"),
     (lambda: _col(epi=1, split=ttl.make_split((704, 672), (2, 2))), ttl.ERR_UNSUPPORTED, "two equal"),
     (lambda: _col(epi=7), ttl.ERR_UNSUPPORTED, "epilogue"),
+    (lambda: _col(lay=2), ttl.ERR_UNSUPPORTED, "weight layout"),
+    (lambda: _col(k=16384, n=65536, lay=1), ttl.ERR_UNSUPPORTED, "2 GiB"),
+    (lambda: _row(lay=-1), ttl.ERR_UNSUPPORTED, "weight layout"),
     (lambda: _row(P=None), ttl.ERR_NULL, "non-NULL"),
     (lambda: _row(n=0), ttl.ERR_SHAPE, ""),
     (lambda: _row(rank=5), ttl.ERR_RANK, ""),

@@ -36,14 +36,15 @@ def _host(d, rows=None):
     return out
 
 
-def _mlp_device_chain(ttl, X, R, gamma, Wgu, Wd, w, b):
+def _mlp_device_chain(ttl, X, R, gamma, Wgu, Wd, w, b, lay=0):
+    """Wgu and Wd are stored as `lay` says (transposed copies for the [n][k] layout)."""
     t, H, I = w.t, w.hidden, w.intermediate
     sp = ttl.merged_gate_up_split(I, t)
     P = torch.empty((t, b, H), dtype=torch.bfloat16, device="cuda")
     acts = []
     for r in range(t):
-        act = ttl.shard_linear_col(X, Wgu, t, r, sp, ttl.EPI_SILU_MUL)
-        ttl.shard_linear_row(act, Wd, t, r, True, P=P[r])
+        act = ttl.shard_linear_col(X, Wgu, t, r, sp, ttl.EPI_SILU_MUL, w_layout=lay)
+        ttl.shard_linear_row(act, Wd, t, r, True, P=P[r], w_layout=lay)
         acts.append(act)
     rout, y = ttl.reduce_partials_rmsnorm(P, gamma, w.eps, R)
     return acts, P, rout, y
@@ -60,9 +61,14 @@ def _mlp_oracle_rows(o, X_rows, R_rows, w):
                                  (wl.LLAMA3_8B_MLP_TP8, 256), (wl.LLAMA3_70B_MLP_TP8, 64),
                                  (wl.LLAMA3_70B_MLP_TP8, 4096)],
                          ids=lambda v: v.name if hasattr(v, "name") else f"b{v}")
-def test_mlp_shard_full_size(ttl, w, b):
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+def test_mlp_shard_full_size(ttl, w, b, layout):
     d = wl.mlp_inputs(w, b, seed=0, device="cuda")
-    acts, P, rout, y = _mlp_device_chain(ttl, d["X"], d["R"], d["gamma"], d["Wgu"], d["Wd"], w, b)
+    lay = ttl.W_KN if layout == "kn" else ttl.W_NK
+    Wgu_s = d["Wgu"] if layout == "kn" else d["Wgu"].t().contiguous()
+    Wd_s = d["Wd"] if layout == "kn" else d["Wd"].t().contiguous()
+    acts, P, rout, y = _mlp_device_chain(ttl, d["X"], d["R"], d["gamma"], Wgu_s, Wd_s, w, b, lay)
+    del Wgu_s, Wd_s
     rows = sample_rows(b)
     print(f"{w.name} b={b}: checking rows {rows}", flush=True)
     o = _host({k: d[k] for k in ("Wgu", "Wd", "gamma")})
@@ -112,22 +118,29 @@ def test_attn_projections_8b_tp4(ttl):
     assert_close(from_gpu(qcat), Xs @ o["Wqkv"][:, :w.n_q_heads * w.head_dim], "q concat over ranks")
 
 
-def test_decoder_layer_70b_tp8(ttl):
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+def test_decoder_layer_70b_tp8(ttl, layout):
     """Full linear path of one Llama-3-70B-shaped layer on one TP=8 rank's shapes, all ranks."""
     w = wl.LLAMA3_70B_LAYER_TP8
     b = w.batches[0]
     d = wl.layer_inputs(w, b, seed=0, device="cuda")
     t, H, I = w.t, w.hidden, w.intermediate
+    lay = ttl.W_KN if layout == "kn" else ttl.W_NK
+    st = (lambda v: v) if layout == "kn" else (lambda v: v.t().contiguous())
     sp_c = ttl.qkv_split(w.n_q_heads, w.n_kv_heads, w.head_dim, t)
     sp_o = oracle.qkv_split(w.n_q_heads, w.n_kv_heads, w.head_dim, t)
     kr = w.n_q_heads * w.head_dim // t
-    qkv = [ttl.shard_linear_col(d["X"], d["Wqkv"], t, r, sp_c) for r in range(t)]
+    Wqkv_s = st(d["Wqkv"])
+    qkv = [ttl.shard_linear_col(d["X"], Wqkv_s, t, r, sp_c, w_layout=lay) for r in range(t)]
+    del Wqkv_s
     assert qkv[0].shape == (b, 1280)  # 8 q + 1 kv heads of 128 per rank
     P = torch.empty((t, b, H), dtype=torch.bfloat16, device="cuda")
+    Wo_s = st(d["Wo"])
     for r in range(t):
-        ttl.shard_linear_row(d["A"], d["Wo"], t, r, False, P=P[r])  # full input, sliced in place
+        ttl.shard_linear_row(d["A"], Wo_s, t, r, False, P=P[r], w_layout=lay)  # full input, sliced in place
+    del Wo_s
     r1, y1 = ttl.reduce_partials_rmsnorm(P, d["gamma_attn"], w.eps, d["R"])
-    acts, P2, r2, y2 = _mlp_device_chain(ttl, y1, r1, d["gamma_mlp"], d["Wgu"], d["Wd"], w, b)
+    acts, P2, r2, y2 = _mlp_device_chain(ttl, y1, r1, d["gamma_mlp"], st(d["Wgu"]), st(d["Wd"]), w, b, lay)
     rows = sample_rows(b, extra=(2047, 2048, 2175))
     print(f"layer b={b}: checking rows {rows}", flush=True)
     o = _host({k: d[k] for k in ("Wqkv", "Wo", "gamma_attn", "gamma_mlp", "Wgu", "Wd")})

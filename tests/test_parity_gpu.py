@@ -25,18 +25,27 @@ def ttl():
     return lib
 
 
-def _col_case(ttl, b, k, split_np, split_c, t, seed, epi=0):
+LAYOUTS = pytest.mark.parametrize("layout", ["kn", "nk"])
+
+
+def _stored(ttl, W, layout):
+    """Device copy of the logical W[k, n] in the requested storage layout."""
+    return (gpu(W), ttl.W_KN) if layout == "kn" else (gpu(W.t().contiguous()), ttl.W_NK)
+
+
+def _col_case(ttl, b, k, split_np, split_c, t, seed, epi=0, layout="kn"):
     n = sum(split_np[0])
     X = wl.random_bf16((b, k), seed)
     W = wl.random_bf16((k, n), seed + 1, std=0.05)
-    Xd, Wd = gpu(X), gpu(W)
+    Xd = gpu(X)
+    Wd, lay = _stored(ttl, W, layout)
     Xo, Wo = f64(X), f64(W)
     for r in range(t):
-        Y = ttl.shard_linear_col(Xd, Wd, t, r, split_c, epi)
+        Y = ttl.shard_linear_col(Xd, Wd, t, r, split_c, epi, w_layout=lay)
         ref = oracle.col_shard(Xo, Wo, split_np, t, r)
         if epi == ttl.EPI_SILU_MUL:
             ref = oracle.silu_mul(ref)
-        assert_close(from_gpu(Y), ref, f"col b={b} k={k} n={n} t={t} r={r} epi={epi}")
+        assert_close(from_gpu(Y), ref, f"col b={b} k={k} n={n} t={t} r={r} epi={epi} {layout}")
 
 
 @pytest.mark.parametrize("b,k,I,t", [
@@ -46,14 +55,16 @@ def _col_case(ttl, b, k, split_np, split_c, t, seed, epi=0):
     (257, 512, 1024, 4),    # one row past a 256 tile
     (513, 1024, 2048, 8),   # several tiles in every dimension
 ])
-def test_col_silu_mul(ttl, b, k, I, t):
+@LAYOUTS
+def test_col_silu_mul(ttl, b, k, I, t, layout):
     _col_case(ttl, b, k, oracle.merged_gate_up_split(I, t), ttl.merged_gate_up_split(I, t), t,
-              seed=10 + b, epi=ttl.EPI_SILU_MUL)
+              seed=10 + b, epi=ttl.EPI_SILU_MUL, layout=layout)
 
 
 @pytest.mark.parametrize("b,k,n,t", [(16, 256, 1376, 2), (300, 136, 520, 1), (260, 512, 2048, 4)])
-def test_col_plain(ttl, b, k, n, t):
-    _col_case(ttl, b, k, oracle.plain_split(n, t), None, t, seed=20 + b)
+@LAYOUTS
+def test_col_plain(ttl, b, k, n, t, layout):
+    _col_case(ttl, b, k, oracle.plain_split(n, t), None, t, seed=20 + b, layout=layout)
 
 
 @pytest.mark.parametrize("b,k,nq,nkv,hd,t", [
@@ -62,24 +73,28 @@ def test_col_plain(ttl, b, k, n, t):
     (33, 128, 8, 2, 32, 4),    # t > n_kv: one kv head per rank, replicated twice
     (300, 512, 32, 8, 128, 4), # the 8B attention head layout at a small batch
 ])
-def test_col_qkv(ttl, b, k, nq, nkv, hd, t):
-    _col_case(ttl, b, k, oracle.qkv_split(nq, nkv, hd, t), ttl.qkv_split(nq, nkv, hd, t), t, seed=30 + b)
+@LAYOUTS
+def test_col_qkv(ttl, b, k, nq, nkv, hd, t, layout):
+    _col_case(ttl, b, k, oracle.qkv_split(nq, nkv, hd, t), ttl.qkv_split(nq, nkv, hd, t), t, seed=30 + b,
+              layout=layout)
 
 
 @pytest.mark.parametrize("b,k,n,t", [(16, 688, 256, 2), (300, 344, 520, 1), (257, 1024, 768, 4),
                                      (5, 2048, 264, 8)])
 @pytest.mark.parametrize("x_is_parallel", [True, False])
-def test_row(ttl, b, k, n, t, x_is_parallel):
+@LAYOUTS
+def test_row(ttl, b, k, n, t, x_is_parallel, layout):
     w = k // t
     X = wl.random_bf16((b, k), 40 + b)
     W = wl.random_bf16((k, n), 41 + b, std=0.05)
-    Xd, Wd = gpu(X), gpu(W)
+    Xd = gpu(X)
+    Wd, lay = _stored(ttl, W, layout)
     Xo, Wo = f64(X), f64(W)
     for r in range(t):
         xin = Xd[:, r * w:(r + 1) * w].contiguous() if x_is_parallel else Xd
-        P = ttl.shard_linear_row(xin, Wd, t, r, x_is_parallel)
+        P = ttl.shard_linear_row(xin, Wd, t, r, x_is_parallel, w_layout=lay)
         ref = oracle.row_shard(Xo, Wo, t, r, x_is_parallel=False)
-        assert_close(from_gpu(P), ref, f"row b={b} k={k} n={n} t={t} r={r} par={x_is_parallel}")
+        assert_close(from_gpu(P), ref, f"row b={b} k={k} n={n} t={t} r={r} par={x_is_parallel} {layout}")
 
 
 @pytest.mark.parametrize("t,b,n,with_residual", [(2, 16, 256, True), (8, 5, 4096, True),
@@ -109,12 +124,13 @@ def test_reduce_residual_in_place(ttl):
     assert_close(from_gpu(y), yref, "in-place y")
 
 
-def test_identity_and_one_hot_are_exact(ttl):
+@LAYOUTS
+def test_identity_and_one_hot_are_exact(ttl, layout):
     # W = identity: every column of the output is one column of X, exactly.
     b, k, t = 40, 256, 2
     X = wl.random_bf16((b, k), 70)
-    W = torch.eye(k, dtype=torch.bfloat16)
-    Y0 = ttl.shard_linear_col(gpu(X), gpu(W), t, 1)
+    W, lay = _stored(ttl, torch.eye(k, dtype=torch.bfloat16), layout)
+    Y0 = ttl.shard_linear_col(gpu(X), W, t, 1, w_layout=lay)
     assert torch.equal(Y0.cpu(), X[:, k // t:])
     # one-hot rows of X: each output row is a row of W, exactly (row split: of the rank's rows).
     n = 264
@@ -122,8 +138,21 @@ def test_identity_and_one_hot_are_exact(ttl):
     Xo = torch.zeros((b, k), dtype=torch.bfloat16)
     idx = torch.arange(b) * 7 % k
     Xo[torch.arange(b), idx] = 1.0
-    P = ttl.shard_linear_row(gpu(Xo), gpu(Wr), 1, 0, x_is_parallel=True)
+    Wrd, lay = _stored(ttl, Wr, layout)
+    P = ttl.shard_linear_row(gpu(Xo), Wrd, 1, 0, x_is_parallel=True, w_layout=lay)
     assert torch.equal(P.cpu(), Wr[idx])
+
+
+def test_layouts_agree_bitwise(ttl):
+    """Both weight storages feed the matrix cores the same products in the same k order."""
+    b, k, I, t = 300, 512, 1024, 4
+    X = gpu(wl.random_bf16((b, k), 90))
+    W = wl.random_bf16((k, 2 * I), 91, std=0.05)
+    sp = ttl.merged_gate_up_split(I, t)
+    a = ttl.shard_linear_col(X, gpu(W), t, 2, sp, ttl.EPI_SILU_MUL, w_layout=ttl.W_KN)
+    c = ttl.shard_linear_col(X, gpu(W.t().contiguous()), t, 2, sp, ttl.EPI_SILU_MUL, w_layout=ttl.W_NK)
+    torch.cuda.synchronize()
+    assert torch.equal(a, c)
 
 
 def test_bitwise_deterministic(ttl):
