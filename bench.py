@@ -7,7 +7,13 @@ intermediate 28672, 3584 per rank), over one batch of tokens:
   2. shard_linear_row   down_proj row GEMM -> rank 0's partial [b, 8192] inside P[8, b, 8192]
   3. reduce_partials_rmsnorm   sum of the 8 partials + residual, RMSNorm -> residual_out, y
 The other seven ranks' partials are computed once before timing (their work is identical in
-shape to rank 0's and would run on the other GPUs).
+shape to rank 0's and would run on the other GPUs).  The weight is the logical W[k, n] of the
+statement Y = X·W, stored as W[k][n] (--layout kn, the default) or transposed as W^T[n][k]
+(--layout nk, the storage of PyTorch-style Linear weights).
+
+The secondary 64-token decode line cycles the simulated rank from step to step, so that successive
+steps read different weight slices (1.4 GB in all) and the timing is not served from the 256-MB
+Infinity Cache.
 
 Inputs are synthetic and seeded (X, R ~ N(0,1); W ~ N(0,0.02); gamma ~ N(1,0.1); bf16), drawn on the
 device and resident in HBM before the timed region.  The JSON line reports whole-step throughput as
@@ -19,8 +25,10 @@ bounded sample of the same work.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -30,6 +38,12 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (8 TB/s)
+
+
+# Kernel sources whose HBM traffic counters are recorded under profiles/: the recorded figures
+# apply only while these files are unchanged.
+TRAFFIC_SOURCES = ("tensor_transformer_linear_amd/csrc/gemm_bf16.hip",
+                   "tensor_transformer_linear_amd/csrc/kernels.h")
 
 
 def gemm_flops(b, k, n):
@@ -58,18 +72,27 @@ def parse():
     ap.add_argument("--batch", type=int, default=4096, help="tokens per step (4096 prefill; 64 decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the secondary 64-token decode line")
+    ap.add_argument("--layout", choices=("kn", "nk"), default="kn",
+                    help="weight storage: kn = W[k][n], nk = W^T[n][k]")
     ap.add_argument("--cpu-rows", type=int, default=32, help="token rows in the CPU oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the CPU oracle sample until this much time has passed")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (5 times) and exit: the "
                          "reference for scaling HBM traffic counters")
     return ap.parse_args()
 
 
-def run_mlp(ttl, torch, w, b, steps, warmup, seed):
+def run_mlp(ttl, torch, w, b, steps, warmup, seed, layout, rotate_ranks=False):
     from tensor_transformer_linear_amd import workloads as wl
     dev = "cuda"
     inp = wl.mlp_inputs(w, b, seed=seed, device=dev)
     X, R, gamma, Wgu, Wd = inp["X"], inp["R"], inp["gamma"], inp["Wgu"], inp["Wd"]
+    lay = ttl.W_NK if layout == "nk" else ttl.W_KN
+    if lay == ttl.W_NK:  # the same logical weights, stored transposed (set-up, not timed)
+        Wgu_s, Wd_s = Wgu.t().contiguous(), Wd.t().contiguous()
+    else:
+        Wgu_s, Wd_s = Wgu, Wd
     t, H, I = w.t, w.hidden, w.intermediate
     Ir = I // t
     sp = ttl.merged_gate_up_split(I, t)
@@ -80,39 +103,40 @@ def run_mlp(ttl, torch, w, b, steps, warmup, seed):
     stream = torch.cuda.current_stream()
     # every simulated rank's partial, once
     for r in range(t):
-        ttl.shard_linear_col(X, Wgu, t, r, sp, ttl.EPI_SILU_MUL, Y=act, stream=stream)
-        ttl.shard_linear_row(act, Wd, t, r, True, P=P[r], stream=stream)
+        ttl.shard_linear_col(X, Wgu_s, t, r, sp, ttl.EPI_SILU_MUL, Y=act, stream=stream, w_layout=lay)
+        ttl.shard_linear_row(act, Wd_s, t, r, True, P=P[r], stream=stream, w_layout=lay)
     torch.cuda.synchronize()
 
-    def step(ev=None):
+    def step(i, ev=None):
+        r = i % t if rotate_ranks else 0
         if ev is not None:
             ev[0].record(stream)
-        ttl.shard_linear_col(X, Wgu, t, 0, sp, ttl.EPI_SILU_MUL, Y=act, stream=stream)
+        ttl.shard_linear_col(X, Wgu_s, t, r, sp, ttl.EPI_SILU_MUL, Y=act, stream=stream, w_layout=lay)
         if ev is not None:
             ev[1].record(stream)
-        ttl.shard_linear_row(act, Wd, t, 0, True, P=P[0], stream=stream)
+        ttl.shard_linear_row(act, Wd_s, t, r, True, P=P[r], stream=stream, w_layout=lay)
         if ev is not None:
             ev[2].record(stream)
         ttl.reduce_partials_rmsnorm(P, gamma, w.eps, R, residual_out=rout, Y=y, stream=stream)
         if ev is not None:
             ev[3].record(stream)
 
-    for _ in range(warmup):
-        step()
+    for i in range(warmup):
+        step(i)
     torch.cuda.synchronize()
     # whole-step timing: nothing but the launches between the two events
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
-    for _ in range(steps):
-        step()
+    for i in range(steps):
+        step(i)
     t1.record(stream)
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / steps
-    # per-kernel timing: events between the launches, over the same number of steps
+    # per-kernel timing: events recorded on the kernels' stream between the launches, same steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for i in range(steps):
-        step(evs[i])
+        step(i, evs[i])
     torch.cuda.synchronize()
     k_ms = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j in range(3)]
 
@@ -136,8 +160,33 @@ def run_mlp(ttl, torch, w, b, steps, warmup, seed):
             "tensors": (X, Wgu, Wd, R, gamma)}
 
 
-def cpu_baseline(torch, w, tensors, rows):
-    """The oracle as it stands, on rank 0's work for `rows` token rows (rows are independent)."""
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch recorded from the FETCH_SIZE / WRITE_SIZE counters in profiles/, or None
+    when no record exists or the kernel sources changed since the counters were taken."""
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    digest = h.hexdigest()
+    pat = re.compile(r"^traffic\s+kernel=(\S+)\s+workload=(\S+)\s+bytes_per_launch=(\d+)\s+"
+                     r"source_sha256=([0-9a-f]{64})\s*$")
+    pdir = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(pdir):
+        return None
+    for name in sorted(os.listdir(pdir)):
+        if not name.endswith((".md", ".txt")):
+            continue
+        with open(os.path.join(pdir, name)) as f:
+            for line in f:
+                m = pat.match(line.strip())
+                if m and m.group(1) == kernel and m.group(2) == workload and m.group(4) == digest:
+                    return float(m.group(3))
+    return None
+
+
+def cpu_baseline(torch, w, tensors, rows, seconds):
+    """The oracle as it stands, on rank 0's work for `rows` token rows (rows are independent),
+    repeated until `seconds` have passed."""
     import numpy as np
     import oracle
     from tensor_transformer_linear_amd import workloads as wl
@@ -157,17 +206,22 @@ def cpu_baseline(torch, w, tensors, rows):
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
     split = oracle.merged_gate_up_split(I, t)
+    passes = 0
     t0 = time.perf_counter()
-    act = oracle.round_bf16(oracle.silu_mul(oracle.col_shard(Xs, Wgu64, split, t, 0)))
-    p0 = oracle.round_bf16(oracle.row_shard(act, Wd64, t, 0, x_is_parallel=True))
-    h, y = oracle.reduce_partials_rmsnorm(np.concatenate([p0[None], other]), Rs, gs, w.eps)
-    dt = time.perf_counter() - t0
-    flops = gemm_flops(rows, H, 2 * Ir) + gemm_flops(rows, Ir, H)
+    while True:
+        act = oracle.round_bf16(oracle.silu_mul(oracle.col_shard(Xs, Wgu64, split, t, 0)))
+        p0 = oracle.round_bf16(oracle.row_shard(act, Wd64, t, 0, x_is_parallel=True))
+        h, y = oracle.reduce_partials_rmsnorm(np.concatenate([p0[None], other]), Rs, gs, w.eps)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    flops = passes * (gemm_flops(rows, H, 2 * Ir) + gemm_flops(rows, Ir, H))
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "seconds": dt,
-            "sample": f"rank 0 of t={t}: gate_up+SiLU*up, down partial and reduce+RMSNorm for {rows} of "
-                      f"the token rows (float64 numpy oracle; rows are independent, so throughput "
-                      f"scales to the full batch)"}
+            "sample": f"{passes} passes of rank 0 of t={t} (gate_up+SiLU*up, down partial, reduce of 8 "
+                      f"partials + residual + RMSNorm) over {rows} of the {tensors[0].shape[0]} token rows; "
+                      f"float64 numpy oracle; rows are independent, so the rate applies to the full batch"}
 
 
 def main():
@@ -193,18 +247,23 @@ def main():
     from tensor_transformer_linear_amd import workloads as wl
     w = wl.LLAMA3_70B_MLP_TP8
     b = args.batch
-    res = run_mlp(ttl, torch, w, b, args.steps, args.warmup, seed=0)
+    workload = f"llama3_70b_mlp_tp8_rank0_b{b}_{args.layout}"
+    res = run_mlp(ttl, torch, w, b, args.steps, args.warmup, seed=0, layout=args.layout,
+                  rotate_ranks=(b < 512))
     ms = res["ms_per_step"]
     value = res["flops"] / (ms * 1e9)
     kcol = res["kernels"]["shard_linear_col_silu_mul"]
-    dominant_bound = "mfma" if b >= 512 else "hbm"
-    if dominant_bound == "mfma":
+    traffic = recorded_traffic("shard_linear_col_silu_mul", workload)
+    if b >= 512:
         roof = {"kernel": "shard_linear_col_silu_mul", "bound": "mfma", "achieved": kcol["tflops"],
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": kcol["tflops"] / PEAK_BF16_TFLOPS,
-                "traffic": None}
+                "traffic": traffic}
     else:
         roof = {"kernel": "shard_linear_col_silu_mul", "bound": "hbm", "achieved": kcol["gbs"],
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": kcol["gbs"] / PEAK_HBM_GBS, "traffic": None}
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": kcol["gbs"] / PEAK_HBM_GBS,
+                "traffic": traffic}
+    roof["algorithmic_gflop_per_launch"] = kcol["gflop"]
+    roof["algorithmic_mbytes_per_launch"] = kcol["mbytes"]
     out = {
         "metric": "TFLOP/s and % bf16 MFMA peak, 1-rank shard of Llama-3-70B MLP at TP=8 shape",
         "value": value,
@@ -219,20 +278,21 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"llama3_70b_mlp_tp8_rank0_b{b}", "hidden": w.hidden,
-                   "intermediate": w.intermediate, "t": w.t, "tokens": b,
+        "config": {"workload": workload, "hidden": w.hidden,
+                   "intermediate": w.intermediate, "t": w.t, "tokens": b, "weight_storage": args.layout,
                    "step": "gate_up+SiLU*up (col) -> down (row partial) -> reduce 8 partials + residual + RMSNorm"},
         "roofline": roof,
         "kernels": res["kernels"],
     }
     if not args.no_decode and b != 64:
-        dec = run_mlp(ttl, torch, w, 64, args.steps, args.warmup, seed=1)
-        out["decode64"] = {"ms_per_step": dec["ms_per_step"],
+        dec = run_mlp(ttl, torch, w, 64, args.steps, args.warmup, seed=1, layout=args.layout,
+                      rotate_ranks=True)
+        out["decode64"] = {"ms_per_step": dec["ms_per_step"], "ranks": "cycled 0..7 step by step",
                            "tflops": dec["flops"] / (dec["ms_per_step"] * 1e9),
                            "kernels": dec["kernels"]}
         del dec
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(torch, w, res["tensors"], args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(torch, w, res["tensors"], args.cpu_rows, args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
