@@ -34,7 +34,7 @@
 //
 // Tails in M, N and K: copies whose offsets are pushed past the buffer's record count read zeros, so
 // the k-tail contributes exact zeros and the steady-state loop has no bounds logic; stores are masked.
-#include "kernels.h"
+#include "gemm_common.h"
 
 #ifndef TTL_GEMM_BK
 #define TTL_GEMM_BK 64
@@ -46,16 +46,7 @@
 namespace ttl {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+using namespace gemm;
 
 constexpr int kBM = 256;                   // output rows per tile
 constexpr int kBN = 256;                   // weight columns per tile
@@ -73,8 +64,6 @@ constexpr int kBCopies = kBElems * 2 / 1024 / kWaves;
 constexpr int kLoads = kACopies + kBCopies;             // vmcnt increments per wave per tile
 constexpr int kXcds = 8;                   // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr int kGroupM = 4;                 // row-tiles per L2 group
-constexpr uint32_t kOob = 0x80000000u;     // beyond every record count used below
-constexpr int32_t kMaxRecords = 0x7FFFFFF0;
 
 constexpr int kChunks = kBK / 8;           // 16-B chunks per [rows][k] staged row
 constexpr int kRowsPer256 = 256 / (2 * kBK);  // staged rows per 256 B of LDS
@@ -84,54 +73,6 @@ constexpr int kKK = kBK / 16;              // k16 slices per stage
 static_assert(kBK == 32 || kBK == 64, "stage depth");
 static_assert(kStages >= 2 && kStages <= 5 && kStages * kStageElems * 2 <= 160 * 1024, "LDS ring");
 static_assert(kBCopies % 2 == 0, "[k][n] copies come in k-row-parity pairs");
-
-enum { kPlain = 0, kSiluMul = 1 };
-
-__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-  const f32x2_t f = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));  // round to nearest even
-}
-
-__device__ inline float silu_mul(float g, float u) {
-  // silu(g) * u with silu(g) = g / (1 + exp(-g)); exp overflow gives rcp(inf) = 0, i.e. silu -> -0.
-  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
-}
-
-// Raw buffer descriptor (gfx9): 48-bit base, stride 0, record count in bytes, dword3 = 0x00020000
-// (32-bit data format, the raw untyped setting).  Accesses at offsets >= the record count read 0.
-__device__ inline i32x4_t buffer_desc(const void* base, int64_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const int32_t rec = bytes <= 0 ? 0 : (bytes > kMaxRecords ? kMaxRecords : (int32_t)bytes);
-  i32x4_t d;
-  d.x = (int32_t)(uint32_t)a;
-  d.y = (int32_t)((uint32_t)(a >> 32) & 0xFFFFu);
-  d.z = rec;
-  d.w = 0x00020000;
-  return d;
-}
-
-// One 16-byte-per-lane copy from global memory straight into LDS (buffer_load_dwordx4 ... lds):
-// lane i's 16 bytes land at lds_base + 16*i.  Written as asm so that the compiler's wait insertion,
-// which cannot follow the ring's stage ownership across the loop, does not drain the ring; every
-// wait for these copies is explicit (wait_vmcnt).  M0 holds the LDS base; one wait state must
-// separate its write from the copy.
-__device__ inline void copy16_to_lds(i32x4_t desc, uint32_t voffset, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :: "v"(voffset), "s"(desc), "s"(lds_base) : "memory");
-}
-
-// Wait until at most N of this wave's vector-memory operations are outstanding.
-template <int N>
-__device__ inline void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
-
-// Workgroup barrier for the ring.  __syncthreads() carries a release fence, which would make the
-// compiler drain every outstanding copy (vmcnt(0)) before it; the waits this kernel needs are
-// explicit (wait_vmcnt for this wave's copies, lgkmcnt(0) for its LDS reads), and the memory clobber
-// keeps the compiler from moving LDS accesses across the barrier.
-__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Remap the block index so that the tiles one XCD runs form compact groups, then walk tiles in
 // groups of kGroupM row-tiles.  Both maps are bijections on [0, tiles).
@@ -415,7 +356,7 @@ void launch_one(const GemmParams& p, hipStream_t stream) {
 int gemm_tile_rows() { return kBM; }
 int gemm_tile_cols(int mode) { return mode == kSiluMul ? kBN / 2 : kBN; }
 
-hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t stream) {
+hipError_t launch_gemm_tiled(const GemmParams& p, hipStream_t stream) {
   if (p.mode == kSiluMul)
     p.w_nk ? launch_one<kSiluMul, true>(p, stream) : launch_one<kSiluMul, false>(p, stream);
   else

@@ -1,0 +1,120 @@
+// Kernel choice for one GEMM launch, split-K sizing, and the library's split-K workspace.
+//
+// 256 x 256 tiles keep the matrix cores busiest per byte staged, but a launch needs about one tile
+// per CU to fill the chip; decode batches (a few dozen rows) and small shards give far fewer.
+// Those go to the split-K kernel, whose 32..128-row x 128-column tiles are additionally cut along
+// k into as many ranges as keep the grid within one workgroup per CU: a CU streams at its full
+// rate with one workgroup, and a grid that does not divide evenly over the CUs leaves a slow tail.
+//
+// Workspace: split-K launches with more than one split write fp32 partial tiles that a second
+// kernel reduces.  The library keeps one device buffer per GPU for them, allocated (or grown) on
+// first need by the calling thread.  Launches that overlap in time on one GPU (different streams)
+// would share it and must not be issued; a launch that needs to grow it waits for the device first.
+//
+// Environment overrides, read at every launch (for tests and measurements):
+//   TTL_GEMM_KERNEL=tiled|splitk  use that kernel whatever the shape;
+//   TTL_GEMM_SPLITS=<n>           split-K kernel: use n splits (at most one per k-tile).
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "kernels.h"
+
+namespace ttl {
+namespace {
+
+constexpr int kCUs = 256;               // MI355X compute units
+constexpr int kTiledMinTiles = 192;     // 256 x 256 tiles when they occupy >= 3/4 of the CUs
+constexpr int kSkinnyBlocks = kCUs;     // split-K grid: at most one workgroup per CU
+constexpr int kMinKTilesPerSplit = 4;   // keep each split's copy pipeline full
+
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::vector<Workspace> g_ws;
+
+// Device buffer of at least `bytes` for this GPU.
+hipError_t get_workspace(size_t bytes, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
+  Workspace& w = g_ws[dev];
+  if (w.bytes < bytes) {
+    if (w.ptr != nullptr) {
+      // Earlier launches may still read the old buffer.
+      if ((e = hipDeviceSynchronize()) != hipSuccess) return e;
+      if ((e = hipFree(w.ptr)) != hipSuccess) return e;
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    const size_t mib = (size_t)1 << 20;
+    const size_t nb = (bytes + mib - 1) / mib * mib;
+    if ((e = hipMalloc(&w.ptr, nb)) != hipSuccess) return e;
+    w.bytes = nb;
+  }
+  *out = w.ptr;
+  return hipSuccess;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// 0: by shape, 1: 256 x 256 tiles, 2: split-K.
+int forced_kernel() {
+  const char* s = std::getenv("TTL_GEMM_KERNEL");
+  if (s == nullptr) return 0;
+  if (std::strcmp(s, "tiled") == 0) return 1;
+  if (std::strcmp(s, "splitk") == 0) return 2;
+  return 0;
+}
+
+int64_t forced_splits() {
+  const char* s = std::getenv("TTL_GEMM_SPLITS");
+  return s == nullptr ? 0 : std::atoll(s);
+}
+
+}  // namespace
+
+hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
+  const int64_t tiled_m = cdiv(p.M, gemm_tile_rows());
+  const int64_t tiled_n = cdiv(p.N, gemm_tile_cols(p.mode));
+  const int force = forced_kernel();
+  if (force == 1 || (force == 0 && tiled_m * tiled_n >= kTiledMinTiles)) {
+    p.tiles_m = (int32_t)tiled_m;
+    p.tiles_n = (int32_t)tiled_n;
+    return launch_gemm_tiled(p, stream);
+  }
+
+  const int mb = p.M <= 32 ? 1 : (p.M <= 64 ? 2 : 4);
+  const int64_t tiles_m = cdiv(p.M, 32 * mb);
+  const int64_t tiles_n = cdiv(p.N, p.mode == 1 ? kSkinnyCols / 2 : kSkinnyCols);
+  const int64_t tiles = tiles_m * tiles_n;
+  const int64_t nk = cdiv(p.K, kSkinnyK);
+  int64_t splits = kSkinnyBlocks / tiles;
+  const int64_t max_splits = nk / kMinKTilesPerSplit > 1 ? nk / kMinKTilesPerSplit : 1;
+  if (splits > max_splits) splits = max_splits;
+  const int64_t fs = forced_splits();
+  if (fs > 0) splits = fs < nk ? fs : nk;
+  if (splits < 1) splits = 1;
+  const int64_t kt_per = cdiv(nk, splits);
+  splits = cdiv(nk, kt_per);  // every split gets at least one k-tile
+  p.tiles_m = (int32_t)tiles_m;
+  p.tiles_n = (int32_t)tiles_n;
+  p.splits = (int32_t)splits;
+  p.kt_per_split = (int32_t)kt_per;
+  p.ws_ld = tiles_n * kSkinnyCols;
+  p.ws = nullptr;
+  if (splits > 1) {
+    void* base = nullptr;
+    const hipError_t e = get_workspace((size_t)splits * p.M * p.ws_ld * sizeof(float), &base);
+    if (e != hipSuccess) return e;
+    p.ws = static_cast<float*>(base);
+  }
+  return launch_gemm_skinny(p, mb, stream);
+}
+
+}  // namespace ttl

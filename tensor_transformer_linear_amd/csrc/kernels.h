@@ -25,13 +25,28 @@ struct GemmParams {
   int32_t tiles_m, tiles_n;
   int32_t w_nk;           // weight stored transposed ([n][k])
   int64_t b_rows;         // w_nk: rows of W^T reachable from B
+  // Split-K kernel only: fp32 partial sums [splits][M][ws_ld].
+  float* ws;
+  int64_t ws_ld;
+  int32_t splits, kt_per_split;
 };
 
-// Output tile of one workgroup: rows, and output columns for a mode (0 plain, 1 SiLU·up).
+// Picks the kernel for the shape and launches it: the 256 x 256-tile kernel when its tiles fill the
+// chip, otherwise the split-K kernel (short M: decode batches, small shards).  Sets the tiling
+// fields of p.  May allocate the library's split-K workspace on first use.
+hipError_t launch_gemm(GemmParams& p, hipStream_t stream);
+
+// 256 x 256 tiles (tiles_m, tiles_n set by the caller from the two functions below).
 int gemm_tile_rows();
 int gemm_tile_cols(int mode);
+hipError_t launch_gemm_tiled(const GemmParams& p, hipStream_t stream);
 
-hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t stream);
+// Split-K kernel with 32*mb-row tiles (mb = 1, 2 or 4) of 128 weight columns, followed (splits > 1)
+// by the kernel that sums the splits; tiles_m, tiles_n, splits, kt_per_split, ws and ws_ld set by
+// the caller.
+constexpr int kSkinnyCols = 128;  // weight columns per tile (64 act columns in SiLU·up mode)
+constexpr int kSkinnyK = 64;      // k per pipeline stage
+hipError_t launch_gemm_skinny(const GemmParams& p, int mb, hipStream_t stream);
 
 struct ReduceNormParams {
   const uint16_t* P;

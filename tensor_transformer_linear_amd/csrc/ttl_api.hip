@@ -35,6 +35,8 @@ constexpr int64_t kMaxDim = 0x7FFFFFFF;
 // Per-tile buffer offsets are 32-bit: 256 input rows and 65 weight rows of pitch must stay < 2^31 B.
 constexpr int64_t kMaxLda = (int64_t)1 << 21;
 constexpr int64_t kMaxLdb = (int64_t)1 << 23;
+// Output elements of one GEMM (keeps every tile and workgroup count far inside 32 bits).
+constexpr int64_t kMaxOutput = (int64_t)1 << 40;
 // A [n][k] weight is addressed with 32-bit byte offsets from its base.
 constexpr int64_t kMaxNkBytes = (int64_t)0x7FFFFFF0 - 16;
 
@@ -132,7 +134,6 @@ ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k, const uint1
     p.ldc = width[0];
     p.gate_w0 = wcol0[0];
     p.up_w0 = wcol0[1];
-    p.tiles_n = (p.N + ttl::gemm_tile_cols(1) - 1) / ttl::gemm_tile_cols(1);
   } else {
     p.mode = 0;
     p.N = (int32_t)n_r;
@@ -145,12 +146,10 @@ ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k, const uint1
       out0 += width[s];
     }
     p.seg_out0[sp.nseg] = (int32_t)out0;
-    p.tiles_n = (p.N + ttl::gemm_tile_cols(0) - 1) / ttl::gemm_tile_cols(0);
   }
-  p.tiles_m = (p.M + ttl::gemm_tile_rows() - 1) / ttl::gemm_tile_rows();
-  if ((int64_t)p.tiles_m * p.tiles_n > kMaxDim)
-    return fail(TTL_ERR_SHAPE, "%s: too many tiles", who);
-  return launch_status(ttl::launch_gemm_bf16(p, static_cast<hipStream_t>(stream)), who);
+  if (b * (int64_t)p.N > kMaxOutput)
+    return fail(TTL_ERR_SHAPE, "%s: output of %lld x %d elements is too large", who, (long long)b, p.N);
+  return launch_status(ttl::launch_gemm(p, static_cast<hipStream_t>(stream)), who);
 }
 
 ttl_status shard_linear_row(const uint16_t* X, int64_t b, int64_t k, int32_t x_is_parallel,
@@ -198,11 +197,10 @@ ttl_status shard_linear_row(const uint16_t* X, int64_t b, int64_t k, int32_t x_i
   p.seg_out0[0] = 0;
   p.seg_out0[1] = (int32_t)n;
   p.seg_w0[0] = 0;
-  p.tiles_m = (p.M + ttl::gemm_tile_rows() - 1) / ttl::gemm_tile_rows();
-  p.tiles_n = (p.N + ttl::gemm_tile_cols(0) - 1) / ttl::gemm_tile_cols(0);
-  if ((int64_t)p.tiles_m * p.tiles_n > kMaxDim)
-    return fail(TTL_ERR_SHAPE, "%s: too many tiles", who);
-  return launch_status(ttl::launch_gemm_bf16(p, static_cast<hipStream_t>(stream)), who);
+  if (b * n > kMaxOutput)
+    return fail(TTL_ERR_SHAPE, "%s: output of %lld x %lld elements is too large", who, (long long)b,
+                (long long)n);
+  return launch_status(ttl::launch_gemm(p, static_cast<hipStream_t>(stream)), who);
 }
 
 ttl_status reduce_partials_rmsnorm(const uint16_t* P, int32_t t, int64_t b, int64_t n,

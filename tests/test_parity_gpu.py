@@ -1,7 +1,8 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle, on seeded synthetic inputs.
 
 Small cases compare every element; they span several 256-wide tiles and ragged tails in all three
-GEMM dimensions.  Tolerance, per output tensor: the error beyond the bf16 rounding of each output
+GEMM dimensions.  Each GEMM case runs through both kernels the library has (256 x 256 tiles, and
+the split-K kernel for short M, forced with TTL_GEMM_KERNEL) and through the shape-based choice.  Tolerance, per output tensor: the error beyond the bf16 rounding of each output
 element is at most 2e-2 * rms(ref), the reference being the oracle's unrounded float64 value (bf16
 inputs, so the device-side error is fp32 accumulation and fp32 elementwise math).  Integer-exact
 special cases (identity and one-hot operands) are compared bit for bit.
@@ -26,6 +27,17 @@ def ttl():
 
 
 LAYOUTS = pytest.mark.parametrize("layout", ["kn", "nk"])
+
+
+@pytest.fixture(params=["auto", "tiled", "splitk"])
+def gemm_path(request, monkeypatch):
+    """Which GEMM kernel the library uses for the test (auto = its choice by shape)."""
+    if request.param == "auto":
+        monkeypatch.delenv("TTL_GEMM_KERNEL", raising=False)
+    else:
+        monkeypatch.setenv("TTL_GEMM_KERNEL", request.param)
+    monkeypatch.delenv("TTL_GEMM_SPLITS", raising=False)
+    return request.param
 
 
 def _stored(ttl, W, layout):
@@ -56,14 +68,14 @@ def _col_case(ttl, b, k, split_np, split_c, t, seed, epi=0, layout="kn"):
     (513, 1024, 2048, 8),   # several tiles in every dimension
 ])
 @LAYOUTS
-def test_col_silu_mul(ttl, b, k, I, t, layout):
+def test_col_silu_mul(ttl, gemm_path, b, k, I, t, layout):
     _col_case(ttl, b, k, oracle.merged_gate_up_split(I, t), ttl.merged_gate_up_split(I, t), t,
               seed=10 + b, epi=ttl.EPI_SILU_MUL, layout=layout)
 
 
 @pytest.mark.parametrize("b,k,n,t", [(16, 256, 1376, 2), (300, 136, 520, 1), (260, 512, 2048, 4)])
 @LAYOUTS
-def test_col_plain(ttl, b, k, n, t, layout):
+def test_col_plain(ttl, gemm_path, b, k, n, t, layout):
     _col_case(ttl, b, k, oracle.plain_split(n, t), None, t, seed=20 + b, layout=layout)
 
 
@@ -74,7 +86,7 @@ def test_col_plain(ttl, b, k, n, t, layout):
     (300, 512, 32, 8, 128, 4), # the 8B attention head layout at a small batch
 ])
 @LAYOUTS
-def test_col_qkv(ttl, b, k, nq, nkv, hd, t, layout):
+def test_col_qkv(ttl, gemm_path, b, k, nq, nkv, hd, t, layout):
     _col_case(ttl, b, k, oracle.qkv_split(nq, nkv, hd, t), ttl.qkv_split(nq, nkv, hd, t), t, seed=30 + b,
               layout=layout)
 
@@ -83,7 +95,7 @@ def test_col_qkv(ttl, b, k, nq, nkv, hd, t, layout):
                                      (5, 2048, 264, 8)])
 @pytest.mark.parametrize("x_is_parallel", [True, False])
 @LAYOUTS
-def test_row(ttl, b, k, n, t, x_is_parallel, layout):
+def test_row(ttl, gemm_path, b, k, n, t, x_is_parallel, layout):
     w = k // t
     X = wl.random_bf16((b, k), 40 + b)
     W = wl.random_bf16((k, n), 41 + b, std=0.05)
@@ -125,7 +137,7 @@ def test_reduce_residual_in_place(ttl):
 
 
 @LAYOUTS
-def test_identity_and_one_hot_are_exact(ttl, layout):
+def test_identity_and_one_hot_are_exact(ttl, gemm_path, layout):
     # W = identity: every column of the output is one column of X, exactly.
     b, k, t = 40, 256, 2
     X = wl.random_bf16((b, k), 70)
@@ -143,7 +155,7 @@ def test_identity_and_one_hot_are_exact(ttl, layout):
     assert torch.equal(P.cpu(), Wr[idx])
 
 
-def test_layouts_agree_bitwise(ttl):
+def test_layouts_agree_bitwise(ttl, gemm_path):
     """Both weight storages feed the matrix cores the same products in the same k order."""
     b, k, I, t = 300, 512, 1024, 4
     X = gpu(wl.random_bf16((b, k), 90))
@@ -155,7 +167,7 @@ def test_layouts_agree_bitwise(ttl):
     assert torch.equal(a, c)
 
 
-def test_bitwise_deterministic(ttl):
+def test_bitwise_deterministic(ttl, gemm_path):
     b, k, I, t = 300, 512, 1024, 2
     X, Wgu = gpu(wl.random_bf16((b, k), 80)), gpu(wl.random_bf16((k, 2 * I), 81, std=0.05))
     Wd = gpu(wl.random_bf16((I, k), 82, std=0.05))
@@ -169,6 +181,51 @@ def test_bitwise_deterministic(ttl):
         outs.append((act.cpu(), P.cpu(), r.cpu(), y.cpu()))
     for a, c in zip(*outs):
         assert torch.equal(a, c)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 65])
+@LAYOUTS
+def test_splitk_split_counts(ttl, monkeypatch, splits, layout):
+    """Split-K with a given number of k ranges, k tail of 8 (4104 = 64 * 64 + 8), ragged M and N.
+
+    65 splits puts one k-tile in each range, the last one holding only the 8-wide tail."""
+    monkeypatch.setenv("TTL_GEMM_KERNEL", "splitk")
+    monkeypatch.setenv("TTL_GEMM_SPLITS", str(splits))
+    b, k = 37, 4104
+    _col_case(ttl, b, k, oracle.merged_gate_up_split(200, 1), ttl.merged_gate_up_split(200, 1), 1,
+              seed=100 + splits, epi=ttl.EPI_SILU_MUL, layout=layout)
+    _col_case(ttl, 3, k, oracle.qkv_split(8, 2, 32, 2), ttl.qkv_split(8, 2, 32, 2), 2, seed=110 + splits,
+              layout=layout)
+    n, t = 392, 2
+    X = wl.random_bf16((b, 2 * k), 120 + splits)
+    W = wl.random_bf16((2 * k, n), 121 + splits, std=0.05)
+    Wd, lay = _stored(ttl, W, layout)
+    for r in range(t):
+        P = ttl.shard_linear_row(gpu(X), Wd, t, r, x_is_parallel=False, w_layout=lay)
+        assert_close(from_gpu(P), oracle.row_shard(f64(X), f64(W), t, r, x_is_parallel=False),
+                     f"split-K row splits={splits} r={r} {layout}")
+
+
+def test_splitk_repeated_launches_reuse_workspace(ttl, monkeypatch):
+    """Back-to-back split-K launches of different sizes share (and grow) the library's workspace;
+    a repeated shape must reproduce its first result bit for bit."""
+    monkeypatch.setenv("TTL_GEMM_KERNEL", "splitk")
+    monkeypatch.delenv("TTL_GEMM_SPLITS", raising=False)
+    shapes = [(64, 8192, 1024), (1, 4096, 3584), (64, 8192, 1024), (200, 2048, 4096), (1, 4096, 3584)]
+    outs = {}
+    for i, (b, k, n) in enumerate(shapes):
+        X = gpu(wl.random_bf16((b, k), 130 + b))
+        W = gpu(wl.random_bf16((k, n), 131 + n, std=0.05))
+        Y = ttl.shard_linear_col(X, W, 1, 0)
+        key = (b, k, n)
+        if key in outs:
+            assert torch.equal(Y, outs[key]), f"launch {i} {key} differs from its first run"
+        else:
+            outs[key] = Y
+            Xs, Ws = X.cpu(), W.cpu()
+            rows = [0, b - 1]
+            ref = oracle.col_shard(f64(Xs[rows]), f64(Ws), oracle.plain_split(n, 1), 1, 0)
+            assert_close(from_gpu(Y[rows]), ref, f"repeated split-K {key}")
 
 
 def test_tiny_mlp_chain_all_ranks(ttl):
