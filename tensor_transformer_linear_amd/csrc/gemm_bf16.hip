@@ -51,10 +51,18 @@ using namespace gemm;
 constexpr int kBM = 256;                   // output rows per tile
 constexpr int kBN = 256;                   // weight columns per tile
 constexpr int kBK = TTL_GEMM_BK;           // k per stage (64: 128-B global row pieces)
-constexpr int kWaves = 8;
+#ifndef TTL_GEMM_WAVES
+#define TTL_GEMM_WAVES 8
+#endif
+// 8: two waves per SIMD, 128 x 64 each.  4 (one wave per SIMD, 128 x 128 each, accumulators in
+// AGPRs, a third fewer LDS reads) measured ~10% slower: with one wave per SIMD nothing hides its
+// own LDS waits and barrier stalls.
+constexpr int kWaves = TTL_GEMM_WAVES;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStages = TTL_GEMM_STAGES;
-constexpr int kWN = 64;                    // weight columns per wave (2 x 4 wave grid)
+constexpr int kWM = 128;                   // rows per wave
+constexpr int kWavesN = kWaves / (kBM / kWM);
+constexpr int kWN = kBN / kWavesN;         // weight columns per wave (2 x kWavesN wave grid)
 constexpr int kNI = kWN / 32;              // 32-wide accumulator blocks per wave along n
 constexpr int kAElems = kBM * kBK;         // A stage (bf16 elements)
 constexpr int kBElems = kBK * kBN;         // B stage
@@ -94,12 +102,12 @@ __device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, i
 template <int MODE>
 __device__ inline int64_t weight_column(const GemmParams& p, int n0, int c, bool& ok) {
   if (MODE == kSiluMul) {
-    // Tile column c = w*64 + nb*32 + j: block nb = 0 of a wave holds gate columns and nb = 1 the up
-    // columns of the same act columns, so gate and up of one output meet in one lane.
+    // Tile column c = w*kWN + nb*32 + j: blocks nb < kNI/2 of a wave hold gate columns and the
+    // others the up columns of the same act columns, so gate and up of one output meet in one lane.
     const int w = c / kWN, nb = (c % kWN) / 32, j = c % 32;
-    const int act = n0 + w * (kWN / 2) + j;
+    const int act = n0 + w * (kWN / 2) + (nb % (kNI / 2)) * 32 + j;
     ok = act < p.N;
-    return (nb == 0 ? p.gate_w0 : p.up_w0) + act;
+    return (nb < kNI / 2 ? p.gate_w0 : p.up_w0) + act;
   }
   const int oc = n0 + c;
   ok = oc < p.N;
@@ -111,15 +119,15 @@ __device__ inline int64_t weight_column(const GemmParams& p, int n0, int c, bool
 }
 
 template <int MODE, bool WNK>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void gemm_bf16_kernel(const GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages * kStageElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2;  // rows wm*128 .. +127
-  const int wn = wave & 3;   // weight columns wn*64 .. +63
+  const int wm = wave / kWavesN;  // rows wm*128 .. +127
+  const int wn = wave % kWavesN;  // weight columns wn*kWN .. +kWN-1
 
   int tile_m, tile_n;
   tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tile_m, tile_n);
@@ -195,7 +203,7 @@ void gemm_bf16_kernel(const GemmParams p) {
 #pragma unroll
   for (int kk = 0; kk < kKK; ++kk) {
     const int slot = (kk * 2 + a_half) ^ rs;
-    ra_off[kk] = (wm * 128 + a_r) * kBK + slot * 8;
+    ra_off[kk] = (wm * kWM + a_r) * kBK + slot * 8;
     rb_off[kk] = kAElems + (wn * kWN + a_r) * kBK + slot * 8;  // WNK: B rows are weight columns
   }
   // [k][n] staging: 16-lane group g = lane/16 reads k row kk*16 + 8*(g/2) + 4*h + (lane%16)/4 at
@@ -208,7 +216,7 @@ void gemm_bf16_kernel(const GemmParams p) {
     const int c = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni)
-      rt_off[ni] = kAElems + krow * kBN + ((8 * wn + 4 * ni + c) ^ x) * 8 + 4 * (lane & 1);
+      rt_off[ni] = kAElems + krow * kBN + (((kWN / 8) * wn + 4 * ni + c) ^ x) * 8 + 4 * (lane & 1);
   }
 
   bf16x8_t af[2][4], bv[2][kNI];
@@ -260,7 +268,8 @@ void gemm_bf16_kernel(const GemmParams p) {
 
   // One k-tile: the MFMAs of each k16 slice overlap the reads of the next; the barrier that
   // publishes tile kt+1 sits before the MFMAs of the last slice, which overlap the first reads of
-  // tile kt+1.
+  // tile kt+1.  (Issuing the next tile's copies spread over the slices instead of in one burst at
+  // the start measured slower.)
   auto compute_tile = [&](int kt, auto wait) {
 #pragma unroll
     for (int kk = 0; kk + 1 < kKK; ++kk) {
@@ -308,7 +317,7 @@ void gemm_bf16_kernel(const GemmParams p) {
 
   // Epilogue straight from the accumulators: each lane owns 4 consecutive columns of one row per
   // register group, stored as one 8-byte piece.
-  const int row_base = m0 + wm * 128 + a_r;
+  const int row_base = m0 + wm * kWM + a_r;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
     const int row = row_base + mi * 32;
@@ -329,12 +338,15 @@ void gemm_bf16_kernel(const GemmParams p) {
         }
     } else {
 #pragma unroll
+      for (int ni = 0; ni < kNI / 2; ++ni)
+#pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int col = n0 + wn * (kWN / 2) + g * 8 + a_half * 4;
+        const int col = n0 + wn * (kWN / 2) + ni * 32 + g * 8 + a_half * 4;
         if (col < p.N) {
           float a[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) a[e] = silu_mul(acc[mi][0][4 * g + e], acc[mi][1][4 * g + e]);
+          for (int e = 0; e < 4; ++e)
+            a[e] = silu_mul(acc[mi][ni][4 * g + e], acc[mi][ni + kNI / 2][4 * g + e]);
           u32x2_t v;
           v.x = pack_bf16x2(a[0], a[1]);
           v.y = pack_bf16x2(a[2], a[3]);
