@@ -27,6 +27,12 @@
  *     call returns and frees nothing of the caller's.  Calls are asynchronous: they validate, then
  *     enqueue kernels on `stream` (a hipStream_t; NULL = the default stream) and return.  Buffers
  *     must stay alive until the stream has run the work.
+ *   - Workspace: GEMMs with few token rows (decode batches, small shards) are cut along k and need
+ *     fp32 partial sums.  The library keeps one device buffer per GPU for them, allocated on the
+ *     first such call (and grown, after waiting for the device, when a later call needs more); it
+ *     lives until the process ends.  Calls whose work overlaps in time on one GPU (different
+ *     streams) share it and race: serialise them on one stream.  A failed allocation is
+ *     TTL_ERR_HIP.
  *   - Errors: every call returns a ttl_status.  Arguments are validated synchronously before any
  *     launch; on a non-OK status nothing has been enqueued and ttl_last_error() returns a message
  *     (thread-local).  A launch failure reported by the runtime is TTL_ERR_HIP.  A fault inside a
