@@ -77,6 +77,10 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=32, help="token rows in the CPU oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the CPU oracle sample until this much time has passed")
+    ap.add_argument("--no-yardstick", action="store_true",
+                    help="skip timing torch.matmul (hipBLASLt) on the same GEMM shapes")
+    ap.add_argument("--no-power", action="store_true",
+                    help="skip sampling socket power and GFX clock while the step repeats")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (5 times) and exit: the "
                          "reference for scaling HBM traffic counters")
@@ -157,7 +161,70 @@ def run_mlp(ttl, torch, w, b, steps, warmup, seed, layout, rotate_ranks=False):
         d["frac_mfma_peak"] = d.get("tflops", 0.0) / PEAK_BF16_TFLOPS
         d["frac_hbm_peak"] = d["gbs"] / PEAK_HBM_GBS
     return {"ms_per_step": ms_step, "flops": f_col + f_row, "kernels": kern,
-            "tensors": (X, Wgu, Wd, R, gamma)}
+            "tensors": (X, Wgu, Wd, R, gamma), "step": step}
+
+
+def yardstick(torch, w, layout):
+    """torch.matmul (hipBLASLt) on this rank's GEMM shapes, as an off-path reference: the plain
+    products only (no SiLU·up, no column map: the rank's weight slice is a separate dense tensor).
+    Decode shapes cycle through 8 weight copies so that the Infinity Cache does not hold them."""
+    H, Ir = w.hidden, w.intermediate // w.t
+    out = {}
+    for M, K, N, name in ((4096, H, 2 * Ir, "gate_up_b4096"), (4096, Ir, H, "down_b4096"),
+                          (64, H, 2 * Ir, "gate_up_b64"), (64, Ir, H, "down_b64")):
+        X = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+        copies = 8 if M < 512 else 1
+        Ws = [(torch.randn(N, K, device="cuda") * 0.02).to(torch.bfloat16) if layout == "nk"
+              else (torch.randn(K, N, device="cuda") * 0.02).to(torch.bfloat16) for _ in range(copies)]
+        mm = (lambda i: torch.matmul(X, Ws[i % copies].t())) if layout == "nk" else \
+             (lambda i: torch.matmul(X, Ws[i % copies]))
+        for i in range(5):
+            mm(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        n = 20
+        e0.record()
+        for i in range(n):
+            mm(i)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / n * 1e3
+        out[name] = {"us": us, "tflops": 2.0 * M * K * N / (us * 1e6)}
+        del X, Ws
+    return {"library": "torch.matmul (hipBLASLt)", "weight_storage": layout, "shapes": out}
+
+
+def sample_power_clock(torch, step, seconds=2.0):
+    """Socket power and GFX clocks reported by amd-smi while `step` runs back to back (the GPU
+    settles at its power limit within a fraction of a second).  None if amd-smi is unavailable."""
+    import subprocess
+    t0 = time.perf_counter()
+    proc, i = None, 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
+        if proc is None and time.perf_counter() - t0 > seconds / 2:
+            try:
+                proc = subprocess.Popen(["amd-smi", "metric", "-p", "-c", "--json"], stdout=subprocess.PIPE,
+                                        stderr=subprocess.DEVNULL, text=True)
+            except OSError:
+                return None
+    if proc is None:
+        return None
+    try:
+        out, _ = proc.communicate(timeout=30)
+        d = json.loads(out)
+        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        clocks = [v["clk"]["value"] for k, v in g["clock"].items() if k.startswith("gfx_")]
+        return {"socket_power_w": g["power"]["socket_power"]["value"],
+                "gfx_clock_mhz_mean": sum(clocks) / len(clocks), "gfx_clock_mhz_min": min(clocks),
+                "gfx_clock_mhz_max": max(clocks),
+                "sampled": "amd-smi metric -p -c, once, while the step repeated for %.1f s" % seconds}
+    except Exception:  # pragma: no cover - tool output not as expected
+        return None
 
 
 def recorded_traffic(kernel, workload):
@@ -263,6 +330,7 @@ def main():
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": kcol["gbs"] / PEAK_HBM_GBS,
                 "traffic": traffic}
     roof["algorithmic_gflop_per_launch"] = kcol["gflop"]
+    power = None if args.no_power else sample_power_clock(torch, res["step"])
     roof["algorithmic_mbytes_per_launch"] = kcol["mbytes"]
     out = {
         "metric": "TFLOP/s and % bf16 MFMA peak, 1-rank shard of Llama-3-70B MLP at TP=8 shape",
@@ -282,6 +350,7 @@ def main():
                    "intermediate": w.intermediate, "t": w.t, "tokens": b, "weight_storage": args.layout,
                    "step": "gate_up+SiLU*up (col) -> down (row partial) -> reduce 8 partials + residual + RMSNorm"},
         "roofline": roof,
+        "power_clock": power,
         "kernels": res["kernels"],
     }
     if not args.no_decode and b != 64:
@@ -291,6 +360,7 @@ def main():
                            "tflops": dec["flops"] / (dec["ms_per_step"] * 1e9),
                            "kernels": dec["kernels"]}
         del dec
+    out["yardstick"] = None if args.no_yardstick else yardstick(torch, w, args.layout)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(torch, w, res["tensors"], args.cpu_rows, args.cpu_seconds)
     else:
