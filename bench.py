@@ -81,6 +81,9 @@ def parse():
                     help="skip timing torch.matmul (hipBLASLt) on the same GEMM shapes")
     ap.add_argument("--no-power", action="store_true",
                     help="skip sampling socket power and GFX clock while the step repeats")
+    ap.add_argument("--steady-state", action="store_true",
+                    help="only run each b=4096 GEMM (ours and hipBLASLt's) back to back for 2 s, sample "
+                         "power and clock, time 30 launches, print one JSON line per GEMM and exit")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (5 times) and exit: the "
                          "reference for scaling HBM traffic counters")
@@ -195,60 +198,86 @@ def yardstick(torch, w, layout):
     return {"library": "torch.matmul (hipBLASLt)", "weight_storage": layout, "shapes": out}
 
 
-def sample_power_clock(torch, step, seconds=2.0):
-    """Socket power and GFX clocks reported by amd-smi while `step` runs back to back (the GPU
-    settles at its power limit within a fraction of a second).  None if amd-smi is unavailable."""
+def read_power_clock():
+    """(socket power W, mean GFX clock MHz) from amd-smi, or None."""
     import subprocess
+    try:
+        out = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True,
+                             timeout=30).stdout
+        d = json.loads(out)
+        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        clocks = [v["clk"]["value"] for k, v in g["clock"].items() if k.startswith("gfx_")]
+        return g["power"]["socket_power"]["value"], sum(clocks) / len(clocks)
+    except Exception:  # pragma: no cover - tool missing or output not as expected
+        return None
+
+
+def steady_state(ttl, torch, w, layout):
+    """Each b=4096 GEMM of the rank, ours and hipBLASLt's, at the power limit: run back to back for
+    2 s, sample power and clock once in the middle, then time 30 launches."""
+    lay = ttl.W_NK if layout == "nk" else ttl.W_KN
+    b, H, I, t = 4096, w.hidden, w.intermediate, w.t
+    Ir = I // t
+    X = torch.randn(b, H, device="cuda").to(torch.bfloat16)
+    Wgu = (torch.randn(H, 2 * I, device="cuda") * 0.02).to(torch.bfloat16)
+    Wd = (torch.randn(I, H, device="cuda") * 0.02).to(torch.bfloat16)
+    act = torch.randn(b, Ir, device="cuda").to(torch.bfloat16)
+    P = torch.empty(b, H, device="cuda", dtype=torch.bfloat16)
+    sp = ttl.merged_gate_up_split(I, t)
+    # rank 0's slices as separate dense tensors for torch.matmul
+    Wg_r = torch.cat([Wgu[:, :Ir], Wgu[:, I:I + Ir]], dim=1).contiguous()  # [H, 2*Ir]
+    Wd_r = Wd[:Ir].contiguous()                                            # [Ir, H]
+    if lay == ttl.W_NK:
+        Wgu, Wd = Wgu.t().contiguous(), Wd.t().contiguous()
+        Wg_r, Wd_r = Wg_r.t().contiguous(), Wd_r.t().contiguous()
+        mm_g = lambda: torch.matmul(X, Wg_r.t())
+        mm_d = lambda: torch.matmul(act, Wd_r.t())
+    else:
+        mm_g = lambda: torch.matmul(X, Wg_r)
+        mm_d = lambda: torch.matmul(act, Wd_r)
+    cases = (("ours_gate_up_silu", 2.0 * b * H * 2 * Ir,
+              lambda: ttl.shard_linear_col(X, Wgu, t, 0, sp, ttl.EPI_SILU_MUL, Y=act, w_layout=lay)),
+             ("ours_down", 2.0 * b * Ir * H, lambda: ttl.shard_linear_row(act, Wd, t, 0, P=P, w_layout=lay)),
+             ("hipblaslt_gate_up_plain", 2.0 * b * H * 2 * Ir, mm_g),
+             ("hipblaslt_down", 2.0 * b * Ir * H, mm_d))
+    for name, flops, fn in cases:
+        t0 = time.perf_counter()
+        pc = None
+        while time.perf_counter() - t0 < 2.0:
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
+            if pc is None and time.perf_counter() - t0 > 1.0:
+                pc = read_power_clock() or (None, None)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(30):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / 30 * 1e3
+        print(json.dumps({"gemm": name, "weight_storage": layout, "us": us, "tflops": flops / (us * 1e6),
+                          "socket_power_w": pc[0] if pc else None,
+                          "gfx_clock_mhz_mean": pc[1] if pc else None}), flush=True)
+
+
+def sample_power_clock(torch, step, seconds=2.0):
+    """Socket power and GFX clock reported by amd-smi once while `step` runs back to back (the GPU
+    settles at its power limit within a fraction of a second).  None if amd-smi is unavailable."""
     t0 = time.perf_counter()
-    proc, i = None, 0
+    pc, i = None, 0
     while time.perf_counter() - t0 < seconds:
         for _ in range(20):
             step(i)
             i += 1
         torch.cuda.synchronize()
-        if proc is None and time.perf_counter() - t0 > seconds / 2:
-            try:
-                proc = subprocess.Popen(["amd-smi", "metric", "-p", "-c", "--json"], stdout=subprocess.PIPE,
-                                        stderr=subprocess.DEVNULL, text=True)
-            except OSError:
-                return None
-    if proc is None:
+        if pc is None and time.perf_counter() - t0 > seconds / 2:
+            pc = read_power_clock() or (None, None)
+    if not pc or pc[0] is None:
         return None
-    try:
-        out, _ = proc.communicate(timeout=30)
-        d = json.loads(out)
-        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
-        clocks = [v["clk"]["value"] for k, v in g["clock"].items() if k.startswith("gfx_")]
-        return {"socket_power_w": g["power"]["socket_power"]["value"],
-                "gfx_clock_mhz_mean": sum(clocks) / len(clocks), "gfx_clock_mhz_min": min(clocks),
-                "gfx_clock_mhz_max": max(clocks),
-                "sampled": "amd-smi metric -p -c, once, while the step repeated for %.1f s" % seconds}
-    except Exception:  # pragma: no cover - tool output not as expected
-        return None
-
-
-def recorded_traffic(kernel, workload):
-    """HBM bytes per launch recorded from the FETCH_SIZE / WRITE_SIZE counters in profiles/, or None
-    when no record exists or the kernel sources changed since the counters were taken."""
-    h = hashlib.sha256()
-    for rel in TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    digest = h.hexdigest()
-    pat = re.compile(r"^traffic\s+kernel=(\S+)\s+workload=(\S+)\s+bytes_per_launch=(\d+)\s+"
-                     r"source_sha256=([0-9a-f]{64})\s*$")
-    pdir = os.path.join(ROOT, "profiles")
-    if not os.path.isdir(pdir):
-        return None
-    for name in sorted(os.listdir(pdir)):
-        if not name.endswith((".md", ".txt")):
-            continue
-        with open(os.path.join(pdir, name)) as f:
-            for line in f:
-                m = pat.match(line.strip())
-                if m and m.group(1) == kernel and m.group(2) == workload and m.group(4) == digest:
-                    return float(m.group(3))
-    return None
+    return {"socket_power_w": pc[0], "gfx_clock_mhz_mean": pc[1],
+            "sampled": "amd-smi metric -p -c --json, once, while the step repeated for %.1f s" % seconds}
 
 
 def cpu_baseline(torch, w, tensors, rows, seconds):
@@ -313,6 +342,9 @@ def main():
     from tensor_transformer_linear_amd import ttl
     from tensor_transformer_linear_amd import workloads as wl
     w = wl.LLAMA3_70B_MLP_TP8
+    if args.steady_state:
+        steady_state(ttl, torch, w, args.layout)
+        return 0
     b = args.batch
     workload = f"llama3_70b_mlp_tp8_rank0_b{b}_{args.layout}"
     res = run_mlp(ttl, torch, w, b, args.steps, args.warmup, seed=0, layout=args.layout,
