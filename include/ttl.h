@@ -117,6 +117,27 @@ ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k,
                             void* stream);
 
 /*
+ * shard_linear_col_gathered — ColumnParallelLinear forward with gather_output=True (vLLM
+ * walkthrough, sections "ColumnParallelLinear" and "all-gather"): the rank's output is placed in its
+ * block of the all-gathered tensor, the concatenation of the t rank outputs along the last dimension
+ * in rank order.  On one GPU the simulated ranks fill the whole gathered tensor; with a plain split
+ * it equals X · W (and with SILU_MUL the full silu(X·W_gate)·(X·W_up)).  Used, for one, by a
+ * vocab-parallel LM head (the "Tensor Parallelism" manual, section "Vocab Parallel": each rank owns
+ * a contiguous vocabulary slice, and the logits are all-gathered).
+ *
+ *   Y_all  [b, t·w] bf16, w = the rank output width of shard_linear_col (n_r, or n_r/2 with
+ *          SILU_MUL); this call writes columns [rank·w, (rank+1)·w) and nothing else.
+ * Every other argument, and every error, as shard_linear_col.
+ */
+ttl_status shard_linear_col_gathered(const uint16_t* X, int64_t b, int64_t k,
+                                     const uint16_t* W, int64_t n, ttl_weight_layout w_layout,
+                                     int32_t t, int32_t rank,
+                                     const ttl_col_split* split,
+                                     ttl_epilogue epi,
+                                     uint16_t* Y_all,
+                                     void* stream);
+
+/*
  * shard_linear_row — RowParallelLinear forward of rank `rank` of `t` with reduce_results=False:
  * the rank's partial sum, which a later reduction adds up (vLLM walkthrough, section
  * "RowParallelLinear"; section 12 of "vLLM Code Reading (Section 5)": Y_i = X_i A_i, Y = Σ_i Y_i).
@@ -161,6 +182,31 @@ ttl_status reduce_partials_rmsnorm(const uint16_t* P, int32_t t, int64_t b, int6
                                    uint16_t* residual_out,
                                    uint16_t* Y,
                                    void* stream);
+
+/*
+ * reduce_scatter_partials_rmsnorm — the sequence-parallel form of reduce_partials_rmsnorm: the
+ * partial sums are reduce-scattered over the token rows, so rank `rank` reduces, adds its residual
+ * shard to and normalises only its chunk of b/t rows, [rank·b/t, (rank+1)·b/t) ("Tensor
+ * Parallelism" manual, section "Communication Patterns": after reduce-scatter each rank holds one
+ * reduced chunk; "vLLM Code Reading (Section 5)", section 4, "PP + SP 下的 all_gather_tensors":
+ * under sequence parallelism the residual is kept scattered over the ranks, the token count padded
+ * for it).
+ *
+ *   P         [t, b, n] bf16 partials of all t ranks over all b rows.
+ *   residual  [b/t, n] bf16, this rank's shard of the residual stream, or NULL.
+ *   residual_out, Y  [b/t, n] bf16, this rank's shards of the outputs (as reduce_partials_rmsnorm).
+ * The t calls rank = 0..t-1 together produce exactly reduce_partials_rmsnorm's outputs, row chunk
+ * by row chunk (the all-gather that follows is their concatenation).
+ * Errors: as reduce_partials_rmsnorm; rank outside [0, t) -> RANK; b not divisible by t ->
+ * NOT_DIVISIBLE (the caller pads the token count).
+ */
+ttl_status reduce_scatter_partials_rmsnorm(const uint16_t* P, int32_t t, int64_t b, int64_t n,
+                                           int32_t rank,
+                                           const uint16_t* residual,
+                                           const uint16_t* gamma, float eps,
+                                           uint16_t* residual_out,
+                                           uint16_t* Y,
+                                           void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* ttl_last_error(void);

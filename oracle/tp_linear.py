@@ -21,6 +21,9 @@ Sources (page title, then section):
   [VLLM-CR5] "vLLM Code Reading (Section 5): GPUWorker.execute_model 与 PP/TP 通信"
              (jeremyguo.space), sections 12 (Y_i = X_i A_i, Y = sum_i Y_i) and 14 (activation runs on
              the local shard).
+  [MLXCEL]   "Tensor Parallelism" (mlxcel.ai manual), sections "Vocab Parallel" (each rank owns a
+             contiguous vocabulary slice; logits all-gathered) and "Communication Patterns"
+             (reduce-scatter leaves each rank one reduced chunk).
   [UNDERCUR] "Tensor & pipeline parallelism" (wrynx.github.io, Undercurrent docs), sections
              "residual_stream" (post_attention_layernorm(hidden, residual) returns the updated pair;
              the residual stream is hidden + residual) and "final_norm" (RMSNorm(hidden, eps), not
@@ -50,6 +53,7 @@ __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "round_bf16", "divide", "qkv_local_heads",
     "column_split", "merged_gate_up_split", "qkv_split", "plain_split", "rank_columns",
     "col_shard", "silu", "silu_mul", "row_shard", "reduce_partials_rmsnorm", "mlp_rank_chain",
+    "col_gathered", "reduce_scatter_partials_rmsnorm",
 ]
 
 
@@ -238,6 +242,31 @@ def reduce_partials_rmsnorm(P, residual, gamma, eps: float):
     ms = np.mean(h * h, axis=-1, keepdims=True)
     y = h / np.sqrt(ms + eps) * np.asarray(gamma, dtype=np.float64)
     return h, y
+
+
+def col_gathered(X, W, split, t: int, epi_silu_mul: bool = False) -> np.ndarray:
+    """ColumnParallelLinear with gather_output=True: the all-gather of the t rank outputs, i.e. their
+    concatenation along the last dimension in rank order.  ([VLLM-TP] "ColumnParallelLinear"
+    forward, gather_output branch, and "all-gather"; [MLXCEL] "Vocab Parallel": logits of the
+    vocabulary slices all-gathered.)"""
+    outs = []
+    for r in range(t):
+        y = col_shard(X, W, split, t, r)
+        outs.append(silu_mul(y) if epi_silu_mul else y)
+    return np.concatenate(outs, axis=-1)
+
+
+def reduce_scatter_partials_rmsnorm(P, residual_shard, gamma, eps: float, t: int, rank: int):
+    """Sequence-parallel reduction: rank `rank` reduces and normalises only its chunk of b/t token
+    rows, [rank*b/t, (rank+1)*b/t), with its shard of the residual stream.  ([MLXCEL]
+    "Communication Patterns": after reduce-scatter each rank holds one reduced chunk;
+    [VLLM-CR5] section 4, PP + SP: the residual stays scattered over the ranks.)  Returns (h, y) of
+    the chunk."""
+    P = np.asarray(P, dtype=np.float64)
+    b = P.shape[1]
+    rows = divide(b, t)
+    chunk = P[:, rank * rows:(rank + 1) * rows]
+    return reduce_partials_rmsnorm(chunk, residual_shard, gamma, eps)
 
 
 def mlp_rank_chain(X, Wgu, Wd, t: int, intermediate: int, store_bf16: bool = True):

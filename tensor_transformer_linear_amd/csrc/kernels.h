@@ -48,6 +48,7 @@ constexpr int kSkinnyCols = 128;  // weight columns per tile (64 act columns in 
 constexpr int kSkinnyK = 64;      // k per pipeline stage
 hipError_t launch_gemm_skinny(const GemmParams& p, int mb, hipStream_t stream);
 
+// Rows [0, b) of the outputs; row i reads the partials at P + i*n + r*plane, r = 0..t-1.
 struct ReduceNormParams {
   const uint16_t* P;
   const uint16_t* residual;  // may be null
@@ -55,6 +56,7 @@ struct ReduceNormParams {
   uint16_t* residual_out;
   uint16_t* Y;
   int64_t b, n;
+  int64_t plane;             // elements between consecutive ranks' partials
   int32_t t;
   float eps;
 };

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(THREADS) void reduce_rmsnorm_kernel(const ReduceNor
   const int64_t row = blockIdx.x;
   const int64_t n = p.n;
   const int pieces = (int)(n >> 3);
-  const int64_t plane = p.b * n;  // elements of one rank's partial
+  const int64_t plane = p.plane;  // elements between consecutive ranks' partials
 
   float h[CPT][8];
 #pragma unroll

@@ -45,18 +45,13 @@ ttl_status launch_status(hipError_t e, const char* who) {
   return TTL_OK;
 }
 
-}  // namespace
 
-extern "C" {
-
-const char* ttl_last_error(void) { return g_last_error.c_str(); }
-
-int32_t ttl_version(void) { return 100; }  // 0.1.0
-
-ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k, const uint16_t* W, int64_t n,
-                            ttl_weight_layout w_layout, int32_t t, int32_t rank,
-                            const ttl_col_split* split, ttl_epilogue epi, uint16_t* Y, void* stream) {
-  static const char* who = "shard_linear_col";
+// Validation and GEMM parameters shared by the column entry points; the output placement (C, ldc)
+// is left to the caller.  `width` receives the rank's output width (act columns with SILU_MUL).
+ttl_status col_setup(const char* who, const uint16_t* X, int64_t b, int64_t k, const uint16_t* W,
+                     int64_t n, ttl_weight_layout w_layout, int32_t t, int32_t rank,
+                     const ttl_col_split* split, ttl_epilogue epi, const uint16_t* Y,
+                     ttl::GemmParams& p, int64_t& out_width) {
   if (X == nullptr || W == nullptr || Y == nullptr)
     return fail(TTL_ERR_NULL, "%s: X, W and Y must be non-NULL", who);
   if (b <= 0 || k <= 0 || n <= 0 || b > kMaxDim || k > kMaxDim || n > kMaxDim)
@@ -80,7 +75,7 @@ ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k, const uint1
   if (sp.nseg < 1 || sp.nseg > TTL_MAX_SEGMENTS)
     return fail(TTL_ERR_UNSUPPORTED, "%s: nseg=%d must be 1..%d", who, sp.nseg, TTL_MAX_SEGMENTS);
 
-  ttl::GemmParams p = {};
+  p = {};
   int64_t sum = 0, n_r = 0, wcol0[TTL_MAX_SEGMENTS], width[TTL_MAX_SEGMENTS];
   for (int s = 0; s < sp.nseg; ++s) {
     const int64_t ns = sp.seg_n[s];
@@ -122,7 +117,6 @@ ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k, const uint1
   p.w_nk = w_layout == TTL_W_NK;
   p.ldb = p.w_nk ? k : n;
   p.b_rows = n;
-  p.C = Y;
   p.M = (int32_t)b;
   p.K = (int32_t)k;
   if (epi == TTL_EPI_SILU_MUL) {
@@ -131,13 +125,11 @@ ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k, const uint1
                   "%s: SiLU*up needs two equal segments (gate | up) with equal part counts", who);
     p.mode = 1;
     p.N = (int32_t)width[0];
-    p.ldc = width[0];
     p.gate_w0 = wcol0[0];
     p.up_w0 = wcol0[1];
   } else {
     p.mode = 0;
     p.N = (int32_t)n_r;
-    p.ldc = n_r;
     p.nseg = sp.nseg;
     int64_t out0 = 0;
     for (int s = 0; s < sp.nseg; ++s) {
@@ -147,10 +139,92 @@ ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k, const uint1
     }
     p.seg_out0[sp.nseg] = (int32_t)out0;
   }
-  if (b * (int64_t)p.N > kMaxOutput)
+  if (b * (int64_t)p.N * t > kMaxOutput)
     return fail(TTL_ERR_SHAPE, "%s: output of %lld x %d elements is too large", who, (long long)b, p.N);
+  out_width = p.N;
+  return TTL_OK;
+}
+
+
+// Validation and parameters of the reduction over rows [row0, row0 + rows) of P[t][b][n]; the
+// residual and the outputs hold exactly those rows.
+ttl_status reduce_setup(const char* who, const uint16_t* P, int32_t t, int64_t b, int64_t n,
+                        int64_t row0, int64_t rows, const uint16_t* residual, const uint16_t* gamma,
+                        float eps, uint16_t* residual_out, uint16_t* Y, ttl::ReduceNormParams& p) {
+  if (P == nullptr || gamma == nullptr || residual_out == nullptr || Y == nullptr)
+    return fail(TTL_ERR_NULL, "%s: P, gamma, residual_out and Y must be non-NULL", who);
+  if (t < 1) return fail(TTL_ERR_RANK, "%s: t=%d must be >= 1", who, t);
+  if (b <= 0 || n <= 0 || b > kMaxDim || n > 65536)
+    return fail(TTL_ERR_SHAPE, "%s: need 1 <= b < 2^31 and 1 <= n <= 65536 (b=%lld n=%lld)", who,
+                (long long)b, (long long)n);
+  if (!(eps >= 0.0f)) return fail(TTL_ERR_SHAPE, "%s: eps must be >= 0", who);
+  if (n % 8 != 0) return fail(TTL_ERR_ALIGN, "%s: n=%lld must be a multiple of 8", who, (long long)n);
+  if (!aligned16(P) || !aligned16(gamma) || !aligned16(residual_out) || !aligned16(Y) ||
+      (residual != nullptr && !aligned16(residual)))
+    return fail(TTL_ERR_ALIGN, "%s: all tensors must be 16-byte aligned", who);
+  const int64_t out_bytes = rows * n * 2;
+  const int64_t p_bytes = b * n * 2 * t;
+  if (overlaps(Y, out_bytes, P, p_bytes) || overlaps(Y, out_bytes, gamma, n * 2) ||
+      overlaps(Y, out_bytes, residual_out, out_bytes) ||
+      (residual != nullptr && overlaps(Y, out_bytes, residual, out_bytes)))
+    return fail(TTL_ERR_UNSUPPORTED, "%s: Y must not overlap any other tensor", who);
+  if (overlaps(residual_out, out_bytes, P, p_bytes) || overlaps(residual_out, out_bytes, gamma, n * 2) ||
+      (residual != nullptr && residual != residual_out &&
+       overlaps(residual_out, out_bytes, residual, out_bytes)))
+    return fail(TTL_ERR_UNSUPPORTED,
+                "%s: residual_out may alias residual exactly but must not overlap anything else", who);
+  p.P = P + row0 * n;
+  p.residual = residual;
+  p.gamma = gamma;
+  p.residual_out = residual_out;
+  p.Y = Y;
+  p.b = rows;
+  p.n = n;
+  p.plane = b * n;
+  p.t = t;
+  p.eps = eps;
+  return TTL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ttl_last_error(void) { return g_last_error.c_str(); }
+
+int32_t ttl_version(void) { return 100; }  // 0.1.0
+
+ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k, const uint16_t* W, int64_t n,
+                            ttl_weight_layout w_layout, int32_t t, int32_t rank,
+                            const ttl_col_split* split, ttl_epilogue epi, uint16_t* Y, void* stream) {
+  static const char* who = "shard_linear_col";
+  ttl::GemmParams p;
+  int64_t width = 0;
+  const ttl_status st = col_setup(who, X, b, k, W, n, w_layout, t, rank, split, epi, Y, p, width);
+  if (st != TTL_OK) return st;
+  p.C = Y;
+  p.ldc = width;
   return launch_status(ttl::launch_gemm(p, static_cast<hipStream_t>(stream)), who);
 }
+
+ttl_status shard_linear_col_gathered(const uint16_t* X, int64_t b, int64_t k, const uint16_t* W,
+                                     int64_t n, ttl_weight_layout w_layout, int32_t t, int32_t rank,
+                                     const ttl_col_split* split, ttl_epilogue epi, uint16_t* Y_all,
+                                     void* stream) {
+  static const char* who = "shard_linear_col_gathered";
+  ttl::GemmParams p;
+  int64_t width = 0;
+  const ttl_status st = col_setup(who, X, b, k, W, n, w_layout, t, rank, split, epi, Y_all, p, width);
+  if (st != TTL_OK) return st;
+  if (width * t > kMaxLda)
+    return fail(TTL_ERR_SHAPE, "%s: gathered row of %lld columns exceeds the supported pitch", who,
+                (long long)(width * t));
+  p.C = Y_all + (int64_t)rank * width;  // this rank's block of the gathered row
+  p.ldc = width * t;
+  return launch_status(ttl::launch_gemm(p, static_cast<hipStream_t>(stream)), who);
+}
+
+
 
 ttl_status shard_linear_row(const uint16_t* X, int64_t b, int64_t k, int32_t x_is_parallel,
                             const uint16_t* W, int64_t n, ttl_weight_layout w_layout, int32_t t,
@@ -207,38 +281,28 @@ ttl_status reduce_partials_rmsnorm(const uint16_t* P, int32_t t, int64_t b, int6
                                    const uint16_t* residual, const uint16_t* gamma, float eps,
                                    uint16_t* residual_out, uint16_t* Y, void* stream) {
   static const char* who = "reduce_partials_rmsnorm";
-  if (P == nullptr || gamma == nullptr || residual_out == nullptr || Y == nullptr)
-    return fail(TTL_ERR_NULL, "%s: P, gamma, residual_out and Y must be non-NULL", who);
-  if (t < 1) return fail(TTL_ERR_RANK, "%s: t=%d must be >= 1", who, t);
-  if (b <= 0 || n <= 0 || b > kMaxDim || n > 65536)
-    return fail(TTL_ERR_SHAPE, "%s: need 1 <= b < 2^31 and 1 <= n <= 65536 (b=%lld n=%lld)", who,
-                (long long)b, (long long)n);
-  if (!(eps >= 0.0f)) return fail(TTL_ERR_SHAPE, "%s: eps must be >= 0", who);
-  if (n % 8 != 0) return fail(TTL_ERR_ALIGN, "%s: n=%lld must be a multiple of 8", who, (long long)n);
-  if (!aligned16(P) || !aligned16(gamma) || !aligned16(residual_out) || !aligned16(Y) ||
-      (residual != nullptr && !aligned16(residual)))
-    return fail(TTL_ERR_ALIGN, "%s: all tensors must be 16-byte aligned", who);
-  const int64_t row_bytes = b * n * 2;
-  const int64_t p_bytes = row_bytes * t;
-  if (overlaps(Y, row_bytes, P, p_bytes) || overlaps(Y, row_bytes, gamma, n * 2) ||
-      overlaps(Y, row_bytes, residual_out, row_bytes) ||
-      (residual != nullptr && overlaps(Y, row_bytes, residual, row_bytes)))
-    return fail(TTL_ERR_UNSUPPORTED, "%s: Y must not overlap any other tensor", who);
-  if (overlaps(residual_out, row_bytes, P, p_bytes) || overlaps(residual_out, row_bytes, gamma, n * 2) ||
-      (residual != nullptr && residual != residual_out && overlaps(residual_out, row_bytes, residual, row_bytes)))
-    return fail(TTL_ERR_UNSUPPORTED,
-                "%s: residual_out may alias residual exactly but must not overlap anything else", who);
-
   ttl::ReduceNormParams p;
-  p.P = P;
-  p.residual = residual;
-  p.gamma = gamma;
-  p.residual_out = residual_out;
-  p.Y = Y;
-  p.b = b;
-  p.n = n;
-  p.t = t;
-  p.eps = eps;
+  const ttl_status st =
+      reduce_setup(who, P, t, b, n, 0, b, residual, gamma, eps, residual_out, Y, p);
+  if (st != TTL_OK) return st;
+  return launch_status(ttl::launch_reduce_rmsnorm(p, static_cast<hipStream_t>(stream)), who);
+}
+
+ttl_status reduce_scatter_partials_rmsnorm(const uint16_t* P, int32_t t, int64_t b, int64_t n,
+                                           int32_t rank, const uint16_t* residual,
+                                           const uint16_t* gamma, float eps, uint16_t* residual_out,
+                                           uint16_t* Y, void* stream) {
+  static const char* who = "reduce_scatter_partials_rmsnorm";
+  if (t < 1 || rank < 0 || rank >= t)
+    return fail(TTL_ERR_RANK, "%s: need t >= 1 and 0 <= rank < t (t=%d rank=%d)", who, t, rank);
+  if (b > 0 && b % t != 0)
+    return fail(TTL_ERR_NOT_DIVISIBLE, "%s: b=%lld rows are not divisible by t=%d", who,
+                (long long)b, t);
+  const int64_t rows = b / t;
+  ttl::ReduceNormParams p;
+  const ttl_status st = reduce_setup(who, P, t, b, n, (int64_t)rank * rows, rows, residual, gamma, eps,
+                                     residual_out, Y, p);
+  if (st != TTL_OK) return st;
   return launch_status(ttl::launch_reduce_rmsnorm(p, static_cast<hipStream_t>(stream)), who);
 }
 

@@ -30,7 +30,8 @@ EPI_SILU_MUL = 1
 W_KN = 0  # weight stored [k][n] (row stride n)
 W_NK = 1  # weight stored transposed, [n][k] (row stride k), as PyTorch-style Linear weights are
 MAX_SEGMENTS = 3
-EXPORTED = ("shard_linear_col", "shard_linear_row", "reduce_partials_rmsnorm", "ttl_last_error",
+EXPORTED = ("shard_linear_col", "shard_linear_col_gathered", "shard_linear_row",
+            "reduce_partials_rmsnorm", "reduce_scatter_partials_rmsnorm", "ttl_last_error",
             "ttl_version")
 
 
@@ -45,6 +46,8 @@ _lib.shard_linear_col.restype = ctypes.c_int32
 _lib.shard_linear_col.argtypes = [_c_u16p, ctypes.c_int64, ctypes.c_int64, _c_u16p, ctypes.c_int64,
                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                   ctypes.POINTER(ColSplit), ctypes.c_int32, _c_u16p, ctypes.c_void_p]
+_lib.shard_linear_col_gathered.restype = ctypes.c_int32
+_lib.shard_linear_col_gathered.argtypes = _lib.shard_linear_col.argtypes
 _lib.shard_linear_row.restype = ctypes.c_int32
 _lib.shard_linear_row.argtypes = [_c_u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, _c_u16p,
                                   ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -53,6 +56,10 @@ _lib.reduce_partials_rmsnorm.restype = ctypes.c_int32
 _lib.reduce_partials_rmsnorm.argtypes = [_c_u16p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                          _c_u16p, _c_u16p, ctypes.c_float, _c_u16p, _c_u16p,
                                          ctypes.c_void_p]
+_lib.reduce_scatter_partials_rmsnorm.restype = ctypes.c_int32
+_lib.reduce_scatter_partials_rmsnorm.argtypes = [_c_u16p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                                 ctypes.c_int32, _c_u16p, _c_u16p, ctypes.c_float,
+                                                 _c_u16p, _c_u16p, ctypes.c_void_p]
 _lib.ttl_last_error.restype = ctypes.c_char_p
 _lib.ttl_last_error.argtypes = []
 _lib.ttl_version.restype = ctypes.c_int32
@@ -162,6 +169,26 @@ def shard_linear_col(X: torch.Tensor, W: torch.Tensor, t: int, rank: int,
     return Y
 
 
+def shard_linear_col_gathered(X: torch.Tensor, W: torch.Tensor, t: int, rank: int,
+                              split: Optional[ColSplit] = None, epi: int = EPI_NONE,
+                              Y_all: Optional[torch.Tensor] = None, stream=None,
+                              w_layout: int = W_KN) -> torch.Tensor:
+    """Like shard_linear_col with gather_output=True: writes the rank's output into its column block
+    [rank*w, (rank+1)*w) of the all-gathered Y_all[b, t*w]."""
+    b, k = X.shape
+    kw, n = _weight_dims(W, w_layout)
+    if kw != k:
+        raise ValueError(f"X is [{b},{k}] but W is {tuple(W.shape)} (layout {w_layout})")
+    width = split_width(split, n, t) if t >= 1 else 0
+    ncols = width // 2 if epi == EPI_SILU_MUL else width
+    if Y_all is None:
+        Y_all = torch.empty((b, max(ncols * t, 0)), dtype=torch.bfloat16, device=X.device)
+    _check(_lib.shard_linear_col_gathered(_dev_ptr(X, "X"), b, k, _dev_ptr(W, "W"), n, w_layout, t, rank,
+                                          ctypes.byref(split) if split is not None else None, epi,
+                                          _dev_ptr(Y_all, "Y_all"), _stream_handle(stream)))
+    return Y_all
+
+
 def shard_linear_row(X: torch.Tensor, W: torch.Tensor, t: int, rank: int,
                      x_is_parallel: bool = True, P: Optional[torch.Tensor] = None,
                      stream=None, w_layout: int = W_KN) -> torch.Tensor:
@@ -191,6 +218,26 @@ def reduce_partials_rmsnorm(P: torch.Tensor, gamma: torch.Tensor, eps: float,
                                         _dev_ptr(gamma, "gamma"), float(eps),
                                         _dev_ptr(residual_out, "residual_out"), _dev_ptr(Y, "Y"),
                                         _stream_handle(stream)))
+    return residual_out, Y
+
+
+def reduce_scatter_partials_rmsnorm(P: torch.Tensor, gamma: torch.Tensor, eps: float, rank: int,
+                                    residual: Optional[torch.Tensor] = None,
+                                    residual_out: Optional[torch.Tensor] = None,
+                                    Y: Optional[torch.Tensor] = None,
+                                    stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Sequence-parallel reduction: rank `rank`'s chunk of b/t rows of the sum of P[t,b,n] + its
+    residual shard, then RMSNorm; returns (residual_out, Y), each [b/t, n]."""
+    t, b, n = P.shape
+    rows = b // t if t > 0 else 0
+    if residual_out is None:
+        residual_out = torch.empty((rows, n), dtype=torch.bfloat16, device=P.device)
+    if Y is None:
+        Y = torch.empty((rows, n), dtype=torch.bfloat16, device=P.device)
+    _check(_lib.reduce_scatter_partials_rmsnorm(_dev_ptr(P, "P"), t, b, n, rank,
+                                                _dev_ptr(residual, "residual"), _dev_ptr(gamma, "gamma"),
+                                                float(eps), _dev_ptr(residual_out, "residual_out"),
+                                                _dev_ptr(Y, "Y"), _stream_handle(stream)))
     return residual_out, Y
 
 

@@ -59,6 +59,15 @@ def _col(X=A, b=16, k=256, W=B, n=1376, t=2, rank=0, split=None, epi=0, Y=C, lay
     return ttl.lib().shard_linear_col(X, b, k, W, n, lay, t, rank, sp, epi, Y, None)
 
 
+def _colg(X=A, b=16, k=256, W=B, n=1376, t=2, rank=0, split=None, epi=0, Y=C, lay=0):
+    sp = None if split is None else ttl.ctypes.byref(split)
+    return ttl.lib().shard_linear_col_gathered(X, b, k, W, n, lay, t, rank, sp, epi, Y, None)
+
+
+def _rs(P=A, t=2, b=16, n=256, rank=0, R=B, gamma=D, eps=1e-5, Rout=B, Y=C):
+    return ttl.lib().reduce_scatter_partials_rmsnorm(P, t, b, n, rank, R, gamma, eps, Rout, Y, None)
+
+
 def _row(X=A, b=16, k=688, par=1, W=B, n=256, t=2, rank=0, P=C, lay=0):
     return ttl.lib().shard_linear_row(X, b, k, par, W, n, lay, t, rank, P, None)
 
@@ -87,6 +96,11 @@ def _red(P=A, t=2, b=16, n=256, R=B, gamma=D, eps=1e-5, Rout=B, Y=C):
     (lambda: _col(epi=7), ttl.ERR_UNSUPPORTED, "epilogue"),
     (lambda: _col(lay=2), ttl.ERR_UNSUPPORTED, "weight layout"),
     (lambda: _col(k=16384, n=65536, lay=1), ttl.ERR_UNSUPPORTED, "2 GiB"),
+    (lambda: _colg(Y=None), ttl.ERR_NULL, "non-NULL"),
+    (lambda: _colg(rank=2), ttl.ERR_RANK, "rank=2"),
+    (lambda: _colg(n=1370, t=4), ttl.ERR_NOT_DIVISIBLE, "not divisible"),
+    (lambda: _colg(epi=1), ttl.ERR_UNSUPPORTED, "two equal segments"),
+    (lambda: _colg(k=252), ttl.ERR_ALIGN, "multiples of 8"),
     (lambda: _row(lay=-1), ttl.ERR_UNSUPPORTED, "weight layout"),
     (lambda: _row(P=None), ttl.ERR_NULL, "non-NULL"),
     (lambda: _row(n=0), ttl.ERR_SHAPE, ""),
@@ -105,6 +119,13 @@ def _red(P=A, t=2, b=16, n=256, R=B, gamma=D, eps=1e-5, Rout=B, Y=C):
     (lambda: _red(Y=A + 16), ttl.ERR_UNSUPPORTED, "overlap"),
     (lambda: _red(Rout=A), ttl.ERR_UNSUPPORTED, "alias"),
     (lambda: _red(R=B, Rout=B + 16), ttl.ERR_UNSUPPORTED, "alias"),
+    (lambda: _rs(P=None), ttl.ERR_NULL, ""),
+    (lambda: _rs(rank=2), ttl.ERR_RANK, "rank=2"),
+    (lambda: _rs(rank=-1), ttl.ERR_RANK, ""),
+    (lambda: _rs(b=15), ttl.ERR_NOT_DIVISIBLE, "not divisible by t=2"),
+    (lambda: _rs(n=65544), ttl.ERR_SHAPE, "65536"),
+    (lambda: _rs(n=252), ttl.ERR_ALIGN, "multiple of 8"),
+    (lambda: _rs(Y=A + 16), ttl.ERR_UNSUPPORTED, "overlap"),
 ], ids=lambda v: v if isinstance(v, (int, str)) else "")
 def test_validation_rejects_before_launch(call, status, needle):
     got = call()

@@ -298,10 +298,65 @@ def pin_chain_composition():
     np.testing.assert_allclose(P2[1], oracle.row_shard(acts2_s[1], Wd, t, 1, True), rtol=0, atol=0)
 
 
+def pin_gathered_columns():
+    # gather_output=True: the rank outputs concatenated in rank order.  Plain split: equals the
+    # unsharded X @ W, checked element by element against fsum dot products; SiLU·up: equals the
+    # full silu(X Wg) * (X Wu) by its closed form.
+    b, k, n, t = 3, 24, 32, 4
+    X, Xl = _bf16((b, k), 61)
+    W, Wl = _bf16((k, n), 62, std=0.5)
+    G = oracle.col_gathered(X, W, oracle.plain_split(n, t), t)
+    assert G.shape == (b, n)
+    for a in range(b):
+        for c in range(n):
+            ref = _fsum_dot(Xl[a], Wl, c, range(k))
+            assert abs(G[a, c] - ref) <= _fp64_bound(Xl[a], Wl, c, range(k))
+    I = 16
+    Wgu, Wgul = _bf16((k, 2 * I), 63, std=0.3)
+    A = oracle.col_gathered(X, Wgu, oracle.merged_gate_up_split(I, t), t, epi_silu_mul=True)
+    assert A.shape == (b, I)
+    for a in range(b):
+        for j in range(I):
+            g = _fsum_dot(Xl[a], Wgul, j, range(k))
+            u = _fsum_dot(Xl[a], Wgul, I + j, range(k))
+            want = g / (1.0 + math.exp(-g)) * u
+            assert abs(A[a, j] - want) <= 1e-12 * (1 + abs(want))
+    # rank order matters: block r is rank r's own output
+    sp = oracle.plain_split(n, t)
+    for r in range(t):
+        np.testing.assert_array_equal(G[:, r * n // t:(r + 1) * n // t], oracle.col_shard(X, W, sp, t, r))
+
+
+def pin_reduce_scatter_chunks():
+    # The t reduce-scatter calls produce the full reduction's rows, chunk by chunk; each chunk is
+    # also checked by brute force (fsum over ranks, residual shard, closed-form RMSNorm).
+    t, b, n = 4, 8, 16
+    P, Pl = _bf16((t, b, n), 71)
+    R, Rl = _bf16((b, n), 72)
+    gamma, gl = _bf16((n,), 73, mean=1.0, std=0.1)
+    h_full, y_full = oracle.reduce_partials_rmsnorm(P, R, gamma, 1e-5)
+    rows = b // t
+    for r in range(t):
+        h, y = oracle.reduce_scatter_partials_rmsnorm(P, R[r * rows:(r + 1) * rows], gamma, 1e-5, t, r)
+        assert h.shape == (rows, n)
+        np.testing.assert_array_equal(h, h_full[r * rows:(r + 1) * rows])
+        np.testing.assert_array_equal(y, y_full[r * rows:(r + 1) * rows])
+        for i in range(rows):
+            a = r * rows + i
+            hr = [math.fsum([Pl[q][a][j] for q in range(t)] + [Rl[a][j]]) for j in range(n)]
+            ms = math.fsum(v * v for v in hr) / n
+            for j in range(n):
+                assert abs(h[i, j] - hr[j]) <= 1e-14 * (1 + abs(hr[j]))
+                want = hr[j] / math.sqrt(ms + 1e-5) * gl[j]
+                assert abs(y[i, j] - want) <= 1e-13 * (1 + abs(want))
+    with pytest.raises(ValueError):
+        oracle.reduce_scatter_partials_rmsnorm(np.zeros((4, 6, 8)), None, np.ones(8), 1e-5, 4, 0)
+
+
 PINS = [pin_decode, pin_rounding_vs_torch, pin_rounding_ties, pin_col_brute_force,
         pin_col_concat_invariant, pin_row_brute_force, pin_row_sum_invariant, pin_silu_closed_forms,
         pin_silu_mul, pin_rmsnorm_closed_forms, pin_reduce_residual, pin_head_arithmetic_golden,
-        pin_divisibility, pin_chain_composition]
+        pin_divisibility, pin_chain_composition, pin_gathered_columns, pin_reduce_scatter_chunks]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -400,6 +455,20 @@ def _mut_decode_shift(orig):
     return f
 
 
+def _mut_gather_reversed(orig):
+    def bad(X, W, split, t, epi_silu_mul=False):
+        y = orig(X, W, split, t, epi_silu_mul)
+        w = y.shape[-1] // t
+        return np.concatenate([y[:, r * w:(r + 1) * w] for r in reversed(range(t))], axis=-1)
+    return bad
+
+
+def _mut_scatter_wrong_chunk(orig):
+    def bad(P, residual_shard, gamma, eps, t, rank):
+        return orig(P, residual_shard, gamma, eps, t, (rank + 1) % t)
+    return bad
+
+
 MUTANTS = [
     ("rank_columns", _mut_rank_offset),
     ("merged_gate_up_split", _mut_gate_up_contiguous),
@@ -413,6 +482,8 @@ MUTANTS = [
     ("round_bf16", _mut_round_truncate),
     ("qkv_split", _mut_kv_replica),
     ("bf16_bits_to_f64", _mut_decode_shift),
+    ("col_gathered", _mut_gather_reversed),
+    ("reduce_scatter_partials_rmsnorm", _mut_scatter_wrong_chunk),
 ]
 
 

@@ -258,3 +258,68 @@ def test_tiny_mlp_chain_all_ranks(ttl):
     full = (oracle.silu(o["X"] @ o["Wgu"][:, :w.intermediate]) * (o["X"] @ o["Wgu"][:, w.intermediate:])) @ o["Wd"]
     psum = from_gpu(P).sum(0)
     assert_close(psum, full, "tiny sum of partials vs unsharded MLP")
+
+
+# ---- gather_output=True and the sequence-parallel reduction ---------------------------------------
+
+@pytest.mark.parametrize("case", ["plain", "silu", "qkv"])
+@LAYOUTS
+def test_col_gathered(ttl, gemm_path, case, layout):
+    """Every simulated rank writes its block of the all-gathered output; together they equal the
+    oracle's gathered result (for a plain split: X @ W)."""
+    b, k, t = 70, 512, 4
+    if case == "plain":
+        n, sp_o, sp_c, epi = 1056, oracle.plain_split(1056, t), None, ttl.EPI_NONE
+    elif case == "silu":
+        I = 688 * 2
+        n, sp_o, sp_c, epi = 2 * I, oracle.merged_gate_up_split(I, t), ttl.merged_gate_up_split(I, t), ttl.EPI_SILU_MUL
+    else:
+        sp_o, sp_c, epi = oracle.qkv_split(16, 2, 32, t), ttl.qkv_split(16, 2, 32, t), ttl.EPI_NONE
+        n = sum(sp_o[0])
+    X = wl.random_bf16((b, k), 140)
+    W = wl.random_bf16((k, n), 141, std=0.05)
+    Xd = gpu(X)
+    Wd_, lay = _stored(ttl, W, layout)
+    width = ttl.split_width(sp_c, n, t) // (2 if epi == ttl.EPI_SILU_MUL else 1)
+    # sentinel fill: a rank's call must touch its own block only
+    Y = torch.full((b, t * width), float("nan"), dtype=torch.bfloat16, device="cuda")
+    for r in range(t):
+        ttl.shard_linear_col_gathered(Xd, Wd_, t, r, sp_c, epi, Y_all=Y, w_layout=lay)
+        torch.cuda.synchronize()
+        done = Y[:, : (r + 1) * width]
+        assert not torch.isnan(done).any(), f"rank {r} left part of its block unwritten"
+        if r + 1 < t:
+            assert torch.isnan(Y[:, (r + 1) * width:]).all(), f"rank {r} wrote outside its block"
+        # the gathered block is the plain column output of the same rank, bit for bit
+        single = ttl.shard_linear_col(Xd, Wd_, t, r, sp_c, epi, w_layout=lay)
+        assert torch.equal(Y[:, r * width:(r + 1) * width], single)
+    ref = oracle.col_gathered(f64(X), f64(W), sp_o, t, epi_silu_mul=(epi == ttl.EPI_SILU_MUL))
+    assert_close(from_gpu(Y), ref, f"gathered {case} {layout} {gemm_path}")
+
+
+@pytest.mark.parametrize("t,b,n,with_residual", [(2, 16, 256, True), (4, 2048, 4096, True),
+                                                  (8, 64, 8192, True), (8, 8, 1024, False),
+                                                  (3, 9, 4104, True)])
+def test_reduce_scatter_rmsnorm(ttl, t, b, n, with_residual):
+    """Each rank reduces and normalises its b/t rows; the chunks together are the full reduction."""
+    P = wl.random_bf16((t, b, n), 150 + n)
+    R = wl.random_bf16((b, n), 151 + n) if with_residual else None
+    gamma = wl.random_bf16((n,), 152 + n, mean=1.0, std=0.1)
+    Pd, gd = gpu(P), gpu(gamma)
+    rows = b // t
+    Ro = f64(R) if with_residual else None
+    for r in range(t):
+        Rs = gpu(R[r * rows:(r + 1) * rows].contiguous()) if with_residual else None
+        rout, y = ttl.reduce_scatter_partials_rmsnorm(Pd, gd, 1e-5, r, Rs)
+        assert rout.shape == (rows, n) and y.shape == (rows, n)
+        Rr = Ro[r * rows:(r + 1) * rows] if with_residual else None
+        h, yref = oracle.reduce_scatter_partials_rmsnorm(f64(P), Rr, f64(gamma), 1e-5, t, r)
+        assert_close(from_gpu(rout), h, f"reduce-scatter residual_out t={t} b={b} n={n} r={r}")
+        assert_close(from_gpu(y), yref, f"reduce-scatter y t={t} b={b} n={n} r={r}")
+
+
+def test_reduce_scatter_rejects_ragged_rows(ttl):
+    P = torch.zeros((4, 6, 8), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ttl.TTLError) as e:
+        ttl.reduce_scatter_partials_rmsnorm(P, torch.ones(8, dtype=torch.bfloat16, device="cuda"), 1e-5, 0)
+    assert e.value.status == ttl.ERR_NOT_DIVISIBLE
