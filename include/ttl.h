@@ -67,7 +67,8 @@ typedef int32_t ttl_epilogue;
  *   TTL_W_KN: row-major [k][n], row stride n — the statement's own layout;
  *   TTL_W_NK: the transpose stored row-major, [n][k], row stride k — how PyTorch-style Linear
  *             weights ([out_features, in_features]) are kept; the matrix cores read it without a
- *             transpose.  Its byte extent must stay below 2 GiB. */
+ *             transpose.  The rows one call reads (from the rank's first to its last weight
+ *             column; for the row-parallel call all n rows) must span less than 2 GiB. */
 typedef int32_t ttl_weight_layout;
 #define TTL_W_KN 0
 #define TTL_W_NK 1
@@ -106,7 +107,7 @@ typedef struct {
  * Errors: NULL X/W/Y -> NULL; b,k,n <= 0 -> SHAPE; bad t/rank -> RANK; a segment width not
  * divisible by its part count, part count neither t nor a divisor of t, or widths not summing to n
  * -> NOT_DIVISIBLE; misalignment -> ALIGN; SILU_MUL with an unsuitable split, nseg outside 1..3, an
- * unknown w_layout or a TTL_W_NK weight of 2 GiB or more -> UNSUPPORTED.
+ * unknown w_layout, or TTL_W_NK rows read spanning 2 GiB or more -> UNSUPPORTED.
  */
 ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k,
                             const uint16_t* W, int64_t n, ttl_weight_layout w_layout,

@@ -37,7 +37,7 @@ constexpr int64_t kMaxLda = (int64_t)1 << 21;
 constexpr int64_t kMaxLdb = (int64_t)1 << 23;
 // Output elements of one GEMM (keeps every tile and workgroup count far inside 32 bits).
 constexpr int64_t kMaxOutput = (int64_t)1 << 40;
-// A [n][k] weight is addressed with 32-bit byte offsets from its base.
+// [n][k] weight rows are addressed with 32-bit byte offsets from the first row read.
 constexpr int64_t kMaxNkBytes = (int64_t)0x7FFFFFF0 - 16;
 
 ttl_status launch_status(hipError_t e, const char* who) {
@@ -108,15 +108,29 @@ ttl_status col_setup(const char* who, const uint16_t* X, int64_t b, int64_t k, c
   if (k > kMaxLda || n > kMaxLdb)
     return fail(TTL_ERR_SHAPE, "%s: k=%lld or n=%lld exceeds the supported row pitch", who,
                 (long long)k, (long long)n);
-  if (w_layout == TTL_W_NK && n * k * 2 >= kMaxNkBytes)
-    return fail(TTL_ERR_UNSUPPORTED, "%s: a [n][k] weight must stay below 2 GiB", who);
+  // A [n][k] weight is addressed from the first row the rank reads, with 32-bit byte offsets: the
+  // rows between the rank's first and last weight column must span less than 2 GiB (the whole
+  // weight may be larger, e.g. a vocabulary-sized LM head).
+  int64_t row_lo = 0, row_hi = n;
+  if (w_layout == TTL_W_NK) {
+    row_lo = wcol0[0];
+    row_hi = wcol0[0] + width[0];
+    for (int s = 1; s < sp.nseg; ++s) {
+      row_lo = wcol0[s] < row_lo ? wcol0[s] : row_lo;
+      row_hi = wcol0[s] + width[s] > row_hi ? wcol0[s] + width[s] : row_hi;
+    }
+    if ((row_hi - row_lo) * k * 2 >= kMaxNkBytes)
+      return fail(TTL_ERR_UNSUPPORTED,
+                  "%s: the [n][k] rows this rank reads must span less than 2 GiB", who);
+    for (int s = 0; s < sp.nseg; ++s) wcol0[s] -= row_lo;
+  }
 
   p.A = X;
   p.lda = k;
-  p.B = W;
   p.w_nk = w_layout == TTL_W_NK;
+  p.B = p.w_nk ? W + row_lo * k : W;
   p.ldb = p.w_nk ? k : n;
-  p.b_rows = n;
+  p.b_rows = row_hi - row_lo;
   p.M = (int32_t)b;
   p.K = (int32_t)k;
   if (epi == TTL_EPI_SILU_MUL) {

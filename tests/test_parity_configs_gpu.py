@@ -164,19 +164,26 @@ def test_decoder_layer_70b_tp8(ttl, layout):
 
 
 @pytest.mark.parametrize("b", [64, 2048])
-def test_vocab_parallel_lm_head_70b_tp8(ttl, b):
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+def test_vocab_parallel_lm_head_70b_tp8(ttl, b, layout):
     """Vocab-parallel LM head ("Tensor Parallelism" manual, section "Vocab Parallel"): the column
     GEMM over Llama-3's 128256-token vocabulary at hidden 8192, t = 8 (16032 logits per rank),
     gathered into the full logits row.  Ranks 0 and 7 are checked against the oracle on sampled
-    rows; every rank's gathered block equals its own column output bit for bit."""
+    rows; every rank's gathered block equals its own column output bit for bit.  Stored [n][k] the
+    weight is 2.1 GB, beyond 32-bit offsets from its base; each rank's rows (263 MB) are within
+    them."""
     hidden, vocab, t = 8192, 128256, 8
     g = torch.Generator(device="cuda").manual_seed(0)
     X = torch.randn(b, hidden, device="cuda", generator=g).to(torch.bfloat16)
     W = (torch.randn(hidden, vocab, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    lay = ttl.W_KN
+    Ws = W
+    if layout == "nk":
+        lay, Ws = ttl.W_NK, W.t().contiguous()
     width = vocab // t
     logits = torch.empty((b, vocab), dtype=torch.bfloat16, device="cuda")
     for r in range(t):
-        ttl.shard_linear_col_gathered(X, W, t, r, Y_all=logits)
+        ttl.shard_linear_col_gathered(X, Ws, t, r, Y_all=logits, w_layout=lay)
     torch.cuda.synchronize()
     rows = sample_rows(b)
     Xh = f64(X[rows].cpu())
@@ -184,11 +191,11 @@ def test_vocab_parallel_lm_head_70b_tp8(ttl, b):
     for r in (0, t - 1):
         cols = slice(r * width, (r + 1) * width)
         Wr = f64(W[:, cols].cpu())
-        own = ttl.shard_linear_col(X, W, t, r)
+        own = ttl.shard_linear_col(X, Ws, t, r, w_layout=lay)
         torch.cuda.synchronize()
         assert torch.equal(logits[:, cols], own)
         ref = oracle.col_shard(Xh, Wr, oracle.plain_split(width, 1), 1, 0)
         assert_close(from_gpu(logits[rows][:, cols]), ref, f"LM head b={b} rank {r}")
-    del W, logits
+    del W, Ws, logits
     gc.collect()
     torch.cuda.empty_cache()
