@@ -84,6 +84,10 @@ def parse():
     ap.add_argument("--steady-state", action="store_true",
                     help="only run each b=4096 GEMM (ours and hipBLASLt's) back to back for 2 s, sample "
                          "power and clock, time 30 launches, print one JSON line per GEMM and exit")
+    ap.add_argument("--config-table", action="store_true",
+                    help="only time every kernel of one rank's step for each of the five workloads "
+                         "(tiny MLP, 8B MLP b=1/32/256, 8B attention, 70B MLP b=4096/64, 70B layer), "
+                         "print one JSON line per workload and exit")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (5 times) and exit: the "
                          "reference for scaling HBM traffic counters")
@@ -196,6 +200,150 @@ def yardstick(torch, w, layout):
         out[name] = {"us": us, "tflops": 2.0 * M * K * N / (us * 1e6)}
         del X, Ws
     return {"library": "torch.matmul (hipBLASLt)", "weight_storage": layout, "shapes": out}
+
+
+RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+
+
+def _time_chain(torch, ops, reps, warmup, cycle):
+    """ops: list of (name, fn(rank), flops, bytes).  Runs the chain `reps` times (rank cycling through
+    0..cycle-1 when cycle > 1, else rank 0) with HIP events recorded between the launches on the
+    launching stream; returns {name: average microseconds}."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        for _, fn, _, _ in ops:
+            fn(i % cycle)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(reps)]
+    for i in range(reps):
+        evs[i][0].record(stream)
+        for j, (_, fn, _, _) in enumerate(ops):
+            fn(i % cycle)
+            evs[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    return {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / reps * 1e3
+            for j, (name, _, _, _) in enumerate(ops)}
+
+
+def config_table(ttl, torch, layout, reps=20, warmup=3):
+    """Every kernel of one rank's step for each workload, one JSON line each.  Decode-size batches
+    (b < 512) cycle the simulated rank from repetition to repetition so that the weight slices are
+    not served from the Infinity Cache."""
+    from tensor_transformer_linear_amd import workloads as wl
+    lay = ttl.W_NK if layout == "nk" else ttl.W_KN
+    dev = "cuda"
+
+    def stored(W):
+        return W.t().contiguous() if lay == ttl.W_NK else W
+
+    def col_op(name, X, W, split, epi, Y, t, n_w, n_out):
+        b, k = X.shape
+        return (name, lambda r: ttl.shard_linear_col(X, W, t, r, split, epi, Y=Y, w_layout=lay),
+                gemm_flops(b, k, n_w), 2.0 * (b * k + k * n_w + b * n_out))
+
+    def row_op(name, X, W, P, t, k, n, parallel):
+        b = X.shape[0]
+        kr = k // t
+        return (name, lambda r: ttl.shard_linear_row(X, W, t, r, parallel, P=P[r], w_layout=lay),
+                gemm_flops(b, kr, n), 2.0 * (b * kr + kr * n + b * n))
+
+    def red_op(name, P, gamma, eps, R, rout, y):
+        t, b, n = P.shape
+        return (name, lambda r: ttl.reduce_partials_rmsnorm(P, gamma, eps, R, residual_out=rout, Y=y),
+                0.0, reduce_bytes(t, b, n))
+
+    def graph_step_us(ops, cycle, replays=10):
+        """The chain for ranks 0..cycle-1 captured once into a HIP graph and replayed: the step time
+        without host launch overhead (small shapes are otherwise bound by the launch rate)."""
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for r in range(cycle):
+                    for _, fn, _, _ in ops:
+                        fn(r)
+        torch.cuda.current_stream().wait_stream(s)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (replays * cycle) * 1e3
+
+    def report(wname, b, t, us, ops, graph_us):
+        kern = {}
+        for name, _, fl, by in ops:
+            u = us[name]
+            tf, gbs = fl / (u * 1e6), by / (u * 1e3)
+            bound = "mfma" if fl / by > RIDGE_FLOP_PER_BYTE else "hbm"
+            kern[name] = {"us": u, "tflops": tf, "gbs": gbs, "bound": bound,
+                          "frac": tf / PEAK_BF16_TFLOPS if bound == "mfma" else gbs / PEAK_HBM_GBS}
+        print(json.dumps({"workload": wname, "tokens": b, "t": t, "weight_storage": layout,
+                          "step_us": sum(us.values()), "step_us_graph": graph_us, "kernels": kern}),
+              flush=True)
+
+    for w in (wl.TINY_MLP_T2, wl.LLAMA3_8B_MLP_TP8, wl.LLAMA3_70B_MLP_TP8):
+        for b in w.batches:
+            inp = wl.mlp_inputs(w, b, seed=0, device=dev)
+            t, H, I = w.t, w.hidden, w.intermediate
+            Ir = I // t
+            Wgu, Wd = stored(inp["Wgu"]), stored(inp["Wd"])
+            act = torch.empty((b, Ir), dtype=torch.bfloat16, device=dev)
+            P = torch.empty((t, b, H), dtype=torch.bfloat16, device=dev)
+            rout, y = torch.empty((b, H), dtype=torch.bfloat16, device=dev), torch.empty((b, H), dtype=torch.bfloat16, device=dev)
+            sp = ttl.merged_gate_up_split(I, t)
+            ops = [col_op("gate_up_silu", inp["X"], Wgu, sp, ttl.EPI_SILU_MUL, act, t, 2 * Ir, Ir),
+                   row_op("down", act, Wd, P, t, I, H, True),
+                   red_op("reduce_rmsnorm", P, inp["gamma"], w.eps, inp["R"], rout, y)]
+            for r in range(t):  # every rank's partial once
+                ops[0][1](r)
+                ops[1][1](r)
+            cyc = t if b < 512 else 1
+            report(w.name, b, t, _time_chain(torch, ops, reps, warmup, cyc), ops, graph_step_us(ops, cyc))
+            del inp, Wgu, Wd, act, P, rout, y, ops
+            torch.cuda.empty_cache()
+
+    for w in (wl.LLAMA3_8B_ATTN_TP4, wl.LLAMA3_70B_LAYER_TP8):
+        for b in w.batches:
+            is_layer = isinstance(w, wl.LayerShard)
+            inp = (wl.layer_inputs if is_layer else wl.attn_inputs)(w, b, seed=0, device=dev)
+            t, H = w.t, w.hidden
+            nq, nkv, hd = w.n_q_heads, w.n_kv_heads, w.head_dim
+            sp = ttl.qkv_split(nq, nkv, hd, t)
+            n_qkv = (nq + 2 * nkv) * hd
+            w_r = ttl.split_width(sp, n_qkv, t)
+            Wqkv, Wo = stored(inp["Wqkv"]), stored(inp["Wo"])
+            qkv = torch.empty((b, w_r), dtype=torch.bfloat16, device=dev)
+            Pa = torch.empty((t, b, H), dtype=torch.bfloat16, device=dev)
+            rout, y = torch.empty((b, H), dtype=torch.bfloat16, device=dev), torch.empty((b, H), dtype=torch.bfloat16, device=dev)
+            gamma = inp["gamma_attn"] if is_layer else inp["gamma"]
+            ops = [col_op("qkv", inp["X"], Wqkv, sp, ttl.EPI_NONE, qkv, t, w_r, w_r),
+                   row_op("o_proj", inp["A"], Wo, Pa, t, nq * hd, H, False),
+                   red_op("reduce_rmsnorm_attn", Pa, gamma, w.eps, inp["R"], rout, y)]
+            keep = [Wqkv, Wo, qkv, Pa, rout, y]
+            if is_layer:
+                I = w.intermediate
+                Ir = I // t
+                Wgu, Wd = stored(inp["Wgu"]), stored(inp["Wd"])
+                act = torch.empty((b, Ir), dtype=torch.bfloat16, device=dev)
+                Pm = torch.empty((t, b, H), dtype=torch.bfloat16, device=dev)
+                rout2, y2 = torch.empty((b, H), dtype=torch.bfloat16, device=dev), torch.empty((b, H), dtype=torch.bfloat16, device=dev)
+                gsp = ttl.merged_gate_up_split(I, t)
+                ops += [col_op("gate_up_silu", y, Wgu, gsp, ttl.EPI_SILU_MUL, act, t, 2 * Ir, Ir),
+                        row_op("down", act, Wd, Pm, t, I, H, True),
+                        red_op("reduce_rmsnorm_mlp", Pm, inp["gamma_mlp"], w.eps, rout, rout2, y2)]
+                keep += [Wgu, Wd, act, Pm, rout2, y2]
+            for r in range(t):  # every rank's partials once, in chain order
+                for _, fn, _, _ in ops:
+                    fn(r)
+            cyc = t if b < 512 else 1
+            report(w.name, b, t, _time_chain(torch, ops, reps, warmup, cyc), ops, graph_step_us(ops, cyc))
+            del inp, ops, keep
+            torch.cuda.empty_cache()
 
 
 def read_power_clock():
@@ -344,6 +492,9 @@ def main():
     w = wl.LLAMA3_70B_MLP_TP8
     if args.steady_state:
         steady_state(ttl, torch, w, args.layout)
+        return 0
+    if args.config_table:
+        config_table(ttl, torch, args.layout)
         return 0
     b = args.batch
     workload = f"llama3_70b_mlp_tp8_rank0_b{b}_{args.layout}"

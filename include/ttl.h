@@ -29,10 +29,12 @@
  *     must stay alive until the stream has run the work.
  *   - Workspace: GEMMs with few token rows (decode batches, small shards) are cut along k and need
  *     fp32 partial sums.  The library keeps one device buffer per GPU for them, allocated on the
- *     first such call (and grown, after waiting for the device, when a later call needs more); it
- *     lives until the process ends.  Calls whose work overlaps in time on one GPU (different
- *     streams) share it and race: serialise them on one stream.  A failed allocation is
- *     TTL_ERR_HIP.
+ *     first such call and replaced by a larger one when a later call needs more (the outgrown
+ *     buffer is kept, so work already enqueued or captured in a graph stays valid); buffers live
+ *     until the process ends.  The allocation cannot run inside a stream capture: make one eager
+ *     call of the shape before capturing it.  Calls whose work overlaps in time on one GPU
+ *     (different streams) share the buffer and race: serialise them on one stream.  A failed
+ *     allocation is TTL_ERR_HIP.
  *   - Errors: every call returns a ttl_status.  Arguments are validated synchronously before any
  *     launch; on a non-OK status nothing has been enqueued and ttl_last_error() returns a message
  *     (thread-local).  A launch failure reported by the runtime is TTL_ERR_HIP.  A fault inside a

@@ -8,8 +8,10 @@
 //
 // Workspace: split-K launches with more than one split write fp32 partial tiles that a second
 // kernel reduces.  The library keeps one device buffer per GPU for them, allocated (or grown) on
-// first need by the calling thread.  Launches that overlap in time on one GPU (different streams)
-// would share it and must not be issued; a launch that needs to grow it waits for the device first.
+// first need by the calling thread; allocation cannot happen inside a stream capture, so a graph
+// that captures such launches must be recorded after one eager call of the same (or a larger)
+// shape.  Launches that overlap in time on one GPU (different streams) would share the buffer and
+// must not be issued.
 //
 // Environment overrides, read at every launch (for tests and measurements):
 //   TTL_GEMM_KERNEL=tiled|splitk  use that kernel whatever the shape;
@@ -36,7 +38,9 @@ struct Workspace {
 std::mutex g_ws_mutex;
 std::vector<Workspace> g_ws;
 
-// Device buffer of at least `bytes` for this GPU.
+// Device buffer of at least `bytes` for this GPU.  A buffer that is outgrown is retired, not freed:
+// work already enqueued, or captured into a graph, keeps using it safely.  Growth at least doubles
+// the size, so few buffers are ever retired; all of them live until the process ends.
 hipError_t get_workspace(size_t bytes, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -45,16 +49,12 @@ hipError_t get_workspace(size_t bytes, void** out) {
   if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
   Workspace& w = g_ws[dev];
   if (w.bytes < bytes) {
-    if (w.ptr != nullptr) {
-      // Earlier launches may still read the old buffer.
-      if ((e = hipDeviceSynchronize()) != hipSuccess) return e;
-      if ((e = hipFree(w.ptr)) != hipSuccess) return e;
-      w.ptr = nullptr;
-      w.bytes = 0;
-    }
     const size_t mib = (size_t)1 << 20;
-    const size_t nb = (bytes + mib - 1) / mib * mib;
-    if ((e = hipMalloc(&w.ptr, nb)) != hipSuccess) return e;
+    size_t nb = (bytes + mib - 1) / mib * mib;
+    if (nb < 2 * w.bytes) nb = 2 * w.bytes;
+    void* ptr = nullptr;
+    if ((e = hipMalloc(&ptr, nb)) != hipSuccess) return e;
+    w.ptr = ptr;  // the previous buffer, if any, stays allocated
     w.bytes = nb;
   }
   *out = w.ptr;

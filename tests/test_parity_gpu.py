@@ -323,3 +323,63 @@ def test_reduce_scatter_rejects_ragged_rows(ttl):
     with pytest.raises(ttl.TTLError) as e:
         ttl.reduce_scatter_partials_rmsnorm(P, torch.ones(8, dtype=torch.bfloat16, device="cuda"), 1e-5, 0)
     assert e.value.status == ttl.ERR_NOT_DIVISIBLE
+
+
+# ---- stream capture -------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("b", [64, 600])
+def test_graph_replay_matches_eager(ttl, monkeypatch, b):
+    """The rank chain (gate_up + SiLU·up, down, reduce + RMSNorm over all ranks) captured into a HIP
+    graph and replayed three times, with eager work between the replays (including a split-K call
+    large enough to replace the library's workspace), reproduces the eager outputs bit for bit.
+    b = 64 runs the split-K kernel with its workspace, b = 600 the 256 x 256 tiles."""
+    monkeypatch.delenv("TTL_GEMM_KERNEL", raising=False)
+    monkeypatch.delenv("TTL_GEMM_SPLITS", raising=False)
+    if b == 600:
+        monkeypatch.setenv("TTL_GEMM_KERNEL", "tiled")
+    t, H, I = 4, 1024, 2048
+    X = gpu(wl.random_bf16((b, H), 160))
+    R = gpu(wl.random_bf16((b, H), 161))
+    gamma = gpu(wl.random_bf16((H,), 162, mean=1.0, std=0.1))
+    Wgu = gpu(wl.random_bf16((H, 2 * I), 163, std=0.05))
+    Wd = gpu(wl.random_bf16((I, H), 164, std=0.05))
+    sp = ttl.merged_gate_up_split(I, t)
+    act = torch.empty((t, b, I // t), dtype=torch.bfloat16, device="cuda")
+    P = torch.empty((t, b, H), dtype=torch.bfloat16, device="cuda")
+    rout = torch.empty((b, H), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((b, H), dtype=torch.bfloat16, device="cuda")
+
+    def chain():
+        for r in range(t):
+            ttl.shard_linear_col(X, Wgu, t, r, sp, ttl.EPI_SILU_MUL, Y=act[r])
+            ttl.shard_linear_row(act[r], Wd, t, r, True, P=P[r])
+        ttl.reduce_partials_rmsnorm(P, gamma, 1e-5, R, residual_out=rout, Y=y)
+
+    chain()  # eager; also allocates the workspace before capture
+    torch.cuda.synchronize()
+    want = [v.clone() for v in (act, P, rout, y)]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            chain()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    Xbig = gpu(wl.random_bf16((32, 8192), 165))
+    Wbig = gpu(wl.random_bf16((8192, 16384), 166, std=0.02))
+    for rep in range(3):
+        for v in (act, P, rout, y):
+            v.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, exp in zip((act, P, rout, y), want):
+            assert torch.equal(got, exp), f"replay {rep} differs from the eager run"
+        # eager work between replays: a split-K call whose workspace need (64 splits of 32 x 16384
+        # fp32 = 134 MB) exceeds every earlier one, so the library replaces its buffer
+        with monkeypatch.context() as m:
+            m.setenv("TTL_GEMM_KERNEL", "splitk")
+            m.setenv("TTL_GEMM_SPLITS", str(64 + rep))
+            Ybig = ttl.shard_linear_col(Xbig, Wbig, 1, 0)
+        torch.cuda.synchronize()
+        assert torch.isfinite(Ybig.float()).all()
