@@ -42,7 +42,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (8 TB/s)
 
 # Kernel sources whose HBM traffic counters are recorded under profiles/: the recorded figures
 # apply only while these files are unchanged.
-TRAFFIC_SOURCES = ("tensor_transformer_linear_amd/csrc/gemm_bf16.hip",
+TRAFFIC_SOURCES = ("tensor_transformer_linear_amd/csrc/gemm_bigwave.hip",
+                   "tensor_transformer_linear_amd/csrc/gemm_common.h",
                    "tensor_transformer_linear_amd/csrc/kernels.h")
 
 
@@ -426,6 +427,30 @@ def sample_power_clock(torch, step, seconds=2.0):
         return None
     return {"socket_power_w": pc[0], "gfx_clock_mhz_mean": pc[1],
             "sampled": "amd-smi metric -p -c --json, once, while the step repeated for %.1f s" % seconds}
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch recorded from the FETCH_SIZE / WRITE_SIZE counters in profiles/, or None
+    when no record exists or the kernel sources changed since the counters were taken."""
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    digest = h.hexdigest()
+    pat = re.compile(r"^traffic\s+kernel=(\S+)\s+workload=(\S+)\s+bytes_per_launch=(\d+)\s+"
+                     r"source_sha256=([0-9a-f]{64})\s*$")
+    pdir = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(pdir):
+        return None
+    for name in sorted(os.listdir(pdir)):
+        if not name.endswith((".md", ".txt")):
+            continue
+        with open(os.path.join(pdir, name)) as f:
+            for line in f:
+                m = pat.match(line.strip())
+                if m and m.group(1) == kernel and m.group(2) == workload and m.group(4) == digest:
+                    return float(m.group(3))
+    return None
 
 
 def cpu_baseline(torch, w, tensors, rows, seconds):

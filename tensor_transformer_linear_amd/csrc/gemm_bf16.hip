@@ -75,8 +75,6 @@ constexpr int kStageElems = kAElems + kBElems;
 constexpr int kACopies = kAElems * 2 / 1024 / kWaves;   // 1-KiB copies per wave per tile
 constexpr int kBCopies = kBElems * 2 / 1024 / kWaves;
 constexpr int kLoads = kACopies + kBCopies;             // vmcnt increments per wave per tile
-constexpr int kXcds = 8;                   // MI355X: 8 XCDs, workgroups dealt round-robin
-constexpr int kGroupM = 4;                 // row-tiles per L2 group
 
 constexpr int kChunks = kBK / 8;           // 16-B chunks per [rows][k] staged row
 constexpr int kRowsPer256 = 256 / (2 * kBK);  // staged rows per 256 B of LDS
@@ -86,42 +84,6 @@ constexpr int kKK = kBK / 16;              // k16 slices per stage
 static_assert(kBK == 32 || kBK == 64, "stage depth");
 static_assert(kStages >= 2 && kStages <= 5 && kStages * kStageElems * 2 <= 160 * 1024, "LDS ring");
 static_assert(kBCopies % 2 == 0, "[k][n] copies come in k-row-parity pairs");
-
-// Remap the block index so that the tiles one XCD runs form compact groups, then walk tiles in
-// groups of kGroupM row-tiles.  Both maps are bijections on [0, tiles).
-__device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int tiles = tiles_m * tiles_n;
-  const int q = tiles / kXcds, r = tiles % kXcds;
-  const int x = bid % kXcds, local = bid / kXcds;
-  const int L = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
-  const int per_group = kGroupM * tiles_n;
-  const int g = L / per_group;
-  const int first = g * kGroupM;
-  const int gsize = min(tiles_m - first, kGroupM);
-  const int inner = L - g * per_group;
-  tm = first + inner % gsize;
-  tn = inner / gsize;
-}
-
-// Weight column of tile column c (the first of 8 consecutive ones), and whether it is in range.
-template <int MODE>
-__device__ inline int64_t weight_column(const GemmParams& p, int n0, int c, bool& ok) {
-  if (MODE == kSiluMul) {
-    // Tile column c = w*kWN + nb*32 + j: blocks nb < kNI/2 of a wave hold gate columns and the
-    // others the up columns of the same act columns, so gate and up of one output meet in one lane.
-    const int w = c / kWN, nb = (c % kWN) / 32, j = c % 32;
-    const int act = n0 + w * (kWN / 2) + (nb % (kNI / 2)) * 32 + j;
-    ok = act < p.N;
-    return (nb < kNI / 2 ? p.gate_w0 : p.up_w0) + act;
-  }
-  const int oc = n0 + c;
-  ok = oc < p.N;
-  int64_t w0 = p.seg_w0[0];
-  int s0 = p.seg_out0[0];
-  if (p.nseg > 1 && oc >= p.seg_out0[1]) { w0 = p.seg_w0[1]; s0 = p.seg_out0[1]; }
-  if (p.nseg > 2 && oc >= p.seg_out0[2]) { w0 = p.seg_w0[2]; s0 = p.seg_out0[2]; }
-  return w0 + (oc - s0);
-}
 
 template <int MODE, bool WNK>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
@@ -163,7 +125,7 @@ void gemm_bf16_kernel(const GemmParams p) {
     if (WNK) {
       const int n = q * kRowsPerCopy + lane / kChunks;  // tile column = staged row
       const int chunk = (lane % kChunks) ^ ((n / kRowsPer256) % kChunks);
-      const int64_t wrow = weight_column<MODE>(p, n0, n & ~7, ok) + (n & 7);
+      const int64_t wrow = weight_column<MODE, kWN>(p, n0, n & ~7, ok) + (n & 7);
       b_off[i] = ok ? (uint32_t)((wrow * p.ldb + chunk * 8) * 2) : kOob;
       b_kc[i] = chunk * 8;
     } else {
@@ -171,7 +133,7 @@ void gemm_bf16_kernel(const GemmParams p) {
       // (l%32) ^ (4*(row%4)), row%4 = 2*(q%2) + l/32 = 2*(i%2) + l/32.
       const int krow = 2 * q + (lane >> 5);
       const int chunk = (lane & 31) ^ (4 * (2 * (i & 1) + (lane >> 5)));
-      const int64_t wcol = weight_column<MODE>(p, n0, chunk * 8, ok);
+      const int64_t wcol = weight_column<MODE, kWN>(p, n0, chunk * 8, ok);
       b_off[i] = ok ? (uint32_t)(((int64_t)krow * p.ldb + wcol) * 2) : kOob;
       b_kc[i] = krow;
     }
@@ -417,13 +379,13 @@ void gemm_pingpong_kernel(const GemmParams p) {
       if (WNK) {
         const int n = q * kRowsPerCopy + lane / kChunks;
         const int chunk = (lane % kChunks) ^ ((n / kRowsPer256) % kChunks);
-        const int64_t wrow = weight_column<MODE>(p, n0, n & ~7, ok) + (n & 7);
+        const int64_t wrow = weight_column<MODE, kWN>(p, n0, n & ~7, ok) + (n & 7);
         c_off[i] = ok ? (uint32_t)((wrow * p.ldb + chunk * 8) * 2) : kOob;
         c_k[i] = chunk * 8;
       } else {
         const int krow = 2 * q + (lane >> 5);
         const int chunk = (lane & 31) ^ (4 * (krow % 4));
-        const int64_t wcol = weight_column<MODE>(p, n0, chunk * 8, ok);
+        const int64_t wcol = weight_column<MODE, kWN>(p, n0, chunk * 8, ok);
         c_off[i] = ok ? (uint32_t)(((int64_t)krow * p.ldb + wcol) * 2) : kOob;
         c_k[i] = krow;
       }

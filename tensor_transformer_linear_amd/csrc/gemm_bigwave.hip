@@ -1,0 +1,317 @@
+// Tiled bf16 GEMM with one wave64 per SIMD: 256 x 256 tiles, four waves of 128 x 128 outputs each.
+//
+// C[M, N] = A[M, K] · B[K, map(N)] with the operands, column maps, LDS layouts and M/N tails of the
+// eight-wave kernel in gemm_bf16.hip; what differs is how the matrix cores are fed.  A wave owning
+// 128 x 128 outputs keeps 16 v_mfma_f32_32x32x16_bf16 accumulators (256 registers, in the
+// accumulation registers) and reads 4 A + 4 B fragments per 16 MFMAs: a third fewer LDS bytes per
+// product than the 128 x 64 waves of the eight-wave kernel.  With one wave per SIMD its
+// 512-register budget also holds the fragments of all four k16 slices of a k-tile, so LDS reads
+// can run two slices (~1000 cycles) ahead of their MFMAs.
+//
+// With no second wave on the SIMD to hide stalls, everything is placed explicitly (the order below
+// is pinned with scheduling barriers).  Per k-tile t and wave (4 slices of 16 MFMAs):
+//   slice 0: MFMAs of slice 0, with the LDS reads of slices 2 and 3 of tile t;
+//   slice 1: MFMAs of slice 1;
+//   barrier: the wave waits for its own copies of tile t+1, then the workgroup barrier publishes
+//            tile t+1 and certifies that every wave's reads of tile t have returned;
+//   slice 2: MFMAs, reads of slice 0 of tile t+1, and half of the direct-to-LDS copies of tile t+2
+//            (into tile t's stage, now free), one after every second MFMA;
+//   slice 3: MFMAs, reads of slice 1 of tile t+1, the other half of the copies.
+// The copies of a tile thus have until the next barrier (two slices and more) to land.  Measured
+// alternatives: a copy after every MFMA of one slice starves the wave's matrix core (the copies'
+// issue blocks it); copies spread over all four slices (B staged three-deep to allow it) or moved
+// before the barrier were slower; k-tiles of 32 with a five-stage ring were slower still (twice the
+// L2 requests for the same bytes).
+//
+// K must be a multiple of 64 (no k tail); the eight-wave kernel serves the other shapes.
+#include <type_traits>
+
+#include "gemm_common.h"
+
+namespace ttl {
+namespace {
+
+using namespace gemm;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kWM = 128, kWN = 128;      // outputs per wave (2 x 2 wave grid)
+constexpr int kMI = kWM / 32, kNI = kWN / 32;
+constexpr int kKK = kBK / 16;            // k16 slices per k-tile
+constexpr int kAElems = kBM * kBK, kBElems = kBK * kBN, kStageElems = kAElems + kBElems;
+constexpr int kACopies = kAElems * 2 / 1024 / kWaves;  // 1-KiB copies per wave per k-tile: 8
+constexpr int kBCopies = kBElems * 2 / 1024 / kWaves;  // 8
+constexpr int kCopies = kACopies + kBCopies;
+constexpr int kChunks = kBK / 8;         // 16-B chunks per staged [rows][k] row
+constexpr int kRowsPer256 = 256 / (2 * kBK);
+constexpr int kRowsPerCopy = 1024 / (2 * kBK);
+
+static_assert(kKK == 4 && kACopies == 8 && kBCopies == 8, "the slice schedule assumes these counts");
+
+template <int MODE, bool WNK>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+void gemm_bigwave_kernel(const GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * kStageElems];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / 2, wn = wave % 2;
+
+  int tile_m, tile_n;
+  tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tile_m, tile_n);
+  const int m0 = tile_m * kBM;
+  const int n0 = tile_n * (MODE == kSiluMul ? kBN / 2 : kBN);  // first output column of the tile
+  const int nk = p.K / kBK;
+  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds);
+
+  // ---- Copy offsets, fixed for the whole k loop (the descriptors move with k0).  Copy i < 8 of
+  // this wave moves block 8*wave + i of the A stage, copy 8 + i block 8*wave + i of the B stage.
+  uint32_t c_off[kCopies];
+#pragma unroll
+  for (int i = 0; i < kACopies; ++i) {
+    // [256 rows][64 k]: block q holds rows 8q .. 8q+7; lane l lands in row 8q + l/8 at slot l%8,
+    // which holds k-chunk slot ^ ((row/2) % 8).
+    const int row = (kACopies * wave + i) * kRowsPerCopy + lane / kChunks;
+    const int chunk = (lane % kChunks) ^ ((row / kRowsPer256) % kChunks);
+    c_off[i] = (m0 + row < p.M) ? (uint32_t)(((int64_t)row * p.lda + chunk * 8) * 2) : kOob;
+  }
+#pragma unroll
+  for (int i = 0; i < kBCopies; ++i) {
+    const int q = kBCopies * wave + i;
+    bool ok;
+    if (WNK) {
+      const int n = q * kRowsPerCopy + lane / kChunks;  // tile column = staged row
+      const int chunk = (lane % kChunks) ^ ((n / kRowsPer256) % kChunks);
+      const int64_t wrow = weight_column<MODE, kWN>(p, n0, n & ~7, ok) + (n & 7);
+      c_off[kACopies + i] = ok ? (uint32_t)((wrow * p.ldb + chunk * 8) * 2) : kOob;
+    } else {
+      // [64 k][256 n]: block q holds k rows 2q, 2q+1; lane l lands in row 2q + l/32 at slot l%32,
+      // which holds n-chunk slot ^ (4 * (row % 4)).
+      const int krow = 2 * q + (lane >> 5);
+      const int chunk = (lane & 31) ^ (4 * (krow % 4));
+      const int64_t wcol = weight_column<MODE, kWN>(p, n0, chunk * 8, ok);
+      c_off[kACopies + i] = ok ? (uint32_t)(((int64_t)krow * p.ldb + wcol) * 2) : kOob;
+    }
+  }
+  auto a_desc = [&](int t) {
+    const int k0 = t * kBK;
+    return buffer_desc(p.A + (int64_t)m0 * p.lda + k0, ((int64_t)(p.M - m0 - 1) * p.lda + (p.K - k0)) * 2);
+  };
+  auto b_desc = [&](int t) {
+    const int k0 = t * kBK;
+    return WNK ? buffer_desc(p.B + k0, ((int64_t)(p.b_rows - 1) * p.ldb + (p.K - k0)) * 2)
+               : buffer_desc(p.B + (int64_t)k0 * p.ldb, (int64_t)(p.K - k0) * p.ldb * 2);
+  };
+  // Copy i of tile t into stage t % 2: the wave's 8-KiB block of the A or B half plus a constant.
+  const uint32_t wave_lds = lds0 + (uint32_t)(wave * kACopies * 1024);
+  auto copy_one = [&](int t, int i, i32x4_t ad, i32x4_t bd) {
+    const uint32_t st = wave_lds + (uint32_t)((t & 1) * kStageElems * 2);
+    if (i < kACopies) copy16_to_lds_at(ad, c_off[i], st, i * 1024);
+    else copy16_to_lds_at(bd, c_off[i], st, kAElems * 2 + (i - kACopies) * 1024);
+  };
+  auto copy_tile = [&](int t) {
+    const i32x4_t ad = a_desc(t), bd = b_desc(t);
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) copy_one(t, i, ad, bd);
+  };
+
+  // ---- Fragment offsets (elements within a stage).  [rows][64 k] staging: row r, k-chunk
+  // 2*kk + lane/32 at slot chunk ^ ((r/2) % 8); for the rows a wave reads the swizzle term is
+  // ((lane%32) / 2) % 8.
+  const int a_r = lane & 31;
+  const int a_half = lane >> 5;
+  const int rs = (a_r / kRowsPer256) % kChunks;
+  int ra_off[kKK], rb_off[kKK];
+#pragma unroll
+  for (int kk = 0; kk < kKK; ++kk) {
+    const int slot = (kk * 2 + a_half) ^ rs;
+    ra_off[kk] = (wm * kWM + a_r) * kBK + slot * 8;
+    rb_off[kk] = kAElems + (wn * kWN + a_r) * kBK + slot * 8;  // W^T: B rows are weight columns
+  }
+  // [64 k][256 n] staging, read with ds_read_b64_tr_b16 (each 16-lane group receives the transpose
+  // of a 4 (k) x 16 (n) block): group g = lane/16 reads k row 16*kk + 8*(g/2) + 4*h + (lane%16)/4 at
+  // n = 128*wn + 32*ni + 16*(g%2) + 4*(lane%4), i.e. chunk 16*wn + 4*ni + 2*(g%2) + (lane%4)/2, stored
+  // at slot chunk ^ (4 * (k%4)) with k%4 = (lane%16)/4.
+  int rt_off[kNI];
+  {
+    const int krow = 8 * (lane >> 5) + ((lane & 15) >> 2);
+    const int x = 4 * ((lane & 15) >> 2);
+    const int c = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni)
+      rt_off[ni] = kAElems + krow * kBN + (((kWN / 8) * wn + 4 * ni + c) ^ x) * 8 + 4 * (lane & 1);
+  }
+
+  // Fragments of the four slices (buffer = slice index).  [k][n] weights: the two halves of each B
+  // fragment are read separately and joined at the MFMA.
+  bf16x8_t af[kKK][kMI], bv[kKK][kNI];
+  i16x4_t bl[kKK][kNI], bh[kKK][kNI];
+  // LDS read j of slice kk of tile t: j < 4 are the A fragments, then the B fragments (one read
+  // each when W is stored [n][k], two half reads each when stored [k][n]).
+  constexpr int kReadsPerSlice = kMI + (WNK ? 1 : 2) * kNI;
+  auto read_one = [&](int t, int kk, int j) {
+    const uint16_t* st = lds + (t & 1) * kStageElems;
+    if (j < kMI) {
+      af[kk][j] = *reinterpret_cast<const bf16x8_t*>(st + ra_off[kk] + j * 32 * kBK);
+    } else if constexpr (WNK) {
+      const int ni = j - kMI;
+      bv[kk][ni] = *reinterpret_cast<const bf16x8_t*>(st + rb_off[kk] + ni * 32 * kBK);
+    } else {
+      const int ni = (j - kMI) / 2, h = (j - kMI) % 2;
+      const uint16_t* b = st + rt_off[ni] + kk * 16 * kBN + h * 4 * kBN;
+      const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b));
+      if (h == 0) bl[kk][ni] = v;
+      else bh[kk][ni] = v;
+    }
+  };
+
+  f32x16_t acc[kMI][kNI];
+#pragma unroll
+  for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+
+  // MFMA j (0..15) of slice kk: the weight fragment as the first operand, so lane l holds output
+  // row (l & 31) and, in accumulator register r, column 8*(r/4) + 4*(l/32) + r%4 of the 32 x 32 block.
+  auto mfma_one = [&](int kk, int j) {
+    const int mi = j / kNI, ni = j % kNI;
+    bf16x8_t b;
+    if constexpr (WNK) b = bv[kk][ni];
+    else b = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(bl[kk][ni], bh[kk][ni], 0, 1, 2, 3, 4, 5, 6, 7));
+    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, af[kk][mi], acc[mi][ni], 0, 0, 0);
+  };
+
+  // ---- Prologue: tiles 0 and 1 in flight, tile 0 landed, slices 0 and 1 of tile 0 read.
+  copy_tile(0);
+  if (nk > 1) {
+    copy_tile(1);
+    wait_vmcnt<kCopies>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  lds_barrier();
+#pragma unroll
+  for (int j = 0; j < kReadsPerSlice; ++j) read_one(0, 0, j);
+#pragma unroll
+  for (int j = 0; j < kReadsPerSlice; ++j) read_one(0, 1, j);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // One k-tile.  NEXT: tile t+1 exists (barrier, and its reads); COPY: tile t+2 exists (its
+  // copies).  The main loop runs with both; the last two tiles are peeled, so the loop has no
+  // branches.
+  auto k_tile = [&](int t, auto next_c, auto copy_c) {
+    constexpr bool NEXT = decltype(next_c)::value, COPY = decltype(copy_c)::value;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      mfma_one(0, j);
+#pragma unroll
+      for (int r = j * 2 * kReadsPerSlice / 16; r < (j + 1) * 2 * kReadsPerSlice / 16; ++r)
+        read_one(t, 2 + r / kReadsPerSlice, r % kReadsPerSlice);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      mfma_one(1, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (NEXT) {
+      wait_vmcnt<0>();  // this wave's copies of tile t+1 landed
+      lds_barrier();    // ... everyone's; and every wave's reads of tile t returned
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    i32x4_t ad = {0, 0, 0, 0}, bd = {0, 0, 0, 0};
+    if (COPY) {
+      ad = a_desc(t + 2);
+      bd = b_desc(t + 2);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      mfma_one(2, j);
+      if (COPY && j % 2 == 0) copy_one(t + 2, j / 2, ad, bd);
+      if (NEXT) {
+#pragma unroll
+        for (int r = j * kReadsPerSlice / 16; r < (j + 1) * kReadsPerSlice / 16; ++r) read_one(t + 1, 0, r);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      mfma_one(3, j);
+      if (COPY && j % 2 == 0) copy_one(t + 2, kACopies + j / 2, ad, bd);
+      if (NEXT) {
+#pragma unroll
+        for (int r = j * kReadsPerSlice / 16; r < (j + 1) * kReadsPerSlice / 16; ++r) read_one(t + 1, 1, r);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  int t = 0;
+  for (; t + 2 < nk; ++t) k_tile(t, std::true_type{}, std::true_type{});
+  if (t + 1 < nk) k_tile(t++, std::true_type{}, std::false_type{});
+  k_tile(t, std::false_type{}, std::false_type{});
+
+  // ---- Epilogue straight from the accumulators: each lane owns 4 consecutive columns of one row
+  // per register group, stored as one 8-byte piece.
+  const int row_base = m0 + wm * kWM + a_r;
+#pragma unroll
+  for (int mi = 0; mi < kMI; ++mi) {
+    const int row = row_base + mi * 32;
+    if (row >= p.M) continue;
+    uint16_t* crow = p.C + (int64_t)row * p.ldc;
+    if (MODE == kPlain) {
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = n0 + wn * kWN + ni * 32 + g * 8 + a_half * 4;
+          if (col < p.N) {
+            u32x2_t v;
+            v.x = pack_bf16x2(acc[mi][ni][4 * g + 0], acc[mi][ni][4 * g + 1]);
+            v.y = pack_bf16x2(acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]);
+            *reinterpret_cast<u32x2_t*>(crow + col) = v;
+          }
+        }
+    } else {
+#pragma unroll
+      for (int ni = 0; ni < kNI / 2; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = n0 + wn * (kWN / 2) + ni * 32 + g * 8 + a_half * 4;
+          if (col < p.N) {
+            float a[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              a[e] = silu_mul(acc[mi][ni][4 * g + e], acc[mi][ni + kNI / 2][4 * g + e]);
+            u32x2_t v;
+            v.x = pack_bf16x2(a[0], a[1]);
+            v.y = pack_bf16x2(a[2], a[3]);
+            *reinterpret_cast<u32x2_t*>(crow + col) = v;
+          }
+        }
+    }
+  }
+}
+
+template <int MODE, bool WNK>
+void launch_one(const GemmParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_bigwave_kernel<MODE, WNK>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
+                     dim3(kThreads), 0, stream, p);
+}
+
+}  // namespace
+
+bool gemm_bigwave_supports(const GemmParams& p) { return p.K % kBK == 0 && p.K > 0; }
+
+hipError_t launch_gemm_bigwave(const GemmParams& p, hipStream_t stream) {
+  if (p.mode == kSiluMul)
+    p.w_nk ? launch_one<kSiluMul, true>(p, stream) : launch_one<kSiluMul, false>(p, stream);
+  else
+    p.w_nk ? launch_one<kPlain, true>(p, stream) : launch_one<kPlain, false>(p, stream);
+  return hipGetLastError();
+}
+
+}  // namespace ttl

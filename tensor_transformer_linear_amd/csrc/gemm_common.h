@@ -56,6 +56,13 @@ __device__ inline void copy16_to_lds(i32x4_t desc, uint32_t voffset, uint32_t ld
                :: "v"(voffset), "s"(desc), "s"(lds_base) : "memory");
 }
 
+// The same copy with the LDS destination lds_base + lds_imm (a compile-time constant) summed
+// straight into M0 (one scalar instruction fewer per copy; the add writes SCC).
+__device__ inline void copy16_to_lds_at(i32x4_t desc, uint32_t voffset, uint32_t lds_base, uint32_t lds_imm) {
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voffset), "s"(desc), "s"(lds_base), "n"(lds_imm) : "memory", "scc");
+}
+
 // Wait until at most N of this wave's vector-memory operations are outstanding.
 template <int N>
 __device__ inline void wait_vmcnt() {
@@ -68,6 +75,49 @@ __device__ inline void wait_vmcnt() {
 // explicit (wait_vmcnt for this wave's copies, lgkmcnt(0) for its LDS reads), and the memory clobber
 // keeps the compiler from moving LDS accesses across the barrier.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Tile order of the 256 x 256-tile kernels.  Consecutive workgroups are dealt to different XCDs
+// (8 on MI355X), each with its own L2: the block index is remapped so that each XCD runs a compact
+// run of tiles, and tiles are walked in groups of kGroupM row-tiles (all columns of a group before
+// the next), so that one XCD's tiles share A rows and weight columns in its L2.  Both maps are
+// bijections on [0, tiles_m * tiles_n).
+__device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int kXcds = 8, kGroupM = 4;
+  const int tiles = tiles_m * tiles_n;
+  const int q = tiles / kXcds, r = tiles % kXcds;
+  const int x = bid % kXcds, local = bid / kXcds;
+  const int L = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
+  const int per_group = kGroupM * tiles_n;
+  const int g = L / per_group;
+  const int first = g * kGroupM;
+  const int gsize = min(tiles_m - first, kGroupM);
+  const int inner = L - g * per_group;
+  tm = first + inner % gsize;
+  tn = inner / gsize;
+}
+
+// Weight column of tile column c (the first of 8 consecutive ones) of the tile whose first output
+// column is n0, and whether it is in range, for waves owning WN tile columns each as WN/32 blocks of
+// 32.  SiLU·up: tile column c = w*WN + nb*32 + j; a wave's blocks nb < WN/64 hold gate columns and
+// the others the up columns of the same act columns, so gate and up of one output meet in one lane.
+// Plain: output column n0 + c through the (up to three) segments of the column map.
+template <int MODE, int WN>
+__device__ inline int64_t weight_column(const GemmParams& p, int n0, int c, bool& ok) {
+  constexpr int NI = WN / 32;
+  if (MODE == kSiluMul) {
+    const int w = c / WN, nb = (c % WN) / 32, j = c % 32;
+    const int act = n0 + w * (WN / 2) + (nb % (NI / 2)) * 32 + j;
+    ok = act < p.N;
+    return (nb < NI / 2 ? p.gate_w0 : p.up_w0) + act;
+  }
+  const int oc = n0 + c;
+  ok = oc < p.N;
+  int64_t w0 = p.seg_w0[0];
+  int s0 = p.seg_out0[0];
+  if (p.nseg > 1 && oc >= p.seg_out0[1]) { w0 = p.seg_w0[1]; s0 = p.seg_out0[1]; }
+  if (p.nseg > 2 && oc >= p.seg_out0[2]) { w0 = p.seg_w0[2]; s0 = p.seg_out0[2]; }
+  return w0 + (oc - s0);
+}
 
 }  // namespace gemm
 }  // namespace ttl

@@ -14,7 +14,9 @@
 // must not be issued.
 //
 // Environment overrides, read at every launch (for tests and measurements):
-//   TTL_GEMM_KERNEL=tiled|splitk  use that kernel whatever the shape;
+//   TTL_GEMM_KERNEL=tiled|splitk  use that kernel family whatever the shape;
+//   TTL_GEMM_KERNEL=eightwave     the 256 x 256 tiles, by the eight-wave kernel even where K is a
+//                                 multiple of 64 (where the four-wave kernel runs by default);
 //   TTL_GEMM_SPLITS=<n>           split-K kernel: use n splits (at most one per k-tile).
 #include <cstdlib>
 #include <cstring>
@@ -63,12 +65,13 @@ hipError_t get_workspace(size_t bytes, void** out) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// 0: by shape, 1: 256 x 256 tiles, 2: split-K.
+// 0: by shape, 1: 256 x 256 tiles, 2: split-K, 3: 256 x 256 tiles by the eight-wave kernel.
 int forced_kernel() {
   const char* s = std::getenv("TTL_GEMM_KERNEL");
   if (s == nullptr) return 0;
   if (std::strcmp(s, "tiled") == 0) return 1;
   if (std::strcmp(s, "splitk") == 0) return 2;
+  if (std::strcmp(s, "eightwave") == 0) return 3;
   return 0;
 }
 
@@ -83,9 +86,10 @@ hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
   const int64_t tiled_m = cdiv(p.M, gemm_tile_rows());
   const int64_t tiled_n = cdiv(p.N, gemm_tile_cols(p.mode));
   const int force = forced_kernel();
-  if (force == 1 || (force == 0 && tiled_m * tiled_n >= kTiledMinTiles)) {
+  if (force == 1 || force == 3 || (force == 0 && tiled_m * tiled_n >= kTiledMinTiles)) {
     p.tiles_m = (int32_t)tiled_m;
     p.tiles_n = (int32_t)tiled_n;
+    if (force != 3 && gemm_bigwave_supports(p)) return launch_gemm_bigwave(p, stream);
     return launch_gemm_tiled(p, stream);
   }
 

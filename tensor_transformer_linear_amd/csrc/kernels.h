@@ -36,10 +36,14 @@ struct GemmParams {
 // fields of p.  May allocate the library's split-K workspace on first use.
 hipError_t launch_gemm(GemmParams& p, hipStream_t stream);
 
-// 256 x 256 tiles (tiles_m, tiles_n set by the caller from the two functions below).
+// 256 x 256 tiles (tiles_m, tiles_n set by the caller from the two functions below), by either of
+// two kernels with identical results: eight waves (two per SIMD, any K), or four waves of 128 x 128
+// outputs (one per SIMD, faster; K a multiple of 64).
 int gemm_tile_rows();
 int gemm_tile_cols(int mode);
 hipError_t launch_gemm_tiled(const GemmParams& p, hipStream_t stream);
+bool gemm_bigwave_supports(const GemmParams& p);
+hipError_t launch_gemm_bigwave(const GemmParams& p, hipStream_t stream);
 
 // Split-K kernel with 32*mb-row tiles (mb = 1, 2 or 4) of 128 weight columns, followed (splits > 1)
 // by the kernel that sums the splits; tiles_m, tiles_n, splits, kt_per_split, ws and ws_ld set by

@@ -1,8 +1,9 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle, on seeded synthetic inputs.
 
 Small cases compare every element; they span several 256-wide tiles and ragged tails in all three
-GEMM dimensions.  Each GEMM case runs through both kernels the library has (256 x 256 tiles, and
-the split-K kernel for short M, forced with TTL_GEMM_KERNEL) and through the shape-based choice.  Tolerance, per output tensor: the error beyond the bf16 rounding of each output
+GEMM dimensions.  Each GEMM case runs through every kernel the library has, forced with
+TTL_GEMM_KERNEL (256 x 256 tiles by the four-wave kernel where K is a multiple of 64, by the
+eight-wave kernel, and the split-K kernel for short M), and through the shape-based choice.  Tolerance, per output tensor: the error beyond the bf16 rounding of each output
 element is at most 2e-2 * rms(ref), the reference being the oracle's unrounded float64 value (bf16
 inputs, so the device-side error is fp32 accumulation and fp32 elementwise math).  Integer-exact
 special cases (identity and one-hot operands) are compared bit for bit.
@@ -29,7 +30,7 @@ def ttl():
 LAYOUTS = pytest.mark.parametrize("layout", ["kn", "nk"])
 
 
-@pytest.fixture(params=["auto", "tiled", "splitk"])
+@pytest.fixture(params=["auto", "tiled", "eightwave", "splitk"])
 def gemm_path(request, monkeypatch):
     """Which GEMM kernel the library uses for the test (auto = its choice by shape)."""
     if request.param == "auto":
@@ -165,6 +166,28 @@ def test_layouts_agree_bitwise(ttl, gemm_path):
     c = ttl.shard_linear_col(X, gpu(W.t().contiguous()), t, 2, sp, ttl.EPI_SILU_MUL, w_layout=ttl.W_NK)
     torch.cuda.synchronize()
     assert torch.equal(a, c)
+
+
+@pytest.mark.parametrize("k", [64, 128, 192, 320, 576])
+@LAYOUTS
+def test_tiled_kernels_short_k(ttl, monkeypatch, k, layout):
+    """The four-wave 256 x 256 kernel over 1, 2, 3, 5 and 9 k-tiles (its prologue and the two
+    peeled k-tiles), ragged in M and N, matches the oracle and the eight-wave kernel bit for bit
+    (both accumulate the same products in the same k order)."""
+    monkeypatch.delenv("TTL_GEMM_SPLITS", raising=False)
+    b, I, t = 300, 688, 2
+    X = wl.random_bf16((b, k), 95 + k)
+    W = wl.random_bf16((k, 2 * I), 96 + k, std=0.05)
+    Wd_, lay = _stored(ttl, W, layout)
+    sp = ttl.merged_gate_up_split(I, t)
+    outs = {}
+    for kern in ("tiled", "eightwave"):
+        monkeypatch.setenv("TTL_GEMM_KERNEL", kern)
+        outs[kern] = ttl.shard_linear_col(gpu(X), Wd_, t, 1, sp, ttl.EPI_SILU_MUL, w_layout=lay)
+        torch.cuda.synchronize()
+    ref = oracle.silu_mul(oracle.col_shard(f64(X), f64(W), oracle.merged_gate_up_split(I, t), t, 1))
+    assert_close(from_gpu(outs["tiled"]), ref, f"four-wave k={k} {layout}")
+    assert torch.equal(outs["tiled"], outs["eightwave"])
 
 
 def test_bitwise_deterministic(ttl, gemm_path):
