@@ -5,6 +5,9 @@
 // Those go to the split-K kernel, whose 32..128-row x 128-column tiles are additionally cut along
 // k into as many ranges as keep the grid within one workgroup per CU: a CU streams at its full
 // rate with one workgroup, and a grid that does not divide evenly over the CUs leaves a slow tail.
+// A launch of whole rounds of 256 x 256 tiles plus a short last round (e.g. 288 tiles: 2176 rows
+// x 8192 columns) is cut by rows: the whole rounds to the tiled kernel, the last few row-tiles to
+// the split-K kernel.
 //
 // Workspace: split-K launches with more than one split write fp32 partial tiles that a second
 // kernel reduces.  The library keeps one device buffer per GPU for them, allocated (or grown) on
@@ -80,19 +83,15 @@ int64_t forced_splits() {
   return s == nullptr ? 0 : std::atoll(s);
 }
 
-}  // namespace
+// 256 x 256 tiles over all of p: the four-wave kernel where it applies, unless force == 3.
+hipError_t launch_tiles(GemmParams& p, int force, hipStream_t stream) {
+  p.tiles_m = (int32_t)cdiv(p.M, gemm_tile_rows());
+  p.tiles_n = (int32_t)cdiv(p.N, gemm_tile_cols(p.mode));
+  if (force != 3 && gemm_bigwave_supports(p)) return launch_gemm_bigwave(p, stream);
+  return launch_gemm_tiled(p, stream);
+}
 
-hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
-  const int64_t tiled_m = cdiv(p.M, gemm_tile_rows());
-  const int64_t tiled_n = cdiv(p.N, gemm_tile_cols(p.mode));
-  const int force = forced_kernel();
-  if (force == 1 || force == 3 || (force == 0 && tiled_m * tiled_n >= kTiledMinTiles)) {
-    p.tiles_m = (int32_t)tiled_m;
-    p.tiles_n = (int32_t)tiled_n;
-    if (force != 3 && gemm_bigwave_supports(p)) return launch_gemm_bigwave(p, stream);
-    return launch_gemm_tiled(p, stream);
-  }
-
+hipError_t launch_splitk(GemmParams& p, hipStream_t stream) {
   const int mb = p.M <= 32 ? 1 : (p.M <= 64 ? 2 : 4);
   const int64_t tiles_m = cdiv(p.M, 32 * mb);
   const int64_t tiles_n = cdiv(p.N, p.mode == 1 ? kSkinnyCols / 2 : kSkinnyCols);
@@ -119,6 +118,38 @@ hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
     p.ws = static_cast<float*>(base);
   }
   return launch_gemm_skinny(p, mb, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
+  const int force = forced_kernel();
+  if (force == 1 || force == 3) return launch_tiles(p, force, stream);
+  if (force == 2) return launch_splitk(p, stream);
+  const int64_t tiled_m = cdiv(p.M, gemm_tile_rows());
+  const int64_t tiled_n = cdiv(p.N, gemm_tile_cols(p.mode));
+  const int64_t tiles = tiled_m * tiled_n;
+  if (tiles < kTiledMinTiles) return launch_splitk(p, stream);
+  // Whole rounds of one tile per CU plus a short last round (at most half the CUs): that round
+  // would take a whole tile's time with most of the chip idle.  The row-tiles that fill the whole
+  // rounds go to the tiled kernel, the remaining rows (a few row-tiles) to the split-K kernel,
+  // which spreads them over all CUs.
+  const int64_t rounds = tiles / kCUs, rem = tiles % kCUs;
+  if (rounds >= 1 && rem > 0 && 2 * rem <= kCUs) {
+    const int64_t head_row_tiles = rounds * kCUs / tiled_n;
+    if (head_row_tiles >= 1 && head_row_tiles < tiled_m) {
+      GemmParams head = p;
+      head.M = (int32_t)(head_row_tiles * gemm_tile_rows());
+      hipError_t e = launch_tiles(head, 0, stream);
+      if (e != hipSuccess) return e;
+      GemmParams tail = p;
+      tail.A = p.A + (int64_t)head.M * p.lda;
+      tail.C = p.C + (int64_t)head.M * p.ldc;
+      tail.M = p.M - head.M;
+      return launch_splitk(tail, stream);
+    }
+  }
+  return launch_tiles(p, 0, stream);
 }
 
 }  // namespace ttl

@@ -190,6 +190,40 @@ def test_tiled_kernels_short_k(ttl, monkeypatch, k, layout):
     assert torch.equal(outs["tiled"], outs["eightwave"])
 
 
+@pytest.mark.parametrize("silu", [False, True])
+@LAYOUTS
+def test_short_last_round_split_by_rows(ttl, monkeypatch, silu, layout):
+    """2176 x 8192 outputs are 288 tiles of 256 x 256: one whole round on 256 CUs plus 32 tiles.
+    By default the first 2048 rows run as tiles and the last 128 rows through the split-K kernel;
+    sampled rows on both sides of the cut match the oracle, and the head rows match the forced
+    tiled run bit for bit."""
+    monkeypatch.delenv("TTL_GEMM_SPLITS", raising=False)
+    b, k = 2176, 256
+    n = 8192
+    X = wl.random_bf16((b, k), 97)
+    if silu:
+        W = wl.random_bf16((k, 2 * n), 98, std=0.05)
+        sp_c, sp_np, epi = ttl.merged_gate_up_split(n, 1), oracle.merged_gate_up_split(n, 1), ttl.EPI_SILU_MUL
+    else:
+        W = wl.random_bf16((k, n), 98, std=0.05)
+        sp_c, sp_np, epi = None, oracle.plain_split(n, 1), 0
+    Wd_, lay = _stored(ttl, W, layout)
+    outs = {}
+    for kern in ("auto", "tiled"):
+        if kern == "auto":
+            monkeypatch.delenv("TTL_GEMM_KERNEL", raising=False)
+        else:
+            monkeypatch.setenv("TTL_GEMM_KERNEL", kern)
+        outs[kern] = ttl.shard_linear_col(gpu(X), Wd_, 1, 0, sp_c, epi, w_layout=lay)
+        torch.cuda.synchronize()
+    rows = np.r_[0:8, 2040:2056, 2100:2108, 2168:2176]
+    ref = oracle.col_shard(f64(X)[rows], f64(W), sp_np, 1, 0)
+    if silu:
+        ref = oracle.silu_mul(ref)
+    assert_close(from_gpu(outs["auto"])[rows], ref, f"row-cut rows silu={silu} {layout}")
+    assert torch.equal(outs["auto"][:2048], outs["tiled"][:2048])
+
+
 def test_bitwise_deterministic(ttl, gemm_path):
     b, k, I, t = 300, 512, 1024, 2
     X, Wgu = gpu(wl.random_bf16((b, k), 80)), gpu(wl.random_bf16((k, 2 * I), 81, std=0.05))
