@@ -24,6 +24,11 @@
 // L2 requests for the same bytes).
 //
 // K must be a multiple of 64 (no k tail); the eight-wave kernel serves the other shapes.
+//
+// Split-K launches (few tiles, long K: the qkv and o_proj shards at prefill sizes): workgroup
+// split * tiles + tile runs k-tiles [split * kt_per_split, ...) of its tile and writes the fp32
+// partial tile to the workspace (plain mode; SiLU·up runs as the gate columns then the up columns),
+// which the split-K finalize kernel sums in split order.
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -59,11 +64,15 @@ void gemm_bigwave_kernel(const GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / 2, wn = wave % 2;
 
+  // Split-K launches: block = split * tiles + tile; split s runs k-tiles [s * kt_per_split, ...).
+  const int tiles = p.tiles_m * p.tiles_n;
+  const int split = p.splits > 1 ? (int)blockIdx.x / tiles : 0;
   int tile_m, tile_n;
-  tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tile_m, tile_n);
+  tile_coords((int)blockIdx.x - split * tiles, p.tiles_m, p.tiles_n, tile_m, tile_n);
   const int m0 = tile_m * kBM;
   const int n0 = tile_n * (MODE == kSiluMul ? kBN / 2 : kBN);  // first output column of the tile
-  const int nk = p.K / kBK;
+  const int kt0 = split * p.kt_per_split;
+  const int nk = p.splits > 1 ? min(p.kt_per_split, p.K / kBK - kt0) : p.K / kBK;  // >= 1
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds);
 
   // ---- Copy offsets, fixed for the whole k loop (the descriptors move with k0).  Copy i < 8 of
@@ -96,11 +105,11 @@ void gemm_bigwave_kernel(const GemmParams p) {
     }
   }
   auto a_desc = [&](int t) {
-    const int k0 = t * kBK;
+    const int k0 = (kt0 + t) * kBK;
     return buffer_desc(p.A + (int64_t)m0 * p.lda + k0, ((int64_t)(p.M - m0 - 1) * p.lda + (p.K - k0)) * 2);
   };
   auto b_desc = [&](int t) {
-    const int k0 = t * kBK;
+    const int k0 = (kt0 + t) * kBK;
     return WNK ? buffer_desc(p.B + k0, ((int64_t)(p.b_rows - 1) * p.ldb + (p.K - k0)) * 2)
                : buffer_desc(p.B + (int64_t)k0 * p.ldb, (int64_t)(p.K - k0) * p.ldb * 2);
   };
@@ -254,9 +263,12 @@ void gemm_bigwave_kernel(const GemmParams p) {
   if (t + 1 < nk) k_tile(t++, std::true_type{}, std::false_type{});
   k_tile(t, std::false_type{}, std::false_type{});
 
-  // ---- Epilogue straight from the accumulators: each lane owns 4 consecutive columns of one row
-  // per register group, stored as one 8-byte piece.
   const int row_base = m0 + wm * kWM + a_r;
+  // ---- Epilogue straight from the accumulators: each lane owns 4 consecutive columns of one row
+  // per register group, stored as one 8-byte bf16 piece, or (split-K, plain mode) as one 16-byte
+  // fp32 piece of the partial tile in workspace slice `split`.
+  const bool partial = MODE == kPlain && p.splits > 1;
+  float* wbase = partial ? p.ws + (int64_t)split * p.M * p.ws_ld : nullptr;
 #pragma unroll
   for (int mi = 0; mi < kMI; ++mi) {
     const int row = row_base + mi * 32;
@@ -268,7 +280,10 @@ void gemm_bigwave_kernel(const GemmParams p) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int col = n0 + wn * kWN + ni * 32 + g * 8 + a_half * 4;
-          if (col < p.N) {
+          if (partial) {
+            const float4 v = {acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]};
+            *reinterpret_cast<float4*>(wbase + (int64_t)row * p.ws_ld + col) = v;
+          } else if (col < p.N) {
             u32x2_t v;
             v.x = pack_bf16x2(acc[mi][ni][4 * g + 0], acc[mi][ni][4 * g + 1]);
             v.y = pack_bf16x2(acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]);
@@ -298,7 +313,8 @@ void gemm_bigwave_kernel(const GemmParams p) {
 
 template <int MODE, bool WNK>
 void launch_one(const GemmParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_bigwave_kernel<MODE, WNK>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
+  const int splits = p.splits > 1 ? p.splits : 1;
+  hipLaunchKernelGGL((gemm_bigwave_kernel<MODE, WNK>), dim3((unsigned)(splits * p.tiles_m * p.tiles_n)),
                      dim3(kThreads), 0, stream, p);
 }
 
@@ -307,6 +323,7 @@ void launch_one(const GemmParams& p, hipStream_t stream) {
 bool gemm_bigwave_supports(const GemmParams& p) { return p.K % kBK == 0 && p.K > 0; }
 
 hipError_t launch_gemm_bigwave(const GemmParams& p, hipStream_t stream) {
+  if (p.mode == kSiluMul && p.splits > 1) return hipErrorInvalidValue;  // split SiLU·up runs as halves
   if (p.mode == kSiluMul)
     p.w_nk ? launch_one<kSiluMul, true>(p, stream) : launch_one<kSiluMul, false>(p, stream);
   else

@@ -20,6 +20,8 @@
 //   TTL_GEMM_KERNEL=tiled|splitk  use that kernel family whatever the shape;
 //   TTL_GEMM_KERNEL=eightwave     the 256 x 256 tiles, by the eight-wave kernel even where K is a
 //                                 multiple of 64 (where the four-wave kernel runs by default);
+//   TTL_GEMM_KERNEL=tilesplit     256 x 256 tiles cut along k (four-wave kernel; K a multiple of 64,
+//                                 else the split-K kernel), TTL_GEMM_SPLITS or at least 2 splits;
 //   TTL_GEMM_SPLITS=<n>           split-K kernel: use n splits (at most one per k-tile).
 #include <cstdlib>
 #include <cstring>
@@ -35,6 +37,8 @@ constexpr int kCUs = 256;               // MI355X compute units
 constexpr int kTiledMinTiles = 192;     // 256 x 256 tiles when they occupy >= 3/4 of the CUs
 constexpr int kSkinnyBlocks = kCUs;     // split-K grid: at most one workgroup per CU
 constexpr int kMinKTilesPerSplit = 4;   // keep each split's copy pipeline full
+constexpr int kTileSplitMinRows = 512;  // 256 x 256 tiles cut along k from this many rows
+constexpr int kMinKTilesPerTileSplit = 16;
 
 struct Workspace {
   void* ptr = nullptr;
@@ -68,13 +72,15 @@ hipError_t get_workspace(size_t bytes, void** out) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// 0: by shape, 1: 256 x 256 tiles, 2: split-K, 3: 256 x 256 tiles by the eight-wave kernel.
+// 0: by shape, 1: 256 x 256 tiles, 2: split-K, 3: 256 x 256 tiles by the eight-wave kernel,
+// 4: 256 x 256 tiles cut along k.
 int forced_kernel() {
   const char* s = std::getenv("TTL_GEMM_KERNEL");
   if (s == nullptr) return 0;
   if (std::strcmp(s, "tiled") == 0) return 1;
   if (std::strcmp(s, "splitk") == 0) return 2;
   if (std::strcmp(s, "eightwave") == 0) return 3;
+  if (std::strcmp(s, "tilesplit") == 0) return 4;
   return 0;
 }
 
@@ -87,8 +93,35 @@ int64_t forced_splits() {
 hipError_t launch_tiles(GemmParams& p, int force, hipStream_t stream) {
   p.tiles_m = (int32_t)cdiv(p.M, gemm_tile_rows());
   p.tiles_n = (int32_t)cdiv(p.N, gemm_tile_cols(p.mode));
+  p.splits = 1;
   if (force != 3 && gemm_bigwave_supports(p)) return launch_gemm_bigwave(p, stream);
   return launch_gemm_tiled(p, stream);
+}
+
+// 256 x 256 tiles of the four-wave kernel cut into `splits` k ranges (plain mode; SiLU·up as the
+// gate columns then the up columns), then the split-K finalize kernel.
+hipError_t launch_tiles_splitk(GemmParams& p, int64_t splits, hipStream_t stream) {
+  GemmParams q = p.mode == 1 ? silu_as_plain_halves(p) : p;
+  q.tiles_m = (int32_t)cdiv(q.M, gemm_tile_rows());
+  q.tiles_n = (int32_t)cdiv(q.N, gemm_tile_cols(0));
+  const int64_t nk = q.K / 64;
+  if (splits > nk) splits = nk;
+  const int64_t kt_per = cdiv(nk, splits);
+  splits = cdiv(nk, kt_per);  // every split gets at least one k-tile
+  if (splits < 2) return launch_tiles(p, 0, stream);
+  q.splits = (int32_t)splits;
+  q.kt_per_split = (int32_t)kt_per;
+  q.ws_ld = (int64_t)q.tiles_n * gemm_tile_cols(0);
+  void* base = nullptr;
+  hipError_t e = get_workspace((size_t)splits * q.M * q.ws_ld * sizeof(float), &base);
+  if (e != hipSuccess) return e;
+  q.ws = static_cast<float*>(base);
+  if ((e = launch_gemm_bigwave(q, stream)) != hipSuccess) return e;
+  GemmParams f = p;
+  f.ws = q.ws;
+  f.ws_ld = q.ws_ld;
+  f.splits = q.splits;
+  return launch_splitk_finalize(f, stream);
 }
 
 hipError_t launch_splitk(GemmParams& p, hipStream_t stream) {
@@ -125,11 +158,27 @@ hipError_t launch_splitk(GemmParams& p, hipStream_t stream) {
 hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
   const int force = forced_kernel();
   if (force == 1 || force == 3) return launch_tiles(p, force, stream);
-  if (force == 2) return launch_splitk(p, stream);
+  if (force == 2 || (force == 4 && !gemm_bigwave_supports(p))) return launch_splitk(p, stream);
   const int64_t tiled_m = cdiv(p.M, gemm_tile_rows());
   const int64_t tiled_n = cdiv(p.N, gemm_tile_cols(p.mode));
   const int64_t tiles = tiled_m * tiled_n;
-  if (tiles < kTiledMinTiles) return launch_splitk(p, stream);
+  if (force == 4) {
+    const int64_t fs = forced_splits();
+    const int64_t auto_splits = kCUs / tiles;
+    return launch_tiles_splitk(p, fs > 0 ? fs : (auto_splits > 2 ? auto_splits : 2), stream);
+  }
+  if (tiles < kTiledMinTiles) {
+    // Few 256 x 256 tiles.  With many rows and a long k, 256 x 256 tiles cut along k into about
+    // one workgroup per CU keep the matrix cores busier than the split-K kernel's 128-row tiles;
+    // each split takes at least kMinKTilesPerTileSplit k-tiles, as the fp32 partial tiles cost HBM
+    // traffic (k = 1024 with 2 splits measured slower than the split-K kernel).  Decode-sized
+    // launches stay on the split-K kernel, which is built to stream the weight.
+    const int64_t by_k = (p.K / 64) / kMinKTilesPerTileSplit;
+    const int64_t splits = kCUs / tiles < by_k ? kCUs / tiles : by_k;
+    if (p.M >= kTileSplitMinRows && gemm_bigwave_supports(p) && splits >= 2)
+      return launch_tiles_splitk(p, splits, stream);
+    return launch_splitk(p, stream);
+  }
   // Whole rounds of one tile per CU plus a short last round (at most half the CUs): that round
   // would take a whole tile's time with most of the chip idle.  The row-tiles that fill the whole
   // rounds go to the tiled kernel, the remaining rows (a few row-tiles) to the split-K kernel,

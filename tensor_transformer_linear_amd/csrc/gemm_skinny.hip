@@ -349,16 +349,7 @@ void launch_one(const GemmParams& p, hipStream_t stream) {
     // (tile column c of tile j = output j*128 + c; the same tile count as the paired layout), so
     // that each k row of a [k][n] weight is read in 256-byte runs rather than 128-byte gate and up
     // halves; the finalize kernel pairs output j with output N + j.
-    GemmParams q = p;
-    q.mode = kPlain;
-    q.N = 2 * p.N;
-    q.nseg = 2;
-    q.seg_out0[0] = 0;
-    q.seg_out0[1] = p.N;
-    q.seg_out0[2] = q.seg_out0[3] = 2 * p.N;
-    q.seg_w0[0] = p.gate_w0;
-    q.seg_w0[1] = p.up_w0;
-    q.seg_w0[2] = 0;
+    const GemmParams q = silu_as_plain_halves(p);
     hipLaunchKernelGGL((gemm_skinny_kernel<kPlain, WNK, MB, kStages>), dim3(grid), dim3(kThreads), 0,
                        stream, q);
   } else {
@@ -380,6 +371,14 @@ void launch_mb(const GemmParams& p, int mb, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_splitk_finalize(const GemmParams& p, hipStream_t stream) {
+  const int64_t threads = (int64_t)p.M * (p.N / 4);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (p.mode == kSiluMul) hipLaunchKernelGGL((splitk_finalize_kernel<kSiluMul>), grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((splitk_finalize_kernel<kPlain>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_skinny(const GemmParams& p, int mb, hipStream_t stream) {
   if (p.mode == kSiluMul)

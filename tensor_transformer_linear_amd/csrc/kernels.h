@@ -25,11 +25,29 @@ struct GemmParams {
   int32_t tiles_m, tiles_n;
   int32_t w_nk;           // weight stored transposed ([n][k])
   int64_t b_rows;         // w_nk: rows of W^T reachable from B
-  // Split-K kernel only: fp32 partial sums [splits][M][ws_ld].
+  // Split-K launches (splits > 1): fp32 partial sums [splits][M][ws_ld], split s covering k-tiles
+  // [s * kt_per_split, (s + 1) * kt_per_split).
   float* ws;
   int64_t ws_ld;
   int32_t splits, kt_per_split;
 };
+
+// SiLU·up as a plain GEMM over the gate columns followed by the up columns (2N outputs, two column
+// segments), for split-K partial sums: output j and output N + j are the gate and up inputs of act
+// column j, which the finalize kernel pairs.
+inline GemmParams silu_as_plain_halves(const GemmParams& p) {
+  GemmParams q = p;
+  q.mode = 0;
+  q.N = 2 * p.N;
+  q.nseg = 2;
+  q.seg_out0[0] = 0;
+  q.seg_out0[1] = p.N;
+  q.seg_out0[2] = q.seg_out0[3] = 2 * p.N;
+  q.seg_w0[0] = p.gate_w0;
+  q.seg_w0[1] = p.up_w0;
+  q.seg_w0[2] = 0;
+  return q;
+}
 
 // Picks the kernel for the shape and launches it: the 256 x 256-tile kernel when its tiles fill the
 // chip, otherwise the split-K kernel (short M: decode batches, small shards).  Sets the tiling
@@ -43,6 +61,8 @@ int gemm_tile_rows();
 int gemm_tile_cols(int mode);
 hipError_t launch_gemm_tiled(const GemmParams& p, hipStream_t stream);
 bool gemm_bigwave_supports(const GemmParams& p);
+// The four-wave kernel also takes split-K launches (plain mode only): splits * tiles_m * tiles_n
+// workgroups, each writing its fp32 partial tile; launch_splitk_finalize then sums them.
 hipError_t launch_gemm_bigwave(const GemmParams& p, hipStream_t stream);
 
 // Split-K kernel with 32*mb-row tiles (mb = 1, 2 or 4) of 128 weight columns, followed (splits > 1)
@@ -51,6 +71,10 @@ hipError_t launch_gemm_bigwave(const GemmParams& p, hipStream_t stream);
 constexpr int kSkinnyCols = 128;  // weight columns per tile (64 act columns in SiLU·up mode)
 constexpr int kSkinnyK = 64;      // k per pipeline stage
 hipError_t launch_gemm_skinny(const GemmParams& p, int mb, hipStream_t stream);
+
+// Sum of the p.splits fp32 partials in p.ws (ascending split order), then the epilogue of p.mode
+// (SiLU·up: gate at workspace column j, up at column N + j), into p.C.
+hipError_t launch_splitk_finalize(const GemmParams& p, hipStream_t stream);
 
 // Rows [0, b) of the outputs; row i reads the partials at P + i*n + r*plane, r = 0..t-1.
 struct ReduceNormParams {

@@ -3,7 +3,8 @@
 Small cases compare every element; they span several 256-wide tiles and ragged tails in all three
 GEMM dimensions.  Each GEMM case runs through every kernel the library has, forced with
 TTL_GEMM_KERNEL (256 x 256 tiles by the four-wave kernel where K is a multiple of 64, by the
-eight-wave kernel, and the split-K kernel for short M), and through the shape-based choice.  Tolerance, per output tensor: the error beyond the bf16 rounding of each output
+eight-wave kernel, the four-wave kernel's tiles cut along k, and the split-K kernel for short M),
+and through the shape-based choice.  Tolerance, per output tensor: the error beyond the bf16 rounding of each output
 element is at most 2e-2 * rms(ref), the reference being the oracle's unrounded float64 value (bf16
 inputs, so the device-side error is fp32 accumulation and fp32 elementwise math).  Integer-exact
 special cases (identity and one-hot operands) are compared bit for bit.
@@ -30,7 +31,7 @@ def ttl():
 LAYOUTS = pytest.mark.parametrize("layout", ["kn", "nk"])
 
 
-@pytest.fixture(params=["auto", "tiled", "eightwave", "splitk"])
+@pytest.fixture(params=["auto", "tiled", "eightwave", "tilesplit", "splitk"])
 def gemm_path(request, monkeypatch):
     """Which GEMM kernel the library uses for the test (auto = its choice by shape)."""
     if request.param == "auto":
@@ -188,6 +189,33 @@ def test_tiled_kernels_short_k(ttl, monkeypatch, k, layout):
     ref = oracle.silu_mul(oracle.col_shard(f64(X), f64(W), oracle.merged_gate_up_split(I, t), t, 1))
     assert_close(from_gpu(outs["tiled"]), ref, f"four-wave k={k} {layout}")
     assert torch.equal(outs["tiled"], outs["eightwave"])
+
+
+@pytest.mark.parametrize("splits", [2, 3, 7])
+@pytest.mark.parametrize("silu", [False, True])
+@LAYOUTS
+def test_tiles_cut_along_k(ttl, monkeypatch, splits, silu, layout):
+    """256 x 256 tiles of the four-wave kernel cut into k ranges (10 k-tiles of 64: ranges of 5+5,
+    4+4+2 and 2+2+2+2+2), ragged in M and N, against the oracle; SiLU·up runs as the gate columns
+    then the up columns and is paired by the finalize kernel."""
+    monkeypatch.setenv("TTL_GEMM_KERNEL", "tilesplit")
+    monkeypatch.setenv("TTL_GEMM_SPLITS", str(splits))
+    b, k, t = 600, 640, 2
+    X = wl.random_bf16((b, k), 99 + splits)
+    if silu:
+        I = 1040
+        W = wl.random_bf16((k, 2 * I), 100 + splits, std=0.05)
+        sp_c, sp_np, epi = ttl.merged_gate_up_split(I, t), oracle.merged_gate_up_split(I, t), ttl.EPI_SILU_MUL
+    else:
+        W = wl.random_bf16((k, 1072), 100 + splits, std=0.05)
+        sp_c, sp_np, epi = None, oracle.plain_split(1072, t), 0
+    Wd_, lay = _stored(ttl, W, layout)
+    for r in range(t):
+        Y = ttl.shard_linear_col(gpu(X), Wd_, t, r, sp_c, epi, w_layout=lay)
+        ref = oracle.col_shard(f64(X), f64(W), sp_np, t, r)
+        if silu:
+            ref = oracle.silu_mul(ref)
+        assert_close(from_gpu(Y), ref, f"tiles cut along k: splits={splits} silu={silu} r={r} {layout}")
 
 
 @pytest.mark.parametrize("silu", [False, True])
