@@ -10,14 +10,14 @@
 // Workgroup tile 256 x 256 weight columns, k-tiles of 64 (each A row and W^T row then contributes
 // one whole 128-B line per k-tile).  Eight wave64s (two per SIMD, so one
 // wave's LDS reads, waits and barrier overlap the other's matrix work) in a 2 x 4 grid, each owning
-// 128 x 64 outputs as 4 x 2 v_mfma_f32_32x32x16_bf16 accumulators.
+// 128 x 64 outputs as 4 x 2 v_mfma_f32_32x32x16_bf16 accumulators.  This kernel takes any K; where
+// K is a multiple of 64 the four-wave kernel (gemm_bigwave.hip) is used instead, as it is faster.
 //
 // Data movement (gfx950):
 //  * Global -> LDS without registers: buffer_load_dwordx4 ... lds moves 64 lanes x 16 B = 1 KiB per
 //    instruction, lane i landing at byte 16*i of the instruction's block.  Each lane picks the global
 //    piece that must land there, which is how the LDS layouts below get their XOR swizzles.
-//  * A ring of kStages k-tiles in LDS (two 64-KiB stages): tiles kt+1 .. kt+kStages-1 are in flight
-//    while tile kt is read; one wait + barrier per k-tile.
+//  * A ring of two 64-KiB k-tile stages in LDS, refilled as the ping-pong schedule below describes.
 //  * LDS has 64 banks of 4 B; 16 lanes reading 16 B each (or 32 lanes reading 8 B each) are
 //    conflict-free when they cover 256 distinct bytes modulo 256.
 //  * A (and B when stored [n][k]) is staged as [256 rows][64 k]: eight 16-B chunks per 128-B row,
@@ -36,13 +36,6 @@
 // the k-tail contributes exact zeros and the steady-state loop has no bounds logic; stores are masked.
 #include "gemm_common.h"
 
-#ifndef TTL_GEMM_BK
-#define TTL_GEMM_BK 64
-#endif
-#ifndef TTL_GEMM_STAGES
-#define TTL_GEMM_STAGES (TTL_GEMM_BK == 64 ? 2 : 4)
-#endif
-
 namespace ttl {
 namespace {
 
@@ -50,21 +43,10 @@ using namespace gemm;
 
 constexpr int kBM = 256;                   // output rows per tile
 constexpr int kBN = 256;                   // weight columns per tile
-constexpr int kBK = TTL_GEMM_BK;           // k per stage (64: 128-B global row pieces)
-// 1: launch the ping-pong schedule (gemm_pingpong_kernel); 0: the single-phase kernel, which also
-// serves the other wave counts, stage depths and k-tile sizes below.  Both give identical results.
-#ifndef TTL_GEMM_PINGPONG
-#define TTL_GEMM_PINGPONG 1
-#endif
-#ifndef TTL_GEMM_WAVES
-#define TTL_GEMM_WAVES 8
-#endif
-// 8: two waves per SIMD, 128 x 64 each.  4 (one wave per SIMD, 128 x 128 each, accumulators in
-// AGPRs, a third fewer LDS reads) measured ~10% slower: with one wave per SIMD nothing hides its
-// own LDS waits and barrier stalls.
-constexpr int kWaves = TTL_GEMM_WAVES;
+constexpr int kBK = 64;                    // k per stage (128-B global row pieces)
+constexpr int kWaves = 8;                  // two per SIMD, 128 x 64 outputs each
 constexpr int kThreads = 64 * kWaves;
-constexpr int kStages = TTL_GEMM_STAGES;
+constexpr int kStages = 2;                 // two 64-KiB stages
 constexpr int kWM = 128;                   // rows per wave
 constexpr int kWavesN = kWaves / (kBM / kWM);
 constexpr int kWN = kBN / kWavesN;         // weight columns per wave (2 x kWavesN wave grid)
@@ -81,250 +63,9 @@ constexpr int kRowsPer256 = 256 / (2 * kBK);  // staged rows per 256 B of LDS
 constexpr int kRowsPerCopy = 1024 / (2 * kBK);
 constexpr int kKK = kBK / 16;              // k16 slices per stage
 
-static_assert(kBK == 32 || kBK == 64, "stage depth");
-static_assert(kStages >= 2 && kStages <= 5 && kStages * kStageElems * 2 <= 160 * 1024, "LDS ring");
-static_assert(kBCopies % 2 == 0, "[k][n] copies come in k-row-parity pairs");
+static_assert(kStages * kStageElems * 2 <= 160 * 1024, "LDS ring");
 
-template <int MODE, bool WNK>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
-void gemm_bf16_kernel(const GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages * kStageElems];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / kWavesN;  // rows wm*128 .. +127
-  const int wn = wave % kWavesN;  // weight columns wn*kWN .. +kWN-1
-
-  int tile_m, tile_n;
-  tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tile_m, tile_n);
-  const int m0 = tile_m * kBM;
-  const int n0 = tile_n * (MODE == kSiluMul ? kBN / 2 : kBN);  // first output column of the tile
-  const int nk = (p.K + kBK - 1) / kBK;
-  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds);
-
-  // ---- Copy offsets, fixed for the whole k loop (the descriptors move with k0).
-  // [rows][kBK] staging (A, and B when WNK): copy i of the wave is block q = kACopies*wave + i of
-  // kRowsPerCopy rows; lane l lands in row q*kRowsPerCopy + l/kChunks at slot l%kChunks, which holds
-  // k-chunk slot ^ ((row / kRowsPer256) % kChunks).
-  uint32_t a_off[kACopies];
-  int a_kc[kACopies];  // first k of the chunk each copy lane moves, for the k-tail test
-#pragma unroll
-  for (int i = 0; i < kACopies; ++i) {
-    const int row = (kACopies * wave + i) * kRowsPerCopy + lane / kChunks;
-    const int chunk = (lane % kChunks) ^ ((row / kRowsPer256) % kChunks);
-    a_kc[i] = chunk * 8;
-    a_off[i] = (m0 + row < p.M) ? (uint32_t)(((int64_t)row * p.lda + chunk * 8) * 2) : kOob;
-  }
-  uint32_t b_off[kBCopies];
-  int b_kc[kBCopies];  // k of each copy lane (first k of its chunk, or its k row), for the k-tail test
-#pragma unroll
-  for (int i = 0; i < kBCopies; ++i) {
-    const int q = kBCopies * wave + i;
-    bool ok;
-    if (WNK) {
-      const int n = q * kRowsPerCopy + lane / kChunks;  // tile column = staged row
-      const int chunk = (lane % kChunks) ^ ((n / kRowsPer256) % kChunks);
-      const int64_t wrow = weight_column<MODE, kWN>(p, n0, n & ~7, ok) + (n & 7);
-      b_off[i] = ok ? (uint32_t)((wrow * p.ldb + chunk * 8) * 2) : kOob;
-      b_kc[i] = chunk * 8;
-    } else {
-      // copy q covers k rows 2q, 2q+1: lane l lands in row 2q + l/32 at slot l%32, holding chunk
-      // (l%32) ^ (4*(row%4)), row%4 = 2*(q%2) + l/32 = 2*(i%2) + l/32.
-      const int krow = 2 * q + (lane >> 5);
-      const int chunk = (lane & 31) ^ (4 * (2 * (i & 1) + (lane >> 5)));
-      const int64_t wcol = weight_column<MODE, kWN>(p, n0, chunk * 8, ok);
-      b_off[i] = ok ? (uint32_t)(((int64_t)krow * p.ldb + wcol) * 2) : kOob;
-      b_kc[i] = krow;
-    }
-  }
-
-  auto copy_tile = [&](int t, bool ktail) {
-    const int k0 = t * kBK;
-    const uint32_t st = lds0 + (uint32_t)((t % kStages) * kStageElems * 2);
-    const i32x4_t ad =
-        buffer_desc(p.A + (int64_t)m0 * p.lda + k0, ((int64_t)(p.M - m0 - 1) * p.lda + (p.K - k0)) * 2);
-#pragma unroll
-    for (int i = 0; i < kACopies; ++i) {
-      const uint32_t off = (ktail && k0 + a_kc[i] >= p.K) ? kOob : a_off[i];
-      copy16_to_lds(ad, off, st + (kACopies * wave + i) * 1024);
-    }
-    // B: the rows of W^T (b_rows of them, pitch ldb) from column k0, or k rows k0.. of W.
-    const i32x4_t bd =
-        WNK ? buffer_desc(p.B + k0, ((int64_t)(p.b_rows - 1) * p.ldb + (p.K - k0)) * 2)
-            : buffer_desc(p.B + (int64_t)k0 * p.ldb, (int64_t)(p.K - k0) * p.ldb * 2);
-#pragma unroll
-    for (int i = 0; i < kBCopies; ++i) {
-      const uint32_t off = (ktail && k0 + b_kc[i] >= p.K) ? kOob : b_off[i];
-      copy16_to_lds(bd, off, st + kAElems * 2 + (kBCopies * wave + i) * 1024);
-    }
-  };
-
-  // ---- Fragment reads (element offsets within a stage).
-  // [rows][kBK] staging: row r, k-chunk kk*2 + lane/32 at slot chunk ^ ((r / kRowsPer256) % kChunks);
-  // for the rows a wave reads, the swizzle term is ((lane%32) / kRowsPer256) % kChunks.
-  const int a_r = lane & 31;
-  const int a_half = lane >> 5;
-  const int rs = (a_r / kRowsPer256) % kChunks;
-  int ra_off[kKK], rb_off[kKK];
-#pragma unroll
-  for (int kk = 0; kk < kKK; ++kk) {
-    const int slot = (kk * 2 + a_half) ^ rs;
-    ra_off[kk] = (wm * kWM + a_r) * kBK + slot * 8;
-    rb_off[kk] = kAElems + (wn * kWN + a_r) * kBK + slot * 8;  // WNK: B rows are weight columns
-  }
-  // [k][n] staging: 16-lane group g = lane/16 reads k row kk*16 + 8*(g/2) + 4*h + (lane%16)/4 at
-  // n = wn*64 + ni*32 + 16*(g%2) + 4*(lane%4): chunk 8*wn + 4*ni + c with c = 2*(g%2) + (lane%4)/2,
-  // stored at slot chunk ^ (4*(k%4)) where k%4 = (lane%16)/4.
-  int rt_off[kNI];
-  {
-    const int krow = 8 * (lane >> 5) + ((lane & 15) >> 2);
-    const int x = 4 * ((lane & 15) >> 2);
-    const int c = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-#pragma unroll
-    for (int ni = 0; ni < kNI; ++ni)
-      rt_off[ni] = kAElems + krow * kBN + (((kWN / 8) * wn + 4 * ni + c) ^ x) * 8 + 4 * (lane & 1);
-  }
-
-  bf16x8_t af[2][4], bv[2][kNI];
-  auto read_frags = [&](int t, int kk, int buf) {
-    const uint16_t* st = lds + (t % kStages) * kStageElems;
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-      af[buf][mi] = *reinterpret_cast<const bf16x8_t*>(st + ra_off[kk] + mi * 32 * kBK);
-#pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) {
-      if (WNK) {
-        bv[buf][ni] = *reinterpret_cast<const bf16x8_t*>(st + rb_off[kk] + ni * 32 * kBK);
-      } else {
-        const uint16_t* b = st + rt_off[ni] + kk * 16 * kBN;
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b));
-        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b + 4 * kBN));
-        bv[buf][ni] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-    }
-  };
-
-  f32x16_t acc[4][kNI];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < kNI; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
-
-  auto mfma_block = [&](int buf) {
-    // Weight block as the first operand: lane l then holds output row (l & 31) and, in
-    // accumulator register r, output column 8*(r/4) + 4*(l/32) + r%4 of the 32 x 32 block.
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < kNI; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[buf][ni], af[buf][mi], acc[mi][ni], 0, 0, 0);
-  };
-  auto interleave_hint = [&]() {
-    // The MFMAs of a slice with the next slice's fragment reads placed one after each MFMA.
-    constexpr int kReads = 4 + (WNK ? 1 : 2) * kNI, kMfma = 4 * kNI;
-#pragma unroll
-    for (int i = 0; i < kReads; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-    }
-    if (kMfma > kReads) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
-  };
-
-  // One k-tile: the MFMAs of each k16 slice overlap the reads of the next; the barrier that
-  // publishes tile kt+1 sits before the MFMAs of the last slice, which overlap the first reads of
-  // tile kt+1.  (Issuing the next tile's copies spread over the slices instead of in one burst at
-  // the start measured slower.)
-  auto compute_tile = [&](int kt, auto wait) {
-#pragma unroll
-    for (int kk = 0; kk + 1 < kKK; ++kk) {
-      read_frags(kt, kk + 1, (kk + 1) & 1);
-      mfma_block(kk & 1);
-      interleave_hint();
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    wait();
-    lds_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < nk) read_frags(kt + 1, 0, 0);
-    mfma_block((kKK - 1) & 1);
-    interleave_hint();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  const bool ktail = (p.K % kBK) != 0;
-  // Prologue: tiles 0 .. kStages-2 in flight, tile 0 landed and its first fragments read.
-  for (int t = 0; t < kStages - 1 && t < nk; ++t) copy_tile(t, ktail && t == nk - 1);
-  if (nk >= kStages - 1) wait_vmcnt<(kStages - 2) * kLoads>();
-  else wait_vmcnt<0>();
-  lds_barrier();
-  read_frags(0, 0, 0);
-
-  int kt = 0;
-  // Steady state: the copy of tile kt + kStages - 1 refills the stage of tile kt - 1, which every
-  // wave left behind at the barrier inside step kt - 1; before the barrier of step kt, tile kt+1
-  // must have landed, i.e. at most the kStages - 2 newer tiles' copies may still be in flight.
-  for (; kt + kStages - 1 < nk; ++kt) {
-    copy_tile(kt + kStages - 1, ktail && kt + kStages - 1 == nk - 1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute_tile(kt, [] { wait_vmcnt<(kStages - 2) * kLoads>(); });
-  }
-  // Drain: no more copies; before each barrier only the tiles after kt+1 may still be in flight.
-  for (; kt < nk; ++kt) {
-    const int newer = nk - 1 - (kt + 1);
-    compute_tile(kt, [&] {
-      if (newer >= 3) wait_vmcnt<(kStages >= 5 ? 3 * kLoads : 0)>();
-      else if (newer == 2) wait_vmcnt<(kStages >= 4 ? 2 * kLoads : 0)>();
-      else if (newer == 1) wait_vmcnt<kLoads>();
-      else wait_vmcnt<0>();
-    });
-  }
-
-  // Epilogue straight from the accumulators: each lane owns 4 consecutive columns of one row per
-  // register group, stored as one 8-byte piece.
-  const int row_base = m0 + wm * kWM + a_r;
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    const int row = row_base + mi * 32;
-    if (row >= p.M) continue;
-    uint16_t* crow = p.C + (int64_t)row * p.ldc;
-    if (MODE == kPlain) {
-#pragma unroll
-      for (int ni = 0; ni < kNI; ++ni)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = n0 + wn * kWN + ni * 32 + g * 8 + a_half * 4;
-          if (col < p.N) {
-            u32x2_t v;
-            v.x = pack_bf16x2(acc[mi][ni][4 * g + 0], acc[mi][ni][4 * g + 1]);
-            v.y = pack_bf16x2(acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]);
-            *reinterpret_cast<u32x2_t*>(crow + col) = v;
-          }
-        }
-    } else {
-#pragma unroll
-      for (int ni = 0; ni < kNI / 2; ++ni)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = n0 + wn * (kWN / 2) + ni * 32 + g * 8 + a_half * 4;
-        if (col < p.N) {
-          float a[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            a[e] = silu_mul(acc[mi][ni][4 * g + e], acc[mi][ni + kNI / 2][4 * g + e]);
-          u32x2_t v;
-          v.x = pack_bf16x2(a[0], a[1]);
-          v.y = pack_bf16x2(a[2], a[3]);
-          *reinterpret_cast<u32x2_t*>(crow + col) = v;
-        }
-      }
-    }
-  }
-}
-
-// ---- Ping-pong schedule of the same tile.
+// ---- Ping-pong schedule.
 //
 // The two row halves of the tile (waves 0-3: rows 0..127, waves 4-7: rows 128..255; one wave of
 // each half per SIMD) alternate between two phases, offset by one phase, with a workgroup barrier
@@ -407,7 +148,11 @@ void gemm_pingpong_kernel(const GemmParams p) {
     }
   };
 
-  // ---- Fragment reads of a whole tile (same LDS layouts as the kernel above).
+  // ---- Fragment reads of a whole tile.  [rows][64 k] staging: row r, k-chunk 2*kk + lane/32 at
+  // slot chunk ^ ((r/2) % 8); for the rows a wave reads the swizzle term is ((lane%32) / 2) % 8.
+  // [64 k][256 n] staging, read with ds_read_b64_tr_b16: 16-lane group g = lane/16 reads k row
+  // 16*kk + 8*(g/2) + 4*h + (lane%16)/4 at n = 64*wn + 32*ni + 16*(g%2) + 4*(lane%4), i.e. chunk
+  // 8*wn + 4*ni + 2*(g%2) + (lane%4)/2, stored at slot chunk ^ (4 * (k%4)), k%4 = (lane%16)/4.
   const int a_r = lane & 31;
   const int a_half = lane >> 5;
   const int rs = (a_r / kRowsPer256) % kChunks;
@@ -514,7 +259,8 @@ void gemm_pingpong_kernel(const GemmParams p) {
   }
   if (wm == 0) phase_end();  // matches group 1's last phase
 
-  // Epilogue (as in the kernel above).
+  // Epilogue straight from the accumulators: each lane owns 4 consecutive columns of one row per
+  // register group, stored as one 8-byte piece.
   const int row_base = m0 + wm * kWM + a_r;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
@@ -557,13 +303,8 @@ void gemm_pingpong_kernel(const GemmParams p) {
 
 template <int MODE, bool WNK>
 void launch_one(const GemmParams& p, hipStream_t stream) {
-#if TTL_GEMM_PINGPONG
   hipLaunchKernelGGL((gemm_pingpong_kernel<MODE, WNK>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
                      dim3(kThreads), 0, stream, p);
-#else
-  hipLaunchKernelGGL((gemm_bf16_kernel<MODE, WNK>), dim3((unsigned)(p.tiles_m * p.tiles_n)),
-                     dim3(kThreads), 0, stream, p);
-#endif
 }
 
 }  // namespace

@@ -338,11 +338,7 @@ __global__ __launch_bounds__(256) void splitk_finalize_kernel(const GemmParams p
 
 template <int MODE, bool WNK, int MB>
 void launch_one(const GemmParams& p, hipStream_t stream) {
-#ifdef TTL_SKINNY_STAGES
-  constexpr int kStages = MB == 4 ? 3 : TTL_SKINNY_STAGES;
-#else
   constexpr int kStages = 3;  // MB 1, 2: 60 / 72 KiB, two workgroups per CU; MB 4: 96 KiB
-#endif
   const unsigned grid = (unsigned)(p.splits * p.tiles_m * p.tiles_n);
   if (MODE == kSiluMul && p.splits > 1) {
     // Partial sums only: the gate and up columns run as two plain column segments of 2N outputs
