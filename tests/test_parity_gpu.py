@@ -114,7 +114,10 @@ def test_row(ttl, gemm_path, b, k, n, t, x_is_parallel, layout):
 @pytest.mark.parametrize("t,b,n,with_residual", [(2, 16, 256, True), (8, 5, 4096, True),
                                                   (1, 3, 8, True), (4, 33, 8192, False),
                                                   (3, 7, 4104, True), (2, 4, 16384, True),
-                                                  (2, 2, 65536, True)])
+                                                  (2, 2, 65536, True),
+                                                  # the many-row launch shapes of n = 4096 and 8192
+                                                  (4, 1100, 4096, True), (2, 2600, 4096, False),
+                                                  (8, 1030, 8192, True), (3, 4100, 8192, True)])
 def test_reduce_rmsnorm(ttl, t, b, n, with_residual):
     P = wl.random_bf16((t, b, n), 50 + n)
     R = wl.random_bf16((b, n), 51 + n) if with_residual else None
