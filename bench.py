@@ -8,8 +8,9 @@ intermediate 28672, 3584 per rank), over one batch of tokens:
   3. reduce_partials_rmsnorm   sum of the 8 partials + residual, RMSNorm -> residual_out, y
 The other seven ranks' partials are computed once before timing (their work is identical in
 shape to rank 0's and would run on the other GPUs).  The weight is the logical W[k, n] of the
-statement Y = X·W, stored as W[k][n] (--layout kn, the default) or transposed as W^T[n][k]
-(--layout nk, the storage of PyTorch-style Linear weights).
+statement Y = X·W, stored as W[k][n] (--layout kn, the default), transposed as W^T[n][k]
+(--layout nk, the storage of PyTorch-style Linear weights), or packed in 64 x 128 blocks whose
+128-column strips are contiguous (--layout blk, packed once before timing).
 
 The secondary 64-token decode line cycles the simulated rank from step to step, so that successive
 steps read different weight slices (1.4 GB in all) and the timing is not served from the 256-MB
@@ -73,8 +74,8 @@ def parse():
     ap.add_argument("--batch", type=int, default=4096, help="tokens per step (4096 prefill; 64 decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the secondary 64-token decode line")
-    ap.add_argument("--layout", choices=("kn", "nk"), default="kn",
-                    help="weight storage: kn = W[k][n], nk = W^T[n][k]")
+    ap.add_argument("--layout", choices=("kn", "nk", "blk"), default="kn",
+                    help="weight storage: kn = W[k][n], nk = W^T[n][k], blk = 64 x 128 blocks")
     ap.add_argument("--cpu-rows", type=int, default=32, help="token rows in the CPU oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the CPU oracle sample until this much time has passed")
@@ -95,16 +96,27 @@ def parse():
     return ap.parse_args()
 
 
+def layout_code(ttl, layout):
+    return {"kn": ttl.W_KN, "nk": ttl.W_NK, "blk": ttl.W_BLOCKED}[layout]
+
+
+def stored_weight(ttl, W, lay):
+    """The logical weight W[k, n] in storage `lay` (a copy for nk and blk)."""
+    if lay == ttl.W_NK:
+        return W.t().contiguous()
+    if lay == ttl.W_BLOCKED:
+        return ttl.pack_weight_blocked(W)
+    return W
+
+
 def run_mlp(ttl, torch, w, b, steps, warmup, seed, layout, rotate_ranks=False):
     from tensor_transformer_linear_amd import workloads as wl
     dev = "cuda"
     inp = wl.mlp_inputs(w, b, seed=seed, device=dev)
     X, R, gamma, Wgu, Wd = inp["X"], inp["R"], inp["gamma"], inp["Wgu"], inp["Wd"]
-    lay = ttl.W_NK if layout == "nk" else ttl.W_KN
-    if lay == ttl.W_NK:  # the same logical weights, stored transposed (set-up, not timed)
-        Wgu_s, Wd_s = Wgu.t().contiguous(), Wd.t().contiguous()
-    else:
-        Wgu_s, Wd_s = Wgu, Wd
+    lay = layout_code(ttl, layout)
+    # the same logical weights in the chosen storage (set-up, not timed)
+    Wgu_s, Wd_s = stored_weight(ttl, Wgu, lay), stored_weight(ttl, Wd, lay)
     t, H, I = w.t, w.hidden, w.intermediate
     Ir = I // t
     sp = ttl.merged_gate_up_split(I, t)
@@ -177,6 +189,7 @@ def yardstick(torch, w, layout):
     products only (no SiLU·up, no column map: the rank's weight slice is a separate dense tensor).
     Decode shapes cycle through 8 weight copies so that the Infinity Cache does not hold them."""
     H, Ir = w.hidden, w.intermediate // w.t
+    layout = "nk" if layout == "nk" else "kn"  # no blocked storage in hipBLASLt: W[k][n] stands in
     out = {}
     for M, K, N, name in ((4096, H, 2 * Ir, "gate_up_b4096"), (4096, Ir, H, "down_b4096"),
                           (64, H, 2 * Ir, "gate_up_b64"), (64, Ir, H, "down_b64")):
@@ -231,18 +244,25 @@ def config_table(ttl, torch, layout, reps=20, warmup=3):
     (b < 512) cycle the simulated rank from repetition to repetition so that the weight slices are
     not served from the Infinity Cache."""
     from tensor_transformer_linear_amd import workloads as wl
-    lay = ttl.W_NK if layout == "nk" else ttl.W_KN
     dev = "cuda"
+    names = {ttl.W_KN: "kn", ttl.W_NK: "nk", ttl.W_BLOCKED: "blk"}
 
-    def stored(W):
-        return W.t().contiguous() if lay == ttl.W_NK else W
+    def storage_for(t, weights):
+        """The requested storage, or W[k][n] where a blocked weight would not fit the shapes
+        (k % 64, n % 128, and (k / t) % 64 for row weights).  weights: (W, is_row) pairs."""
+        lay = layout_code(ttl, layout)
+        if lay == ttl.W_BLOCKED and not all(W.shape[0] % 64 == 0 and W.shape[1] % 128 == 0 and
+                                            (not row or (W.shape[0] // t) % 64 == 0)
+                                            for W, row in weights):
+            return ttl.W_KN
+        return lay
 
-    def col_op(name, X, W, split, epi, Y, t, n_w, n_out):
+    def col_op(name, X, W, split, epi, Y, t, n_w, n_out, lay):
         b, k = X.shape
         return (name, lambda r: ttl.shard_linear_col(X, W, t, r, split, epi, Y=Y, w_layout=lay),
                 gemm_flops(b, k, n_w), 2.0 * (b * k + k * n_w + b * n_out))
 
-    def row_op(name, X, W, P, t, k, n, parallel):
+    def row_op(name, X, W, P, t, k, n, parallel, lay):
         b = X.shape[0]
         kr = k // t
         return (name, lambda r: ttl.shard_linear_row(X, W, t, r, parallel, P=P[r], w_layout=lay),
@@ -275,7 +295,7 @@ def config_table(ttl, torch, layout, reps=20, warmup=3):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / (replays * cycle) * 1e3
 
-    def report(wname, b, t, us, ops, graph_us):
+    def report(wname, b, t, us, ops, graph_us, lay):
         kern = {}
         for name, _, fl, by in ops:
             u = us[name]
@@ -283,7 +303,7 @@ def config_table(ttl, torch, layout, reps=20, warmup=3):
             bound = "mfma" if fl / by > RIDGE_FLOP_PER_BYTE else "hbm"
             kern[name] = {"us": u, "tflops": tf, "gbs": gbs, "bound": bound,
                           "frac": tf / PEAK_BF16_TFLOPS if bound == "mfma" else gbs / PEAK_HBM_GBS}
-        print(json.dumps({"workload": wname, "tokens": b, "t": t, "weight_storage": layout,
+        print(json.dumps({"workload": wname, "tokens": b, "t": t, "weight_storage": names[lay],
                           "step_us": sum(us.values()), "step_us_graph": graph_us, "kernels": kern}),
               flush=True)
 
@@ -292,19 +312,20 @@ def config_table(ttl, torch, layout, reps=20, warmup=3):
             inp = wl.mlp_inputs(w, b, seed=0, device=dev)
             t, H, I = w.t, w.hidden, w.intermediate
             Ir = I // t
-            Wgu, Wd = stored(inp["Wgu"]), stored(inp["Wd"])
+            lay = storage_for(t, ((inp["Wgu"], False), (inp["Wd"], True)))
+            Wgu, Wd = stored_weight(ttl, inp["Wgu"], lay), stored_weight(ttl, inp["Wd"], lay)
             act = torch.empty((b, Ir), dtype=torch.bfloat16, device=dev)
             P = torch.empty((t, b, H), dtype=torch.bfloat16, device=dev)
             rout, y = torch.empty((b, H), dtype=torch.bfloat16, device=dev), torch.empty((b, H), dtype=torch.bfloat16, device=dev)
             sp = ttl.merged_gate_up_split(I, t)
-            ops = [col_op("gate_up_silu", inp["X"], Wgu, sp, ttl.EPI_SILU_MUL, act, t, 2 * Ir, Ir),
-                   row_op("down", act, Wd, P, t, I, H, True),
+            ops = [col_op("gate_up_silu", inp["X"], Wgu, sp, ttl.EPI_SILU_MUL, act, t, 2 * Ir, Ir, lay),
+                   row_op("down", act, Wd, P, t, I, H, True, lay),
                    red_op("reduce_rmsnorm", P, inp["gamma"], w.eps, inp["R"], rout, y)]
             for r in range(t):  # every rank's partial once
                 ops[0][1](r)
                 ops[1][1](r)
             cyc = t if b < 512 else 1
-            report(w.name, b, t, _time_chain(torch, ops, reps, warmup, cyc), ops, graph_step_us(ops, cyc))
+            report(w.name, b, t, _time_chain(torch, ops, reps, warmup, cyc), ops, graph_step_us(ops, cyc), lay)
             del inp, Wgu, Wd, act, P, rout, y, ops
             torch.cuda.empty_cache()
 
@@ -317,32 +338,36 @@ def config_table(ttl, torch, layout, reps=20, warmup=3):
             sp = ttl.qkv_split(nq, nkv, hd, t)
             n_qkv = (nq + 2 * nkv) * hd
             w_r = ttl.split_width(sp, n_qkv, t)
-            Wqkv, Wo = stored(inp["Wqkv"]), stored(inp["Wo"])
+            weights = [(inp["Wqkv"], False), (inp["Wo"], True)]
+            if is_layer:
+                weights += [(inp["Wgu"], False), (inp["Wd"], True)]
+            lay = storage_for(t, weights)
+            Wqkv, Wo = stored_weight(ttl, inp["Wqkv"], lay), stored_weight(ttl, inp["Wo"], lay)
             qkv = torch.empty((b, w_r), dtype=torch.bfloat16, device=dev)
             Pa = torch.empty((t, b, H), dtype=torch.bfloat16, device=dev)
             rout, y = torch.empty((b, H), dtype=torch.bfloat16, device=dev), torch.empty((b, H), dtype=torch.bfloat16, device=dev)
             gamma = inp["gamma_attn"] if is_layer else inp["gamma"]
-            ops = [col_op("qkv", inp["X"], Wqkv, sp, ttl.EPI_NONE, qkv, t, w_r, w_r),
-                   row_op("o_proj", inp["A"], Wo, Pa, t, nq * hd, H, False),
+            ops = [col_op("qkv", inp["X"], Wqkv, sp, ttl.EPI_NONE, qkv, t, w_r, w_r, lay),
+                   row_op("o_proj", inp["A"], Wo, Pa, t, nq * hd, H, False, lay),
                    red_op("reduce_rmsnorm_attn", Pa, gamma, w.eps, inp["R"], rout, y)]
             keep = [Wqkv, Wo, qkv, Pa, rout, y]
             if is_layer:
                 I = w.intermediate
                 Ir = I // t
-                Wgu, Wd = stored(inp["Wgu"]), stored(inp["Wd"])
+                Wgu, Wd = stored_weight(ttl, inp["Wgu"], lay), stored_weight(ttl, inp["Wd"], lay)
                 act = torch.empty((b, Ir), dtype=torch.bfloat16, device=dev)
                 Pm = torch.empty((t, b, H), dtype=torch.bfloat16, device=dev)
                 rout2, y2 = torch.empty((b, H), dtype=torch.bfloat16, device=dev), torch.empty((b, H), dtype=torch.bfloat16, device=dev)
                 gsp = ttl.merged_gate_up_split(I, t)
-                ops += [col_op("gate_up_silu", y, Wgu, gsp, ttl.EPI_SILU_MUL, act, t, 2 * Ir, Ir),
-                        row_op("down", act, Wd, Pm, t, I, H, True),
+                ops += [col_op("gate_up_silu", y, Wgu, gsp, ttl.EPI_SILU_MUL, act, t, 2 * Ir, Ir, lay),
+                        row_op("down", act, Wd, Pm, t, I, H, True, lay),
                         red_op("reduce_rmsnorm_mlp", Pm, inp["gamma_mlp"], w.eps, rout, rout2, y2)]
                 keep += [Wgu, Wd, act, Pm, rout2, y2]
             for r in range(t):  # every rank's partials once, in chain order
                 for _, fn, _, _ in ops:
                     fn(r)
             cyc = t if b < 512 else 1
-            report(w.name, b, t, _time_chain(torch, ops, reps, warmup, cyc), ops, graph_step_us(ops, cyc))
+            report(w.name, b, t, _time_chain(torch, ops, reps, warmup, cyc), ops, graph_step_us(ops, cyc), lay)
             del inp, ops, keep
             torch.cuda.empty_cache()
 
@@ -364,7 +389,7 @@ def read_power_clock():
 def steady_state(ttl, torch, w, layout):
     """Each b=4096 GEMM of the rank, ours and hipBLASLt's, at the power limit: run back to back for
     2 s, sample power and clock once in the middle, then time 30 launches."""
-    lay = ttl.W_NK if layout == "nk" else ttl.W_KN
+    lay = layout_code(ttl, layout)
     b, H, I, t = 4096, w.hidden, w.intermediate, w.t
     Ir = I // t
     X = torch.randn(b, H, device="cuda").to(torch.bfloat16)
@@ -381,7 +406,9 @@ def steady_state(ttl, torch, w, layout):
         Wg_r, Wd_r = Wg_r.t().contiguous(), Wd_r.t().contiguous()
         mm_g = lambda: torch.matmul(X, Wg_r.t())
         mm_d = lambda: torch.matmul(act, Wd_r.t())
-    else:
+    else:  # hipBLASLt has no blocked storage: its products read W[k][n]
+        if lay == ttl.W_BLOCKED:
+            Wgu, Wd = ttl.pack_weight_blocked(Wgu), ttl.pack_weight_blocked(Wd)
         mm_g = lambda: torch.matmul(X, Wg_r)
         mm_d = lambda: torch.matmul(act, Wd_r)
     cases = (("ours_gate_up_silu", 2.0 * b * H * 2 * Ir,

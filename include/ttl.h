@@ -71,9 +71,19 @@ typedef int32_t ttl_epilogue;
  *             weights ([out_features, in_features]) are kept; the matrix cores read it without a
  *             transpose.  The rows one call reads (from the rank's first to its last weight
  *             column; for the row-parallel call all n rows) must span less than 2 GiB. */
+/*   TTL_W_BLOCKED: [k][n] cut into blocks of 64 k-rows x 128 columns, each block row-major (its 128
+ *             columns contiguous), the blocks of one 128-column strip stored one after another
+ *             down k, the strips one after another along n: element (i, j) lives at
+ *             ((j/128)·(k/64) + i/64)·8192 + (i%64)·128 + j%128.  Needs k % 64 == 0 and
+ *             n % 128 == 0 (and, for the row-parallel call, (k/t) % 64 == 0); ttl_pack_weight_blocked
+ *             converts a [k][n] weight.  Each 128-column strip is one contiguous range, which the
+ *             weight-bound decode GEMMs stream faster than rows of [k][n] or [n][k] (HBM reads whole
+ *             DRAM pages instead of 128-256-byte pieces of many rows).  The strips one call reads
+ *             must span less than 2 GiB. */
 typedef int32_t ttl_weight_layout;
 #define TTL_W_KN 0
 #define TTL_W_NK 1
+#define TTL_W_BLOCKED 2
 
 #define TTL_MAX_SEGMENTS 3
 
@@ -108,8 +118,9 @@ typedef struct {
  *   Y      output, row stride n_r (or n_r/2), caller-allocated.
  * Errors: NULL X/W/Y -> NULL; b,k,n <= 0 -> SHAPE; bad t/rank -> RANK; a segment width not
  * divisible by its part count, part count neither t nor a divisor of t, or widths not summing to n
- * -> NOT_DIVISIBLE; misalignment -> ALIGN; SILU_MUL with an unsuitable split, nseg outside 1..3, an
- * unknown w_layout, or TTL_W_NK rows read spanning 2 GiB or more -> UNSUPPORTED.
+ * -> NOT_DIVISIBLE; misalignment, or TTL_W_BLOCKED with k % 64 != 0 or n % 128 != 0 -> ALIGN;
+ * SILU_MUL with an unsuitable split, nseg outside 1..3, an unknown w_layout, or TTL_W_NK rows
+ * (TTL_W_BLOCKED strips) read spanning 2 GiB or more -> UNSUPPORTED.
  */
 ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k,
                             const uint16_t* W, int64_t n, ttl_weight_layout w_layout,
@@ -152,7 +163,8 @@ ttl_status shard_linear_col_gathered(const uint16_t* X, int64_t b, int64_t k,
  *   W      the full weight W[k, n] stored as `w_layout` says; W's rows [r·k/t, (r+1)·k/t) are read.
  *   P      [b, n] bf16 partial for this rank (for simulated ranks, the caller passes P + r·b·n of
  *          a [t, b, n] buffer).
- * Errors: as above; k not divisible by t -> NOT_DIVISIBLE.
+ * Errors: as above; k not divisible by t -> NOT_DIVISIBLE; TTL_W_BLOCKED with (k/t) % 64 != 0 ->
+ * ALIGN.
  */
 ttl_status shard_linear_row(const uint16_t* X, int64_t b, int64_t k,
                             int32_t x_is_parallel,
@@ -212,6 +224,16 @@ ttl_status reduce_scatter_partials_rmsnorm(const uint16_t* P, int32_t t, int64_t
                                            void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
+/*
+ * ttl_pack_weight_blocked — W_blk = W stored as TTL_W_BLOCKED (see above), from W[k][n] row-major.
+ * Set-up work for a weight that is used many times; not on the hot path.
+ *
+ *   W      [k, n] bf16, row-major.      W_blk  k·n bf16, caller-allocated, must not overlap W.
+ * Errors: NULL W/W_blk -> NULL; k, n <= 0 or k·n >= 2^31 -> SHAPE; k % 64, n % 128 or 16-byte
+ * alignment -> ALIGN; overlapping buffers -> UNSUPPORTED.  Enqueued on `stream`.
+ */
+ttl_status ttl_pack_weight_blocked(const uint16_t* W, int64_t k, int64_t n, uint16_t* W_blk, void* stream);
+
 const char* ttl_last_error(void);
 
 /* Library version: major * 10000 + minor * 100 + patch. */

@@ -127,7 +127,9 @@ void gemm_pingpong_kernel(const GemmParams p) {
         const int krow = 2 * q + (lane >> 5);
         const int chunk = (lane & 31) ^ (4 * (krow % 4));
         const int64_t wcol = weight_column<MODE, kWN>(p, n0, chunk * 8, ok);
-        c_off[i] = ok ? (uint32_t)(((int64_t)krow * p.ldb + wcol) * 2) : kOob;
+        c_off[i] = !ok ? kOob
+                 : p.w_blk ? blocked_offset(krow, wcol, p.ldb)
+                           : (uint32_t)(((int64_t)krow * p.ldb + wcol) * 2);
         c_k[i] = krow;
       }
     }
@@ -138,8 +140,9 @@ void gemm_pingpong_kernel(const GemmParams p) {
     const bool tail = ktail && t == nk - 1;
     const i32x4_t d =
         wm == 0 ? buffer_desc(p.A + (int64_t)m0 * p.lda + k0, ((int64_t)(p.M - m0 - 1) * p.lda + (p.K - k0)) * 2)
-                : (WNK ? buffer_desc(p.B + k0, ((int64_t)(p.b_rows - 1) * p.ldb + (p.K - k0)) * 2)
-                       : buffer_desc(p.B + (int64_t)k0 * p.ldb, (int64_t)(p.K - k0) * p.ldb * 2));
+                : (WNK       ? buffer_desc(p.B + k0, ((int64_t)(p.b_rows - 1) * p.ldb + (p.K - k0)) * 2)
+                   : p.w_blk ? blocked_desc(p.B, p.b_rows, k0)
+                             : buffer_desc(p.B + (int64_t)k0 * p.ldb, (int64_t)(p.K - k0) * p.ldb * 2));
     const uint32_t st = lds0 + (uint32_t)((t % kStages) * kStageElems * 2) + (wm == 0 ? 0u : kAElems * 2u);
 #pragma unroll
     for (int i = 0; i < kCopies; ++i) {

@@ -101,7 +101,9 @@ void gemm_bigwave_kernel(const GemmParams p) {
       const int krow = 2 * q + (lane >> 5);
       const int chunk = (lane & 31) ^ (4 * (krow % 4));
       const int64_t wcol = weight_column<MODE, kWN>(p, n0, chunk * 8, ok);
-      c_off[kACopies + i] = ok ? (uint32_t)(((int64_t)krow * p.ldb + wcol) * 2) : kOob;
+      c_off[kACopies + i] = !ok ? kOob
+                          : p.w_blk ? blocked_offset(krow, wcol, p.ldb)
+                                    : (uint32_t)(((int64_t)krow * p.ldb + wcol) * 2);
     }
   }
   auto a_desc = [&](int t) {
@@ -111,7 +113,8 @@ void gemm_bigwave_kernel(const GemmParams p) {
   auto b_desc = [&](int t) {
     const int k0 = (kt0 + t) * kBK;
     return WNK ? buffer_desc(p.B + k0, ((int64_t)(p.b_rows - 1) * p.ldb + (p.K - k0)) * 2)
-               : buffer_desc(p.B + (int64_t)k0 * p.ldb, (int64_t)(p.K - k0) * p.ldb * 2);
+           : p.w_blk ? blocked_desc(p.B, p.b_rows, k0)
+                     : buffer_desc(p.B + (int64_t)k0 * p.ldb, (int64_t)(p.K - k0) * p.ldb * 2);
   };
   // Copy i of tile t into stage t % 2: the wave's 8-KiB block of the A or B half plus a constant.
   const uint32_t wave_lds = lds0 + (uint32_t)(wave * kACopies * 1024);

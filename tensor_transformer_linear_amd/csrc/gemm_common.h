@@ -76,6 +76,19 @@ __device__ inline void wait_vmcnt() {
 // keeps the compiler from moving LDS accesses across the barrier.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Byte offset of element (krow, wcol) of a k-tile of 64 rows in a blocked weight (64 x 128 blocks,
+// 128-column strips `strip` elements apart), from the k-tile's first block of strip 0.
+__device__ inline uint32_t blocked_offset(int krow, int64_t wcol, int64_t strip) {
+  return (uint32_t)(((wcol >> 7) * strip + krow * 128 + (wcol & 127)) * 2);
+}
+
+// Buffer descriptor of k-tile k0 / 64 of a blocked weight: from its block in strip 0 to the end of
+// the strips the call reads.
+__device__ inline i32x4_t blocked_desc(const uint16_t* B, int64_t b_elems, int k0) {
+  const int64_t e0 = (int64_t)(k0 / 64) * 8192;
+  return buffer_desc(B + e0, (b_elems - e0) * 2);
+}
+
 // Tile order of the 256 x 256-tile kernels.  Consecutive workgroups are dealt to different XCDs
 // (8 on MI355X), each with its own L2: the block index is remapped so that each XCD runs a compact
 // run of tiles, and tiles are walked in groups of kGroupM row-tiles (all columns of a group before

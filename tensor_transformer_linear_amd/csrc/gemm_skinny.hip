@@ -123,7 +123,9 @@ void gemm_skinny_kernel(const GemmParams p) {
       const int krow = 4 * q + (lane >> 4);
       const int chunk = (lane & 15) ^ (4 * (lane >> 4));
       const int64_t wcol = tile_weight_column<MODE>(p, tile_n, chunk * 8, ok);
-      b_off[i] = ok ? (uint32_t)(((int64_t)krow * p.ldb + wcol) * 2) : kOob;
+      b_off[i] = !ok ? kOob
+               : p.w_blk ? blocked_offset(krow, wcol, p.ldb)
+                         : (uint32_t)(((int64_t)krow * p.ldb + wcol) * 2);
       b_kc[i] = krow;
     }
   }
@@ -140,8 +142,9 @@ void gemm_skinny_kernel(const GemmParams p) {
       copy16_to_lds(ad, off, st + (kACopies * wave + i) * 1024);
     }
     const i32x4_t bd =
-        WNK ? buffer_desc(p.B + k0, ((int64_t)(p.b_rows - 1) * p.ldb + (p.K - k0)) * 2)
-            : buffer_desc(p.B + (int64_t)k0 * p.ldb, (int64_t)(p.K - k0) * p.ldb * 2);
+        WNK       ? buffer_desc(p.B + k0, ((int64_t)(p.b_rows - 1) * p.ldb + (p.K - k0)) * 2)
+        : p.w_blk ? blocked_desc(p.B, p.b_rows, k0)
+                  : buffer_desc(p.B + (int64_t)k0 * p.ldb, (int64_t)(p.K - k0) * p.ldb * 2);
 #pragma unroll
     for (int i = 0; i < kBCopies; ++i) {
       const uint32_t off = (ktail && k0 + b_kc[i] >= p.K) ? kOob : b_off[i];

@@ -24,7 +24,12 @@ struct GemmParams {
   int64_t gate_w0, up_w0; // mode 1: weight columns of act column 0's gate and up inputs
   int32_t tiles_m, tiles_n;
   int32_t w_nk;           // weight stored transposed ([n][k])
-  int64_t b_rows;         // w_nk: rows of W^T reachable from B
+  // w_blk: weight stored in 64 x 128 blocks, 128-column strips (TTL_W_BLOCKED).  B is the first
+  // block of the first strip the call reads (at its first k row), column 0 the strip's first
+  // column; ldb is the strip stride in elements (k_full * 128); element (k, j) of the call is at
+  // B + (j / 128) * ldb + (k / 64) * 8192 + (k % 64) * 128 + j % 128.
+  int32_t w_blk;
+  int64_t b_rows;         // w_nk: rows of W^T reachable from B; w_blk: elements reachable from B
   // Split-K launches (splits > 1): fp32 partial sums [splits][M][ws_ld], split s covering k-tiles
   // [s * kt_per_split, (s + 1) * kt_per_split).
   float* ws;
@@ -90,5 +95,9 @@ struct ReduceNormParams {
 };
 
 hipError_t launch_reduce_rmsnorm(const ReduceNormParams& p, hipStream_t stream);
+
+// W[k][n] row-major -> the blocked layout (64 x 128 blocks, 128-column strips); k % 64 == 0,
+// n % 128 == 0, k * n < 2^31.
+hipError_t launch_pack_blocked(const uint16_t* W, int64_t k, int64_t n, uint16_t* W_blk, hipStream_t stream);
 
 }  // namespace ttl

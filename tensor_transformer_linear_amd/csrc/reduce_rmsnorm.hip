@@ -161,12 +161,13 @@ hipError_t launch(const ReduceNormParams& p, hipStream_t stream) {
 hipError_t launch_reduce_rmsnorm(const ReduceNormParams& p, hipStream_t stream) {
   const int64_t pieces = p.n / 8;  // n <= 65536, checked by the caller
   if (p.b >= 1024) {
-    // Many rows (prefill): 256 threads per row, four partials' loads in flight per thread; the
-    // rows in flight per CU keep HBM busy.  How many rows fit on the chip at once depends on the
-    // shape (registers per thread, threads per row), and a row count just above a whole number of
-    // such rounds leaves a slow last round: the shapes below were measured at the rows of the
-    // workloads (n = 4096: 18 µs against 21 µs at t = 4, b = 2048; n = 8192: 64 µs against 67 µs
-    // at t = 8, b = 2176, equal at b = 2048 and 4096).
+    // Many rows (prefill): a few hundred threads per row, two to four partials' loads in flight
+    // per thread; the rows in flight per CU keep HBM busy.  How many rows fit on the chip at once
+    // depends on the shape (pieces per thread, threads per row, loads in flight), and a row count
+    // just above a whole number of such rounds leaves a slow last round: the shapes below were
+    // measured at the rows of the workloads, each repeated on one set of inputs (n = 4096: 18 µs
+    // against 21 µs at t = 4, b = 2048; n = 8192: 64 µs against 67 µs at t = 8, b = 2176, equal at
+    // b = 2048 and 4096).
     if (pieces <= 64) return launch<1, 64, 4>(p, stream);
     if (pieces <= 128) return launch<1, 128, 4>(p, stream);
     if (pieces <= 256) return launch<1, 256, 4>(p, stream);

@@ -61,7 +61,7 @@ ttl_status col_setup(const char* who, const uint16_t* X, int64_t b, int64_t k, c
     return fail(TTL_ERR_RANK, "%s: need t >= 1 and 0 <= rank < t (t=%d rank=%d)", who, t, rank);
   if (epi != TTL_EPI_NONE && epi != TTL_EPI_SILU_MUL)
     return fail(TTL_ERR_UNSUPPORTED, "%s: unknown epilogue %d", who, epi);
-  if (w_layout != TTL_W_KN && w_layout != TTL_W_NK)
+  if (w_layout != TTL_W_KN && w_layout != TTL_W_NK && w_layout != TTL_W_BLOCKED)
     return fail(TTL_ERR_UNSUPPORTED, "%s: unknown weight layout %d", who, w_layout);
 
   ttl_col_split sp;
@@ -124,6 +124,25 @@ ttl_status col_setup(const char* who, const uint16_t* X, int64_t b, int64_t k, c
                   "%s: the [n][k] rows this rank reads must span less than 2 GiB", who);
     for (int s = 0; s < sp.nseg; ++s) wcol0[s] -= row_lo;
   }
+  // A blocked weight is addressed from the first 128-column strip the rank reads; the strips up to
+  // its last column must span less than 2 GiB.
+  int64_t strip_lo = 0, strip_hi = 0;
+  if (w_layout == TTL_W_BLOCKED) {
+    if (k % 64 != 0 || n % 128 != 0)
+      return fail(TTL_ERR_ALIGN, "%s: a blocked weight needs k %% 64 == 0 and n %% 128 == 0 (k=%lld n=%lld)",
+                  who, (long long)k, (long long)n);
+    int64_t lo = wcol0[0], hi = wcol0[0] + width[0];
+    for (int s = 1; s < sp.nseg; ++s) {
+      lo = wcol0[s] < lo ? wcol0[s] : lo;
+      hi = wcol0[s] + width[s] > hi ? wcol0[s] + width[s] : hi;
+    }
+    strip_lo = lo / 128;
+    strip_hi = (hi + 127) / 128;
+    if ((strip_hi - strip_lo) * k * 128 * 2 >= kMaxNkBytes)
+      return fail(TTL_ERR_UNSUPPORTED, "%s: the blocked strips this rank reads must span less than 2 GiB",
+                  who);
+    for (int s = 0; s < sp.nseg; ++s) wcol0[s] -= strip_lo * 128;
+  }
 
   p.A = X;
   p.lda = k;
@@ -131,6 +150,12 @@ ttl_status col_setup(const char* who, const uint16_t* X, int64_t b, int64_t k, c
   p.B = p.w_nk ? W + row_lo * k : W;
   p.ldb = p.w_nk ? k : n;
   p.b_rows = row_hi - row_lo;
+  if (w_layout == TTL_W_BLOCKED) {
+    p.w_blk = 1;
+    p.B = W + strip_lo * k * 128;
+    p.ldb = k * 128;
+    p.b_rows = (strip_hi - strip_lo) * k * 128;
+  }
   p.M = (int32_t)b;
   p.K = (int32_t)k;
   if (epi == TTL_EPI_SILU_MUL) {
@@ -206,6 +231,19 @@ extern "C" {
 
 const char* ttl_last_error(void) { return g_last_error.c_str(); }
 
+ttl_status ttl_pack_weight_blocked(const uint16_t* W, int64_t k, int64_t n, uint16_t* W_blk, void* stream) {
+  static const char* who = "ttl_pack_weight_blocked";
+  if (W == nullptr || W_blk == nullptr) return fail(TTL_ERR_NULL, "%s: W and W_blk must be non-NULL", who);
+  if (k <= 0 || n <= 0 || k * n >= ((int64_t)1 << 31))
+    return fail(TTL_ERR_SHAPE, "%s: need k, n >= 1 and k*n < 2^31 (k=%lld n=%lld)", who, (long long)k,
+                (long long)n);
+  if (k % 64 != 0 || n % 128 != 0 || !aligned16(W) || !aligned16(W_blk))
+    return fail(TTL_ERR_ALIGN, "%s: need k %% 64 == 0, n %% 128 == 0 and 16-byte aligned buffers", who);
+  if (overlaps(W, k * n * 2, W_blk, k * n * 2))
+    return fail(TTL_ERR_UNSUPPORTED, "%s: W and W_blk must not overlap", who);
+  return launch_status(ttl::launch_pack_blocked(W, k, n, W_blk, static_cast<hipStream_t>(stream)), who);
+}
+
 int32_t ttl_version(void) { return 100; }  // 0.1.0
 
 ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k, const uint16_t* W, int64_t n,
@@ -251,7 +289,7 @@ ttl_status shard_linear_row(const uint16_t* X, int64_t b, int64_t k, int32_t x_i
                 (long long)k, (long long)n);
   if (t < 1 || rank < 0 || rank >= t)
     return fail(TTL_ERR_RANK, "%s: need t >= 1 and 0 <= rank < t (t=%d rank=%d)", who, t, rank);
-  if (w_layout != TTL_W_KN && w_layout != TTL_W_NK)
+  if (w_layout != TTL_W_KN && w_layout != TTL_W_NK && w_layout != TTL_W_BLOCKED)
     return fail(TTL_ERR_UNSUPPORTED, "%s: unknown weight layout %d", who, w_layout);
   if (k % t != 0)
     return fail(TTL_ERR_NOT_DIVISIBLE, "%s: k=%lld is not divisible by t=%d", who, (long long)k, t);
@@ -266,6 +304,12 @@ ttl_status shard_linear_row(const uint16_t* X, int64_t b, int64_t k, int32_t x_i
     return fail(TTL_ERR_SHAPE, "%s: row pitch of X or W exceeds the supported range", who);
   if (w_layout == TTL_W_NK && n * k * 2 >= kMaxNkBytes)
     return fail(TTL_ERR_UNSUPPORTED, "%s: a [n][k] weight must stay below 2 GiB", who);
+  if (w_layout == TTL_W_BLOCKED) {
+    if (k % 64 != 0 || kr % 64 != 0 || n % 128 != 0)
+      return fail(TTL_ERR_ALIGN, "%s: a blocked weight needs k %% 64, (k/t) %% 64 and n %% 128 == 0", who);
+    if (n * k * 2 >= kMaxNkBytes)
+      return fail(TTL_ERR_UNSUPPORTED, "%s: a blocked weight must stay below 2 GiB", who);
+  }
 
   ttl::GemmParams p = {};
   p.A = x_is_parallel ? X : X + (int64_t)rank * kr;
@@ -275,6 +319,14 @@ ttl_status shard_linear_row(const uint16_t* X, int64_t b, int64_t k, int32_t x_i
   p.B = p.w_nk ? W + (int64_t)rank * kr : W + (int64_t)rank * kr * n;
   p.ldb = p.w_nk ? k : n;
   p.b_rows = n;
+  if (w_layout == TTL_W_BLOCKED) {
+    // the rank's k rows start at block row r*(k/t)/64 of every strip
+    const int64_t e0 = (int64_t)rank * kr / 64 * 8192;
+    p.w_blk = 1;
+    p.B = W + e0;
+    p.ldb = k * 128;
+    p.b_rows = n / 128 * k * 128 - e0;
+  }
   p.C = P;
   p.ldc = n;
   p.M = (int32_t)b;

@@ -29,10 +29,11 @@ EPI_NONE = 0
 EPI_SILU_MUL = 1
 W_KN = 0  # weight stored [k][n] (row stride n)
 W_NK = 1  # weight stored transposed, [n][k] (row stride k), as PyTorch-style Linear weights are
+W_BLOCKED = 2  # [k][n] in 64 x 128 blocks, 128-column strips contiguous (see pack_weight_blocked)
 MAX_SEGMENTS = 3
 EXPORTED = ("shard_linear_col", "shard_linear_col_gathered", "shard_linear_row",
-            "reduce_partials_rmsnorm", "reduce_scatter_partials_rmsnorm", "ttl_last_error",
-            "ttl_version")
+            "reduce_partials_rmsnorm", "reduce_scatter_partials_rmsnorm", "ttl_pack_weight_blocked",
+            "ttl_last_error", "ttl_version")
 
 
 class ColSplit(ctypes.Structure):
@@ -60,6 +61,8 @@ _lib.reduce_scatter_partials_rmsnorm.restype = ctypes.c_int32
 _lib.reduce_scatter_partials_rmsnorm.argtypes = [_c_u16p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                                  ctypes.c_int32, _c_u16p, _c_u16p, ctypes.c_float,
                                                  _c_u16p, _c_u16p, ctypes.c_void_p]
+_lib.ttl_pack_weight_blocked.restype = ctypes.c_int32
+_lib.ttl_pack_weight_blocked.argtypes = [_c_u16p, ctypes.c_int64, ctypes.c_int64, _c_u16p, ctypes.c_void_p]
 _lib.ttl_last_error.restype = ctypes.c_char_p
 _lib.ttl_last_error.argtypes = []
 _lib.ttl_version.restype = ctypes.c_int32
@@ -145,6 +148,16 @@ def _weight_dims(W: torch.Tensor, w_layout: int):
     else:
         k, n = W.shape
     return k, n
+
+
+def pack_weight_blocked(W: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The [k, n] weight W re-laid out for W_BLOCKED (64 x 128 blocks, 128-column strips); the
+    result is a [k, n] tensor whose memory holds that layout.  k % 64 == 0 and n % 128 == 0."""
+    k, n = W.shape
+    if out is None:
+        out = torch.empty((k, n), dtype=torch.bfloat16, device=W.device)
+    _check(_lib.ttl_pack_weight_blocked(_dev_ptr(W, "W"), k, n, _dev_ptr(out, "out"), _stream_handle(stream)))
+    return out
 
 
 def shard_linear_col(X: torch.Tensor, W: torch.Tensor, t: int, rank: int,

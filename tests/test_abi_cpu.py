@@ -60,6 +60,7 @@ def test_status_codes_match_header():
     assert codes["TTL_ERR_HIP"] == ttl.ERR_HIP
     assert codes["TTL_EPI_SILU_MUL"] == ttl.EPI_SILU_MUL
     assert codes["TTL_W_KN"] == ttl.W_KN and codes["TTL_W_NK"] == ttl.W_NK
+    assert codes["TTL_W_BLOCKED"] == ttl.W_BLOCKED
     assert codes["TTL_MAX_SEGMENTS"] == ttl.MAX_SEGMENTS
     assert ttl.version() >= 100
 
@@ -80,6 +81,10 @@ def _rs(P=A, t=2, b=16, n=256, rank=0, R=B, gamma=D, eps=1e-5, Rout=B, Y=C):
 
 def _row(X=A, b=16, k=688, par=1, W=B, n=256, t=2, rank=0, P=C, lay=0):
     return ttl.lib().shard_linear_row(X, b, k, par, W, n, lay, t, rank, P, None)
+
+
+def _pack(W=A, k=256, n=1024, out=B):
+    return ttl.lib().ttl_pack_weight_blocked(W, k, n, out, None)
 
 
 def _red(P=A, t=2, b=16, n=256, R=B, gamma=D, eps=1e-5, Rout=B, Y=C):
@@ -104,7 +109,10 @@ def _red(P=A, t=2, b=16, n=256, R=B, gamma=D, eps=1e-5, Rout=B, Y=C):
     (lambda: _col(epi=1), ttl.ERR_UNSUPPORTED, "two equal segments"),
     (lambda: _col(epi=1, split=ttl.make_split((704, 672), (2, 2))), ttl.ERR_UNSUPPORTED, "two equal"),
     (lambda: _col(epi=7), ttl.ERR_UNSUPPORTED, "epilogue"),
-    (lambda: _col(lay=2), ttl.ERR_UNSUPPORTED, "weight layout"),
+    (lambda: _col(lay=3), ttl.ERR_UNSUPPORTED, "weight layout"),
+    (lambda: _col(lay=ttl.W_BLOCKED), ttl.ERR_ALIGN, "blocked weight"),          # n % 128 != 0
+    (lambda: _col(k=200, n=1536, lay=ttl.W_BLOCKED), ttl.ERR_ALIGN, "blocked weight"),
+    (lambda: _col(k=16384, n=131072, t=1, lay=ttl.W_BLOCKED), ttl.ERR_UNSUPPORTED, "2 GiB"),
     (lambda: _col(k=16384, n=65536, t=1, lay=1), ttl.ERR_UNSUPPORTED, "2 GiB"),
     (lambda: _col(k=16384, n=131072, t=2, lay=1), ttl.ERR_UNSUPPORTED, "2 GiB"),
     (lambda: _colg(Y=None), ttl.ERR_NULL, "non-NULL"),
@@ -113,6 +121,16 @@ def _red(P=A, t=2, b=16, n=256, R=B, gamma=D, eps=1e-5, Rout=B, Y=C):
     (lambda: _colg(epi=1), ttl.ERR_UNSUPPORTED, "two equal segments"),
     (lambda: _colg(k=252), ttl.ERR_ALIGN, "multiples of 8"),
     (lambda: _row(lay=-1), ttl.ERR_UNSUPPORTED, "weight layout"),
+    (lambda: _row(lay=ttl.W_BLOCKED), ttl.ERR_ALIGN, "blocked weight"),          # k % 64 != 0
+    (lambda: _row(k=1024, t=32, lay=ttl.W_BLOCKED), ttl.ERR_ALIGN, "blocked weight"),  # k/t = 32
+    (lambda: _row(k=16384, n=65536, t=1, lay=ttl.W_BLOCKED), ttl.ERR_UNSUPPORTED, "2 GiB"),
+    (lambda: _pack(W=None), ttl.ERR_NULL, "non-NULL"),
+    (lambda: _pack(k=0), ttl.ERR_SHAPE, ""),
+    (lambda: _pack(k=65536, n=65536), ttl.ERR_SHAPE, "2^31"),
+    (lambda: _pack(k=100), ttl.ERR_ALIGN, "k % 64"),
+    (lambda: _pack(n=1000), ttl.ERR_ALIGN, "n % 128"),
+    (lambda: _pack(out=B + 8), ttl.ERR_ALIGN, "aligned"),
+    (lambda: _pack(out=A + 16), ttl.ERR_UNSUPPORTED, "overlap"),
     (lambda: _row(P=None), ttl.ERR_NULL, "non-NULL"),
     (lambda: _row(n=0), ttl.ERR_SHAPE, ""),
     (lambda: _row(rank=5), ttl.ERR_RANK, ""),

@@ -255,6 +255,57 @@ def test_short_last_round_split_by_rows(ttl, monkeypatch, silu, layout):
     assert torch.equal(outs["auto"][:2048], outs["tiled"][:2048])
 
 
+def _blocked_reference(W):
+    """The TTL_W_BLOCKED memory order of a [k, n] weight, by index arithmetic on the host."""
+    k, n = W.shape
+    return W.reshape(k // 64, 64, n // 128, 128).permute(2, 0, 1, 3).reshape(k, n).contiguous()
+
+
+def test_pack_weight_blocked(ttl):
+    W = wl.random_bf16((192, 384), 130)
+    got = ttl.pack_weight_blocked(gpu(W))
+    assert torch.equal(got.cpu(), _blocked_reference(W))
+
+
+@pytest.mark.parametrize("b", [5, 300])
+def test_blocked_weights_match_kn_bitwise(ttl, gemm_path, b):
+    """Weights stored in 64 x 128 blocks give bit-identical results to [k][n] storage through every
+    kernel (only the addresses differ), for SiLU·up, qkv and gathered column calls and the row
+    call; one of each is also checked against the oracle."""
+    k, I, t = 512, 1024, 4
+    X = gpu(wl.random_bf16((b, k), 131))
+    Wgu = wl.random_bf16((k, 2 * I), 132, std=0.05)
+    sp = ttl.merged_gate_up_split(I, t)
+    Wgu_kn, Wgu_blk = gpu(Wgu), ttl.pack_weight_blocked(gpu(Wgu))
+    for r in (0, t - 1):
+        a = ttl.shard_linear_col(X, Wgu_kn, t, r, sp, ttl.EPI_SILU_MUL, w_layout=ttl.W_KN)
+        c = ttl.shard_linear_col(X, Wgu_blk, t, r, sp, ttl.EPI_SILU_MUL, w_layout=ttl.W_BLOCKED)
+        torch.cuda.synchronize()
+        assert torch.equal(a, c), f"SiLU·up rank {r}"
+    ref = oracle.silu_mul(oracle.col_shard(f64(X.cpu()), f64(Wgu), oracle.merged_gate_up_split(I, t), t, t - 1))
+    assert_close(from_gpu(c), ref, f"blocked SiLU·up b={b}")
+    # qkv: 8 q heads, 4 kv heads of 64 (n = 1024)
+    Wqkv = wl.random_bf16((k, 1024), 133, std=0.05)
+    spq = ttl.qkv_split(8, 4, 64, t)
+    a = ttl.shard_linear_col(X, gpu(Wqkv), t, 1, spq, w_layout=ttl.W_KN)
+    c = ttl.shard_linear_col(X, ttl.pack_weight_blocked(gpu(Wqkv)), t, 1, spq, w_layout=ttl.W_BLOCKED)
+    g = torch.full((b, t * 256), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ttl.shard_linear_col_gathered(X, ttl.pack_weight_blocked(gpu(Wqkv)), t, 1, spq, Y_all=g,
+                                  w_layout=ttl.W_BLOCKED)
+    torch.cuda.synchronize()
+    assert torch.equal(a, c) and torch.equal(g[:, 256:512], a), "qkv"
+    # row: k = 1024, rank rows of 256
+    Wd = wl.random_bf16((1024, 768), 134, std=0.05)
+    Xr = gpu(wl.random_bf16((b, 1024), 135))
+    for r in range(t):
+        a = ttl.shard_linear_row(Xr, gpu(Wd), t, r, False, w_layout=ttl.W_KN)
+        c = ttl.shard_linear_row(Xr, ttl.pack_weight_blocked(gpu(Wd)), t, r, False, w_layout=ttl.W_BLOCKED)
+        torch.cuda.synchronize()
+        assert torch.equal(a, c), f"row rank {r}"
+    assert_close(from_gpu(c), oracle.row_shard(f64(Xr.cpu()), f64(Wd), t, t - 1, x_is_parallel=False),
+                 f"blocked row b={b}")
+
+
 def test_bitwise_deterministic(ttl, gemm_path):
     b, k, I, t = 300, 512, 1024, 2
     X, Wgu = gpu(wl.random_bf16((b, k), 80)), gpu(wl.random_bf16((k, 2 * I), 81, std=0.05))
