@@ -141,6 +141,28 @@ def test_reduce_residual_in_place(ttl):
     assert_close(from_gpu(y), yref, "in-place y")
 
 
+def test_empty_batch(ttl):
+    """No tokens (b = 0): every entry point returns empty outputs and leaves other memory alone."""
+    k, I, H, t = 256, 688, 256, 2
+    X = gpu(wl.random_bf16((0, k), 1))
+    Wgu = gpu(wl.random_bf16((k, 2 * I), 2, std=0.05))
+    Wd = gpu(wl.random_bf16((I, H), 3, std=0.05))
+    act = ttl.shard_linear_col(X, Wgu, t, 1, ttl.merged_gate_up_split(I, t), ttl.EPI_SILU_MUL)
+    assert act.shape == (0, I // t)
+    g = torch.full((0, I), 7, dtype=torch.bfloat16, device="cuda")
+    ttl.shard_linear_col_gathered(X, Wgu, t, 1, ttl.merged_gate_up_split(I, t), ttl.EPI_SILU_MUL, Y_all=g)
+    P = torch.empty((t, 0, H), dtype=torch.bfloat16, device="cuda")
+    ttl.shard_linear_row(act, Wd, t, 1, True, P=P[1])
+    gamma = gpu(wl.random_bf16((H,), 4))
+    guard = torch.full((8,), 3, dtype=torch.bfloat16, device="cuda")
+    rout, y = ttl.reduce_partials_rmsnorm(P, gamma, 1e-5, None)
+    assert rout.shape == (0, H) and y.shape == (0, H)
+    rout, y = ttl.reduce_scatter_partials_rmsnorm(P, gamma, 1e-5, 0, None)
+    assert rout.shape == (0, H) and y.shape == (0, H)
+    torch.cuda.synchronize()
+    assert torch.equal(guard, torch.full((8,), 3, dtype=torch.bfloat16, device="cuda"))
+
+
 @LAYOUTS
 def test_identity_and_one_hot_are_exact(ttl, gemm_path, layout):
     # W = identity: every column of the output is one column of X, exactly.
