@@ -14,7 +14,8 @@ statement Y = X·W, stored as W[k][n] (--layout kn, the default), transposed as 
 
 The secondary 64-token decode line cycles the simulated rank from step to step, so that successive
 steps read different weight slices (1.4 GB in all) and the timing is not served from the 256-MB
-Infinity Cache.
+Infinity Cache.  It is timed eagerly and, as a decode loop would run it, captured once into a HIP
+graph (eight steps, one per rank) and replayed.
 
 Inputs are synthetic and seeded (X, R ~ N(0,1); W ~ N(0,0.02); gamma ~ N(1,0.1); bf16), drawn on the
 device and resident in HBM before the timed region.  The JSON line reports whole-step throughput as
@@ -109,7 +110,7 @@ def stored_weight(ttl, W, lay):
     return W
 
 
-def run_mlp(ttl, torch, w, b, steps, warmup, seed, layout, rotate_ranks=False):
+def run_mlp(ttl, torch, w, b, steps, warmup, seed, layout, rotate_ranks=False, graph=False):
     from tensor_transformer_linear_amd import workloads as wl
     dev = "cuda"
     inp = wl.mlp_inputs(w, b, seed=seed, device=dev)
@@ -131,19 +132,20 @@ def run_mlp(ttl, torch, w, b, steps, warmup, seed, layout, rotate_ranks=False):
         ttl.shard_linear_row(act, Wd_s, t, r, True, P=P[r], stream=stream, w_layout=lay)
     torch.cuda.synchronize()
 
-    def step(i, ev=None):
+    def step(i, ev=None, st=None):
+        st = stream if st is None else st
         r = i % t if rotate_ranks else 0
         if ev is not None:
-            ev[0].record(stream)
-        ttl.shard_linear_col(X, Wgu_s, t, r, sp, ttl.EPI_SILU_MUL, Y=act, stream=stream, w_layout=lay)
+            ev[0].record(st)
+        ttl.shard_linear_col(X, Wgu_s, t, r, sp, ttl.EPI_SILU_MUL, Y=act, stream=st, w_layout=lay)
         if ev is not None:
-            ev[1].record(stream)
-        ttl.shard_linear_row(act, Wd_s, t, r, True, P=P[r], stream=stream, w_layout=lay)
+            ev[1].record(st)
+        ttl.shard_linear_row(act, Wd_s, t, r, True, P=P[r], stream=st, w_layout=lay)
         if ev is not None:
-            ev[2].record(stream)
-        ttl.reduce_partials_rmsnorm(P, gamma, w.eps, R, residual_out=rout, Y=y, stream=stream)
+            ev[2].record(st)
+        ttl.reduce_partials_rmsnorm(P, gamma, w.eps, R, residual_out=rout, Y=y, stream=st)
         if ev is not None:
-            ev[3].record(stream)
+            ev[3].record(st)
 
     for i in range(warmup):
         step(i)
@@ -180,8 +182,31 @@ def run_mlp(ttl, torch, w, b, steps, warmup, seed, layout, rotate_ranks=False):
     for name, d in kern.items():
         d["frac_mfma_peak"] = d.get("tflops", 0.0) / PEAK_BF16_TFLOPS
         d["frac_hbm_peak"] = d["gbs"] / PEAK_HBM_GBS
-    return {"ms_per_step": ms_step, "flops": f_col + f_row, "kernels": kern,
-            "tensors": (X, Wgu, Wd, R, gamma), "step": step}
+    res = {"ms_per_step": ms_step, "flops": f_col + f_row, "kernels": kern,
+           "tensors": (X, Wgu, Wd, R, gamma), "step": step}
+    if graph:
+        # The same steps captured once into a HIP graph (one step per simulated rank, as a decode
+        # loop would replay them) and replayed: the step time without host launch overhead.  The
+        # split-K workspace was allocated by the eager steps above.
+        cycle = t if rotate_ranks else 1
+        g = torch.cuda.CUDAGraph()
+        gs = torch.cuda.Stream()
+        gs.wait_stream(stream)
+        with torch.cuda.stream(gs):
+            with torch.cuda.graph(g, stream=gs):
+                for i in range(cycle):
+                    step(i, st=gs)
+        stream.wait_stream(gs)
+        g.replay()
+        torch.cuda.synchronize()
+        replays = max(1, steps // cycle)
+        t0.record(stream)
+        for _ in range(replays):
+            g.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        res["ms_per_step_graph"] = t0.elapsed_time(t1) / (replays * cycle)
+    return res
 
 
 def yardstick(torch, w, layout):
@@ -590,9 +615,11 @@ def main():
     }
     if not args.no_decode and b != 64:
         dec = run_mlp(ttl, torch, w, 64, args.steps, args.warmup, seed=1, layout=args.layout,
-                      rotate_ranks=True)
+                      rotate_ranks=True, graph=True)
         out["decode64"] = {"ms_per_step": dec["ms_per_step"], "ranks": "cycled 0..7 step by step",
                            "tflops": dec["flops"] / (dec["ms_per_step"] * 1e9),
+                           "ms_per_step_graph": dec["ms_per_step_graph"],
+                           "tflops_graph": dec["flops"] / (dec["ms_per_step_graph"] * 1e9),
                            "kernels": dec["kernels"]}
         del dec
     out["yardstick"] = None if args.no_yardstick else yardstick(torch, w, args.layout)
