@@ -141,6 +141,46 @@ def test_reduce_residual_in_place(ttl):
     assert_close(from_gpu(y), yref, "in-place y")
 
 
+@pytest.mark.parametrize("case", ["col_k_max", "col_k_max_nk", "col_n_max", "row_k_max"])
+@pytest.mark.parametrize("kern", ["auto", "tiled"])
+def test_maximum_row_pitches(ttl, monkeypatch, case, kern):
+    """The largest row pitches the ABI accepts: X rows of k = 2^21 elements (the row GEMM reading
+    the upper half of each row), and W rows of n = 2^23 columns.  Every 32-bit byte offset inside a
+    tile is then within a factor of two of its limit; sampled outputs match the oracle."""
+    monkeypatch.delenv("TTL_GEMM_SPLITS", raising=False)
+    if kern == "auto":
+        monkeypatch.delenv("TTL_GEMM_KERNEL", raising=False)
+    else:
+        monkeypatch.setenv("TTL_GEMM_KERNEL", kern)
+    if case == "col_n_max":
+        b, k, n = 8, 64, 1 << 23
+    else:
+        b, k, n = 260, 1 << 21, 128
+    X = wl.random_bf16((b, k), 300, device="cuda")
+    W = wl.random_bf16((k, n), 301, std=0.02, device="cuda")
+    rows = [0, 1, 127, 128, 255, 256, b - 1] if b > 256 else list(range(b))
+    if case == "row_k_max":
+        t, r = 2, 1
+        P = ttl.shard_linear_row(X, W, t, r, False)
+        ref = oracle.row_shard(from_gpu(X[rows]), from_gpu(W), t, r, x_is_parallel=False)
+        assert_close(from_gpu(P[rows]), ref, f"row k=2^21 {kern}")
+        return
+    if case == "col_n_max":
+        gen = np.random.default_rng(302)
+        cols = np.r_[0:64, n - 64:n, np.sort(gen.choice(np.arange(64, n - 64), 64, replace=False))]
+        Y = ttl.shard_linear_col(X, W, 1, 0)
+        Wc = W[:, torch.as_tensor(cols, device="cuda")].contiguous()
+        ref = oracle.col_shard(from_gpu(X), from_gpu(Wc), oracle.plain_split(len(cols), 1), 1, 0)
+        assert_close(from_gpu(Y)[:, cols], ref, f"col n=2^23 {kern}")
+        return
+    if case == "col_k_max_nk":
+        Y = ttl.shard_linear_col(X, W.t().contiguous(), 1, 0, w_layout=ttl.W_NK)
+    else:
+        Y = ttl.shard_linear_col(X, W, 1, 0)
+    ref = oracle.col_shard(from_gpu(X[rows]), from_gpu(W), oracle.plain_split(n, 1), 1, 0)
+    assert_close(from_gpu(Y[rows]), ref, f"{case} {kern}")
+
+
 def test_empty_batch(ttl):
     """No tokens (b = 0): every entry point returns empty outputs and leaves other memory alone."""
     k, I, H, t = 256, 688, 256, 2
