@@ -116,9 +116,7 @@ typedef struct {
  *          section 14 of "vLLM Code Reading (Section 5)" (jeremyguo.space).  gate and up never
  *          reach memory.
  *   Y      output, row stride n_r (or n_r/2), caller-allocated.
- * b = 0 is an empty call: everything is validated as usual, nothing is enqueued, and X and Y may
- * be NULL.
- * Errors: NULL W, or NULL X/Y with b > 0 -> NULL; b < 0 or k, n <= 0 -> SHAPE; bad t/rank -> RANK; a segment width not
+ * Errors: NULL X/W/Y -> NULL; b,k,n <= 0 -> SHAPE; bad t/rank -> RANK; a segment width not
  * divisible by its part count, part count neither t nor a divisor of t, or widths not summing to n
  * -> NOT_DIVISIBLE; misalignment, or TTL_W_BLOCKED with k % 64 != 0 or n % 128 != 0 -> ALIGN;
  * SILU_MUL with an unsuitable split, nseg outside 1..3, an unknown w_layout, or TTL_W_NK rows
@@ -165,7 +163,6 @@ ttl_status shard_linear_col_gathered(const uint16_t* X, int64_t b, int64_t k,
  *   W      the full weight W[k, n] stored as `w_layout` says; W's rows [r·k/t, (r+1)·k/t) are read.
  *   P      [b, n] bf16 partial for this rank (for simulated ranks, the caller passes P + r·b·n of
  *          a [t, b, n] buffer).
- * b = 0 is an empty call (X and P may be NULL), as for shard_linear_col.
  * Errors: as above; k not divisible by t -> NOT_DIVISIBLE; TTL_W_BLOCKED with (k/t) % 64 != 0 ->
  * ALIGN.
  */
@@ -191,9 +188,7 @@ ttl_status shard_linear_row(const uint16_t* X, int64_t b, int64_t k,
  *             ascending r, then the residual); may alias `residual`.
  *   Y         [b, n] bf16: h / sqrt(mean_j h_j² + eps) · gamma, from the fp32 h.
  * The summation order is fixed, so results are bitwise reproducible run to run.
- * b = 0 is an empty call: validated, nothing enqueued; P, residual, residual_out and Y may be NULL.
- * Errors: NULL gamma, or NULL P/residual_out/Y with b > 0 -> NULL; t < 1 -> RANK; b < 0, n <= 0 or
- * n > 65536 -> SHAPE;
+ * Errors: NULL P/gamma/residual_out/Y -> NULL; t < 1 -> RANK; b, n <= 0 or n > 65536 -> SHAPE;
  * misalignment -> ALIGN; Y aliasing an input -> UNSUPPORTED.
  */
 ttl_status reduce_partials_rmsnorm(const uint16_t* P, int32_t t, int64_t b, int64_t n,

@@ -25,9 +25,8 @@ ttl_status fail(ttl_status status, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Byte ranges [a, a+na) and [b, b+nb) overlap (an empty range overlaps nothing).
+// Byte ranges [a, a+na) and [b, b+nb) overlap.
 bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
-  if (na <= 0 || nb <= 0) return false;
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
 }
@@ -53,12 +52,11 @@ ttl_status col_setup(const char* who, const uint16_t* X, int64_t b, int64_t k, c
                      int64_t n, ttl_weight_layout w_layout, int32_t t, int32_t rank,
                      const ttl_col_split* split, ttl_epilogue epi, const uint16_t* Y,
                      ttl::GemmParams& p, int64_t& out_width) {
-  // b = 0 is an empty call: X and Y hold no element and may be NULL.
-  if (W == nullptr || (b != 0 && (X == nullptr || Y == nullptr)))
-    return fail(TTL_ERR_NULL, "%s: W, and for b > 0 X and Y, must be non-NULL", who);
-  if (b < 0 || k <= 0 || n <= 0 || b > kMaxDim || k > kMaxDim || n > kMaxDim)
-    return fail(TTL_ERR_SHAPE, "%s: need 0 <= b < 2^31 and 1 <= k, n < 2^31 (b=%lld k=%lld n=%lld)", who,
-                (long long)b, (long long)k, (long long)n);
+  if (X == nullptr || W == nullptr || Y == nullptr)
+    return fail(TTL_ERR_NULL, "%s: X, W and Y must be non-NULL", who);
+  if (b <= 0 || k <= 0 || n <= 0 || b > kMaxDim || k > kMaxDim || n > kMaxDim)
+    return fail(TTL_ERR_SHAPE, "%s: b=%lld k=%lld n=%lld must be in [1, 2^31)", who, (long long)b,
+                (long long)k, (long long)n);
   if (t < 1 || rank < 0 || rank >= t)
     return fail(TTL_ERR_RANK, "%s: need t >= 1 and 0 <= rank < t (t=%d rank=%d)", who, t, rank);
   if (epi != TTL_EPI_NONE && epi != TTL_EPI_SILU_MUL)
@@ -192,12 +190,11 @@ ttl_status col_setup(const char* who, const uint16_t* X, int64_t b, int64_t k, c
 ttl_status reduce_setup(const char* who, const uint16_t* P, int32_t t, int64_t b, int64_t n,
                         int64_t row0, int64_t rows, const uint16_t* residual, const uint16_t* gamma,
                         float eps, uint16_t* residual_out, uint16_t* Y, ttl::ReduceNormParams& p) {
-  // No rows (b = 0): P, the residual and the outputs hold no element and may be NULL.
-  if (gamma == nullptr || (rows != 0 && (P == nullptr || residual_out == nullptr || Y == nullptr)))
-    return fail(TTL_ERR_NULL, "%s: gamma, and for b > 0 P, residual_out and Y, must be non-NULL", who);
+  if (P == nullptr || gamma == nullptr || residual_out == nullptr || Y == nullptr)
+    return fail(TTL_ERR_NULL, "%s: P, gamma, residual_out and Y must be non-NULL", who);
   if (t < 1) return fail(TTL_ERR_RANK, "%s: t=%d must be >= 1", who, t);
-  if (b < 0 || n <= 0 || b > kMaxDim || n > 65536)
-    return fail(TTL_ERR_SHAPE, "%s: need 0 <= b < 2^31 and 1 <= n <= 65536 (b=%lld n=%lld)", who,
+  if (b <= 0 || n <= 0 || b > kMaxDim || n > 65536)
+    return fail(TTL_ERR_SHAPE, "%s: need 1 <= b < 2^31 and 1 <= n <= 65536 (b=%lld n=%lld)", who,
                 (long long)b, (long long)n);
   if (!(eps >= 0.0f)) return fail(TTL_ERR_SHAPE, "%s: eps must be >= 0", who);
   if (n % 8 != 0) return fail(TTL_ERR_ALIGN, "%s: n=%lld must be a multiple of 8", who, (long long)n);
@@ -256,7 +253,7 @@ ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k, const uint1
   ttl::GemmParams p;
   int64_t width = 0;
   const ttl_status st = col_setup(who, X, b, k, W, n, w_layout, t, rank, split, epi, Y, p, width);
-  if (st != TTL_OK || b == 0) return st;
+  if (st != TTL_OK) return st;
   p.C = Y;
   p.ldc = width;
   return launch_status(ttl::launch_gemm(p, static_cast<hipStream_t>(stream)), who);
@@ -274,7 +271,6 @@ ttl_status shard_linear_col_gathered(const uint16_t* X, int64_t b, int64_t k, co
   if (width * t > kMaxLda)
     return fail(TTL_ERR_SHAPE, "%s: gathered row of %lld columns exceeds the supported pitch", who,
                 (long long)(width * t));
-  if (b == 0) return TTL_OK;
   p.C = Y_all + (int64_t)rank * width;  // this rank's block of the gathered row
   p.ldc = width * t;
   return launch_status(ttl::launch_gemm(p, static_cast<hipStream_t>(stream)), who);
@@ -286,12 +282,11 @@ ttl_status shard_linear_row(const uint16_t* X, int64_t b, int64_t k, int32_t x_i
                             const uint16_t* W, int64_t n, ttl_weight_layout w_layout, int32_t t,
                             int32_t rank, uint16_t* P, void* stream) {
   static const char* who = "shard_linear_row";
-  // b = 0 is an empty call: X and P hold no element and may be NULL.
-  if (W == nullptr || (b != 0 && (X == nullptr || P == nullptr)))
-    return fail(TTL_ERR_NULL, "%s: W, and for b > 0 X and P, must be non-NULL", who);
-  if (b < 0 || k <= 0 || n <= 0 || b > kMaxDim || k > kMaxDim || n > kMaxDim)
-    return fail(TTL_ERR_SHAPE, "%s: need 0 <= b < 2^31 and 1 <= k, n < 2^31 (b=%lld k=%lld n=%lld)", who,
-                (long long)b, (long long)k, (long long)n);
+  if (X == nullptr || W == nullptr || P == nullptr)
+    return fail(TTL_ERR_NULL, "%s: X, W and P must be non-NULL", who);
+  if (b <= 0 || k <= 0 || n <= 0 || b > kMaxDim || k > kMaxDim || n > kMaxDim)
+    return fail(TTL_ERR_SHAPE, "%s: b=%lld k=%lld n=%lld must be in [1, 2^31)", who, (long long)b,
+                (long long)k, (long long)n);
   if (t < 1 || rank < 0 || rank >= t)
     return fail(TTL_ERR_RANK, "%s: need t >= 1 and 0 <= rank < t (t=%d rank=%d)", who, t, rank);
   if (w_layout != TTL_W_KN && w_layout != TTL_W_NK && w_layout != TTL_W_BLOCKED)
@@ -345,7 +340,6 @@ ttl_status shard_linear_row(const uint16_t* X, int64_t b, int64_t k, int32_t x_i
   if (b * n > kMaxOutput)
     return fail(TTL_ERR_SHAPE, "%s: output of %lld x %lld elements is too large", who, (long long)b,
                 (long long)n);
-  if (b == 0) return TTL_OK;
   return launch_status(ttl::launch_gemm(p, static_cast<hipStream_t>(stream)), who);
 }
 
@@ -356,7 +350,7 @@ ttl_status reduce_partials_rmsnorm(const uint16_t* P, int32_t t, int64_t b, int6
   ttl::ReduceNormParams p;
   const ttl_status st =
       reduce_setup(who, P, t, b, n, 0, b, residual, gamma, eps, residual_out, Y, p);
-  if (st != TTL_OK || b == 0) return st;
+  if (st != TTL_OK) return st;
   return launch_status(ttl::launch_reduce_rmsnorm(p, static_cast<hipStream_t>(stream)), who);
 }
 
@@ -374,7 +368,7 @@ ttl_status reduce_scatter_partials_rmsnorm(const uint16_t* P, int32_t t, int64_t
   ttl::ReduceNormParams p;
   const ttl_status st = reduce_setup(who, P, t, b, n, (int64_t)rank * rows, rows, residual, gamma, eps,
                                      residual_out, Y, p);
-  if (st != TTL_OK || rows == 0) return st;
+  if (st != TTL_OK) return st;
   return launch_status(ttl::launch_reduce_rmsnorm(p, static_cast<hipStream_t>(stream)), who);
 }
 

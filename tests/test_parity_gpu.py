@@ -181,26 +181,27 @@ def test_maximum_row_pitches(ttl, monkeypatch, case, kern):
     assert_close(from_gpu(Y[rows]), ref, f"{case} {kern}")
 
 
-def test_empty_batch(ttl):
-    """No tokens (b = 0): every entry point returns empty outputs and leaves other memory alone."""
+def test_empty_batch_is_a_shape_error(ttl):
+    """Sizes must be at least 1: a batch of no tokens is TTL_ERR_SHAPE at every entry point, raised
+    by the binding before anything is enqueued, and nothing is written."""
     k, I, H, t = 256, 688, 256, 2
     X = gpu(wl.random_bf16((0, k), 1))
     Wgu = gpu(wl.random_bf16((k, 2 * I), 2, std=0.05))
     Wd = gpu(wl.random_bf16((I, H), 3, std=0.05))
-    act = ttl.shard_linear_col(X, Wgu, t, 1, ttl.merged_gate_up_split(I, t), ttl.EPI_SILU_MUL)
-    assert act.shape == (0, I // t)
-    g = torch.full((0, I), 7, dtype=torch.bfloat16, device="cuda")
-    ttl.shard_linear_col_gathered(X, Wgu, t, 1, ttl.merged_gate_up_split(I, t), ttl.EPI_SILU_MUL, Y_all=g)
-    P = torch.empty((t, 0, H), dtype=torch.bfloat16, device="cuda")
-    ttl.shard_linear_row(act, Wd, t, 1, True, P=P[1])
     gamma = gpu(wl.random_bf16((H,), 4))
-    guard = torch.full((8,), 3, dtype=torch.bfloat16, device="cuda")
-    rout, y = ttl.reduce_partials_rmsnorm(P, gamma, 1e-5, None)
-    assert rout.shape == (0, H) and y.shape == (0, H)
-    rout, y = ttl.reduce_scatter_partials_rmsnorm(P, gamma, 1e-5, 0, None)
-    assert rout.shape == (0, H) and y.shape == (0, H)
-    torch.cuda.synchronize()
-    assert torch.equal(guard, torch.full((8,), 3, dtype=torch.bfloat16, device="cuda"))
+    P = torch.empty((t, 0, H), dtype=torch.bfloat16, device="cuda")
+    act = torch.empty((0, I // t), dtype=torch.bfloat16, device="cuda")
+    calls = [
+        lambda: ttl.shard_linear_col(X, Wgu, t, 1, ttl.merged_gate_up_split(I, t), ttl.EPI_SILU_MUL),
+        lambda: ttl.shard_linear_col_gathered(X, Wgu, t, 1, ttl.merged_gate_up_split(I, t), ttl.EPI_SILU_MUL),
+        lambda: ttl.shard_linear_row(act, Wd, t, 1, True),
+        lambda: ttl.reduce_partials_rmsnorm(P, gamma, 1e-5, None),
+        lambda: ttl.reduce_scatter_partials_rmsnorm(P, gamma, 1e-5, 0, None),
+    ]
+    for call in calls:
+        with pytest.raises(ttl.TTLError) as err:
+            call()
+        assert err.value.status == ttl.ERR_SHAPE, err.value
 
 
 @LAYOUTS
