@@ -52,11 +52,12 @@ ttl_status col_setup(const char* who, const uint16_t* X, int64_t b, int64_t k, c
                      int64_t n, ttl_weight_layout w_layout, int32_t t, int32_t rank,
                      const ttl_col_split* split, ttl_epilogue epi, const uint16_t* Y,
                      ttl::GemmParams& p, int64_t& out_width) {
-  if (X == nullptr || W == nullptr || Y == nullptr)
-    return fail(TTL_ERR_NULL, "%s: X, W and Y must be non-NULL", who);
+  // Sizes first: an empty tensor (a size of 0) is a shape error even where its pointer is NULL.
   if (b <= 0 || k <= 0 || n <= 0 || b > kMaxDim || k > kMaxDim || n > kMaxDim)
     return fail(TTL_ERR_SHAPE, "%s: b=%lld k=%lld n=%lld must be in [1, 2^31)", who, (long long)b,
                 (long long)k, (long long)n);
+  if (X == nullptr || W == nullptr || Y == nullptr)
+    return fail(TTL_ERR_NULL, "%s: X, W and Y must be non-NULL", who);
   if (t < 1 || rank < 0 || rank >= t)
     return fail(TTL_ERR_RANK, "%s: need t >= 1 and 0 <= rank < t (t=%d rank=%d)", who, t, rank);
   if (epi != TTL_EPI_NONE && epi != TTL_EPI_SILU_MUL)
@@ -190,12 +191,12 @@ ttl_status col_setup(const char* who, const uint16_t* X, int64_t b, int64_t k, c
 ttl_status reduce_setup(const char* who, const uint16_t* P, int32_t t, int64_t b, int64_t n,
                         int64_t row0, int64_t rows, const uint16_t* residual, const uint16_t* gamma,
                         float eps, uint16_t* residual_out, uint16_t* Y, ttl::ReduceNormParams& p) {
-  if (P == nullptr || gamma == nullptr || residual_out == nullptr || Y == nullptr)
-    return fail(TTL_ERR_NULL, "%s: P, gamma, residual_out and Y must be non-NULL", who);
-  if (t < 1) return fail(TTL_ERR_RANK, "%s: t=%d must be >= 1", who, t);
   if (b <= 0 || n <= 0 || b > kMaxDim || n > 65536)
     return fail(TTL_ERR_SHAPE, "%s: need 1 <= b < 2^31 and 1 <= n <= 65536 (b=%lld n=%lld)", who,
                 (long long)b, (long long)n);
+  if (P == nullptr || gamma == nullptr || residual_out == nullptr || Y == nullptr)
+    return fail(TTL_ERR_NULL, "%s: P, gamma, residual_out and Y must be non-NULL", who);
+  if (t < 1) return fail(TTL_ERR_RANK, "%s: t=%d must be >= 1", who, t);
   if (!(eps >= 0.0f)) return fail(TTL_ERR_SHAPE, "%s: eps must be >= 0", who);
   if (n % 8 != 0) return fail(TTL_ERR_ALIGN, "%s: n=%lld must be a multiple of 8", who, (long long)n);
   if (!aligned16(P) || !aligned16(gamma) || !aligned16(residual_out) || !aligned16(Y) ||
@@ -233,10 +234,10 @@ const char* ttl_last_error(void) { return g_last_error.c_str(); }
 
 ttl_status ttl_pack_weight_blocked(const uint16_t* W, int64_t k, int64_t n, uint16_t* W_blk, void* stream) {
   static const char* who = "ttl_pack_weight_blocked";
-  if (W == nullptr || W_blk == nullptr) return fail(TTL_ERR_NULL, "%s: W and W_blk must be non-NULL", who);
   if (k <= 0 || n <= 0 || k * n >= ((int64_t)1 << 31))
     return fail(TTL_ERR_SHAPE, "%s: need k, n >= 1 and k*n < 2^31 (k=%lld n=%lld)", who, (long long)k,
                 (long long)n);
+  if (W == nullptr || W_blk == nullptr) return fail(TTL_ERR_NULL, "%s: W and W_blk must be non-NULL", who);
   if (k % 64 != 0 || n % 128 != 0 || !aligned16(W) || !aligned16(W_blk))
     return fail(TTL_ERR_ALIGN, "%s: need k %% 64 == 0, n %% 128 == 0 and 16-byte aligned buffers", who);
   if (overlaps(W, k * n * 2, W_blk, k * n * 2))
@@ -282,11 +283,11 @@ ttl_status shard_linear_row(const uint16_t* X, int64_t b, int64_t k, int32_t x_i
                             const uint16_t* W, int64_t n, ttl_weight_layout w_layout, int32_t t,
                             int32_t rank, uint16_t* P, void* stream) {
   static const char* who = "shard_linear_row";
-  if (X == nullptr || W == nullptr || P == nullptr)
-    return fail(TTL_ERR_NULL, "%s: X, W and P must be non-NULL", who);
   if (b <= 0 || k <= 0 || n <= 0 || b > kMaxDim || k > kMaxDim || n > kMaxDim)
     return fail(TTL_ERR_SHAPE, "%s: b=%lld k=%lld n=%lld must be in [1, 2^31)", who, (long long)b,
                 (long long)k, (long long)n);
+  if (X == nullptr || W == nullptr || P == nullptr)
+    return fail(TTL_ERR_NULL, "%s: X, W and P must be non-NULL", who);
   if (t < 1 || rank < 0 || rank >= t)
     return fail(TTL_ERR_RANK, "%s: need t >= 1 and 0 <= rank < t (t=%d rank=%d)", who, t, rank);
   if (w_layout != TTL_W_KN && w_layout != TTL_W_NK && w_layout != TTL_W_BLOCKED)
