@@ -40,23 +40,33 @@ using namespace gemm;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kWM = 128, kWN = 128;      // outputs per wave (2 x 2 wave grid)
-constexpr int kMI = kWM / 32, kNI = kWN / 32;
+constexpr int kBM = 256, kBK = 64;
+constexpr int kWM = 128;                 // output rows per wave (2 x 2 wave grid)
+constexpr int kMI = kWM / 32;
 constexpr int kKK = kBK / 16;            // k16 slices per k-tile
-constexpr int kAElems = kBM * kBK, kBElems = kBK * kBN, kStageElems = kAElems + kBElems;
+constexpr int kAElems = kBM * kBK;
 constexpr int kACopies = kAElems * 2 / 1024 / kWaves;  // 1-KiB copies per wave per k-tile: 8
-constexpr int kBCopies = kBElems * 2 / 1024 / kWaves;  // 8
-constexpr int kCopies = kACopies + kBCopies;
 constexpr int kChunks = kBK / 8;         // 16-B chunks per staged [rows][k] row
 constexpr int kRowsPer256 = 256 / (2 * kBK);
 constexpr int kRowsPerCopy = 1024 / (2 * kBK);
 
-static_assert(kKK == 4 && kACopies == 8 && kBCopies == 8, "the slice schedule assumes these counts");
+static_assert(kKK == 4 && kACopies == 8, "the slice schedule assumes these counts");
 
-template <int MODE, bool WNK>
+// WN output columns per wave: 128 (256 x 256 tiles) or 64 (256 x 128 tiles, for launches that
+// have too few 256 x 256 tiles to fill the chip).  The B stage holds 64 k rows of the tile's
+// 2 * WN weight columns.
+template <int MODE, bool WNK, int WN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void gemm_bigwave_kernel(const GemmParams p) {
+  static_assert(WN == 128 || WN == 64, "wave widths built: 128 and 64 columns");
+  constexpr int kBN = 2 * WN;                    // weight columns per tile
+  constexpr int kNI = WN / 32;
+  constexpr int kMps = kMI * kNI;                // MFMAs per k16 slice: 16 or 8
+  constexpr int kBElems = kBK * kBN, kStageElems = kAElems + kBElems;
+  constexpr int kBCopies = kBElems * 2 / 1024 / kWaves;  // 8 or 4
+  constexpr int kCopies = kACopies + kBCopies;
+  constexpr int kBChunks = kBN / 8;              // 16-B chunks per staged [k][n] row: 32 or 16
+  constexpr int kKRowsPerCopy = 64 / kBChunks;   // k rows per 1-KiB copy of a [k][n] stage: 2 or 4
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * kStageElems];
 
   const int tid = threadIdx.x;
@@ -93,14 +103,14 @@ void gemm_bigwave_kernel(const GemmParams p) {
     if (WNK) {
       const int n = q * kRowsPerCopy + lane / kChunks;  // tile column = staged row
       const int chunk = (lane % kChunks) ^ ((n / kRowsPer256) % kChunks);
-      const int64_t wrow = weight_column<MODE, kWN>(p, n0, n & ~7, ok) + (n & 7);
+      const int64_t wrow = weight_column<MODE, WN>(p, n0, n & ~7, ok) + (n & 7);
       c_off[kACopies + i] = ok ? (uint32_t)((wrow * p.ldb + chunk * 8) * 2) : kOob;
     } else {
-      // [64 k][256 n]: block q holds k rows 2q, 2q+1; lane l lands in row 2q + l/32 at slot l%32,
-      // which holds n-chunk slot ^ (4 * (row % 4)).
-      const int krow = 2 * q + (lane >> 5);
-      const int chunk = (lane & 31) ^ (4 * (krow % 4));
-      const int64_t wcol = weight_column<MODE, kWN>(p, n0, chunk * 8, ok);
+      // [64 k][kBN n]: block q holds k rows kKRowsPerCopy*q ..; lane l lands in row
+      // kKRowsPerCopy*q + l/kBChunks at slot l%kBChunks, which holds n-chunk slot ^ (4 * (row % 4)).
+      const int krow = kKRowsPerCopy * q + lane / kBChunks;
+      const int chunk = (lane % kBChunks) ^ (4 * (krow % 4));
+      const int64_t wcol = weight_column<MODE, WN>(p, n0, chunk * 8, ok);
       c_off[kACopies + i] = !ok ? kOob
                           : p.w_blk ? blocked_offset(krow, wcol, p.ldb)
                                     : (uint32_t)(((int64_t)krow * p.ldb + wcol) * 2);
@@ -116,12 +126,13 @@ void gemm_bigwave_kernel(const GemmParams p) {
            : p.w_blk ? blocked_desc(p.B, p.b_rows, k0)
                      : buffer_desc(p.B + (int64_t)k0 * p.ldb, (int64_t)(p.K - k0) * p.ldb * 2);
   };
-  // Copy i of tile t into stage t % 2: the wave's 8-KiB block of the A or B half plus a constant.
-  const uint32_t wave_lds = lds0 + (uint32_t)(wave * kACopies * 1024);
+  // Copy i of tile t into stage t % 2: the wave's block of the A or B half plus a constant.
+  const uint32_t wave_lds_a = lds0 + (uint32_t)(wave * kACopies * 1024);
+  const uint32_t wave_lds_b = lds0 + (uint32_t)(kAElems * 2 + wave * kBCopies * 1024);
   auto copy_one = [&](int t, int i, i32x4_t ad, i32x4_t bd) {
-    const uint32_t st = wave_lds + (uint32_t)((t & 1) * kStageElems * 2);
-    if (i < kACopies) copy16_to_lds_at(ad, c_off[i], st, i * 1024);
-    else copy16_to_lds_at(bd, c_off[i], st, kAElems * 2 + (i - kACopies) * 1024);
+    const uint32_t so = (uint32_t)((t & 1) * kStageElems * 2);
+    if (i < kACopies) copy16_to_lds_at(ad, c_off[i], wave_lds_a + so, i * 1024);
+    else copy16_to_lds_at(bd, c_off[i], wave_lds_b + so, (i - kACopies) * 1024);
   };
   auto copy_tile = [&](int t) {
     const i32x4_t ad = a_desc(t), bd = b_desc(t);
@@ -140,12 +151,12 @@ void gemm_bigwave_kernel(const GemmParams p) {
   for (int kk = 0; kk < kKK; ++kk) {
     const int slot = (kk * 2 + a_half) ^ rs;
     ra_off[kk] = (wm * kWM + a_r) * kBK + slot * 8;
-    rb_off[kk] = kAElems + (wn * kWN + a_r) * kBK + slot * 8;  // W^T: B rows are weight columns
+    rb_off[kk] = kAElems + (wn * WN + a_r) * kBK + slot * 8;  // W^T: B rows are weight columns
   }
-  // [64 k][256 n] staging, read with ds_read_b64_tr_b16 (each 16-lane group receives the transpose
+  // [64 k][kBN n] staging, read with ds_read_b64_tr_b16 (each 16-lane group receives the transpose
   // of a 4 (k) x 16 (n) block): group g = lane/16 reads k row 16*kk + 8*(g/2) + 4*h + (lane%16)/4 at
-  // n = 128*wn + 32*ni + 16*(g%2) + 4*(lane%4), i.e. chunk 16*wn + 4*ni + 2*(g%2) + (lane%4)/2, stored
-  // at slot chunk ^ (4 * (k%4)) with k%4 = (lane%16)/4.
+  // n = WN*wn + 32*ni + 16*(g%2) + 4*(lane%4), i.e. chunk (WN/8)*wn + 4*ni + 2*(g%2) + (lane%4)/2,
+  // stored at slot chunk ^ (4 * (k%4)) with k%4 = (lane%16)/4.
   int rt_off[kNI];
   {
     const int krow = 8 * (lane >> 5) + ((lane & 15) >> 2);
@@ -153,7 +164,7 @@ void gemm_bigwave_kernel(const GemmParams p) {
     const int c = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
 #pragma unroll
     for (int ni = 0; ni < kNI; ++ni)
-      rt_off[ni] = kAElems + krow * kBN + (((kWN / 8) * wn + 4 * ni + c) ^ x) * 8 + 4 * (lane & 1);
+      rt_off[ni] = kAElems + krow * kBN + (((WN / 8) * wn + 4 * ni + c) ^ x) * 8 + 4 * (lane & 1);
   }
 
   // Fragments of the four slices (buffer = slice index).  [k][n] weights: the two halves of each B
@@ -187,7 +198,7 @@ void gemm_bigwave_kernel(const GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
-  // MFMA j (0..15) of slice kk: the weight fragment as the first operand, so lane l holds output
+  // MFMA j (0 .. kMps-1) of slice kk: the weight fragment as the first operand, so lane l holds output
   // row (l & 31) and, in accumulator register r, column 8*(r/4) + 4*(l/32) + r%4 of the 32 x 32 block.
   auto mfma_one = [&](int kk, int j) {
     const int mi = j / kNI, ni = j % kNI;
@@ -218,15 +229,15 @@ void gemm_bigwave_kernel(const GemmParams p) {
   auto k_tile = [&](int t, auto next_c, auto copy_c) {
     constexpr bool NEXT = decltype(next_c)::value, COPY = decltype(copy_c)::value;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < kMps; ++j) {
       mfma_one(0, j);
 #pragma unroll
-      for (int r = j * 2 * kReadsPerSlice / 16; r < (j + 1) * 2 * kReadsPerSlice / 16; ++r)
+      for (int r = j * 2 * kReadsPerSlice / kMps; r < (j + 1) * 2 * kReadsPerSlice / kMps; ++r)
         read_one(t, 2 + r / kReadsPerSlice, r % kReadsPerSlice);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < kMps; ++j) {
       mfma_one(1, j);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -240,23 +251,34 @@ void gemm_bigwave_kernel(const GemmParams p) {
       ad = a_desc(t + 2);
       bd = b_desc(t + 2);
     }
+    // Copy c of the tile's kCopies follows MFMA slot c * 2*kMps / kCopies of slices 2-3 (slots
+    // kMps.. are slice 3's): at 16 MFMAs per slice, the A copies after every second MFMA of slice
+    // 2 and the B copies after every second MFMA of slice 3.
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < kMps; ++j) {
       mfma_one(2, j);
-      if (COPY && j % 2 == 0) copy_one(t + 2, j / 2, ad, bd);
+      if (COPY) {
+#pragma unroll
+        for (int c = 0; c < kCopies; ++c)
+          if (c * 2 * kMps / kCopies == j) copy_one(t + 2, c, ad, bd);
+      }
       if (NEXT) {
 #pragma unroll
-        for (int r = j * kReadsPerSlice / 16; r < (j + 1) * kReadsPerSlice / 16; ++r) read_one(t + 1, 0, r);
+        for (int r = j * kReadsPerSlice / kMps; r < (j + 1) * kReadsPerSlice / kMps; ++r) read_one(t + 1, 0, r);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < kMps; ++j) {
       mfma_one(3, j);
-      if (COPY && j % 2 == 0) copy_one(t + 2, kACopies + j / 2, ad, bd);
+      if (COPY) {
+#pragma unroll
+        for (int c = 0; c < kCopies; ++c)
+          if (c * 2 * kMps / kCopies == kMps + j) copy_one(t + 2, c, ad, bd);
+      }
       if (NEXT) {
 #pragma unroll
-        for (int r = j * kReadsPerSlice / 16; r < (j + 1) * kReadsPerSlice / 16; ++r) read_one(t + 1, 1, r);
+        for (int r = j * kReadsPerSlice / kMps; r < (j + 1) * kReadsPerSlice / kMps; ++r) read_one(t + 1, 1, r);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -282,7 +304,7 @@ void gemm_bigwave_kernel(const GemmParams p) {
       for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int col = n0 + wn * kWN + ni * 32 + g * 8 + a_half * 4;
+          const int col = n0 + wn * WN + ni * 32 + g * 8 + a_half * 4;
           if (partial) {
             const float4 v = {acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]};
             *reinterpret_cast<float4*>(wbase + (int64_t)row * p.ws_ld + col) = v;
@@ -298,7 +320,7 @@ void gemm_bigwave_kernel(const GemmParams p) {
       for (int ni = 0; ni < kNI / 2; ++ni)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int col = n0 + wn * (kWN / 2) + ni * 32 + g * 8 + a_half * 4;
+          const int col = n0 + wn * (WN / 2) + ni * 32 + g * 8 + a_half * 4;
           if (col < p.N) {
             float a[4];
 #pragma unroll
@@ -314,23 +336,33 @@ void gemm_bigwave_kernel(const GemmParams p) {
   }
 }
 
-template <int MODE, bool WNK>
+template <int MODE, bool WNK, int WN>
 void launch_one(const GemmParams& p, hipStream_t stream) {
   const int splits = p.splits > 1 ? p.splits : 1;
-  hipLaunchKernelGGL((gemm_bigwave_kernel<MODE, WNK>), dim3((unsigned)(splits * p.tiles_m * p.tiles_n)),
+  hipLaunchKernelGGL((gemm_bigwave_kernel<MODE, WNK, WN>), dim3((unsigned)(splits * p.tiles_m * p.tiles_n)),
                      dim3(kThreads), 0, stream, p);
+}
+
+template <int WN>
+void launch_width(const GemmParams& p, hipStream_t stream) {
+  if (p.mode == kSiluMul)
+    p.w_nk ? launch_one<kSiluMul, true, WN>(p, stream) : launch_one<kSiluMul, false, WN>(p, stream);
+  else
+    p.w_nk ? launch_one<kPlain, true, WN>(p, stream) : launch_one<kPlain, false, WN>(p, stream);
 }
 
 }  // namespace
 
 bool gemm_bigwave_supports(const GemmParams& p) { return p.K % kBK == 0 && p.K > 0; }
 
+int gemm_bigwave_tile_cols(int mode, bool narrow) {
+  const int cols = narrow ? 128 : 256;
+  return mode == kSiluMul ? cols / 2 : cols;
+}
+
 hipError_t launch_gemm_bigwave(const GemmParams& p, hipStream_t stream) {
   if (p.mode == kSiluMul && p.splits > 1) return hipErrorInvalidValue;  // split SiLU·up runs as halves
-  if (p.mode == kSiluMul)
-    p.w_nk ? launch_one<kSiluMul, true>(p, stream) : launch_one<kSiluMul, false>(p, stream);
-  else
-    p.w_nk ? launch_one<kPlain, true>(p, stream) : launch_one<kPlain, false>(p, stream);
+  p.narrow ? launch_width<64>(p, stream) : launch_width<128>(p, stream);
   return hipGetLastError();
 }
 

@@ -22,6 +22,9 @@
 //                                 multiple of 64 (where the four-wave kernel runs by default);
 //   TTL_GEMM_KERNEL=tilesplit     256 x 256 tiles cut along k (four-wave kernel; K a multiple of 64,
 //                                 else the split-K kernel), TTL_GEMM_SPLITS or at least 2 splits;
+//   TTL_GEMM_KERNEL=narrow        256 x 128 tiles of the four-wave kernel (K a multiple of 64, else
+//                                 the eight-wave kernel's 256 x 256 tiles);
+//   TTL_GEMM_KERNEL=narrowsplit   256 x 128 tiles cut along k, as tilesplit;
 //   TTL_GEMM_SPLITS=<n>           split-K kernel: use n splits (at most one per k-tile).
 #include <cstdlib>
 #include <cstring>
@@ -73,7 +76,7 @@ hipError_t get_workspace(size_t bytes, void** out) {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // 0: by shape, 1: 256 x 256 tiles, 2: split-K, 3: 256 x 256 tiles by the eight-wave kernel,
-// 4: 256 x 256 tiles cut along k.
+// 4: 256 x 256 tiles cut along k, 5: 256 x 128 tiles, 6: 256 x 128 tiles cut along k.
 int forced_kernel() {
   const char* s = std::getenv("TTL_GEMM_KERNEL");
   if (s == nullptr) return 0;
@@ -81,6 +84,8 @@ int forced_kernel() {
   if (std::strcmp(s, "splitk") == 0) return 2;
   if (std::strcmp(s, "eightwave") == 0) return 3;
   if (std::strcmp(s, "tilesplit") == 0) return 4;
+  if (std::strcmp(s, "narrow") == 0) return 5;
+  if (std::strcmp(s, "narrowsplit") == 0) return 6;
   return 0;
 }
 
@@ -94,24 +99,35 @@ hipError_t launch_tiles(GemmParams& p, int force, hipStream_t stream) {
   p.tiles_m = (int32_t)cdiv(p.M, gemm_tile_rows());
   p.tiles_n = (int32_t)cdiv(p.N, gemm_tile_cols(p.mode));
   p.splits = 1;
+  p.narrow = 0;
   if (force != 3 && gemm_bigwave_supports(p)) return launch_gemm_bigwave(p, stream);
   return launch_gemm_tiled(p, stream);
 }
 
-// 256 x 256 tiles of the four-wave kernel cut into `splits` k ranges (plain mode; SiLU·up as the
-// gate columns then the up columns), then the split-K finalize kernel.
-hipError_t launch_tiles_splitk(GemmParams& p, int64_t splits, hipStream_t stream) {
+// 256 x 128 tiles of the four-wave kernel over all of p (K a multiple of 64).
+hipError_t launch_narrow(GemmParams& p, hipStream_t stream) {
+  p.tiles_m = (int32_t)cdiv(p.M, gemm_tile_rows());
+  p.tiles_n = (int32_t)cdiv(p.N, gemm_bigwave_tile_cols(p.mode, true));
+  p.splits = 1;
+  p.narrow = 1;
+  return launch_gemm_bigwave(p, stream);
+}
+
+// 256 x 256 (or, narrow, 256 x 128) tiles of the four-wave kernel cut into `splits` k ranges
+// (plain mode; SiLU·up as the gate columns then the up columns), then the split-K finalize kernel.
+hipError_t launch_tiles_splitk(GemmParams& p, int64_t splits, bool narrow, hipStream_t stream) {
   GemmParams q = p.mode == 1 ? silu_as_plain_halves(p) : p;
+  q.narrow = narrow ? 1 : 0;
   q.tiles_m = (int32_t)cdiv(q.M, gemm_tile_rows());
-  q.tiles_n = (int32_t)cdiv(q.N, gemm_tile_cols(0));
+  q.tiles_n = (int32_t)cdiv(q.N, gemm_bigwave_tile_cols(0, narrow));
   const int64_t nk = q.K / 64;
   if (splits > nk) splits = nk;
   const int64_t kt_per = cdiv(nk, splits);
   splits = cdiv(nk, kt_per);  // every split gets at least one k-tile
-  if (splits < 2) return launch_tiles(p, 0, stream);
+  if (splits < 2) return narrow ? launch_narrow(p, stream) : launch_tiles(p, 0, stream);
   q.splits = (int32_t)splits;
   q.kt_per_split = (int32_t)kt_per;
-  q.ws_ld = (int64_t)q.tiles_n * gemm_tile_cols(0);
+  q.ws_ld = (int64_t)q.tiles_n * gemm_bigwave_tile_cols(0, narrow);
   void* base = nullptr;
   hipError_t e = get_workspace((size_t)splits * q.M * q.ws_ld * sizeof(float), &base);
   if (e != hipSuccess) return e;
@@ -158,14 +174,16 @@ hipError_t launch_splitk(GemmParams& p, hipStream_t stream) {
 hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
   const int force = forced_kernel();
   if (force == 1 || force == 3) return launch_tiles(p, force, stream);
-  if (force == 2 || (force == 4 && !gemm_bigwave_supports(p))) return launch_splitk(p, stream);
+  if (force == 5) return gemm_bigwave_supports(p) ? launch_narrow(p, stream) : launch_tiles(p, 3, stream);
+  if (force == 2 || ((force == 4 || force == 6) && !gemm_bigwave_supports(p))) return launch_splitk(p, stream);
   const int64_t tiled_m = cdiv(p.M, gemm_tile_rows());
   const int64_t tiled_n = cdiv(p.N, gemm_tile_cols(p.mode));
   const int64_t tiles = tiled_m * tiled_n;
-  if (force == 4) {
+  const int64_t narrow_tiles = tiled_m * cdiv(p.N, gemm_bigwave_tile_cols(p.mode, true));
+  if (force == 4 || force == 6) {
     const int64_t fs = forced_splits();
-    const int64_t auto_splits = kCUs / tiles;
-    return launch_tiles_splitk(p, fs > 0 ? fs : (auto_splits > 2 ? auto_splits : 2), stream);
+    const int64_t auto_splits = kCUs / (force == 4 ? tiles : narrow_tiles);
+    return launch_tiles_splitk(p, fs > 0 ? fs : (auto_splits > 2 ? auto_splits : 2), force == 6, stream);
   }
   if (tiles < kTiledMinTiles) {
     // Few 256 x 256 tiles.  With many rows and a long k, 256 x 256 tiles cut along k into about
@@ -173,10 +191,14 @@ hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
     // each split takes at least kMinKTilesPerTileSplit k-tiles, as the fp32 partial tiles cost HBM
     // traffic (k = 1024 with 2 splits measured slower than the split-K kernel).  Decode-sized
     // launches stay on the split-K kernel, which is built to stream the weight.
+    // Where 256 x 128 tiles fill at least as much of the chip in one round, they run whole.
+    if (p.M >= kTileSplitMinRows && gemm_bigwave_supports(p) && narrow_tiles >= kTiledMinTiles &&
+        narrow_tiles <= kCUs)
+      return launch_narrow(p, stream);
     const int64_t by_k = (p.K / 64) / kMinKTilesPerTileSplit;
     const int64_t splits = kCUs / tiles < by_k ? kCUs / tiles : by_k;
     if (p.M >= kTileSplitMinRows && gemm_bigwave_supports(p) && splits >= 2)
-      return launch_tiles_splitk(p, splits, stream);
+      return launch_tiles_splitk(p, splits, false, stream);
     return launch_splitk(p, stream);
   }
   // Whole rounds of one tile per CU plus a short last round (at most half the CUs): that round

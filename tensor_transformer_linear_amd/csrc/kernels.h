@@ -23,6 +23,7 @@ struct GemmParams {
   int64_t seg_w0[3];      // mode 0: weight column of segment s's first output column
   int64_t gate_w0, up_w0; // mode 1: weight columns of act column 0's gate and up inputs
   int32_t tiles_m, tiles_n;
+  int32_t narrow;         // four-wave kernel: 1 = tiles of 256 rows x 128 weight columns, 0 = 256 x 256
   int32_t w_nk;           // weight stored transposed ([n][k])
   // w_blk: weight stored in 64 x 128 blocks, 128-column strips (TTL_W_BLOCKED).  B is the first
   // block of the first strip the call reads (at its first k row), column 0 the strip's first
@@ -66,6 +67,9 @@ int gemm_tile_rows();
 int gemm_tile_cols(int mode);
 hipError_t launch_gemm_tiled(const GemmParams& p, hipStream_t stream);
 bool gemm_bigwave_supports(const GemmParams& p);
+// Output columns of one four-wave tile: 256 (128 act columns in SiLU·up mode), or with p.narrow
+// 128 (64).
+int gemm_bigwave_tile_cols(int mode, bool narrow);
 // The four-wave kernel also takes split-K launches (plain mode only): splits * tiles_m * tiles_n
 // workgroups, each writing its fp32 partial tile; launch_splitk_finalize then sums them.
 hipError_t launch_gemm_bigwave(const GemmParams& p, hipStream_t stream);

@@ -3,8 +3,8 @@
 Small cases compare every element; they span several 256-wide tiles and ragged tails in all three
 GEMM dimensions.  Each GEMM case runs through every kernel the library has, forced with
 TTL_GEMM_KERNEL (256 x 256 tiles by the four-wave kernel where K is a multiple of 64, by the
-eight-wave kernel, the four-wave kernel's tiles cut along k, and the split-K kernel for short M),
-and through the shape-based choice.  Tolerance, per output tensor: the error beyond the bf16 rounding of each output
+eight-wave kernel, the four-wave kernel's tiles cut along k, its 256 x 128 tiles, and the split-K
+kernel for short M), and through the shape-based choice.  Tolerance, per output tensor: the error beyond the bf16 rounding of each output
 element is at most 2e-2 * rms(ref), the reference being the oracle's unrounded float64 value (bf16
 inputs, so the device-side error is fp32 accumulation and fp32 elementwise math).  Integer-exact
 special cases (identity and one-hot operands) are compared bit for bit.
@@ -31,7 +31,7 @@ def ttl():
 LAYOUTS = pytest.mark.parametrize("layout", ["kn", "nk"])
 
 
-@pytest.fixture(params=["auto", "tiled", "eightwave", "tilesplit", "splitk"])
+@pytest.fixture(params=["auto", "tiled", "eightwave", "tilesplit", "narrow", "splitk"])
 def gemm_path(request, monkeypatch):
     """Which GEMM kernel the library uses for the test (auto = its choice by shape)."""
     if request.param == "auto":
@@ -238,9 +238,9 @@ def test_layouts_agree_bitwise(ttl, gemm_path):
 @pytest.mark.parametrize("k", [64, 128, 192, 320, 576])
 @LAYOUTS
 def test_tiled_kernels_short_k(ttl, monkeypatch, k, layout):
-    """The four-wave 256 x 256 kernel over 1, 2, 3, 5 and 9 k-tiles (its prologue and the two
-    peeled k-tiles), ragged in M and N, matches the oracle and the eight-wave kernel bit for bit
-    (both accumulate the same products in the same k order)."""
+    """The four-wave kernel's 256 x 256 and 256 x 128 tiles over 1, 2, 3, 5 and 9 k-tiles (its
+    prologue and the two peeled k-tiles), ragged in M and N, match the oracle and the eight-wave
+    kernel bit for bit (all accumulate the same products in the same k order)."""
     monkeypatch.delenv("TTL_GEMM_SPLITS", raising=False)
     b, I, t = 300, 688, 2
     X = wl.random_bf16((b, k), 95 + k)
@@ -248,23 +248,25 @@ def test_tiled_kernels_short_k(ttl, monkeypatch, k, layout):
     Wd_, lay = _stored(ttl, W, layout)
     sp = ttl.merged_gate_up_split(I, t)
     outs = {}
-    for kern in ("tiled", "eightwave"):
+    for kern in ("tiled", "eightwave", "narrow"):
         monkeypatch.setenv("TTL_GEMM_KERNEL", kern)
         outs[kern] = ttl.shard_linear_col(gpu(X), Wd_, t, 1, sp, ttl.EPI_SILU_MUL, w_layout=lay)
         torch.cuda.synchronize()
     ref = oracle.silu_mul(oracle.col_shard(f64(X), f64(W), oracle.merged_gate_up_split(I, t), t, 1))
     assert_close(from_gpu(outs["tiled"]), ref, f"four-wave k={k} {layout}")
     assert torch.equal(outs["tiled"], outs["eightwave"])
+    assert torch.equal(outs["tiled"], outs["narrow"])
 
 
 @pytest.mark.parametrize("splits", [2, 3, 7])
 @pytest.mark.parametrize("silu", [False, True])
+@pytest.mark.parametrize("kern", ["tilesplit", "narrowsplit"])
 @LAYOUTS
-def test_tiles_cut_along_k(ttl, monkeypatch, splits, silu, layout):
-    """256 x 256 tiles of the four-wave kernel cut into k ranges (10 k-tiles of 64: ranges of 5+5,
-    4+4+2 and 2+2+2+2+2), ragged in M and N, against the oracle; SiLU·up runs as the gate columns
-    then the up columns and is paired by the finalize kernel."""
-    monkeypatch.setenv("TTL_GEMM_KERNEL", "tilesplit")
+def test_tiles_cut_along_k(ttl, monkeypatch, splits, silu, kern, layout):
+    """256 x 256 (and 256 x 128) tiles of the four-wave kernel cut into k ranges (10 k-tiles of 64:
+    ranges of 5+5, 4+4+2 and 2+2+2+2+2), ragged in M and N, against the oracle; SiLU·up runs as the
+    gate columns then the up columns and is paired by the finalize kernel."""
+    monkeypatch.setenv("TTL_GEMM_KERNEL", kern)
     monkeypatch.setenv("TTL_GEMM_SPLITS", str(splits))
     b, k, t = 600, 640, 2
     X = wl.random_bf16((b, k), 99 + splits)
