@@ -67,7 +67,10 @@ void gemm_bigwave_kernel(const GemmParams p) {
   constexpr int kCopies = kACopies + kBCopies;
   constexpr int kBChunks = kBN / 8;              // 16-B chunks per staged [k][n] row: 32 or 16
   constexpr int kKRowsPerCopy = 64 / kBChunks;   // k rows per 1-KiB copy of a [k][n] stage: 2 or 4
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * kStageElems];
+  // Ring depth: two stages of 64 KiB for 256 x 256 tiles; three of 48 KiB for 256 x 128 tiles,
+  // whose k-tiles take half as long, so that their copies still have about two k-tiles to land.
+  constexpr int kStages = WN == 128 ? 2 : 3;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages * kStageElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -130,7 +133,7 @@ void gemm_bigwave_kernel(const GemmParams p) {
   const uint32_t wave_lds_a = lds0 + (uint32_t)(wave * kACopies * 1024);
   const uint32_t wave_lds_b = lds0 + (uint32_t)(kAElems * 2 + wave * kBCopies * 1024);
   auto copy_one = [&](int t, int i, i32x4_t ad, i32x4_t bd) {
-    const uint32_t so = (uint32_t)((t & 1) * kStageElems * 2);
+    const uint32_t so = (uint32_t)(((unsigned)t % kStages) * kStageElems * 2);
     if (i < kACopies) copy16_to_lds_at(ad, c_off[i], wave_lds_a + so, i * 1024);
     else copy16_to_lds_at(bd, c_off[i], wave_lds_b + so, (i - kACopies) * 1024);
   };
@@ -175,7 +178,7 @@ void gemm_bigwave_kernel(const GemmParams p) {
   // each when W is stored [n][k], two half reads each when stored [k][n]).
   constexpr int kReadsPerSlice = kMI + (WNK ? 1 : 2) * kNI;
   auto read_one = [&](int t, int kk, int j) {
-    const uint16_t* st = lds + (t & 1) * kStageElems;
+    const uint16_t* st = lds + ((unsigned)t % kStages) * kStageElems;
     if (j < kMI) {
       af[kk][j] = *reinterpret_cast<const bf16x8_t*>(st + ra_off[kk] + j * 32 * kBK);
     } else if constexpr (WNK) {
@@ -208,9 +211,13 @@ void gemm_bigwave_kernel(const GemmParams p) {
     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, af[kk][mi], acc[mi][ni], 0, 0, 0);
   };
 
-  // ---- Prologue: tiles 0 and 1 in flight, tile 0 landed, slices 0 and 1 of tile 0 read.
+  // ---- Prologue: tiles 0 .. kStages-1 in flight, tile 0 landed, slices 0 and 1 of tile 0 read.
   copy_tile(0);
-  if (nk > 1) {
+  if (nk >= kStages) {
+#pragma unroll
+    for (int s = 1; s < kStages; ++s) copy_tile(s);
+    wait_vmcnt<(kStages - 1) * kCopies>();
+  } else if (nk > 1) {  // three stages, two k-tiles
     copy_tile(1);
     wait_vmcnt<kCopies>();
   } else {
@@ -223,11 +230,13 @@ void gemm_bigwave_kernel(const GemmParams p) {
   for (int j = 0; j < kReadsPerSlice; ++j) read_one(0, 1, j);
   __builtin_amdgcn_sched_barrier(0);
 
-  // One k-tile.  NEXT: tile t+1 exists (barrier, and its reads); COPY: tile t+2 exists (its
-  // copies).  The main loop runs with both; the last two tiles are peeled, so the loop has no
-  // branches.
-  auto k_tile = [&](int t, auto next_c, auto copy_c) {
+  // One k-tile.  NEXT: tile t+1 exists (barrier, and its reads); COPY: tile t+kStages exists (its
+  // copies, into tile t's stage); WAITN: this wave's copies of the tiles after t+1 that are in
+  // flight at the barrier (kStages-2 tiles in the main loop, fewer near the end).  The main loop
+  // runs with NEXT and COPY; the last kStages tiles are peeled, so the loop has no branches.
+  auto k_tile = [&](int t, auto next_c, auto copy_c, auto waitn_c) {
     constexpr bool NEXT = decltype(next_c)::value, COPY = decltype(copy_c)::value;
+    constexpr int WAITN = decltype(waitn_c)::value;
 #pragma unroll
     for (int j = 0; j < kMps; ++j) {
       mfma_one(0, j);
@@ -242,14 +251,14 @@ void gemm_bigwave_kernel(const GemmParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     if (NEXT) {
-      wait_vmcnt<0>();  // this wave's copies of tile t+1 landed
-      lds_barrier();    // ... everyone's; and every wave's reads of tile t returned
+      wait_vmcnt<WAITN>();  // this wave's copies of tile t+1 landed
+      lds_barrier();        // ... everyone's; and every wave's reads of tile t returned
       __builtin_amdgcn_sched_barrier(0);
     }
     i32x4_t ad = {0, 0, 0, 0}, bd = {0, 0, 0, 0};
     if (COPY) {
-      ad = a_desc(t + 2);
-      bd = b_desc(t + 2);
+      ad = a_desc(t + kStages);
+      bd = b_desc(t + kStages);
     }
     // Copy c of the tile's kCopies follows MFMA slot c * 2*kMps / kCopies of slices 2-3 (slots
     // kMps.. are slice 3's): at 16 MFMAs per slice, the A copies after every second MFMA of slice
@@ -260,7 +269,7 @@ void gemm_bigwave_kernel(const GemmParams p) {
       if (COPY) {
 #pragma unroll
         for (int c = 0; c < kCopies; ++c)
-          if (c * 2 * kMps / kCopies == j) copy_one(t + 2, c, ad, bd);
+          if (c * 2 * kMps / kCopies == j) copy_one(t + kStages, c, ad, bd);
       }
       if (NEXT) {
 #pragma unroll
@@ -274,7 +283,7 @@ void gemm_bigwave_kernel(const GemmParams p) {
       if (COPY) {
 #pragma unroll
         for (int c = 0; c < kCopies; ++c)
-          if (c * 2 * kMps / kCopies == kMps + j) copy_one(t + 2, c, ad, bd);
+          if (c * 2 * kMps / kCopies == kMps + j) copy_one(t + kStages, c, ad, bd);
       }
       if (NEXT) {
 #pragma unroll
@@ -283,10 +292,16 @@ void gemm_bigwave_kernel(const GemmParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  using W0 = std::integral_constant<int, 0>;
+  using WMain = std::integral_constant<int, (kStages - 2) * kCopies>;
+  using W1 = std::integral_constant<int, kCopies>;
   int t = 0;
-  for (; t + 2 < nk; ++t) k_tile(t, std::true_type{}, std::true_type{});
-  if (t + 1 < nk) k_tile(t++, std::true_type{}, std::false_type{});
-  k_tile(t, std::false_type{}, std::false_type{});
+  for (; t + kStages < nk; ++t) k_tile(t, std::true_type{}, std::true_type{}, WMain{});
+  if constexpr (kStages == 3) {
+    if (t + 2 < nk) k_tile(t++, std::true_type{}, std::false_type{}, W1{});  // tile t+2 in flight
+  }
+  if (t + 1 < nk) k_tile(t++, std::true_type{}, std::false_type{}, W0{});
+  k_tile(t, std::false_type{}, std::false_type{}, W0{});
 
   const int row_base = m0 + wm * kWM + a_r;
   // ---- Epilogue straight from the accumulators: each lane owns 4 consecutive columns of one row

@@ -195,10 +195,16 @@ hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
     if (p.M >= kTileSplitMinRows && gemm_bigwave_supports(p) && narrow_tiles >= kTiledMinTiles &&
         narrow_tiles <= kCUs)
       return launch_narrow(p, stream);
+    // Otherwise tiles cut along k: 256 x 256 tiles, or 256 x 128 tiles where those occupy at
+    // least as many CUs (then with half the partial bytes per output).
     const int64_t by_k = (p.K / 64) / kMinKTilesPerTileSplit;
     const int64_t splits = kCUs / tiles < by_k ? kCUs / tiles : by_k;
-    if (p.M >= kTileSplitMinRows && gemm_bigwave_supports(p) && splits >= 2)
-      return launch_tiles_splitk(p, splits, false, stream);
+    const int64_t nsplits = kCUs / narrow_tiles < by_k ? kCUs / narrow_tiles : by_k;
+    if (p.M >= kTileSplitMinRows && gemm_bigwave_supports(p)) {
+      if (nsplits >= 2 && narrow_tiles * nsplits >= tiles * splits)
+        return launch_tiles_splitk(p, nsplits, true, stream);
+      if (splits >= 2) return launch_tiles_splitk(p, splits, false, stream);
+    }
     return launch_splitk(p, stream);
   }
   // Whole rounds of one tile per CU plus a short last round (at most half the CUs): that round
