@@ -320,6 +320,32 @@ def test_short_last_round_split_by_rows(ttl, monkeypatch, silu, layout):
     assert torch.equal(outs["auto"][:2048], outs["tiled"][:2048])
 
 
+@pytest.mark.parametrize("case", ["narrow", "narrowsplit"])
+def test_auto_choice_of_narrow_tiles(ttl, monkeypatch, case):
+    """Shapes whose 256 x 256 tiles fill too few CUs: 512 x 12288 outputs (96 wide tiles, 192
+    narrow ones: narrow tiles, whole k) and 512 x 6144 outputs at k = 4096 (48 wide tiles x 4
+    splits against 96 narrow tiles x 2 splits: narrow tile splits).  The shape-based choice matches
+    the forced kernel bit for bit and sampled rows match the oracle."""
+    monkeypatch.delenv("TTL_GEMM_SPLITS", raising=False)
+    b, k, n = (512, 256, 12288) if case == "narrow" else (512, 4096, 6144)
+    X = wl.random_bf16((b, k), 310)
+    W = wl.random_bf16((k, n), 311, std=0.05)
+    outs = {}
+    for kern in ("auto", case):
+        if kern == "auto":
+            monkeypatch.delenv("TTL_GEMM_KERNEL", raising=False)
+        else:
+            monkeypatch.setenv("TTL_GEMM_KERNEL", kern)
+            if kern == "narrowsplit":
+                monkeypatch.setenv("TTL_GEMM_SPLITS", "2")
+        outs[kern] = ttl.shard_linear_col(gpu(X), gpu(W), 1, 0)
+        torch.cuda.synchronize()
+    assert torch.equal(outs["auto"], outs[case])
+    rows = np.r_[0:4, 254:258, 508:512]
+    ref = oracle.col_shard(f64(X)[rows], f64(W), oracle.plain_split(n, 1), 1, 0)
+    assert_close(from_gpu(outs["auto"])[rows], ref, f"auto {case}")
+
+
 def _blocked_reference(W):
     """The TTL_W_BLOCKED memory order of a [k, n] weight, by index arithmetic on the host."""
     k, n = W.shape
