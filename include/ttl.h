@@ -86,6 +86,7 @@ typedef int32_t ttl_weight_layout;
 #define TTL_W_BLOCKED 2
 
 #define TTL_MAX_SEGMENTS 3
+#define TTL_MAX_PEERS 16   /* partial buffers reduce_partials_rmsnorm_peers accepts */
 
 /*
  * Column split of the full W[k,n] ("MergedColumnParallelLinear / QkvParallelLinear" on the vLLM
@@ -222,6 +223,37 @@ ttl_status reduce_scatter_partials_rmsnorm(const uint16_t* P, int32_t t, int64_t
                                            uint16_t* residual_out,
                                            uint16_t* Y,
                                            void* stream);
+
+/*
+ * reduce_partials_rmsnorm_peers — reduce_partials_rmsnorm over rows [row0, row0 + rows) of t
+ * partials held in t separate buffers, one pointer per rank: the compute half of an all-reduce
+ * that reads the other ranks' buffers in place (on several GPUs, buffers mapped from the peers;
+ * "vLLM 源码完全拆解（十一）", section "RowParallelLinear": the row layer's output is the sum of
+ * the ranks' partials; "Tensor Parallelism" manual, section "Communication Patterns": a
+ * reduce-scatter leaves each rank one reduced chunk, which an all-gather then shares).  With
+ * row0 = 0 and rows = b every row is reduced (one-shot); with row0 = rank·b/t and rows = b/t,
+ * rank `rank` reduces its chunk (two-shot, the reduce-scatter half).
+ *
+ *   P_ranks   HOST array of t DEVICE pointers; P_ranks[r] is rank r's partial [b, n] bf16.
+ *             1 <= t <= TTL_MAX_PEERS.  The array is read during the call only.
+ *   residual  [rows, n] bf16 (the residual rows of the range) or NULL.
+ *   residual_out, Y  [rows, n] bf16, as reduce_partials_rmsnorm, for the rows of the range.
+ * Same arithmetic as reduce_partials_rmsnorm.  With the partials as one [t, b, n] slab, a call
+ * over the same number of rows returns the same bits: reduce_partials_rmsnorm for all rows,
+ * reduce_scatter_partials_rmsnorm for a rank's chunk.  (residual_out is a per-element sum; y also
+ * depends on the order in which a row's mean square is reduced across threads, which is fixed for
+ * a given row count and n.)
+ * Errors: b, n, or the row range empty or out of [0, b) -> SHAPE; t < 1 -> RANK;
+ * t > TTL_MAX_PEERS -> UNSUPPORTED; NULL P_ranks, an entry of it, gamma, residual_out or Y -> NULL;
+ * misalignment -> ALIGN; outputs overlapping a partial or each other -> UNSUPPORTED.
+ */
+ttl_status reduce_partials_rmsnorm_peers(const uint16_t* const* P_ranks, int32_t t, int64_t b, int64_t n,
+                                         int64_t row0, int64_t rows,
+                                         const uint16_t* residual,
+                                         const uint16_t* gamma, float eps,
+                                         uint16_t* residual_out,
+                                         uint16_t* Y,
+                                         void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 /*

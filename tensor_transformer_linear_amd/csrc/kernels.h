@@ -86,6 +86,8 @@ hipError_t launch_gemm_skinny(const GemmParams& p, int mb, hipStream_t stream);
 hipError_t launch_splitk_finalize(const GemmParams& p, hipStream_t stream);
 
 // Rows [0, b) of the outputs; row i reads the partials at P + i*n + r*plane, r = 0..t-1.
+constexpr int kMaxPeers = 16;  // partials passed as separate pointers (one per rank)
+
 struct ReduceNormParams {
   const uint16_t* P;
   const uint16_t* residual;  // may be null
@@ -96,6 +98,10 @@ struct ReduceNormParams {
   int64_t plane;             // elements between consecutive ranks' partials
   int32_t t;
   float eps;
+  // peers != 0: rank r's partial of the call's row i is at peer[r] + i * n (t <= kMaxPeers), in
+  // place of P + r * plane + i * n.
+  int32_t peers;
+  const uint16_t* peer[kMaxPeers];
 };
 
 hipError_t launch_reduce_rmsnorm(const ReduceNormParams& p, hipStream_t stream);

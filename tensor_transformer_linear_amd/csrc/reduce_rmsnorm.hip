@@ -1,4 +1,6 @@
-// Sum of t simulated-rank partials + residual add + RMSNorm, one pass over HBM.
+// Sum of t simulated-rank partials + residual add + RMSNorm, one pass over HBM.  The partials are
+// either t slabs of one [t][b][n] buffer or t separate [b][n] buffers (one pointer per rank, as a
+// reduction over peers' buffers would see them).
 //
 // One workgroup per token row.  Each thread owns CPT pieces of 8 consecutive bf16 columns
 // (piece c = tid + THREADS*j), read with 16-byte loads so that a wave covers 1 KiB of a row per
@@ -69,7 +71,8 @@ __global__ __launch_bounds__(THREADS) void reduce_rmsnorm_kernel(const ReduceNor
     u32x4_t v[RANKS][CPT];
 #pragma unroll
     for (int rr = 0; rr < RANKS; ++rr) {
-      const uint16_t* src = prow + (int64_t)(r0 + rr) * plane;
+      const int r = r0 + rr < p.t ? r0 + rr : p.t - 1;  // loads past t are skipped below
+      const uint16_t* src = p.peers ? p.peer[r] + row * n : prow + (int64_t)r * plane;
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
         const int c = tid + THREADS * j;

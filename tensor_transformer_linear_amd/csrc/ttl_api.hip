@@ -213,6 +213,7 @@ ttl_status reduce_setup(const char* who, const uint16_t* P, int32_t t, int64_t b
        overlaps(residual_out, out_bytes, residual, out_bytes)))
     return fail(TTL_ERR_UNSUPPORTED,
                 "%s: residual_out may alias residual exactly but must not overlap anything else", who);
+  p = {};
   p.P = P + row0 * n;
   p.residual = residual;
   p.gamma = gamma;
@@ -352,6 +353,41 @@ ttl_status reduce_partials_rmsnorm(const uint16_t* P, int32_t t, int64_t b, int6
   const ttl_status st =
       reduce_setup(who, P, t, b, n, 0, b, residual, gamma, eps, residual_out, Y, p);
   if (st != TTL_OK) return st;
+  return launch_status(ttl::launch_reduce_rmsnorm(p, static_cast<hipStream_t>(stream)), who);
+}
+
+ttl_status reduce_partials_rmsnorm_peers(const uint16_t* const* P_ranks, int32_t t, int64_t b, int64_t n,
+                                         int64_t row0, int64_t rows, const uint16_t* residual,
+                                         const uint16_t* gamma, float eps, uint16_t* residual_out,
+                                         uint16_t* Y, void* stream) {
+  static const char* who = "reduce_partials_rmsnorm_peers";
+  if (b <= 0 || n <= 0 || b > kMaxDim || n > 65536)
+    return fail(TTL_ERR_SHAPE, "%s: need 1 <= b < 2^31 and 1 <= n <= 65536 (b=%lld n=%lld)", who,
+                (long long)b, (long long)n);
+  if (row0 < 0 || rows <= 0 || row0 + rows > b)
+    return fail(TTL_ERR_SHAPE, "%s: rows [%lld, %lld) must be a non-empty range inside [0, %lld)", who,
+                (long long)row0, (long long)(row0 + rows), (long long)b);
+  if (t < 1) return fail(TTL_ERR_RANK, "%s: t=%d must be >= 1", who, t);
+  if (t > TTL_MAX_PEERS)
+    return fail(TTL_ERR_UNSUPPORTED, "%s: t=%d partial buffers exceed the %d supported", who, t, TTL_MAX_PEERS);
+  if (P_ranks == nullptr) return fail(TTL_ERR_NULL, "%s: P_ranks must be non-NULL", who);
+  for (int r = 0; r < t; ++r) {
+    if (P_ranks[r] == nullptr) return fail(TTL_ERR_NULL, "%s: P_ranks[%d] is NULL", who, r);
+    if (!aligned16(P_ranks[r])) return fail(TTL_ERR_ALIGN, "%s: P_ranks[%d] is not 16-byte aligned", who, r);
+  }
+  // Shape, eps, alignment and aliasing of the residual, gamma and outputs, with rank 0's buffer as
+  // the partial; then the outputs against every other rank's buffer.
+  ttl::ReduceNormParams p;
+  const ttl_status st = reduce_setup(who, P_ranks[0] + row0 * n, 1, rows, n, 0, rows, residual, gamma, eps,
+                                     residual_out, Y, p);
+  if (st != TTL_OK) return st;
+  const int64_t out_bytes = rows * n * 2, slab = b * n * 2;
+  for (int r = 0; r < t; ++r)
+    if (overlaps(Y, out_bytes, P_ranks[r], slab) || overlaps(residual_out, out_bytes, P_ranks[r], slab))
+      return fail(TTL_ERR_UNSUPPORTED, "%s: the outputs must not overlap P_ranks[%d]", who, r);
+  p.t = t;
+  p.peers = 1;
+  for (int r = 0; r < t; ++r) p.peer[r] = P_ranks[r] + row0 * n;
   return launch_status(ttl::launch_reduce_rmsnorm(p, static_cast<hipStream_t>(stream)), who);
 }
 

@@ -31,9 +31,10 @@ W_KN = 0  # weight stored [k][n] (row stride n)
 W_NK = 1  # weight stored transposed, [n][k] (row stride k), as PyTorch-style Linear weights are
 W_BLOCKED = 2  # [k][n] in 64 x 128 blocks, 128-column strips contiguous (see pack_weight_blocked)
 MAX_SEGMENTS = 3
+MAX_PEERS = 16
 EXPORTED = ("shard_linear_col", "shard_linear_col_gathered", "shard_linear_row",
-            "reduce_partials_rmsnorm", "reduce_scatter_partials_rmsnorm", "ttl_pack_weight_blocked",
-            "ttl_last_error", "ttl_version")
+            "reduce_partials_rmsnorm", "reduce_scatter_partials_rmsnorm", "reduce_partials_rmsnorm_peers",
+            "ttl_pack_weight_blocked", "ttl_last_error", "ttl_version")
 
 
 class ColSplit(ctypes.Structure):
@@ -61,6 +62,10 @@ _lib.reduce_scatter_partials_rmsnorm.restype = ctypes.c_int32
 _lib.reduce_scatter_partials_rmsnorm.argtypes = [_c_u16p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                                  ctypes.c_int32, _c_u16p, _c_u16p, ctypes.c_float,
                                                  _c_u16p, _c_u16p, ctypes.c_void_p]
+_lib.reduce_partials_rmsnorm_peers.restype = ctypes.c_int32
+_lib.reduce_partials_rmsnorm_peers.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.c_int64,
+                                               ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _c_u16p, _c_u16p,
+                                               ctypes.c_float, _c_u16p, _c_u16p, ctypes.c_void_p]
 _lib.ttl_pack_weight_blocked.restype = ctypes.c_int32
 _lib.ttl_pack_weight_blocked.argtypes = [_c_u16p, ctypes.c_int64, ctypes.c_int64, _c_u16p, ctypes.c_void_p]
 _lib.ttl_last_error.restype = ctypes.c_char_p
@@ -251,6 +256,34 @@ def reduce_scatter_partials_rmsnorm(P: torch.Tensor, gamma: torch.Tensor, eps: f
                                                 _dev_ptr(residual, "residual"), _dev_ptr(gamma, "gamma"),
                                                 float(eps), _dev_ptr(residual_out, "residual_out"),
                                                 _dev_ptr(Y, "Y"), _stream_handle(stream)))
+    return residual_out, Y
+
+
+def reduce_partials_rmsnorm_peers(P_ranks, gamma: torch.Tensor, eps: float, row0: int = 0,
+                                  rows: Optional[int] = None,
+                                  residual: Optional[torch.Tensor] = None,
+                                  residual_out: Optional[torch.Tensor] = None,
+                                  Y: Optional[torch.Tensor] = None,
+                                  stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The reduction over rows [row0, row0 + rows) of t partials held in t separate [b, n]
+    tensors (one per rank); returns (residual_out, Y), each [rows, n]."""
+    P_ranks = list(P_ranks)
+    t = len(P_ranks)
+    b, n = P_ranks[0].shape if t else (0, 0)
+    for P in P_ranks:
+        if tuple(P.shape) != (b, n):
+            raise ValueError(f"every partial must be [{b}, {n}], got {tuple(P.shape)}")
+    rows = b - row0 if rows is None else rows
+    dev = P_ranks[0].device if t else gamma.device
+    if residual_out is None:
+        residual_out = torch.empty((max(rows, 0), n), dtype=torch.bfloat16, device=dev)
+    if Y is None:
+        Y = torch.empty((max(rows, 0), n), dtype=torch.bfloat16, device=dev)
+    ptrs = (ctypes.c_void_p * max(t, 1))(*[_dev_ptr(P, f"P_ranks[{r}]") for r, P in enumerate(P_ranks)])
+    _check(_lib.reduce_partials_rmsnorm_peers(ptrs, t, b, n, row0, rows, _dev_ptr(residual, "residual"),
+                                              _dev_ptr(gamma, "gamma"), float(eps),
+                                              _dev_ptr(residual_out, "residual_out"), _dev_ptr(Y, "Y"),
+                                              _stream_handle(stream)))
     return residual_out, Y
 
 

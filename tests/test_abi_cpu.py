@@ -91,6 +91,15 @@ def _red(P=A, t=2, b=16, n=256, R=B, gamma=D, eps=1e-5, Rout=B, Y=C):
     return ttl.lib().reduce_partials_rmsnorm(P, t, b, n, R, gamma, eps, Rout, Y, None)
 
 
+PEERS = [0x100000 + 0x10000 * r for r in range(17)]  # fake, 16-byte aligned, 64 KiB apart
+
+
+def _peers(ptrs=None, t=2, b=16, n=256, row0=0, rows=16, R=B, gamma=D, eps=1e-5, Rout=B, Y=C):
+    ptrs = PEERS[:t] if ptrs is None else ptrs
+    arr = None if ptrs == "null" else (ttl.ctypes.c_void_p * max(len(ptrs), 1))(*ptrs)
+    return ttl.lib().reduce_partials_rmsnorm_peers(arr, t, b, n, row0, rows, R, gamma, eps, Rout, Y, None)
+
+
 @pytest.mark.parametrize("call,status,needle", [
     (lambda: _col(X=None), ttl.ERR_NULL, "non-NULL"),
     (lambda: _col(Y=None), ttl.ERR_NULL, "non-NULL"),
@@ -148,6 +157,19 @@ def _red(P=A, t=2, b=16, n=256, R=B, gamma=D, eps=1e-5, Rout=B, Y=C):
     (lambda: _red(Y=A + 16), ttl.ERR_UNSUPPORTED, "overlap"),
     (lambda: _red(Rout=A), ttl.ERR_UNSUPPORTED, "alias"),
     (lambda: _red(R=B, Rout=B + 16), ttl.ERR_UNSUPPORTED, "alias"),
+    (lambda: _peers(t=0), ttl.ERR_RANK, "t=0"),
+    (lambda: _peers(t=17), ttl.ERR_UNSUPPORTED, "17"),
+    (lambda: _peers(ptrs="null"), ttl.ERR_NULL, "P_ranks"),
+    (lambda: _peers(ptrs=[PEERS[0], None]), ttl.ERR_NULL, "P_ranks[1]"),
+    (lambda: _peers(ptrs=[PEERS[0], PEERS[1] + 8]), ttl.ERR_ALIGN, "P_ranks[1]"),
+    (lambda: _peers(b=0), ttl.ERR_SHAPE, ""),
+    (lambda: _peers(row0=8, rows=9), ttl.ERR_SHAPE, "rows [8, 17)"),
+    (lambda: _peers(rows=0), ttl.ERR_SHAPE, ""),
+    (lambda: _peers(row0=-1), ttl.ERR_SHAPE, ""),
+    (lambda: _peers(n=252), ttl.ERR_ALIGN, "multiple of 8"),
+    (lambda: _peers(gamma=None), ttl.ERR_NULL, ""),
+    (lambda: _peers(Y=PEERS[1] + 64), ttl.ERR_UNSUPPORTED, "P_ranks[1]"),
+    (lambda: _peers(Rout=PEERS[0]), ttl.ERR_UNSUPPORTED, ""),
     (lambda: _rs(P=None), ttl.ERR_NULL, ""),
     (lambda: _rs(rank=2), ttl.ERR_RANK, "rank=2"),
     (lambda: _rs(rank=-1), ttl.ERR_RANK, ""),

@@ -548,6 +548,39 @@ def test_reduce_scatter_rmsnorm(ttl, t, b, n, with_residual):
         assert_close(from_gpu(y), yref, f"reduce-scatter y t={t} b={b} n={n} r={r}")
 
 
+@pytest.mark.parametrize("t,b,n,with_residual", [(8, 4096, 8192, True), (8, 64, 8192, True),
+                                                  (4, 2048, 4096, False), (3, 9, 4104, True),
+                                                  (16, 32, 1024, True), (1, 5, 256, True)])
+def test_reduce_over_peer_buffers(ttl, t, b, n, with_residual):
+    """The partials in t separate buffers (one per rank, as peers' buffers would be mapped): over
+    all rows (one-shot) bit-equal to reduce_partials_rmsnorm of the same partials as one [t, b, n]
+    slab, over each rank's b/t rows (two-shot) bit-equal to reduce_scatter_partials_rmsnorm (the
+    same row count, so the same launch shape and order of the mean square's reduction), and equal
+    to the oracle."""
+    P = wl.random_bf16((t, b, n), 160 + t, device="cuda")
+    peers = [P[r].clone() for r in range(t)]  # separate allocations
+    R = wl.random_bf16((b, n), 161, device="cuda") if with_residual else None
+    gamma = wl.random_bf16((n,), 162, mean=1.0, std=0.1, device="cuda")
+    rout, y = ttl.reduce_partials_rmsnorm_peers(peers, gamma, 1e-5, residual=R)
+    rout_s, y_s = ttl.reduce_partials_rmsnorm(P, gamma, 1e-5, R)
+    torch.cuda.synchronize()
+    assert torch.equal(rout, rout_s) and torch.equal(y, y_s)
+    sample = torch.as_tensor(np.unique(np.r_[0:2, b // 2, b - 1]), device="cuda")
+    Ro = from_gpu(R[sample]) if with_residual else None
+    h, yref = oracle.reduce_partials_rmsnorm(from_gpu(P[:, sample]), Ro, from_gpu(gamma), 1e-5)
+    assert_close(from_gpu(rout[sample]), h, f"peers residual_out t={t} b={b} n={n}")
+    assert_close(from_gpu(y[sample]), yref, f"peers y t={t} b={b} n={n}")
+    if b % t == 0:
+        rows = b // t
+        for r in range(t):
+            Rs = R[r * rows:(r + 1) * rows].contiguous() if with_residual else None
+            ro, yo = ttl.reduce_partials_rmsnorm_peers(peers, gamma, 1e-5, row0=r * rows, rows=rows, residual=Rs)
+            ro_s, yo_s = ttl.reduce_scatter_partials_rmsnorm(P, gamma, 1e-5, r, Rs)
+            torch.cuda.synchronize()
+            assert torch.equal(ro, ro_s) and torch.equal(yo, yo_s), f"two-shot chunk {r}"
+            assert torch.equal(ro, rout_s[r * rows:(r + 1) * rows]), f"two-shot chunk {r}"  # h: per element
+
+
 def test_reduce_scatter_rejects_ragged_rows(ttl):
     P = torch.zeros((4, 6, 8), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ttl.TTLError) as e:
