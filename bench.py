@@ -164,7 +164,9 @@ def run_mlp(ttl, torch, w, b, steps, warmup, seed, layout, rotate_ranks=False, g
     for i in range(steps):
         step(i, evs[i])
     torch.cuda.synchronize()
-    k_ms = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j in range(3)]
+    per_step = [[e[j].elapsed_time(e[j + 1]) for e in evs] for j in range(3)]
+    k_ms = [sum(v) / steps for v in per_step]
+    k_med = [sorted(v)[len(v) // 2] for v in per_step]
 
     f_col = gemm_flops(b, H, 2 * Ir)
     f_row = gemm_flops(b, Ir, H)
@@ -179,7 +181,8 @@ def run_mlp(ttl, torch, w, b, steps, warmup, seed, layout, rotate_ranks=False, g
         "reduce_partials_rmsnorm": {"avg_us": k_ms[2] * 1e3, "mbytes": by_red / 1e6,
                                     "gbs": by_red / (k_ms[2] * 1e6)},
     }
-    for name, d in kern.items():
+    for j, (name, d) in enumerate(kern.items()):
+        d["median_us"] = k_med[j] * 1e3
         d["frac_mfma_peak"] = d.get("tflops", 0.0) / PEAK_BF16_TFLOPS
         d["frac_hbm_peak"] = d["gbs"] / PEAK_HBM_GBS
     res = {"ms_per_step": ms_step, "flops": f_col + f_row, "kernels": kern,
