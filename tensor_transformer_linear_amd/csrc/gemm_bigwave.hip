@@ -1,4 +1,6 @@
-// Tiled bf16 GEMM with one wave64 per SIMD: 256 x 256 tiles, four waves of 128 x 128 outputs each.
+// Tiled bf16 GEMM with one wave64 per SIMD: 256 x 256 tiles, four waves of 128 x 128 outputs each
+// (WN = 128), or 256 x 128 tiles of 128 x 64 per wave (WN = 64) for launches whose wide tiles
+// would leave much of the chip idle.
 //
 // C[M, N] = A[M, K] · B[K, map(N)] with the operands, column maps, LDS layouts and M/N tails of the
 // eight-wave kernel in gemm_bf16.hip; what differs is how the matrix cores are fed.  A wave owning
@@ -14,10 +16,11 @@
 //   slice 1: MFMAs of slice 1;
 //   barrier: the wave waits for its own copies of tile t+1, then the workgroup barrier publishes
 //            tile t+1 and certifies that every wave's reads of tile t have returned;
-//   slice 2: MFMAs, reads of slice 0 of tile t+1, and half of the direct-to-LDS copies of tile t+2
-//            (into tile t's stage, now free), one after every second MFMA;
+//   slice 2: MFMAs, reads of slice 0 of tile t+1, and half of the direct-to-LDS copies of tile
+//            t+kStages (into tile t's stage, now free), one after every second MFMA;
 //   slice 3: MFMAs, reads of slice 1 of tile t+1, the other half of the copies.
-// The copies of a tile thus have until the next barrier (two slices and more) to land.  Measured
+// With two stages (WN = 128) the copies of a tile have until the next barrier (two slices and
+// more) to land; the WN = 64 tiles' k-tiles take half as long, so they use three stages.  Measured
 // alternatives: a copy after every MFMA of one slice starves the wave's matrix core (the copies'
 // issue blocks it); copies spread over all four slices (B staged three-deep to allow it) or moved
 // before the barrier were slower; k-tiles of 32 with a five-stage ring were slower still (twice the
