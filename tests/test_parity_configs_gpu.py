@@ -36,6 +36,15 @@ def _host(d, rows=None):
     return out
 
 
+def _stored(ttl, W, layout):
+    """The logical weight W[k, n] in the requested storage: [k][n], [n][k], or the blocked layout."""
+    if layout == "nk":
+        return W.t().contiguous(), ttl.W_NK
+    if layout == "blk":
+        return ttl.pack_weight_blocked(W), ttl.W_BLOCKED
+    return W, ttl.W_KN
+
+
 def _mlp_device_chain(ttl, X, R, gamma, Wgu, Wd, w, b, lay=0):
     """Wgu and Wd are stored as `lay` says (transposed copies for the [n][k] layout)."""
     t, H, I = w.t, w.hidden, w.intermediate
@@ -61,12 +70,11 @@ def _mlp_oracle_rows(o, X_rows, R_rows, w):
                                  (wl.LLAMA3_8B_MLP_TP8, 256), (wl.LLAMA3_70B_MLP_TP8, 64),
                                  (wl.LLAMA3_70B_MLP_TP8, 4096)],
                          ids=lambda v: v.name if hasattr(v, "name") else f"b{v}")
-@pytest.mark.parametrize("layout", ["kn", "nk"])
+@pytest.mark.parametrize("layout", ["kn", "nk", "blk"])
 def test_mlp_shard_full_size(ttl, w, b, layout):
     d = wl.mlp_inputs(w, b, seed=0, device="cuda")
-    lay = ttl.W_KN if layout == "kn" else ttl.W_NK
-    Wgu_s = d["Wgu"] if layout == "kn" else d["Wgu"].t().contiguous()
-    Wd_s = d["Wd"] if layout == "kn" else d["Wd"].t().contiguous()
+    Wgu_s, lay = _stored(ttl, d["Wgu"], layout)
+    Wd_s, _ = _stored(ttl, d["Wd"], layout)
     acts, P, rout, y = _mlp_device_chain(ttl, d["X"], d["R"], d["gamma"], Wgu_s, Wd_s, w, b, lay)
     del Wgu_s, Wd_s
     rows = sample_rows(b)
@@ -118,15 +126,15 @@ def test_attn_projections_8b_tp4(ttl):
     assert_close(from_gpu(qcat), Xs @ o["Wqkv"][:, :w.n_q_heads * w.head_dim], "q concat over ranks")
 
 
-@pytest.mark.parametrize("layout", ["kn", "nk"])
+@pytest.mark.parametrize("layout", ["kn", "nk", "blk"])
 def test_decoder_layer_70b_tp8(ttl, layout):
     """Full linear path of one Llama-3-70B-shaped layer on one TP=8 rank's shapes, all ranks."""
     w = wl.LLAMA3_70B_LAYER_TP8
     b = w.batches[0]
     d = wl.layer_inputs(w, b, seed=0, device="cuda")
     t, H, I = w.t, w.hidden, w.intermediate
-    lay = ttl.W_KN if layout == "kn" else ttl.W_NK
-    st = (lambda v: v) if layout == "kn" else (lambda v: v.t().contiguous())
+    lay = {"kn": ttl.W_KN, "nk": ttl.W_NK, "blk": ttl.W_BLOCKED}[layout]
+    st = lambda v: _stored(ttl, v, layout)[0]
     sp_c = ttl.qkv_split(w.n_q_heads, w.n_kv_heads, w.head_dim, t)
     sp_o = oracle.qkv_split(w.n_q_heads, w.n_kv_heads, w.head_dim, t)
     kr = w.n_q_heads * w.head_dim // t
@@ -164,7 +172,7 @@ def test_decoder_layer_70b_tp8(ttl, layout):
 
 
 @pytest.mark.parametrize("b", [64, 2048])
-@pytest.mark.parametrize("layout", ["kn", "nk"])
+@pytest.mark.parametrize("layout", ["kn", "nk", "blk"])
 def test_vocab_parallel_lm_head_70b_tp8(ttl, b, layout):
     """Vocab-parallel LM head ("Tensor Parallelism" manual, section "Vocab Parallel"): the column
     GEMM over Llama-3's 128256-token vocabulary at hidden 8192, t = 8 (16032 logits per rank),
@@ -176,10 +184,7 @@ def test_vocab_parallel_lm_head_70b_tp8(ttl, b, layout):
     g = torch.Generator(device="cuda").manual_seed(0)
     X = torch.randn(b, hidden, device="cuda", generator=g).to(torch.bfloat16)
     W = (torch.randn(hidden, vocab, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
-    lay = ttl.W_KN
-    Ws = W
-    if layout == "nk":
-        lay, Ws = ttl.W_NK, W.t().contiguous()
+    Ws, lay = _stored(ttl, W, layout)
     width = vocab // t
     logits = torch.empty((b, vocab), dtype=torch.bfloat16, device="cuda")
     for r in range(t):
