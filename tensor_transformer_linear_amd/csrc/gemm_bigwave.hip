@@ -43,25 +43,28 @@ using namespace gemm;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 256, kBK = 64;
-constexpr int kWM = 128;                 // output rows per wave (2 x 2 wave grid)
-constexpr int kMI = kWM / 32;
+constexpr int kBK = 64;
 constexpr int kKK = kBK / 16;            // k16 slices per k-tile
-constexpr int kAElems = kBM * kBK;
-constexpr int kACopies = kAElems * 2 / 1024 / kWaves;  // 1-KiB copies per wave per k-tile: 8
 constexpr int kChunks = kBK / 8;         // 16-B chunks per staged [rows][k] row
 constexpr int kRowsPer256 = 256 / (2 * kBK);
 constexpr int kRowsPerCopy = 1024 / (2 * kBK);
 
-static_assert(kKK == 4 && kACopies == 8, "the slice schedule assumes these counts");
+static_assert(kKK == 4, "the slice schedule assumes four k16 slices per k-tile");
 
 // WN output columns per wave: 128 (256 x 256 tiles) or 64 (256 x 128 tiles, for launches that
 // have too few 256 x 256 tiles to fill the chip).  The B stage holds 64 k rows of the tile's
-// 2 * WN weight columns.
-template <int MODE, bool WNK, int WN>
+// 2 * WN weight columns.  BM rows per tile: 256, or 192 (96 per wave) for the last round of a
+// launch whose 256-row tiles would leave that round partly idle.
+template <int MODE, bool WNK, int WN, int BM>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void gemm_bigwave_kernel(const GemmParams p) {
   static_assert(WN == 128 || WN == 64, "wave widths built: 128 and 64 columns");
+  static_assert(BM == 256 || (BM == 192 && WN == 128), "tile heights built: 256, and 192 at WN = 128");
+  constexpr int kBM = BM;
+  constexpr int kWM = BM / 2;                    // output rows per wave (2 x 2 wave grid)
+  constexpr int kMI = kWM / 32;
+  constexpr int kAElems = kBM * kBK;
+  constexpr int kACopies = kAElems * 2 / 1024 / kWaves;  // 1-KiB copies per wave per k-tile: 8 or 6
   constexpr int kBN = 2 * WN;                    // weight columns per tile
   constexpr int kNI = WN / 32;
   constexpr int kMps = kMI * kNI;                // MFMAs per k16 slice: 16 or 8
@@ -81,11 +84,24 @@ void gemm_bigwave_kernel(const GemmParams p) {
   const int wm = wave / 2, wn = wave % 2;
 
   // Split-K launches: block = split * tiles + tile; split s runs k-tiles [s * kt_per_split, ...).
+  // Tile sets (p.rects > 0, no splits): block b < rect_tmc[0] * rect_tnc[0] is a tile of
+  // rectangle 0, the rest of rectangle 1; rectangle i is rect_tmc[i] row-tiles from row
+  // rect_row0[i] by rect_tnc[i] tile columns from tile column rect_tn0[i].
   const int tiles = p.tiles_m * p.tiles_n;
   const int split = p.splits > 1 ? (int)blockIdx.x / tiles : 0;
-  int tile_m, tile_n;
-  tile_coords((int)blockIdx.x - split * tiles, p.tiles_m, p.tiles_n, tile_m, tile_n);
-  const int m0 = tile_m * kBM;
+  int tile_m, tile_n, row0 = 0;
+  if (p.rects > 0) {
+    const int c0 = p.rect_tmc[0] * p.rect_tnc[0];
+    const bool second = p.rects > 1 && (int)blockIdx.x >= c0;
+    const int tmc = second ? p.rect_tmc[1] : p.rect_tmc[0];
+    const int tnc = second ? p.rect_tnc[1] : p.rect_tnc[0];
+    tile_coords((int)blockIdx.x - (second ? c0 : 0), tmc, tnc, tile_m, tile_n);
+    tile_n += second ? p.rect_tn0[1] : p.rect_tn0[0];
+    row0 = second ? p.rect_row0[1] : p.rect_row0[0];
+  } else {
+    tile_coords((int)blockIdx.x - split * tiles, p.tiles_m, p.tiles_n, tile_m, tile_n);
+  }
+  const int m0 = row0 + tile_m * kBM;
   const int n0 = tile_n * (MODE == kSiluMul ? kBN / 2 : kBN);  // first output column of the tile
   const int kt0 = split * p.kt_per_split;
   const int nk = p.splits > 1 ? min(p.kt_per_split, p.K / kBK - kt0) : p.K / kBK;  // >= 1
@@ -354,19 +370,20 @@ void gemm_bigwave_kernel(const GemmParams p) {
   }
 }
 
-template <int MODE, bool WNK, int WN>
+template <int MODE, bool WNK, int WN, int BM>
 void launch_one(const GemmParams& p, hipStream_t stream) {
   const int splits = p.splits > 1 ? p.splits : 1;
-  hipLaunchKernelGGL((gemm_bigwave_kernel<MODE, WNK, WN>), dim3((unsigned)(splits * p.tiles_m * p.tiles_n)),
-                     dim3(kThreads), 0, stream, p);
+  const int blocks = p.rects > 0 ? p.rect_tmc[0] * p.rect_tnc[0] + (p.rects > 1 ? p.rect_tmc[1] * p.rect_tnc[1] : 0)
+                                 : splits * p.tiles_m * p.tiles_n;
+  hipLaunchKernelGGL((gemm_bigwave_kernel<MODE, WNK, WN, BM>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
 }
 
-template <int WN>
+template <int WN, int BM>
 void launch_width(const GemmParams& p, hipStream_t stream) {
   if (p.mode == kSiluMul)
-    p.w_nk ? launch_one<kSiluMul, true, WN>(p, stream) : launch_one<kSiluMul, false, WN>(p, stream);
+    p.w_nk ? launch_one<kSiluMul, true, WN, BM>(p, stream) : launch_one<kSiluMul, false, WN, BM>(p, stream);
   else
-    p.w_nk ? launch_one<kPlain, true, WN>(p, stream) : launch_one<kPlain, false, WN>(p, stream);
+    p.w_nk ? launch_one<kPlain, true, WN, BM>(p, stream) : launch_one<kPlain, false, WN, BM>(p, stream);
 }
 
 }  // namespace
@@ -380,7 +397,16 @@ int gemm_bigwave_tile_cols(int mode, bool narrow) {
 
 hipError_t launch_gemm_bigwave(const GemmParams& p, hipStream_t stream) {
   if (p.mode == kSiluMul && p.splits > 1) return hipErrorInvalidValue;  // split SiLU·up runs as halves
-  p.narrow ? launch_width<64>(p, stream) : launch_width<128>(p, stream);
+  if (p.tile_rows == 192) {
+    // Short tiles: wide columns only, no k splits, rows given by a tile set.
+    if (p.narrow || p.splits > 1 || p.rects < 1) return hipErrorInvalidValue;
+    launch_width<128, 192>(p, stream);
+  } else if (p.tile_rows == 256 || p.tile_rows == 0) {
+    if (p.rects > 0 && p.splits > 1) return hipErrorInvalidValue;
+    p.narrow ? launch_width<64, 256>(p, stream) : launch_width<128, 256>(p, stream);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

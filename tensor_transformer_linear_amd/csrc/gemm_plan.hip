@@ -7,7 +7,9 @@
 // rate with one workgroup, and a grid that does not divide evenly over the CUs leaves a slow tail.
 // A launch of whole rounds of 256 x 256 tiles plus a short last round (e.g. 288 tiles: 2176 rows
 // x 8192 columns) is cut by rows: the whole rounds to the tiled kernel, the last few row-tiles to
-// the split-K kernel.
+// the split-K kernel.  One whose last round is more than half full (e.g. 448 tiles: 4096 rows x
+// 3584 SiLU·up columns) is cut per column strip into 256-row tiles that fill the whole rounds and
+// 192-row tiles that fill one more round, which then takes three quarters of a round's time.
 //
 // Workspace: split-K launches with more than one split write fp32 partial tiles that a second
 // kernel reduces.  The library keeps one device buffer per GPU for them, allocated (or grown) on
@@ -25,9 +27,16 @@
 //   TTL_GEMM_KERNEL=narrow        256 x 128 tiles of the four-wave kernel (K a multiple of 64, else
 //                                 the eight-wave kernel's 256 x 256 tiles);
 //   TTL_GEMM_KERNEL=narrowsplit   256 x 128 tiles cut along k, as tilesplit;
-//   TTL_GEMM_SPLITS=<n>           split-K kernel: use n splits (at most one per k-tile).
+//   TTL_GEMM_KERNEL=short         192 x 256 tiles of the four-wave kernel over the whole GEMM (K a
+//                                 multiple of 64, else as by shape);
+//   TTL_GEMM_KERNEL=mixed         the 256-row / 192-row cut wherever one beats whole tiles, planned
+//                                 for TTL_GEMM_PLAN_CUS compute units (default 256);
+//   TTL_GEMM_SPLITS=<n>           split-K kernel: use n splits (at most one per k-tile);
+//   TTL_GEMM_TRACE=1              print each 256-row / 192-row cut to stderr.
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -76,7 +85,8 @@ hipError_t get_workspace(size_t bytes, void** out) {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // 0: by shape, 1: 256 x 256 tiles, 2: split-K, 3: 256 x 256 tiles by the eight-wave kernel,
-// 4: 256 x 256 tiles cut along k, 5: 256 x 128 tiles, 6: 256 x 128 tiles cut along k.
+// 4: 256 x 256 tiles cut along k, 5: 256 x 128 tiles, 6: 256 x 128 tiles cut along k,
+// 7: 192 x 256 tiles, 8: the 256-row / 192-row cut planned for TTL_GEMM_PLAN_CUS CUs.
 int forced_kernel() {
   const char* s = std::getenv("TTL_GEMM_KERNEL");
   if (s == nullptr) return 0;
@@ -86,7 +96,14 @@ int forced_kernel() {
   if (std::strcmp(s, "tilesplit") == 0) return 4;
   if (std::strcmp(s, "narrow") == 0) return 5;
   if (std::strcmp(s, "narrowsplit") == 0) return 6;
+  if (std::strcmp(s, "short") == 0) return 7;
+  if (std::strcmp(s, "mixed") == 0) return 8;
   return 0;
+}
+
+int64_t env_int(const char* name, int64_t dflt) {
+  const char* s = std::getenv(name);
+  return s == nullptr ? dflt : std::atoll(s);
 }
 
 int64_t forced_splits() {
@@ -111,6 +128,109 @@ hipError_t launch_narrow(GemmParams& p, hipStream_t stream) {
   p.splits = 1;
   p.narrow = 1;
   return launch_gemm_bigwave(p, stream);
+}
+
+// Row cut of one launch into 256-row and 192-row tiles (four-wave kernel, 256 weight columns per
+// tile): column strips [0, S) take a[0] 256-row tiles from row 0 and b[0] 192-row tiles for the
+// rows below them, strips [S, tiles_n) take a[1] and b[1].
+struct MixedRows {
+  int64_t S, a[2], b[2];
+};
+
+// A launch of `full` whole rounds of 256-row tiles plus a last round more than half full: find a
+// cut whose 256-row tiles fit in `full` rounds and whose 192-row tiles fit in one.  A 192-row tile
+// holds three quarters of a 256-row tile's work, so the launch takes full + 3/4 rounds instead of
+// full + 1.  Among the cuts that fit, the one with the most 256-row tiles (the more efficient
+// ones).  Strip classes: for a[0] > a[1], the 256-row count full(S) = S*(a0-a1) + tn*a1 grows with
+// S and the 192-row count short(S) = S*(b0-b1) + tn*b1 shrinks, so each pair (a0, a1) admits an
+// interval of S, whose largest member is taken.
+bool plan_mixed_rows(int64_t M, int64_t tn, int64_t cus, MixedRows& out) {
+  if (cus < 1) return false;
+  const int64_t tm = cdiv(M, 256);
+  const int64_t full = (tm * tn) / cus;
+  if (full < 1 || tm > 256 || 2 * ((tm * tn) % cus) <= cus) return false;
+  const int64_t cap_full = full * cus;
+  int64_t best_full = -1;
+  auto shorts = [&](int64_t a) { return M > 256 * a ? cdiv(M - 256 * a, 192) : 0; };
+  for (int64_t a0 = 1; a0 <= tm; ++a0)
+    for (int64_t a1 = 0; a1 <= a0; ++a1) {
+      const int64_t b0 = shorts(a0), b1 = shorts(a1);
+      int64_t lo = 1, hi = tn;  // S in [lo, hi]; S = tn leaves class 1 empty
+      if (a0 == a1) {
+        if (tn * a0 > cap_full || tn * b0 > cus) continue;
+      } else {
+        // S*(a0-a1) + tn*a1 <= cap_full
+        if (tn * a1 > cap_full) continue;
+        hi = std::min(tn - 1, (cap_full - tn * a1) / (a0 - a1));
+        // S*(b1-b0) >= tn*b1 - cus (b1 >= b0)
+        const int64_t need = tn * b1 - cus;
+        if (need > 0) {
+          if (b1 == b0) continue;
+          lo = std::max(lo, cdiv(need, b1 - b0));
+        }
+      }
+      if (lo > hi) continue;
+      const int64_t S = a0 == a1 ? tn : hi;
+      const int64_t nf = S * a0 + (tn - S) * a1, ns = S * b0 + (tn - S) * b1;
+      if (ns == 0 || ns > cus || nf > cap_full) continue;
+      if (nf > best_full) {
+        best_full = nf;
+        out.S = S;
+        out.a[0] = a0;
+        out.a[1] = a1;
+        out.b[0] = b0;
+        out.b[1] = S < tn ? b1 : 0;
+        if (S == tn) out.a[1] = 0;
+      }
+    }
+  return best_full >= 0;
+}
+
+// The cut's two launches of the four-wave kernel: the 256-row tiles of both strip classes, then the
+// 192-row tiles below them.
+hipError_t launch_mixed(GemmParams& p, const MixedRows& m, hipStream_t stream) {
+  const int64_t tn = cdiv(p.N, gemm_tile_cols(p.mode));
+  if (env_int("TTL_GEMM_TRACE", 0) > 0)
+    std::fprintf(stderr, "ttl gemm cut: M=%d N=%d K=%d strips [0,%lld) %lld x 256 + %lld x 192, "
+                 "[%lld,%lld) %lld x 256 + %lld x 192\n", p.M, p.N, p.K, (long long)m.S, (long long)m.a[0],
+                 (long long)m.b[0], (long long)m.S, (long long)tn, (long long)m.a[1], (long long)m.b[1]);
+  for (int pass = 0; pass < 2; ++pass) {
+    GemmParams q = p;
+    q.splits = 1;
+    q.narrow = 0;
+    q.tiles_m = q.tiles_n = 0;
+    q.tile_rows = pass == 0 ? 256 : 192;
+    q.rects = 0;
+    for (int c = 0; c < 2; ++c) {
+      const int64_t width = c == 0 ? m.S : tn - m.S;
+      const int64_t count = pass == 0 ? m.a[c] : m.b[c];
+      if (width <= 0 || count <= 0) continue;
+      const int r = q.rects++;
+      q.rect_tn0[r] = (int32_t)(c == 0 ? 0 : m.S);
+      q.rect_tnc[r] = (int32_t)width;
+      q.rect_row0[r] = (int32_t)(pass == 0 ? 0 : 256 * m.a[c]);
+      q.rect_tmc[r] = (int32_t)count;
+    }
+    if (q.rects == 0) continue;
+    const hipError_t e = launch_gemm_bigwave(q, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// 192 x 256 tiles of the four-wave kernel over all of p, as one tile set.
+hipError_t launch_short(GemmParams& p, hipStream_t stream) {
+  GemmParams q = p;
+  q.splits = 1;
+  q.narrow = 0;
+  q.tiles_m = q.tiles_n = 0;
+  q.tile_rows = 192;
+  q.rects = 1;
+  q.rect_tn0[0] = 0;
+  q.rect_tnc[0] = (int32_t)cdiv(p.N, gemm_tile_cols(p.mode));
+  q.rect_row0[0] = 0;
+  q.rect_tmc[0] = (int32_t)cdiv(p.M, 192);
+  return launch_gemm_bigwave(q, stream);
 }
 
 // 256 x 256 (or, narrow, 256 x 128) tiles of the four-wave kernel cut into `splits` k ranges
@@ -174,6 +294,13 @@ hipError_t launch_splitk(GemmParams& p, hipStream_t stream) {
 hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
   const int force = forced_kernel();
   if (force == 1 || force == 3) return launch_tiles(p, force, stream);
+  if (force == 7 && gemm_bigwave_supports(p)) return launch_short(p, stream);
+  if (force == 8 && gemm_bigwave_supports(p)) {
+    MixedRows m;
+    if (plan_mixed_rows(p.M, cdiv(p.N, gemm_tile_cols(p.mode)), env_int("TTL_GEMM_PLAN_CUS", kCUs), m))
+      return launch_mixed(p, m, stream);
+    return launch_tiles(p, 0, stream);
+  }
   if (force == 5) return gemm_bigwave_supports(p) ? launch_narrow(p, stream) : launch_tiles(p, 3, stream);
   if (force == 2 || ((force == 4 || force == 6) && !gemm_bigwave_supports(p))) return launch_splitk(p, stream);
   const int64_t tiled_m = cdiv(p.M, gemm_tile_rows());
@@ -207,11 +334,17 @@ hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
     }
     return launch_splitk(p, stream);
   }
-  // Whole rounds of one tile per CU plus a short last round (at most half the CUs): that round
-  // would take a whole tile's time with most of the chip idle.  The row-tiles that fill the whole
-  // rounds go to the tiled kernel, the remaining rows (a few row-tiles) to the split-K kernel,
-  // which spreads them over all CUs.
+  // Whole rounds of one tile per CU plus a last round more than half full: 256-row tiles for the
+  // whole rounds and 192-row tiles for the last one, which then takes 3/4 of a round's time.
   const int64_t rounds = tiles / kCUs, rem = tiles % kCUs;
+  if (gemm_bigwave_supports(p)) {
+    MixedRows m;
+    if (plan_mixed_rows(p.M, tiled_n, kCUs, m)) return launch_mixed(p, m, stream);
+  }
+  // Whole rounds plus a short last round (at most half the CUs): that round would take a whole
+  // tile's time with most of the chip idle.  The row-tiles that fill the whole rounds go to the
+  // tiled kernel, the remaining rows (a few row-tiles) to the split-K kernel, which spreads them
+  // over all CUs.
   if (rounds >= 1 && rem > 0 && 2 * rem <= kCUs) {
     const int64_t head_row_tiles = rounds * kCUs / tiled_n;
     if (head_row_tiles >= 1 && head_row_tiles < tiled_m) {

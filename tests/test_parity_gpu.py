@@ -3,8 +3,8 @@
 Small cases compare every element; they span several 256-wide tiles and ragged tails in all three
 GEMM dimensions.  Each GEMM case runs through every kernel the library has, forced with
 TTL_GEMM_KERNEL (256 x 256 tiles by the four-wave kernel where K is a multiple of 64, by the
-eight-wave kernel, the four-wave kernel's tiles cut along k, its 256 x 128 tiles, and the split-K
-kernel for short M), and through the shape-based choice.  Tolerance, per output tensor: the error beyond the bf16 rounding of each output
+eight-wave kernel, the four-wave kernel's tiles cut along k, its 256 x 128 tiles, its 192 x 256
+tiles, and the split-K kernel for short M), and through the shape-based choice.  Tolerance, per output tensor: the error beyond the bf16 rounding of each output
 element is at most 2e-2 * rms(ref), the reference being the oracle's unrounded float64 value (bf16
 inputs, so the device-side error is fp32 accumulation and fp32 elementwise math).  Integer-exact
 special cases (identity and one-hot operands) are compared bit for bit.
@@ -31,7 +31,7 @@ def ttl():
 LAYOUTS = pytest.mark.parametrize("layout", ["kn", "nk"])
 
 
-@pytest.fixture(params=["auto", "tiled", "eightwave", "tilesplit", "narrow", "splitk"])
+@pytest.fixture(params=["auto", "tiled", "eightwave", "tilesplit", "narrow", "short", "splitk"])
 def gemm_path(request, monkeypatch):
     """Which GEMM kernel the library uses for the test (auto = its choice by shape)."""
     if request.param == "auto":
@@ -344,6 +344,105 @@ def test_auto_choice_of_narrow_tiles(ttl, monkeypatch, case):
     rows = np.r_[0:4, 254:258, 508:512]
     ref = oracle.col_shard(f64(X)[rows], f64(W), oracle.plain_split(n, 1), 1, 0)
     assert_close(from_gpu(outs["auto"])[rows], ref, f"auto {case}")
+
+
+def _stored3(ttl, W, layout):
+    """_stored, plus the blocked storage (packed on the device)."""
+    if layout == "blk":
+        return ttl.pack_weight_blocked(gpu(W)), ttl.W_BLOCKED
+    return _stored(ttl, W, layout)
+
+
+# (b, k, n, silu, cus): the cut the planner makes for `cus` compute units, in 256-column strips
+# (128 act columns with SiLU·up):
+MIXED_CASES = [
+    # 7 SiLU·up strips: strips [0, 3) take 4 x 256 rows (the last ragged), [3, 7) 1 x 256 + 4 x 192
+    # rows (the last ragged); 4 k-tiles
+    (1000, 256, 896, True, 16),
+    # 7 plain strips, the last one 128 columns wide; one k-tile
+    (1000, 64, 1664, False, 16),
+    # 28 plain strips: [0, 26) 9 x 256 rows (the last ragged), [26, 28) 3 x 256 + 8 x 192; 3 k-tiles
+    (2176, 192, 7168, False, 16),
+]
+
+
+@pytest.mark.parametrize("b,k,n,silu,cus", MIXED_CASES)
+@pytest.mark.parametrize("layout", ["kn", "nk", "blk"])
+def test_mixed_row_cut(ttl, monkeypatch, capfd, b, k, n, silu, cus, layout):
+    """A launch cut per column strip into 256-row tiles (whole rounds) and 192-row tiles below
+    them (one more round), planned for a small CU count so that small shapes take the cut: the
+    cut runs (the planner's trace line), its result equals the 256 x 256 tiles' and the 192 x 256
+    tiles' bit for bit (same products, same k order), and every element matches the oracle."""
+    monkeypatch.delenv("TTL_GEMM_SPLITS", raising=False)
+    monkeypatch.setenv("TTL_GEMM_TRACE", "1")
+    monkeypatch.setenv("TTL_GEMM_PLAN_CUS", str(cus))
+    X = wl.random_bf16((b, k), 400 + b + k)
+    if silu:
+        W = wl.random_bf16((k, 2 * n), 401 + k, std=0.05)
+        sp_c, sp_np, epi = ttl.merged_gate_up_split(n, 1), oracle.merged_gate_up_split(n, 1), ttl.EPI_SILU_MUL
+    else:
+        W = wl.random_bf16((k, n), 401 + k, std=0.05)
+        sp_c, sp_np, epi = None, oracle.plain_split(n, 1), 0
+    Wd_, lay = _stored3(ttl, W, layout)
+    capfd.readouterr()
+    outs = {}
+    for kern in ("mixed", "tiled", "short"):
+        monkeypatch.setenv("TTL_GEMM_KERNEL", kern)
+        outs[kern] = ttl.shard_linear_col(gpu(X), Wd_, 1, 0, sp_c, epi, w_layout=lay)
+        torch.cuda.synchronize()
+    err = capfd.readouterr().err
+    assert err.count("ttl gemm cut") == 1, err
+    assert torch.equal(outs["mixed"], outs["tiled"])
+    assert torch.equal(outs["short"], outs["tiled"])
+    ref = oracle.col_shard(f64(X), f64(W), sp_np, 1, 0)
+    if silu:
+        ref = oracle.silu_mul(ref)
+    assert_close(from_gpu(outs["mixed"]), ref, f"mixed cut b={b} k={k} n={n} silu={silu} {layout}")
+
+
+@pytest.mark.parametrize("silu", [False, True])
+def test_auto_mixed_row_cut(ttl, monkeypatch, capfd, silu):
+    """At 256 CUs the shape-based choice cuts 2500 x 10240 outputs (400 tiles of 256 x 256: one
+    round plus 144 tiles) and 4096 x 3584 SiLU·up outputs (448 tiles: one round plus 192) into
+    256-row and 192-row tiles; bit-equal to the 256 x 256 tiles, sampled rows (both sides of every
+    strip class's cut) against the oracle; the row GEMM of 4096 x 8192 (512 tiles, two whole
+    rounds) is not cut."""
+    monkeypatch.delenv("TTL_GEMM_SPLITS", raising=False)
+    monkeypatch.delenv("TTL_GEMM_PLAN_CUS", raising=False)
+    monkeypatch.setenv("TTL_GEMM_TRACE", "1")
+    k = 128
+    if silu:
+        b, n = 4096, 3584
+        W = wl.random_bf16((k, 2 * n), 411, std=0.05)
+        sp_c, sp_np, epi = ttl.merged_gate_up_split(n, 1), oracle.merged_gate_up_split(n, 1), ttl.EPI_SILU_MUL
+        rows = np.r_[0:2, 1022:1026, 1214:1218, 2558:2562, 2750:2754, 4094:4096]
+    else:
+        b, n = 2500, 10240
+        W = wl.random_bf16((k, n), 411, std=0.05)
+        sp_c, sp_np, epi = None, oracle.plain_split(n, 1), 0
+        rows = np.r_[0:2, 254:258, 446:450, 1790:1794, 1982:1986, 2496:2500]
+    X = wl.random_bf16((b, k), 410)
+    capfd.readouterr()
+    outs = {}
+    for kern in ("auto", "tiled"):
+        if kern == "auto":
+            monkeypatch.delenv("TTL_GEMM_KERNEL", raising=False)
+        else:
+            monkeypatch.setenv("TTL_GEMM_KERNEL", kern)
+        outs[kern] = ttl.shard_linear_col(gpu(X), gpu(W), 1, 0, sp_c, epi)
+        torch.cuda.synchronize()
+    err = capfd.readouterr().err
+    assert err.count("ttl gemm cut") == 1, err
+    assert torch.equal(outs["auto"], outs["tiled"])
+    ref = oracle.col_shard(f64(X)[rows], f64(W), sp_np, 1, 0)
+    if silu:
+        ref = oracle.silu_mul(ref)
+    assert_close(from_gpu(outs["auto"])[rows], ref, f"auto cut silu={silu}")
+    # two whole rounds: no cut
+    Xr = gpu(wl.random_bf16((4096, 256), 412))
+    ttl.shard_linear_row(Xr, gpu(wl.random_bf16((256, 8192), 413, std=0.05)), 1, 0, True)
+    torch.cuda.synchronize()
+    assert "ttl gemm cut" not in capfd.readouterr().err
 
 
 def _blocked_reference(W):

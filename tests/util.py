@@ -64,7 +64,10 @@ def assert_close(got: np.ndarray, ref: np.ndarray, what: str, tol: float = TOL):
 def sample_rows(b: int, extra=()) -> list:
     """Rows checked one by one at full size: both ends, tile boundaries and a few seeded picks."""
     rows = {0, b - 1}
-    for edge in (31, 32, 127, 128, 255, 256, 511, 512, 2047, 2048, 4095):
+    # tile edges, and the 256-row / 192-row cut of 4096-row SiLU·up launches (1024 + 192 * j,
+    # 2560 + 192 * j)
+    for edge in (31, 32, 127, 128, 255, 256, 511, 512, 1023, 1024, 1215, 1216, 2047, 2048, 2559,
+                 2560, 2751, 2752, 4095):
         if edge < b:
             rows.add(edge)
     rng = np.random.default_rng(1234 + b)
