@@ -86,7 +86,8 @@ void gemm_bigwave_kernel(const GemmParams p) {
   // Split-K launches: block = split * tiles + tile; split s runs k-tiles [s * kt_per_split, ...).
   // Tile sets (p.rects > 0, no splits): block b < rect_tmc[0] * rect_tnc[0] is a tile of
   // rectangle 0, the rest of rectangle 1; rectangle i is rect_tmc[i] row-tiles from row
-  // rect_row0[i] by rect_tnc[i] tile columns from tile column rect_tn0[i].
+  // rect_row0[i] by rect_tnc[i] tile columns from tile column rect_tn0[i], walked in groups of
+  // rect_group[i] row-tiles.
   const int tiles = p.tiles_m * p.tiles_n;
   const int split = p.splits > 1 ? (int)blockIdx.x / tiles : 0;
   int tile_m, tile_n, row0 = 0;
@@ -95,7 +96,8 @@ void gemm_bigwave_kernel(const GemmParams p) {
     const bool second = p.rects > 1 && (int)blockIdx.x >= c0;
     const int tmc = second ? p.rect_tmc[1] : p.rect_tmc[0];
     const int tnc = second ? p.rect_tnc[1] : p.rect_tnc[0];
-    tile_coords((int)blockIdx.x - (second ? c0 : 0), tmc, tnc, tile_m, tile_n);
+    const int group = second ? p.rect_group[1] : p.rect_group[0];
+    tile_coords((int)blockIdx.x - (second ? c0 : 0), tmc, tnc, tile_m, tile_n, group > 0 ? group : 4);
     tile_n += second ? p.rect_tn0[1] : p.rect_tn0[0];
     row0 = second ? p.rect_row0[1] : p.rect_row0[0];
   } else {

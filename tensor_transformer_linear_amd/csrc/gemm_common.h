@@ -91,19 +91,20 @@ __device__ inline i32x4_t blocked_desc(const uint16_t* B, int64_t b_elems, int k
 
 // Tile order of the 256 x 256-tile kernels.  Consecutive workgroups are dealt to different XCDs
 // (8 on MI355X), each with its own L2: the block index is remapped so that each XCD runs a compact
-// run of tiles, and tiles are walked in groups of kGroupM row-tiles (all columns of a group before
+// run of tiles, and tiles are walked in groups of `group` row-tiles (all columns of a group before
 // the next), so that one XCD's tiles share A rows and weight columns in its L2.  Both maps are
-// bijections on [0, tiles_m * tiles_n).
-__device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int kXcds = 8, kGroupM = 4;
+// bijections on [0, tiles_m * tiles_n) for any group >= 1.  Also compiled for the host, where the
+// launch planner scores candidate group heights with it.
+__host__ __device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn, int group = 4) {
+  constexpr int kXcds = 8;
   const int tiles = tiles_m * tiles_n;
   const int q = tiles / kXcds, r = tiles % kXcds;
   const int x = bid % kXcds, local = bid / kXcds;
   const int L = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
-  const int per_group = kGroupM * tiles_n;
+  const int per_group = group * tiles_n;
   const int g = L / per_group;
-  const int first = g * kGroupM;
-  const int gsize = min(tiles_m - first, kGroupM);
+  const int first = g * group;
+  const int gsize = tiles_m - first < group ? tiles_m - first : group;
   const int inner = L - g * per_group;
   tm = first + inner % gsize;
   tn = inner / gsize;

@@ -40,7 +40,7 @@
 #include <mutex>
 #include <vector>
 
-#include "kernels.h"
+#include "gemm_common.h"
 
 namespace ttl {
 namespace {
@@ -186,33 +186,125 @@ bool plan_mixed_rows(int64_t M, int64_t tn, int64_t cus, MixedRows& out) {
   return best_full >= 0;
 }
 
-// The cut's two launches of the four-wave kernel: the 256-row tiles of both strip classes, then the
-// 192-row tiles below them.
-hipError_t launch_mixed(GemmParams& p, const MixedRows& m, hipStream_t stream) {
-  const int64_t tn = cdiv(p.N, gemm_tile_cols(p.mode));
-  if (env_int("TTL_GEMM_TRACE", 0) > 0)
-    std::fprintf(stderr, "ttl gemm cut: M=%d N=%d K=%d strips [0,%lld) %lld x 256 + %lld x 192, "
-                 "[%lld,%lld) %lld x 256 + %lld x 192\n", p.M, p.N, p.K, (long long)m.S, (long long)m.a[0],
-                 (long long)m.b[0], (long long)m.S, (long long)tn, (long long)m.a[1], (long long)m.b[1]);
+// Bytes that the 8 XCDs' L2s fetch per k-tile for a tile-set launch, if each XCD fetches every A
+// row-block and weight strip its tiles use once per k-tile (the launch's tiles run concurrently, one
+// per CU, in step along k).  With 4-MB L2s this matches the FETCH_SIZE counter of these launches.
+int64_t tile_set_fetch(const GemmParams& q, int64_t M, int64_t tn) {
+  constexpr int kXcds = 8;
+  const int64_t rblocks = cdiv(M, 64);
+  std::vector<int> a_seen((size_t)(rblocks * kXcds), 0), b_seen((size_t)(tn * kXcds), 0);
+  int64_t a_count = 0, b_count = 0;
+  int bid = 0;
+  for (int r = 0; r < q.rects; ++r)
+    for (int b = 0; b < q.rect_tmc[r] * q.rect_tnc[r]; ++b, ++bid) {
+      int tm = 0, tc = 0;
+      gemm::tile_coords(b, q.rect_tmc[r], q.rect_tnc[r], tm, tc, q.rect_group[r]);
+      const int x = bid % kXcds;
+      const int64_t rb = (q.rect_row0[r] + (int64_t)tm * q.tile_rows) / 64;
+      const int64_t st = q.rect_tn0[r] + tc;
+      if (rb < rblocks && !a_seen[(size_t)(x * rblocks + rb)]++) ++a_count;
+      if (st < tn && !b_seen[(size_t)(x * tn + st)]++) ++b_count;
+    }
+  return a_count * q.tile_rows * 128 + b_count * 256 * 128;
+}
+
+// Group heights for the rectangles of a tile-set launch that minimise tile_set_fetch.
+void choose_groups(GemmParams& q, int64_t M, int64_t tn) {
+  int best[2] = {4, 4};
+  int64_t best_bytes = -1;
+  const int g1max = q.rects > 1 ? q.rect_tmc[1] : 1;
+  for (int g0 = 1; g0 <= q.rect_tmc[0]; ++g0)
+    for (int g1 = 1; g1 <= g1max; ++g1) {
+      q.rect_group[0] = g0;
+      q.rect_group[1] = g1;
+      const int64_t bytes = tile_set_fetch(q, M, tn);
+      if (best_bytes < 0 || bytes < best_bytes) {
+        best_bytes = bytes;
+        best[0] = g0;
+        best[1] = g1;
+      }
+    }
+  q.rect_group[0] = best[0];
+  q.rect_group[1] = best[1];
+}
+
+// The cut's two launches of the four-wave kernel: the 256-row tiles of both strip classes, then
+// the 192-row tiles below them, each with the group heights that keep its L2 fetches lowest.
+// Plans are cached per (M, N, K, mode, CU count): the group search costs about a millisecond.
+struct MixedLaunch {
+  int64_t M, N, K, cus;
+  int32_t mode;
+  GemmParams q[2];  // tiling fields only
+};
+std::mutex g_plan_mutex;
+std::vector<MixedLaunch> g_plans;
+
+void build_mixed(const GemmParams& p, const MixedRows& m, int64_t tn, GemmParams q[2]) {
   for (int pass = 0; pass < 2; ++pass) {
-    GemmParams q = p;
-    q.splits = 1;
-    q.narrow = 0;
-    q.tiles_m = q.tiles_n = 0;
-    q.tile_rows = pass == 0 ? 256 : 192;
-    q.rects = 0;
+    GemmParams& t = q[pass];
+    t = p;
+    t.splits = 1;
+    t.narrow = 0;
+    t.tiles_m = t.tiles_n = 0;
+    t.tile_rows = pass == 0 ? 256 : 192;
+    t.rects = 0;
     for (int c = 0; c < 2; ++c) {
       const int64_t width = c == 0 ? m.S : tn - m.S;
       const int64_t count = pass == 0 ? m.a[c] : m.b[c];
       if (width <= 0 || count <= 0) continue;
-      const int r = q.rects++;
-      q.rect_tn0[r] = (int32_t)(c == 0 ? 0 : m.S);
-      q.rect_tnc[r] = (int32_t)width;
-      q.rect_row0[r] = (int32_t)(pass == 0 ? 0 : 256 * m.a[c]);
-      q.rect_tmc[r] = (int32_t)count;
+      const int r = t.rects++;
+      t.rect_tn0[r] = (int32_t)(c == 0 ? 0 : m.S);
+      t.rect_tnc[r] = (int32_t)width;
+      t.rect_row0[r] = (int32_t)(pass == 0 ? 0 : 256 * m.a[c]);
+      t.rect_tmc[r] = (int32_t)count;
+      t.rect_group[r] = 4;
     }
-    if (q.rects == 0) continue;
-    const hipError_t e = launch_gemm_bigwave(q, stream);
+    if (t.rects > 0) choose_groups(t, p.M, tn);
+  }
+}
+
+hipError_t launch_mixed(GemmParams& p, const MixedRows& m, int64_t cus, hipStream_t stream) {
+  const int64_t tn = cdiv(p.N, gemm_tile_cols(p.mode));
+  GemmParams q[2];
+  bool cached = false;
+  {
+    std::lock_guard<std::mutex> lock(g_plan_mutex);
+    for (const MixedLaunch& c : g_plans)
+      if (c.M == p.M && c.N == p.N && c.K == p.K && c.mode == p.mode && c.cus == cus) {
+        q[0] = c.q[0];
+        q[1] = c.q[1];
+        cached = true;
+        break;
+      }
+  }
+  if (!cached) {
+    build_mixed(p, m, tn, q);
+    std::lock_guard<std::mutex> lock(g_plan_mutex);
+    if (g_plans.size() < 64) g_plans.push_back({p.M, p.N, p.K, cus, p.mode, {q[0], q[1]}});
+  }
+  if (env_int("TTL_GEMM_TRACE", 0) > 0)
+    std::fprintf(stderr, "ttl gemm cut: M=%d N=%d K=%d strips [0,%lld) %lld x 256 + %lld x 192, "
+                 "[%lld,%lld) %lld x 256 + %lld x 192, groups %d/%d and %d/%d\n", p.M, p.N, p.K,
+                 (long long)m.S, (long long)m.a[0], (long long)m.b[0], (long long)m.S, (long long)tn,
+                 (long long)m.a[1], (long long)m.b[1], q[0].rect_group[0], q[0].rect_group[1],
+                 q[1].rect_group[0], q[1].rect_group[1]);
+  for (int pass = 0; pass < 2; ++pass) {
+    if (q[pass].rects == 0) continue;
+    // The cached tiling fields with this call's pointers and strides.
+    GemmParams t = p;
+    t.splits = 1;
+    t.narrow = 0;
+    t.tiles_m = t.tiles_n = 0;
+    t.tile_rows = q[pass].tile_rows;
+    t.rects = q[pass].rects;
+    for (int r = 0; r < 2; ++r) {
+      t.rect_tn0[r] = q[pass].rect_tn0[r];
+      t.rect_tnc[r] = q[pass].rect_tnc[r];
+      t.rect_row0[r] = q[pass].rect_row0[r];
+      t.rect_tmc[r] = q[pass].rect_tmc[r];
+      t.rect_group[r] = q[pass].rect_group[r];
+    }
+    const hipError_t e = launch_gemm_bigwave(t, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -297,8 +389,8 @@ hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
   if (force == 7 && gemm_bigwave_supports(p)) return launch_short(p, stream);
   if (force == 8 && gemm_bigwave_supports(p)) {
     MixedRows m;
-    if (plan_mixed_rows(p.M, cdiv(p.N, gemm_tile_cols(p.mode)), env_int("TTL_GEMM_PLAN_CUS", kCUs), m))
-      return launch_mixed(p, m, stream);
+    const int64_t cus = env_int("TTL_GEMM_PLAN_CUS", kCUs);
+    if (plan_mixed_rows(p.M, cdiv(p.N, gemm_tile_cols(p.mode)), cus, m)) return launch_mixed(p, m, cus, stream);
     return launch_tiles(p, 0, stream);
   }
   if (force == 5) return gemm_bigwave_supports(p) ? launch_narrow(p, stream) : launch_tiles(p, 3, stream);
@@ -339,7 +431,7 @@ hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
   const int64_t rounds = tiles / kCUs, rem = tiles % kCUs;
   if (gemm_bigwave_supports(p)) {
     MixedRows m;
-    if (plan_mixed_rows(p.M, tiled_n, kCUs, m)) return launch_mixed(p, m, stream);
+    if (plan_mixed_rows(p.M, tiled_n, kCUs, m)) return launch_mixed(p, m, kCUs, stream);
   }
   // Whole rounds plus a short last round (at most half the CUs): that round would take a whole
   // tile's time with most of the chip idle.  The row-tiles that fill the whole rounds go to the

@@ -39,10 +39,11 @@ struct GemmParams {
   // Four-wave kernel: tile_rows = 256 (0 means 256) or 192.  192-row tiles run only as a tile set.
   // Tile sets (rects = 1 or 2, no splits): the launch covers rectangle 0 then rectangle 1, rectangle
   // i being rect_tmc[i] row-tiles of tile_rows rows from row rect_row0[i], by rect_tnc[i] tile
-  // columns from tile column rect_tn0[i]; rects = 0 is tiles_m x tiles_n tiles from (0, 0).
+  // columns from tile column rect_tn0[i], walked in groups of rect_group[i] row-tiles (0: 4); rects
+  // = 0 is tiles_m x tiles_n tiles from (0, 0).
   int32_t tile_rows;
   int32_t rects;
-  int32_t rect_tn0[2], rect_tnc[2], rect_row0[2], rect_tmc[2];
+  int32_t rect_tn0[2], rect_tnc[2], rect_row0[2], rect_tmc[2], rect_group[2];
 };
 
 // SiLU·up as a plain GEMM over the gate columns followed by the up columns (2N outputs, two column
