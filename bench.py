@@ -46,6 +46,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (8 TB/s)
 # apply only while these files are unchanged.
 TRAFFIC_SOURCES = ("tensor_transformer_linear_amd/csrc/gemm_bigwave.hip",
                    "tensor_transformer_linear_amd/csrc/gemm_common.h",
+                   "tensor_transformer_linear_amd/csrc/gemm_plan.hip",
                    "tensor_transformer_linear_amd/csrc/kernels.h")
 
 

@@ -30,13 +30,14 @@
 //   TTL_GEMM_KERNEL=short         192 x 256 tiles of the four-wave kernel over the whole GEMM (K a
 //                                 multiple of 64, else as by shape);
 //   TTL_GEMM_KERNEL=mixed         the 256-row / 192-row cut wherever one beats whole tiles, planned
-//                                 for TTL_GEMM_PLAN_CUS compute units (default 256);
+//                                 for TTL_GEMM_PLAN_CUS compute units (default: the device's);
 //   TTL_GEMM_SPLITS=<n>           split-K kernel: use n splits (at most one per k-tile);
 //   TTL_GEMM_TRACE=1              print each 256-row / 192-row cut to stderr.
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -45,9 +46,7 @@
 namespace ttl {
 namespace {
 
-constexpr int kCUs = 256;               // MI355X compute units
-constexpr int kTiledMinTiles = 192;     // 256 x 256 tiles when they occupy >= 3/4 of the CUs
-constexpr int kSkinnyBlocks = kCUs;     // split-K grid: at most one workgroup per CU
+constexpr int kDefaultCUs = 256;        // MI355X compute units (a whole-chip device)
 constexpr int kMinKTilesPerSplit = 4;   // keep each split's copy pipeline full
 constexpr int kTileSplitMinRows = 512;  // 256 x 256 tiles cut along k from this many rows
 constexpr int kMinKTilesPerTileSplit = 16;
@@ -83,6 +82,23 @@ hipError_t get_workspace(size_t bytes, void** out) {
 }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Compute units of the current device (256 on a whole MI355X; fewer on a compute partition), read
+// once per device: every launch shape below is sized against it.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+int64_t device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return kDefaultCUs;
+  int n = g_cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = kDefaultCUs;
+    g_cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 // 0: by shape, 1: 256 x 256 tiles, 2: split-K, 3: 256 x 256 tiles by the eight-wave kernel,
 // 4: 256 x 256 tiles cut along k, 5: 256 x 128 tiles, 6: 256 x 128 tiles cut along k,
@@ -358,7 +374,7 @@ hipError_t launch_splitk(GemmParams& p, hipStream_t stream) {
   const int64_t tiles_n = cdiv(p.N, p.mode == 1 ? kSkinnyCols / 2 : kSkinnyCols);
   const int64_t tiles = tiles_m * tiles_n;
   const int64_t nk = cdiv(p.K, kSkinnyK);
-  int64_t splits = kSkinnyBlocks / tiles;
+  int64_t splits = device_cus() / tiles;  // split-K grid: at most one workgroup per CU
   const int64_t max_splits = nk / kMinKTilesPerSplit > 1 ? nk / kMinKTilesPerSplit : 1;
   if (splits > max_splits) splits = max_splits;
   const int64_t fs = forced_splits();
@@ -385,11 +401,13 @@ hipError_t launch_splitk(GemmParams& p, hipStream_t stream) {
 
 hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
   const int force = forced_kernel();
+  const int64_t n_cu = device_cus();
+  const int64_t min_tiled = n_cu * 3 / 4;  // 256 x 256 tiles when they occupy >= 3/4 of the CUs
   if (force == 1 || force == 3) return launch_tiles(p, force, stream);
   if (force == 7 && gemm_bigwave_supports(p)) return launch_short(p, stream);
   if (force == 8 && gemm_bigwave_supports(p)) {
     MixedRows m;
-    const int64_t cus = env_int("TTL_GEMM_PLAN_CUS", kCUs);
+    const int64_t cus = env_int("TTL_GEMM_PLAN_CUS", device_cus());
     if (plan_mixed_rows(p.M, cdiv(p.N, gemm_tile_cols(p.mode)), cus, m)) return launch_mixed(p, m, cus, stream);
     return launch_tiles(p, 0, stream);
   }
@@ -401,24 +419,24 @@ hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
   const int64_t narrow_tiles = tiled_m * cdiv(p.N, gemm_bigwave_tile_cols(p.mode, true));
   if (force == 4 || force == 6) {
     const int64_t fs = forced_splits();
-    const int64_t auto_splits = kCUs / (force == 4 ? tiles : narrow_tiles);
+    const int64_t auto_splits = n_cu / (force == 4 ? tiles : narrow_tiles);
     return launch_tiles_splitk(p, fs > 0 ? fs : (auto_splits > 2 ? auto_splits : 2), force == 6, stream);
   }
-  if (tiles < kTiledMinTiles) {
+  if (tiles < min_tiled) {
     // Few 256 x 256 tiles.  With many rows and a long k, 256 x 256 tiles cut along k into about
     // one workgroup per CU keep the matrix cores busier than the split-K kernel's 128-row tiles;
     // each split takes at least kMinKTilesPerTileSplit k-tiles, as the fp32 partial tiles cost HBM
     // traffic (k = 1024 with 2 splits measured slower than the split-K kernel).  Decode-sized
     // launches stay on the split-K kernel, which is built to stream the weight.
     // Where 256 x 128 tiles fill at least as much of the chip in one round, they run whole.
-    if (p.M >= kTileSplitMinRows && gemm_bigwave_supports(p) && narrow_tiles >= kTiledMinTiles &&
-        narrow_tiles <= kCUs)
+    if (p.M >= kTileSplitMinRows && gemm_bigwave_supports(p) && narrow_tiles >= min_tiled &&
+        narrow_tiles <= n_cu)
       return launch_narrow(p, stream);
     // Otherwise tiles cut along k: 256 x 256 tiles, or 256 x 128 tiles where those occupy at
     // least as many CUs (then with half the partial bytes per output).
     const int64_t by_k = (p.K / 64) / kMinKTilesPerTileSplit;
-    const int64_t splits = kCUs / tiles < by_k ? kCUs / tiles : by_k;
-    const int64_t nsplits = kCUs / narrow_tiles < by_k ? kCUs / narrow_tiles : by_k;
+    const int64_t splits = n_cu / tiles < by_k ? n_cu / tiles : by_k;
+    const int64_t nsplits = n_cu / narrow_tiles < by_k ? n_cu / narrow_tiles : by_k;
     if (p.M >= kTileSplitMinRows && gemm_bigwave_supports(p)) {
       if (nsplits >= 2 && narrow_tiles * nsplits >= tiles * splits)
         return launch_tiles_splitk(p, nsplits, true, stream);
@@ -428,17 +446,17 @@ hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
   }
   // Whole rounds of one tile per CU plus a last round more than half full: 256-row tiles for the
   // whole rounds and 192-row tiles for the last one, which then takes 3/4 of a round's time.
-  const int64_t rounds = tiles / kCUs, rem = tiles % kCUs;
+  const int64_t rounds = tiles / n_cu, rem = tiles % n_cu;
   if (gemm_bigwave_supports(p)) {
     MixedRows m;
-    if (plan_mixed_rows(p.M, tiled_n, kCUs, m)) return launch_mixed(p, m, kCUs, stream);
+    if (plan_mixed_rows(p.M, tiled_n, n_cu, m)) return launch_mixed(p, m, n_cu, stream);
   }
   // Whole rounds plus a short last round (at most half the CUs): that round would take a whole
   // tile's time with most of the chip idle.  The row-tiles that fill the whole rounds go to the
   // tiled kernel, the remaining rows (a few row-tiles) to the split-K kernel, which spreads them
   // over all CUs.
-  if (rounds >= 1 && rem > 0 && 2 * rem <= kCUs) {
-    const int64_t head_row_tiles = rounds * kCUs / tiled_n;
+  if (rounds >= 1 && rem > 0 && 2 * rem <= n_cu) {
+    const int64_t head_row_tiles = rounds * n_cu / tiled_n;
     if (head_row_tiles >= 1 && head_row_tiles < tiled_m) {
       GemmParams head = p;
       head.M = (int32_t)(head_row_tiles * gemm_tile_rows());

@@ -689,16 +689,22 @@ def test_reduce_scatter_rejects_ragged_rows(ttl):
 
 # ---- stream capture -------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("b", [64, 600])
-def test_graph_replay_matches_eager(ttl, monkeypatch, b):
+@pytest.mark.parametrize("b", [64, 600, 1000])
+def test_graph_replay_matches_eager(ttl, monkeypatch, capfd, b):
     """The rank chain (gate_up + SiLU·up, down, reduce + RMSNorm over all ranks) captured into a HIP
     graph and replayed three times, with eager work between the replays (including a split-K call
     large enough to replace the library's workspace), reproduces the eager outputs bit for bit.
-    b = 64 runs the split-K kernel with its workspace, b = 600 the 256 x 256 tiles."""
+    b = 64 runs the split-K kernel with its workspace, b = 600 the 256 x 256 tiles, b = 1000 the
+    256-row / 192-row cut (planned for 10 CUs: both GEMMs are 16 tiles of 256 x 256, one round
+    plus 6 tiles, cut into 10 tiles of 256 rows and 10 of 192 rows)."""
     monkeypatch.delenv("TTL_GEMM_KERNEL", raising=False)
     monkeypatch.delenv("TTL_GEMM_SPLITS", raising=False)
     if b == 600:
         monkeypatch.setenv("TTL_GEMM_KERNEL", "tiled")
+    if b == 1000:
+        monkeypatch.setenv("TTL_GEMM_KERNEL", "mixed")
+        monkeypatch.setenv("TTL_GEMM_PLAN_CUS", "10")
+        monkeypatch.setenv("TTL_GEMM_TRACE", "1")
     t, H, I = 4, 1024, 2048
     X = gpu(wl.random_bf16((b, H), 160))
     R = gpu(wl.random_bf16((b, H), 161))
@@ -717,8 +723,11 @@ def test_graph_replay_matches_eager(ttl, monkeypatch, b):
             ttl.shard_linear_row(act[r], Wd, t, r, True, P=P[r])
         ttl.reduce_partials_rmsnorm(P, gamma, 1e-5, R, residual_out=rout, Y=y)
 
+    capfd.readouterr()
     chain()  # eager; also allocates the workspace before capture
     torch.cuda.synchronize()
+    if b == 1000:
+        assert capfd.readouterr().err.count("ttl gemm cut") == 2 * t  # both GEMMs of every rank
     want = [v.clone() for v in (act, P, rout, y)]
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
