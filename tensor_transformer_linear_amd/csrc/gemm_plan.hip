@@ -202,13 +202,16 @@ bool plan_mixed_rows(int64_t M, int64_t tn, int64_t cus, MixedRows& out) {
   return best_full >= 0;
 }
 
-// Bytes that the 8 XCDs' L2s fetch per k-tile for a tile-set launch, if each XCD fetches every A
-// row-block and weight strip its tiles use once per k-tile (the launch's tiles run concurrently, one
-// per CU, in step along k).  With 4-MB L2s this matches the FETCH_SIZE counter of these launches.
-int64_t tile_set_fetch(const GemmParams& q, int64_t M, int64_t tn) {
+// Bytes that the 8 XCDs' L2s fetch per k-tile for a tile-set launch of at most one round (its
+// tiles run concurrently, one per CU, in step along k), if each XCD fetches every A row-block and
+// weight strip its tiles use once per k-tile.  With 4-MB L2s this matches the FETCH_SIZE counter
+// of these launches.  a_seen / b_seen: scratch of 8 * ceil(M / 64) and 8 * tn entries.
+int64_t tile_set_fetch(const GemmParams& q, int64_t M, int64_t tn, std::vector<int>& a_seen,
+                       std::vector<int>& b_seen) {
   constexpr int kXcds = 8;
   const int64_t rblocks = cdiv(M, 64);
-  std::vector<int> a_seen((size_t)(rblocks * kXcds), 0), b_seen((size_t)(tn * kXcds), 0);
+  std::fill(a_seen.begin(), a_seen.end(), 0);
+  std::fill(b_seen.begin(), b_seen.end(), 0);
   int64_t a_count = 0, b_count = 0;
   int bid = 0;
   for (int r = 0; r < q.rects; ++r)
@@ -224,16 +227,24 @@ int64_t tile_set_fetch(const GemmParams& q, int64_t M, int64_t tn) {
   return a_count * q.tile_rows * 128 + b_count * 256 * 128;
 }
 
-// Group heights for the rectangles of a tile-set launch that minimise tile_set_fetch.
-void choose_groups(GemmParams& q, int64_t M, int64_t tn) {
+// Group heights (1..32 row-tiles) for the rectangles of a tile-set launch that minimise
+// tile_set_fetch.  Launches of more than one round keep groups of 4: their rounds do not run
+// concurrently, which the count assumes.
+void choose_groups(GemmParams& q, int64_t M, int64_t tn, int64_t cus) {
+  q.rect_group[0] = q.rect_group[1] = 4;
+  int64_t tiles = 0;
+  for (int r = 0; r < q.rects; ++r) tiles += (int64_t)q.rect_tmc[r] * q.rect_tnc[r];
+  if (tiles > cus) return;
+  std::vector<int> a_seen((size_t)(cdiv(M, 64) * 8)), b_seen((size_t)(tn * 8));
   int best[2] = {4, 4};
   int64_t best_bytes = -1;
-  const int g1max = q.rects > 1 ? q.rect_tmc[1] : 1;
-  for (int g0 = 1; g0 <= q.rect_tmc[0]; ++g0)
+  const int g0max = std::min(q.rect_tmc[0], 32);
+  const int g1max = q.rects > 1 ? std::min(q.rect_tmc[1], 32) : 1;
+  for (int g0 = 1; g0 <= g0max; ++g0)
     for (int g1 = 1; g1 <= g1max; ++g1) {
       q.rect_group[0] = g0;
       q.rect_group[1] = g1;
-      const int64_t bytes = tile_set_fetch(q, M, tn);
+      const int64_t bytes = tile_set_fetch(q, M, tn, a_seen, b_seen);
       if (best_bytes < 0 || bytes < best_bytes) {
         best_bytes = bytes;
         best[0] = g0;
@@ -246,7 +257,7 @@ void choose_groups(GemmParams& q, int64_t M, int64_t tn) {
 
 // The cut's two launches of the four-wave kernel: the 256-row tiles of both strip classes, then
 // the 192-row tiles below them, each with the group heights that keep its L2 fetches lowest.
-// Plans are cached per (M, N, K, mode, CU count): the group search costs about a millisecond.
+// Plans are cached per (M, N, K, mode, CU count): the group search costs up to a few milliseconds.
 struct MixedLaunch {
   int64_t M, N, K, cus;
   int32_t mode;
@@ -255,7 +266,7 @@ struct MixedLaunch {
 std::mutex g_plan_mutex;
 std::vector<MixedLaunch> g_plans;
 
-void build_mixed(const GemmParams& p, const MixedRows& m, int64_t tn, GemmParams q[2]) {
+void build_mixed(const GemmParams& p, const MixedRows& m, int64_t tn, int64_t cus, GemmParams q[2]) {
   for (int pass = 0; pass < 2; ++pass) {
     GemmParams& t = q[pass];
     t = p;
@@ -275,7 +286,7 @@ void build_mixed(const GemmParams& p, const MixedRows& m, int64_t tn, GemmParams
       t.rect_tmc[r] = (int32_t)count;
       t.rect_group[r] = 4;
     }
-    if (t.rects > 0) choose_groups(t, p.M, tn);
+    if (t.rects > 0) choose_groups(t, p.M, tn, cus);
   }
 }
 
@@ -294,7 +305,7 @@ hipError_t launch_mixed(GemmParams& p, const MixedRows& m, int64_t cus, hipStrea
       }
   }
   if (!cached) {
-    build_mixed(p, m, tn, q);
+    build_mixed(p, m, tn, cus, q);
     std::lock_guard<std::mutex> lock(g_plan_mutex);
     if (g_plans.size() < 64) g_plans.push_back({p.M, p.N, p.K, cus, p.mode, {q[0], q[1]}});
   }
