@@ -1,0 +1,129 @@
+// Host-side checks of the GEMM launch planner (gemm_plan.hip): the 256-row / 192-row cut, the tile
+// map of the four-wave kernel, and the L2 fetch count that picks its group heights.  Built with
+// hipcc for the host and run without a GPU: the launchers are stubs that record the launches.
+#include <cstdio>
+#include <cstdlib>
+#include <random>
+#include <vector>
+
+#include "gemm_plan.hip"
+
+namespace ttl {
+int gemm_tile_rows() { return 256; }
+int gemm_tile_cols(int mode) { return mode == 1 ? 128 : 256; }
+bool gemm_bigwave_supports(const GemmParams& p) { return p.K % 64 == 0 && p.K > 0; }
+int gemm_bigwave_tile_cols(int mode, bool narrow) { const int c = narrow ? 128 : 256; return mode == 1 ? c / 2 : c; }
+hipError_t launch_gemm_tiled(const GemmParams&, hipStream_t) { return hipSuccess; }
+hipError_t launch_gemm_skinny(const GemmParams&, int, hipStream_t) { return hipSuccess; }
+hipError_t launch_splitk_finalize(const GemmParams&, hipStream_t) { return hipSuccess; }
+std::vector<GemmParams> g_launched;
+hipError_t launch_gemm_bigwave(const GemmParams& p, hipStream_t) { g_launched.push_back(p); return hipSuccess; }
+}  // namespace ttl
+
+static int failures = 0;
+#define CHECK(cond, ...) do { if (!(cond)) { ++failures; std::printf("FAIL %s:%d: ", __FILE__, __LINE__); \
+  std::printf(__VA_ARGS__); std::printf("\n"); } } while (0)
+
+using ttl::GemmParams;
+
+// Every tile of a tile-set launch, as (first row, strip), through the kernel's own tile map.
+static void tiles_of(const GemmParams& q, std::vector<std::pair<int64_t, int64_t>>& out) {
+  for (int r = 0; r < q.rects; ++r)
+    for (int b = 0; b < q.rect_tmc[r] * q.rect_tnc[r]; ++b) {
+      int tm = -1, tn = -1;
+      ttl::gemm::tile_coords(b, q.rect_tmc[r], q.rect_tnc[r], tm, tn, q.rect_group[r] > 0 ? q.rect_group[r] : 4);
+      out.push_back({q.rect_row0[r] + (int64_t)tm * q.tile_rows, q.rect_tn0[r] + tn});
+    }
+}
+
+// A cut planned for (M, strips, cus) and launched through launch_mixed: the two launches together
+// cover every 64-row block of every strip exactly once, each launch fits its rounds, and no tile
+// starts at or beyond row M.  Returns whether a cut was planned.
+static bool check_cut(int64_t M, int64_t tn, int64_t cus, int mode) {
+  ttl::MixedRows m;
+  if (!ttl::plan_mixed_rows(M, tn, cus, m)) return false;
+  const int64_t tm = ttl::cdiv(M, 256), T = tm * tn, full = T / cus;
+  CHECK(2 * (T % cus) > cus, "M=%lld tn=%lld cus=%lld: cut planned for a short last round", (long long)M, (long long)tn, (long long)cus);
+  GemmParams p = {};
+  p.M = (int32_t)M;
+  p.N = (int32_t)(tn * (mode == 1 ? 128 : 256));
+  p.K = 512;
+  p.mode = mode;
+  ttl::g_launched.clear();
+  CHECK(ttl::launch_mixed(p, m, cus, nullptr) == hipSuccess, "launch_mixed failed");
+  CHECK(ttl::g_launched.size() >= 1 && ttl::g_launched.size() <= 2, "%zu launches", ttl::g_launched.size());
+  const int64_t rb = ttl::cdiv(M, 64);
+  std::vector<int> cover((size_t)(rb * tn), 0);
+  for (size_t l = 0; l < ttl::g_launched.size(); ++l) {
+    const GemmParams& q = ttl::g_launched[l];
+    // a[0] >= 1 always, so the first launch holds the 256-row tiles and a second one the 192-row
+    CHECK(q.tile_rows == (l == 0 ? 256 : 192), "launch %zu: tile_rows %d", l, q.tile_rows);
+    CHECK(q.rects >= 1 && q.rects <= 2 && q.splits == 1 && q.narrow == 0, "launch fields");
+    std::vector<std::pair<int64_t, int64_t>> t;
+    tiles_of(q, t);
+    const int64_t cap = q.tile_rows == 256 ? full * cus : cus;
+    CHECK((int64_t)t.size() <= cap, "M=%lld tn=%lld cus=%lld: %zu tiles of %d rows > %lld",
+          (long long)M, (long long)tn, (long long)cus, t.size(), q.tile_rows, (long long)cap);
+    for (auto& [row, strip] : t) {
+      CHECK(row >= 0 && row < M && strip >= 0 && strip < tn, "tile (%lld, %lld) outside", (long long)row, (long long)strip);
+      if (!(row >= 0 && row < M && strip >= 0 && strip < tn)) continue;
+      for (int64_t r = row; r < row + q.tile_rows && r < M; r += 64) ++cover[(size_t)((r / 64) * tn + strip)];
+    }
+  }
+  for (int64_t i = 0; i < rb * tn; ++i)
+    CHECK(cover[(size_t)i] == 1, "M=%lld tn=%lld cus=%lld: row block %lld of strip %lld covered %d times",
+          (long long)M, (long long)tn, (long long)cus, (long long)(i / tn), (long long)(i % tn), cover[(size_t)i]);
+  return true;
+}
+
+int main() {
+  // The tile map is a bijection for every shape and group height.
+  for (int tmc = 1; tmc <= 20; ++tmc)
+    for (int tnc = 1; tnc <= 37; tnc += 3)
+      for (int g = 1; g <= tmc + 1; ++g) {
+        std::vector<int> seen((size_t)(tmc * tnc), 0);
+        for (int b = 0; b < tmc * tnc; ++b) {
+          int tm = -1, tn = -1;
+          ttl::gemm::tile_coords(b, tmc, tnc, tm, tn, g);
+          if (tm >= 0 && tm < tmc && tn >= 0 && tn < tnc) ++seen[(size_t)(tm * tnc + tn)];
+        }
+        for (int i = 0; i < tmc * tnc; ++i) CHECK(seen[(size_t)i] == 1, "tile map %d x %d group %d", tmc, tnc, g);
+      }
+
+  // The 4096 x 3584 SiLU·up launch (28 strips of 128 act columns) on 256 CUs: strips 0-23 take
+  // 10 x 256 + 8 x 192 rows, strips 24-27 take 4 x 256 + 16 x 192; the chosen group heights fetch
+  // 436 and 419 MB over 128 k-tiles (the counters read 441 and 420 MB).
+  {
+    ttl::MixedRows m;
+    CHECK(ttl::plan_mixed_rows(4096, 28, 256, m), "no cut for 4096 x 28 strips");
+    CHECK(m.S == 24 && m.a[0] == 10 && m.b[0] == 8 && m.a[1] == 4 && m.b[1] == 16,
+          "cut S=%lld a=%lld,%lld b=%lld,%lld", (long long)m.S, (long long)m.a[0], (long long)m.a[1],
+          (long long)m.b[0], (long long)m.b[1]);
+    CHECK(check_cut(4096, 28, 256, 1), "4096 x 28");
+    std::vector<int> a_seen(64 * 8), b_seen(28 * 8);
+    const int64_t f0 = ttl::tile_set_fetch(ttl::g_launched[0], 4096, 28, a_seen, b_seen);
+    const int64_t f1 = ttl::tile_set_fetch(ttl::g_launched[1], 4096, 28, a_seen, b_seen);
+    CHECK(f0 * 128 == 436207616 && f1 * 128 == 419430400, "fetch %lld %lld", (long long)(f0 * 128), (long long)(f1 * 128));
+    CHECK(ttl::g_launched[0].rect_group[0] == 5 && ttl::g_launched[1].rect_group[0] == 8, "groups %d %d",
+          ttl::g_launched[0].rect_group[0], ttl::g_launched[1].rect_group[0]);
+  }
+  // Whole rounds (4096 x 8192: 512 tiles) and short last rounds are not cut.
+  {
+    ttl::MixedRows m;
+    CHECK(!ttl::plan_mixed_rows(4096, 32, 256, m), "cut planned for two whole rounds");
+    CHECK(!ttl::plan_mixed_rows(2176, 32, 256, m), "cut planned for a short last round (288 tiles)");
+    CHECK(!ttl::plan_mixed_rows(2048, 6, 256, m), "cut planned for one partial round");
+  }
+  // Seeded shapes of every size class: each planned cut covers every row once and fits its rounds.
+  std::mt19937 rng(7);
+  int planned = 0;
+  for (int i = 0; i < 3000; ++i) {
+    const int64_t cus = std::vector<int64_t>{8, 10, 16, 32, 80, 256}[rng() % 6];
+    const int64_t M = 1 + rng() % 9000, tn = 1 + rng() % 64;
+    planned += check_cut(M, tn, cus, (int)(rng() % 2)) ? 1 : 0;
+  }
+  CHECK(planned > 100, "only %d of the seeded shapes were cut", planned);
+  std::printf("%d seeded cuts checked\n", planned);
+  if (failures == 0) std::printf("ALL OK\n");
+  return failures == 0 ? 0 : 1;
+}
