@@ -156,7 +156,8 @@ struct MixedRows {
 // A launch of `full` whole rounds of 256-row tiles plus a last round more than half full: find a
 // cut whose 256-row tiles fit in `full` rounds and whose 192-row tiles fit in one.  A 192-row tile
 // holds three quarters of a 256-row tile's work, so the launch takes full + 3/4 rounds instead of
-// full + 1.  Among the cuts that fit, the one with the most 256-row tiles (the more efficient
+// full + 1; a cut exists only where the last round holds at most about three quarters of a round
+// of 256-row tiles (e.g. 448 tiles on 256 CUs), and none is returned otherwise.  Among the cuts that fit, the one with the most 256-row tiles (the more efficient
 // ones).  Strip classes: for a[0] > a[1], the 256-row count full(S) = S*(a0-a1) + tn*a1 grows with
 // S and the 192-row count short(S) = S*(b0-b1) + tn*b1 shrinks, so each pair (a0, a1) admits an
 // interval of S, whose largest member is taken.
