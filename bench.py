@@ -28,6 +28,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import math
 import json
 import os
 import re
@@ -48,6 +49,26 @@ TRAFFIC_SOURCES = ("tensor_transformer_linear_amd/csrc/gemm_bigwave.hip",
                    "tensor_transformer_linear_amd/csrc/gemm_common.h",
                    "tensor_transformer_linear_amd/csrc/gemm_plan.hip",
                    "tensor_transformer_linear_amd/csrc/kernels.h")
+
+
+# The Infinity Cache holds 256 MB: HBM-bound kernels whose operands are smaller are timed over
+# enough copies of them, used in turn, that each launch reads at least this many distinct bytes.
+CACHE_COLD_BYTES = 512e6
+MAX_ROTATION_COPIES = 64
+
+
+def rotation_copies(bytes_per_launch):
+    """Copies of a launch's operands that make successive launches read >= CACHE_COLD_BYTES."""
+    return int(max(1, min(MAX_ROTATION_COPIES, math.ceil(CACHE_COLD_BYTES / max(bytes_per_launch, 1.0)))))
+
+
+def cache_label(copies, bytes_per_launch):
+    total = copies * bytes_per_launch
+    if total >= CACHE_COLD_BYTES:
+        return (f"cold: {copies} operand copies used in turn ({total / 1e6:.0f} MB)" if copies > 1 else
+                f"cold: operands {bytes_per_launch / 1e6:.0f} MB per launch")
+    return (f"warm: {copies} operand copies ({total / 1e6:.1f} MB) fit the 256-MB Infinity Cache; "
+            f"a fixed cost bounds this launch")
 
 
 def gemm_flops(b, k, n):
@@ -80,7 +101,7 @@ def parse():
                     help="weight storage: kn = W[k][n], nk = W^T[n][k], blk = 64 x 128 blocks")
     ap.add_argument("--cpu-rows", type=int, default=32, help="token rows in the CPU oracle sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="repeat the CPU oracle sample until this much time has passed")
+                    help="CPU oracle time per core setting (all cores, then one core): 80 %% GEMMs, 20 %% reduce")
     ap.add_argument("--no-yardstick", action="store_true",
                     help="skip timing torch.matmul (hipBLASLt) on the same GEMM shapes")
     ap.add_argument("--no-power", action="store_true",
@@ -124,27 +145,34 @@ def run_mlp(ttl, torch, w, b, steps, warmup, seed, layout, rotate_ranks=False, g
     sp = ttl.merged_gate_up_split(I, t)
     act = torch.empty((b, Ir), dtype=torch.bfloat16, device=dev)
     P = torch.empty((t, b, H), dtype=torch.bfloat16, device=dev)
-    rout = torch.empty((b, H), dtype=torch.bfloat16, device=dev)
-    y = torch.empty((b, H), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
     # every simulated rank's partial, once
     for r in range(t):
         ttl.shard_linear_col(X, Wgu_s, t, r, sp, ttl.EPI_SILU_MUL, Y=act, stream=stream, w_layout=lay)
         ttl.shard_linear_row(act, Wd_s, t, r, True, P=P[r], stream=stream, w_layout=lay)
     torch.cuda.synchronize()
+    # The reduction's operands (partials, residual, outputs) in enough copies, used in turn, that
+    # successive steps do not find them in the 256-MB Infinity Cache.
+    ncopy = rotation_copies(reduce_bytes(t, b, H))
+    Ps = [P] + [P.clone() for _ in range(ncopy - 1)]
+    Rs = [R] + [R.clone() for _ in range(ncopy - 1)]
+    routs = [torch.empty((b, H), dtype=torch.bfloat16, device=dev) for _ in range(ncopy)]
+    ys = [torch.empty((b, H), dtype=torch.bfloat16, device=dev) for _ in range(ncopy)]
+    rout, y = routs[0], ys[0]
 
     def step(i, ev=None, st=None):
         st = stream if st is None else st
         r = i % t if rotate_ranks else 0
+        c = i % ncopy
         if ev is not None:
             ev[0].record(st)
         ttl.shard_linear_col(X, Wgu_s, t, r, sp, ttl.EPI_SILU_MUL, Y=act, stream=st, w_layout=lay)
         if ev is not None:
             ev[1].record(st)
-        ttl.shard_linear_row(act, Wd_s, t, r, True, P=P[r], stream=st, w_layout=lay)
+        ttl.shard_linear_row(act, Wd_s, t, r, True, P=Ps[c][r], stream=st, w_layout=lay)
         if ev is not None:
             ev[2].record(st)
-        ttl.reduce_partials_rmsnorm(P, gamma, w.eps, R, residual_out=rout, Y=y, stream=st)
+        ttl.reduce_partials_rmsnorm(Ps[c], gamma, w.eps, Rs[c], residual_out=routs[c], Y=ys[c], stream=st)
         if ev is not None:
             ev[3].record(st)
 
@@ -186,6 +214,12 @@ def run_mlp(ttl, torch, w, b, steps, warmup, seed, layout, rotate_ranks=False, g
         d["median_us"] = k_med[j] * 1e3
         d["frac_mfma_peak"] = d.get("tflops", 0.0) / PEAK_BF16_TFLOPS
         d["frac_hbm_peak"] = d["gbs"] / PEAK_HBM_GBS
+    wbytes = 2.0 * H * 2 * I + 2.0 * I * H  # both full weights; each step reads rank r's slices
+    kern["shard_linear_col_silu_mul"]["cache"] = kern["shard_linear_row"]["cache"] = (
+        f"cold: ranks cycled, {t} weight slices ({wbytes / 1e6:.0f} MB) in turn" if rotate_ranks else
+        (f"cold: weights ({wbytes / t / 1e6:.0f} MB) exceed the Infinity Cache" if wbytes / t > CACHE_COLD_BYTES
+         else "warm: one weight slice every step"))
+    kern["reduce_partials_rmsnorm"]["cache"] = cache_label(ncopy, reduce_bytes(t, b, H))
     res = {"ms_per_step": ms_step, "flops": f_col + f_row, "kernels": kern,
            "tensors": (X, Wgu, Wd, R, gamma), "step": step}
     if graph:
@@ -193,9 +227,14 @@ def run_mlp(ttl, torch, w, b, steps, warmup, seed, layout, rotate_ranks=False, g
         # loop would replay them) and replayed: the step time without host launch overhead.  The
         # split-K workspace was allocated by the eager steps above.
         cycle = t if rotate_ranks else 1
+        cycle = cycle * ncopy // math.gcd(cycle, ncopy)  # every rank and every operand copy
         g = torch.cuda.CUDAGraph()
         gs = torch.cuda.Stream()
         gs.wait_stream(stream)
+        with torch.cuda.stream(gs):  # eager once on the capturing stream: its split-K workspace
+            for i in range(cycle):
+                step(i, st=gs)
+        torch.cuda.synchronize()
         with torch.cuda.stream(gs):
             with torch.cuda.graph(g, stream=gs):
                 for i in range(cycle):
@@ -248,30 +287,31 @@ def yardstick(torch, w, layout):
 RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
 
 
-def _time_chain(torch, ops, reps, warmup, cycle):
-    """ops: list of (name, fn(rank), flops, bytes).  Runs the chain `reps` times (rank cycling through
-    0..cycle-1 when cycle > 1, else rank 0) with HIP events recorded between the launches on the
-    launching stream; returns {name: average microseconds}."""
+def _time_chain(torch, ops, reps, warmup):
+    """ops: list of (name, fn(i), flops, bytes, cache).  Runs the chain `reps` times (step i passes
+    i to every op, which picks its simulated rank and operand copy from it) with HIP events recorded
+    between the launches on the launching stream; returns {name: average microseconds}."""
     stream = torch.cuda.current_stream()
     for i in range(warmup):
-        for _, fn, _, _ in ops:
-            fn(i % cycle)
+        for op in ops:
+            op[1](i)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(reps)]
     for i in range(reps):
         evs[i][0].record(stream)
-        for j, (_, fn, _, _) in enumerate(ops):
-            fn(i % cycle)
+        for j, op in enumerate(ops):
+            op[1](i)
             evs[i][j + 1].record(stream)
     torch.cuda.synchronize()
-    return {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / reps * 1e3
-            for j, (name, _, _, _) in enumerate(ops)}
+    return {op[0]: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / reps * 1e3 for j, op in enumerate(ops)}
 
 
 def config_table(ttl, torch, layout, reps=20, warmup=3):
     """Every kernel of one rank's step for each workload, one JSON line each.  Decode-size batches
-    (b < 512) cycle the simulated rank from repetition to repetition so that the weight slices are
-    not served from the Infinity Cache."""
+    (b < 512) cycle the simulated rank from repetition to repetition, so that the weight slices are
+    not served from the Infinity Cache; the reductions rotate their operands (partials, residual,
+    outputs) among enough copies that each launch reads at least 512 MB of distinct bytes (at most
+    64 copies: the smallest decode reductions stay cache-resident, and say so)."""
     from tensor_transformer_linear_amd import workloads as wl
     dev = "cuda"
     names = {ttl.W_KN: "kn", ttl.W_NK: "nk", ttl.W_BLOCKED: "blk"}
@@ -286,33 +326,65 @@ def config_table(ttl, torch, layout, reps=20, warmup=3):
             return ttl.W_KN
         return lay
 
-    def col_op(name, X, W, split, epi, Y, t, n_w, n_out, lay):
-        b, k = X.shape
-        return (name, lambda r: ttl.shard_linear_col(X, W, t, r, split, epi, Y=Y, w_layout=lay),
-                gemm_flops(b, k, n_w), 2.0 * (b * k + k * n_w + b * n_out))
+    def bf(*shape):
+        return torch.empty(shape, dtype=torch.bfloat16, device=dev)
 
-    def row_op(name, X, W, P, t, k, n, parallel, lay):
-        b = X.shape[0]
-        kr = k // t
-        return (name, lambda r: ttl.shard_linear_row(X, W, t, r, parallel, P=P[r], w_layout=lay),
-                gemm_flops(b, kr, n), 2.0 * (b * kr + kr * n + b * n))
+    class Chain:
+        """One rank's chain: the GEMMs cycle the simulated rank when `cycle` > 1; each reduction
+        has its own rotation of partial-sum buffers, shared with the row GEMM that fills it."""
 
-    def red_op(name, P, gamma, eps, R, rout, y):
-        t, b, n = P.shape
-        return (name, lambda r: ttl.reduce_partials_rmsnorm(P, gamma, eps, R, residual_out=rout, Y=y),
-                0.0, reduce_bytes(t, b, n))
+        def __init__(self, t, b, H, cycle):
+            self.t, self.b, self.H, self.cycle = t, b, H, cycle
+            self.ops = []
+
+        def rank(self, i, r=None):
+            return i % self.cycle if r is None else r
+
+        def col(self, name, X_of, W, split, epi, Y, n_w, n_out, lay, wbytes):
+            b, k = self.b, W.shape[0] if lay != ttl.W_NK else W.shape[1]
+            cache = (f"cold: ranks cycled, {self.t} weight slices ({wbytes / 1e6:.0f} MB) in turn" if self.cycle > 1
+                     else "as in the step chain (weight slice re-read every repetition)")
+            self.ops.append((name, lambda i, r=None: ttl.shard_linear_col(X_of(i), W, self.t, self.rank(i, r), split,
+                                                                          epi, Y=Y, w_layout=lay),
+                             gemm_flops(b, k, n_w), 2.0 * (b * k + k * n_w + b * n_out), cache))
+
+        def partials(self):
+            """A rotation of [t, b, H] partial buffers with their residual and outputs."""
+            rb = reduce_bytes(self.t, self.b, self.H)
+            n = rotation_copies(rb)
+            return {"P": [bf(self.t, self.b, self.H) for _ in range(n)], "rout": [bf(self.b, self.H) for _ in range(n)],
+                    "y": [bf(self.b, self.H) for _ in range(n)], "n": n, "bytes": rb}
+
+        def row(self, name, X_of, W, part, k, n, parallel, lay, wbytes):
+            b, kr = self.b, k // self.t
+            cache = (f"cold: ranks cycled, {self.t} weight slices ({wbytes / 1e6:.0f} MB) in turn" if self.cycle > 1
+                     else "as in the step chain (weight slice re-read every repetition)")
+            self.ops.append((name, lambda i, r=None: ttl.shard_linear_row(
+                X_of(i), W, self.t, self.rank(i, r), parallel, P=part["P"][i % part["n"]][self.rank(i, r)],
+                w_layout=lay),
+                             gemm_flops(b, kr, n), 2.0 * (b * kr + kr * n + b * n), cache))
+
+        def red(self, name, part, gamma, eps, R_of):
+            self.ops.append((name, lambda i, r=None: ttl.reduce_partials_rmsnorm(
+                part["P"][i % part["n"]], gamma, eps, R_of(i), residual_out=part["rout"][i % part["n"]],
+                Y=part["y"][i % part["n"]]), 0.0, part["bytes"], cache_label(part["n"], part["bytes"])))
 
     def graph_step_us(ops, cycle, replays=10):
-        """The chain for ranks 0..cycle-1 captured once into a HIP graph and replayed: the step time
+        """The chain for steps 0..cycle-1 captured once into a HIP graph and replayed: the step time
         without host launch overhead (small shapes are otherwise bound by the launch rate)."""
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):  # eager once on the capturing stream: its split-K workspace
+            for i in range(cycle):
+                for op in ops:
+                    op[1](i)
+        torch.cuda.synchronize()
         with torch.cuda.stream(s):
             with torch.cuda.graph(g, stream=s):
-                for r in range(cycle):
-                    for _, fn, _, _ in ops:
-                        fn(r)
+                for i in range(cycle):
+                    for op in ops:
+                        op[1](i)
         torch.cuda.current_stream().wait_stream(s)
         g.replay()
         torch.cuda.synchronize()
@@ -326,15 +398,31 @@ def config_table(ttl, torch, layout, reps=20, warmup=3):
 
     def report(wname, b, t, us, ops, graph_us, lay):
         kern = {}
-        for name, _, fl, by in ops:
+        for name, _, fl, by, cache in ops:
             u = us[name]
             tf, gbs = fl / (u * 1e6), by / (u * 1e3)
             bound = "mfma" if fl / by > RIDGE_FLOP_PER_BYTE else "hbm"
             kern[name] = {"us": u, "tflops": tf, "gbs": gbs, "bound": bound,
-                          "frac": tf / PEAK_BF16_TFLOPS if bound == "mfma" else gbs / PEAK_HBM_GBS}
+                          "frac": tf / PEAK_BF16_TFLOPS if bound == "mfma" else gbs / PEAK_HBM_GBS,
+                          "cache": cache}
         print(json.dumps({"workload": wname, "tokens": b, "t": t, "weight_storage": names[lay],
                           "step_us": sum(us.values()), "step_us_graph": graph_us, "kernels": kern}),
               flush=True)
+
+    def run(wname, b, t, chain, parts, lay, keep):
+        # every rank's partials into every copy of the rotations, in chain order
+        copies = max(p["n"] for p in parts)
+        for c in range(copies):
+            for r in range(t):
+                for op in chain.ops:
+                    op[1](c, r)
+        torch.cuda.synchronize()
+        # a whole number of rank cycles and operand rotations per graph
+        gcycle = chain.cycle
+        for p in parts:
+            gcycle = gcycle * p["n"] // math.gcd(gcycle, p["n"])
+        us = _time_chain(torch, chain.ops, max(reps, gcycle if gcycle <= 64 else reps), warmup)
+        report(wname, b, t, us, chain.ops, graph_step_us(chain.ops, min(gcycle, 64)), lay)
 
     for w in (wl.TINY_MLP_T2, wl.LLAMA3_8B_MLP_TP8, wl.LLAMA3_70B_MLP_TP8):
         for b in w.batches:
@@ -343,19 +431,16 @@ def config_table(ttl, torch, layout, reps=20, warmup=3):
             Ir = I // t
             lay = storage_for(t, ((inp["Wgu"], False), (inp["Wd"], True)))
             Wgu, Wd = stored_weight(ttl, inp["Wgu"], lay), stored_weight(ttl, inp["Wd"], lay)
-            act = torch.empty((b, Ir), dtype=torch.bfloat16, device=dev)
-            P = torch.empty((t, b, H), dtype=torch.bfloat16, device=dev)
-            rout, y = torch.empty((b, H), dtype=torch.bfloat16, device=dev), torch.empty((b, H), dtype=torch.bfloat16, device=dev)
+            act = bf(b, Ir)
             sp = ttl.merged_gate_up_split(I, t)
-            ops = [col_op("gate_up_silu", inp["X"], Wgu, sp, ttl.EPI_SILU_MUL, act, t, 2 * Ir, Ir, lay),
-                   row_op("down", act, Wd, P, t, I, H, True, lay),
-                   red_op("reduce_rmsnorm", P, inp["gamma"], w.eps, inp["R"], rout, y)]
-            for r in range(t):  # every rank's partial once
-                ops[0][1](r)
-                ops[1][1](r)
-            cyc = t if b < 512 else 1
-            report(w.name, b, t, _time_chain(torch, ops, reps, warmup, cyc), ops, graph_step_us(ops, cyc), lay)
-            del inp, Wgu, Wd, act, P, rout, y, ops
+            ch = Chain(t, b, H, t if b < 512 else 1)
+            part = ch.partials()
+            X, R = inp["X"], inp["R"]
+            ch.col("gate_up_silu", lambda i: X, Wgu, sp, ttl.EPI_SILU_MUL, act, 2 * Ir, Ir, lay, 2.0 * H * 2 * I)
+            ch.row("down", lambda i: act, Wd, part, I, H, True, lay, 2.0 * I * H)
+            ch.red("reduce_rmsnorm", part, inp["gamma"], w.eps, lambda i: R)
+            run(w.name, b, t, ch, [part], lay, None)
+            del inp, Wgu, Wd, act, part, ch
             torch.cuda.empty_cache()
 
     for w in (wl.LLAMA3_8B_ATTN_TP4, wl.LLAMA3_70B_LAYER_TP8):
@@ -372,32 +457,32 @@ def config_table(ttl, torch, layout, reps=20, warmup=3):
                 weights += [(inp["Wgu"], False), (inp["Wd"], True)]
             lay = storage_for(t, weights)
             Wqkv, Wo = stored_weight(ttl, inp["Wqkv"], lay), stored_weight(ttl, inp["Wo"], lay)
-            qkv = torch.empty((b, w_r), dtype=torch.bfloat16, device=dev)
-            Pa = torch.empty((t, b, H), dtype=torch.bfloat16, device=dev)
-            rout, y = torch.empty((b, H), dtype=torch.bfloat16, device=dev), torch.empty((b, H), dtype=torch.bfloat16, device=dev)
+            qkv = bf(b, w_r)
             gamma = inp["gamma_attn"] if is_layer else inp["gamma"]
-            ops = [col_op("qkv", inp["X"], Wqkv, sp, ttl.EPI_NONE, qkv, t, w_r, w_r, lay),
-                   row_op("o_proj", inp["A"], Wo, Pa, t, nq * hd, H, False, lay),
-                   red_op("reduce_rmsnorm_attn", Pa, gamma, w.eps, inp["R"], rout, y)]
-            keep = [Wqkv, Wo, qkv, Pa, rout, y]
+            ch = Chain(t, b, H, t if b < 512 else 1)
+            pa = ch.partials()
+            X, A, R = inp["X"], inp["A"], inp["R"]
+            ch.col("qkv", lambda i: X, Wqkv, sp, ttl.EPI_NONE, qkv, w_r, w_r, lay, 2.0 * H * n_qkv)
+            ch.row("o_proj", lambda i: A, Wo, pa, nq * hd, H, False, lay, 2.0 * nq * hd * H)
+            ch.red("reduce_rmsnorm_attn", pa, gamma, w.eps, lambda i: R)
+            parts = [pa]
+            keep = [Wqkv, Wo, qkv]
             if is_layer:
                 I = w.intermediate
                 Ir = I // t
                 Wgu, Wd = stored_weight(ttl, inp["Wgu"], lay), stored_weight(ttl, inp["Wd"], lay)
-                act = torch.empty((b, Ir), dtype=torch.bfloat16, device=dev)
-                Pm = torch.empty((t, b, H), dtype=torch.bfloat16, device=dev)
-                rout2, y2 = torch.empty((b, H), dtype=torch.bfloat16, device=dev), torch.empty((b, H), dtype=torch.bfloat16, device=dev)
+                act = bf(b, Ir)
+                pm = ch.partials()
                 gsp = ttl.merged_gate_up_split(I, t)
-                ops += [col_op("gate_up_silu", y, Wgu, gsp, ttl.EPI_SILU_MUL, act, t, 2 * Ir, Ir, lay),
-                        row_op("down", act, Wd, Pm, t, I, H, True, lay),
-                        red_op("reduce_rmsnorm_mlp", Pm, inp["gamma_mlp"], w.eps, rout, rout2, y2)]
-                keep += [Wgu, Wd, act, Pm, rout2, y2]
-            for r in range(t):  # every rank's partials once, in chain order
-                for _, fn, _, _ in ops:
-                    fn(r)
-            cyc = t if b < 512 else 1
-            report(w.name, b, t, _time_chain(torch, ops, reps, warmup, cyc), ops, graph_step_us(ops, cyc), lay)
-            del inp, ops, keep
+                # the MLP half reads the attention half's outputs of the same step
+                ch.col("gate_up_silu", lambda i: pa["y"][i % pa["n"]], Wgu, gsp, ttl.EPI_SILU_MUL, act,
+                       2 * Ir, Ir, lay, 2.0 * H * 2 * I)
+                ch.row("down", lambda i: act, Wd, pm, I, H, True, lay, 2.0 * I * H)
+                ch.red("reduce_rmsnorm_mlp", pm, inp["gamma_mlp"], w.eps, lambda i: pa["rout"][i % pa["n"]])
+                parts.append(pm)
+                keep += [Wgu, Wd, act]
+            run(w.name, b, t, ch, parts, lay, keep)
+            del inp, ch, keep, parts, pa
             torch.cuda.empty_cache()
 
 
@@ -509,12 +594,28 @@ def recorded_traffic(kernel, workload):
     return None
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(torch, w, tensors, rows, seconds):
-    """The oracle as it stands, on rank 0's work for `rows` token rows (rows are independent),
-    repeated until `seconds` have passed."""
+    """The oracle as it stands, on rank 0's work for `rows` token rows (rows are independent), timed
+    on the host's cores twice: with every core this process may run on (os.sched_getaffinity) as
+    numpy's BLAS threads, and with one.  Each run times the two GEMM steps (gate_up + SiLU·up, then
+    the down partial) and the reduction (8 partials + residual + RMSNorm) separately, each repeated
+    until its share of `seconds` has passed."""
     import numpy as np
     import oracle
     from tensor_transformer_linear_amd import workloads as wl
+    from threadpoolctl import threadpool_info, threadpool_limits
     X, Wgu, Wd, R, gamma = tensors
     t, H, I = w.t, w.hidden, w.intermediate
     Ir = I // t
@@ -524,29 +625,50 @@ def cpu_baseline(torch, w, tensors, rows, seconds):
     gs = oracle.bf16_bits_to_f64(wl.bf16_bits(gamma.cpu()))
     Wgu64 = oracle.bf16_bits_to_f64(wl.bf16_bits(Wgu.cpu()))
     Wd64 = oracle.bf16_bits_to_f64(wl.bf16_bits(Wd.cpu()))
-    other = np.zeros((t - 1, rows, H))  # the other ranks' partials: same shape, values irrelevant to time
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
     split = oracle.merged_gate_up_split(I, t)
-    passes = 0
-    t0 = time.perf_counter()
-    while True:
+    rng = np.random.default_rng(0)
+    others = oracle.round_bf16(rng.standard_normal((t - 1, rows, H)))  # the other ranks' partials
+
+    def gemms():
         act = oracle.round_bf16(oracle.silu_mul(oracle.col_shard(Xs, Wgu64, split, t, 0)))
-        p0 = oracle.round_bf16(oracle.row_shard(act, Wd64, t, 0, x_is_parallel=True))
-        h, y = oracle.reduce_partials_rmsnorm(np.concatenate([p0[None], other]), Rs, gs, w.eps)
-        passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= seconds:
-            break
-    flops = passes * (gemm_flops(rows, H, 2 * Ir) + gemm_flops(rows, Ir, H))
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "seconds": dt,
-            "sample": f"{passes} passes of rank 0 of t={t} (gate_up+SiLU*up, down partial, reduce of 8 "
-                      f"partials + residual + RMSNorm) over {rows} of the {tensors[0].shape[0]} token rows; "
-                      f"float64 numpy oracle; rows are independent, so the rate applies to the full batch"}
+        return oracle.round_bf16(oracle.row_shard(act, Wd64, t, 0, x_is_parallel=True))
+
+    p0 = gemms()
+    P = np.concatenate([p0[None], others])
+
+    def timed(fn, budget):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            n += 1
+            dt = time.perf_counter() - t0
+            if dt >= budget:
+                return n, dt
+
+    gemm_flops_pass = gemm_flops(rows, H, 2 * Ir) + gemm_flops(rows, Ir, H)
+    red_bytes_pass = reduce_bytes(t, rows, H)
+    affinity = len(os.sched_getaffinity(0))
+    runs = {}
+    for label, limit in (("all_cores", affinity), ("one_core", 1)):
+        with threadpool_limits(limits=limit):
+            threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+            ng, tg = timed(gemms, 0.4 * seconds)
+            nr, tr = timed(lambda: oracle.reduce_partials_rmsnorm(P, Rs, gs, w.eps), 0.1 * seconds)
+        runs[label] = {"threads": int(threads), "gemm_tflops": ng * gemm_flops_pass / tg / 1e12,
+                       "gemm_passes": ng, "gemm_seconds": tg,
+                       "reduce_gbs": nr * red_bytes_pass / tr / 1e9, "reduce_passes": nr, "reduce_seconds": tr,
+                       "step_tflops": gemm_flops_pass / (tg / ng + tr / nr) / 1e12}
+    allc = runs["all_cores"]
+    return {"value": allc["step_tflops"], "unit": "TFLOP/s", "cores": allc["threads"], "kind": "oracle",
+            "cpu_model": cpu_model(), "affinity_cores": affinity,
+            "gemm_tflops": allc["gemm_tflops"], "reduce_gbs": allc["reduce_gbs"],
+            "one_core": runs["one_core"], "all_cores": allc,
+            "seconds": sum(r["gemm_seconds"] + r["reduce_seconds"] for r in runs.values()),
+            "sample": f"rank 0 of t={t} over {rows} of the {tensors[0].shape[0]} token rows: gate_up+SiLU*up and "
+                      f"the down partial (GEMM TFLOP/s), the reduction of {t} partials + residual + RMSNorm "
+                      f"(GB/s of its algorithmic bytes); value = the step's GEMM flops over the step's time "
+                      f"(both parts) with all cores; float64 numpy oracle; rows are independent, so the rates "
+                      f"apply to the full batch"}
 
 
 def main():

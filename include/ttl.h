@@ -28,12 +28,13 @@
  *     enqueue kernels on `stream` (a hipStream_t; NULL = the default stream) and return.  Buffers
  *     must stay alive until the stream has run the work.
  *   - Workspace: GEMMs with few token rows (decode batches, small shards) are cut along k and need
- *     fp32 partial sums.  The library keeps one device buffer per GPU for them, allocated on the
- *     first such call and replaced by a larger one when a later call needs more (the outgrown
- *     buffer is kept, so work already enqueued or captured in a graph stays valid); buffers live
- *     until the process ends.  The allocation cannot run inside a stream capture: make one eager
- *     call of the shape before capturing it.  Calls whose work overlaps in time on one GPU
- *     (different streams) share the buffer and race: serialise them on one stream.  A failed
+ *     fp32 partial sums.  The library keeps one device buffer per (GPU, stream) for them, allocated
+ *     on the first such call on that stream and replaced by a larger one when a later call needs
+ *     more (the outgrown buffer is kept, so work already enqueued or captured in a graph stays
+ *     valid); buffers live until the process ends.  Calls on different streams therefore never
+ *     share a buffer and may overlap in time.  The allocation cannot run inside a stream capture:
+ *     make one eager call of the shape on the capturing stream before capturing it (a capture that
+ *     would need a new or larger buffer fails with TTL_ERR_HIP and enqueues nothing).  A failed
  *     allocation is TTL_ERR_HIP.
  *   - Errors: every call returns a ttl_status.  Arguments are validated synchronously before any
  *     launch; on a non-OK status nothing has been enqueued and ttl_last_error() returns a message
@@ -108,7 +109,8 @@ typedef struct {
  * (vLLM walkthrough, section "ColumnParallelLinear": the rank keeps its own n/t columns).
  *
  *   X      [b, k]  bf16, the full (replicated) input.
- *   W      the full weight W[k, n] stored as `w_layout` says; only the rank's columns are read.
+ *   W      the full weight W[k, n], row-major [k][n] (row stride n), the statement's own storage;
+ *          only the rank's columns are read.
  *   split  column split (see ttl_col_split); NULL means one segment cut into t slices.
  *   epi    TTL_EPI_NONE: Y[b, n_r] = X · W[:, C_r], n_r = Σ_i seg_n[i] / seg_parts[i].
  *          TTL_EPI_SILU_MUL: the split must have two equal segments (gate | up) with equal part
@@ -116,20 +118,35 @@ typedef struct {
  *          computed in fp32 from the fp32 accumulators — the activation "on the local shard" of
  *          section 14 of "vLLM Code Reading (Section 5)" (jeremyguo.space).  gate and up never
  *          reach memory.
- *   Y      output, row stride n_r (or n_r/2), caller-allocated.
+ *   Y      output, row stride n_r (or n_r/2), caller-allocated; must not overlap X or W.
  * Errors: NULL X/W/Y -> NULL; b,k,n <= 0 -> SHAPE; bad t/rank -> RANK; a segment width not
  * divisible by its part count, part count neither t nor a divisor of t, or widths not summing to n
- * -> NOT_DIVISIBLE; misalignment, or TTL_W_BLOCKED with k % 64 != 0 or n % 128 != 0 -> ALIGN;
- * SILU_MUL with an unsuitable split, nseg outside 1..3, an unknown w_layout, or TTL_W_NK rows
- * (TTL_W_BLOCKED strips) read spanning 2 GiB or more -> UNSUPPORTED.
+ * -> NOT_DIVISIBLE; misalignment -> ALIGN; SILU_MUL with an unsuitable split, nseg outside 1..3,
+ * or Y overlapping X or W -> UNSUPPORTED.
  */
 ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k,
-                            const uint16_t* W, int64_t n, ttl_weight_layout w_layout,
+                            const uint16_t* W, int64_t n,
                             int32_t t, int32_t rank,
                             const ttl_col_split* split,
                             ttl_epilogue epi,
                             uint16_t* Y,
                             void* stream);
+
+/*
+ * shard_linear_col_stored — shard_linear_col with the weight in any of the storages above
+ * (`w_layout`); the logical operand is still W[k, n] and the results are bit for bit those of
+ * shard_linear_col on the same logical weight.  TTL_W_KN is exactly shard_linear_col.
+ * Errors: as shard_linear_col; TTL_W_BLOCKED with k % 64 != 0 or n % 128 != 0 -> ALIGN; an
+ * unknown w_layout, or TTL_W_NK rows (TTL_W_BLOCKED strips) read spanning 2 GiB or more ->
+ * UNSUPPORTED.
+ */
+ttl_status shard_linear_col_stored(const uint16_t* X, int64_t b, int64_t k,
+                                   const uint16_t* W, int64_t n, ttl_weight_layout w_layout,
+                                   int32_t t, int32_t rank,
+                                   const ttl_col_split* split,
+                                   ttl_epilogue epi,
+                                   uint16_t* Y,
+                                   void* stream);
 
 /*
  * shard_linear_col_gathered — ColumnParallelLinear forward with gather_output=True (vLLM
@@ -140,9 +157,10 @@ ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k,
  * vocab-parallel LM head (the "Tensor Parallelism" manual, section "Vocab Parallel": each rank owns
  * a contiguous vocabulary slice, and the logits are all-gathered).
  *
+ *   W      stored as `w_layout` says (as shard_linear_col_stored).
  *   Y_all  [b, t·w] bf16, w = the rank output width of shard_linear_col (n_r, or n_r/2 with
  *          SILU_MUL); this call writes columns [rank·w, (rank+1)·w) and nothing else.
- * Every other argument, and every error, as shard_linear_col.
+ * Every other argument, and every error, as shard_linear_col_stored.
  */
 ttl_status shard_linear_col_gathered(const uint16_t* X, int64_t b, int64_t k,
                                      const uint16_t* W, int64_t n, ttl_weight_layout w_layout,
@@ -161,18 +179,31 @@ ttl_status shard_linear_col_gathered(const uint16_t* X, int64_t b, int64_t k,
  *          act of shard_linear_col);  x_is_parallel == 0: the full input [b, k], whose columns
  *          [r·k/t, (r+1)·k/t) are used (split along the last dimension).
  *   k      the FULL input dimension of W.
- *   W      the full weight W[k, n] stored as `w_layout` says; W's rows [r·k/t, (r+1)·k/t) are read.
+ *   W      the full weight W[k, n], row-major [k][n]; W's rows [r·k/t, (r+1)·k/t) are read.
  *   P      [b, n] bf16 partial for this rank (for simulated ranks, the caller passes P + r·b·n of
- *          a [t, b, n] buffer).
- * Errors: as above; k not divisible by t -> NOT_DIVISIBLE; TTL_W_BLOCKED with (k/t) % 64 != 0 ->
- * ALIGN.
+ *          a [t, b, n] buffer); must not overlap X or W.
+ * Errors: as shard_linear_col; k not divisible by t -> NOT_DIVISIBLE; P overlapping X or W ->
+ * UNSUPPORTED.
  */
 ttl_status shard_linear_row(const uint16_t* X, int64_t b, int64_t k,
                             int32_t x_is_parallel,
-                            const uint16_t* W, int64_t n, ttl_weight_layout w_layout,
+                            const uint16_t* W, int64_t n,
                             int32_t t, int32_t rank,
                             uint16_t* P,
                             void* stream);
+
+/*
+ * shard_linear_row_stored — shard_linear_row with the weight in any of the storages above
+ * (`w_layout`); bit for bit the results of shard_linear_row on the same logical weight.
+ * Errors: as shard_linear_row; TTL_W_BLOCKED with k % 64, (k/t) % 64 or n % 128 != 0 -> ALIGN; an
+ * unknown w_layout, or a TTL_W_NK / TTL_W_BLOCKED weight of 2 GiB or more -> UNSUPPORTED.
+ */
+ttl_status shard_linear_row_stored(const uint16_t* X, int64_t b, int64_t k,
+                                   int32_t x_is_parallel,
+                                   const uint16_t* W, int64_t n, ttl_weight_layout w_layout,
+                                   int32_t t, int32_t rank,
+                                   uint16_t* P,
+                                   void* stream);
 
 /*
  * reduce_partials_rmsnorm — the row-parallel reduction of t rank partials held in one HBM,
@@ -255,7 +286,6 @@ ttl_status reduce_partials_rmsnorm_peers(const uint16_t* const* P_ranks, int32_t
                                          uint16_t* Y,
                                          void* stream);
 
-/* Message for the last non-OK status returned on this thread ("" if none). */
 /*
  * ttl_pack_weight_blocked — W_blk = W stored as TTL_W_BLOCKED (see above), from W[k][n] row-major.
  * Set-up work for a weight that is used many times; not on the hot path.
@@ -266,7 +296,33 @@ ttl_status reduce_partials_rmsnorm_peers(const uint16_t* const* P_ranks, int32_t
  */
 ttl_status ttl_pack_weight_blocked(const uint16_t* W, int64_t k, int64_t n, uint16_t* W_blk, void* stream);
 
+/* Message for the last non-OK status returned on this thread ("" if none). */
 const char* ttl_last_error(void);
+
+/*
+ * ttl_set_gemm_override — for tests and measurements only: force the GEMM kernel family that every
+ * later shard_linear_* call in the process uses, whatever the shape, instead of the library's
+ * choice by shape.  Every kernel family computes the same products in the same k order within a
+ * tile, so results differ only by the summation order of k-splits (bit-equal where the split
+ * count is equal).  Process-wide; not for concurrent use with GEMM calls on other threads.
+ *
+ *   kernel    TTL_GEMM_AUTO restores the choice by shape; the others name a family (below).
+ *   splits    > 0: the k-split count of the split-K kernel and of tiles cut along k; 0 = by shape.
+ *   plan_cus  > 0: compute units the 256-row / 192-row cut (TTL_GEMM_MIXED) is planned for; 0 = the
+ *             device's.
+ *   trace     != 0: print each 256-row / 192-row cut to stderr.
+ * Errors: an unknown kernel, or a negative splits/plan_cus -> UNSUPPORTED.
+ */
+#define TTL_GEMM_AUTO 0
+#define TTL_GEMM_TILED 1        /* 256 x 256 tiles: the four-wave kernel where K % 64 == 0 */
+#define TTL_GEMM_SPLITK 2       /* the split-K kernel (32..128-row tiles, k cut into splits) */
+#define TTL_GEMM_EIGHTWAVE 3    /* 256 x 256 tiles by the eight-wave kernel (any K) */
+#define TTL_GEMM_TILESPLIT 4    /* 256 x 256 tiles cut along k */
+#define TTL_GEMM_NARROW 5       /* 256 x 128 tiles */
+#define TTL_GEMM_NARROWSPLIT 6  /* 256 x 128 tiles cut along k */
+#define TTL_GEMM_SHORT 7        /* 192 x 256 tiles */
+#define TTL_GEMM_MIXED 8        /* the 256-row / 192-row cut wherever one exists */
+ttl_status ttl_set_gemm_override(int32_t kernel, int32_t splits, int32_t plan_cus, int32_t trace);
 
 /* Library version: major * 10000 + minor * 100 + patch. */
 int32_t ttl_version(void);

@@ -12,33 +12,22 @@
 // 192-row tiles that fill one more round, which then takes three quarters of a round's time.
 //
 // Workspace: split-K launches with more than one split write fp32 partial tiles that a second
-// kernel reduces.  The library keeps one device buffer per GPU for them, allocated (or grown) on
-// first need by the calling thread; allocation cannot happen inside a stream capture, so a graph
-// that captures such launches must be recorded after one eager call of the same (or a larger)
-// shape.  Launches that overlap in time on one GPU (different streams) would share the buffer and
-// must not be issued.
+// kernel reduces.  The library keeps one device buffer per (GPU, stream) for them, allocated (or
+// grown) on first need by the calling thread, so launches on different streams never share one.
+// Allocation cannot happen inside a stream capture: a graph that captures such launches must be
+// recorded after one eager call of the same (or a larger) shape on the capturing stream.
 //
-// Environment overrides, read at every launch (for tests and measurements):
-//   TTL_GEMM_KERNEL=tiled|splitk  use that kernel family whatever the shape;
-//   TTL_GEMM_KERNEL=eightwave     the 256 x 256 tiles, by the eight-wave kernel even where K is a
-//                                 multiple of 64 (where the four-wave kernel runs by default);
-//   TTL_GEMM_KERNEL=tilesplit     256 x 256 tiles cut along k (four-wave kernel; K a multiple of 64,
-//                                 else the split-K kernel), TTL_GEMM_SPLITS or at least 2 splits;
-//   TTL_GEMM_KERNEL=narrow        256 x 128 tiles of the four-wave kernel (K a multiple of 64, else
-//                                 the eight-wave kernel's 256 x 256 tiles);
-//   TTL_GEMM_KERNEL=narrowsplit   256 x 128 tiles cut along k, as tilesplit;
-//   TTL_GEMM_KERNEL=short         192 x 256 tiles of the four-wave kernel over the whole GEMM (K a
-//                                 multiple of 64, else as by shape);
-//   TTL_GEMM_KERNEL=mixed         the 256-row / 192-row cut wherever one beats whole tiles, planned
-//                                 for TTL_GEMM_PLAN_CUS compute units (default: the device's);
-//   TTL_GEMM_SPLITS=<n>           split-K kernel: use n splits (at most one per k-tile);
-//   TTL_GEMM_TRACE=1              print each 256-row / 192-row cut to stderr.
+// Overrides for tests and measurements (ttl_set_gemm_override): a forced kernel family, a forced
+// split count, the CU count the 256-row / 192-row cut is planned for, and a trace of each cut.
+// They are process-wide atomics read once per launch; nothing here reads the environment.
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <algorithm>
 #include <atomic>
+#include <map>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "gemm_common.h"
@@ -56,19 +45,22 @@ struct Workspace {
   size_t bytes = 0;
 };
 std::mutex g_ws_mutex;
-std::vector<Workspace> g_ws;
+std::map<std::pair<int, uintptr_t>, Workspace> g_ws;  // (device, stream) -> buffer
 
-// Device buffer of at least `bytes` for this GPU.  A buffer that is outgrown is retired, not freed:
-// work already enqueued, or captured into a graph, keeps using it safely.  Growth at least doubles
-// the size, so few buffers are ever retired; all of them live until the process ends.
-hipError_t get_workspace(size_t bytes, void** out) {
+// Device buffer of at least `bytes` for this GPU and `stream`.  A buffer that is outgrown is
+// retired, not freed: work already enqueued, or captured into a graph, keeps using it safely.
+// Growth at least doubles the size, so few buffers are ever retired; all of them live until the
+// process ends.  A stream that is being captured cannot allocate: such a launch fails instead.
+hipError_t get_workspace(size_t bytes, hipStream_t stream, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> lock(g_ws_mutex);
-  if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
-  Workspace& w = g_ws[dev];
+  Workspace& w = g_ws[{dev, reinterpret_cast<uintptr_t>(stream)}];
   if (w.bytes < bytes) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if ((e = hipStreamIsCapturing(stream, &cs)) != hipSuccess) return e;
+    if (cs != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
     const size_t mib = (size_t)1 << 20;
     size_t nb = (bytes + mib - 1) / mib * mib;
     if (nb < 2 * w.bytes) nb = 2 * w.bytes;
@@ -80,6 +72,9 @@ hipError_t get_workspace(size_t bytes, void** out) {
   *out = w.ptr;
   return hipSuccess;
 }
+
+// Test and measurement overrides (see ttl_set_gemm_override).
+std::atomic<int> g_force_kernel{0}, g_force_splits{0}, g_force_plan_cus{0}, g_trace{0};
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -100,32 +95,11 @@ int64_t device_cus() {
   return n;
 }
 
-// 0: by shape, 1: 256 x 256 tiles, 2: split-K, 3: 256 x 256 tiles by the eight-wave kernel,
-// 4: 256 x 256 tiles cut along k, 5: 256 x 128 tiles, 6: 256 x 128 tiles cut along k,
-// 7: 192 x 256 tiles, 8: the 256-row / 192-row cut planned for TTL_GEMM_PLAN_CUS CUs.
-int forced_kernel() {
-  const char* s = std::getenv("TTL_GEMM_KERNEL");
-  if (s == nullptr) return 0;
-  if (std::strcmp(s, "tiled") == 0) return 1;
-  if (std::strcmp(s, "splitk") == 0) return 2;
-  if (std::strcmp(s, "eightwave") == 0) return 3;
-  if (std::strcmp(s, "tilesplit") == 0) return 4;
-  if (std::strcmp(s, "narrow") == 0) return 5;
-  if (std::strcmp(s, "narrowsplit") == 0) return 6;
-  if (std::strcmp(s, "short") == 0) return 7;
-  if (std::strcmp(s, "mixed") == 0) return 8;
-  return 0;
-}
-
-int64_t env_int(const char* name, int64_t dflt) {
-  const char* s = std::getenv(name);
-  return s == nullptr ? dflt : std::atoll(s);
-}
-
-int64_t forced_splits() {
-  const char* s = std::getenv("TTL_GEMM_SPLITS");
-  return s == nullptr ? 0 : std::atoll(s);
-}
+// The forced kernel family: 0 by shape, 1 256 x 256 tiles, 2 split-K, 3 256 x 256 tiles by the
+// eight-wave kernel, 4 256 x 256 tiles cut along k, 5 256 x 128 tiles, 6 256 x 128 tiles cut along
+// k, 7 192 x 256 tiles, 8 the 256-row / 192-row cut planned for the override's CU count.
+int forced_kernel() { return g_force_kernel.load(std::memory_order_relaxed); }
+int64_t forced_splits() { return g_force_splits.load(std::memory_order_relaxed); }
 
 // 256 x 256 tiles over all of p: the four-wave kernel where it applies, unless force == 3.
 hipError_t launch_tiles(GemmParams& p, int force, hipStream_t stream) {
@@ -258,12 +232,14 @@ void choose_groups(GemmParams& q, int64_t M, int64_t tn, int64_t cus) {
 
 // The cut's two launches of the four-wave kernel: the 256-row tiles of both strip classes, then
 // the 192-row tiles below them, each with the group heights that keep its L2 fetches lowest.
-// Plans are cached per (M, N, K, mode, CU count): the group search costs up to a few milliseconds.
+// Plans are cached per (M, N, K, mode, CU count), most recently used first, up to kPlanCache of
+// them: the group search costs up to a few milliseconds.
 struct MixedLaunch {
   int64_t M, N, K, cus;
   int32_t mode;
   GemmParams q[2];  // tiling fields only
 };
+constexpr size_t kPlanCache = 64;
 std::mutex g_plan_mutex;
 std::vector<MixedLaunch> g_plans;
 
@@ -297,20 +273,25 @@ hipError_t launch_mixed(GemmParams& p, const MixedRows& m, int64_t cus, hipStrea
   bool cached = false;
   {
     std::lock_guard<std::mutex> lock(g_plan_mutex);
-    for (const MixedLaunch& c : g_plans)
+    for (size_t i = 0; i < g_plans.size(); ++i) {
+      const MixedLaunch& c = g_plans[i];
       if (c.M == p.M && c.N == p.N && c.K == p.K && c.mode == p.mode && c.cus == cus) {
         q[0] = c.q[0];
         q[1] = c.q[1];
         cached = true;
+        std::rotate(g_plans.begin(), g_plans.begin() + i, g_plans.begin() + i + 1);  // most recent first
         break;
       }
+    }
   }
   if (!cached) {
     build_mixed(p, m, tn, cus, q);
     std::lock_guard<std::mutex> lock(g_plan_mutex);
-    if (g_plans.size() < 64) g_plans.push_back({p.M, p.N, p.K, cus, p.mode, {q[0], q[1]}});
+    // Least recently used plans make room once the cache is full.
+    if (g_plans.size() >= kPlanCache) g_plans.pop_back();
+    g_plans.insert(g_plans.begin(), {p.M, p.N, p.K, cus, p.mode, {q[0], q[1]}});
   }
-  if (env_int("TTL_GEMM_TRACE", 0) > 0)
+  if (g_trace.load(std::memory_order_relaxed))
     std::fprintf(stderr, "ttl gemm cut: M=%d N=%d K=%d strips [0,%lld) %lld x 256 + %lld x 192, "
                  "[%lld,%lld) %lld x 256 + %lld x 192, groups %d/%d and %d/%d\n", p.M, p.N, p.K,
                  (long long)m.S, (long long)m.a[0], (long long)m.b[0], (long long)m.S, (long long)tn,
@@ -369,7 +350,7 @@ hipError_t launch_tiles_splitk(GemmParams& p, int64_t splits, bool narrow, hipSt
   q.kt_per_split = (int32_t)kt_per;
   q.ws_ld = (int64_t)q.tiles_n * gemm_bigwave_tile_cols(0, narrow);
   void* base = nullptr;
-  hipError_t e = get_workspace((size_t)splits * q.M * q.ws_ld * sizeof(float), &base);
+  hipError_t e = get_workspace((size_t)splits * q.M * q.ws_ld * sizeof(float), stream, &base);
   if (e != hipSuccess) return e;
   q.ws = static_cast<float*>(base);
   if ((e = launch_gemm_bigwave(q, stream)) != hipSuccess) return e;
@@ -402,7 +383,7 @@ hipError_t launch_splitk(GemmParams& p, hipStream_t stream) {
   p.ws = nullptr;
   if (splits > 1) {
     void* base = nullptr;
-    const hipError_t e = get_workspace((size_t)splits * p.M * p.ws_ld * sizeof(float), &base);
+    const hipError_t e = get_workspace((size_t)splits * p.M * p.ws_ld * sizeof(float), stream, &base);
     if (e != hipSuccess) return e;
     p.ws = static_cast<float*>(base);
   }
@@ -410,6 +391,13 @@ hipError_t launch_splitk(GemmParams& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+void set_gemm_override(int kernel, int splits, int plan_cus, bool trace) {
+  g_force_kernel.store(kernel, std::memory_order_relaxed);
+  g_force_splits.store(splits, std::memory_order_relaxed);
+  g_force_plan_cus.store(plan_cus, std::memory_order_relaxed);
+  g_trace.store(trace ? 1 : 0, std::memory_order_relaxed);
+}
 
 hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
   const int force = forced_kernel();
@@ -419,7 +407,8 @@ hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
   if (force == 7 && gemm_bigwave_supports(p)) return launch_short(p, stream);
   if (force == 8 && gemm_bigwave_supports(p)) {
     MixedRows m;
-    const int64_t cus = env_int("TTL_GEMM_PLAN_CUS", device_cus());
+    const int64_t pc = g_force_plan_cus.load(std::memory_order_relaxed);
+    const int64_t cus = pc > 0 ? pc : device_cus();
     if (plan_mixed_rows(p.M, cdiv(p.N, gemm_tile_cols(p.mode)), cus, m)) return launch_mixed(p, m, cus, stream);
     return launch_tiles(p, 0, stream);
   }

@@ -65,8 +65,13 @@ inline GemmParams silu_as_plain_halves(const GemmParams& p) {
 
 // Picks the kernel for the shape and launches it: the 256 x 256-tile kernel when its tiles fill the
 // chip, otherwise the split-K kernel (short M: decode batches, small shards).  Sets the tiling
-// fields of p.  May allocate the library's split-K workspace on first use.
+// fields of p.  May allocate the split-K workspace of (device, stream) on first use.
 hipError_t launch_gemm(GemmParams& p, hipStream_t stream);
+
+// Process-wide test and measurement overrides of launch_gemm's choice (ttl_set_gemm_override):
+// kernel family (0 = by shape), split count (0 = by shape), CUs the row cut is planned for (0 =
+// the device's), and a trace of each cut on stderr.
+void set_gemm_override(int kernel, int splits, int plan_cus, bool trace);
 
 // 256 x 256 tiles (tiles_m, tiles_n set by the caller from the two functions below), by either of
 // two kernels with identical results: eight waves (two per SIMD, any K), or four waves of 128 x 128

@@ -31,6 +31,12 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
   return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
 }
 
+// A GEMM output of out_elems bf16 elements overlapping its input (x_elems) or weight (w_elems).
+bool output_overlaps(const uint16_t* out, int64_t out_elems, const uint16_t* x, int64_t x_elems,
+                     const uint16_t* w, int64_t w_elems) {
+  return overlaps(out, out_elems * 2, x, x_elems * 2) || overlaps(out, out_elems * 2, w, w_elems * 2);
+}
+
 constexpr int64_t kMaxDim = 0x7FFFFFFF;
 // Per-tile buffer offsets are 32-bit: 256 input rows and 65 weight rows of pitch must stay < 2^31 B.
 constexpr int64_t kMaxLda = (int64_t)1 << 21;
@@ -186,6 +192,88 @@ ttl_status col_setup(const char* who, const uint16_t* X, int64_t b, int64_t k, c
 }
 
 
+// Validation, shard addressing and launch of the column-parallel GEMM (both column entry points).
+ttl_status col_entry(const char* who, const uint16_t* X, int64_t b, int64_t k, const uint16_t* W,
+                     int64_t n, ttl_weight_layout w_layout, int32_t t, int32_t rank,
+                     const ttl_col_split* split, ttl_epilogue epi, uint16_t* Y, void* stream) {
+  ttl::GemmParams p;
+  int64_t width = 0;
+  const ttl_status st = col_setup(who, X, b, k, W, n, w_layout, t, rank, split, epi, Y, p, width);
+  if (st != TTL_OK) return st;
+  if (output_overlaps(Y, b * width, X, b * k, W, k * n))
+    return fail(TTL_ERR_UNSUPPORTED, "%s: Y must not overlap X or W", who);
+  p.C = Y;
+  p.ldc = width;
+  return launch_status(ttl::launch_gemm(p, static_cast<hipStream_t>(stream)), who);
+}
+
+// Validation, shard addressing and launch of the row-parallel GEMM (both row entry points).
+ttl_status row_entry(const char* who, const uint16_t* X, int64_t b, int64_t k, int32_t x_is_parallel,
+                     const uint16_t* W, int64_t n, ttl_weight_layout w_layout, int32_t t, int32_t rank,
+                     uint16_t* P, void* stream) {
+  if (b <= 0 || k <= 0 || n <= 0 || b > kMaxDim || k > kMaxDim || n > kMaxDim)
+    return fail(TTL_ERR_SHAPE, "%s: b=%lld k=%lld n=%lld must be in [1, 2^31)", who, (long long)b,
+                (long long)k, (long long)n);
+  if (X == nullptr || W == nullptr || P == nullptr)
+    return fail(TTL_ERR_NULL, "%s: X, W and P must be non-NULL", who);
+  if (t < 1 || rank < 0 || rank >= t)
+    return fail(TTL_ERR_RANK, "%s: need t >= 1 and 0 <= rank < t (t=%d rank=%d)", who, t, rank);
+  if (w_layout != TTL_W_KN && w_layout != TTL_W_NK && w_layout != TTL_W_BLOCKED)
+    return fail(TTL_ERR_UNSUPPORTED, "%s: unknown weight layout %d", who, w_layout);
+  if (k % t != 0)
+    return fail(TTL_ERR_NOT_DIVISIBLE, "%s: k=%lld is not divisible by t=%d", who, (long long)k, t);
+  const int64_t kr = k / t;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(P))
+    return fail(TTL_ERR_ALIGN, "%s: X, W and P must be 16-byte aligned", who);
+  if (kr % 8 != 0 || n % 8 != 0 || k % 8 != 0)
+    return fail(TTL_ERR_ALIGN, "%s: k/t=%lld and n=%lld must be multiples of 8", who,
+                (long long)kr, (long long)n);
+  const int64_t lda = x_is_parallel ? kr : k;
+  if (lda > kMaxLda || n > kMaxLdb || k > kMaxLdb)
+    return fail(TTL_ERR_SHAPE, "%s: row pitch of X or W exceeds the supported range", who);
+  if (w_layout == TTL_W_NK && n * k * 2 >= kMaxNkBytes)
+    return fail(TTL_ERR_UNSUPPORTED, "%s: a [n][k] weight must stay below 2 GiB", who);
+  if (w_layout == TTL_W_BLOCKED) {
+    if (k % 64 != 0 || kr % 64 != 0 || n % 128 != 0)
+      return fail(TTL_ERR_ALIGN, "%s: a blocked weight needs k %% 64, (k/t) %% 64 and n %% 128 == 0", who);
+    if (n * k * 2 >= kMaxNkBytes)
+      return fail(TTL_ERR_UNSUPPORTED, "%s: a blocked weight must stay below 2 GiB", who);
+  }
+
+  ttl::GemmParams p = {};
+  p.A = x_is_parallel ? X : X + (int64_t)rank * kr;
+  p.lda = lda;
+  p.w_nk = w_layout == TTL_W_NK;
+  // W[k][n]: the rank's k rows start at row r*k/t.  W^T[n][k]: they are columns r*k/t.. of each row.
+  p.B = p.w_nk ? W + (int64_t)rank * kr : W + (int64_t)rank * kr * n;
+  p.ldb = p.w_nk ? k : n;
+  p.b_rows = n;
+  if (w_layout == TTL_W_BLOCKED) {
+    // the rank's k rows start at block row r*(k/t)/64 of every strip
+    const int64_t e0 = (int64_t)rank * kr / 64 * 8192;
+    p.w_blk = 1;
+    p.B = W + e0;
+    p.ldb = k * 128;
+    p.b_rows = n / 128 * k * 128 - e0;
+  }
+  p.C = P;
+  p.ldc = n;
+  p.M = (int32_t)b;
+  p.N = (int32_t)n;
+  p.K = (int32_t)kr;
+  p.mode = 0;
+  p.nseg = 1;
+  p.seg_out0[0] = 0;
+  p.seg_out0[1] = (int32_t)n;
+  p.seg_w0[0] = 0;
+  if (b * n > kMaxOutput)
+    return fail(TTL_ERR_SHAPE, "%s: output of %lld x %lld elements is too large", who, (long long)b,
+                (long long)n);
+  if (output_overlaps(P, b * n, X, b * lda, W, k * n))
+    return fail(TTL_ERR_UNSUPPORTED, "%s: P must not overlap X or W", who);
+  return launch_status(ttl::launch_gemm(p, static_cast<hipStream_t>(stream)), who);
+}
+
 // Validation and parameters of the reduction over rows [row0, row0 + rows) of P[t][b][n]; the
 // residual and the outputs hold exactly those rows.
 ttl_status reduce_setup(const char* who, const uint16_t* P, int32_t t, int64_t b, int64_t n,
@@ -248,17 +336,16 @@ ttl_status ttl_pack_weight_blocked(const uint16_t* W, int64_t k, int64_t n, uint
 
 int32_t ttl_version(void) { return 100; }  // 0.1.0
 
+ttl_status shard_linear_col_stored(const uint16_t* X, int64_t b, int64_t k, const uint16_t* W, int64_t n,
+                                   ttl_weight_layout w_layout, int32_t t, int32_t rank,
+                                   const ttl_col_split* split, ttl_epilogue epi, uint16_t* Y, void* stream) {
+  return col_entry("shard_linear_col_stored", X, b, k, W, n, w_layout, t, rank, split, epi, Y, stream);
+}
+
 ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k, const uint16_t* W, int64_t n,
-                            ttl_weight_layout w_layout, int32_t t, int32_t rank,
-                            const ttl_col_split* split, ttl_epilogue epi, uint16_t* Y, void* stream) {
-  static const char* who = "shard_linear_col";
-  ttl::GemmParams p;
-  int64_t width = 0;
-  const ttl_status st = col_setup(who, X, b, k, W, n, w_layout, t, rank, split, epi, Y, p, width);
-  if (st != TTL_OK) return st;
-  p.C = Y;
-  p.ldc = width;
-  return launch_status(ttl::launch_gemm(p, static_cast<hipStream_t>(stream)), who);
+                            int32_t t, int32_t rank, const ttl_col_split* split, ttl_epilogue epi,
+                            uint16_t* Y, void* stream) {
+  return col_entry("shard_linear_col", X, b, k, W, n, TTL_W_KN, t, rank, split, epi, Y, stream);
 }
 
 ttl_status shard_linear_col_gathered(const uint16_t* X, int64_t b, int64_t k, const uint16_t* W,
@@ -273,76 +360,33 @@ ttl_status shard_linear_col_gathered(const uint16_t* X, int64_t b, int64_t k, co
   if (width * t > kMaxLda)
     return fail(TTL_ERR_SHAPE, "%s: gathered row of %lld columns exceeds the supported pitch", who,
                 (long long)(width * t));
+  if (output_overlaps(Y_all, b * width * t, X, b * k, W, k * n))
+    return fail(TTL_ERR_UNSUPPORTED, "%s: Y_all must not overlap X or W", who);
   p.C = Y_all + (int64_t)rank * width;  // this rank's block of the gathered row
   p.ldc = width * t;
   return launch_status(ttl::launch_gemm(p, static_cast<hipStream_t>(stream)), who);
 }
 
-
+ttl_status shard_linear_row_stored(const uint16_t* X, int64_t b, int64_t k, int32_t x_is_parallel,
+                                   const uint16_t* W, int64_t n, ttl_weight_layout w_layout, int32_t t,
+                                   int32_t rank, uint16_t* P, void* stream) {
+  return row_entry("shard_linear_row_stored", X, b, k, x_is_parallel, W, n, w_layout, t, rank, P, stream);
+}
 
 ttl_status shard_linear_row(const uint16_t* X, int64_t b, int64_t k, int32_t x_is_parallel,
-                            const uint16_t* W, int64_t n, ttl_weight_layout w_layout, int32_t t,
-                            int32_t rank, uint16_t* P, void* stream) {
-  static const char* who = "shard_linear_row";
-  if (b <= 0 || k <= 0 || n <= 0 || b > kMaxDim || k > kMaxDim || n > kMaxDim)
-    return fail(TTL_ERR_SHAPE, "%s: b=%lld k=%lld n=%lld must be in [1, 2^31)", who, (long long)b,
-                (long long)k, (long long)n);
-  if (X == nullptr || W == nullptr || P == nullptr)
-    return fail(TTL_ERR_NULL, "%s: X, W and P must be non-NULL", who);
-  if (t < 1 || rank < 0 || rank >= t)
-    return fail(TTL_ERR_RANK, "%s: need t >= 1 and 0 <= rank < t (t=%d rank=%d)", who, t, rank);
-  if (w_layout != TTL_W_KN && w_layout != TTL_W_NK && w_layout != TTL_W_BLOCKED)
-    return fail(TTL_ERR_UNSUPPORTED, "%s: unknown weight layout %d", who, w_layout);
-  if (k % t != 0)
-    return fail(TTL_ERR_NOT_DIVISIBLE, "%s: k=%lld is not divisible by t=%d", who, (long long)k, t);
-  const int64_t kr = k / t;
-  if (!aligned16(X) || !aligned16(W) || !aligned16(P))
-    return fail(TTL_ERR_ALIGN, "%s: X, W and P must be 16-byte aligned", who);
-  if (kr % 8 != 0 || n % 8 != 0 || k % 8 != 0)
-    return fail(TTL_ERR_ALIGN, "%s: k/t=%lld and n=%lld must be multiples of 8", who,
-                (long long)kr, (long long)n);
-  const int64_t lda = x_is_parallel ? kr : k;
-  if (lda > kMaxLda || n > kMaxLdb || k > kMaxLdb)
-    return fail(TTL_ERR_SHAPE, "%s: row pitch of X or W exceeds the supported range", who);
-  if (w_layout == TTL_W_NK && n * k * 2 >= kMaxNkBytes)
-    return fail(TTL_ERR_UNSUPPORTED, "%s: a [n][k] weight must stay below 2 GiB", who);
-  if (w_layout == TTL_W_BLOCKED) {
-    if (k % 64 != 0 || kr % 64 != 0 || n % 128 != 0)
-      return fail(TTL_ERR_ALIGN, "%s: a blocked weight needs k %% 64, (k/t) %% 64 and n %% 128 == 0", who);
-    if (n * k * 2 >= kMaxNkBytes)
-      return fail(TTL_ERR_UNSUPPORTED, "%s: a blocked weight must stay below 2 GiB", who);
-  }
+                            const uint16_t* W, int64_t n, int32_t t, int32_t rank, uint16_t* P,
+                            void* stream) {
+  return row_entry("shard_linear_row", X, b, k, x_is_parallel, W, n, TTL_W_KN, t, rank, P, stream);
+}
 
-  ttl::GemmParams p = {};
-  p.A = x_is_parallel ? X : X + (int64_t)rank * kr;
-  p.lda = lda;
-  p.w_nk = w_layout == TTL_W_NK;
-  // W[k][n]: the rank's k rows start at row r*k/t.  W^T[n][k]: they are columns r*k/t.. of each row.
-  p.B = p.w_nk ? W + (int64_t)rank * kr : W + (int64_t)rank * kr * n;
-  p.ldb = p.w_nk ? k : n;
-  p.b_rows = n;
-  if (w_layout == TTL_W_BLOCKED) {
-    // the rank's k rows start at block row r*(k/t)/64 of every strip
-    const int64_t e0 = (int64_t)rank * kr / 64 * 8192;
-    p.w_blk = 1;
-    p.B = W + e0;
-    p.ldb = k * 128;
-    p.b_rows = n / 128 * k * 128 - e0;
-  }
-  p.C = P;
-  p.ldc = n;
-  p.M = (int32_t)b;
-  p.N = (int32_t)n;
-  p.K = (int32_t)kr;
-  p.mode = 0;
-  p.nseg = 1;
-  p.seg_out0[0] = 0;
-  p.seg_out0[1] = (int32_t)n;
-  p.seg_w0[0] = 0;
-  if (b * n > kMaxOutput)
-    return fail(TTL_ERR_SHAPE, "%s: output of %lld x %lld elements is too large", who, (long long)b,
-                (long long)n);
-  return launch_status(ttl::launch_gemm(p, static_cast<hipStream_t>(stream)), who);
+ttl_status ttl_set_gemm_override(int32_t kernel, int32_t splits, int32_t plan_cus, int32_t trace) {
+  static const char* who = "ttl_set_gemm_override";
+  if (kernel < TTL_GEMM_AUTO || kernel > TTL_GEMM_MIXED)
+    return fail(TTL_ERR_UNSUPPORTED, "%s: unknown kernel family %d", who, kernel);
+  if (splits < 0 || plan_cus < 0)
+    return fail(TTL_ERR_UNSUPPORTED, "%s: splits=%d and plan_cus=%d must be >= 0", who, splits, plan_cus);
+  ttl::set_gemm_override(kernel, splits, plan_cus, trace != 0);
+  return TTL_OK;
 }
 
 ttl_status reduce_partials_rmsnorm(const uint16_t* P, int32_t t, int64_t b, int64_t n,

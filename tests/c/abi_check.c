@@ -36,17 +36,25 @@ int main(void) {
     printf("FAIL version %d\n", ttl_version());
     ++failures;
   }
-  expect("col: NULL X", shard_linear_col(NULL, 16, 256, W, 1376, TTL_W_KN, 2, 0, &split, TTL_EPI_SILU_MUL, Y, NULL),
+  /* the statement's form: X[b,k], W[k,n], t, rank */
+  expect("col: NULL X", shard_linear_col(NULL, 16, 256, W, 1376, 2, 0, &split, TTL_EPI_SILU_MUL, Y, NULL),
          TTL_ERR_NULL);
-  expect("col: rank >= t", shard_linear_col(X, 16, 256, W, 1376, TTL_W_KN, 2, 2, &split, TTL_EPI_SILU_MUL, Y, NULL),
+  expect("col: rank >= t", shard_linear_col(X, 16, 256, W, 1376, 2, 2, &split, TTL_EPI_SILU_MUL, Y, NULL),
          TTL_ERR_RANK);
-  expect("col: unknown layout", shard_linear_col(X, 16, 256, W, 1376, 7, 2, 0, &split, TTL_EPI_SILU_MUL, Y, NULL),
+  expect("col: Y overlapping W",
+         shard_linear_col(X, 16, 256, W, 1376, 2, 0, &split, TTL_EPI_SILU_MUL, (uint16_t*)(uintptr_t)0x20400, NULL),
+         TTL_ERR_UNSUPPORTED);
+  expect("col (stored): unknown layout",
+         shard_linear_col_stored(X, 16, 256, W, 1376, 7, 2, 0, &split, TTL_EPI_SILU_MUL, Y, NULL),
          TTL_ERR_UNSUPPORTED);
   expect("gathered: b = 0",
          shard_linear_col_gathered(X, 0, 256, W, 1376, TTL_W_KN, 2, 0, &split, TTL_EPI_NONE, Y, NULL),
          TTL_ERR_SHAPE);
-  expect("row: k not divisible by t", shard_linear_row(X, 16, 689, 1, W, 256, TTL_W_KN, 2, 0, Y, NULL),
+  expect("row: k not divisible by t", shard_linear_row(X, 16, 689, 1, W, 256, 2, 0, Y, NULL),
          TTL_ERR_NOT_DIVISIBLE);
+  expect("row (stored): blocked with (k/t) % 64", shard_linear_row_stored(X, 16, 1024, 1, W, 256, TTL_W_BLOCKED, 32, 0, Y, NULL),
+         TTL_ERR_ALIGN);
+  expect("override: unknown kernel", ttl_set_gemm_override(TTL_GEMM_MIXED + 1, 0, 0, 0), TTL_ERR_UNSUPPORTED);
   expect("reduce: misaligned Y", reduce_partials_rmsnorm(X, 2, 16, 256, NULL, gamma, 1e-5f, Y, Y + 2, NULL),
          TTL_ERR_ALIGN);
   expect("reduce-scatter: b not divisible by t",

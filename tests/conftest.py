@@ -27,3 +27,29 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+class GemmForce:
+    """The library's test-only GEMM override (ttl_set_gemm_override), set field by field."""
+
+    def __init__(self):
+        from tensor_transformer_linear_amd import ttl
+        self._ttl = ttl
+        self.state = dict(kernel="auto", splits=0, plan_cus=0, trace=False)
+
+    def set(self, **kw):
+        self.state.update(kw)
+        self._ttl.set_gemm_override(**self.state)
+
+    def reset(self):
+        self.state = dict(kernel="auto", splits=0, plan_cus=0, trace=False)
+        self._ttl.set_gemm_override()
+
+
+@pytest.fixture
+def gemm_force():
+    """Forces GEMM kernel choices for one test; the choice by shape is restored afterwards."""
+    f = GemmForce()
+    f.reset()
+    yield f
+    f.reset()

@@ -65,9 +65,13 @@ def test_status_codes_match_header():
     assert ttl.version() >= 100
 
 
-def _col(X=A, b=16, k=256, W=B, n=1376, t=2, rank=0, split=None, epi=0, Y=C, lay=0):
+def _col(X=A, b=16, k=256, W=B, n=1376, t=2, rank=0, split=None, epi=0, Y=C, lay=None):
+    """shard_linear_col (the [k][n] form of the statement) when lay is None, else
+    shard_linear_col_stored with that storage."""
     sp = None if split is None else ttl.ctypes.byref(split)
-    return ttl.lib().shard_linear_col(X, b, k, W, n, lay, t, rank, sp, epi, Y, None)
+    if lay is None:
+        return ttl.lib().shard_linear_col(X, b, k, W, n, t, rank, sp, epi, Y, None)
+    return ttl.lib().shard_linear_col_stored(X, b, k, W, n, lay, t, rank, sp, epi, Y, None)
 
 
 def _colg(X=A, b=16, k=256, W=B, n=1376, t=2, rank=0, split=None, epi=0, Y=C, lay=0):
@@ -79,8 +83,14 @@ def _rs(P=A, t=2, b=16, n=256, rank=0, R=B, gamma=D, eps=1e-5, Rout=B, Y=C):
     return ttl.lib().reduce_scatter_partials_rmsnorm(P, t, b, n, rank, R, gamma, eps, Rout, Y, None)
 
 
-def _row(X=A, b=16, k=688, par=1, W=B, n=256, t=2, rank=0, P=C, lay=0):
-    return ttl.lib().shard_linear_row(X, b, k, par, W, n, lay, t, rank, P, None)
+def _row(X=A, b=16, k=688, par=1, W=B, n=256, t=2, rank=0, P=C, lay=None):
+    if lay is None:
+        return ttl.lib().shard_linear_row(X, b, k, par, W, n, t, rank, P, None)
+    return ttl.lib().shard_linear_row_stored(X, b, k, par, W, n, lay, t, rank, P, None)
+
+
+# far-apart fake buffers for the overlap rules (the defaults above sit 64 KiB apart)
+FX, FW, FY = 0x1000000, 0x2000000, 0x3000000
 
 
 def _pack(W=A, k=256, n=1024, out=B):
@@ -119,6 +129,14 @@ def _peers(ptrs=None, t=2, b=16, n=256, row0=0, rows=16, R=B, gamma=D, eps=1e-5,
     (lambda: _col(epi=1, split=ttl.make_split((704, 672), (2, 2))), ttl.ERR_UNSUPPORTED, "two equal"),
     (lambda: _col(epi=7), ttl.ERR_UNSUPPORTED, "epilogue"),
     (lambda: _col(lay=3), ttl.ERR_UNSUPPORTED, "weight layout"),
+    (lambda: _col(lay=ttl.W_KN, X=None), ttl.ERR_NULL, "shard_linear_col_stored"),
+    (lambda: _col(X=FX, W=FW, Y=FW + 4096), ttl.ERR_UNSUPPORTED, "overlap"),       # Y inside W
+    (lambda: _col(X=FX, W=FW, Y=FX + 16), ttl.ERR_UNSUPPORTED, "overlap"),         # Y inside X
+    (lambda: _col(X=FX, W=FW, Y=FW - 16, lay=ttl.W_NK, n=1376, k=256), ttl.ERR_UNSUPPORTED, "overlap"),
+    (lambda: _colg(X=FX, W=FW, Y=FX + 32), ttl.ERR_UNSUPPORTED, "overlap"),
+    (lambda: _row(X=FX, W=FW, P=FW + 1024), ttl.ERR_UNSUPPORTED, "overlap"),       # P inside W
+    (lambda: _row(X=FX, W=FW, P=FX + 16, par=0), ttl.ERR_UNSUPPORTED, "overlap"),  # P inside full X
+    (lambda: _row(X=FX, W=FW, P=FW + 1024, lay=ttl.W_NK), ttl.ERR_UNSUPPORTED, "overlap"),
     (lambda: _col(lay=ttl.W_BLOCKED), ttl.ERR_ALIGN, "blocked weight"),          # n % 128 != 0
     (lambda: _col(k=200, n=1536, lay=ttl.W_BLOCKED), ttl.ERR_ALIGN, "blocked weight"),
     (lambda: _col(k=16384, n=131072, t=1, lay=ttl.W_BLOCKED), ttl.ERR_UNSUPPORTED, "2 GiB"),
@@ -130,6 +148,10 @@ def _peers(ptrs=None, t=2, b=16, n=256, row0=0, rows=16, R=B, gamma=D, eps=1e-5,
     (lambda: _colg(epi=1), ttl.ERR_UNSUPPORTED, "two equal segments"),
     (lambda: _colg(k=252), ttl.ERR_ALIGN, "multiples of 8"),
     (lambda: _row(lay=-1), ttl.ERR_UNSUPPORTED, "weight layout"),
+    (lambda: _row(lay=ttl.W_KN, P=None), ttl.ERR_NULL, "shard_linear_row_stored"),
+    (lambda: ttl.lib().ttl_set_gemm_override(9, 0, 0, 0), ttl.ERR_UNSUPPORTED, "unknown kernel"),
+    (lambda: ttl.lib().ttl_set_gemm_override(2, -1, 0, 0), ttl.ERR_UNSUPPORTED, "splits=-1"),
+    (lambda: ttl.lib().ttl_set_gemm_override(0, 0, -4, 0), ttl.ERR_UNSUPPORTED, "plan_cus=-4"),
     (lambda: _row(lay=ttl.W_BLOCKED), ttl.ERR_ALIGN, "blocked weight"),          # k % 64 != 0
     (lambda: _row(k=1024, t=32, lay=ttl.W_BLOCKED), ttl.ERR_ALIGN, "blocked weight"),  # k/t = 32
     (lambda: _row(k=16384, n=65536, t=1, lay=ttl.W_BLOCKED), ttl.ERR_UNSUPPORTED, "2 GiB"),
@@ -192,7 +214,66 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError, match="GPU"):
         ttl.shard_linear_col(X, W, 2, 0, ttl.merged_gate_up_split(688, 2), ttl.EPI_SILU_MUL)
     with pytest.raises(TypeError, match="bfloat16"):
-        ttl.shard_linear_row(X.float(), W, 2, 0)
+        ttl.shard_linear_row(X[:, :128].float().contiguous(), W, 2, 0)
+
+
+def test_exact_and_stored_forms_validate_alike():
+    """The statement's [k][n] form and the storage-taking form apply the same rules."""
+    for kw in (dict(b=0), dict(rank=3), dict(n=1370, t=4), dict(X=A + 8)):
+        assert _col(**kw) == _col(lay=ttl.W_KN, **kw)
+    for kw in (dict(k=689), dict(rank=2), dict(P=None)):
+        assert _row(**kw) == _row(lay=ttl.W_KN, **kw)
+
+
+def _cpu(*shape):
+    import torch
+    return torch.zeros(*shape, dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("call,needle", [
+    # caller-supplied outputs of the wrong shape
+    (lambda: ttl.shard_linear_col(_cpu(16, 256), _cpu(256, 1376), 2, 0, ttl.merged_gate_up_split(688, 2),
+                                  ttl.EPI_SILU_MUL, Y=_cpu(16, 688)), "Y must be [16, 344]"),
+    (lambda: ttl.shard_linear_col(_cpu(16, 256), _cpu(256, 1376), 2, 0, Y=_cpu(8, 688)), "Y must be [16, 688]"),
+    (lambda: ttl.shard_linear_col_gathered(_cpu(16, 256), _cpu(256, 1376), 2, 1, Y_all=_cpu(16, 688)),
+     "Y_all must be [16, 1376]"),
+    (lambda: ttl.shard_linear_row(_cpu(16, 344), _cpu(688, 256), 2, 0, P=_cpu(16, 255)), "P must be [16, 256]"),
+    # the row GEMM's input must be [b, k/t] (parallel) or [b, k] (full)
+    (lambda: ttl.shard_linear_row(_cpu(16, 344), _cpu(688, 256), 2, 0, x_is_parallel=False), "X must be [16, 688]"),
+    (lambda: ttl.shard_linear_row(_cpu(16, 688), _cpu(688, 256), 2, 0, x_is_parallel=True), "X must be [16, 344]"),
+    (lambda: ttl.shard_linear_row(_cpu(16, 688), _cpu(256, 688), 2, 0, x_is_parallel=False, w_layout=ttl.W_NK,
+                                  P=_cpu(16, 200)), "P must be [16, 256]"),
+    # X and W disagree on k
+    (lambda: ttl.shard_linear_col(_cpu(16, 200), _cpu(256, 1376), 2, 0), "X is [16,200]"),
+    # the reduction's operands
+    (lambda: ttl.reduce_partials_rmsnorm(_cpu(2, 16, 256), _cpu(255), 1e-5), "gamma must be [256]"),
+    (lambda: ttl.reduce_partials_rmsnorm(_cpu(2, 16, 256), _cpu(256), 1e-5, residual=_cpu(16, 128)),
+     "residual must be [16, 256]"),
+    (lambda: ttl.reduce_partials_rmsnorm(_cpu(2, 16, 256), _cpu(256), 1e-5, Y=_cpu(15, 256)), "Y must be [16, 256]"),
+    (lambda: ttl.reduce_partials_rmsnorm(_cpu(16, 256), _cpu(256), 1e-5), "3-D"),
+    (lambda: ttl.reduce_scatter_partials_rmsnorm(_cpu(2, 16, 256), _cpu(256), 1e-5, 0, residual=_cpu(16, 256)),
+     "residual must be [8, 256]"),
+    (lambda: ttl.reduce_partials_rmsnorm_peers([_cpu(16, 256)] * 2, _cpu(256), 1e-5, row0=8, rows=8,
+                                               Y=_cpu(16, 256)), "Y must be [8, 256]"),
+    (lambda: ttl.pack_weight_blocked(_cpu(256, 1024), out=_cpu(1024, 256)), "out must be [256, 1024]"),
+])
+def test_binding_checks_shapes_before_any_call(call, needle):
+    """Every tensor's shape is checked against the sizes the call will read and write before the C
+    entry point is reached: these host tensors would otherwise be refused later, as host memory."""
+    with pytest.raises(ValueError, match=re.escape(needle)):
+        call()
+
+
+def test_gemm_override_setter():
+    """The test-only kernel override is set and cleared through its entry point; no environment
+    variable is read by the library."""
+    with ttl.gemm_override("splitk", splits=3):
+        pass
+    with pytest.raises(ValueError):
+        ttl.set_gemm_override("bogus")
+    out = subprocess.run(["nm", "-D", "--undefined-only", ttl.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    assert "getenv" not in out
 
 
 def test_split_helpers_match_header_rule():

@@ -50,3 +50,22 @@ def test_recorded_traffic_requires_matching_sources(tmp_path, monkeypatch):
     # With the profiles as committed the function returns a number or None, never raises.
     v = bench.recorded_traffic("shard_linear_col_silu_mul", "no_such_workload")
     assert v is None
+
+
+def test_cpu_baseline_fields():
+    """The CPU baseline leg on the tiny workload: all-core and one-core runs, the CPU model, and
+    GEMM TFLOP/s and reduce GB/s as separate fields."""
+    import torch
+    spec = importlib.util.spec_from_file_location("bench_mod", BENCH)
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    from tensor_transformer_linear_amd import workloads as wl
+    w = wl.TINY_MLP_T2
+    inp = wl.mlp_inputs(w, 16, seed=0)
+    out = bench.cpu_baseline(torch, w, (inp["X"], inp["Wgu"], inp["Wd"], inp["R"], inp["gamma"]), 8, 0.2)
+    assert out["kind"] == "oracle" and out["unit"] == "TFLOP/s" and out["value"] > 0
+    assert out["one_core"]["threads"] == 1 and out["cores"] >= 1
+    assert out["affinity_cores"] == len(os.sched_getaffinity(0))
+    for run in (out["one_core"], out["all_cores"]):
+        assert run["gemm_tflops"] > 0 and run["reduce_gbs"] > 0
+    assert out["cpu_model"]

@@ -1,9 +1,12 @@
 """Parity at the full Llama-shaped sizes, in the same launch configuration the benchmark times.
 
-The device computes every rank's shard at full size through the C ABI; the oracle recomputes a
-sample of token rows (both ends, tile boundaries, seeded picks) for every rank.  Rows are
-independent through every step — GEMM rows, SiLU·up, per-row RMSNorm — so the sampled rows of the
-full device result are compared exactly with the oracle's values for those rows.
+The device computes every rank's shard at full size through the C ABI; the oracle recomputes every
+token row at decode sizes (b <= 256) and at least 256 rows at prefill sizes (the first and last row
+of every 64-row block, so at least one row of every tile the GEMMs launch, plus seeded picks), for
+every rank.  Rows are independent through every step — GEMM rows, SiLU·up, per-row RMSNorm — so the
+sampled rows of the full device result are compared exactly with the oracle's values for those
+rows.  y and residual_out are held to max|err| <= 2e-2 * rms(ref) as stated; the activations and
+partials to the error beyond their bf16 storage rounding.
 
 Inputs are drawn on the device from the seeded generator (same recipe as every other test) and
 copied to the host for the oracle.
@@ -17,7 +20,7 @@ import torch
 
 import oracle
 from tensor_transformer_linear_amd import workloads as wl
-from tests.util import assert_close, f64, from_gpu, sample_rows
+from tests.util import assert_close, f64, from_gpu, parity_rows
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -77,16 +80,16 @@ def test_mlp_shard_full_size(ttl, w, b, layout):
     Wd_s, _ = _stored(ttl, d["Wd"], layout)
     acts, P, rout, y = _mlp_device_chain(ttl, d["X"], d["R"], d["gamma"], Wgu_s, Wd_s, w, b, lay)
     del Wgu_s, Wd_s
-    rows = sample_rows(b)
-    print(f"{w.name} b={b}: checking rows {rows}", flush=True)
+    rows = parity_rows(b)
+    print(f"{w.name} b={b}: checking {len(rows)} rows", flush=True)
     o = _host({k: d[k] for k in ("Wgu", "Wd", "gamma")})
     Xs, Rs = f64(d["X"][rows].cpu()), f64(d["R"][rows].cpu())
     racts, rP, h, yref = _mlp_oracle_rows(o, Xs, Rs, w)
     for r in range(w.t):
-        assert_close(from_gpu(acts[r][rows]), racts[r], f"{w.name} b={b} act r={r}")
-        assert_close(from_gpu(P[r][rows]), rP[r], f"{w.name} b={b} partial r={r}")
-    assert_close(from_gpu(rout[rows]), h, f"{w.name} b={b} residual_out")
-    assert_close(from_gpu(y[rows]), yref, f"{w.name} b={b} y")
+        assert_close(from_gpu(acts[r][rows]), racts[r], f"{w.name} b={b} {layout} act r={r}")
+        assert_close(from_gpu(P[r][rows]), rP[r], f"{w.name} b={b} {layout} partial r={r}")
+    assert_close(from_gpu(rout[rows]), h, f"{w.name} b={b} {layout} residual_out", literal=True)
+    assert_close(from_gpu(y[rows]), yref, f"{w.name} b={b} {layout} y", literal=True)
     # property at every row (no oracle needed): y is finite and has rms(y / gamma) ~ 1
     yall = y.float() / d["gamma"].float()
     ms = (yall * yall).mean(dim=1)
@@ -110,17 +113,18 @@ def test_attn_projections_8b_tp4(ttl):
     for r in range(t):
         ttl.shard_linear_row(d["A"][:, r * kr:(r + 1) * kr].contiguous(), d["Wo"], t, r, True, P=P[r])
     rout, y = ttl.reduce_partials_rmsnorm(P, d["gamma"], w.eps, d["R"])
-    rows = sample_rows(b)
+    rows = parity_rows(b)
     o = _host({k: d[k] for k in ("Wqkv", "Wo", "gamma")})
     Xs, As, Rs = f64(d["X"][rows].cpu()), f64(d["A"][rows].cpu()), f64(d["R"][rows].cpu())
     for r in range(t):
-        assert_close(from_gpu(qkv[r][rows]), oracle.col_shard(Xs, o["Wqkv"], sp_o, t, r), f"qkv r={r}")
+        assert_close(from_gpu(qkv[r][rows]), oracle.col_shard(Xs, o["Wqkv"], sp_o, t, r),
+                     f"llama3_8b_attn_tp4 qkv r={r}")
     rP = np.stack([oracle.row_shard(As, o["Wo"], t, r, False) for r in range(t)])
     for r in range(t):
-        assert_close(from_gpu(P[r][rows]), rP[r], f"o_proj partial r={r}")
+        assert_close(from_gpu(P[r][rows]), rP[r], f"llama3_8b_attn_tp4 o_proj partial r={r}")
     h, yref = oracle.reduce_partials_rmsnorm(oracle.round_bf16(rP), Rs, o["gamma"], w.eps)
-    assert_close(from_gpu(rout[rows]), h, "attn residual_out")
-    assert_close(from_gpu(y[rows]), yref, "attn y")
+    assert_close(from_gpu(rout[rows]), h, "llama3_8b_attn_tp4 residual_out", literal=True)
+    assert_close(from_gpu(y[rows]), yref, "llama3_8b_attn_tp4 y", literal=True)
     # concatenating the q slices of all ranks gives the unsharded q projection (column invariant)
     qcat = torch.cat([q[rows][:, :kr] for q in qkv], dim=1)
     assert_close(from_gpu(qcat), Xs @ o["Wqkv"][:, :w.n_q_heads * w.head_dim], "q concat over ranks")
@@ -149,26 +153,27 @@ def test_decoder_layer_70b_tp8(ttl, layout):
     del Wo_s
     r1, y1 = ttl.reduce_partials_rmsnorm(P, d["gamma_attn"], w.eps, d["R"])
     acts, P2, r2, y2 = _mlp_device_chain(ttl, y1, r1, d["gamma_mlp"], st(d["Wgu"]), st(d["Wd"]), w, b, lay)
-    rows = sample_rows(b, extra=(2047, 2048, 2175))
-    print(f"layer b={b}: checking rows {rows}", flush=True)
+    rows = parity_rows(b, extra=(2047, 2048, 2175))
+    print(f"layer b={b}: checking {len(rows)} rows", flush=True)
     o = _host({k: d[k] for k in ("Wqkv", "Wo", "gamma_attn", "gamma_mlp", "Wgu", "Wd")})
     Xs, As, Rs = f64(d["X"][rows].cpu()), f64(d["A"][rows].cpu()), f64(d["R"][rows].cpu())
     for r in range(t):
-        assert_close(from_gpu(qkv[r][rows]), oracle.col_shard(Xs, o["Wqkv"], sp_o, t, r), f"qkv r={r}")
+        assert_close(from_gpu(qkv[r][rows]), oracle.col_shard(Xs, o["Wqkv"], sp_o, t, r),
+                     f"llama3_70b_layer_tp8 {layout} qkv r={r}")
     rP = np.stack([oracle.row_shard(As, o["Wo"], t, r, False) for r in range(t)])
     for r in range(t):
-        assert_close(from_gpu(P[r][rows]), rP[r], f"layer o_proj partial r={r}")
+        assert_close(from_gpu(P[r][rows]), rP[r], f"llama3_70b_layer_tp8 {layout} o_proj partial r={r}")
     h1, yr1 = oracle.reduce_partials_rmsnorm(oracle.round_bf16(rP), Rs, o["gamma_attn"], w.eps)
-    assert_close(from_gpu(r1[rows]), h1, "layer attn residual_out")
-    assert_close(from_gpu(y1[rows]), yr1, "layer attn y")
+    assert_close(from_gpu(r1[rows]), h1, f"llama3_70b_layer_tp8 {layout} attn residual_out", literal=True)
+    assert_close(from_gpu(y1[rows]), yr1, f"llama3_70b_layer_tp8 {layout} attn y", literal=True)
     # MLP half: the oracle continues from its own (bf16-stored) attention outputs
     o2 = {"Wgu": o["Wgu"], "Wd": o["Wd"], "gamma": o["gamma_mlp"]}
     racts, rP2, h2, yr2 = _mlp_oracle_rows(o2, oracle.round_bf16(yr1), oracle.round_bf16(h1), w)
     for r in range(t):
-        assert_close(from_gpu(acts[r][rows]), racts[r], f"layer act r={r}")
-        assert_close(from_gpu(P2[r][rows]), rP2[r], f"layer down partial r={r}")
-    assert_close(from_gpu(r2[rows]), h2, "layer mlp residual_out")
-    assert_close(from_gpu(y2[rows]), yr2, "layer mlp y")
+        assert_close(from_gpu(acts[r][rows]), racts[r], f"llama3_70b_layer_tp8 {layout} act r={r}")
+        assert_close(from_gpu(P2[r][rows]), rP2[r], f"llama3_70b_layer_tp8 {layout} down partial r={r}")
+    assert_close(from_gpu(r2[rows]), h2, f"llama3_70b_layer_tp8 {layout} mlp residual_out", literal=True)
+    assert_close(from_gpu(y2[rows]), yr2, f"llama3_70b_layer_tp8 {layout} mlp y", literal=True)
 
 
 @pytest.mark.parametrize("b", [64, 2048])
@@ -190,7 +195,7 @@ def test_vocab_parallel_lm_head_70b_tp8(ttl, b, layout):
     for r in range(t):
         ttl.shard_linear_col_gathered(X, Ws, t, r, Y_all=logits, w_layout=lay)
     torch.cuda.synchronize()
-    rows = sample_rows(b)
+    rows = parity_rows(b)
     Xh = f64(X[rows].cpu())
     sp = oracle.plain_split(vocab, t)
     for r in (0, t - 1):

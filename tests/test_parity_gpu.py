@@ -2,7 +2,7 @@
 
 Small cases compare every element; they span several 256-wide tiles and ragged tails in all three
 GEMM dimensions.  Each GEMM case runs through every kernel the library has, forced with
-TTL_GEMM_KERNEL (256 x 256 tiles by the four-wave kernel where K is a multiple of 64, by the
+the library's test-only override (256 x 256 tiles by the four-wave kernel where K is a multiple of 64, by the
 eight-wave kernel, the four-wave kernel's tiles cut along k, its 256 x 128 tiles, its 192 x 256
 tiles, and the split-K kernel for short M), and through the shape-based choice.  Tolerance, per output tensor: the error beyond the bf16 rounding of each output
 element is at most 2e-2 * rms(ref), the reference being the oracle's unrounded float64 value (bf16
@@ -32,13 +32,13 @@ LAYOUTS = pytest.mark.parametrize("layout", ["kn", "nk"])
 
 
 @pytest.fixture(params=["auto", "tiled", "eightwave", "tilesplit", "narrow", "short", "splitk"])
-def gemm_path(request, monkeypatch):
+def gemm_path(request, gemm_force):
     """Which GEMM kernel the library uses for the test (auto = its choice by shape)."""
     if request.param == "auto":
-        monkeypatch.delenv("TTL_GEMM_KERNEL", raising=False)
+        gemm_force.set(kernel="auto")
     else:
-        monkeypatch.setenv("TTL_GEMM_KERNEL", request.param)
-    monkeypatch.delenv("TTL_GEMM_SPLITS", raising=False)
+        gemm_force.set(kernel=request.param)
+    gemm_force.set(splits=0)
     return request.param
 
 
@@ -125,8 +125,8 @@ def test_reduce_rmsnorm(ttl, t, b, n, with_residual):
     Rd = gpu(R) if with_residual else None
     rout, y = ttl.reduce_partials_rmsnorm(gpu(P), gpu(gamma), 1e-5, Rd)
     h, yref = oracle.reduce_partials_rmsnorm(f64(P), f64(R) if with_residual else None, f64(gamma), 1e-5)
-    assert_close(from_gpu(rout), h, f"reduce residual_out t={t} b={b} n={n}")
-    assert_close(from_gpu(y), yref, f"reduce y t={t} b={b} n={n}")
+    assert_close(from_gpu(rout), h, f"reduce residual_out t={t} b={b} n={n}", literal=True)
+    assert_close(from_gpu(y), yref, f"reduce y t={t} b={b} n={n}", literal=True)
 
 
 def test_reduce_residual_in_place(ttl):
@@ -137,21 +137,21 @@ def test_reduce_residual_in_place(ttl):
     rout, y = ttl.reduce_partials_rmsnorm(gpu(P), gpu(gamma), 1e-5, Rd, residual_out=Rd)
     assert rout.data_ptr() == Rd.data_ptr()
     h, yref = oracle.reduce_partials_rmsnorm(f64(P), f64(R), f64(gamma), 1e-5)
-    assert_close(from_gpu(Rd), h, "in-place residual")
-    assert_close(from_gpu(y), yref, "in-place y")
+    assert_close(from_gpu(Rd), h, "in-place residual", literal=True)
+    assert_close(from_gpu(y), yref, "in-place y", literal=True)
 
 
 @pytest.mark.parametrize("case", ["col_k_max", "col_k_max_nk", "col_n_max", "row_k_max"])
 @pytest.mark.parametrize("kern", ["auto", "tiled"])
-def test_maximum_row_pitches(ttl, monkeypatch, case, kern):
+def test_maximum_row_pitches(ttl, gemm_force, case, kern):
     """The largest row pitches the ABI accepts: X rows of k = 2^21 elements (the row GEMM reading
     the upper half of each row), and W rows of n = 2^23 columns.  Every 32-bit byte offset inside a
     tile is then within a factor of two of its limit; sampled outputs match the oracle."""
-    monkeypatch.delenv("TTL_GEMM_SPLITS", raising=False)
+    gemm_force.set(splits=0)
     if kern == "auto":
-        monkeypatch.delenv("TTL_GEMM_KERNEL", raising=False)
+        gemm_force.set(kernel="auto")
     else:
-        monkeypatch.setenv("TTL_GEMM_KERNEL", kern)
+        gemm_force.set(kernel=kern)
     if case == "col_n_max":
         b, k, n = 8, 64, 1 << 23
     else:
@@ -237,11 +237,11 @@ def test_layouts_agree_bitwise(ttl, gemm_path):
 
 @pytest.mark.parametrize("k", [64, 128, 192, 320, 576])
 @LAYOUTS
-def test_tiled_kernels_short_k(ttl, monkeypatch, k, layout):
+def test_tiled_kernels_short_k(ttl, gemm_force, k, layout):
     """The four-wave kernel's 256 x 256 and 256 x 128 tiles over 1, 2, 3, 5 and 9 k-tiles (its
     prologue and the two peeled k-tiles), ragged in M and N, match the oracle and the eight-wave
     kernel bit for bit (all accumulate the same products in the same k order)."""
-    monkeypatch.delenv("TTL_GEMM_SPLITS", raising=False)
+    gemm_force.set(splits=0)
     b, I, t = 300, 688, 2
     X = wl.random_bf16((b, k), 95 + k)
     W = wl.random_bf16((k, 2 * I), 96 + k, std=0.05)
@@ -249,7 +249,7 @@ def test_tiled_kernels_short_k(ttl, monkeypatch, k, layout):
     sp = ttl.merged_gate_up_split(I, t)
     outs = {}
     for kern in ("tiled", "eightwave", "narrow"):
-        monkeypatch.setenv("TTL_GEMM_KERNEL", kern)
+        gemm_force.set(kernel=kern)
         outs[kern] = ttl.shard_linear_col(gpu(X), Wd_, t, 1, sp, ttl.EPI_SILU_MUL, w_layout=lay)
         torch.cuda.synchronize()
     ref = oracle.silu_mul(oracle.col_shard(f64(X), f64(W), oracle.merged_gate_up_split(I, t), t, 1))
@@ -262,12 +262,12 @@ def test_tiled_kernels_short_k(ttl, monkeypatch, k, layout):
 @pytest.mark.parametrize("silu", [False, True])
 @pytest.mark.parametrize("kern", ["tilesplit", "narrowsplit"])
 @LAYOUTS
-def test_tiles_cut_along_k(ttl, monkeypatch, splits, silu, kern, layout):
+def test_tiles_cut_along_k(ttl, gemm_force, splits, silu, kern, layout):
     """256 x 256 (and 256 x 128) tiles of the four-wave kernel cut into k ranges (10 k-tiles of 64:
     ranges of 5+5, 4+4+2 and 2+2+2+2+2), ragged in M and N, against the oracle; SiLU·up runs as the
     gate columns then the up columns and is paired by the finalize kernel."""
-    monkeypatch.setenv("TTL_GEMM_KERNEL", kern)
-    monkeypatch.setenv("TTL_GEMM_SPLITS", str(splits))
+    gemm_force.set(kernel=kern)
+    gemm_force.set(splits=splits)
     b, k, t = 600, 640, 2
     X = wl.random_bf16((b, k), 99 + splits)
     if silu:
@@ -288,12 +288,12 @@ def test_tiles_cut_along_k(ttl, monkeypatch, splits, silu, kern, layout):
 
 @pytest.mark.parametrize("silu", [False, True])
 @LAYOUTS
-def test_short_last_round_split_by_rows(ttl, monkeypatch, silu, layout):
+def test_short_last_round_split_by_rows(ttl, gemm_force, silu, layout):
     """2176 x 8192 outputs are 288 tiles of 256 x 256: one whole round on 256 CUs plus 32 tiles.
     By default the first 2048 rows run as tiles and the last 128 rows through the split-K kernel;
     sampled rows on both sides of the cut match the oracle, and the head rows match the forced
     tiled run bit for bit."""
-    monkeypatch.delenv("TTL_GEMM_SPLITS", raising=False)
+    gemm_force.set(splits=0)
     b, k = 2176, 256
     n = 8192
     X = wl.random_bf16((b, k), 97)
@@ -307,9 +307,9 @@ def test_short_last_round_split_by_rows(ttl, monkeypatch, silu, layout):
     outs = {}
     for kern in ("auto", "tiled"):
         if kern == "auto":
-            monkeypatch.delenv("TTL_GEMM_KERNEL", raising=False)
+            gemm_force.set(kernel="auto")
         else:
-            monkeypatch.setenv("TTL_GEMM_KERNEL", kern)
+            gemm_force.set(kernel=kern)
         outs[kern] = ttl.shard_linear_col(gpu(X), Wd_, 1, 0, sp_c, epi, w_layout=lay)
         torch.cuda.synchronize()
     rows = np.r_[0:8, 2040:2056, 2100:2108, 2168:2176]
@@ -321,23 +321,23 @@ def test_short_last_round_split_by_rows(ttl, monkeypatch, silu, layout):
 
 
 @pytest.mark.parametrize("case", ["narrow", "narrowsplit"])
-def test_auto_choice_of_narrow_tiles(ttl, monkeypatch, case):
+def test_auto_choice_of_narrow_tiles(ttl, gemm_force, case):
     """Shapes whose 256 x 256 tiles fill too few CUs: 512 x 12288 outputs (96 wide tiles, 192
     narrow ones: narrow tiles, whole k) and 512 x 6144 outputs at k = 4096 (48 wide tiles x 4
     splits against 96 narrow tiles x 2 splits: narrow tile splits).  The shape-based choice matches
     the forced kernel bit for bit and sampled rows match the oracle."""
-    monkeypatch.delenv("TTL_GEMM_SPLITS", raising=False)
+    gemm_force.set(splits=0)
     b, k, n = (512, 256, 12288) if case == "narrow" else (512, 4096, 6144)
     X = wl.random_bf16((b, k), 310)
     W = wl.random_bf16((k, n), 311, std=0.05)
     outs = {}
     for kern in ("auto", case):
         if kern == "auto":
-            monkeypatch.delenv("TTL_GEMM_KERNEL", raising=False)
+            gemm_force.set(kernel="auto")
         else:
-            monkeypatch.setenv("TTL_GEMM_KERNEL", kern)
+            gemm_force.set(kernel=kern)
             if kern == "narrowsplit":
-                monkeypatch.setenv("TTL_GEMM_SPLITS", "2")
+                gemm_force.set(splits=2)
         outs[kern] = ttl.shard_linear_col(gpu(X), gpu(W), 1, 0)
         torch.cuda.synchronize()
     assert torch.equal(outs["auto"], outs[case])
@@ -370,14 +370,14 @@ MIXED_CASES = [
 
 @pytest.mark.parametrize("b,k,n,silu,cus", MIXED_CASES)
 @pytest.mark.parametrize("layout", ["kn", "nk", "blk"])
-def test_mixed_row_cut(ttl, monkeypatch, capfd, b, k, n, silu, cus, layout):
+def test_mixed_row_cut(ttl, gemm_force, capfd, b, k, n, silu, cus, layout):
     """A launch cut per column strip into 256-row tiles (whole rounds) and 192-row tiles below
     them (one more round), planned for a small CU count so that small shapes take the cut: the
     cut runs (the planner's trace line), its result equals the 256 x 256 tiles' and the 192 x 256
     tiles' bit for bit (same products, same k order), and every element matches the oracle."""
-    monkeypatch.delenv("TTL_GEMM_SPLITS", raising=False)
-    monkeypatch.setenv("TTL_GEMM_TRACE", "1")
-    monkeypatch.setenv("TTL_GEMM_PLAN_CUS", str(cus))
+    gemm_force.set(splits=0)
+    gemm_force.set(trace=True)
+    gemm_force.set(plan_cus=cus)
     X = wl.random_bf16((b, k), 400 + b + k)
     if silu:
         W = wl.random_bf16((k, 2 * n), 401 + k, std=0.05)
@@ -391,7 +391,7 @@ def test_mixed_row_cut(ttl, monkeypatch, capfd, b, k, n, silu, cus, layout):
     capfd.readouterr()
     outs = {}
     for kern in ("mixed", "tiled", "short"):
-        monkeypatch.setenv("TTL_GEMM_KERNEL", kern)
+        gemm_force.set(kernel=kern)
         outs[kern] = ttl.shard_linear_col(gpu(X), Wd_, 1, 0, sp_c, epi, w_layout=lay)
         torch.cuda.synchronize()
     err = capfd.readouterr().err
@@ -405,15 +405,15 @@ def test_mixed_row_cut(ttl, monkeypatch, capfd, b, k, n, silu, cus, layout):
 
 
 @pytest.mark.parametrize("silu", [False, True])
-def test_auto_mixed_row_cut(ttl, monkeypatch, capfd, silu):
+def test_auto_mixed_row_cut(ttl, gemm_force, capfd, silu):
     """At 256 CUs the shape-based choice cuts 2500 x 10240 outputs (400 tiles of 256 x 256: one
     round plus 144 tiles) and 4096 x 3584 SiLU·up outputs (448 tiles: one round plus 192) into
     256-row and 192-row tiles; bit-equal to the 256 x 256 tiles, sampled rows (both sides of every
     strip class's cut) against the oracle; the row GEMM of 4096 x 8192 (512 tiles, two whole
     rounds) is not cut."""
-    monkeypatch.delenv("TTL_GEMM_SPLITS", raising=False)
-    monkeypatch.delenv("TTL_GEMM_PLAN_CUS", raising=False)
-    monkeypatch.setenv("TTL_GEMM_TRACE", "1")
+    gemm_force.set(splits=0)
+    gemm_force.set(plan_cus=0)
+    gemm_force.set(trace=True)
     k = 128
     if silu:
         b, n = 4096, 3584
@@ -430,9 +430,9 @@ def test_auto_mixed_row_cut(ttl, monkeypatch, capfd, silu):
     outs = {}
     for kern in ("auto", "tiled"):
         if kern == "auto":
-            monkeypatch.delenv("TTL_GEMM_KERNEL", raising=False)
+            gemm_force.set(kernel="auto")
         else:
-            monkeypatch.setenv("TTL_GEMM_KERNEL", kern)
+            gemm_force.set(kernel=kern)
         outs[kern] = ttl.shard_linear_col(gpu(X), gpu(W), 1, 0, sp_c, epi)
         torch.cuda.synchronize()
     err = capfd.readouterr().err
@@ -518,12 +518,12 @@ def test_bitwise_deterministic(ttl, gemm_path):
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 65])
 @LAYOUTS
-def test_splitk_split_counts(ttl, monkeypatch, splits, layout):
+def test_splitk_split_counts(ttl, gemm_force, splits, layout):
     """Split-K with a given number of k ranges, k tail of 8 (4104 = 64 * 64 + 8), ragged M and N.
 
     65 splits puts one k-tile in each range, the last one holding only the 8-wide tail."""
-    monkeypatch.setenv("TTL_GEMM_KERNEL", "splitk")
-    monkeypatch.setenv("TTL_GEMM_SPLITS", str(splits))
+    gemm_force.set(kernel="splitk")
+    gemm_force.set(splits=splits)
     b, k = 37, 4104
     _col_case(ttl, b, k, oracle.merged_gate_up_split(200, 1), ttl.merged_gate_up_split(200, 1), 1,
               seed=100 + splits, epi=ttl.EPI_SILU_MUL, layout=layout)
@@ -539,11 +539,11 @@ def test_splitk_split_counts(ttl, monkeypatch, splits, layout):
                      f"split-K row splits={splits} r={r} {layout}")
 
 
-def test_splitk_repeated_launches_reuse_workspace(ttl, monkeypatch):
+def test_splitk_repeated_launches_reuse_workspace(ttl, gemm_force):
     """Back-to-back split-K launches of different sizes share (and grow) the library's workspace;
     a repeated shape must reproduce its first result bit for bit."""
-    monkeypatch.setenv("TTL_GEMM_KERNEL", "splitk")
-    monkeypatch.delenv("TTL_GEMM_SPLITS", raising=False)
+    gemm_force.set(kernel="splitk")
+    gemm_force.set(splits=0)
     shapes = [(64, 8192, 1024), (1, 4096, 3584), (64, 8192, 1024), (200, 2048, 4096), (1, 4096, 3584)]
     outs = {}
     for i, (b, k, n) in enumerate(shapes):
@@ -559,6 +559,74 @@ def test_splitk_repeated_launches_reuse_workspace(ttl, monkeypatch):
             rows = [0, b - 1]
             ref = oracle.col_shard(f64(Xs[rows]), f64(Ws), oracle.plain_split(n, 1), 1, 0)
             assert_close(from_gpu(Y[rows]), ref, f"repeated split-K {key}")
+
+
+@pytest.mark.parametrize("kern", ["splitk", "tilesplit"])
+def test_splitk_on_two_streams_at_once(ttl, gemm_force, kern):
+    """Split-K launches on two streams at once write their fp32 partials to separate workspaces (one
+    per stream): every result equals the same call made alone on one stream, bit for bit.  The two
+    shapes need different workspace sizes, and their launches are interleaved across the streams so
+    that they overlap on the device."""
+    gemm_force.set(kernel=kern, splits=8)
+    cases = [((64, 8192), (8192, 2048)), ((128, 4096), (4096, 4096))] if kern == "splitk" else \
+            [((512, 4096), (4096, 1024)), ((768, 2048), (2048, 2048))]
+    ops = []
+    for i, (xs, ws) in enumerate(cases):
+        X = gpu(wl.random_bf16(xs, 170 + i))
+        W = gpu(wl.random_bf16(ws, 172 + i, std=0.05))
+        ops.append((X, W))
+    main = torch.cuda.current_stream()
+    alone = []
+    for X, W in ops:
+        alone.append(ttl.shard_linear_col(X, W, 1, 0, stream=main))
+        torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(main)
+    reps = 6
+    outs = [[torch.empty_like(alone[i]) for _ in range(reps)] for i in range(2)]
+    for rep in range(reps):
+        for i, (X, W) in enumerate(ops):
+            ttl.shard_linear_col(X, W, 1, 0, Y=outs[i][rep], stream=streams[i])
+    torch.cuda.synchronize()
+    for i in range(2):
+        for rep in range(reps):
+            assert torch.equal(outs[i][rep], alone[i]), f"stream {i} launch {rep} differs from the lone call"
+    rows = [0, ops[0][0].shape[0] - 1]
+    ref = oracle.col_shard(f64(ops[0][0][rows].cpu()), f64(ops[0][1].cpu()),
+                           oracle.plain_split(ops[0][1].shape[1], 1), 1, 0)
+    assert_close(from_gpu(alone[0][rows]), ref, f"{kern} two-stream case")
+
+
+def test_capture_needing_a_new_workspace_is_refused(ttl, gemm_force):
+    """A split-K call captured on a stream that has no workspace yet fails with TTL_ERR_HIP before
+    anything is enqueued (a buffer cannot be allocated during capture); after one eager call on
+    that stream the same capture succeeds and its replay matches the eager result."""
+    gemm_force.set(kernel="splitk", splits=4)
+    X = gpu(wl.random_bf16((48, 2048), 180))
+    W = gpu(wl.random_bf16((2048, 1024), 181, std=0.05))
+    Y = torch.empty((48, 1024), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(ttl.TTLError) as e:
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                ttl.shard_linear_col(X, W, 1, 0, Y=Y)
+    assert e.value.status == ttl.ERR_HIP
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        want = ttl.shard_linear_col(X, W, 1, 0).clone()
+    torch.cuda.synchronize()
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g2, stream=s):
+            ttl.shard_linear_col(X, W, 1, 0, Y=Y)
+    for _ in range(2):
+        Y.zero_()
+        g2.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, want)
 
 
 def test_tiny_mlp_chain_all_ranks(ttl):
@@ -581,8 +649,8 @@ def test_tiny_mlp_chain_all_ranks(ttl):
     for r in range(w.t):
         assert_close(from_gpu(acts[r]), ref_acts[r], f"tiny act r={r}")
         assert_close(from_gpu(P[r]), ref_P[r], f"tiny partial r={r}")
-    assert_close(from_gpu(rout), h, "tiny residual_out")
-    assert_close(from_gpu(y), yref, "tiny y")
+    assert_close(from_gpu(rout), h, "tiny residual_out", literal=True)
+    assert_close(from_gpu(y), yref, "tiny y", literal=True)
     # the unrounded float64 chain (no bf16 storage between steps) is within tolerance too
     _, P64, _, _ = oracle.mlp_rank_chain(o["X"], o["Wgu"], o["Wd"], w.t, w.intermediate, store_bf16=False)
     h64, y64 = oracle.reduce_partials_rmsnorm(P64, o["R"], o["gamma"], w.eps)
@@ -647,8 +715,8 @@ def test_reduce_scatter_rmsnorm(ttl, t, b, n, with_residual):
         assert rout.shape == (rows, n) and y.shape == (rows, n)
         Rr = Ro[r * rows:(r + 1) * rows] if with_residual else None
         h, yref = oracle.reduce_scatter_partials_rmsnorm(f64(P), Rr, f64(gamma), 1e-5, t, r)
-        assert_close(from_gpu(rout), h, f"reduce-scatter residual_out t={t} b={b} n={n} r={r}")
-        assert_close(from_gpu(y), yref, f"reduce-scatter y t={t} b={b} n={n} r={r}")
+        assert_close(from_gpu(rout), h, f"reduce-scatter residual_out t={t} b={b} n={n} r={r}", literal=True)
+        assert_close(from_gpu(y), yref, f"reduce-scatter y t={t} b={b} n={n} r={r}", literal=True)
 
 
 @pytest.mark.parametrize("t,b,n,with_residual", [(8, 4096, 8192, True), (8, 64, 8192, True),
@@ -671,8 +739,8 @@ def test_reduce_over_peer_buffers(ttl, t, b, n, with_residual):
     sample = torch.as_tensor(np.unique(np.r_[0:2, b // 2, b - 1]), device="cuda")
     Ro = from_gpu(R[sample]) if with_residual else None
     h, yref = oracle.reduce_partials_rmsnorm(from_gpu(P[:, sample]), Ro, from_gpu(gamma), 1e-5)
-    assert_close(from_gpu(rout[sample]), h, f"peers residual_out t={t} b={b} n={n}")
-    assert_close(from_gpu(y[sample]), yref, f"peers y t={t} b={b} n={n}")
+    assert_close(from_gpu(rout[sample]), h, f"peers residual_out t={t} b={b} n={n}", literal=True)
+    assert_close(from_gpu(y[sample]), yref, f"peers y t={t} b={b} n={n}", literal=True)
     if b % t == 0:
         rows = b // t
         for r in range(t):
@@ -694,21 +762,21 @@ def test_reduce_scatter_rejects_ragged_rows(ttl):
 # ---- stream capture -------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("b", [64, 600, 1000])
-def test_graph_replay_matches_eager(ttl, monkeypatch, capfd, b):
+def test_graph_replay_matches_eager(ttl, gemm_force, capfd, b):
     """The rank chain (gate_up + SiLU·up, down, reduce + RMSNorm over all ranks) captured into a HIP
     graph and replayed three times, with eager work between the replays (including a split-K call
     large enough to replace the library's workspace), reproduces the eager outputs bit for bit.
     b = 64 runs the split-K kernel with its workspace, b = 600 the 256 x 256 tiles, b = 1000 the
     256-row / 192-row cut (planned for 10 CUs: both GEMMs are 16 tiles of 256 x 256, one round
     plus 6 tiles, cut into 10 tiles of 256 rows and 10 of 192 rows)."""
-    monkeypatch.delenv("TTL_GEMM_KERNEL", raising=False)
-    monkeypatch.delenv("TTL_GEMM_SPLITS", raising=False)
+    gemm_force.set(kernel="auto")
+    gemm_force.set(splits=0)
     if b == 600:
-        monkeypatch.setenv("TTL_GEMM_KERNEL", "tiled")
+        gemm_force.set(kernel="tiled")
     if b == 1000:
-        monkeypatch.setenv("TTL_GEMM_KERNEL", "mixed")
-        monkeypatch.setenv("TTL_GEMM_PLAN_CUS", "10")
-        monkeypatch.setenv("TTL_GEMM_TRACE", "1")
+        gemm_force.set(kernel="mixed")
+        gemm_force.set(plan_cus=10)
+        gemm_force.set(trace=True)
     t, H, I = 4, 1024, 2048
     X = gpu(wl.random_bf16((b, H), 160))
     R = gpu(wl.random_bf16((b, H), 161))
@@ -728,7 +796,7 @@ def test_graph_replay_matches_eager(ttl, monkeypatch, capfd, b):
         ttl.reduce_partials_rmsnorm(P, gamma, 1e-5, R, residual_out=rout, Y=y)
 
     capfd.readouterr()
-    chain()  # eager; also allocates the workspace before capture
+    chain()  # eager, on the current stream
     torch.cuda.synchronize()
     if b == 1000:
         assert capfd.readouterr().err.count("ttl gemm cut") == 2 * t  # both GEMMs of every rank
@@ -736,6 +804,9 @@ def test_graph_replay_matches_eager(ttl, monkeypatch, capfd, b):
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        chain()  # eager on the capturing stream: allocates its split-K workspace before capture
+    torch.cuda.synchronize()
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
             chain()
@@ -750,11 +821,13 @@ def test_graph_replay_matches_eager(ttl, monkeypatch, capfd, b):
         torch.cuda.synchronize()
         for got, exp in zip((act, P, rout, y), want):
             assert torch.equal(got, exp), f"replay {rep} differs from the eager run"
-        # eager work between replays: a split-K call whose workspace need (64 splits of 32 x 16384
-        # fp32 = 134 MB) exceeds every earlier one, so the library replaces its buffer
-        with monkeypatch.context() as m:
-            m.setenv("TTL_GEMM_KERNEL", "splitk")
-            m.setenv("TTL_GEMM_SPLITS", str(64 + rep))
+        # eager work between replays on the capturing stream: a split-K call whose workspace need
+        # (64 splits of 32 x 16384 fp32 = 134 MB) exceeds every earlier one, so the library
+        # replaces that stream's buffer (the captured graph keeps the one it recorded)
+        saved = dict(gemm_force.state)
+        gemm_force.set(kernel="splitk", splits=64 + rep)
+        with torch.cuda.stream(s):
             Ybig = ttl.shard_linear_col(Xbig, Wbig, 1, 0)
+        gemm_force.set(**saved)
         torch.cuda.synchronize()
         assert torch.isfinite(Ybig.float()).all()
