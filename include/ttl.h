@@ -149,6 +149,31 @@ ttl_status shard_linear_col_stored(const uint16_t* X, int64_t b, int64_t k,
                                    void* stream);
 
 /*
+ * shard_linear_col_noalloc — shard_linear_col_stored for callers that cannot allocate device memory:
+ * code recorded under HIP graph capture, tight serving loops, and harnesses that forbid allocation
+ * after start-up.  Same arguments, same kernels and bit for bit the same results as
+ * shard_linear_col_stored; the only difference is where split-K launches (decode batches, few
+ * tiles with a long k) keep their fp32 partial sums: a 64-MiB array inside the library's device
+ * code (TTL_NOALLOC_SCRATCH_BYTES), one per GPU, held until the process ends, instead of the
+ * per-stream buffers the other entry points allocate on first use.  The call allocates and frees
+ * nothing (the array's device address is looked up on the first call on each GPU).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's partials (nothing in
+ * it needs to start at zero: each call writes every partial it reads): calls whose work overlaps
+ * in time on one GPU (different streams) race and must be serialised, e.g. on one stream.
+ * Errors: as shard_linear_col_stored; a call whose split-K partials would need more than
+ * TTL_NOALLOC_SCRATCH_BYTES -> UNSUPPORTED, before anything is enqueued; the array's address not
+ * obtainable -> HIP.
+ */
+#define TTL_NOALLOC_SCRATCH_BYTES (64 * 1024 * 1024)
+ttl_status shard_linear_col_noalloc(const uint16_t* X, int64_t b, int64_t k,
+                                    const uint16_t* W, int64_t n, ttl_weight_layout w_layout,
+                                    int32_t t, int32_t rank,
+                                    const ttl_col_split* split,
+                                    ttl_epilogue epi,
+                                    uint16_t* Y,
+                                    void* stream);
+
+/*
  * shard_linear_col_gathered — ColumnParallelLinear forward with gather_output=True (vLLM
  * walkthrough, sections "ColumnParallelLinear" and "all-gather"): the rank's output is placed in its
  * block of the all-gathered tensor, the concatenation of the t rank outputs along the last dimension

@@ -73,6 +73,38 @@ hipError_t get_workspace(size_t bytes, hipStream_t stream, void** out) {
   return hipSuccess;
 }
 
+// One call's launch context: its stream, where split-K partials go, and whether anything launches.
+// A dry pass (dry = true) walks the same plan, launches nothing and allocates nothing, and records
+// in `need` the largest workspace any of the call's launches would use; a call with a fixed
+// workspace (the caller's or the library's static scratch) uses that buffer for every split-K
+// launch instead of the per-stream buffers.
+struct Ctx {
+  hipStream_t stream = nullptr;
+  void* fixed_ws = nullptr;
+  size_t fixed_bytes = 0;
+  bool dry = false;
+  size_t need = 0;
+};
+
+hipError_t workspace(Ctx& c, size_t bytes, void** out) {
+  c.need = bytes > c.need ? bytes : c.need;
+  *out = nullptr;
+  if (c.dry) return hipSuccess;
+  if (c.fixed_ws != nullptr) {
+    if (bytes > c.fixed_bytes) return hipErrorInvalidValue;  // callers check the dry pass first
+    *out = c.fixed_ws;
+    return hipSuccess;
+  }
+  return get_workspace(bytes, c.stream, out);
+}
+
+hipError_t run_bigwave(Ctx& c, const GemmParams& p) { return c.dry ? hipSuccess : launch_gemm_bigwave(p, c.stream); }
+hipError_t run_tiled(Ctx& c, const GemmParams& p) { return c.dry ? hipSuccess : launch_gemm_tiled(p, c.stream); }
+hipError_t run_skinny(Ctx& c, const GemmParams& p, int mb) {
+  return c.dry ? hipSuccess : launch_gemm_skinny(p, mb, c.stream);
+}
+hipError_t run_finalize(Ctx& c, const GemmParams& p) { return c.dry ? hipSuccess : launch_splitk_finalize(p, c.stream); }
+
 // Test and measurement overrides (see ttl_set_gemm_override).
 std::atomic<int> g_force_kernel{0}, g_force_splits{0}, g_force_plan_cus{0}, g_trace{0};
 
@@ -102,22 +134,22 @@ int forced_kernel() { return g_force_kernel.load(std::memory_order_relaxed); }
 int64_t forced_splits() { return g_force_splits.load(std::memory_order_relaxed); }
 
 // 256 x 256 tiles over all of p: the four-wave kernel where it applies, unless force == 3.
-hipError_t launch_tiles(GemmParams& p, int force, hipStream_t stream) {
+hipError_t launch_tiles(GemmParams& p, int force, Ctx& c) {
   p.tiles_m = (int32_t)cdiv(p.M, gemm_tile_rows());
   p.tiles_n = (int32_t)cdiv(p.N, gemm_tile_cols(p.mode));
   p.splits = 1;
   p.narrow = 0;
-  if (force != 3 && gemm_bigwave_supports(p)) return launch_gemm_bigwave(p, stream);
-  return launch_gemm_tiled(p, stream);
+  if (force != 3 && gemm_bigwave_supports(p)) return run_bigwave(c, p);
+  return run_tiled(c, p);
 }
 
 // 256 x 128 tiles of the four-wave kernel over all of p (K a multiple of 64).
-hipError_t launch_narrow(GemmParams& p, hipStream_t stream) {
+hipError_t launch_narrow(GemmParams& p, Ctx& c) {
   p.tiles_m = (int32_t)cdiv(p.M, gemm_tile_rows());
   p.tiles_n = (int32_t)cdiv(p.N, gemm_bigwave_tile_cols(p.mode, true));
   p.splits = 1;
   p.narrow = 1;
-  return launch_gemm_bigwave(p, stream);
+  return run_bigwave(c, p);
 }
 
 // Row cut of one launch into 256-row and 192-row tiles (four-wave kernel, 256 weight columns per
@@ -267,7 +299,7 @@ void build_mixed(const GemmParams& p, const MixedRows& m, int64_t tn, int64_t cu
   }
 }
 
-hipError_t launch_mixed(GemmParams& p, const MixedRows& m, int64_t cus, hipStream_t stream) {
+hipError_t launch_mixed(GemmParams& p, const MixedRows& m, int64_t cus, Ctx& c) {
   const int64_t tn = cdiv(p.N, gemm_tile_cols(p.mode));
   GemmParams q[2];
   bool cached = false;
@@ -291,7 +323,7 @@ hipError_t launch_mixed(GemmParams& p, const MixedRows& m, int64_t cus, hipStrea
     if (g_plans.size() >= kPlanCache) g_plans.pop_back();
     g_plans.insert(g_plans.begin(), {p.M, p.N, p.K, cus, p.mode, {q[0], q[1]}});
   }
-  if (g_trace.load(std::memory_order_relaxed))
+  if (!c.dry && g_trace.load(std::memory_order_relaxed))
     std::fprintf(stderr, "ttl gemm cut: M=%d N=%d K=%d strips [0,%lld) %lld x 256 + %lld x 192, "
                  "[%lld,%lld) %lld x 256 + %lld x 192, groups %d/%d and %d/%d\n", p.M, p.N, p.K,
                  (long long)m.S, (long long)m.a[0], (long long)m.b[0], (long long)m.S, (long long)tn,
@@ -313,14 +345,14 @@ hipError_t launch_mixed(GemmParams& p, const MixedRows& m, int64_t cus, hipStrea
       t.rect_tmc[r] = q[pass].rect_tmc[r];
       t.rect_group[r] = q[pass].rect_group[r];
     }
-    const hipError_t e = launch_gemm_bigwave(t, stream);
+    const hipError_t e = run_bigwave(c, t);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
 // 192 x 256 tiles of the four-wave kernel over all of p, as one tile set.
-hipError_t launch_short(GemmParams& p, hipStream_t stream) {
+hipError_t launch_short(GemmParams& p, Ctx& c) {
   GemmParams q = p;
   q.splits = 1;
   q.narrow = 0;
@@ -331,12 +363,12 @@ hipError_t launch_short(GemmParams& p, hipStream_t stream) {
   q.rect_tnc[0] = (int32_t)cdiv(p.N, gemm_tile_cols(p.mode));
   q.rect_row0[0] = 0;
   q.rect_tmc[0] = (int32_t)cdiv(p.M, 192);
-  return launch_gemm_bigwave(q, stream);
+  return run_bigwave(c, q);
 }
 
 // 256 x 256 (or, narrow, 256 x 128) tiles of the four-wave kernel cut into `splits` k ranges
 // (plain mode; SiLU·up as the gate columns then the up columns), then the split-K finalize kernel.
-hipError_t launch_tiles_splitk(GemmParams& p, int64_t splits, bool narrow, hipStream_t stream) {
+hipError_t launch_tiles_splitk(GemmParams& p, int64_t splits, bool narrow, Ctx& c) {
   GemmParams q = p.mode == 1 ? silu_as_plain_halves(p) : p;
   q.narrow = narrow ? 1 : 0;
   q.tiles_m = (int32_t)cdiv(q.M, gemm_tile_rows());
@@ -345,23 +377,23 @@ hipError_t launch_tiles_splitk(GemmParams& p, int64_t splits, bool narrow, hipSt
   if (splits > nk) splits = nk;
   const int64_t kt_per = cdiv(nk, splits);
   splits = cdiv(nk, kt_per);  // every split gets at least one k-tile
-  if (splits < 2) return narrow ? launch_narrow(p, stream) : launch_tiles(p, 0, stream);
+  if (splits < 2) return narrow ? launch_narrow(p, c) : launch_tiles(p, 0, c);
   q.splits = (int32_t)splits;
   q.kt_per_split = (int32_t)kt_per;
   q.ws_ld = (int64_t)q.tiles_n * gemm_bigwave_tile_cols(0, narrow);
   void* base = nullptr;
-  hipError_t e = get_workspace((size_t)splits * q.M * q.ws_ld * sizeof(float), stream, &base);
+  hipError_t e = workspace(c, (size_t)splits * q.M * q.ws_ld * sizeof(float), &base);
   if (e != hipSuccess) return e;
   q.ws = static_cast<float*>(base);
-  if ((e = launch_gemm_bigwave(q, stream)) != hipSuccess) return e;
+  if ((e = run_bigwave(c, q)) != hipSuccess) return e;
   GemmParams f = p;
   f.ws = q.ws;
   f.ws_ld = q.ws_ld;
   f.splits = q.splits;
-  return launch_splitk_finalize(f, stream);
+  return run_finalize(c, f);
 }
 
-hipError_t launch_splitk(GemmParams& p, hipStream_t stream) {
+hipError_t launch_splitk(GemmParams& p, Ctx& c) {
   const int mb = p.M <= 32 ? 1 : (p.M <= 64 ? 2 : 4);
   const int64_t tiles_m = cdiv(p.M, 32 * mb);
   const int64_t tiles_n = cdiv(p.N, p.mode == 1 ? kSkinnyCols / 2 : kSkinnyCols);
@@ -383,11 +415,86 @@ hipError_t launch_splitk(GemmParams& p, hipStream_t stream) {
   p.ws = nullptr;
   if (splits > 1) {
     void* base = nullptr;
-    const hipError_t e = get_workspace((size_t)splits * p.M * p.ws_ld * sizeof(float), stream, &base);
+    const hipError_t e = workspace(c, (size_t)splits * p.M * p.ws_ld * sizeof(float), &base);
     if (e != hipSuccess) return e;
     p.ws = static_cast<float*>(base);
   }
-  return launch_gemm_skinny(p, mb, stream);
+  return run_skinny(c, p, mb);
+}
+
+// The kernel choice for one call (see the notes at the top), launched through the call's context.
+hipError_t plan_and_launch(GemmParams& p, Ctx& c) {
+  const int force = forced_kernel();
+  const int64_t n_cu = device_cus();
+  const int64_t min_tiled = n_cu * 3 / 4;  // 256 x 256 tiles when they occupy >= 3/4 of the CUs
+  if (force == 1 || force == 3) return launch_tiles(p, force, c);
+  if (force == 7 && gemm_bigwave_supports(p)) return launch_short(p, c);
+  if (force == 8 && gemm_bigwave_supports(p)) {
+    MixedRows m;
+    const int64_t pc = g_force_plan_cus.load(std::memory_order_relaxed);
+    const int64_t cus = pc > 0 ? pc : device_cus();
+    if (plan_mixed_rows(p.M, cdiv(p.N, gemm_tile_cols(p.mode)), cus, m)) return launch_mixed(p, m, cus, c);
+    return launch_tiles(p, 0, c);
+  }
+  if (force == 5) return gemm_bigwave_supports(p) ? launch_narrow(p, c) : launch_tiles(p, 3, c);
+  if (force == 2 || ((force == 4 || force == 6) && !gemm_bigwave_supports(p))) return launch_splitk(p, c);
+  const int64_t tiled_m = cdiv(p.M, gemm_tile_rows());
+  const int64_t tiled_n = cdiv(p.N, gemm_tile_cols(p.mode));
+  const int64_t tiles = tiled_m * tiled_n;
+  const int64_t narrow_tiles = tiled_m * cdiv(p.N, gemm_bigwave_tile_cols(p.mode, true));
+  if (force == 4 || force == 6) {
+    const int64_t fs = forced_splits();
+    const int64_t auto_splits = n_cu / (force == 4 ? tiles : narrow_tiles);
+    return launch_tiles_splitk(p, fs > 0 ? fs : (auto_splits > 2 ? auto_splits : 2), force == 6, c);
+  }
+  if (tiles < min_tiled) {
+    // Few 256 x 256 tiles.  With many rows and a long k, 256 x 256 tiles cut along k into about
+    // one workgroup per CU keep the matrix cores busier than the split-K kernel's 128-row tiles;
+    // each split takes at least kMinKTilesPerTileSplit k-tiles, as the fp32 partial tiles cost HBM
+    // traffic (k = 1024 with 2 splits measured slower than the split-K kernel).  Decode-sized
+    // launches stay on the split-K kernel, which is built to stream the weight.
+    // Where 256 x 128 tiles fill at least as much of the chip in one round, they run whole.
+    if (p.M >= kTileSplitMinRows && gemm_bigwave_supports(p) && narrow_tiles >= min_tiled &&
+        narrow_tiles <= n_cu)
+      return launch_narrow(p, c);
+    // Otherwise tiles cut along k: 256 x 256 tiles, or 256 x 128 tiles where those occupy at
+    // least as many CUs (then with half the partial bytes per output).
+    const int64_t by_k = (p.K / 64) / kMinKTilesPerTileSplit;
+    const int64_t splits = n_cu / tiles < by_k ? n_cu / tiles : by_k;
+    const int64_t nsplits = n_cu / narrow_tiles < by_k ? n_cu / narrow_tiles : by_k;
+    if (p.M >= kTileSplitMinRows && gemm_bigwave_supports(p)) {
+      if (nsplits >= 2 && narrow_tiles * nsplits >= tiles * splits)
+        return launch_tiles_splitk(p, nsplits, true, c);
+      if (splits >= 2) return launch_tiles_splitk(p, splits, false, c);
+    }
+    return launch_splitk(p, c);
+  }
+  // Whole rounds of one tile per CU plus a last round more than half full: 256-row tiles for the
+  // whole rounds and 192-row tiles for the last one, which then takes 3/4 of a round's time.
+  const int64_t rounds = tiles / n_cu, rem = tiles % n_cu;
+  if (gemm_bigwave_supports(p)) {
+    MixedRows m;
+    if (plan_mixed_rows(p.M, tiled_n, n_cu, m)) return launch_mixed(p, m, n_cu, c);
+  }
+  // Whole rounds plus a short last round (at most half the CUs): that round would take a whole
+  // tile's time with most of the chip idle.  The row-tiles that fill the whole rounds go to the
+  // tiled kernel, the remaining rows (a few row-tiles) to the split-K kernel, which spreads them
+  // over all CUs.
+  if (rounds >= 1 && rem > 0 && 2 * rem <= n_cu) {
+    const int64_t head_row_tiles = rounds * n_cu / tiled_n;
+    if (head_row_tiles >= 1 && head_row_tiles < tiled_m) {
+      GemmParams head = p;
+      head.M = (int32_t)(head_row_tiles * gemm_tile_rows());
+      hipError_t e = launch_tiles(head, 0, c);
+      if (e != hipSuccess) return e;
+      GemmParams tail = p;
+      tail.A = p.A + (int64_t)head.M * p.lda;
+      tail.C = p.C + (int64_t)head.M * p.ldc;
+      tail.M = p.M - head.M;
+      return launch_splitk(tail, c);
+    }
+  }
+  return launch_tiles(p, 0, c);
 }
 
 }  // namespace
@@ -400,77 +507,25 @@ void set_gemm_override(int kernel, int splits, int plan_cus, bool trace) {
 }
 
 hipError_t launch_gemm(GemmParams& p, hipStream_t stream) {
-  const int force = forced_kernel();
-  const int64_t n_cu = device_cus();
-  const int64_t min_tiled = n_cu * 3 / 4;  // 256 x 256 tiles when they occupy >= 3/4 of the CUs
-  if (force == 1 || force == 3) return launch_tiles(p, force, stream);
-  if (force == 7 && gemm_bigwave_supports(p)) return launch_short(p, stream);
-  if (force == 8 && gemm_bigwave_supports(p)) {
-    MixedRows m;
-    const int64_t pc = g_force_plan_cus.load(std::memory_order_relaxed);
-    const int64_t cus = pc > 0 ? pc : device_cus();
-    if (plan_mixed_rows(p.M, cdiv(p.N, gemm_tile_cols(p.mode)), cus, m)) return launch_mixed(p, m, cus, stream);
-    return launch_tiles(p, 0, stream);
-  }
-  if (force == 5) return gemm_bigwave_supports(p) ? launch_narrow(p, stream) : launch_tiles(p, 3, stream);
-  if (force == 2 || ((force == 4 || force == 6) && !gemm_bigwave_supports(p))) return launch_splitk(p, stream);
-  const int64_t tiled_m = cdiv(p.M, gemm_tile_rows());
-  const int64_t tiled_n = cdiv(p.N, gemm_tile_cols(p.mode));
-  const int64_t tiles = tiled_m * tiled_n;
-  const int64_t narrow_tiles = tiled_m * cdiv(p.N, gemm_bigwave_tile_cols(p.mode, true));
-  if (force == 4 || force == 6) {
-    const int64_t fs = forced_splits();
-    const int64_t auto_splits = n_cu / (force == 4 ? tiles : narrow_tiles);
-    return launch_tiles_splitk(p, fs > 0 ? fs : (auto_splits > 2 ? auto_splits : 2), force == 6, stream);
-  }
-  if (tiles < min_tiled) {
-    // Few 256 x 256 tiles.  With many rows and a long k, 256 x 256 tiles cut along k into about
-    // one workgroup per CU keep the matrix cores busier than the split-K kernel's 128-row tiles;
-    // each split takes at least kMinKTilesPerTileSplit k-tiles, as the fp32 partial tiles cost HBM
-    // traffic (k = 1024 with 2 splits measured slower than the split-K kernel).  Decode-sized
-    // launches stay on the split-K kernel, which is built to stream the weight.
-    // Where 256 x 128 tiles fill at least as much of the chip in one round, they run whole.
-    if (p.M >= kTileSplitMinRows && gemm_bigwave_supports(p) && narrow_tiles >= min_tiled &&
-        narrow_tiles <= n_cu)
-      return launch_narrow(p, stream);
-    // Otherwise tiles cut along k: 256 x 256 tiles, or 256 x 128 tiles where those occupy at
-    // least as many CUs (then with half the partial bytes per output).
-    const int64_t by_k = (p.K / 64) / kMinKTilesPerTileSplit;
-    const int64_t splits = n_cu / tiles < by_k ? n_cu / tiles : by_k;
-    const int64_t nsplits = n_cu / narrow_tiles < by_k ? n_cu / narrow_tiles : by_k;
-    if (p.M >= kTileSplitMinRows && gemm_bigwave_supports(p)) {
-      if (nsplits >= 2 && narrow_tiles * nsplits >= tiles * splits)
-        return launch_tiles_splitk(p, nsplits, true, stream);
-      if (splits >= 2) return launch_tiles_splitk(p, splits, false, stream);
-    }
-    return launch_splitk(p, stream);
-  }
-  // Whole rounds of one tile per CU plus a last round more than half full: 256-row tiles for the
-  // whole rounds and 192-row tiles for the last one, which then takes 3/4 of a round's time.
-  const int64_t rounds = tiles / n_cu, rem = tiles % n_cu;
-  if (gemm_bigwave_supports(p)) {
-    MixedRows m;
-    if (plan_mixed_rows(p.M, tiled_n, n_cu, m)) return launch_mixed(p, m, n_cu, stream);
-  }
-  // Whole rounds plus a short last round (at most half the CUs): that round would take a whole
-  // tile's time with most of the chip idle.  The row-tiles that fill the whole rounds go to the
-  // tiled kernel, the remaining rows (a few row-tiles) to the split-K kernel, which spreads them
-  // over all CUs.
-  if (rounds >= 1 && rem > 0 && 2 * rem <= n_cu) {
-    const int64_t head_row_tiles = rounds * n_cu / tiled_n;
-    if (head_row_tiles >= 1 && head_row_tiles < tiled_m) {
-      GemmParams head = p;
-      head.M = (int32_t)(head_row_tiles * gemm_tile_rows());
-      hipError_t e = launch_tiles(head, 0, stream);
-      if (e != hipSuccess) return e;
-      GemmParams tail = p;
-      tail.A = p.A + (int64_t)head.M * p.lda;
-      tail.C = p.C + (int64_t)head.M * p.ldc;
-      tail.M = p.M - head.M;
-      return launch_splitk(tail, stream);
-    }
-  }
-  return launch_tiles(p, 0, stream);
+  Ctx c;
+  c.stream = stream;
+  return plan_and_launch(p, c);
+}
+
+size_t gemm_workspace_bytes(const GemmParams& p) {
+  GemmParams q = p;
+  Ctx c;
+  c.dry = true;
+  plan_and_launch(q, c);
+  return c.need;
+}
+
+hipError_t launch_gemm_fixed_workspace(GemmParams& p, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Ctx c;
+  c.stream = stream;
+  c.fixed_ws = ws;
+  c.fixed_bytes = ws_bytes;
+  return plan_and_launch(p, c);
 }
 
 }  // namespace ttl

@@ -68,6 +68,14 @@ inline GemmParams silu_as_plain_halves(const GemmParams& p) {
 // fields of p.  May allocate the split-K workspace of (device, stream) on first use.
 hipError_t launch_gemm(GemmParams& p, hipStream_t stream);
 
+// Bytes of split-K workspace launch_gemm would use for p (0 when no launch of its plan splits k):
+// the plan walked without launching or allocating anything.
+size_t gemm_workspace_bytes(const GemmParams& p);
+
+// launch_gemm with every split-K launch writing its partials to `ws` (ws_bytes, at least
+// gemm_workspace_bytes(p)) instead of the library's per-stream buffers; allocates nothing.
+hipError_t launch_gemm_fixed_workspace(GemmParams& p, void* ws, size_t ws_bytes, hipStream_t stream);
+
 // Process-wide test and measurement overrides of launch_gemm's choice (ttl_set_gemm_override):
 // kernel family (0 = by shape), split count (0 = by shape), CUs the row cut is planned for (0 =
 // the device's), and a trace of each cut on stderr.

@@ -4,14 +4,43 @@
 // success it enqueues its kernel on the caller's stream and returns without waiting.
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "kernels.h"
 #include "ttl.h"
 
+// Split-K partial sums of shard_linear_col_noalloc: this array, not a buffer the library allocates.
+// Each GPU the library runs on holds its own copy until the process ends.  In host code the name
+// stands for a host-side placeholder, not the device memory: the device address is looked up once
+// per device (scratch_address below) and only that address reaches a kernel.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static_assert(kScratchBytes == (size_t)TTL_NOALLOC_SCRATCH_BYTES, "the header states the scratch size");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 thread_local std::string g_last_error;
+
+// Device address of `scratch` on the current device, looked up on the first call on that device.
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 ttl_status fail(ttl_status status, const char* fmt, ...) {
   char buf[512];
@@ -346,6 +375,34 @@ ttl_status shard_linear_col(const uint16_t* X, int64_t b, int64_t k, const uint1
                             int32_t t, int32_t rank, const ttl_col_split* split, ttl_epilogue epi,
                             uint16_t* Y, void* stream) {
   return col_entry("shard_linear_col", X, b, k, W, n, TTL_W_KN, t, rank, split, epi, Y, stream);
+}
+
+ttl_status shard_linear_col_noalloc(const uint16_t* X, int64_t b, int64_t k, const uint16_t* W, int64_t n,
+                                    ttl_weight_layout w_layout, int32_t t, int32_t rank,
+                                    const ttl_col_split* split, ttl_epilogue epi, uint16_t* Y,
+                                    void* stream) {
+  static const char* who = "shard_linear_col_noalloc";
+  ttl::GemmParams p;
+  int64_t width = 0;
+  const ttl_status st = col_setup(who, X, b, k, W, n, w_layout, t, rank, split, epi, Y, p, width);
+  if (st != TTL_OK) return st;
+  if (output_overlaps(Y, b * width, X, b * k, W, k * n))
+    return fail(TTL_ERR_UNSUPPORTED, "%s: Y must not overlap X or W", who);
+  p.C = Y;
+  p.ldc = width;
+  // The plan is walked once without launching to size its split-K partials: a call that needs more
+  // than the static scratch is refused before anything is enqueued.
+  const size_t need = ttl::gemm_workspace_bytes(p);
+  if (need > kScratchBytes)
+    return fail(TTL_ERR_UNSUPPORTED,
+                "%s: this call's split-K partials need %zu bytes, more than the %zu-byte static scratch "
+                "(shard_linear_col_stored serves it with an allocated workspace)", who, need, kScratchBytes);
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess)
+    return fail(TTL_ERR_HIP, "%s: no device address for the static scratch: %s", who, hipGetErrorString(e));
+  return launch_status(ttl::launch_gemm_fixed_workspace(p, ws, kScratchBytes, static_cast<hipStream_t>(stream)),
+                       who);
 }
 
 ttl_status shard_linear_col_gathered(const uint16_t* X, int64_t b, int64_t k, const uint16_t* W,

@@ -33,7 +33,7 @@ W_NK = 1  # weight stored transposed, [n][k] (row stride k), as PyTorch-style Li
 W_BLOCKED = 2  # [k][n] in 64 x 128 blocks, 128-column strips contiguous (see pack_weight_blocked)
 MAX_SEGMENTS = 3
 MAX_PEERS = 16
-EXPORTED = ("shard_linear_col", "shard_linear_col_stored", "shard_linear_col_gathered",
+EXPORTED = ("shard_linear_col", "shard_linear_col_stored", "shard_linear_col_noalloc", "shard_linear_col_gathered",
             "shard_linear_row", "shard_linear_row_stored",
             "reduce_partials_rmsnorm", "reduce_scatter_partials_rmsnorm", "reduce_partials_rmsnorm_peers",
             "ttl_pack_weight_blocked", "ttl_last_error", "ttl_version", "ttl_set_gemm_override")
@@ -56,6 +56,9 @@ _lib.shard_linear_col.argtypes = [_c_u16p, _I64, _I64, _c_u16p, _I64, _I32, _I32
 _lib.shard_linear_col_stored.restype = _I32
 _lib.shard_linear_col_stored.argtypes = [_c_u16p, _I64, _I64, _c_u16p, _I64, _I32, _I32, _I32,
                                          ctypes.POINTER(ColSplit), _I32, _c_u16p, ctypes.c_void_p]
+_lib.shard_linear_col_noalloc.restype = _I32
+_lib.shard_linear_col_noalloc.argtypes = _lib.shard_linear_col_stored.argtypes
+NOALLOC_SCRATCH_BYTES = 64 << 20
 _lib.shard_linear_col_gathered.restype = _I32
 _lib.shard_linear_col_gathered.argtypes = _lib.shard_linear_col_stored.argtypes
 _lib.shard_linear_row.restype = _I32
@@ -224,6 +227,23 @@ def shard_linear_col(X: torch.Tensor, W: torch.Tensor, t: int, rank: int,
         st = _lib.shard_linear_col_stored(_dev_ptr(X, "X"), b, k, _dev_ptr(W, "W"), n, w_layout, t, rank,
                                           sp, epi, _dev_ptr(Y, "Y"), _stream_handle(stream))
     _check(st)
+    return Y
+
+
+def shard_linear_col_noalloc(X: torch.Tensor, W: torch.Tensor, t: int, rank: int,
+                             split: Optional[ColSplit] = None, epi: int = EPI_NONE,
+                             Y: Optional[torch.Tensor] = None, stream=None,
+                             w_layout: int = W_KN) -> torch.Tensor:
+    """shard_linear_col with split-K partials kept in the library's static device scratch instead of
+    an allocated workspace (the C entry point shard_linear_col_noalloc).  Pass Y to keep the call
+    itself free of allocation."""
+    b, k, n, ncols = _col_dims(X, W, w_layout, split, t, epi)
+    if Y is None:
+        Y = torch.empty((b, max(ncols, 0)), dtype=torch.bfloat16, device=X.device)
+    _expect_shape(Y, "Y", (b, ncols))
+    _check(_lib.shard_linear_col_noalloc(_dev_ptr(X, "X"), b, k, _dev_ptr(W, "W"), n, w_layout, t, rank,
+                                         ctypes.byref(split) if split is not None else None, epi,
+                                         _dev_ptr(Y, "Y"), _stream_handle(stream)))
     return Y
 
 

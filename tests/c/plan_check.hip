@@ -50,7 +50,8 @@ static bool check_cut(int64_t M, int64_t tn, int64_t cus, int mode) {
   p.K = 512;
   p.mode = mode;
   ttl::g_launched.clear();
-  CHECK(ttl::launch_mixed(p, m, cus, nullptr) == hipSuccess, "launch_mixed failed");
+  ttl::Ctx ctx;
+  CHECK(ttl::launch_mixed(p, m, cus, ctx) == hipSuccess, "launch_mixed failed");
   CHECK(ttl::g_launched.size() >= 1 && ttl::g_launched.size() <= 2, "%zu launches", ttl::g_launched.size());
   const int64_t rb = ttl::cdiv(M, 64);
   std::vector<int> cover((size_t)(rb * tn), 0);
@@ -113,6 +114,45 @@ int main() {
     CHECK(!ttl::plan_mixed_rows(4096, 32, 256, m), "cut planned for two whole rounds");
     CHECK(!ttl::plan_mixed_rows(2176, 32, 256, m), "cut planned for a short last round (288 tiles)");
     CHECK(!ttl::plan_mixed_rows(2048, 6, 256, m), "cut planned for one partial round");
+  }
+  // The dry pass sizes a call's split-K partials and launches nothing: the 70B layer's qkv
+  // (2176 x 1280, k = 8192: 45 tiles of 256 x 256 in 5 k-splits), a 64-token 70B gate_up (SiLU·up,
+  // 3584 act columns: the split-K kernel, 56 tiles in 4 k-splits over the gate then up columns),
+  // and the 4096 x 8192 row GEMM (two whole rounds of tiles, no partials).
+  {
+    GemmParams p = {};
+    p.M = 2176;
+    p.N = 1280;
+    p.K = 8192;
+    ttl::g_launched.clear();
+    size_t need = ttl::gemm_workspace_bytes(p);
+    CHECK(need == (size_t)5 * 2176 * 1280 * 4, "qkv workspace %zu", need);
+    CHECK(ttl::g_launched.empty(), "the dry pass launched %zu kernels", ttl::g_launched.size());
+    p = {};
+    p.M = 64;
+    p.N = 3584;
+    p.K = 8192;
+    p.mode = 1;
+    need = ttl::gemm_workspace_bytes(p);
+    CHECK(need == (size_t)4 * 64 * 7168 * 4, "decode gate_up workspace %zu", need);
+    p = {};
+    p.M = 4096;
+    p.N = 8192;
+    p.K = 3584;
+    need = ttl::gemm_workspace_bytes(p);
+    CHECK(need == 0 && ttl::g_launched.empty(), "row GEMM workspace %zu", need);
+    // The same plan launched with a fixed workspace: the launches the dry pass stood in for.
+    p = {};
+    p.M = 2176;
+    p.N = 1280;
+    p.K = 8192;
+    float fake[4];
+    CHECK(ttl::launch_gemm_fixed_workspace(p, fake, (size_t)5 * 2176 * 1280 * 4, nullptr) == hipSuccess, "fixed");
+    CHECK(ttl::g_launched.size() == 1 && ttl::g_launched[0].splits == 5 && ttl::g_launched[0].ws == fake,
+          "fixed-workspace launch: %zu launches", ttl::g_launched.size());
+    ttl::g_launched.clear();
+    CHECK(ttl::launch_gemm_fixed_workspace(p, fake, 1024, nullptr) == hipErrorInvalidValue, "undersized workspace");
+    CHECK(ttl::g_launched.empty(), "an undersized workspace launched");
   }
   // Seeded shapes of every size class: each planned cut covers every row once and fits its rounds.
   std::mt19937 rng(7);

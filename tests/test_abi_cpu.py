@@ -79,6 +79,11 @@ def _colg(X=A, b=16, k=256, W=B, n=1376, t=2, rank=0, split=None, epi=0, Y=C, la
     return ttl.lib().shard_linear_col_gathered(X, b, k, W, n, lay, t, rank, sp, epi, Y, None)
 
 
+def _noalloc(X=A, b=16, k=256, W=B, n=1376, t=2, rank=0, split=None, epi=0, Y=C, lay=0):
+    sp = None if split is None else ttl.ctypes.byref(split)
+    return ttl.lib().shard_linear_col_noalloc(X, b, k, W, n, lay, t, rank, sp, epi, Y, None)
+
+
 def _rs(P=A, t=2, b=16, n=256, rank=0, R=B, gamma=D, eps=1e-5, Rout=B, Y=C):
     return ttl.lib().reduce_scatter_partials_rmsnorm(P, t, b, n, rank, R, gamma, eps, Rout, Y, None)
 
@@ -142,6 +147,11 @@ def _peers(ptrs=None, t=2, b=16, n=256, row0=0, rows=16, R=B, gamma=D, eps=1e-5,
     (lambda: _col(k=16384, n=131072, t=1, lay=ttl.W_BLOCKED), ttl.ERR_UNSUPPORTED, "2 GiB"),
     (lambda: _col(k=16384, n=65536, t=1, lay=1), ttl.ERR_UNSUPPORTED, "2 GiB"),
     (lambda: _col(k=16384, n=131072, t=2, lay=1), ttl.ERR_UNSUPPORTED, "2 GiB"),
+    (lambda: _noalloc(X=None), ttl.ERR_NULL, "shard_linear_col_noalloc"),
+    (lambda: _noalloc(rank=2), ttl.ERR_RANK, "rank=2"),
+    (lambda: _noalloc(epi=1), ttl.ERR_UNSUPPORTED, "two equal segments"),
+    (lambda: _noalloc(lay=3), ttl.ERR_UNSUPPORTED, "weight layout"),
+    (lambda: _noalloc(X=FX, W=FW, Y=FW + 4096), ttl.ERR_UNSUPPORTED, "overlap"),
     (lambda: _colg(Y=None), ttl.ERR_NULL, "non-NULL"),
     (lambda: _colg(rank=2), ttl.ERR_RANK, "rank=2"),
     (lambda: _colg(n=1370, t=4), ttl.ERR_NOT_DIVISIBLE, "not divisible"),
@@ -215,6 +225,17 @@ def test_binding_refuses_host_tensors():
         ttl.shard_linear_col(X, W, 2, 0, ttl.merged_gate_up_split(688, 2), ttl.EPI_SILU_MUL)
     with pytest.raises(TypeError, match="bfloat16"):
         ttl.shard_linear_row(X[:, :128].float().contiguous(), W, 2, 0)
+
+
+@no_device
+def test_noalloc_refuses_a_call_beyond_its_scratch():
+    """A call whose split-K partials would exceed the static scratch (64 k-splits of 256 x 16384
+    fp32 = 1 GiB) is refused before anything is launched: the plan is sized by a dry pass."""
+    with ttl.gemm_override("splitk", splits=64):
+        got = _noalloc(X=FX, b=256, k=8192, W=FW, n=16384, t=1, Y=0x40000000)
+    assert got == ttl.ERR_UNSUPPORTED, (got, ttl.last_error())
+    assert "static scratch" in ttl.last_error() and str(64 * 256 * 16384 * 4) in ttl.last_error()
+    assert ttl.NOALLOC_SCRATCH_BYTES == 64 << 20
 
 
 def test_exact_and_stored_forms_validate_alike():
