@@ -113,6 +113,15 @@ def parse():
                     help="only time every kernel of one rank's step for each of the five workloads "
                          "(tiny MLP, 8B MLP b=1/32/256, 8B attention, 70B MLP b=4096/64, 70B layer), "
                          "print one JSON line per workload and exit")
+    ap.add_argument("--workload", default=None,
+                    help="with --config-table: only this workload (e.g. llama3_8b_attn_tp4), optionally "
+                         "with the token count after a colon (llama3_8b_mlp_tp8:256)")
+    ap.add_argument("--traffic-record", metavar="DIR", default=None,
+                    help="only summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs found under DIR "
+                         "(pmc_<COUNTER>_<layout>/ of this bench's b=4096 step, copy_<COUNTER>/ of "
+                         "--copy-calibration-mib) into HBM bytes per call and print the traffic lines "
+                         "for profiles/, stamped with the current kernel sources' hash, then exit")
+    ap.add_argument("--commit", default="", help="with --traffic-record: the commit the counters were taken at")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (5 times) and exit: the "
                          "reference for scaling HBM traffic counters")
@@ -306,7 +315,7 @@ def _time_chain(torch, ops, reps, warmup):
     return {op[0]: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / reps * 1e3 for j, op in enumerate(ops)}
 
 
-def config_table(ttl, torch, layout, reps=20, warmup=3):
+def config_table(ttl, torch, layout, reps=20, warmup=3, only=None):
     """Every kernel of one rank's step for each workload, one JSON line each.  Decode-size batches
     (b < 512) cycle the simulated rank from repetition to repetition, so that the weight slices are
     not served from the Infinity Cache; the reductions rotate their operands (partials, residual,
@@ -424,8 +433,16 @@ def config_table(ttl, torch, layout, reps=20, warmup=3):
         us = _time_chain(torch, chain.ops, max(reps, gcycle if gcycle <= 64 else reps), warmup)
         report(wname, b, t, us, chain.ops, graph_step_us(chain.ops, min(gcycle, 64)), lay)
 
+    def wanted(w, b):
+        if only is None:
+            return True
+        name, _, tokens = only.partition(":")
+        return w.name == name and (not tokens or int(tokens) == b)
+
     for w in (wl.TINY_MLP_T2, wl.LLAMA3_8B_MLP_TP8, wl.LLAMA3_70B_MLP_TP8):
         for b in w.batches:
+            if not wanted(w, b):
+                continue
             inp = wl.mlp_inputs(w, b, seed=0, device=dev)
             t, H, I = w.t, w.hidden, w.intermediate
             Ir = I // t
@@ -445,6 +462,8 @@ def config_table(ttl, torch, layout, reps=20, warmup=3):
 
     for w in (wl.LLAMA3_8B_ATTN_TP4, wl.LLAMA3_70B_LAYER_TP8):
         for b in w.batches:
+            if not wanted(w, b):
+                continue
             is_layer = isinstance(w, wl.LayerShard)
             inp = (wl.layer_inputs if is_layer else wl.attn_inputs)(w, b, seed=0, device=dev)
             t, H = w.t, w.hidden
@@ -570,14 +589,108 @@ def sample_power_clock(torch, step, seconds=2.0):
             "sampled": "amd-smi metric -p -c --json, once, while the step repeated for %.1f s" % seconds}
 
 
-def recorded_traffic(kernel, workload):
-    """HBM bytes per launch recorded from the FETCH_SIZE / WRITE_SIZE counters in profiles/, or None
-    when no record exists or the kernel sources changed since the counters were taken."""
+def traffic_sources_digest():
     h = hashlib.sha256()
     for rel in TRAFFIC_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
-    digest = h.hexdigest()
+    return h.hexdigest()
+
+
+def read_counter_csv(path, counter):
+    """{kernel name: [value per dispatch]} of one rocprofv3 --pmc counter_collection.csv."""
+    import csv
+    out = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") == counter:
+                out.setdefault((row["Kernel_Name"], int(row["Grid_Size"])), []).append(float(row["Counter_Value"]))
+    return out
+
+
+def classify_dispatch(name):
+    """Which entry point of the bench step a dispatch belongs to (None for the set-up kernels)."""
+    if "gemm_bigwave_kernel<1," in name or "gemm_skinny_kernel<1," in name or "splitk_finalize_kernel<1>" in name:
+        return "shard_linear_col_silu_mul"
+    if "gemm_bigwave_kernel<0," in name or "gemm_skinny_kernel<0," in name or "splitk_finalize_kernel<0>" in name:
+        return "shard_linear_row"
+    if "reduce_rmsnorm_kernel" in name:
+        return "reduce_partials_rmsnorm"
+    return None
+
+
+def traffic_record(directory, commit, b=4096, t=8, H=8192, I=28672):
+    """HBM bytes per call of each entry point from FETCH_SIZE and WRITE_SIZE counter runs.  Each
+    counter is scaled by what it reads for a plain device copy of known size; a call's traffic is the
+    sum, over the distinct dispatches (kernel, grid) one call issues, of their mean per dispatch."""
+    import glob
+
+    def one(sub, counter):
+        files = glob.glob(os.path.join(directory, sub, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise FileNotFoundError(f"no counter_collection.csv under {os.path.join(directory, sub)}")
+        return read_counter_csv(files[0], counter)
+
+    factor = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        d = one(f"copy_{counter}", counter)
+        copies = [(k, v) for k, v in d.items() if "copyBuffer" in k[0] or "copy" in k[0].lower()]
+        (name, _), vals = max(copies, key=lambda kv: kv[0][1])
+        nbytes = None
+        for log in glob.glob(os.path.join(directory, f"copy_{counter}*.log")):
+            for line in open(log):
+                if line.startswith("{") and "copy_bytes_per_launch" in line:
+                    nbytes = json.loads(line)["copy_bytes_per_launch"]
+        if nbytes is None:
+            raise RuntimeError(f"copy size not found in {directory}/copy_{counter}*.log")
+        kib = sum(vals) / len(vals)
+        factor[counter] = nbytes / (kib * 1024.0)
+    alg = {"shard_linear_col_silu_mul": col_silu_bytes(b, H, I // t),
+           "shard_linear_row": row_bytes(b, I // t, H),
+           "reduce_partials_rmsnorm": reduce_bytes(t, b, H)}
+    digest = traffic_sources_digest()
+    rows, lines = [], []
+    for lay in ("kn", "nk"):
+        if not os.path.isdir(os.path.join(directory, f"pmc_FETCH_SIZE_{lay}")):
+            continue
+        per_call = {}
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            for (name, grid), vals in one(f"pmc_{counter}_{lay}", counter).items():
+                ep = classify_dispatch(name)
+                if ep is None:
+                    continue
+                mean_bytes = sum(vals) / len(vals) * 1024.0 * factor[counter]
+                per_call.setdefault(ep, {"FETCH_SIZE": 0.0, "WRITE_SIZE": 0.0, "dispatches": []})
+                per_call[ep][counter] += mean_bytes
+                if counter == "FETCH_SIZE":
+                    m = re.search(r"(\w+_kernel<[^>]*>)", name)
+                    per_call[ep]["dispatches"].append(f"{m.group(1) if m else name[:40]} grid {grid}")
+        for ep, d in per_call.items():
+            total = d["FETCH_SIZE"] + d["WRITE_SIZE"]
+            rows.append(f"| {ep} | {lay} | {d['FETCH_SIZE'] / 1e6:.1f} | {d['WRITE_SIZE'] / 1e6:.1f} | "
+                        f"{total / 1e6:.1f} | {alg[ep] / 1e6:.1f} | {total / alg[ep]:.2f} | "
+                        f"{'; '.join(d['dispatches'])} |")
+            if ep == "shard_linear_col_silu_mul":
+                lines.append(f"traffic kernel={ep} workload=llama3_70b_mlp_tp8_rank0_b{b}_{lay} "
+                             f"bytes_per_launch={int(round(total))} source_sha256={digest}")
+    print(f"counters scaled by a {factor['FETCH_SIZE']:.4f} (FETCH_SIZE) and {factor['WRITE_SIZE']:.4f} "
+          f"(WRITE_SIZE) factor from the plain device copy; sources sha256 {digest}"
+          + (f"; taken at commit {commit}" if commit else ""))
+    print("| entry point (per call) | weight storage | read MB | written MB | traffic MB | algorithmic MB "
+          "| ratio | dispatches |")
+    print("|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        print(r)
+    print()
+    for line in lines:
+        print(line)
+    return lines
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch recorded from the FETCH_SIZE / WRITE_SIZE counters in profiles/, or None
+    when no record exists or the kernel sources changed since the counters were taken."""
+    digest = traffic_sources_digest()
     pat = re.compile(r"^traffic\s+kernel=(\S+)\s+workload=(\S+)\s+bytes_per_launch=(\d+)\s+"
                      r"source_sha256=([0-9a-f]{64})\s*$")
     pdir = os.path.join(ROOT, "profiles")
@@ -677,6 +790,9 @@ def main():
         print("bench.py measures one GPU's share of the tensor-parallel work (ranks are simulated in one "
               "HBM); runs on more than one GPU are not part of this benchmark.", file=sys.stderr)
         return 2
+    if args.traffic_record:
+        traffic_record(args.traffic_record, args.commit)
+        return 0
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -697,7 +813,7 @@ def main():
         steady_state(ttl, torch, w, args.layout)
         return 0
     if args.config_table:
-        config_table(ttl, torch, args.layout)
+        config_table(ttl, torch, args.layout, only=args.workload)
         return 0
     b = args.batch
     workload = f"llama3_70b_mlp_tp8_rank0_b{b}_{args.layout}"

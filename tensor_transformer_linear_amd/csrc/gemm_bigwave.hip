@@ -87,62 +87,74 @@ void gemm_bigwave_kernel(const GemmParams p) {
   // Tile sets (p.rects > 0, no splits): block b < rect_tmc[0] * rect_tnc[0] is a tile of
   // rectangle 0, the rest of rectangle 1; rectangle i is rect_tmc[i] row-tiles from row
   // rect_row0[i] by rect_tnc[i] tile columns from tile column rect_tn0[i], walked in groups of
-  // rect_group[i] row-tiles.
+  // rect_group[i] row-tiles.  Persistent launches (p.persist): tiles blockIdx.x + j * gridDim.x.
   const int tiles = p.tiles_m * p.tiles_n;
   const int split = p.splits > 1 ? (int)blockIdx.x / tiles : 0;
-  int tile_m, tile_n, row0 = 0;
-  if (p.rects > 0) {
-    const int c0 = p.rect_tmc[0] * p.rect_tnc[0];
-    const bool second = p.rects > 1 && (int)blockIdx.x >= c0;
-    const int tmc = second ? p.rect_tmc[1] : p.rect_tmc[0];
-    const int tnc = second ? p.rect_tnc[1] : p.rect_tnc[0];
-    const int group = second ? p.rect_group[1] : p.rect_group[0];
-    tile_coords((int)blockIdx.x - (second ? c0 : 0), tmc, tnc, tile_m, tile_n, group > 0 ? group : 4);
-    tile_n += second ? p.rect_tn0[1] : p.rect_tn0[0];
-    row0 = second ? p.rect_row0[1] : p.rect_row0[0];
-  } else {
-    tile_coords((int)blockIdx.x - split * tiles, p.tiles_m, p.tiles_n, tile_m, tile_n);
-  }
-  const int m0 = row0 + tile_m * kBM;
-  const int n0 = tile_n * (MODE == kSiluMul ? kBN / 2 : kBN);  // first output column of the tile
+  auto tile_origin = [&](int bid, int& tm0, int& tn0) {
+    int tile_m, tile_n, row0 = 0;
+    if (p.rects > 0) {
+      const int c0 = p.rect_tmc[0] * p.rect_tnc[0];
+      const bool second = p.rects > 1 && bid >= c0;
+      const int tmc = second ? p.rect_tmc[1] : p.rect_tmc[0];
+      const int tnc = second ? p.rect_tnc[1] : p.rect_tnc[0];
+      const int group = second ? p.rect_group[1] : p.rect_group[0];
+      tile_coords(bid - (second ? c0 : 0), tmc, tnc, tile_m, tile_n, group > 0 ? group : 4);
+      tile_n += second ? p.rect_tn0[1] : p.rect_tn0[0];
+      row0 = second ? p.rect_row0[1] : p.rect_row0[0];
+    } else {
+      tile_coords(bid - split * tiles, p.tiles_m, p.tiles_n, tile_m, tile_n);
+    }
+    tm0 = row0 + tile_m * kBM;
+    tn0 = tile_n * (MODE == kSiluMul ? kBN / 2 : kBN);  // first output column of the tile
+  };
+  int m0, n0;
+  tile_origin((int)blockIdx.x, m0, n0);
   const int kt0 = split * p.kt_per_split;
   const int nk = p.splits > 1 ? min(p.kt_per_split, p.K / kBK - kt0) : p.K / kBK;  // >= 1
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds);
+  constexpr bool kCanPersist = WN == 128 && BM == 256;
+  const bool persist = kCanPersist && p.persist != 0;
 
-  // ---- Copy offsets, fixed for the whole k loop (the descriptors move with k0).  Copy i < 8 of
-  // this wave moves block 8*wave + i of the A stage, copy 8 + i block 8*wave + i of the B stage.
+  // ---- Copy offsets, fixed for a tile's whole k loop (the descriptors move with k0).  Copy i < 8
+  // of this wave moves block 8*wave + i of the A stage, copy 8 + i block 8*wave + i of the B stage.
   uint32_t c_off[kCopies];
+  auto set_copy_offsets = [&](int tm0, int tn0) {
 #pragma unroll
-  for (int i = 0; i < kACopies; ++i) {
-    // [256 rows][64 k]: block q holds rows 8q .. 8q+7; lane l lands in row 8q + l/8 at slot l%8,
-    // which holds k-chunk slot ^ ((row/2) % 8).
-    const int row = (kACopies * wave + i) * kRowsPerCopy + lane / kChunks;
-    const int chunk = (lane % kChunks) ^ ((row / kRowsPer256) % kChunks);
-    c_off[i] = (m0 + row < p.M) ? (uint32_t)(((int64_t)row * p.lda + chunk * 8) * 2) : kOob;
-  }
-#pragma unroll
-  for (int i = 0; i < kBCopies; ++i) {
-    const int q = kBCopies * wave + i;
-    bool ok;
-    if (WNK) {
-      const int n = q * kRowsPerCopy + lane / kChunks;  // tile column = staged row
-      const int chunk = (lane % kChunks) ^ ((n / kRowsPer256) % kChunks);
-      const int64_t wrow = weight_column<MODE, WN>(p, n0, n & ~7, ok) + (n & 7);
-      c_off[kACopies + i] = ok ? (uint32_t)((wrow * p.ldb + chunk * 8) * 2) : kOob;
-    } else {
-      // [64 k][kBN n]: block q holds k rows kKRowsPerCopy*q ..; lane l lands in row
-      // kKRowsPerCopy*q + l/kBChunks at slot l%kBChunks, which holds n-chunk slot ^ (4 * (row % 4)).
-      const int krow = kKRowsPerCopy * q + lane / kBChunks;
-      const int chunk = (lane % kBChunks) ^ (4 * (krow % 4));
-      const int64_t wcol = weight_column<MODE, WN>(p, n0, chunk * 8, ok);
-      c_off[kACopies + i] = !ok ? kOob
-                          : p.w_blk ? blocked_offset(krow, wcol, p.ldb)
-                                    : (uint32_t)(((int64_t)krow * p.ldb + wcol) * 2);
+    for (int i = 0; i < kACopies; ++i) {
+      // [256 rows][64 k]: block q holds rows 8q .. 8q+7; lane l lands in row 8q + l/8 at slot l%8,
+      // which holds k-chunk slot ^ ((row/2) % 8).
+      const int row = (kACopies * wave + i) * kRowsPerCopy + lane / kChunks;
+      const int chunk = (lane % kChunks) ^ ((row / kRowsPer256) % kChunks);
+      c_off[i] = (tm0 + row < p.M) ? (uint32_t)(((int64_t)row * p.lda + chunk * 8) * 2) : kOob;
     }
-  }
+#pragma unroll
+    for (int i = 0; i < kBCopies; ++i) {
+      const int q = kBCopies * wave + i;
+      bool ok;
+      if (WNK) {
+        const int n = q * kRowsPerCopy + lane / kChunks;  // tile column = staged row
+        const int chunk = (lane % kChunks) ^ ((n / kRowsPer256) % kChunks);
+        const int64_t wrow = weight_column<MODE, WN>(p, tn0, n & ~7, ok) + (n & 7);
+        c_off[kACopies + i] = ok ? (uint32_t)((wrow * p.ldb + chunk * 8) * 2) : kOob;
+      } else {
+        // [64 k][kBN n]: block q holds k rows kKRowsPerCopy*q ..; lane l lands in row
+        // kKRowsPerCopy*q + l/kBChunks at slot l%kBChunks, which holds n-chunk slot ^ (4 * (row % 4)).
+        const int krow = kKRowsPerCopy * q + lane / kBChunks;
+        const int chunk = (lane % kBChunks) ^ (4 * (krow % 4));
+        const int64_t wcol = weight_column<MODE, WN>(p, tn0, chunk * 8, ok);
+        c_off[kACopies + i] = !ok ? kOob
+                            : p.w_blk ? blocked_offset(krow, wcol, p.ldb)
+                                      : (uint32_t)(((int64_t)krow * p.ldb + wcol) * 2);
+      }
+    }
+  };
+  set_copy_offsets(m0, n0);
+  // cm0: first row of the tile whose copies are being issued (the next tile's in the last k-tiles
+  // of a persistent workgroup's current tile).
+  int cm0 = m0;
   auto a_desc = [&](int t) {
     const int k0 = (kt0 + t) * kBK;
-    return buffer_desc(p.A + (int64_t)m0 * p.lda + k0, ((int64_t)(p.M - m0 - 1) * p.lda + (p.K - k0)) * 2);
+    return buffer_desc(p.A + (int64_t)cm0 * p.lda + k0, ((int64_t)(p.M - cm0 - 1) * p.lda + (p.K - k0)) * 2);
   };
   auto b_desc = [&](int t) {
     const int k0 = (kt0 + t) * kBK;
@@ -150,11 +162,14 @@ void gemm_bigwave_kernel(const GemmParams p) {
            : p.w_blk ? blocked_desc(p.B, p.b_rows, k0)
                      : buffer_desc(p.B + (int64_t)k0 * p.ldb, (int64_t)(p.K - k0) * p.ldb * 2);
   };
-  // Copy i of tile t into stage t % 2: the wave's block of the A or B half plus a constant.
+  // Copy i of k-tile t into stage (t + sb) % kStages: the wave's block of the A or B half plus a
+  // constant.  sb moves by the k-tile count from one tile of a persistent workgroup to the next, so
+  // that the next tile's first k-tiles land in the stages its own loop expects.
+  int sb = 0;
   const uint32_t wave_lds_a = lds0 + (uint32_t)(wave * kACopies * 1024);
   const uint32_t wave_lds_b = lds0 + (uint32_t)(kAElems * 2 + wave * kBCopies * 1024);
   auto copy_one = [&](int t, int i, i32x4_t ad, i32x4_t bd) {
-    const uint32_t so = (uint32_t)(((unsigned)t % kStages) * kStageElems * 2);
+    const uint32_t so = (uint32_t)(((unsigned)(t + sb) % kStages) * kStageElems * 2);
     if (i < kACopies) copy16_to_lds_at(ad, c_off[i], wave_lds_a + so, i * 1024);
     else copy16_to_lds_at(bd, c_off[i], wave_lds_b + so, (i - kACopies) * 1024);
   };
@@ -199,7 +214,7 @@ void gemm_bigwave_kernel(const GemmParams p) {
   // each when W is stored [n][k], two half reads each when stored [k][n]).
   constexpr int kReadsPerSlice = kMI + (WNK ? 1 : 2) * kNI;
   auto read_one = [&](int t, int kk, int j) {
-    const uint16_t* st = lds + ((unsigned)t % kStages) * kStageElems;
+    const uint16_t* st = lds + ((unsigned)(t + sb) % kStages) * kStageElems;
     if (j < kMI) {
       af[kk][j] = *reinterpret_cast<const bf16x8_t*>(st + ra_off[kk] + j * 32 * kBK);
     } else if constexpr (WNK) {
@@ -255,9 +270,17 @@ void gemm_bigwave_kernel(const GemmParams p) {
   // copies, into tile t's stage); WAITN: this wave's copies of the tiles after t+1 that are in
   // flight at the barrier (kStages-2 tiles in the main loop, fewer near the end).  The main loop
   // runs with NEXT and COPY; the last kStages tiles are peeled, so the loop has no branches.
-  auto k_tile = [&](int t, auto next_c, auto copy_c, auto waitn_c) {
-    constexpr bool NEXT = decltype(next_c)::value, COPY = decltype(copy_c)::value;
+  //
+  // Copies go into tile t's stage; ckt is the k-tile they fetch: t + kStages of the same tile, or,
+  // in the last two k-tiles of a persistent workgroup's tile, k-tile 0 or 1 of its next tile (cm0
+  // and c_off then describe that tile).  Without NEXT but with COPY (the last k-tile, prefetching),
+  // the barrier still runs: it certifies that every wave's reads of tile t have returned.
+  // rcopy: COPY decided at run time (a uniform branch), for the last two k-tiles, which copy only
+  // when a persistent workgroup has a next tile; one code path keeps the registers as in the loop.
+  auto k_tile = [&](int t, auto next_c, auto copy_c, auto waitn_c, int ckt, bool rcopy) {
+    constexpr bool NEXT = decltype(next_c)::value, CCOPY = decltype(copy_c)::value;
     constexpr int WAITN = decltype(waitn_c)::value;
+    const bool COPY = CCOPY || rcopy;
 #pragma unroll
     for (int j = 0; j < kMps; ++j) {
       mfma_one(0, j);
@@ -271,15 +294,15 @@ void gemm_bigwave_kernel(const GemmParams p) {
       mfma_one(1, j);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (NEXT) {
-      wait_vmcnt<WAITN>();  // this wave's copies of tile t+1 landed
+    if (NEXT || COPY) {
+      if constexpr (NEXT) wait_vmcnt<WAITN>();  // this wave's copies of tile t+1 landed
       lds_barrier();        // ... everyone's; and every wave's reads of tile t returned
       __builtin_amdgcn_sched_barrier(0);
     }
     i32x4_t ad = {0, 0, 0, 0}, bd = {0, 0, 0, 0};
     if (COPY) {
-      ad = a_desc(t + kStages);
-      bd = b_desc(t + kStages);
+      ad = a_desc(ckt);
+      bd = b_desc(ckt);
     }
     // Copy c of the tile's kCopies follows MFMA slot c * 2*kMps / kCopies of slices 2-3 (slots
     // kMps.. are slice 3's): at 16 MFMAs per slice, the A copies after every second MFMA of slice
@@ -316,67 +339,112 @@ void gemm_bigwave_kernel(const GemmParams p) {
   using W0 = std::integral_constant<int, 0>;
   using WMain = std::integral_constant<int, (kStages - 2) * kCopies>;
   using W1 = std::integral_constant<int, kCopies>;
-  int t = 0;
-  for (; t + kStages < nk; ++t) k_tile(t, std::true_type{}, std::true_type{}, WMain{});
-  if constexpr (kStages == 3) {
-    if (t + 2 < nk) k_tile(t++, std::true_type{}, std::false_type{}, W1{});  // tile t+2 in flight
-  }
-  if (t + 1 < nk) k_tile(t++, std::true_type{}, std::false_type{}, W0{});
-  k_tile(t, std::false_type{}, std::false_type{}, W0{});
+  using T = std::true_type;
+  using F = std::false_type;
 
-  const int row_base = m0 + wm * kWM + a_r;
-  // ---- Epilogue straight from the accumulators: each lane owns 4 consecutive columns of one row
-  // per register group, stored as one 8-byte bf16 piece, or (split-K, plain mode) as one 16-byte
-  // fp32 piece of the partial tile in workspace slice `split`.
-  const bool partial = MODE == kPlain && p.splits > 1;
-  float* wbase = partial ? p.ws + (int64_t)split * p.M * p.ws_ld : nullptr;
+  auto epilogue = [&](int em0, int en0) {
+    const int row_base = em0 + wm * kWM + a_r;
+    // ---- Epilogue straight from the accumulators: each lane owns 4 consecutive columns of one row
+    // per register group, stored as one 8-byte bf16 piece, or (split-K, plain mode) as one 16-byte
+    // fp32 piece of the partial tile in workspace slice `split`.
+    const bool partial = MODE == kPlain && p.splits > 1;
+    float* wbase = partial ? p.ws + (int64_t)split * p.M * p.ws_ld : nullptr;
 #pragma unroll
-  for (int mi = 0; mi < kMI; ++mi) {
-    const int row = row_base + mi * 32;
-    if (row >= p.M) continue;
-    uint16_t* crow = p.C + (int64_t)row * p.ldc;
-    if (MODE == kPlain) {
+    for (int mi = 0; mi < kMI; ++mi) {
+      const int row = row_base + mi * 32;
+      if (row >= p.M) continue;
+      uint16_t* crow = p.C + (int64_t)row * p.ldc;
+      if (MODE == kPlain) {
+#pragma unroll
+        for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = en0 + wn * WN + ni * 32 + g * 8 + a_half * 4;
+            if (partial) {
+              const float4 v = {acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]};
+              *reinterpret_cast<float4*>(wbase + (int64_t)row * p.ws_ld + col) = v;
+            } else if (col < p.N) {
+              u32x2_t v;
+              v.x = pack_bf16x2(acc[mi][ni][4 * g + 0], acc[mi][ni][4 * g + 1]);
+              v.y = pack_bf16x2(acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]);
+              *reinterpret_cast<u32x2_t*>(crow + col) = v;
+            }
+          }
+      } else {
+#pragma unroll
+        for (int ni = 0; ni < kNI / 2; ++ni)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = en0 + wn * (WN / 2) + ni * 32 + g * 8 + a_half * 4;
+            if (col < p.N) {
+              float a[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                a[e] = silu_mul(acc[mi][ni][4 * g + e], acc[mi][ni + kNI / 2][4 * g + e]);
+              u32x2_t v;
+              v.x = pack_bf16x2(a[0], a[1]);
+              v.y = pack_bf16x2(a[2], a[3]);
+              *reinterpret_cast<u32x2_t*>(crow + col) = v;
+            }
+          }
+      }
+    }
+  };
+
+  // ---- The tiles of this workgroup: one, or (persistent launches) blockIdx.x and, where it exists,
+  // blockIdx.x + gridDim.x (a persistent launch has at most twice as many tiles as workgroups).
+  int bid = (int)blockIdx.x;
+#pragma unroll
+  for (int jt = 0; jt < 2; ++jt) {
+    const int em0 = m0, en0 = n0;
+    int t = 0;
+    for (; t + kStages < nk; ++t) k_tile(t, T{}, T{}, WMain{}, t + kStages, false);
+    bool has_next = false;
+    if constexpr (kCanPersist) {
+      if (jt == 0 && persist && nk >= 2 && bid + (int)gridDim.x < tiles) {
+        has_next = true;
+        bid += (int)gridDim.x;
+        tile_origin(bid, m0, n0);
+        set_copy_offsets(m0, n0);
+        cm0 = m0;
+      }
+    }
+    // The last k-tiles; with a next tile they copy its k-tiles 0 and 1 into the stages they free,
+    // and this wave's copies of k-tile 0 must have landed before the stores join the vmcnt queue.
+    if constexpr (kStages == 3) {
+      if (t + 2 < nk) k_tile(t++, T{}, F{}, W1{}, 0, false);  // tile t+2 in flight
+    }
+    if (t + 1 < nk) {
+      k_tile(t, T{}, F{}, W0{}, 0, has_next);
+      ++t;
+    }
+    k_tile(t, F{}, F{}, W0{}, 1, has_next);
+    if (has_next) wait_vmcnt<kCopies>();
+    epilogue(em0, en0);
+    if (!has_next) break;
+    // Next tile: accumulators cleared, its k-tile 0 published, slices 0 and 1 read.
+#pragma unroll
+    for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = n0 + wn * WN + ni * 32 + g * 8 + a_half * 4;
-          if (partial) {
-            const float4 v = {acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]};
-            *reinterpret_cast<float4*>(wbase + (int64_t)row * p.ws_ld + col) = v;
-          } else if (col < p.N) {
-            u32x2_t v;
-            v.x = pack_bf16x2(acc[mi][ni][4 * g + 0], acc[mi][ni][4 * g + 1]);
-            v.y = pack_bf16x2(acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]);
-            *reinterpret_cast<u32x2_t*>(crow + col) = v;
-          }
-        }
-    } else {
+        for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+    sb = (sb + nk) % kStages;
+    lds_barrier();
 #pragma unroll
-      for (int ni = 0; ni < kNI / 2; ++ni)
+    for (int j = 0; j < kReadsPerSlice; ++j) read_one(0, 0, j);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = n0 + wn * (WN / 2) + ni * 32 + g * 8 + a_half * 4;
-          if (col < p.N) {
-            float a[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              a[e] = silu_mul(acc[mi][ni][4 * g + e], acc[mi][ni + kNI / 2][4 * g + e]);
-            u32x2_t v;
-            v.x = pack_bf16x2(a[0], a[1]);
-            v.y = pack_bf16x2(a[2], a[3]);
-            *reinterpret_cast<u32x2_t*>(crow + col) = v;
-          }
-        }
-    }
+    for (int j = 0; j < kReadsPerSlice; ++j) read_one(0, 1, j);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 template <int MODE, bool WNK, int WN, int BM>
 void launch_one(const GemmParams& p, hipStream_t stream) {
   const int splits = p.splits > 1 ? p.splits : 1;
-  const int blocks = p.rects > 0 ? p.rect_tmc[0] * p.rect_tnc[0] + (p.rects > 1 ? p.rect_tmc[1] * p.rect_tnc[1] : 0)
-                                 : splits * p.tiles_m * p.tiles_n;
+  int blocks = p.rects > 0 ? p.rect_tmc[0] * p.rect_tnc[0] + (p.rects > 1 ? p.rect_tmc[1] * p.rect_tnc[1] : 0)
+                           : splits * p.tiles_m * p.tiles_n;
+  if (p.persist > 0 && p.persist < blocks) blocks = p.persist;  // persistent: p.persist workgroups
   hipLaunchKernelGGL((gemm_bigwave_kernel<MODE, WNK, WN, BM>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
 }
 
@@ -401,10 +469,11 @@ hipError_t launch_gemm_bigwave(const GemmParams& p, hipStream_t stream) {
   if (p.mode == kSiluMul && p.splits > 1) return hipErrorInvalidValue;  // split SiLU·up runs as halves
   if (p.tile_rows == 192) {
     // Short tiles: wide columns only, no k splits, rows given by a tile set.
-    if (p.narrow || p.splits > 1 || p.rects < 1) return hipErrorInvalidValue;
+    if (p.narrow || p.splits > 1 || p.rects < 1 || p.persist > 0) return hipErrorInvalidValue;
     launch_width<128, 192>(p, stream);
   } else if (p.tile_rows == 256 || p.tile_rows == 0) {
     if (p.rects > 0 && p.splits > 1) return hipErrorInvalidValue;
+    if (p.persist > 0 && (p.rects > 0 || p.splits > 1 || p.narrow)) return hipErrorInvalidValue;
     p.narrow ? launch_width<64, 256>(p, stream) : launch_width<128, 256>(p, stream);
   } else {
     return hipErrorInvalidValue;

@@ -129,7 +129,8 @@ int64_t device_cus() {
 
 // The forced kernel family: 0 by shape, 1 256 x 256 tiles, 2 split-K, 3 256 x 256 tiles by the
 // eight-wave kernel, 4 256 x 256 tiles cut along k, 5 256 x 128 tiles, 6 256 x 128 tiles cut along
-// k, 7 192 x 256 tiles, 8 the 256-row / 192-row cut planned for the override's CU count.
+// k, 7 192 x 256 tiles, 8 the 256-row / 192-row cut planned for the override's CU count, 9 256 x 256
+// tiles by a persistent grid (at most two tiles per workgroup).
 int forced_kernel() { return g_force_kernel.load(std::memory_order_relaxed); }
 int64_t forced_splits() { return g_force_splits.load(std::memory_order_relaxed); }
 
@@ -141,6 +142,26 @@ hipError_t launch_tiles(GemmParams& p, int force, Ctx& c) {
   p.narrow = 0;
   if (force != 3 && gemm_bigwave_supports(p)) return run_bigwave(c, p);
   return run_tiled(c, p);
+}
+
+// 256 x 256 tiles of the four-wave kernel over all of p by a persistent grid (K a multiple of 64, at
+// least two k-tiles): with more tiles than CUs and at most twice as many, one workgroup per CU,
+// each computing tile b and then tile b + CUs, whose first k-tiles it fetches while it finishes the
+// first.  Otherwise as launch_tiles.  The override's CU count, if set, stands in for the device's.
+hipError_t launch_persist(GemmParams& p, Ctx& c) {
+  p.tiles_m = (int32_t)cdiv(p.M, gemm_tile_rows());
+  p.tiles_n = (int32_t)cdiv(p.N, gemm_tile_cols(p.mode));
+  const int64_t pc = g_force_plan_cus.load(std::memory_order_relaxed);
+  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n, cus = pc > 0 ? pc : device_cus();
+  if (!gemm_bigwave_supports(p) || p.K < 128 || tiles <= cus || tiles > 2 * cus) return launch_tiles(p, 0, c);
+  p.splits = 1;
+  p.narrow = 0;
+  p.rects = 0;
+  p.persist = (int32_t)cus;
+  if (!c.dry && g_trace.load(std::memory_order_relaxed))
+    std::fprintf(stderr, "ttl gemm persist: M=%d N=%d K=%d, %lld tiles on %lld workgroups\n", p.M, p.N, p.K,
+                 (long long)tiles, (long long)cus);
+  return run_bigwave(c, p);
 }
 
 // 256 x 128 tiles of the four-wave kernel over all of p (K a multiple of 64).
@@ -428,6 +449,7 @@ hipError_t plan_and_launch(GemmParams& p, Ctx& c) {
   const int64_t n_cu = device_cus();
   const int64_t min_tiled = n_cu * 3 / 4;  // 256 x 256 tiles when they occupy >= 3/4 of the CUs
   if (force == 1 || force == 3) return launch_tiles(p, force, c);
+  if (force == 9) return launch_persist(p, c);
   if (force == 7 && gemm_bigwave_supports(p)) return launch_short(p, c);
   if (force == 8 && gemm_bigwave_supports(p)) {
     MixedRows m;
@@ -469,9 +491,12 @@ hipError_t plan_and_launch(GemmParams& p, Ctx& c) {
     }
     return launch_splitk(p, c);
   }
+  // Exactly two whole rounds (e.g. 512 tiles: 4096 x 8192 row-parallel outputs): a persistent grid,
+  // each workgroup fetching its second tile's first k-tiles while it finishes the first.
+  const int64_t rounds = tiles / n_cu, rem = tiles % n_cu;
+  if (rounds == 2 && rem == 0 && gemm_bigwave_supports(p) && p.K >= 128) return launch_persist(p, c);
   // Whole rounds of one tile per CU plus a last round more than half full: 256-row tiles for the
   // whole rounds and 192-row tiles for the last one, which then takes 3/4 of a round's time.
-  const int64_t rounds = tiles / n_cu, rem = tiles % n_cu;
   if (gemm_bigwave_supports(p)) {
     MixedRows m;
     if (plan_mixed_rows(p.M, tiled_n, n_cu, m)) return launch_mixed(p, m, n_cu, c);

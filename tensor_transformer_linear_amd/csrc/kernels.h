@@ -44,6 +44,10 @@ struct GemmParams {
   int32_t tile_rows;
   int32_t rects;
   int32_t rect_tn0[2], rect_tnc[2], rect_row0[2], rect_tmc[2], rect_group[2];
+  // Four-wave kernel, 256 x 256 tiles, no splits and no tile set: persist = 1 launches fewer
+  // workgroups than tiles; workgroup b then computes tiles b, b + grid, b + 2 grid, ... in turn,
+  // fetching the next tile's first k-tiles while it finishes the current one.
+  int32_t persist;
 };
 
 // SiLU·up as a plain GEMM over the gate columns followed by the up columns (2N outputs, two column

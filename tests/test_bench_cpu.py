@@ -69,3 +69,42 @@ def test_cpu_baseline_fields():
     for run in (out["one_core"], out["all_cores"]):
         assert run["gemm_tflops"] > 0 and run["reduce_gbs"] > 0
     assert out["cpu_model"]
+
+
+def _counter_csv(path, rows, counter):
+    import csv
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f, quoting=csv.QUOTE_ALL)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"])
+        for i, (name, grid, kib) in enumerate(rows):
+            w.writerow([i, name, grid, counter, kib])
+
+
+def test_traffic_record_from_counter_files(tmp_path, capsys):
+    """The traffic lines come from counter files, scaled by the copy calibration, summed over the
+    distinct dispatches of one call, and stamped with the current sources' hash."""
+    spec = importlib.util.spec_from_file_location("bench_mod", BENCH)
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    d = tmp_path / "prof"
+    col256 = "void ttl::(anonymous namespace)::gemm_bigwave_kernel<1, false, 128, 256>(ttl::GemmParams)"
+    col192 = "void ttl::(anonymous namespace)::gemm_bigwave_kernel<1, false, 128, 192>(ttl::GemmParams)"
+    row = "void ttl::(anonymous namespace)::gemm_bigwave_kernel<0, false, 128, 256>(ttl::GemmParams)"
+    setup = "void at::native::vectorized_elementwise_kernel<4>(int)"
+    for counter, factor in (("FETCH_SIZE", 0.5), ("WRITE_SIZE", 1.0)):
+        # a copy of 1 MiB that the counter reads as `factor` of its bytes
+        _counter_csv(str(d / f"copy_{counter}" / "c_counter_collection.csv"),
+                     [("__amd_rocclr_copyBuffer", 4096, 1024 * factor)], counter)
+        (d / f"copy_{counter}.log").write_text('{"copy_bytes_per_launch": 1048576, "launches": 5}\n')
+        rows = [(setup, 100, 1e6), (col256, 65536, 1000 * factor), (col256, 65536, 1200 * factor),
+                (col192, 65536, 500 * factor), (row, 131072, 700 * factor)]
+        _counter_csv(str(d / f"pmc_{counter}_kn" / "b_counter_collection.csv"), rows, counter)
+    lines = bench.traffic_record(str(d), "abc123")
+    out = capsys.readouterr().out
+    # per call: mean of the 256-row dispatches (1100 KiB) + the 192-row dispatch (500 KiB), read and
+    # written, each scaled back to true bytes
+    want = int(round((1100 + 500) * 1024 * 2))
+    assert lines == [f"traffic kernel=shard_linear_col_silu_mul workload=llama3_70b_mlp_tp8_rank0_b4096_kn "
+                     f"bytes_per_launch={want} source_sha256={bench.traffic_sources_digest()}"]
+    assert "taken at commit abc123" in out and "gemm_bigwave_kernel<0, false, 128, 256> grid 131072" in out

@@ -561,6 +561,61 @@ def test_splitk_repeated_launches_reuse_workspace(ttl, gemm_force):
             assert_close(from_gpu(Y[rows]), ref, f"repeated split-K {key}")
 
 
+@pytest.mark.parametrize("b,k,I,t,silu,cus", [
+    (300, 256, 344, 1, True, 3),      # 6 tiles on 3 workgroups, two each
+    (513, 192, 1024, 2, True, 6),     # three k-tiles (an odd count: the stages swap between tiles)
+    (1000, 640, 1536, 1, False, 16),  # 24 tiles on 16 workgroups: 8 of them take a second tile
+    (600, 128, 2000, 1, False, 12),   # two k-tiles, both fetched for the next tile
+    (1024, 1024, 2048, 4, True, 10),  # 16 tiles per rank on 10 workgroups
+    (700, 320, 768, 2, False, 3)])
+@LAYOUTS
+def test_persistent_tiles(ttl, gemm_force, capfd, b, k, I, t, silu, cus, layout):
+    """256 x 256 tiles by a persistent grid (planned for a few CUs so that small shapes have more
+    tiles than workgroups): a workgroup computes its first tile while fetching the first k-tiles of
+    its second.  Bit for bit the whole-tile launch's results (same products, same k order), and
+    every element against the oracle."""
+    X = wl.random_bf16((b, k), 7 + b)
+    n = 2 * I if silu else I
+    W = wl.random_bf16((k, n), 8 + k, std=0.05)
+    Wd_, lay = _stored(ttl, W, layout)
+    sp_c = ttl.merged_gate_up_split(I, t) if silu else None
+    sp_np = oracle.merged_gate_up_split(I, t) if silu else oracle.plain_split(I, t)
+    epi = ttl.EPI_SILU_MUL if silu else 0
+    Xd = gpu(X)
+    capfd.readouterr()
+    for r in range(t):
+        gemm_force.set(kernel="tiled", plan_cus=0, trace=True)
+        whole = ttl.shard_linear_col(Xd, Wd_, t, r, sp_c, epi, w_layout=lay)
+        gemm_force.set(kernel="persist", plan_cus=cus)
+        got = ttl.shard_linear_col(Xd, Wd_, t, r, sp_c, epi, w_layout=lay)
+        torch.cuda.synchronize()
+        assert torch.equal(got, whole), f"persistent tiles differ from whole tiles (rank {r})"
+    assert capfd.readouterr().err.count(f"on {cus} workgroups") == t  # every rank ran persistent
+    ref = oracle.col_shard(f64(X), f64(W), sp_np, t, t - 1)
+    if silu:
+        ref = oracle.silu_mul(ref)
+    assert_close(from_gpu(got), ref, f"persistent tiles b={b} k={k} I={I} t={t} silu={silu} {layout}")
+
+
+def test_persistent_row_gemm_two_rounds(ttl, gemm_force, capfd):
+    """The row GEMM at 4096 x 8192 outputs (512 tiles: two whole rounds on 256 CUs) takes the
+    persistent grid by shape; bit-equal to the whole-tile launch, sampled rows against the oracle."""
+    b, k, n, t = 4096, 3584, 8192, 8
+    X = wl.random_bf16((b, k // t), 175, device="cuda")
+    W = wl.random_bf16((k, n), 176, std=0.02, device="cuda")
+    gemm_force.set(kernel="tiled", trace=True)
+    whole = ttl.shard_linear_row(X, W, t, 5, True)
+    gemm_force.set(kernel="auto")
+    capfd.readouterr()
+    got = ttl.shard_linear_row(X, W, t, 5, True)
+    torch.cuda.synchronize()
+    assert "512 tiles on 256 workgroups" in capfd.readouterr().err
+    assert torch.equal(got, whole)
+    rows = [0, 255, 256, 2047, 2048, 4095]
+    ref = oracle.row_shard(f64(X[rows].cpu()), f64(W.cpu()), t, 5, x_is_parallel=True)
+    assert_close(from_gpu(got[rows]), ref, "persistent row GEMM, two rounds")
+
+
 @pytest.mark.parametrize("kern", ["splitk", "tilesplit"])
 def test_splitk_on_two_streams_at_once(ttl, gemm_force, kern):
     """Split-K launches on two streams at once write their fp32 partials to separate workspaces (one
