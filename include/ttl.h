@@ -348,6 +348,7 @@ const char* ttl_last_error(void);
 #define TTL_GEMM_SHORT 7        /* 192 x 256 tiles */
 #define TTL_GEMM_MIXED 8        /* the 256-row / 192-row cut wherever one exists */
 #define TTL_GEMM_PERSIST 9      /* 256 x 256 tiles by a persistent grid (up to two tiles per CU) */
+#define TTL_GEMM_TILED16 10     /* 256 x 256 tiles fed to 16 x 16 x 32 products */
 ttl_status ttl_set_gemm_override(int32_t kernel, int32_t splits, int32_t plan_cus, int32_t trace);
 
 /* Library version: major * 10000 + minor * 100 + patch. */

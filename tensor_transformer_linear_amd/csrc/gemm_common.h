@@ -63,6 +63,14 @@ __device__ inline void copy16_to_lds_at(i32x4_t desc, uint32_t voffset, uint32_t
                :: "v"(voffset), "s"(desc), "s"(lds_base), "n"(lds_imm) : "memory", "scc");
 }
 
+// The same copy with a uniform byte offset (an SGPR) added to the global address: copies whose
+// per-lane offsets differ only by a per-copy constant share one offset register.
+__device__ inline void copy16_to_lds_so(i32x4_t desc, uint32_t voffset, uint32_t soffset, uint32_t lds_base,
+                                        uint32_t lds_imm) {
+  asm volatile("s_add_u32 m0, %3, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voffset), "s"(desc), "s"(soffset), "s"(lds_base), "n"(lds_imm) : "memory", "scc");
+}
+
 // Wait until at most N of this wave's vector-memory operations are outstanding.
 template <int N>
 __device__ inline void wait_vmcnt() {

@@ -100,6 +100,7 @@ hipError_t workspace(Ctx& c, size_t bytes, void** out) {
 
 hipError_t run_bigwave(Ctx& c, const GemmParams& p) { return c.dry ? hipSuccess : launch_gemm_bigwave(p, c.stream); }
 hipError_t run_tiled(Ctx& c, const GemmParams& p) { return c.dry ? hipSuccess : launch_gemm_tiled(p, c.stream); }
+hipError_t run_tiled16(Ctx& c, const GemmParams& p) { return c.dry ? hipSuccess : launch_gemm_bigwave16(p, c.stream); }
 hipError_t run_skinny(Ctx& c, const GemmParams& p, int mb) {
   return c.dry ? hipSuccess : launch_gemm_skinny(p, mb, c.stream);
 }
@@ -130,7 +131,8 @@ int64_t device_cus() {
 // The forced kernel family: 0 by shape, 1 256 x 256 tiles, 2 split-K, 3 256 x 256 tiles by the
 // eight-wave kernel, 4 256 x 256 tiles cut along k, 5 256 x 128 tiles, 6 256 x 128 tiles cut along
 // k, 7 192 x 256 tiles, 8 the 256-row / 192-row cut planned for the override's CU count, 9 256 x 256
-// tiles by a persistent grid (at most two tiles per workgroup).
+// tiles by a persistent grid (at most two tiles per workgroup), 10 256 x 256 tiles by the 16 x 16 x 32
+// kernel.
 int forced_kernel() { return g_force_kernel.load(std::memory_order_relaxed); }
 int64_t forced_splits() { return g_force_splits.load(std::memory_order_relaxed); }
 
@@ -162,6 +164,19 @@ hipError_t launch_persist(GemmParams& p, Ctx& c) {
     std::fprintf(stderr, "ttl gemm persist: M=%d N=%d K=%d, %lld tiles on %lld workgroups\n", p.M, p.N, p.K,
                  (long long)tiles, (long long)cus);
   return run_bigwave(c, p);
+}
+
+// 256 x 256 tiles over all of p by the 16 x 16 x 32 four-wave kernel where it applies ([n][k]
+// weights), else as launch_tiles.
+hipError_t launch_tiles16(GemmParams& p, Ctx& c) {
+  p.tiles_m = (int32_t)cdiv(p.M, gemm_tile_rows());
+  p.tiles_n = (int32_t)cdiv(p.N, gemm_tile_cols(p.mode));
+  p.splits = 1;
+  p.narrow = 0;
+  p.rects = 0;
+  p.persist = 0;
+  if (gemm_bigwave16_supports(p)) return run_tiled16(c, p);
+  return launch_tiles(p, 0, c);
 }
 
 // 256 x 128 tiles of the four-wave kernel over all of p (K a multiple of 64).
@@ -450,6 +465,7 @@ hipError_t plan_and_launch(GemmParams& p, Ctx& c) {
   const int64_t min_tiled = n_cu * 3 / 4;  // 256 x 256 tiles when they occupy >= 3/4 of the CUs
   if (force == 1 || force == 3) return launch_tiles(p, force, c);
   if (force == 9) return launch_persist(p, c);
+  if (force == 10) return launch_tiles16(p, c);
   if (force == 7 && gemm_bigwave_supports(p)) return launch_short(p, c);
   if (force == 8 && gemm_bigwave_supports(p)) {
     MixedRows m;
@@ -491,9 +507,23 @@ hipError_t plan_and_launch(GemmParams& p, Ctx& c) {
     }
     return launch_splitk(p, c);
   }
+  const int64_t rounds = tiles / n_cu, rem = tiles % n_cu;
+  // Weights stored [n][k]: the 16 x 16 x 32 kernel over whole tiles wherever the last round is full
+  // or more than half full (measured faster than the persistent grid and the row cut of the
+  // 32 x 32 x 16 kernel: 70B TP=8 at 4096 tokens, row GEMM 171-177 against 186 us, SiLU·up column
+  // GEMM 341-343 against 350 us); a short last round still goes to the split-K kernel below.
+  bool nk16 = false;
+  {
+    GemmParams q = p;
+    q.splits = 1;
+    q.narrow = 0;
+    q.rects = 0;
+    q.persist = 0;
+    nk16 = gemm_bigwave16_supports(q);
+  }
+  if (nk16 && (rounds == 0 || rem == 0 || 2 * rem > n_cu)) return launch_tiles16(p, c);
   // Exactly two whole rounds (e.g. 512 tiles: 4096 x 8192 row-parallel outputs): a persistent grid,
   // each workgroup fetching its second tile's first k-tiles while it finishes the first.
-  const int64_t rounds = tiles / n_cu, rem = tiles % n_cu;
   if (rounds == 2 && rem == 0 && gemm_bigwave_supports(p) && p.K >= 128) return launch_persist(p, c);
   // Whole rounds of one tile per CU plus a last round more than half full: 256-row tiles for the
   // whole rounds and 192-row tiles for the last one, which then takes 3/4 of a round's time.
@@ -510,7 +540,7 @@ hipError_t plan_and_launch(GemmParams& p, Ctx& c) {
     if (head_row_tiles >= 1 && head_row_tiles < tiled_m) {
       GemmParams head = p;
       head.M = (int32_t)(head_row_tiles * gemm_tile_rows());
-      hipError_t e = launch_tiles(head, 0, c);
+      hipError_t e = nk16 ? launch_tiles16(head, c) : launch_tiles(head, 0, c);
       if (e != hipSuccess) return e;
       GemmParams tail = p;
       tail.A = p.A + (int64_t)head.M * p.lda;
@@ -519,7 +549,7 @@ hipError_t plan_and_launch(GemmParams& p, Ctx& c) {
       return launch_splitk(tail, c);
     }
   }
-  return launch_tiles(p, 0, c);
+  return nk16 ? launch_tiles16(p, c) : launch_tiles(p, 0, c);
 }
 
 }  // namespace

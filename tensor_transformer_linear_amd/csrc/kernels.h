@@ -99,6 +99,12 @@ int gemm_bigwave_tile_cols(int mode, bool narrow);
 // workgroups, each writing its fp32 partial tile; launch_splitk_finalize then sums them.
 hipError_t launch_gemm_bigwave(const GemmParams& p, hipStream_t stream);
 
+// The 256 x 256 tiles of the four-wave kernel fed to 16 x 16 x 32 products (gemm_bigwave16.hip):
+// [n][k] weights, whole launches of tiles (no k splits, no tile sets, not persistent), K a multiple
+// of 64.  Same results as launch_gemm_bigwave, bit for bit.
+bool gemm_bigwave16_supports(const GemmParams& p);
+hipError_t launch_gemm_bigwave16(const GemmParams& p, hipStream_t stream);
+
 // Split-K kernel with 32*mb-row tiles (mb = 1, 2 or 4) of 128 weight columns, followed (splits > 1)
 // by the kernel that sums the splits; tiles_m, tiles_n, splits, kt_per_split, ws and ws_ld set by
 // the caller.

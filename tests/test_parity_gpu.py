@@ -31,7 +31,7 @@ def ttl():
 LAYOUTS = pytest.mark.parametrize("layout", ["kn", "nk"])
 
 
-@pytest.fixture(params=["auto", "tiled", "eightwave", "tilesplit", "narrow", "short", "splitk"])
+@pytest.fixture(params=["auto", "tiled", "tiled16", "eightwave", "tilesplit", "narrow", "short", "splitk"])
 def gemm_path(request, gemm_force):
     """Which GEMM kernel the library uses for the test (auto = its choice by shape)."""
     if request.param == "auto":
@@ -559,6 +559,39 @@ def test_splitk_repeated_launches_reuse_workspace(ttl, gemm_force):
             rows = [0, b - 1]
             ref = oracle.col_shard(f64(Xs[rows]), f64(Ws), oracle.plain_split(n, 1), 1, 0)
             assert_close(from_gpu(Y[rows]), ref, f"repeated split-K {key}")
+
+
+@pytest.mark.parametrize("b,k,I,t,silu", [
+    (300, 256, 344, 1, True),     # ragged rows and act columns, four k-tiles
+    (513, 1024, 2048, 4, True),   # several tiles per rank
+    (257, 512, 1000, 1, False),   # ragged columns
+    (1000, 640, 1536, 2, False),  # ten k-tiles
+    (64, 64, 128, 1, False),      # one k-tile
+    (600, 128, 2000, 1, False),   # two k-tiles
+    (700, 192, 768, 2, True)])    # three k-tiles
+def test_mfma16_tiles_equal_mfma32_tiles(ttl, gemm_force, b, k, I, t, silu):
+    """[n][k] weights through 256 x 256 tiles of 16 x 16 x 32 products: every output equals the
+    32 x 32 x 16 kernel's bit for bit (each output sums the same products in the same k order), and
+    against the oracle."""
+    X = wl.random_bf16((b, k), 7 + b)
+    n = 2 * I if silu else I
+    W = wl.random_bf16((k, n), 8 + k, std=0.05)
+    Wd_, lay = _stored(ttl, W, "nk")
+    sp_c = ttl.merged_gate_up_split(I, t) if silu else None
+    sp_np = oracle.merged_gate_up_split(I, t) if silu else oracle.plain_split(I, t)
+    epi = ttl.EPI_SILU_MUL if silu else 0
+    Xd = gpu(X)
+    for r in range(t):
+        gemm_force.set(kernel="tiled")
+        a = ttl.shard_linear_col(Xd, Wd_, t, r, sp_c, epi, w_layout=lay)
+        gemm_force.set(kernel="tiled16")
+        c = ttl.shard_linear_col(Xd, Wd_, t, r, sp_c, epi, w_layout=lay)
+        torch.cuda.synchronize()
+        assert torch.equal(a, c), f"16 x 16 x 32 tiles differ from 32 x 32 x 16 tiles (rank {r})"
+    ref = oracle.col_shard(f64(X), f64(W), sp_np, t, t - 1)
+    if silu:
+        ref = oracle.silu_mul(ref)
+    assert_close(from_gpu(c), ref, f"16x16x32 tiles b={b} k={k} I={I} t={t} silu={silu}")
 
 
 @pytest.mark.parametrize("b,k,I,t,silu,cus", [
