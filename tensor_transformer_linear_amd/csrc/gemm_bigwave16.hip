@@ -242,39 +242,59 @@ void gemm_bigwave16_kernel(const GemmParams p) {
   if (t + 1 < nk) k_tile(t++, std::true_type{}, std::false_type{});
   k_tile(t, std::false_type{}, std::false_type{});
 
-  // ---- Epilogue: lane l holds output row 16 mb + l % 16 and columns 16 ni + 4 (l / 16) .. + 3.
-  const int row_base = m0 + wm * kWM + r16;
+  // ---- Epilogue: lane l holds output row 16 mb + l % 16 and columns 16 ni + 4 (l / 16) .. + 3, so
+  // direct stores would write 32-byte pieces of 16 rows per instruction.  Instead each wave writes
+  // 32 rows (two row blocks) at a time into its own quarter of the free ring stage and reads them
+  // back as whole rows: each store instruction then covers 4 rows of 256 bytes (8 of 128 bytes
+  // for SiLU·up).  The stage of the k-tile before the last is free (every read of it returned
+  // before that k-tile's barrier; with one k-tile, stage 1 was never used); the quarter is the
+  // wave's alone and its LDS accesses complete in order, so no barrier is needed.  Chunk c (16
+  // bytes) of staged row r sits at slot c ^ (r % chunks per row).
+  uint16_t* stg = lds + ((unsigned)(t + 1) % kStages) * kStageElems + wave * (kStageElems / kWaves);
+  const int wrow0 = m0 + wm * kWM;
+  auto drain = [&](auto ch_c, int pass, int col0) {
+    constexpr int CH = decltype(ch_c)::value;
+    constexpr int kRowsPerRead = 64 / CH;
 #pragma unroll
-  for (int mb = 0; mb < kMB; ++mb) {
-    const int row = row_base + mb * 16;
-    if (row >= p.M) continue;
-    uint16_t* crow = p.C + (int64_t)row * p.ldc;
+    for (int i = 0; i < 32 / kRowsPerRead; ++i) {
+      const int r = i * kRowsPerRead + lane / CH, c = lane % CH;
+      const i32x4_t v = *reinterpret_cast<const i32x4_t*>(stg + r * CH * 8 + ((c ^ (r % CH)) * 8));
+      const int row = wrow0 + pass * 32 + r, col = col0 + c * 8;
+      if (row < p.M && col < p.N) *reinterpret_cast<i32x4_t*>(p.C + (int64_t)row * p.ldc + col) = v;
+    }
+  };
+#pragma unroll
+  for (int pass = 0; pass < kMB / 2; ++pass) {
     if (MODE == kPlain) {
+      constexpr int CH = kWN / 8;
 #pragma unroll
-      for (int ni = 0; ni < kNB; ++ni) {
-        const int col = n0 + wn * kWN + ni * 16 + 4 * g4;
-        if (col < p.N) {
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int ni = 0; ni < kNB; ++ni) {
+          const int mb = 2 * pass + h, r = 16 * h + r16, c = 2 * ni + g4 / 2;
           u32x2_t v;
           v.x = pack_bf16x2(acc[mb][ni][0], acc[mb][ni][1]);
           v.y = pack_bf16x2(acc[mb][ni][2], acc[mb][ni][3]);
-          *reinterpret_cast<u32x2_t*>(crow + col) = v;
+          *reinterpret_cast<u32x2_t*>(stg + r * CH * 8 + ((c ^ (r % CH)) * 8) + 4 * (g4 % 2)) = v;
         }
-      }
+      drain(std::integral_constant<int, CH>{}, pass, n0 + wn * kWN);
     } else {
       // column blocks 0..3 are the gate columns and 4..7 the up columns of the same act columns
+      constexpr int CH = kWN / 16;
 #pragma unroll
-      for (int ni = 0; ni < kNB / 2; ++ni) {
-        const int col = n0 + wn * (kWN / 2) + ni * 16 + 4 * g4;
-        if (col < p.N) {
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int ni = 0; ni < kNB / 2; ++ni) {
+          const int mb = 2 * pass + h, r = 16 * h + r16, c = 2 * ni + g4 / 2;
           float a[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) a[e] = silu_mul(acc[mb][ni][e], acc[mb][ni + kNB / 2][e]);
           u32x2_t v;
           v.x = pack_bf16x2(a[0], a[1]);
           v.y = pack_bf16x2(a[2], a[3]);
-          *reinterpret_cast<u32x2_t*>(crow + col) = v;
+          *reinterpret_cast<u32x2_t*>(stg + r * CH * 8 + ((c ^ (r % CH)) * 8) + 4 * (g4 % 2)) = v;
         }
-      }
+      drain(std::integral_constant<int, CH>{}, pass, n0 + wn * (kWN / 2));
     }
   }
 }

@@ -57,8 +57,15 @@ __device__ inline void copy16_to_lds(i32x4_t desc, uint32_t voffset, uint32_t ld
 }
 
 // The same copy with the LDS destination lds_base + lds_imm (a compile-time constant) summed
-// straight into M0 (one scalar instruction fewer per copy; the add writes SCC).
+// straight into M0 (one scalar instruction fewer per copy; the add writes SCC).  The descriptor and
+// base are wave-uniform; reading them through readfirstlane states so to the compiler, which
+// otherwise may keep a uniform value in a vector register where the instruction needs a scalar one.
 __device__ inline void copy16_to_lds_at(i32x4_t desc, uint32_t voffset, uint32_t lds_base, uint32_t lds_imm) {
+  desc.x = __builtin_amdgcn_readfirstlane(desc.x);
+  desc.y = __builtin_amdgcn_readfirstlane(desc.y);
+  desc.z = __builtin_amdgcn_readfirstlane(desc.z);
+  desc.w = __builtin_amdgcn_readfirstlane(desc.w);
+  lds_base = __builtin_amdgcn_readfirstlane(lds_base);
   asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :: "v"(voffset), "s"(desc), "s"(lds_base), "n"(lds_imm) : "memory", "scc");
 }

@@ -39,6 +39,7 @@ constexpr int kDefaultCUs = 256;        // MI355X compute units (a whole-chip de
 constexpr int kMinKTilesPerSplit = 4;   // keep each split's copy pipeline full
 constexpr int kTileSplitMinRows = 512;  // 256 x 256 tiles cut along k from this many rows
 constexpr int kMinKTilesPerTileSplit = 16;
+constexpr int kShortK = 2048;           // split-K kernel: k up to this takes its smallest row tiles
 
 struct Workspace {
   void* ptr = nullptr;
@@ -430,7 +431,14 @@ hipError_t launch_tiles_splitk(GemmParams& p, int64_t splits, bool narrow, Ctx& 
 }
 
 hipError_t launch_splitk(GemmParams& p, Ctx& c) {
-  const int mb = p.M <= 32 ? 1 : (p.M <= 64 ? 2 : 4);
+  // Row blocks per tile: 32 * mb rows.  With a short k (at most kShortK), batches of 65..512 rows
+  // take 32-row tiles (64-row above 256 rows): the grid then fills the CUs with few or no k splits,
+  // whose fp32 partials would cost more than the extra passes over the weight (served from L2).
+  // Measured (graph replay, splits as planned): 8B TP=8 row GEMM at 256 tokens 16.8 against 19.9 us
+  // with 128-row tiles; a 128-row 70B o_proj tail (k = 1024) 10.4-11.2 against 19.1 us.  A long k
+  // keeps the larger tiles, whose fewer passes over the weight win there.
+  int mb = p.M <= 32 ? 1 : (p.M <= 64 ? 2 : 4);
+  if (p.M > 64 && p.K <= kShortK) mb = p.M <= 256 ? 1 : 2;
   const int64_t tiles_m = cdiv(p.M, 32 * mb);
   const int64_t tiles_n = cdiv(p.N, p.mode == 1 ? kSkinnyCols / 2 : kSkinnyCols);
   const int64_t tiles = tiles_m * tiles_n;
@@ -522,9 +530,10 @@ hipError_t plan_and_launch(GemmParams& p, Ctx& c) {
     nk16 = gemm_bigwave16_supports(q);
   }
   if (nk16 && (rounds == 0 || rem == 0 || 2 * rem > n_cu)) return launch_tiles16(p, c);
-  // Exactly two whole rounds (e.g. 512 tiles: 4096 x 8192 row-parallel outputs): a persistent grid,
-  // each workgroup fetching its second tile's first k-tiles while it finishes the first.
-  if (rounds == 2 && rem == 0 && gemm_bigwave_supports(p) && p.K >= 128) return launch_persist(p, c);
+  // Whole rounds (e.g. 512 tiles: 4096 x 8192 row-parallel outputs) run as whole tiles: with the
+  // epilogue staged through LDS they beat the persistent grid, whose first tile must store
+  // directly while the ring holds its next tile's first k-tiles (70B TP=8 row GEMM at 4096 tokens,
+  // [k][n] weights: 192.8 against 198.2 us on one box).
   // Whole rounds of one tile per CU plus a last round more than half full: 256-row tiles for the
   // whole rounds and 192-row tiles for the last one, which then takes 3/4 of a round's time.
   if (gemm_bigwave_supports(p)) {

@@ -164,18 +164,19 @@ hipError_t launch(const ReduceNormParams& p, hipStream_t stream) {
 hipError_t launch_reduce_rmsnorm(const ReduceNormParams& p, hipStream_t stream) {
   const int64_t pieces = p.n / 8;  // n <= 65536, checked by the caller
   if (p.b >= 1024) {
-    // Many rows (prefill): a few hundred threads per row, two to four partials' loads in flight
-    // per thread; the rows in flight per CU keep HBM busy.  How many rows fit on the chip at once
-    // depends on the shape (pieces per thread, threads per row, loads in flight), and a row count
-    // just above a whole number of such rounds leaves a slow last round: the shapes below were
-    // measured at the rows of the workloads, each repeated on one set of inputs (n = 4096: 18 µs
-    // against 21 µs at t = 4, b = 2048; n = 8192: 64 µs against 67 µs at t = 8, b = 2176, equal at
-    // b = 2048 and 4096).
+    // Many rows (prefill): a few hundred threads per row; the rows in flight per CU keep HBM busy.
+    // How many rows fit on the chip at once depends on the shape (pieces per thread, threads per
+    // row, loads in flight), and a row count just above a whole number of such rounds leaves a slow
+    // last round.  The shapes for n = 4096 and 8192 were measured at the rows of the workloads with
+    // operands rotated through more than 512 MB (HBM, not the Infinity Cache): one partial's loads
+    // in flight per thread (the residual joining the last) gives more rows in flight than several,
+    // n = 4096, t = 4, b = 2048: 20.3 against 23.7-24.2 us (5.8 TB/s); n = 8192, t = 8: 67.8 and
+    // 121.9 us at b = 2176 and 4096, against 68.8 and 124.0.
     if (pieces <= 64) return launch<1, 64, 4>(p, stream);
     if (pieces <= 128) return launch<1, 128, 4>(p, stream);
     if (pieces <= 256) return launch<1, 256, 4>(p, stream);
-    if (pieces <= 512) return p.b <= 2560 ? launch<4, 128, 4>(p, stream) : launch<1, 512, 2>(p, stream);
-    if (pieces <= 1024) return p.b < 4096 ? launch<2, 512, 4>(p, stream) : launch<4, 256, 4>(p, stream);
+    if (pieces <= 512) return p.b <= 2560 ? launch<4, 128, 1>(p, stream) : launch<1, 512, 2>(p, stream);
+    if (pieces <= 1024) return launch<2, 512, 1>(p, stream);
     if (pieces <= 2048) return launch<8, 256, 2>(p, stream);
     if (pieces <= 4096) return launch<4, 1024, 2>(p, stream);
     return launch<8, 1024, 1>(p, stream);

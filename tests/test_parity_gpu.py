@@ -539,6 +539,27 @@ def test_splitk_split_counts(ttl, gemm_force, splits, layout):
                      f"split-K row splits={splits} r={r} {layout}")
 
 
+@pytest.mark.parametrize("b", [65, 200, 256, 400])
+@pytest.mark.parametrize("splits", [0, 1, 3])
+@LAYOUTS
+def test_splitk_short_k_small_row_tiles(ttl, gemm_force, b, splits, layout):
+    """With a short k (at most 2048) the split-K kernel runs 65..512-row batches in 32-row tiles
+    (64-row above 256 rows): SiLU·up column and row GEMMs with a k tail, at the planned split count
+    (0) and forced ones, against the oracle."""
+    gemm_force.set(kernel="splitk")
+    gemm_force.set(splits=splits)
+    _col_case(ttl, b, 1032, oracle.merged_gate_up_split(272, 2), ttl.merged_gate_up_split(272, 2), 2,
+              seed=130 + b + splits, epi=ttl.EPI_SILU_MUL, layout=layout)
+    k, n, t = 2048, 520, 2
+    X = wl.random_bf16((b, k), 140 + b + splits)
+    W = wl.random_bf16((k, n), 141 + b + splits, std=0.05)
+    Wd, lay = _stored(ttl, W, layout)
+    for r in range(t):
+        P = ttl.shard_linear_row(gpu(X), Wd, t, r, x_is_parallel=False, w_layout=lay)
+        assert_close(from_gpu(P), oracle.row_shard(f64(X), f64(W), t, r, x_is_parallel=False),
+                     f"short-k split-K row b={b} splits={splits} r={r} {layout}")
+
+
 def test_splitk_repeated_launches_reuse_workspace(ttl, gemm_force):
     """Back-to-back split-K launches of different sizes share (and grow) the library's workspace;
     a repeated shape must reproduce its first result bit for bit."""
@@ -631,15 +652,18 @@ def test_persistent_tiles(ttl, gemm_force, capfd, b, k, I, t, silu, cus, layout)
 
 
 def test_persistent_row_gemm_two_rounds(ttl, gemm_force, capfd):
-    """The row GEMM at 4096 x 8192 outputs (512 tiles: two whole rounds on 256 CUs) takes the
-    persistent grid by shape; bit-equal to the whole-tile launch, sampled rows against the oracle."""
+    """The row GEMM at 4096 x 8192 outputs (512 tiles: two whole rounds on 256 CUs): the planner's
+    whole tiles (outputs staged through LDS) and the persistent grid (direct stores while the ring
+    holds the next tile) are bit-equal; sampled rows against the oracle."""
     b, k, n, t = 4096, 3584, 8192, 8
     X = wl.random_bf16((b, k // t), 175, device="cuda")
     W = wl.random_bf16((k, n), 176, std=0.02, device="cuda")
-    gemm_force.set(kernel="tiled", trace=True)
-    whole = ttl.shard_linear_row(X, W, t, 5, True)
-    gemm_force.set(kernel="auto")
+    gemm_force.set(kernel="auto", trace=True)
     capfd.readouterr()
+    whole = ttl.shard_linear_row(X, W, t, 5, True)
+    torch.cuda.synchronize()
+    assert "workgroups" not in capfd.readouterr().err  # whole tiles by shape
+    gemm_force.set(kernel="persist", trace=True)
     got = ttl.shard_linear_row(X, W, t, 5, True)
     torch.cuda.synchronize()
     assert "512 tiles on 256 workgroups" in capfd.readouterr().err
