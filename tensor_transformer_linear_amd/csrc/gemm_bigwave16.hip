@@ -249,7 +249,8 @@ void gemm_bigwave16_kernel(const GemmParams p) {
   // for SiLU·up).  The stage of the k-tile before the last is free (every read of it returned
   // before that k-tile's barrier; with one k-tile, stage 1 was never used); the quarter is the
   // wave's alone and its LDS accesses complete in order, so no barrier is needed.  Chunk c (16
-  // bytes) of staged row r sits at slot c ^ (r % chunks per row).
+  // bytes) of staged row r sits at slot c ^ (r % chunks per row).  Stores carry the non-temporal
+  // hint (outputs are written once, for a later launch).
   uint16_t* stg = lds + ((unsigned)(t + 1) % kStages) * kStageElems + wave * (kStageElems / kWaves);
   const int wrow0 = m0 + wm * kWM;
   auto drain = [&](auto ch_c, int pass, int col0) {
@@ -260,7 +261,7 @@ void gemm_bigwave16_kernel(const GemmParams p) {
       const int r = i * kRowsPerRead + lane / CH, c = lane % CH;
       const i32x4_t v = *reinterpret_cast<const i32x4_t*>(stg + r * CH * 8 + ((c ^ (r % CH)) * 8));
       const int row = wrow0 + pass * 32 + r, col = col0 + c * 8;
-      if (row < p.M && col < p.N) *reinterpret_cast<i32x4_t*>(p.C + (int64_t)row * p.ldc + col) = v;
+      if (row < p.M && col < p.N) __builtin_nontemporal_store(v, reinterpret_cast<i32x4_t*>(p.C + (int64_t)row * p.ldc + col));
     }
   };
 #pragma unroll
