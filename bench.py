@@ -116,6 +116,17 @@ def parse():
     ap.add_argument("--workload", default=None,
                     help="with --config-table: only this workload (e.g. llama3_8b_attn_tp4), optionally "
                          "with the token count after a colon (llama3_8b_mlp_tp8:256)")
+    ap.add_argument("--op", default=None,
+                    help="with --config-table --workload: run and time only this kernel of the step "
+                         "(e.g. qkv, o_proj, gate_up_silu, down, reduce_rmsnorm): under a kernel trace, "
+                         "every dispatch then belongs to it")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="with --config-table: skip the HIP-graph replay (for counter runs)")
+    ap.add_argument("--trace-summary", metavar="DIR", default=None,
+                    help="only summarise rocprofv3 kernel traces found under DIR (one sub-directory per "
+                         "--config-table --op run, holding its *_kernel_trace.csv and the run's JSON line "
+                         "in ct.json) as markdown rows: the kernels of one call with their average "
+                         "durations, their sum, and the call's graph and eager times; then exit")
     ap.add_argument("--traffic-record", metavar="DIR", default=None,
                     help="only summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs found under DIR "
                          "(pmc_<COUNTER>_<layout>/ of this bench's b=4096 step, copy_<COUNTER>/ of "
@@ -315,7 +326,7 @@ def _time_chain(torch, ops, reps, warmup):
     return {op[0]: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / reps * 1e3 for j, op in enumerate(ops)}
 
 
-def config_table(ttl, torch, layout, reps=20, warmup=3, only=None):
+def config_table(ttl, torch, layout, reps=20, warmup=3, only=None, only_op=None, graph=True):
     """Every kernel of one rank's step for each workload, one JSON line each.  Decode-size batches
     (b < 512) cycle the simulated rank from repetition to repetition, so that the weight slices are
     not served from the Infinity Cache; the reductions rotate their operands (partials, residual,
@@ -336,6 +347,10 @@ def config_table(ttl, torch, layout, reps=20, warmup=3, only=None):
         return lay
 
     def bf(*shape):
+        # With a single kernel timed (--op) the chain is not run to fill the buffers, so that a
+        # kernel trace holds that kernel's dispatches only: they get random values instead.
+        if only_op is not None:
+            return torch.randn(shape, device=dev).to(torch.bfloat16)
         return torch.empty(shape, dtype=torch.bfloat16, device=dev)
 
     class Chain:
@@ -419,19 +434,26 @@ def config_table(ttl, torch, layout, reps=20, warmup=3, only=None):
               flush=True)
 
     def run(wname, b, t, chain, parts, lay, keep):
-        # every rank's partials into every copy of the rotations, in chain order
+        # every rank's partials into every copy of the rotations, in chain order (not with --op,
+        # whose buffers hold random values)
         copies = max(p["n"] for p in parts)
-        for c in range(copies):
-            for r in range(t):
-                for op in chain.ops:
-                    op[1](c, r)
+        if only_op is None:
+            for c in range(copies):
+                for r in range(t):
+                    for op in chain.ops:
+                        op[1](c, r)
         torch.cuda.synchronize()
         # a whole number of rank cycles and operand rotations per graph
         gcycle = chain.cycle
         for p in parts:
             gcycle = gcycle * p["n"] // math.gcd(gcycle, p["n"])
-        us = _time_chain(torch, chain.ops, max(reps, gcycle if gcycle <= 64 else reps), warmup)
-        report(wname, b, t, us, chain.ops, graph_step_us(chain.ops, min(gcycle, 64)), lay)
+        ops = chain.ops
+        if only_op is not None:
+            ops = [op for op in chain.ops if op[0] == only_op]
+            if not ops:
+                raise SystemExit(f"{wname}: no kernel named {only_op!r} (one of {[op[0] for op in chain.ops]})")
+        us = _time_chain(torch, ops, max(reps, gcycle if gcycle <= 64 else reps), warmup)
+        report(wname, b, t, us, ops, graph_step_us(ops, min(gcycle, 64)) if graph else float("nan"), lay)
 
     def wanted(w, b):
         if only is None:
@@ -619,21 +641,88 @@ def classify_dispatch(name):
     return None
 
 
-def traffic_record(directory, commit, b=4096, t=8, H=8192, I=28672):
-    """HBM bytes per call of each entry point from FETCH_SIZE and WRITE_SIZE counter runs.  Each
-    counter is scaled by what it reads for a plain device copy of known size; a call's traffic is the
-    sum, over the distinct dispatches (kernel, grid) one call issues, of their mean per dispatch."""
+def _short_kernel_name(name):
+    """The library's kernel name without namespaces and arguments (template arguments kept)."""
+    m = re.search(r"ttl::\(anonymous namespace\)::(\w+)(<[^>]*>)?", name)
+    return (m.group(1) + (m.group(2) or "")) if m else None
+
+
+def trace_summary(directory):
+    """Markdown rows from rocprofv3 kernel traces of single-kernel config-table runs (--op): for each
+    run, the library's dispatches grouped by kernel and grid, their counts and average durations; one
+    call dispatches each group once, so the per-call kernel time is the sum of the averages.  The
+    run's JSON line (ct.json) gives the same call's time in a replayed HIP graph (kernels plus the
+    gaps between them, no host launch cost) and eagerly launched (HIP events around each call)."""
+    import csv
     import glob
+    import statistics
+    csv.field_size_limit(1 << 30)
+    factor = None
+    if os.path.isdir(os.path.join(directory, "copy_FETCH_SIZE")):
+        factor = copy_factors(directory)
+        print(f"HBM counters scaled by {factor['FETCH_SIZE']:.4f} (FETCH_SIZE) and {factor['WRITE_SIZE']:.4f} "
+              f"(WRITE_SIZE) from a plain device copy; sources sha256 {traffic_sources_digest()}")
+        print()
+    print("| workload | tokens | kernel call | dispatches per call: kernel, grid, average us | "
+          "sum of kernels us | graph us | eager us | read MB | written MB | algorithmic MB |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for run in sorted(d for d in glob.glob(os.path.join(directory, "*")) if os.path.isdir(d)):
+        traces = glob.glob(os.path.join(run, "**", "*kernel_trace.csv"), recursive=True)
+        if not traces:
+            continue
+        groups = {}
+        for path in traces:
+            for r in csv.DictReader(open(path)):
+                name = _short_kernel_name(r["Kernel_Name"])
+                if name is None:
+                    continue
+                grid = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+                dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                groups.setdefault((name, grid), []).append(dur)
+        if not groups:
+            continue
+        calls = max(len(v) for v in groups.values())
+        order = sorted(groups, key=lambda k: -statistics.mean(groups[k]))
+        parts = [f"`{k[0]}` {k[1]}: {statistics.mean(groups[k]):.1f}" +
+                 ("" if len(groups[k]) == calls else f" ({len(groups[k])} of {calls} calls)") for k in order]
+        total = sum(statistics.mean(v) * len(v) / calls for v in groups.values())
+        meta = {}
+        ct = os.path.join(run, "ct.json")
+        if os.path.exists(ct):
+            for line in open(ct):
+                if line.startswith("{"):
+                    meta = json.loads(line)
+        kern = next(iter(meta.get("kernels", {}).items()), (os.path.basename(run), {}))
+        traffic = ["", ""]
+        if factor is not None and os.path.isdir(os.path.join(run, "pmc_FETCH_SIZE")):
+            for i, counter in enumerate(("FETCH_SIZE", "WRITE_SIZE")):
+                d = {k: v for k, v in _counter_run(run, f"pmc_{counter}", counter).items()
+                     if _short_kernel_name(k[0]) is not None}
+                n = max(len(v) for v in d.values())
+                per_call = sum(sum(v) / n for v in d.values()) * 1024.0 * factor[counter]
+                traffic[i] = f"{per_call / 1e6:.1f}"
+        alg = kern[1].get("gbs", float("nan")) * kern[1].get("us", float("nan")) * 1e3
+        print(f"| {meta.get('workload', os.path.basename(run))} | {meta.get('tokens', '')} | {kern[0]} | "
+              f"{'; '.join(parts)} | {total:.1f} | {meta.get('step_us_graph', float('nan')):.1f} | "
+              f"{kern[1].get('us', float('nan')):.1f} | {traffic[0]} | {traffic[1]} | {alg / 1e6:.1f} |")
 
-    def one(sub, counter):
-        files = glob.glob(os.path.join(directory, sub, "**", "*counter_collection.csv"), recursive=True)
-        if not files:
-            raise FileNotFoundError(f"no counter_collection.csv under {os.path.join(directory, sub)}")
-        return read_counter_csv(files[0], counter)
 
+def _counter_run(directory, sub, counter):
+    """{(kernel name, grid): [KiB per dispatch]} of the counter run under directory/sub."""
+    import glob
+    files = glob.glob(os.path.join(directory, sub, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {os.path.join(directory, sub)}")
+    return read_counter_csv(files[0], counter)
+
+
+def copy_factors(directory):
+    """Bytes per counted KiB for FETCH_SIZE and WRITE_SIZE: the plain device copy's known size (its
+    JSON line in directory/copy_<COUNTER>*.log) over what the counter read for it (copy_<COUNTER>/)."""
+    import glob
     factor = {}
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-        d = one(f"copy_{counter}", counter)
+        d = _counter_run(directory, f"copy_{counter}", counter)
         copies = [(k, v) for k, v in d.items() if "copyBuffer" in k[0] or "copy" in k[0].lower()]
         (name, _), vals = max(copies, key=lambda kv: kv[0][1])
         nbytes = None
@@ -645,6 +734,17 @@ def traffic_record(directory, commit, b=4096, t=8, H=8192, I=28672):
             raise RuntimeError(f"copy size not found in {directory}/copy_{counter}*.log")
         kib = sum(vals) / len(vals)
         factor[counter] = nbytes / (kib * 1024.0)
+    return factor
+
+
+def traffic_record(directory, commit, b=4096, t=8, H=8192, I=28672):
+    """HBM bytes per call of each entry point from FETCH_SIZE and WRITE_SIZE counter runs.  Each
+    counter is scaled by what it reads for a plain device copy of known size; a call's traffic is the
+    sum, over the distinct dispatches (kernel, grid) one call issues, of their mean per dispatch."""
+    def one(sub, counter):
+        return _counter_run(directory, sub, counter)
+
+    factor = copy_factors(directory)
     alg = {"shard_linear_col_silu_mul": col_silu_bytes(b, H, I // t),
            "shard_linear_row": row_bytes(b, I // t, H),
            "reduce_partials_rmsnorm": reduce_bytes(t, b, H)}
@@ -793,6 +893,9 @@ def main():
     if args.traffic_record:
         traffic_record(args.traffic_record, args.commit)
         return 0
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return 0
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -813,7 +916,7 @@ def main():
         steady_state(ttl, torch, w, args.layout)
         return 0
     if args.config_table:
-        config_table(ttl, torch, args.layout, only=args.workload)
+        config_table(ttl, torch, args.layout, only=args.workload, only_op=args.op, graph=not args.no_graph)
         return 0
     b = args.batch
     workload = f"llama3_70b_mlp_tp8_rank0_b{b}_{args.layout}"

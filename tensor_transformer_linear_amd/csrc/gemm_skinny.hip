@@ -81,13 +81,15 @@ void gemm_skinny_kernel(const GemmParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // Block -> (split, tile_m, tile_n), tile_n fastest: the workgroups that share one k range of A
-  // run together.
-  int bid = blockIdx.x;
-  const int tile_n = bid % p.tiles_n;
-  bid /= p.tiles_n;
-  const int tile_m = bid % p.tiles_m;
-  const int split = bid / p.tiles_m;
+  // Block -> (split, tile_m, tile_n).  Consecutive blocks go to different XCDs, each with its own
+  // L2: the XCD-aware map gives each XCD a compact run of columns (split, tile_n), every row tile of
+  // each, so that the row tiles reading one weight block [k range, columns] share an L2 (numbering
+  // tile_n fastest split them over XCDs whenever the column count was not a multiple of 8: 8B TP=8
+  // SiLU·up at 256 tokens fetched 90 MB for 32 MB of operands).
+  int tile_m = 0, col = 0;
+  tile_coords((int)blockIdx.x, p.tiles_m, p.tiles_n * p.splits, tile_m, col, p.tiles_m);
+  const int split = col / p.tiles_n;
+  const int tile_n = col % p.tiles_n;
   const int m0 = tile_m * kBM;
   const int nk_all = (p.K + kBK - 1) / kBK;
   const int kt0 = split * p.kt_per_split;
