@@ -105,7 +105,7 @@ def parse():
     ap.add_argument("--no-yardstick", action="store_true",
                     help="skip timing torch.matmul (hipBLASLt) on the same GEMM shapes")
     ap.add_argument("--no-power", action="store_true",
-                    help="skip sampling socket power and GFX clock while the step repeats")
+                    help="skip sampling socket power and GFX clock while the step repeats (6 s)")
     ap.add_argument("--steady-state", action="store_true",
                     help="only run each b=4096 GEMM (ours and hipBLASLt's) back to back for 2 s, sample "
                          "power and clock, time 30 launches, print one JSON line per GEMM and exit")
@@ -593,9 +593,11 @@ def steady_state(ttl, torch, w, layout):
                           "gfx_clock_mhz_mean": pc[1] if pc else None}), flush=True)
 
 
-def sample_power_clock(torch, step, seconds=2.0):
+def sample_power_clock(torch, step, seconds=6.0):
     """Socket power and GFX clock reported by amd-smi once while `step` runs back to back (the GPU
-    settles at its power limit within a fraction of a second).  None if amd-smi is unavailable."""
+    settles at its power limit within a fraction of a second).  The repetition lasts longer than a
+    5-s utilisation sampler's period, so an outside observer sees the GPU busy during the bench.
+    None if amd-smi is unavailable."""
     t0 = time.perf_counter()
     pc, i = None, 0
     while time.perf_counter() - t0 < seconds:

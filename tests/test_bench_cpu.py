@@ -4,6 +4,7 @@
 import ast
 import builtins
 import importlib.util
+import json
 import os
 import subprocess
 import sys
@@ -108,3 +109,53 @@ def test_traffic_record_from_counter_files(tmp_path, capsys):
     assert lines == [f"traffic kernel=shard_linear_col_silu_mul workload=llama3_70b_mlp_tp8_rank0_b4096_kn "
                      f"bytes_per_launch={want} source_sha256={bench.traffic_sources_digest()}"]
     assert "taken at commit abc123" in out and "gemm_bigwave_kernel<0, false, 128, 256> grid 131072" in out
+
+
+def _trace_csv(path, rows):
+    """A rocprofv3 kernel-trace CSV: rows of (kernel name, grid workgroups, start ns, end ns)."""
+    import csv
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Grid_Size_X", "Workgroup_Size_X", "Start_Timestamp", "End_Timestamp"])
+        for name, grid, t0, t1 in rows:
+            w.writerow([name, grid * 256, 256, t0, t1])
+
+
+def test_trace_summary_from_trace_and_counter_files(tmp_path, capsys):
+    """One row per single-kernel run: the library's dispatches grouped by kernel and grid (torch's
+    set-up kernels ignored), the per-call sum of their averages, the run's graph and eager times
+    from its JSON line, and the HBM bytes per call from the counter runs scaled by the copy."""
+    spec = importlib.util.spec_from_file_location("bench_mod", BENCH)
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    d = tmp_path / "ops"
+    main = "void ttl::(anonymous namespace)::gemm_bigwave_kernel<2, false, 128, 256, false>(ttl::GemmParams)"
+    fin = "void ttl::(anonymous namespace)::splitk_finalize_kernel<0>(ttl::GemmParams)"
+    setup = "void at::native::(anonymous namespace)::distribution_elementwise_grid_stride_kernel<4>(int)"
+    run = d / "llama3_70b_layer_tp8__qkv"
+    # two calls: main 50 and 54 us, finalize 10 and 12 us; a torch kernel that must not count
+    _trace_csv(str(run / "trace" / "ct_kernel_trace.csv"),
+               [(setup, 2048, 0, 900_000), (main, 225, 1_000_000, 1_050_000), (fin, 2720, 1_051_000, 1_061_000),
+                (main, 225, 2_000_000, 2_054_000), (fin, 2720, 2_055_000, 2_067_000)])
+    (run / "ct.json").write_text(json.dumps({"workload": "llama3_70b_layer_tp8", "tokens": 2176,
+                                             "step_us_graph": 70.0,
+                                             "kernels": {"qkv": {"us": 71.0, "gbs": 1000.0}}}) + "\n")
+    for counter, factor in (("FETCH_SIZE", 0.5), ("WRITE_SIZE", 1.0)):
+        _counter_csv(str(d / f"copy_{counter}" / "c_counter_collection.csv"),
+                     [("__amd_rocclr_copyBuffer", 4096, 1024 * factor)], counter)
+        (d / f"copy_{counter}.log").write_text('{"copy_bytes_per_launch": 1048576, "launches": 5}\n')
+        _counter_csv(str(run / f"pmc_{counter}" / "c_counter_collection.csv"),
+                     [(setup, 100, 1e6), (main, 225 * 256, 2000 * factor), (main, 225 * 256, 2000 * factor),
+                      (fin, 2720 * 256, 500 * factor), (fin, 2720 * 256, 500 * factor)], counter)
+    bench.trace_summary(str(d))
+    out = capsys.readouterr().out
+    row = next(line for line in out.splitlines() if line.startswith("| llama3_70b_layer_tp8"))
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    assert cells[2] == "qkv"
+    assert "`gemm_bigwave_kernel<2, false, 128, 256, false>` 225: 52.0" in cells[3]
+    assert "`splitk_finalize_kernel<0>` 2720: 11.0" in cells[3] and "distribution" not in cells[3]
+    assert cells[4:7] == ["63.0", "70.0", "71.0"]
+    per_call_mb = (2000 + 500) * 1024 / 1e6  # the true bytes: the calibration undoes the counter scale
+    assert cells[7] == f"{per_call_mb:.1f}" and cells[8] == f"{per_call_mb:.1f}"
+    assert cells[9] == f"{1000.0 * 71.0 * 1e3 / 1e6:.1f}"
