@@ -634,9 +634,11 @@ def read_counter_csv(path, counter):
 
 def classify_dispatch(name):
     """Which entry point of the bench step a dispatch belongs to (None for the set-up kernels)."""
-    if "gemm_bigwave_kernel<1," in name or "gemm_skinny_kernel<1," in name or "splitk_finalize_kernel<1>" in name:
+    if ("gemm_bigwave_kernel<1," in name or "gemm_bigwave16_kernel<1>" in name or "gemm_skinny_kernel<1," in name
+            or "splitk_finalize_kernel<1>" in name):
         return "shard_linear_col_silu_mul"
-    if "gemm_bigwave_kernel<0," in name or "gemm_skinny_kernel<0," in name or "splitk_finalize_kernel<0>" in name:
+    if ("gemm_bigwave_kernel<0," in name or "gemm_bigwave16_kernel<0>" in name or "gemm_skinny_kernel<0," in name
+            or "splitk_finalize_kernel<0>" in name):
         return "shard_linear_row"
     if "reduce_rmsnorm_kernel" in name:
         return "reduce_partials_rmsnorm"
