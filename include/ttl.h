@@ -71,8 +71,8 @@ typedef int32_t ttl_epilogue;
  *   TTL_W_NK: the transpose stored row-major, [n][k], row stride k — how PyTorch-style Linear
  *             weights ([out_features, in_features]) are kept; the matrix cores read it without a
  *             transpose.  The rows one call reads (from the rank's first to its last weight
- *             column; for the row-parallel call all n rows) must span less than 2 GiB. */
-/*   TTL_W_BLOCKED: [k][n] cut into blocks of 64 k-rows x 128 columns, each block row-major (its 128
+ *             column; for the row-parallel call all n rows) must span less than 2 GiB.
+ *   TTL_W_BLOCKED: [k][n] cut into blocks of 64 k-rows x 128 columns, each block row-major (its 128
  *             columns contiguous), the blocks of one 128-column strip stored one after another
  *             down k, the strips one after another along n: element (i, j) lives at
  *             ((j/128)·(k/64) + i/64)·8192 + (i%64)·128 + j%128.  Needs k % 64 == 0 and
