@@ -94,6 +94,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="before the warm-up steps, repeat the step for this long (untimed) so that the "
+                         "GPU's clock, which starts from idle, reaches its loaded steady state")
     ap.add_argument("--batch", type=int, default=4096, help="tokens per step (4096 prefill; 64 decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the secondary 64-token decode line")
@@ -152,7 +155,7 @@ def stored_weight(ttl, W, lay):
     return W
 
 
-def run_mlp(ttl, torch, w, b, steps, warmup, seed, layout, rotate_ranks=False, graph=False):
+def run_mlp(ttl, torch, w, b, steps, warmup, seed, layout, rotate_ranks=False, graph=False, settle_ms=0.0):
     from tensor_transformer_linear_amd import workloads as wl
     dev = "cuda"
     inp = wl.mlp_inputs(w, b, seed=seed, device=dev)
@@ -196,6 +199,18 @@ def run_mlp(ttl, torch, w, b, steps, warmup, seed, layout, rotate_ranks=False, g
         if ev is not None:
             ev[3].record(st)
 
+    # Clock settle: the GPU arrives idle, and its clock governor takes tens of milliseconds of load
+    # to reach the steady state of a busy GPU (70B TP=8 step, one box: 702-706 us per step after the
+    # 5 warm-up steps alone, 674-677 us after 100 or 400).  The step repeats, untimed, for
+    # settle_ms first, synchronising every few steps so that the time is the GPU's.
+    t_end = time.perf_counter() + settle_ms / 1e3
+    i = 0
+    while time.perf_counter() < t_end:
+        step(i)
+        i += 1
+        if i % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -924,7 +939,7 @@ def main():
         return 0
     b = args.batch
     workload = f"llama3_70b_mlp_tp8_rank0_b{b}_{args.layout}"
-    res = run_mlp(ttl, torch, w, b, args.steps, args.warmup, seed=0, layout=args.layout,
+    res = run_mlp(ttl, torch, w, b, args.steps, args.warmup, seed=0, layout=args.layout, settle_ms=args.settle_ms,
                   rotate_ranks=(b < 512))
     ms = res["ms_per_step"]
     value = res["flops"] / (ms * 1e9)
@@ -949,6 +964,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
@@ -963,7 +979,7 @@ def main():
         "kernels": res["kernels"],
     }
     if not args.no_decode and b != 64:
-        dec = run_mlp(ttl, torch, w, 64, args.steps, args.warmup, seed=1, layout=args.layout,
+        dec = run_mlp(ttl, torch, w, 64, args.steps, args.warmup, seed=1, layout=args.layout, settle_ms=args.settle_ms,
                       rotate_ranks=True, graph=True)
         out["decode64"] = {"ms_per_step": dec["ms_per_step"], "ranks": "cycled 0..7 step by step",
                            "tflops": dec["flops"] / (dec["ms_per_step"] * 1e9),
