@@ -1,18 +1,23 @@
-// Tiled bf16 GEMM with one wave64 per SIMD and 256 x 256 tiles, fed to v_mfma_f32_16x16x32_bf16,
-// for weights stored [n][k] (both operands then reach the products with plain 16-byte LDS reads).
+// Tiled bf16 GEMM with one wave64 per SIMD and 256 x 256 tiles, fed to v_mfma_f32_16x16x32_bf16.
 //
-// Tiles, LDS layouts, direct-to-LDS copies and the per-k-tile schedule are those of the four-wave
-// kernel in gemm_bigwave.hip (32 x 32 x 16 products); a wave still owns 128 x 128 outputs, now as
-// 8 x 8 blocks of 16 x 16 (64 accumulators of four registers).  A slice is half a k32 step: slice s
-// of a k-tile multiplies the k32 step s / 2 of the wave's row blocks 4 (s % 2) .. 4 (s % 2) + 3 by
-// all eight column blocks, 32 products of 16 cycles, the length of a slice of the other kernel.
-// Each output sums the same products in the same k order as the 32 x 32 x 16 kernel, and the
-// results agree with it bit for bit (tested).  With [n][k] weights this kernel runs the 70B
-// TP=8 row GEMM at 4096 tokens 7 % and the SiLU·up column GEMM 2.5 % faster than the best launch of
-// the other kernel.  With [k][n] weights, whose fragments take two transposed half reads joined
-// at the product, the register allocator could not fit the 64 four-register accumulators beside
-// them (accumulators moved to and from other registers inside the loop), so that storage stays on
-// the 32 x 32 x 16 kernel.
+// Tiles, direct-to-LDS copies and the per-k-tile schedule are those of the four-wave kernel in
+// gemm_bigwave.hip (32 x 32 x 16 products); a wave still owns 128 x 128 outputs, now as 8 x 8
+// blocks of 16 x 16 (64 accumulators of four registers).  A slice is half a k32 step: slice s of a
+// k-tile multiplies the k32 step s / 2 of the wave's row blocks 4 (s % 2) .. 4 (s % 2) + 3 by all
+// eight column blocks, 32 products of 16 cycles, the length of a slice of the other kernel.  Each
+// output sums the same products in the same k order as the 32 x 32 x 16 kernel, and the results
+// agree with it bit for bit (tested).
+//
+// Both kernels keep the matrix cores equally busy per cycle (70B TP=8 row GEMM at 4096 tokens:
+// 2.81-2.87 M active cycles per launch for either kernel and storage), but under the board's power
+// cap this one runs at a higher clock: the 16 x 16 x 32 product moves fewer accumulator bytes per
+// flop.  Measured on one box against the 32 x 32 x 16 kernel's best launch: 8 % faster on that row
+// GEMM and on the SiLU·up column GEMM, with [k][n] or [n][k] weights.
+//
+// Weights stored [n][k] reach the products with plain 16-byte LDS reads, as the activations do.
+// Weights stored [k][n] (plain or in 64 x 128 blocks) are staged [k][n] and read with
+// ds_read_b64_tr_b16, two transposed half reads per fragment, joined at the product; their products
+// are written out as asm with the accumulator tied in place (see mfma_one).
 //
 // Per k-tile t and wave (order pinned with scheduling barriers):
 //   slice 0: 32 MFMAs, with the LDS reads of slice 2 of tile t (its row blocks and the weight
@@ -28,8 +33,7 @@
 // and k = 8 (l / 16) .. + 7 of the k32 step; second operand lane l holds activation row l % 16 and
 // the same k; accumulator register r of lane l is output row l % 16, column 4 (l / 16) + r.
 //
-// K must be a multiple of 64; [n][k] weights; no k splits and no tile sets (whole launches of
-// 256 x 256 tiles).
+// K must be a multiple of 64; no k splits and no tile sets (whole launches of 256 x 256 tiles).
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -54,12 +58,24 @@ constexpr int kACopies = kAElems * 2 / 1024 / kWaves;  // 8
 constexpr int kBCopies = kBElems * 2 / 1024 / kWaves;  // 8
 constexpr int kCopies = kACopies + kBCopies;
 constexpr int kStages = 2;
+constexpr int kBChunks = kBN / 8;                      // 16-B chunks per staged [k][n] row: 32
+constexpr int kKRowsPerCopy = 64 / kBChunks;           // k rows per 1-KiB copy of a [k][n] stage: 2
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-template <int MODE>
+// Slot permutation of a staged [k][n] row (32 chunks of 16 bytes): chunk c of k row r sits at slot
+// c ^ kn_swizzle(r).  A transposed weight read covers 4 consecutive k rows in each 16-lane group,
+// and the two groups of a half-wave are 8 rows apart at the same columns: 4 (r % 4) spreads the 4
+// rows of a group over the banks, 2 ((r / 8) % 2) puts the other group on the other half of them,
+// so that the 32 lanes of a half-wave read 256 distinct bytes (without the second term every read
+// was a two-way bank conflict: 15x the conflict cycles of the [n][k] reads, 70B TP=8 row GEMM).
+__host__ __device__ constexpr int kn_swizzle(int r) { return (4 * (r % 4)) ^ (2 * ((r >> 3) & 1)); }
+
+// WNK: weights stored [n][k]; otherwise [k][n], in 64 x 128 blocks when BLK.
+template <int MODE, bool WNK, bool BLK>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void gemm_bigwave16_kernel(const GemmParams p) {
+  static_assert(!(WNK && BLK), "blocked storage is a [k][n] storage");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages * kStageElems];
 
   const int tid = threadIdx.x;
@@ -90,11 +106,23 @@ void gemm_bigwave16_kernel(const GemmParams p) {
   uint32_t b_off[kBCopies];
 #pragma unroll
   for (int i = 0; i < kBCopies; ++i) {
-    const int n = (kBCopies * wave + i) * kRowsPerCopy + lane / kChunks;
-    const int chunk = (lane % kChunks) ^ ((n / kRowsPer256) % kChunks);
+    const int q = kBCopies * wave + i;
     bool ok;
-    const int64_t wrow = weight_column<MODE, kWN>(p, n0, n & ~7, ok) + (n & 7);
-    b_off[i] = ok ? (uint32_t)((wrow * p.ldb + chunk * 8) * 2) : kOob;
+    if constexpr (WNK) {
+      const int n = q * kRowsPerCopy + lane / kChunks;
+      const int chunk = (lane % kChunks) ^ ((n / kRowsPer256) % kChunks);
+      const int64_t wrow = weight_column<MODE, kWN>(p, n0, n & ~7, ok) + (n & 7);
+      b_off[i] = ok ? (uint32_t)((wrow * p.ldb + chunk * 8) * 2) : kOob;
+    } else {
+      // [64 k][256 n]: block q holds k rows 2q, 2q + 1; lane l lands in row 2q + l/32 at slot l%32,
+      // which holds n-chunk slot ^ kn_swizzle(row).
+      const int krow = kKRowsPerCopy * q + lane / kBChunks;
+      const int chunk = (lane % kBChunks) ^ kn_swizzle(krow);
+      const int64_t wcol = weight_column<MODE, kWN>(p, n0, chunk * 8, ok);
+      b_off[i] = !ok ? kOob
+                 : BLK ? blocked_offset(krow, wcol, p.ldb)
+                           : (uint32_t)(((int64_t)krow * p.ldb + wcol) * 2);
+    }
   }
   // A copy i sits 16 (i / 2) rows past copy i % 2.
   const uint32_t a_step2 = (uint32_t)(2 * kRowsPerCopy * p.lda * 2);
@@ -104,7 +132,9 @@ void gemm_bigwave16_kernel(const GemmParams p) {
   };
   auto b_desc = [&](int t) {
     const int k0 = t * kBK;
-    return buffer_desc(p.B + k0, ((int64_t)(p.b_rows - 1) * p.ldb + (p.K - k0)) * 2);
+    return WNK ? buffer_desc(p.B + k0, ((int64_t)(p.b_rows - 1) * p.ldb + (p.K - k0)) * 2)
+           : BLK ? blocked_desc(p.B, p.b_rows, k0)
+                     : buffer_desc(p.B + (int64_t)k0 * p.ldb, (int64_t)(p.K - k0) * p.ldb * 2);
   };
   const uint32_t wave_lds_a = lds0 + (uint32_t)(wave * kACopies * 1024);
   const uint32_t wave_lds_b = lds0 + (uint32_t)(kAElems * 2 + wave * kBCopies * 1024);
@@ -135,7 +165,20 @@ void gemm_bigwave16_kernel(const GemmParams p) {
     ra_off[step] = (wm * kWM + r16) * kBK + slot * 8;
     rb_off[step] = kAElems + (wn * kWN + r16) * kBK + slot * 8;
   }
+  // [64 k][256 n] staging, read with ds_read_b64_tr_b16 (each 16-lane group receives the transpose
+  // of a 4 (k) x 16 (n) block): group g = lane/16 reads k row 32 step + 8 g + 4 h + (lane%16)/4 of
+  // half h at n = 128 wn + 16 ni + 4 (lane%4), i.e. chunk 16 wn + 2 ni + (lane%4)/2, stored at slot
+  // chunk ^ kn_swizzle(k) = chunk ^ 4 ((lane%16)/4) ^ 2 (g%2).
+  int rt_off[kNB];
+  {
+    const int krow = 8 * g4 + (r16 >> 2);
+    const int x = kn_swizzle(krow);
+#pragma unroll
+    for (int ni = 0; ni < kNB; ++ni)
+      rt_off[ni] = kAElems + krow * kBN + (((kWN / 8) * wn + 2 * ni + ((lane & 3) >> 1)) ^ x) * 8 + 4 * (lane & 1);
+  }
   bf16x8_t af[4][kMB / 2], bv[2][kNB];
+  i16x4_t bl[2][kNB], bh[2][kNB];
   // Reads of slice s: j < 4 are its row-block fragments; an even slice also reads its step's eight
   // weight fragments.
   constexpr int kBReads = kNB;
@@ -146,9 +189,15 @@ void gemm_bigwave16_kernel(const GemmParams p) {
     if (j < kMB / 2) {
       const int mb = (s % 2) * (kMB / 2) + j;
       af[s][j] = *reinterpret_cast<const bf16x8_t*>(st + ra_off[step] + mb * 16 * kBK);
-    } else {
+    } else if constexpr (WNK) {
       const int ni = j - kMB / 2;
       bv[step][ni] = *reinterpret_cast<const bf16x8_t*>(st + rb_off[step] + ni * 16 * kBK);
+    } else {
+      // the two transposed halves (k 8 g .. + 3 and + 4 .. + 7), joined at once into the fragment
+      const int ni = j - kMB / 2;
+      const uint16_t* b = st + rt_off[ni] + step * 32 * kBN;
+      bl[step][ni] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b));
+      bh[step][ni] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b + 4 * kBN));
     }
   };
 
@@ -159,12 +208,37 @@ void gemm_bigwave16_kernel(const GemmParams p) {
     for (int ni = 0; ni < kNB; ++ni)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[mb][ni][r] = 0.0f;
+  if constexpr (!WNK) {
+    // The zeros are placed in the accumulation registers here (the empty statements take them as
+    // operands), and a vector write of a register read as a product's accumulator must lead it by
+    // two wait states: the nops give several.
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+      for (int ni = 0; ni < kNB; ++ni) asm volatile("" : "+a"(acc[mb][ni]));
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7");
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
 
   // MFMA j (0 .. 31) of slice s: row block 4 (s % 2) + j / 8, column block j % 8.
   auto mfma_one = [&](int s, int j) {
     const int ml = j / kNB, ni = j % kNB, mb = (s % 2) * (kMB / 2) + ml, step = s / 2;
-    acc[mb][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[step][ni], af[s][ml], acc[mb][ni], 0, 0, 0);
+    bf16x8_t b;
+    if constexpr (WNK) b = bv[step][ni];
+    else b = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(bl[step][ni], bh[step][ni], 0, 1, 2, 3, 4, 5, 6, 7));
+    if constexpr (WNK) {
+      acc[mb][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, af[s][ml], acc[mb][ni], 0, 0, 0);
+    } else {
+      // Written out, with the accumulator as one read-write operand: through the builtin, the
+      // register allocator gave some products' accumulator input and output different registers
+      // and moved those accumulators through other registers every k-tile (the two-read weight
+      // fragments leave it less room).  The compiler does not see this as a matrix instruction,
+      // so the waits it would insert around one are made explicit (before the first product and
+      // after the last); the products' operands come from LDS reads, whose waits it does insert.
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[mb][ni]) : "v"(b), "v"(af[s][ml]));
+    }
   };
 
   // ---- Prologue: tiles 0 and 1 in flight, tile 0 landed, slices 0 and 1 of tile 0 read.
@@ -241,6 +315,13 @@ void gemm_bigwave16_kernel(const GemmParams p) {
   for (; t + kStages < nk; ++t) k_tile(t, std::true_type{}, std::true_type{});
   if (t + 1 < nk) k_tile(t++, std::true_type{}, std::false_type{});
   k_tile(t, std::false_type{}, std::false_type{});
+  if constexpr (!WNK) {
+    // A product's results may be read by other vector instructions only some wait states after
+    // it (about its pass count plus two; 8 passes here): 32 before the epilogue reads.
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 15\n\ts_nop 15");
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   // ---- Epilogue: lane l holds output row 16 mb + l % 16 and columns 16 ni + 4 (l / 16) .. + 3, so
   // direct stores would write 32-byte pieces of 16 rows per instruction.  Instead each wave writes
@@ -302,14 +383,16 @@ void gemm_bigwave16_kernel(const GemmParams p) {
 
 template <int MODE>
 void launch_one16(const GemmParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE>), dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(kThreads),
-                     0, stream, p);
+  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
+  if (p.w_nk) hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, true, false>), grid, dim3(kThreads), 0, stream, p);
+  else if (p.w_blk) hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, false, true>), grid, dim3(kThreads), 0, stream, p);
+  else hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, false, false>), grid, dim3(kThreads), 0, stream, p);
 }
 
 }  // namespace
 
 bool gemm_bigwave16_supports(const GemmParams& p) {
-  return p.w_nk && p.K % kBK == 0 && p.K > 0 && p.splits <= 1 && p.rects == 0 && !p.narrow && p.persist == 0;
+  return p.K % kBK == 0 && p.K > 0 && p.splits <= 1 && p.rects == 0 && !p.narrow && p.persist == 0;
 }
 
 hipError_t launch_gemm_bigwave16(const GemmParams& p, hipStream_t stream) {

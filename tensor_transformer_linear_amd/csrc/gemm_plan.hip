@@ -8,8 +8,9 @@
 // A launch of whole rounds of 256 x 256 tiles plus a short last round (e.g. 288 tiles: 2176 rows
 // x 8192 columns) is cut by rows: the whole rounds to the tiled kernel, the last few row-tiles to
 // the split-K kernel.  One whose last round is more than half full (e.g. 448 tiles: 4096 rows x
-// 3584 SiLU·up columns) is cut per column strip into 256-row tiles that fill the whole rounds and
-// 192-row tiles that fill one more round, which then takes three quarters of a round's time.
+// 3584 SiLU·up columns) runs as whole tiles of the 16 x 16 x 32 kernel, whatever the weight
+// storage.  The cut of such a launch per column strip into 256-row tiles that fill the whole rounds
+// and 192-row tiles that fill one more round (32 x 32 x 16 kernel) remains as an override.
 //
 // Workspace: split-K launches with more than one split write fp32 partial tiles that a second
 // kernel reduces.  The library keeps one device buffer per (GPU, stream) for them, allocated (or
@@ -167,8 +168,8 @@ hipError_t launch_persist(GemmParams& p, Ctx& c) {
   return run_bigwave(c, p);
 }
 
-// 256 x 256 tiles over all of p by the 16 x 16 x 32 four-wave kernel where it applies ([n][k]
-// weights), else as launch_tiles.
+// 256 x 256 tiles over all of p by the 16 x 16 x 32 four-wave kernel where it applies (K a multiple
+// of 64), else as launch_tiles.
 hipError_t launch_tiles16(GemmParams& p, Ctx& c) {
   p.tiles_m = (int32_t)cdiv(p.M, gemm_tile_rows());
   p.tiles_n = (int32_t)cdiv(p.N, gemm_tile_cols(p.mode));
@@ -516,20 +517,21 @@ hipError_t plan_and_launch(GemmParams& p, Ctx& c) {
     return launch_splitk(p, c);
   }
   const int64_t rounds = tiles / n_cu, rem = tiles % n_cu;
-  // Weights stored [n][k]: the 16 x 16 x 32 kernel over whole tiles wherever the last round is full
-  // or more than half full (measured faster than the persistent grid and the row cut of the
-  // 32 x 32 x 16 kernel: 70B TP=8 at 4096 tokens, row GEMM 171-177 against 186 us, SiLU·up column
-  // GEMM 341-343 against 350 us); a short last round still goes to the split-K kernel below.
-  bool nk16 = false;
+  // The 16 x 16 x 32 kernel over whole tiles wherever the last round is full or more than half
+  // full, for every weight storage (measured faster than the persistent grid and the row cut of the
+  // 32 x 32 x 16 kernel, 70B TP=8 at 4096 tokens: [n][k] weights, row GEMM 171-177 against 186 us,
+  // SiLU·up column GEMM 341-343 against 350 us; [k][n] weights, same box, 172.9 against 188.5 us
+  // and 346.9 against 377.9 us); a short last round still goes to the split-K kernel below.
+  bool use16 = false;
   {
     GemmParams q = p;
     q.splits = 1;
     q.narrow = 0;
     q.rects = 0;
     q.persist = 0;
-    nk16 = gemm_bigwave16_supports(q);
+    use16 = gemm_bigwave16_supports(q);
   }
-  if (nk16 && (rounds == 0 || rem == 0 || 2 * rem > n_cu)) return launch_tiles16(p, c);
+  if (use16 && (rounds == 0 || rem == 0 || 2 * rem > n_cu)) return launch_tiles16(p, c);
   // Whole rounds (e.g. 512 tiles: 4096 x 8192 row-parallel outputs) run as whole tiles: with the
   // epilogue staged through LDS they beat the persistent grid, whose first tile must store
   // directly while the ring holds its next tile's first k-tiles (70B TP=8 row GEMM at 4096 tokens,
@@ -549,7 +551,7 @@ hipError_t plan_and_launch(GemmParams& p, Ctx& c) {
     if (head_row_tiles >= 1 && head_row_tiles < tiled_m) {
       GemmParams head = p;
       head.M = (int32_t)(head_row_tiles * gemm_tile_rows());
-      hipError_t e = nk16 ? launch_tiles16(head, c) : launch_tiles(head, 0, c);
+      hipError_t e = use16 ? launch_tiles16(head, c) : launch_tiles(head, 0, c);
       if (e != hipSuccess) return e;
       GemmParams tail = p;
       tail.A = p.A + (int64_t)head.M * p.lda;
@@ -558,7 +560,7 @@ hipError_t plan_and_launch(GemmParams& p, Ctx& c) {
       return launch_splitk(tail, c);
     }
   }
-  return nk16 ? launch_tiles16(p, c) : launch_tiles(p, 0, c);
+  return use16 ? launch_tiles16(p, c) : launch_tiles(p, 0, c);
 }
 
 }  // namespace
