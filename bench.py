@@ -46,6 +46,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (8 TB/s)
 # Kernel sources whose HBM traffic counters are recorded under profiles/: the recorded figures
 # apply only while these files are unchanged.
 TRAFFIC_SOURCES = ("tensor_transformer_linear_amd/csrc/gemm_bigwave.hip",
+                   "tensor_transformer_linear_amd/csrc/gemm_bigwave16.hip",
                    "tensor_transformer_linear_amd/csrc/gemm_common.h",
                    "tensor_transformer_linear_amd/csrc/gemm_plan.hip",
                    "tensor_transformer_linear_amd/csrc/kernels.h")
@@ -649,10 +650,10 @@ def read_counter_csv(path, counter):
 
 def classify_dispatch(name):
     """Which entry point of the bench step a dispatch belongs to (None for the set-up kernels)."""
-    if ("gemm_bigwave_kernel<1," in name or "gemm_bigwave16_kernel<1>" in name or "gemm_skinny_kernel<1," in name
+    if ("gemm_bigwave_kernel<1," in name or "gemm_bigwave16_kernel<1," in name or "gemm_skinny_kernel<1," in name
             or "splitk_finalize_kernel<1>" in name):
         return "shard_linear_col_silu_mul"
-    if ("gemm_bigwave_kernel<0," in name or "gemm_bigwave16_kernel<0>" in name or "gemm_skinny_kernel<0," in name
+    if ("gemm_bigwave_kernel<0," in name or "gemm_bigwave16_kernel<0," in name or "gemm_skinny_kernel<0," in name
             or "splitk_finalize_kernel<0>" in name):
         return "shard_linear_row"
     if "reduce_rmsnorm_kernel" in name:

@@ -33,7 +33,8 @@
 // and k = 8 (l / 16) .. + 7 of the k32 step; second operand lane l holds activation row l % 16 and
 // the same k; accumulator register r of lane l is output row l % 16, column 4 (l / 16) + r.
 //
-// K must be a multiple of 64; no k splits and no tile sets (whole launches of 256 x 256 tiles).
+// K must be a multiple of 64; no k splits.  Whole launches of 256 x 256 tiles, or tile sets of
+// 256-row or 192-row tiles (the planner's cut of a launch whose last round is partly idle).
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -49,14 +50,10 @@ constexpr int kBK = 64;
 constexpr int kChunks = kBK / 8;         // 16-B chunks per staged [rows][k] row
 constexpr int kRowsPer256 = 256 / (2 * kBK);
 constexpr int kRowsPerCopy = 1024 / (2 * kBK);
-constexpr int kBM = 256, kWM = 128;
 constexpr int kWN = 128, kBN = 256;
-constexpr int kMB = kWM / 16, kNB = kWN / 16;  // 16 x 16 blocks per wave: 8 x 8
-constexpr int kMpsl = (kMB / 2) * kNB;          // MFMAs per slice: 32
-constexpr int kAElems = kBM * kBK, kBElems = kBK * kBN, kStageElems = kAElems + kBElems;
-constexpr int kACopies = kAElems * 2 / 1024 / kWaves;  // 8
+constexpr int kNB = kWN / 16;                   // 16-column blocks per wave: 8
+constexpr int kBElems = kBK * kBN;
 constexpr int kBCopies = kBElems * 2 / 1024 / kWaves;  // 8
-constexpr int kCopies = kACopies + kBCopies;
 constexpr int kStages = 2;
 constexpr int kBChunks = kBN / 8;                      // 16-B chunks per staged [k][n] row: 32
 constexpr int kKRowsPerCopy = 64 / kBChunks;           // k rows per 1-KiB copy of a [k][n] stage: 2
@@ -71,11 +68,20 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // was a two-way bank conflict: 15x the conflict cycles of the [n][k] reads, 70B TP=8 row GEMM).
 __host__ __device__ constexpr int kn_swizzle(int r) { return (4 * (r % 4)) ^ (2 * ((r >> 3) & 1)); }
 
-// WNK: weights stored [n][k]; otherwise [k][n], in 64 x 128 blocks when BLK.
-template <int MODE, bool WNK, bool BLK>
+// WNK: weights stored [n][k]; otherwise [k][n], in 64 x 128 blocks when BLK.  BM rows per tile:
+// 256, or 192 (96 per wave) for the last round of a launch whose 256-row tiles would leave that
+// round partly idle.
+template <int MODE, bool WNK, bool BLK, int BM>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void gemm_bigwave16_kernel(const GemmParams p) {
   static_assert(!(WNK && BLK), "blocked storage is a [k][n] storage");
+  static_assert(BM == 256 || BM == 192, "tile heights built: 256 and 192");
+  constexpr int kBM = BM, kWM = BM / 2;
+  constexpr int kMB = kWM / 16;                          // 16-row blocks per wave: 8 or 6
+  constexpr int kMpsl = (kMB / 2) * kNB;                 // MFMAs per slice: 32 or 24
+  constexpr int kAElems = kBM * kBK, kStageElems = kAElems + kBElems;
+  constexpr int kACopies = kAElems * 2 / 1024 / kWaves;  // 8 or 6
+  constexpr int kCopies = kACopies + kBCopies;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages * kStageElems];
 
   const int tid = threadIdx.x;
@@ -83,19 +89,37 @@ void gemm_bigwave16_kernel(const GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / 2, wn = wave % 2;
 
-  int tile_m, tile_n;
-  tile_coords((int)blockIdx.x, p.tiles_m, p.tiles_n, tile_m, tile_n);
-  const int m0 = tile_m * kBM;
+  // Tile sets (p.rects > 0): block b < rect_tmc[0] * rect_tnc[0] is a tile of rectangle 0, the
+  // rest of rectangle 1; rectangle i is rect_tmc[i] row-tiles from row rect_row0[i] by rect_tnc[i]
+  // tile columns from tile column rect_tn0[i], walked in groups of rect_group[i] row-tiles.
+  int tile_m, tile_n, row0 = 0;
+  {
+    const int bid = (int)blockIdx.x;
+    if (p.rects > 0) {
+      const int c0 = p.rect_tmc[0] * p.rect_tnc[0];
+      const bool second = p.rects > 1 && bid >= c0;
+      const int tmc = second ? p.rect_tmc[1] : p.rect_tmc[0];
+      const int tnc = second ? p.rect_tnc[1] : p.rect_tnc[0];
+      const int group = second ? p.rect_group[1] : p.rect_group[0];
+      tile_coords(bid - (second ? c0 : 0), tmc, tnc, tile_m, tile_n, group > 0 ? group : 4);
+      tile_n += second ? p.rect_tn0[1] : p.rect_tn0[0];
+      row0 = second ? p.rect_row0[1] : p.rect_row0[0];
+    } else {
+      tile_coords(bid, p.tiles_m, p.tiles_n, tile_m, tile_n);
+    }
+  }
+  const int m0 = row0 + tile_m * kBM;
   const int n0 = tile_n * (MODE == kSiluMul ? kBN / 2 : kBN);
   const int nk = p.K / kBK;  // >= 1
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds);
 
-  // ---- Copy offsets.  Copy i < 8 of this wave moves block 8*wave + i of the A stage: rows
-  // 8 (8 wave + i) + l/8, whose swizzle depends on i only through i % 2, so two offset registers
-  // serve all eight (the rest, 16 (i / 2) rows, goes in the copy's scalar offset; rows past M lie
-  // beyond the descriptor's range and read zeros).  Copy 8 + i moves block 8*wave + i of the B
-  // stage, the weight rows (output columns) 8 (8 wave + i) + l/8, through the column map, which may
-  // jump between segments, so each has its own offset register.
+  // ---- Copy offsets.  Copy i < kACopies (8, or 6 for 192-row tiles) of this wave moves block
+  // kACopies*wave + i of the A stage: rows 8 (kACopies wave + i) + l/8, whose swizzle depends on i
+  // only through i % 2, so two offset registers serve all of them (the rest, 16 (i / 2) rows, goes
+  // in the copy's scalar offset; rows past M lie beyond the descriptor's range and read zeros).
+  // Copy kACopies + i moves block 8*wave + i of the B stage: with [n][k] weights the weight rows
+  // (output columns) 8 (8 wave + i) + l/8, through the column map, which may jump between
+  // segments, so each has its own offset register.
   uint32_t a_off[2];
 #pragma unroll
   for (int par = 0; par < 2; ++par) {
@@ -286,24 +310,33 @@ void gemm_bigwave16_kernel(const GemmParams p) {
       ad = a_desc(t + kStages);
       bd = b_desc(t + kStages);
     }
-    // slice 2: reads of slice 0 of tile t+1, copies 0..7 after every fourth MFMA
+    // slice 2: reads of slice 0 of tile t+1; copy c follows MFMA slot (c + 1) 2 kMpsl / kCopies - 1
+    // of slices 2-3 (slots kMpsl.. are slice 3's): after every fourth MFMA for 256-row tiles.
     constexpr int kR2 = kMB / 2 + kBReads;
 #pragma unroll
     for (int j = 0; j < kMpsl; ++j) {
       mfma_one(2, j);
-      if (COPY && j % 4 == 3) copy_one(t + kStages, j / 4, ad, bd);
+      if (COPY) {
+#pragma unroll
+        for (int c = 0; c < kCopies; ++c)
+          if ((c + 1) * 2 * kMpsl / kCopies - 1 == j) copy_one(t + kStages, c, ad, bd);
+      }
       if (NEXT) {
 #pragma unroll
         for (int r = j * kR2 / kMpsl; r < (j + 1) * kR2 / kMpsl; ++r) read_one(t + 1, 0, r);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // slice 3: reads of slice 1 of tile t+1, copies 8..15
+    // slice 3: reads of slice 1 of tile t+1, the other copies
     constexpr int kR3 = kMB / 2;
 #pragma unroll
     for (int j = 0; j < kMpsl; ++j) {
       mfma_one(3, j);
-      if (COPY && j % 4 == 3) copy_one(t + kStages, kCopies / 2 + j / 4, ad, bd);
+      if (COPY) {
+#pragma unroll
+        for (int c = 0; c < kCopies; ++c)
+          if ((c + 1) * 2 * kMpsl / kCopies - 1 == kMpsl + j) copy_one(t + kStages, c, ad, bd);
+      }
       if (NEXT) {
 #pragma unroll
         for (int r = j * kR3 / kMpsl; r < (j + 1) * kR3 / kMpsl; ++r) read_one(t + 1, 1, r);
@@ -381,24 +414,34 @@ void gemm_bigwave16_kernel(const GemmParams p) {
   }
 }
 
-template <int MODE>
+template <int MODE, int BM>
 void launch_one16(const GemmParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
-  if (p.w_nk) hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, true, false>), grid, dim3(kThreads), 0, stream, p);
-  else if (p.w_blk) hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, false, true>), grid, dim3(kThreads), 0, stream, p);
-  else hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, false, false>), grid, dim3(kThreads), 0, stream, p);
+  const int blocks = p.rects > 0 ? p.rect_tmc[0] * p.rect_tnc[0] + (p.rects > 1 ? p.rect_tmc[1] * p.rect_tnc[1] : 0)
+                                 : p.tiles_m * p.tiles_n;
+  const dim3 grid((unsigned)blocks);
+  if (p.w_nk) hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, true, false, BM>), grid, dim3(kThreads), 0, stream, p);
+  else if (p.w_blk) hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, false, true, BM>), grid, dim3(kThreads), 0, stream, p);
+  else hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, false, false, BM>), grid, dim3(kThreads), 0, stream, p);
+}
+
+template <int BM>
+void launch_rows16(const GemmParams& p, hipStream_t stream) {
+  if (p.mode == kSiluMul) launch_one16<kSiluMul, BM>(p, stream);
+  else launch_one16<kPlain, BM>(p, stream);
 }
 
 }  // namespace
 
 bool gemm_bigwave16_supports(const GemmParams& p) {
-  return p.K % kBK == 0 && p.K > 0 && p.splits <= 1 && p.rects == 0 && !p.narrow && p.persist == 0;
+  // Tile sets with 256-row or 192-row tiles, or whole launches of 256-row tiles.
+  const bool rows_ok = p.rects > 0 ? (p.tile_rows == 256 || p.tile_rows == 192) : (p.tile_rows == 0 || p.tile_rows == 256);
+  return p.K % kBK == 0 && p.K > 0 && p.splits <= 1 && !p.narrow && p.persist == 0 && rows_ok;
 }
 
 hipError_t launch_gemm_bigwave16(const GemmParams& p, hipStream_t stream) {
   if (!gemm_bigwave16_supports(p)) return hipErrorInvalidValue;
-  if (p.mode == kSiluMul) launch_one16<kSiluMul>(p, stream);
-  else launch_one16<kPlain>(p, stream);
+  if (p.tile_rows == 192) launch_rows16<192>(p, stream);
+  else launch_rows16<256>(p, stream);
   return hipGetLastError();
 }
 

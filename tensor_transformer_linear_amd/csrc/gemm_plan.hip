@@ -8,9 +8,9 @@
 // A launch of whole rounds of 256 x 256 tiles plus a short last round (e.g. 288 tiles: 2176 rows
 // x 8192 columns) is cut by rows: the whole rounds to the tiled kernel, the last few row-tiles to
 // the split-K kernel.  One whose last round is more than half full (e.g. 448 tiles: 4096 rows x
-// 3584 SiLU·up columns) runs as whole tiles of the 16 x 16 x 32 kernel, whatever the weight
-// storage.  The cut of such a launch per column strip into 256-row tiles that fill the whole rounds
-// and 192-row tiles that fill one more round (32 x 32 x 16 kernel) remains as an override.
+// 3584 SiLU·up columns) is cut per column strip into 256-row tiles that fill the whole rounds and
+// 192-row tiles that fill one more round, which then takes three quarters of a round's time.  The
+// 256 x 256 and 192 x 256 tiles run on the 16 x 16 x 32 kernel for every weight storage.
 //
 // Workspace: split-K launches with more than one split write fp32 partial tiles that a second
 // kernel reduces.  The library keeps one device buffer per (GPU, stream) for them, allocated (or
@@ -103,6 +103,10 @@ hipError_t workspace(Ctx& c, size_t bytes, void** out) {
 hipError_t run_bigwave(Ctx& c, const GemmParams& p) { return c.dry ? hipSuccess : launch_gemm_bigwave(p, c.stream); }
 hipError_t run_tiled(Ctx& c, const GemmParams& p) { return c.dry ? hipSuccess : launch_gemm_tiled(p, c.stream); }
 hipError_t run_tiled16(Ctx& c, const GemmParams& p) { return c.dry ? hipSuccess : launch_gemm_bigwave16(p, c.stream); }
+// A tile set (256-row or 192-row tiles): the 16 x 16 x 32 kernel where it applies, else the 32 x 32 x 16 one.
+hipError_t run_tileset(Ctx& c, const GemmParams& p) {
+  return gemm_bigwave16_supports(p) ? run_tiled16(c, p) : run_bigwave(c, p);
+}
 hipError_t run_skinny(Ctx& c, const GemmParams& p, int mb) {
   return c.dry ? hipSuccess : launch_gemm_skinny(p, mb, c.stream);
 }
@@ -383,13 +387,13 @@ hipError_t launch_mixed(GemmParams& p, const MixedRows& m, int64_t cus, Ctx& c) 
       t.rect_tmc[r] = q[pass].rect_tmc[r];
       t.rect_group[r] = q[pass].rect_group[r];
     }
-    const hipError_t e = run_bigwave(c, t);
+    const hipError_t e = run_tileset(c, t);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
-// 192 x 256 tiles of the four-wave kernel over all of p, as one tile set.
+// 192 x 256 tiles of the four-wave kernels over all of p, as one tile set.
 hipError_t launch_short(GemmParams& p, Ctx& c) {
   GemmParams q = p;
   q.splits = 1;
@@ -401,7 +405,7 @@ hipError_t launch_short(GemmParams& p, Ctx& c) {
   q.rect_tnc[0] = (int32_t)cdiv(p.N, gemm_tile_cols(p.mode));
   q.rect_row0[0] = 0;
   q.rect_tmc[0] = (int32_t)cdiv(p.M, 192);
-  return run_bigwave(c, q);
+  return run_tileset(c, q);
 }
 
 // 256 x 256 (or, narrow, 256 x 128) tiles of the four-wave kernel cut into `splits` k ranges
@@ -517,11 +521,17 @@ hipError_t plan_and_launch(GemmParams& p, Ctx& c) {
     return launch_splitk(p, c);
   }
   const int64_t rounds = tiles / n_cu, rem = tiles % n_cu;
-  // The 16 x 16 x 32 kernel over whole tiles wherever the last round is full or more than half
-  // full, for every weight storage (measured faster than the persistent grid and the row cut of the
-  // 32 x 32 x 16 kernel, 70B TP=8 at 4096 tokens: [n][k] weights, row GEMM 171-177 against 186 us,
-  // SiLU·up column GEMM 341-343 against 350 us; [k][n] weights, same box, 172.9 against 188.5 us
-  // and 346.9 against 377.9 us); a short last round still goes to the split-K kernel below.
+  // The 16 x 16 x 32 kernel, for every weight storage, wherever the last round is full or more than
+  // half full (measured faster than the persistent grid and every launch of the 32 x 32 x 16
+  // kernel, 70B TP=8 at 4096 tokens: [n][k] weights, row GEMM 171-177 against 186 us, SiLU·up column
+  // GEMM 341-343 against 350 us; [k][n] weights, same box, 172.9 against 188.5 us and 346.9 against
+  // 377.9 us): whole tiles, or, for whole rounds plus a last round more than half full, 256-row
+  // tiles for the whole rounds and 192-row tiles for the last one, which then takes about 3/4 of a
+  // round's time (SiLU·up column GEMM 345.1 -> 342.1 us with [k][n] weights, 335.7 -> 329.0 us with
+  // [n][k]).  Whole rounds (e.g. 512 tiles: 4096 x 8192 row-parallel outputs) run as whole tiles:
+  // with the epilogue staged through LDS they beat the persistent grid of the 32 x 32 x 16 kernel,
+  // whose first tile must store directly while the ring holds its next tile's first k-tiles.  A
+  // short last round still goes to the split-K kernel below.
   bool use16 = false;
   {
     GemmParams q = p;
@@ -531,16 +541,10 @@ hipError_t plan_and_launch(GemmParams& p, Ctx& c) {
     q.persist = 0;
     use16 = gemm_bigwave16_supports(q);
   }
-  if (use16 && (rounds == 0 || rem == 0 || 2 * rem > n_cu)) return launch_tiles16(p, c);
-  // Whole rounds (e.g. 512 tiles: 4096 x 8192 row-parallel outputs) run as whole tiles: with the
-  // epilogue staged through LDS they beat the persistent grid, whose first tile must store
-  // directly while the ring holds its next tile's first k-tiles (70B TP=8 row GEMM at 4096 tokens,
-  // [k][n] weights: 192.8 against 198.2 us on one box).
-  // Whole rounds of one tile per CU plus a last round more than half full: 256-row tiles for the
-  // whole rounds and 192-row tiles for the last one, which then takes 3/4 of a round's time.
-  if (gemm_bigwave_supports(p)) {
+  if (use16 && (rounds == 0 || rem == 0 || 2 * rem > n_cu)) {
     MixedRows m;
-    if (plan_mixed_rows(p.M, tiled_n, n_cu, m)) return launch_mixed(p, m, n_cu, c);
+    if (rounds >= 1 && rem > 0 && plan_mixed_rows(p.M, tiled_n, n_cu, m)) return launch_mixed(p, m, n_cu, c);
+    return launch_tiles16(p, c);
   }
   // Whole rounds plus a short last round (at most half the CUs): that round would take a whole
   // tile's time with most of the chip idle.  The row-tiles that fill the whole rounds go to the

@@ -18,7 +18,10 @@ hipError_t launch_gemm_skinny(const GemmParams&, int, hipStream_t) { return hipS
 hipError_t launch_splitk_finalize(const GemmParams&, hipStream_t) { return hipSuccess; }
 std::vector<GemmParams> g_launched;
 hipError_t launch_gemm_bigwave(const GemmParams& p, hipStream_t) { g_launched.push_back(p); return hipSuccess; }
-bool gemm_bigwave16_supports(const GemmParams& p) { return p.w_nk && p.K % 64 == 0 && p.K > 0 && p.splits <= 1 && p.rects == 0; }
+bool gemm_bigwave16_supports(const GemmParams& p) {  // the rule of gemm_bigwave16.hip
+  const bool rows_ok = p.rects > 0 ? (p.tile_rows == 256 || p.tile_rows == 192) : (p.tile_rows == 0 || p.tile_rows == 256);
+  return p.K % 64 == 0 && p.K > 0 && p.splits <= 1 && !p.narrow && p.persist == 0 && rows_ok;
+}
 hipError_t launch_gemm_bigwave16(const GemmParams& p, hipStream_t) { g_launched.push_back(p); return hipSuccess; }
 }  // namespace ttl
 

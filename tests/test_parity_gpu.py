@@ -406,13 +406,12 @@ def test_mixed_row_cut(ttl, gemm_force, capfd, b, k, n, silu, cus, layout):
 
 @pytest.mark.parametrize("layout", ["kn", "nk", "blk"])
 @pytest.mark.parametrize("silu", [False, True])
-def test_auto_last_round_over_half(ttl, gemm_force, capfd, silu, layout):
-    """At 256 CUs the shape-based choice runs 2500 x 10240 outputs (400 tiles of 256 x 256: one
-    round plus 144 tiles) and 4096 x 3584 SiLU·up outputs (448 tiles: one round plus 192) as whole
-    tiles of the 16 x 16 x 32 kernel, for every weight storage: no cut, bit-equal to the 256 x 256
-    tiles of the 32 x 32 x 16 kernel and to its 256-row / 192-row cut; sampled rows (both sides of
-    every strip class's cut row) against the oracle.  The row GEMM of 4096 x 8192 (512 tiles, two
-    whole rounds) is not cut either."""
+def test_auto_mixed_row_cut(ttl, gemm_force, capfd, silu, layout):
+    """At 256 CUs the shape-based choice cuts 2500 x 10240 outputs (400 tiles of 256 x 256: one
+    round plus 144 tiles) and 4096 x 3584 SiLU·up outputs (448 tiles: one round plus 192) into
+    256-row and 192-row tiles of the 16 x 16 x 32 kernel, for every weight storage: bit-equal to the
+    whole 256 x 256 tiles of either kernel; sampled rows (both sides of every strip class's cut row)
+    against the oracle.  The row GEMM of 4096 x 8192 (512 tiles, two whole rounds) is not cut."""
     gemm_force.set(splits=0)
     gemm_force.set(plan_cus=0)
     gemm_force.set(trace=True)
@@ -431,21 +430,21 @@ def test_auto_last_round_over_half(ttl, gemm_force, capfd, silu, layout):
     X = wl.random_bf16((b, k), 410)
     capfd.readouterr()
     outs = {}
-    for kern in ("auto", "tiled", "mixed"):
+    for kern in ("auto", "tiled", "tiled16"):
         gemm_force.set(kernel=kern)
         outs[kern] = ttl.shard_linear_col(gpu(X), Wd_, 1, 0, sp_c, epi, w_layout=lay)
         torch.cuda.synchronize()
         if kern == "auto":
-            assert "ttl gemm cut" not in capfd.readouterr().err
-    assert capfd.readouterr().err.count("ttl gemm cut") == 1  # the forced cut
+            assert capfd.readouterr().err.count("ttl gemm cut") == 1
     assert torch.equal(outs["auto"], outs["tiled"])
-    assert torch.equal(outs["auto"], outs["mixed"])
+    assert torch.equal(outs["auto"], outs["tiled16"])
     ref = oracle.col_shard(f64(X)[rows], f64(W), sp_np, 1, 0)
     if silu:
         ref = oracle.silu_mul(ref)
-    assert_close(from_gpu(outs["auto"])[rows], ref, f"auto whole tiles silu={silu} {layout}")
+    assert_close(from_gpu(outs["auto"])[rows], ref, f"auto cut silu={silu} {layout}")
     # two whole rounds: no cut
     gemm_force.set(kernel="auto")
+    capfd.readouterr()
     Xr = gpu(wl.random_bf16((4096, 256), 412))
     ttl.shard_linear_row(Xr, gpu(wl.random_bf16((256, 8192), 413, std=0.05)), 1, 0, True)
     torch.cuda.synchronize()
