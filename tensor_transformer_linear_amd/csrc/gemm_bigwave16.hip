@@ -33,8 +33,9 @@
 // and k = 8 (l / 16) .. + 7 of the k32 step; second operand lane l holds activation row l % 16 and
 // the same k; accumulator register r of lane l is output row l % 16, column 4 (l / 16) + r.
 //
-// K must be a multiple of 64; no k splits.  Whole launches of 256 x 256 tiles, or tile sets of
-// 256-row or 192-row tiles (the planner's cut of a launch whose last round is partly idle).
+// K must be a multiple of 64.  Whole launches of 256 x 256 tiles, tile sets of 256-row or 192-row
+// tiles (the planner's cut of a launch whose last round is partly idle), or 256 x 256 tiles cut
+// along k (plain columns: fp32 partial tiles for the split-K finalize kernel).
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -60,6 +61,8 @@ constexpr int kKRowsPerCopy = 64 / kBChunks;           // k rows per 1-KiB copy 
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+constexpr int kPartials = 2;  // kernel mode: plain columns, fp32 partial tile of a k split to the workspace
+
 // Slot permutation of a staged [k][n] row (32 chunks of 16 bytes): chunk c of k row r sits at slot
 // c ^ kn_swizzle(r).  A transposed weight read covers 4 consecutive k rows in each 16-lane group,
 // and the two groups of a half-wave are 8 rows apart at the same columns: 4 (r % 4) spreads the 4
@@ -68,14 +71,17 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // was a two-way bank conflict: 15x the conflict cycles of the [n][k] reads, 70B TP=8 row GEMM).
 __host__ __device__ constexpr int kn_swizzle(int r) { return (4 * (r % 4)) ^ (2 * ((r >> 3) & 1)); }
 
-// WNK: weights stored [n][k]; otherwise [k][n], in 64 x 128 blocks when BLK.  BM rows per tile:
-// 256, or 192 (96 per wave) for the last round of a launch whose 256-row tiles would leave that
-// round partly idle.
+// MODE: kPlain (bf16 outputs), kSiluMul, or kPartials (plain columns; workgroup split * tiles + tile
+// runs k-tiles [split * kt_per_split, ...) of its tile and writes the fp32 partial tile to workspace
+// slice `split`, which the split-K finalize kernel sums in split order).  WNK: weights stored
+// [n][k]; otherwise [k][n], in 64 x 128 blocks when BLK.  BM rows per tile: 256, or 192 (96 per
+// wave) for the last round of a launch whose 256-row tiles would leave that round partly idle.
 template <int MODE, bool WNK, bool BLK, int BM>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void gemm_bigwave16_kernel(const GemmParams p) {
   static_assert(!(WNK && BLK), "blocked storage is a [k][n] storage");
   static_assert(BM == 256 || BM == 192, "tile heights built: 256 and 192");
+  static_assert(MODE != kPartials || BM == 256, "k splits: 256-row tiles");
   constexpr int kBM = BM, kWM = BM / 2;
   constexpr int kMB = kWM / 16;                          // 16-row blocks per wave: 8 or 6
   constexpr int kMpsl = (kMB / 2) * kNB;                 // MFMAs per slice: 32 or 24
@@ -92,9 +98,11 @@ void gemm_bigwave16_kernel(const GemmParams p) {
   // Tile sets (p.rects > 0): block b < rect_tmc[0] * rect_tnc[0] is a tile of rectangle 0, the
   // rest of rectangle 1; rectangle i is rect_tmc[i] row-tiles from row rect_row0[i] by rect_tnc[i]
   // tile columns from tile column rect_tn0[i], walked in groups of rect_group[i] row-tiles.
+  const int tiles = p.tiles_m * p.tiles_n;
+  const int split = MODE == kPartials ? (int)blockIdx.x / tiles : 0;
   int tile_m, tile_n, row0 = 0;
   {
-    const int bid = (int)blockIdx.x;
+    const int bid = (int)blockIdx.x - split * tiles;
     if (p.rects > 0) {
       const int c0 = p.rect_tmc[0] * p.rect_tnc[0];
       const bool second = p.rects > 1 && bid >= c0;
@@ -110,7 +118,8 @@ void gemm_bigwave16_kernel(const GemmParams p) {
   }
   const int m0 = row0 + tile_m * kBM;
   const int n0 = tile_n * (MODE == kSiluMul ? kBN / 2 : kBN);
-  const int nk = p.K / kBK;  // >= 1
+  const int kt0 = split * p.kt_per_split;
+  const int nk = MODE == kPartials ? min(p.kt_per_split, p.K / kBK - kt0) : p.K / kBK;  // >= 1
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds);
 
   // ---- Copy offsets.  Copy i < kACopies (8, or 6 for 192-row tiles) of this wave moves block
@@ -151,11 +160,11 @@ void gemm_bigwave16_kernel(const GemmParams p) {
   // A copy i sits 16 (i / 2) rows past copy i % 2.
   const uint32_t a_step2 = (uint32_t)(2 * kRowsPerCopy * p.lda * 2);
   auto a_desc = [&](int t) {
-    const int k0 = t * kBK;
+    const int k0 = (kt0 + t) * kBK;
     return buffer_desc(p.A + (int64_t)m0 * p.lda + k0, ((int64_t)(p.M - m0 - 1) * p.lda + (p.K - k0)) * 2);
   };
   auto b_desc = [&](int t) {
-    const int k0 = t * kBK;
+    const int k0 = (kt0 + t) * kBK;
     return WNK ? buffer_desc(p.B + k0, ((int64_t)(p.b_rows - 1) * p.ldb + (p.K - k0)) * 2)
            : BLK ? blocked_desc(p.B, p.b_rows, k0)
                      : buffer_desc(p.B + (int64_t)k0 * p.ldb, (int64_t)(p.K - k0) * p.ldb * 2);
@@ -380,7 +389,27 @@ void gemm_bigwave16_kernel(const GemmParams p) {
   };
 #pragma unroll
   for (int pass = 0; pass < kMB / 2; ++pass) {
-    if (MODE == kPlain) {
+    if constexpr (MODE == kPartials) {
+      // fp32 partial tile: chunk c (16 bytes) of a staged row holds columns 4c .. 4c+3; lane l holds
+      // columns 16 ni + 4 (l / 16) .. + 3, chunk 4 ni + l / 16.
+      constexpr int CH = kWN / 4;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int ni = 0; ni < kNB; ++ni) {
+          const int mb = 2 * pass + h, r = 16 * h + r16, c = 4 * ni + g4;
+          *reinterpret_cast<f32x4_t*>(stg + r * CH * 8 + ((c ^ (r % CH)) * 8)) = acc[mb][ni];
+        }
+      float* wbase = p.ws + (int64_t)split * p.M * p.ws_ld + n0 + wn * kWN;
+      constexpr int kRowsPerRead = 64 / CH;
+#pragma unroll
+      for (int i = 0; i < 32 / kRowsPerRead; ++i) {
+        const int r = i * kRowsPerRead + lane / CH, c = lane % CH;
+        const i32x4_t v = *reinterpret_cast<const i32x4_t*>(stg + r * CH * 8 + ((c ^ (r % CH)) * 8));
+        const int row = wrow0 + pass * 32 + r;
+        if (row < p.M) __builtin_nontemporal_store(v, reinterpret_cast<i32x4_t*>(wbase + (int64_t)row * p.ws_ld + c * 4));
+      }
+    } else if (MODE == kPlain) {
       constexpr int CH = kWN / 8;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -417,7 +446,7 @@ void gemm_bigwave16_kernel(const GemmParams p) {
 template <int MODE, int BM>
 void launch_one16(const GemmParams& p, hipStream_t stream) {
   const int blocks = p.rects > 0 ? p.rect_tmc[0] * p.rect_tnc[0] + (p.rects > 1 ? p.rect_tmc[1] * p.rect_tnc[1] : 0)
-                                 : p.tiles_m * p.tiles_n;
+                                 : (p.splits > 1 ? p.splits : 1) * p.tiles_m * p.tiles_n;
   const dim3 grid((unsigned)blocks);
   if (p.w_nk) hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, true, false, BM>), grid, dim3(kThreads), 0, stream, p);
   else if (p.w_blk) hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, false, true, BM>), grid, dim3(kThreads), 0, stream, p);
@@ -430,17 +459,25 @@ void launch_rows16(const GemmParams& p, hipStream_t stream) {
   else launch_one16<kPlain, BM>(p, stream);
 }
 
+void launch_splits16(const GemmParams& p, hipStream_t stream) { launch_one16<kPartials, 256>(p, stream); }
+
 }  // namespace
 
 bool gemm_bigwave16_supports(const GemmParams& p) {
-  // Tile sets with 256-row or 192-row tiles, or whole launches of 256-row tiles.
+  // Tile sets with 256-row or 192-row tiles, or whole launches of 256-row tiles, or (plain columns)
+  // 256-row tiles cut along k.
   const bool rows_ok = p.rects > 0 ? (p.tile_rows == 256 || p.tile_rows == 192) : (p.tile_rows == 0 || p.tile_rows == 256);
-  return p.K % kBK == 0 && p.K > 0 && p.splits <= 1 && !p.narrow && p.persist == 0 && rows_ok;
+  const bool splits_ok = p.splits <= 1 || (p.rects == 0 && p.mode == kPlain && p.kt_per_split > 0);
+  return p.K % kBK == 0 && p.K > 0 && splits_ok && !p.narrow && p.persist == 0 && rows_ok;
 }
 
 hipError_t launch_gemm_bigwave16(const GemmParams& p, hipStream_t stream) {
   if (!gemm_bigwave16_supports(p)) return hipErrorInvalidValue;
-  if (p.tile_rows == 192) launch_rows16<192>(p, stream);
+  if (p.splits > 1) {
+    if (p.ws == nullptr || p.ws_ld < (int64_t)p.tiles_n * kBN) return hipErrorInvalidValue;
+    launch_splits16(p, stream);
+  }
+  else if (p.tile_rows == 192) launch_rows16<192>(p, stream);
   else launch_rows16<256>(p, stream);
   return hipGetLastError();
 }

@@ -427,7 +427,8 @@ hipError_t launch_tiles_splitk(GemmParams& p, int64_t splits, bool narrow, Ctx& 
   hipError_t e = workspace(c, (size_t)splits * q.M * q.ws_ld * sizeof(float), &base);
   if (e != hipSuccess) return e;
   q.ws = static_cast<float*>(base);
-  if ((e = run_bigwave(c, q)) != hipSuccess) return e;
+  // 256 x 256 tiles on the 16 x 16 x 32 kernel, 256 x 128 tiles on the 32 x 32 x 16 one.
+  if ((e = (!narrow && gemm_bigwave16_supports(q)) ? run_tiled16(c, q) : run_bigwave(c, q)) != hipSuccess) return e;
   GemmParams f = p;
   f.ws = q.ws;
   f.ws_ld = q.ws_ld;

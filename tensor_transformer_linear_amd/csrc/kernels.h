@@ -100,8 +100,9 @@ int gemm_bigwave_tile_cols(int mode, bool narrow);
 hipError_t launch_gemm_bigwave(const GemmParams& p, hipStream_t stream);
 
 // The 256 x 256 tiles of the four-wave kernel fed to 16 x 16 x 32 products (gemm_bigwave16.hip):
-// every weight storage, whole launches of 256-row tiles or tile sets of 256-row or 192-row tiles (no
-// k splits, not persistent), K a multiple of 64.  Same results as launch_gemm_bigwave, bit for bit.
+// every weight storage, whole launches of 256-row tiles, tile sets of 256-row or 192-row tiles, or
+// (plain columns) 256-row tiles cut along k into fp32 partials for launch_splitk_finalize (not
+// persistent), K a multiple of 64.  Same results as launch_gemm_bigwave, bit for bit.
 bool gemm_bigwave16_supports(const GemmParams& p);
 hipError_t launch_gemm_bigwave16(const GemmParams& p, hipStream_t stream);
 

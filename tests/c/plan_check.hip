@@ -20,7 +20,8 @@ std::vector<GemmParams> g_launched;
 hipError_t launch_gemm_bigwave(const GemmParams& p, hipStream_t) { g_launched.push_back(p); return hipSuccess; }
 bool gemm_bigwave16_supports(const GemmParams& p) {  // the rule of gemm_bigwave16.hip
   const bool rows_ok = p.rects > 0 ? (p.tile_rows == 256 || p.tile_rows == 192) : (p.tile_rows == 0 || p.tile_rows == 256);
-  return p.K % 64 == 0 && p.K > 0 && p.splits <= 1 && !p.narrow && p.persist == 0 && rows_ok;
+  const bool splits_ok = p.splits <= 1 || (p.rects == 0 && p.mode == 0 && p.kt_per_split > 0);
+  return p.K % 64 == 0 && p.K > 0 && splits_ok && !p.narrow && p.persist == 0 && rows_ok;
 }
 hipError_t launch_gemm_bigwave16(const GemmParams& p, hipStream_t) { g_launched.push_back(p); return hipSuccess; }
 }  // namespace ttl
