@@ -17,13 +17,14 @@ hipError_t launch_gemm_tiled(const GemmParams&, hipStream_t) { return hipSuccess
 hipError_t launch_gemm_skinny(const GemmParams&, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_splitk_finalize(const GemmParams&, hipStream_t) { return hipSuccess; }
 std::vector<GemmParams> g_launched;
-hipError_t launch_gemm_bigwave(const GemmParams& p, hipStream_t) { g_launched.push_back(p); return hipSuccess; }
+std::vector<int> g_kernel;  // per launch: 32 (32 x 32 x 16 kernel) or 16 (16 x 16 x 32 kernel)
+hipError_t launch_gemm_bigwave(const GemmParams& p, hipStream_t) { g_launched.push_back(p); g_kernel.push_back(32); return hipSuccess; }
 bool gemm_bigwave16_supports(const GemmParams& p) {  // the rule of gemm_bigwave16.hip
   const bool rows_ok = p.rects > 0 ? (p.tile_rows == 256 || p.tile_rows == 192) : (p.tile_rows == 0 || p.tile_rows == 256);
   const bool splits_ok = p.splits <= 1 || (p.rects == 0 && p.mode == 0 && p.kt_per_split > 0);
   return p.K % 64 == 0 && p.K > 0 && splits_ok && !p.narrow && p.persist == 0 && rows_ok;
 }
-hipError_t launch_gemm_bigwave16(const GemmParams& p, hipStream_t) { g_launched.push_back(p); return hipSuccess; }
+hipError_t launch_gemm_bigwave16(const GemmParams& p, hipStream_t) { g_launched.push_back(p); g_kernel.push_back(16); return hipSuccess; }
 }  // namespace ttl
 
 static int failures = 0;
@@ -159,6 +160,42 @@ int main() {
     ttl::g_launched.clear();
     CHECK(ttl::launch_gemm_fixed_workspace(p, fake, 1024, nullptr) == hipErrorInvalidValue, "undersized workspace");
     CHECK(ttl::g_launched.empty(), "an undersized workspace launched");
+  }
+  // The prefill GEMMs of the 70B TP=8 rank at 4096 tokens, with [k][n] and [n][k] weights, run on
+  // the 16 x 16 x 32 kernel: gate_up + SiLU·up as the 256-row / 192-row cut (two launches), down as
+  // 512 whole tiles; the 70B layer's qkv (2176 x 1280, k = 8192) as 256 x 256 tiles in 5 k splits.
+  for (int nk = 0; nk < 2; ++nk) {
+    GemmParams p = {};
+    p.M = 4096;
+    p.N = 3584;
+    p.K = 8192;
+    p.mode = 1;
+    p.w_nk = nk;
+    ttl::g_launched.clear();
+    ttl::g_kernel.clear();
+    CHECK(ttl::launch_gemm(p, nullptr) == hipSuccess, "gate_up");
+    CHECK(ttl::g_kernel == std::vector<int>({16, 16}) && ttl::g_launched[0].tile_rows == 256 &&
+          ttl::g_launched[1].tile_rows == 192, "gate_up (w_nk %d): %zu launches", nk, ttl::g_kernel.size());
+    p = {};
+    p.M = 4096;
+    p.N = 8192;
+    p.K = 3584;
+    p.w_nk = nk;
+    ttl::g_launched.clear();
+    ttl::g_kernel.clear();
+    CHECK(ttl::launch_gemm(p, nullptr) == hipSuccess, "down");
+    CHECK(ttl::g_kernel == std::vector<int>({16}) && ttl::g_launched[0].tiles_m * ttl::g_launched[0].tiles_n == 512 &&
+          ttl::g_launched[0].rects == 0, "down (w_nk %d)", nk);
+    p = {};
+    p.M = 2176;
+    p.N = 1280;
+    p.K = 8192;
+    p.w_nk = nk;
+    ttl::g_launched.clear();
+    ttl::g_kernel.clear();
+    float ws[4];
+    CHECK(ttl::launch_gemm_fixed_workspace(p, ws, (size_t)5 * 2176 * 1280 * 4, nullptr) == hipSuccess, "qkv");
+    CHECK(ttl::g_kernel == std::vector<int>({16}) && ttl::g_launched[0].splits == 5, "qkv (w_nk %d)", nk);
   }
   // Seeded shapes of every size class: each planned cut covers every row once and fits its rounds.
   std::mt19937 rng(7);

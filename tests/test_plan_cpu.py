@@ -2,8 +2,9 @@
 gemm_plan.hip for the host with stub launchers and checks the 256-row / 192-row cut (every column
 strip's rows covered exactly once, each launch within its rounds, no cut for whole or short last
 rounds, the planned cut of the 4096 x 3584 SiLU·up launch), the four-wave kernel's tile map (a
-bijection for every group height), and the L2 fetch count that picks the group heights (the
-figures the FETCH_SIZE counters confirmed on the device)."""
+bijection for every group height), the L2 fetch count that picks the group heights (the
+figures the FETCH_SIZE counters confirmed on the device), and which kernel the 70B TP=8 prefill
+GEMMs run on (the 16 x 16 x 32 kernel, for [k][n] and [n][k] weights)."""
 
 import os
 import shutil
