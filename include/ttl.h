@@ -335,7 +335,7 @@ const char* ttl_last_error(void);
  *   splits    > 0: the k-split count of the split-K kernel and of tiles cut along k; 0 = by shape.
  *   plan_cus  > 0: compute units the 256-row / 192-row cut (TTL_GEMM_MIXED) is planned for; 0 = the
  *             device's.
- *   trace     != 0: print each 256-row / 192-row cut to stderr.
+ *   trace     != 0: print each 256-row / 192-row cut and each launch with appended rows to stderr.
  * Errors: an unknown kernel, or a negative splits/plan_cus -> UNSUPPORTED.
  */
 #define TTL_GEMM_AUTO 0
@@ -349,6 +349,9 @@ const char* ttl_last_error(void);
 #define TTL_GEMM_MIXED 8        /* the 256-row / 192-row cut wherever one exists */
 #define TTL_GEMM_PERSIST 9      /* 256 x 256 tiles by a persistent grid (up to two tiles per CU) */
 #define TTL_GEMM_TILED16 10     /* 256 x 256 tiles fed to 16 x 16 x 32 products */
+#define TTL_GEMM_APPENDED 11    /* 256 x 256 tiles (16 x 16 x 32) over the whole row-tiles, the rows
+                                   below them appended to the tiles, at most 16 per row-tile (plain
+                                   columns, K % 64 == 0); otherwise the choice by shape */
 ttl_status ttl_set_gemm_override(int32_t kernel, int32_t splits, int32_t plan_cus, int32_t trace);
 
 /* Library version: major * 10000 + minor * 100 + patch. */

@@ -76,18 +76,24 @@ __host__ __device__ constexpr int kn_swizzle(int r) { return (4 * (r % 4)) ^ (2 
 // slice `split`, which the split-K finalize kernel sums in split order).  WNK: weights stored
 // [n][k]; otherwise [k][n], in 64 x 128 blocks when BLK.  BM rows per tile: 256, or 192 (96 per
 // wave) for the last round of a launch whose 256-row tiles would leave that round partly idle.
-template <int MODE, bool WNK, bool BLK, int BM>
+// XR (plain 256-row tiles): 16 appended rows per tile, from row p.xr_row0 + 16 tile_m (see below).
+template <int MODE, bool WNK, bool BLK, int BM, bool XR>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void gemm_bigwave16_kernel(const GemmParams p) {
   static_assert(!(WNK && BLK), "blocked storage is a [k][n] storage");
   static_assert(BM == 256 || BM == 192, "tile heights built: 256 and 192");
   static_assert(MODE != kPartials || BM == 256, "k splits: 256-row tiles");
+  static_assert(!XR || (MODE == kPlain && BM == 256), "appended rows: plain 256-row tiles");
   constexpr int kBM = BM, kWM = BM / 2;
   constexpr int kMB = kWM / 16;                          // 16-row blocks per wave: 8 or 6
   constexpr int kMpsl = (kMB / 2) * kNB;                 // MFMAs per slice: 32 or 24
-  constexpr int kAElems = kBM * kBK, kStageElems = kAElems + kBElems;
-  constexpr int kACopies = kAElems * 2 / 1024 / kWaves;  // 8 or 6
+  constexpr int kAMain = kBM * kBK;                      // the tile's own A rows in a stage
+  constexpr int kAElems = kAMain + (XR ? 16 * kBK : 0), kStageElems = kAElems + kBElems;
+  constexpr int kACopies = kAMain * 2 / 1024 / kWaves;   // 8 or 6
   constexpr int kCopies = kACopies + kBCopies;
+  // Products written as asm with the accumulator tied in place (see mfma_one): [k][n] weights, and
+  // every storage with appended rows.
+  constexpr bool kAsm = !WNK || XR;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages * kStageElems];
 
   const int tid = threadIdx.x;
@@ -118,6 +124,12 @@ void gemm_bigwave16_kernel(const GemmParams p) {
   }
   const int m0 = row0 + tile_m * kBM;
   const int n0 = tile_n * (MODE == kSiluMul ? kBN / 2 : kBN);
+  // Appended rows (XR): staged below the tile's 256 A rows as rows 256 .. 271; rows at or past M read
+  // zeros (a tile may have none).  The wave in row half wm computes them against its column blocks
+  // 2 wm, 2 wm + 1, 2 wm + 4, 2 wm + 5: with XR a wave holds its weight fragments in the order
+  // ni ^ nperm, so that these are its fragments 0, 1, 4 and 5 in every wave.
+  const int xm0 = XR ? p.xr_row0 + tile_m * 16 : 0;
+  const int nperm = XR ? 2 * wm : 0;
   const int kt0 = split * p.kt_per_split;
   const int nk = MODE == kPartials ? min(p.kt_per_split, p.K / kBK - kt0) : p.K / kBK;  // >= 1
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds);
@@ -163,6 +175,17 @@ void gemm_bigwave16_kernel(const GemmParams p) {
     const int k0 = (kt0 + t) * kBK;
     return buffer_desc(p.A + (int64_t)m0 * p.lda + k0, ((int64_t)(p.M - m0 - 1) * p.lda + (p.K - k0)) * 2);
   };
+  // Appended rows: waves 0 and 1 each copy 8 of the 16 (one 1-KiB copy per k-tile), laid out as A.
+  uint32_t x_off = 0;
+  if constexpr (XR) {
+    const int row = kRowsPerCopy * (wave & 1) + lane / kChunks;
+    const int chunk = (lane % kChunks) ^ ((row / kRowsPer256) % kChunks);
+    x_off = (uint32_t)(((int64_t)row * p.lda + chunk * 8) * 2);
+  }
+  auto x_desc = [&](int t) {
+    const int k0 = (kt0 + t) * kBK;
+    return buffer_desc(p.A + (int64_t)xm0 * p.lda + k0, ((int64_t)(p.M - xm0 - 1) * p.lda + (p.K - k0)) * 2);
+  };
   auto b_desc = [&](int t) {
     const int k0 = (kt0 + t) * kBK;
     return WNK ? buffer_desc(p.B + k0, ((int64_t)(p.b_rows - 1) * p.ldb + (p.K - k0)) * 2)
@@ -179,10 +202,16 @@ void gemm_bigwave16_kernel(const GemmParams p) {
       copy16_to_lds_at(bd, b_off[i - kACopies], wave_lds_b + so, (i - kACopies) * 1024);
     }
   };
+  const bool x_copier = XR && wave < 2;
+  auto copy_x = [&](int t, i32x4_t xd) {
+    const uint32_t so = (uint32_t)(((unsigned)t % kStages) * kStageElems * 2);
+    copy16_to_lds_at(xd, x_off, lds0 + so + (uint32_t)(kAMain * 2 + (wave & 1) * 1024), 0);
+  };
   auto copy_tile = [&](int t) {
     const i32x4_t ad = a_desc(t), bd = b_desc(t);
 #pragma unroll
     for (int i = 0; i < kCopies; ++i) copy_one(t, i, ad, bd);
+    if (x_copier) copy_x(t, x_desc(t));
   };
 
   // ---- Fragment offsets (elements within a stage).
@@ -191,12 +220,15 @@ void gemm_bigwave16_kernel(const GemmParams p) {
   const int r16 = lane & 15;
   const int g4 = lane >> 4;
   const int rsw = (r16 / kRowsPer256) % kChunks;  // the row's swizzle term (blocks start at multiples of 16 rows)
-  int ra_off[2], rb_off[2];
+  int ra_off[2], rb_off[2][2], rx_off[2];
 #pragma unroll
   for (int step = 0; step < 2; ++step) {
     const int slot = (4 * step + g4) ^ rsw;
     ra_off[step] = (wm * kWM + r16) * kBK + slot * 8;
-    rb_off[step] = kAElems + (wn * kWN + r16) * kBK + slot * 8;
+    rx_off[step] = kAMain + r16 * kBK + slot * 8;
+    // fragment ni reads block ni ^ nperm: ni + nperm where bit 1 of ni is clear, ni - nperm where set
+    rb_off[step][0] = kAElems + (wn * kWN + r16) * kBK + slot * 8 + nperm * 16 * kBK;
+    rb_off[step][1] = kAElems + (wn * kWN + r16) * kBK + slot * 8 - nperm * 16 * kBK;
   }
   // [64 k][256 n] staging, read with ds_read_b64_tr_b16 (each 16-lane group receives the transpose
   // of a 4 (k) x 16 (n) block): group g = lane/16 reads k row 32 step + 8 g + 4 h + (lane%16)/4 of
@@ -208,13 +240,13 @@ void gemm_bigwave16_kernel(const GemmParams p) {
     const int x = kn_swizzle(krow);
 #pragma unroll
     for (int ni = 0; ni < kNB; ++ni)
-      rt_off[ni] = kAElems + krow * kBN + (((kWN / 8) * wn + 2 * ni + ((lane & 3) >> 1)) ^ x) * 8 + 4 * (lane & 1);
+      rt_off[ni] = kAElems + krow * kBN + (((kWN / 8) * wn + 2 * (ni ^ nperm) + ((lane & 3) >> 1)) ^ x) * 8 + 4 * (lane & 1);
   }
-  bf16x8_t af[4][kMB / 2], bv[2][kNB];
+  bf16x8_t af[4][kMB / 2], bv[2][kNB], afx[2];
   i16x4_t bl[2][kNB], bh[2][kNB];
   // Reads of slice s: j < 4 are its row-block fragments; an even slice also reads its step's eight
-  // weight fragments.
-  constexpr int kBReads = kNB;
+  // weight fragments and (XR) the appended rows' fragment.
+  constexpr int kBReads = kNB + (XR ? 1 : 0);
   auto reads_of = [](int s) { return kMB / 2 + (s % 2 == 0 ? kBReads : 0); };
   auto read_one = [&](int t, int s, int j) {
     const uint16_t* st = lds + ((unsigned)t % kStages) * kStageElems;
@@ -222,9 +254,11 @@ void gemm_bigwave16_kernel(const GemmParams p) {
     if (j < kMB / 2) {
       const int mb = (s % 2) * (kMB / 2) + j;
       af[s][j] = *reinterpret_cast<const bf16x8_t*>(st + ra_off[step] + mb * 16 * kBK);
+    } else if (XR && j == kMB / 2 + kNB) {
+      afx[step] = *reinterpret_cast<const bf16x8_t*>(st + rx_off[step]);
     } else if constexpr (WNK) {
       const int ni = j - kMB / 2;
-      bv[step][ni] = *reinterpret_cast<const bf16x8_t*>(st + rb_off[step] + ni * 16 * kBK);
+      bv[step][ni] = *reinterpret_cast<const bf16x8_t*>(st + rb_off[step][(ni >> 1) & 1] + ni * 16 * kBK);
     } else {
       // the two transposed halves (k 8 g .. + 3 and + 4 .. + 7), joined at once into the fragment
       const int ni = j - kMB / 2;
@@ -241,7 +275,14 @@ void gemm_bigwave16_kernel(const GemmParams p) {
     for (int ni = 0; ni < kNB; ++ni)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[mb][ni][r] = 0.0f;
-  if constexpr (!WNK) {
+  // Appended rows' accumulators (XR), in vector registers (the accumulation registers are full):
+  // accx[e] is that row block against fragment 4 (e / 2) + e % 2.
+  f32x4_t accx[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) accx[e][r] = 0.0f;
+  if constexpr (kAsm) {
     // The zeros are placed in the accumulation registers here (the empty statements take them as
     // operands), and a vector write of a register read as a product's accumulator must lead it by
     // two wait states: the nops give several.
@@ -249,6 +290,10 @@ void gemm_bigwave16_kernel(const GemmParams p) {
     for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
       for (int ni = 0; ni < kNB; ++ni) asm volatile("" : "+a"(acc[mb][ni]));
+    if constexpr (XR) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(accx[e]));
+    }
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_nop 7");
     __builtin_amdgcn_sched_barrier(0);
@@ -261,16 +306,34 @@ void gemm_bigwave16_kernel(const GemmParams p) {
     bf16x8_t b;
     if constexpr (WNK) b = bv[step][ni];
     else b = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(bl[step][ni], bh[step][ni], 0, 1, 2, 3, 4, 5, 6, 7));
-    if constexpr (WNK) {
+    if constexpr (!kAsm) {
       acc[mb][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, af[s][ml], acc[mb][ni], 0, 0, 0);
     } else {
       // Written out, with the accumulator as one read-write operand: through the builtin, the
       // register allocator gave some products' accumulator input and output different registers
       // and moved those accumulators through other registers every k-tile (the two-read weight
-      // fragments leave it less room).  The compiler does not see this as a matrix instruction,
+      // fragments, or the appended rows' registers, leave it less room).  The compiler does not see this as a matrix instruction,
       // so the waits it would insert around one are made explicit (before the first product and
       // after the last); the products' operands come from LDS reads, whose waits it does insert.
       asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[mb][ni]) : "v"(b), "v"(af[s][ml]));
+    }
+  };
+  // Appended rows (XR): product e2 (0, 1) of slice s, the k32 step s / 2 of the appended row block
+  // against fragment 4 (s % 2) + e2 (two per slice, after the slice's own).
+  auto mfma_x = [&](int s, int e2) {
+    const int e = 2 * (s % 2) + e2, ni = 4 * (s % 2) + e2, step = s / 2;
+    bf16x8_t b;
+    if constexpr (WNK) b = bv[step][ni];
+    else b = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(bl[step][ni], bh[step][ni], 0, 1, 2, 3, 4, 5, 6, 7));
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(accx[e]) : "v"(b), "v"(afx[step]));
+  };
+  auto slice_x = [&](int s) {
+    if constexpr (XR) {
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        mfma_x(s, e2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
@@ -278,7 +341,8 @@ void gemm_bigwave16_kernel(const GemmParams p) {
   copy_tile(0);
   if (nk >= 2) {
     copy_tile(1);
-    wait_vmcnt<kCopies>();
+    if (x_copier) wait_vmcnt<kCopies + 1>();
+    else wait_vmcnt<kCopies>();
   } else {
     wait_vmcnt<0>();
   }
@@ -302,6 +366,7 @@ void gemm_bigwave16_kernel(const GemmParams p) {
       for (int r = j * kR0 / kMpsl; r < (j + 1) * kR0 / kMpsl; ++r) read_one(t, 2, r);
       __builtin_amdgcn_sched_barrier(0);
     }
+    slice_x(0);
 #pragma unroll
     for (int j = 0; j < kMpsl; ++j) {
       mfma_one(1, j);
@@ -309,15 +374,17 @@ void gemm_bigwave16_kernel(const GemmParams p) {
       for (int r = j * kR1 / kMpsl; r < (j + 1) * kR1 / kMpsl; ++r) read_one(t, 3, r);
       __builtin_amdgcn_sched_barrier(0);
     }
+    slice_x(1);
     if (NEXT) {
       wait_vmcnt<0>();  // this wave's copies of tile t+1 landed
       lds_barrier();    // ... everyone's; and every wave's reads of tile t returned
       __builtin_amdgcn_sched_barrier(0);
     }
-    i32x4_t ad = {0, 0, 0, 0}, bd = {0, 0, 0, 0};
+    i32x4_t ad = {0, 0, 0, 0}, bd = {0, 0, 0, 0}, xd = {0, 0, 0, 0};
     if (COPY) {
       ad = a_desc(t + kStages);
       bd = b_desc(t + kStages);
+      if (XR) xd = x_desc(t + kStages);
     }
     // slice 2: reads of slice 0 of tile t+1; copy c follows MFMA slot (c + 1) 2 kMpsl / kCopies - 1
     // of slices 2-3 (slots kMpsl.. are slice 3's): after every fourth MFMA for 256-row tiles.
@@ -329,6 +396,7 @@ void gemm_bigwave16_kernel(const GemmParams p) {
 #pragma unroll
         for (int c = 0; c < kCopies; ++c)
           if ((c + 1) * 2 * kMpsl / kCopies - 1 == j) copy_one(t + kStages, c, ad, bd);
+        if (j == kMpsl - 1 && x_copier) copy_x(t + kStages, xd);
       }
       if (NEXT) {
 #pragma unroll
@@ -336,6 +404,7 @@ void gemm_bigwave16_kernel(const GemmParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    slice_x(2);
     // slice 3: reads of slice 1 of tile t+1, the other copies
     constexpr int kR3 = kMB / 2;
 #pragma unroll
@@ -352,12 +421,13 @@ void gemm_bigwave16_kernel(const GemmParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    slice_x(3);
   };
   int t = 0;
   for (; t + kStages < nk; ++t) k_tile(t, std::true_type{}, std::true_type{});
   if (t + 1 < nk) k_tile(t++, std::true_type{}, std::false_type{});
   k_tile(t, std::false_type{}, std::false_type{});
-  if constexpr (!WNK) {
+  if constexpr (kAsm) {
     // A product's results may be read by other vector instructions only some wait states after
     // it (about its pass count plus two; 8 passes here): 32 before the epilogue reads.
     __builtin_amdgcn_sched_barrier(0);
@@ -415,7 +485,7 @@ void gemm_bigwave16_kernel(const GemmParams p) {
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int ni = 0; ni < kNB; ++ni) {
-          const int mb = 2 * pass + h, r = 16 * h + r16, c = 2 * ni + g4 / 2;
+          const int mb = 2 * pass + h, r = 16 * h + r16, c = 2 * (ni ^ nperm) + g4 / 2;
           u32x2_t v;
           v.x = pack_bf16x2(acc[mb][ni][0], acc[mb][ni][1]);
           v.y = pack_bf16x2(acc[mb][ni][2], acc[mb][ni][3]);
@@ -441,16 +511,33 @@ void gemm_bigwave16_kernel(const GemmParams p) {
       drain(std::integral_constant<int, CH>{}, pass, n0 + wn * (kWN / 2));
     }
   }
+  if constexpr (XR) {
+    // Appended rows, straight from the registers: lane l holds row xm0 + l % 16 and, for accx[e],
+    // the four columns from 16 ((4 (e / 2) + e % 2) ^ nperm) + 4 (l / 16) of the wave's 128.
+    const int row = xm0 + r16;
+    if (row < p.M) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int col = n0 + wn * kWN + 16 * ((4 * (e / 2) + e % 2) ^ nperm) + 4 * g4;
+        if (col < p.N) {
+          u32x2_t v;
+          v.x = pack_bf16x2(accx[e][0], accx[e][1]);
+          v.y = pack_bf16x2(accx[e][2], accx[e][3]);
+          *reinterpret_cast<u32x2_t*>(p.C + (int64_t)row * p.ldc + col) = v;
+        }
+      }
+    }
+  }
 }
 
-template <int MODE, int BM>
+template <int MODE, int BM, bool XR = false>
 void launch_one16(const GemmParams& p, hipStream_t stream) {
   const int blocks = p.rects > 0 ? p.rect_tmc[0] * p.rect_tnc[0] + (p.rects > 1 ? p.rect_tmc[1] * p.rect_tnc[1] : 0)
                                  : (p.splits > 1 ? p.splits : 1) * p.tiles_m * p.tiles_n;
   const dim3 grid((unsigned)blocks);
-  if (p.w_nk) hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, true, false, BM>), grid, dim3(kThreads), 0, stream, p);
-  else if (p.w_blk) hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, false, true, BM>), grid, dim3(kThreads), 0, stream, p);
-  else hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, false, false, BM>), grid, dim3(kThreads), 0, stream, p);
+  if (p.w_nk) hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, true, false, BM, XR>), grid, dim3(kThreads), 0, stream, p);
+  else if (p.w_blk) hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, false, true, BM, XR>), grid, dim3(kThreads), 0, stream, p);
+  else hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, false, false, BM, XR>), grid, dim3(kThreads), 0, stream, p);
 }
 
 template <int BM>
@@ -465,10 +552,11 @@ void launch_splits16(const GemmParams& p, hipStream_t stream) { launch_one16<kPa
 
 bool gemm_bigwave16_supports(const GemmParams& p) {
   // Tile sets with 256-row or 192-row tiles, or whole launches of 256-row tiles, or (plain columns)
-  // 256-row tiles cut along k.
+  // 256-row tiles cut along k, or (plain columns) whole launches of 256-row tiles with appended rows.
   const bool rows_ok = p.rects > 0 ? (p.tile_rows == 256 || p.tile_rows == 192) : (p.tile_rows == 0 || p.tile_rows == 256);
   const bool splits_ok = p.splits <= 1 || (p.rects == 0 && p.mode == kPlain && p.kt_per_split > 0);
-  return p.K % kBK == 0 && p.K > 0 && splits_ok && !p.narrow && p.persist == 0 && rows_ok;
+  const bool xr_ok = p.xr_row0 == 0 || (p.xr_row0 > 0 && p.mode == kPlain && p.rects == 0 && p.splits <= 1);
+  return p.K % kBK == 0 && p.K > 0 && splits_ok && xr_ok && !p.narrow && p.persist == 0 && rows_ok;
 }
 
 hipError_t launch_gemm_bigwave16(const GemmParams& p, hipStream_t stream) {
@@ -477,6 +565,7 @@ hipError_t launch_gemm_bigwave16(const GemmParams& p, hipStream_t stream) {
     if (p.ws == nullptr || p.ws_ld < (int64_t)p.tiles_n * kBN) return hipErrorInvalidValue;
     launch_splits16(p, stream);
   }
+  else if (p.xr_row0 > 0) launch_one16<kPlain, 256, true>(p, stream);
   else if (p.tile_rows == 192) launch_rows16<192>(p, stream);
   else launch_rows16<256>(p, stream);
   return hipGetLastError();

@@ -138,7 +138,8 @@ int64_t device_cus() {
 // eight-wave kernel, 4 256 x 256 tiles cut along k, 5 256 x 128 tiles, 6 256 x 128 tiles cut along
 // k, 7 192 x 256 tiles, 8 the 256-row / 192-row cut planned for the override's CU count, 9 256 x 256
 // tiles by a persistent grid (at most two tiles per workgroup), 10 256 x 256 tiles by the 16 x 16 x 32
-// kernel.
+// kernel, 11 the same over the whole row-tiles with the rows below them appended (where those are at
+// most 16 per row-tile; otherwise the choice by shape).
 int forced_kernel() { return g_force_kernel.load(std::memory_order_relaxed); }
 int64_t forced_splits() { return g_force_splits.load(std::memory_order_relaxed); }
 
@@ -183,6 +184,28 @@ hipError_t launch_tiles16(GemmParams& p, Ctx& c) {
   p.persist = 0;
   if (gemm_bigwave16_supports(p)) return run_tiled16(c, p);
   return launch_tiles(p, 0, c);
+}
+
+// 256 x 256 tiles of the 16 x 16 x 32 kernel over rows [0, 256 head) of p, each row-tile with 16
+// appended rows from row 256 head on (the rows below the whole tiles, at most 16 per row-tile):
+// one launch instead of whole tiles plus a launch for the rest.  False if the kernel does not take
+// p that way (then nothing is launched).
+bool launch_tiles16_xr(GemmParams& p, int64_t head, int64_t tn, Ctx& c, hipError_t& e) {
+  GemmParams q = p;
+  q.tiles_m = (int32_t)head;
+  q.tiles_n = (int32_t)tn;
+  q.splits = 1;
+  q.narrow = 0;
+  q.rects = 0;
+  q.persist = 0;
+  q.tile_rows = 256;
+  q.xr_row0 = (int32_t)(head * 256);
+  if (q.mode != 0 || p.M - q.xr_row0 > 16 * head || !gemm_bigwave16_supports(q)) return false;
+  if (!c.dry && g_trace.load(std::memory_order_relaxed))
+    std::fprintf(stderr, "ttl gemm appended rows: M=%d N=%d K=%d, %lld row-tiles of 256 + 16 rows from row %d\n",
+                 p.M, p.N, p.K, (long long)head, q.xr_row0);
+  e = run_tiled16(c, q);
+  return true;
 }
 
 // 256 x 128 tiles of the four-wave kernel over all of p (K a multiple of 64).
@@ -480,6 +503,10 @@ hipError_t plan_and_launch(GemmParams& p, Ctx& c) {
   if (force == 1 || force == 3) return launch_tiles(p, force, c);
   if (force == 9) return launch_persist(p, c);
   if (force == 10) return launch_tiles16(p, c);
+  if (force == 11 && p.M > 256 && p.M % 256 != 0) {
+    hipError_t xe = hipSuccess;
+    if (launch_tiles16_xr(p, p.M / 256, cdiv(p.N, gemm_tile_cols(p.mode)), c, xe)) return xe;
+  }
   if (force == 7 && gemm_bigwave_supports(p)) return launch_short(p, c);
   if (force == 8 && gemm_bigwave_supports(p)) {
     MixedRows m;
@@ -550,9 +577,15 @@ hipError_t plan_and_launch(GemmParams& p, Ctx& c) {
   // Whole rounds plus a short last round (at most half the CUs): that round would take a whole
   // tile's time with most of the chip idle.  The row-tiles that fill the whole rounds go to the
   // tiled kernel, the remaining rows (a few row-tiles) to the split-K kernel, which spreads them
-  // over all CUs.
+  // over all CUs; or, plain columns with at most 16 remaining rows per whole row-tile, the tiles
+  // take those rows as appended rows in the same launch (70B TP=8 layer at 2048 + 128 tokens: each
+  // tile's products grow by 1/16 in place of a split-K launch over the 128 rows).
   if (rounds >= 1 && rem > 0 && 2 * rem <= n_cu) {
     const int64_t head_row_tiles = rounds * n_cu / tiled_n;
+    hipError_t xe = hipSuccess;
+    if (use16 && head_row_tiles >= 1 && head_row_tiles < tiled_m &&
+        launch_tiles16_xr(p, head_row_tiles, tiled_n, c, xe))
+      return xe;
     if (head_row_tiles >= 1 && head_row_tiles < tiled_m) {
       GemmParams head = p;
       head.M = (int32_t)(head_row_tiles * gemm_tile_rows());

@@ -48,6 +48,11 @@ struct GemmParams {
   // workgroups than tiles; workgroup b then computes tiles b, b + grid, b + 2 grid, ... in turn,
   // fetching the next tile's first k-tiles while it finishes the current one.
   int32_t persist;
+  // 16 x 16 x 32 kernel, plain columns, whole launches of 256 x 256 tiles, no splits: xr_row0 > 0
+  // appends 16 rows to every tile, row-tile i taking rows xr_row0 + 16 i .. + 15 (those below M) as
+  // its rows 256 .. 271, so that the rows past the launch's whole 256-row tiles are computed in the
+  // same round instead of by a launch of their own.  0: none.
+  int32_t xr_row0;
 };
 
 // SiLU·up as a plain GEMM over the gate columns followed by the up columns (2N outputs, two column
@@ -102,7 +107,8 @@ hipError_t launch_gemm_bigwave(const GemmParams& p, hipStream_t stream);
 // The 256 x 256 tiles of the four-wave kernel fed to 16 x 16 x 32 products (gemm_bigwave16.hip):
 // every weight storage, whole launches of 256-row tiles, tile sets of 256-row or 192-row tiles, or
 // (plain columns) 256-row tiles cut along k into fp32 partials for launch_splitk_finalize (not
-// persistent), K a multiple of 64.  Same results as launch_gemm_bigwave, bit for bit.
+// persistent), or (plain columns) whole launches of 256-row tiles with 16 appended rows (xr_row0),
+// K a multiple of 64.  Same results as launch_gemm_bigwave, bit for bit.
 bool gemm_bigwave16_supports(const GemmParams& p);
 hipError_t launch_gemm_bigwave16(const GemmParams& p, hipStream_t stream);
 

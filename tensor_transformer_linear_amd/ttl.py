@@ -39,7 +39,8 @@ EXPORTED = ("shard_linear_col", "shard_linear_col_stored", "shard_linear_col_noa
             "ttl_pack_weight_blocked", "ttl_last_error", "ttl_version", "ttl_set_gemm_override")
 # GEMM kernel families ttl_set_gemm_override can force (tests and measurements only)
 GEMM_KERNELS = {"auto": 0, "tiled": 1, "splitk": 2, "eightwave": 3, "tilesplit": 4, "narrow": 5,
-                "narrowsplit": 6, "short": 7, "mixed": 8, "persist": 9, "tiled16": 10}
+                "narrowsplit": 6, "short": 7, "mixed": 8, "persist": 9, "tiled16": 10,
+                "appended": 11}
 
 
 class ColSplit(ctypes.Structure):

@@ -22,7 +22,8 @@ hipError_t launch_gemm_bigwave(const GemmParams& p, hipStream_t) { g_launched.pu
 bool gemm_bigwave16_supports(const GemmParams& p) {  // the rule of gemm_bigwave16.hip
   const bool rows_ok = p.rects > 0 ? (p.tile_rows == 256 || p.tile_rows == 192) : (p.tile_rows == 0 || p.tile_rows == 256);
   const bool splits_ok = p.splits <= 1 || (p.rects == 0 && p.mode == 0 && p.kt_per_split > 0);
-  return p.K % 64 == 0 && p.K > 0 && splits_ok && !p.narrow && p.persist == 0 && rows_ok;
+  const bool xr_ok = p.xr_row0 == 0 || (p.xr_row0 > 0 && p.mode == 0 && p.rects == 0 && p.splits <= 1);
+  return p.K % 64 == 0 && p.K > 0 && splits_ok && xr_ok && !p.narrow && p.persist == 0 && rows_ok;
 }
 hipError_t launch_gemm_bigwave16(const GemmParams& p, hipStream_t) { g_launched.push_back(p); g_kernel.push_back(16); return hipSuccess; }
 }  // namespace ttl
@@ -196,6 +197,54 @@ int main() {
     float ws[4];
     CHECK(ttl::launch_gemm_fixed_workspace(p, ws, (size_t)5 * 2176 * 1280 * 4, nullptr) == hipSuccess, "qkv");
     CHECK(ttl::g_kernel == std::vector<int>({16}) && ttl::g_launched[0].splits == 5, "qkv (w_nk %d)", nk);
+  }
+  // The 70B TP=8 layer at 2048 + 128 tokens: o_proj (k = 1024) and down (k = 3584), 2176 x 8192
+  // outputs, run as one launch of the 16 x 16 x 32 kernel: 8 x 32 tiles of 256 x 256, each with 16
+  // of the last 128 rows appended; no split-K partials.
+  for (int nk = 0; nk < 2; ++nk)
+    for (int K : {1024, 3584}) {
+      GemmParams p = {};
+      p.M = 2176;
+      p.N = 8192;
+      p.K = K;
+      p.w_nk = nk;
+      ttl::g_launched.clear();
+      ttl::g_kernel.clear();
+      CHECK(ttl::gemm_workspace_bytes(p) == 0, "appended rows: workspace");
+      CHECK(ttl::launch_gemm(p, nullptr) == hipSuccess, "2176 x 8192");
+      CHECK(ttl::g_kernel == std::vector<int>({16}) && ttl::g_launched[0].xr_row0 == 2048 &&
+            ttl::g_launched[0].tiles_m == 8 && ttl::g_launched[0].tiles_n == 32 && ttl::g_launched[0].splits == 1,
+            "2176 x 8192 k=%d (w_nk %d): %zu launches", K, nk, ttl::g_kernel.size());
+    }
+  // Seeded plain shapes: wherever the planner appends rows, it is the call's only launch, the whole
+  // row-tiles end where the appended rows begin, and those (16 per row-tile) reach row M.
+  {
+    std::mt19937 rng(11);
+    int appended = 0;
+    for (int i = 0; i < 4000; ++i) {
+      GemmParams p = {};
+      p.M = 1 + (int)(rng() % 9000);
+      p.N = 8 * (1 + (int)(rng() % 2048));
+      p.K = 64 * (1 + (int)(rng() % 40));
+      ttl::g_launched.clear();
+      ttl::g_kernel.clear();
+      // stub launchers touch no memory: a stand-in workspace address of the planned size
+      const size_t need = ttl::gemm_workspace_bytes(p);
+      CHECK(ttl::launch_gemm_fixed_workspace(p, reinterpret_cast<void*>(uintptr_t{4096}), need, nullptr) == hipSuccess,
+            "seeded plain shape M=%d N=%d K=%d", p.M, p.N, p.K);
+      for (size_t l = 0; l < ttl::g_launched.size(); ++l) {
+        const GemmParams& q = ttl::g_launched[l];
+        if (q.xr_row0 == 0) continue;
+        ++appended;
+        CHECK(ttl::g_launched.size() == 1 && ttl::g_kernel[l] == 16, "M=%d N=%d: appended rows among %zu launches",
+              p.M, p.N, ttl::g_launched.size());
+        CHECK(q.xr_row0 == 256 * q.tiles_m && q.xr_row0 < p.M && p.M - q.xr_row0 <= 16 * q.tiles_m && q.M == p.M &&
+              q.tiles_n * 256 >= p.N && q.tiles_m * q.tiles_n <= 256 * ((ttl::cdiv(p.M, 256) * q.tiles_n) / 256),
+              "M=%d N=%d: xr_row0 %d, %d x %d tiles", p.M, p.N, q.xr_row0, q.tiles_m, q.tiles_n);
+      }
+    }
+    CHECK(appended > 20, "only %d seeded shapes appended rows", appended);
+    std::printf("%d seeded launches with appended rows checked\n", appended);
   }
   // Seeded shapes of every size class: each planned cut covers every row once and fits its rounds.
   std::mt19937 rng(7);

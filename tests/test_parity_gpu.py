@@ -404,6 +404,69 @@ def test_mixed_row_cut(ttl, gemm_force, capfd, b, k, n, silu, cus, layout):
     assert_close(from_gpu(outs["mixed"]), ref, f"mixed cut b={b} k={k} n={n} silu={silu} {layout}")
 
 
+# (b, k, n, t, x_is_parallel): row GEMMs with rows past the whole 256-row tiles, at most 16 per
+# row-tile, appended to the tiles
+APPENDED_ROW_CASES = [
+    (528, 128, 512, 1, True),     # 2 row-tiles, 16 appended rows (row-tile 0's)
+    (808, 640, 1152, 2, True),    # 3 row-tiles, 40 rows (16, 16, 8); ragged columns; 5 k-tiles
+    (1044, 64, 768, 1, True),     # one k-tile; 20 rows (16, 4, none, none)
+    (513, 384, 256, 2, False),    # one appended row; X not parallel (the rank's k slice of it)
+]
+
+
+@pytest.mark.parametrize("layout", ["kn", "nk", "blk"])
+@pytest.mark.parametrize("b,k,n,t,x_is_parallel", APPENDED_ROW_CASES)
+def test_appended_rows(ttl, gemm_force, capfd, b, k, n, t, x_is_parallel, layout):
+    """The rows below the whole 256-row tiles appended to the tiles of the 16 x 16 x 32 kernel (16
+    per row-tile, the last ones partly or wholly past M; one launch): each rank bit-equal to whole
+    256 x 256 tiles of the same kernel (the same products in the same k order) and every element
+    against the oracle, for every weight storage."""
+    gemm_force.set(trace=True)
+    w = k // t
+    X = wl.random_bf16((b, k), 50 + b)
+    W = wl.random_bf16((k, n), 51 + b, std=0.05)
+    Xd = gpu(X)
+    Wd, lay = _stored3(ttl, W, layout)
+    Xo, Wo = f64(X), f64(W)
+    capfd.readouterr()
+    for r in range(t):
+        xin = Xd[:, r * w:(r + 1) * w].contiguous() if x_is_parallel else Xd
+        gemm_force.set(kernel="appended")
+        P = ttl.shard_linear_row(xin, Wd, t, r, x_is_parallel, w_layout=lay)
+        torch.cuda.synchronize()
+        err = capfd.readouterr().err
+        assert err.count("ttl gemm appended rows") == 1, err
+        gemm_force.set(kernel="tiled16")
+        Q = ttl.shard_linear_row(xin, Wd, t, r, x_is_parallel, w_layout=lay)
+        torch.cuda.synchronize()
+        assert torch.equal(P, Q), f"appended rows differ from whole tiles (rank {r})"
+        ref = oracle.row_shard(Xo, Wo, t, r, x_is_parallel=False)
+        assert_close(from_gpu(P), ref, f"appended rows b={b} k={k} n={n} t={t} r={r} {layout}")
+
+
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+def test_appended_rows_qkv(ttl, gemm_force, capfd, layout):
+    """Appended rows on a column GEMM through the three head-sliced segments (q, k, v) of a qkv
+    weight: bit-equal to whole tiles, every element against the oracle."""
+    gemm_force.set(trace=True)
+    b, k, nq, nkv, hd, t = 530, 256, 32, 8, 64, 2
+    X = wl.random_bf16((b, k), 60)
+    sp_np, sp_c = oracle.qkv_split(nq, nkv, hd, t), ttl.qkv_split(nq, nkv, hd, t)
+    W = wl.random_bf16((k, sum(sp_np[0])), 61, std=0.05)
+    Wd, lay = _stored(ttl, W, layout)
+    capfd.readouterr()
+    for r in range(t):
+        gemm_force.set(kernel="appended")
+        Y = ttl.shard_linear_col(gpu(X), Wd, t, r, sp_c, 0, w_layout=lay)
+        torch.cuda.synchronize()
+        assert capfd.readouterr().err.count("ttl gemm appended rows") == 1
+        gemm_force.set(kernel="tiled16")
+        Z = ttl.shard_linear_col(gpu(X), Wd, t, r, sp_c, 0, w_layout=lay)
+        torch.cuda.synchronize()
+        assert torch.equal(Y, Z), f"appended rows differ from whole tiles (rank {r})"
+        assert_close(from_gpu(Y), oracle.col_shard(f64(X), f64(W), sp_np, t, r), f"appended qkv r={r} {layout}")
+
+
 @pytest.mark.parametrize("layout", ["kn", "nk", "blk"])
 @pytest.mark.parametrize("silu", [False, True])
 def test_auto_mixed_row_cut(ttl, gemm_force, capfd, silu, layout):
