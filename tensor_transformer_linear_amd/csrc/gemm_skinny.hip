@@ -343,7 +343,9 @@ __global__ __launch_bounds__(256) void splitk_finalize_kernel(const GemmParams p
 
 template <int MODE, bool WNK, int MB>
 void launch_one(const GemmParams& p, hipStream_t stream) {
-  constexpr int kStages = 3;  // MB 1, 2: 60 / 72 KiB, two workgroups per CU; MB 4: 96 KiB
+  // LDS ring: MB 1, four stages (80 KiB: two workgroups per CU; three stages in flight, 8B TP=8 row
+  // GEMM at 256 tokens 16.9 -> 14.9 us); MB 2, three (72 KiB, two per CU); MB 4, three (96 KiB).
+  constexpr int kStages = MB == 1 ? 4 : 3;
   const unsigned grid = (unsigned)(p.splits * p.tiles_m * p.tiles_n);
   if (MODE == kSiluMul && p.splits > 1) {
     // Partial sums only: the gate and up columns run as two plain column segments of 2N outputs
