@@ -34,8 +34,11 @@
 // the same k; accumulator register r of lane l is output row l % 16, column 4 (l / 16) + r.
 //
 // K must be a multiple of 64.  Whole launches of 256 x 256 tiles, tile sets of 256-row or 192-row
-// tiles (the planner's cut of a launch whose last round is partly idle), or 256 x 256 tiles cut
-// along k (plain columns: fp32 partial tiles for the split-K finalize kernel).
+// tiles (the planner's cut of a launch whose last round is partly idle), 256 x 256 tiles with 16
+// appended rows, or 256 x 256 tiles cut along k (plain columns: fp32 partial tiles for the split-K
+// finalize kernel).  Narrow tiles (256 x 128, a wave owning 128 x 64 outputs as 8 x 4 blocks, 16
+// products per slice) serve launches whose 256 x 256 tiles would fill too few CUs, whole or cut
+// along k.
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -51,20 +54,14 @@ constexpr int kBK = 64;
 constexpr int kChunks = kBK / 8;         // 16-B chunks per staged [rows][k] row
 constexpr int kRowsPer256 = 256 / (2 * kBK);
 constexpr int kRowsPerCopy = 1024 / (2 * kBK);
-constexpr int kWN = 128, kBN = 256;
-constexpr int kNB = kWN / 16;                   // 16-column blocks per wave: 8
-constexpr int kBElems = kBK * kBN;
-constexpr int kBCopies = kBElems * 2 / 1024 / kWaves;  // 8
 constexpr int kStages = 2;
-constexpr int kBChunks = kBN / 8;                      // 16-B chunks per staged [k][n] row: 32
-constexpr int kKRowsPerCopy = 64 / kBChunks;           // k rows per 1-KiB copy of a [k][n] stage: 2
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kPartials = 2;  // kernel mode: plain columns, fp32 partial tile of a k split to the workspace
 
-// Slot permutation of a staged [k][n] row (32 chunks of 16 bytes): chunk c of k row r sits at slot
-// c ^ kn_swizzle(r).  A transposed weight read covers 4 consecutive k rows in each 16-lane group,
+// Slot permutation of a staged [k][n] row (32 chunks of 16 bytes, or 16 for narrow tiles; either
+// row is a whole number of bank cycles): chunk c of k row r sits at slot c ^ kn_swizzle(r).  A transposed weight read covers 4 consecutive k rows in each 16-lane group,
 // and the two groups of a half-wave are 8 rows apart at the same columns: 4 (r % 4) spreads the 4
 // rows of a group over the banks, 2 ((r / 8) % 2) puts the other group on the other half of them,
 // so that the 32 lanes of a half-wave read 256 distinct bytes (without the second term every read
@@ -77,16 +74,24 @@ __host__ __device__ constexpr int kn_swizzle(int r) { return (4 * (r % 4)) ^ (2 
 // [n][k]; otherwise [k][n], in 64 x 128 blocks when BLK.  BM rows per tile: 256, or 192 (96 per
 // wave) for the last round of a launch whose 256-row tiles would leave that round partly idle.
 // XR (plain 256-row tiles): 16 appended rows per tile, from row p.xr_row0 + 16 tile_m (see below).
-template <int MODE, bool WNK, bool BLK, int BM, bool XR>
+// WN weight columns per wave: 128 (256-column tiles), or 64 (narrow: 256 x 128 tiles, 256-row).
+template <int MODE, bool WNK, bool BLK, int BM, bool XR, int WN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void gemm_bigwave16_kernel(const GemmParams p) {
   static_assert(!(WNK && BLK), "blocked storage is a [k][n] storage");
   static_assert(BM == 256 || BM == 192, "tile heights built: 256 and 192");
   static_assert(MODE != kPartials || BM == 256, "k splits: 256-row tiles");
-  static_assert(!XR || (MODE == kPlain && BM == 256), "appended rows: plain 256-row tiles");
+  static_assert(!XR || (MODE == kPlain && BM == 256 && WN == 128), "appended rows: plain 256 x 256 tiles");
+  static_assert(WN == 128 || (WN == 64 && BM == 256), "narrow tiles: 256 rows");
+  constexpr int kWN = WN, kBN = 2 * WN;
+  constexpr int kNB = kWN / 16;                          // 16-column blocks per wave: 8 or 4
+  constexpr int kBElems = kBK * kBN;
+  constexpr int kBCopies = kBElems * 2 / 1024 / kWaves;  // 8 or 4
+  constexpr int kBChunks = kBN / 8;                      // 16-B chunks per staged [k][n] row: 32 or 16
+  constexpr int kKRowsPerCopy = 64 / kBChunks;           // k rows per 1-KiB copy of a [k][n] stage: 2 or 4
   constexpr int kBM = BM, kWM = BM / 2;
   constexpr int kMB = kWM / 16;                          // 16-row blocks per wave: 8 or 6
-  constexpr int kMpsl = (kMB / 2) * kNB;                 // MFMAs per slice: 32 or 24
+  constexpr int kMpsl = (kMB / 2) * kNB;                 // MFMAs per slice: 32, 24 or 16
   constexpr int kAMain = kBM * kBK;                      // the tile's own A rows in a stage
   constexpr int kAElems = kAMain + (XR ? 16 * kBK : 0), kStageElems = kAElems + kBElems;
   constexpr int kACopies = kAMain * 2 / 1024 / kWaves;   // 8 or 6
@@ -531,41 +536,43 @@ void gemm_bigwave16_kernel(const GemmParams p) {
   }
 }
 
-template <int MODE, int BM, bool XR = false>
+template <int MODE, int BM, bool XR = false, int WN = 128>
 void launch_one16(const GemmParams& p, hipStream_t stream) {
   const int blocks = p.rects > 0 ? p.rect_tmc[0] * p.rect_tnc[0] + (p.rects > 1 ? p.rect_tmc[1] * p.rect_tnc[1] : 0)
                                  : (p.splits > 1 ? p.splits : 1) * p.tiles_m * p.tiles_n;
   const dim3 grid((unsigned)blocks);
-  if (p.w_nk) hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, true, false, BM, XR>), grid, dim3(kThreads), 0, stream, p);
-  else if (p.w_blk) hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, false, true, BM, XR>), grid, dim3(kThreads), 0, stream, p);
-  else hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, false, false, BM, XR>), grid, dim3(kThreads), 0, stream, p);
+  if (p.w_nk) hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, true, false, BM, XR, WN>), grid, dim3(kThreads), 0, stream, p);
+  else if (p.w_blk) hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, false, true, BM, XR, WN>), grid, dim3(kThreads), 0, stream, p);
+  else hipLaunchKernelGGL((gemm_bigwave16_kernel<MODE, false, false, BM, XR, WN>), grid, dim3(kThreads), 0, stream, p);
 }
 
-template <int BM>
+template <int BM, int WN = 128>
 void launch_rows16(const GemmParams& p, hipStream_t stream) {
-  if (p.mode == kSiluMul) launch_one16<kSiluMul, BM>(p, stream);
-  else launch_one16<kPlain, BM>(p, stream);
+  if (p.mode == kSiluMul) launch_one16<kSiluMul, BM, false, WN>(p, stream);
+  else launch_one16<kPlain, BM, false, WN>(p, stream);
 }
-
-void launch_splits16(const GemmParams& p, hipStream_t stream) { launch_one16<kPartials, 256>(p, stream); }
 
 }  // namespace
 
 bool gemm_bigwave16_supports(const GemmParams& p) {
   // Tile sets with 256-row or 192-row tiles, or whole launches of 256-row tiles, or (plain columns)
-  // 256-row tiles cut along k, or (plain columns) whole launches of 256-row tiles with appended rows.
+  // 256-row tiles cut along k, or (plain columns) whole launches of 256-row tiles with appended rows;
+  // narrow (256 x 128) tiles as whole launches, or (plain columns) cut along k.
   const bool rows_ok = p.rects > 0 ? (p.tile_rows == 256 || p.tile_rows == 192) : (p.tile_rows == 0 || p.tile_rows == 256);
   const bool splits_ok = p.splits <= 1 || (p.rects == 0 && p.mode == kPlain && p.kt_per_split > 0);
   const bool xr_ok = p.xr_row0 == 0 || (p.xr_row0 > 0 && p.mode == kPlain && p.rects == 0 && p.splits <= 1);
-  return p.K % kBK == 0 && p.K > 0 && splits_ok && xr_ok && !p.narrow && p.persist == 0 && rows_ok;
+  const bool narrow_ok = !p.narrow || (p.rects == 0 && p.xr_row0 == 0);
+  return p.K % kBK == 0 && p.K > 0 && splits_ok && xr_ok && narrow_ok && p.persist == 0 && rows_ok;
 }
 
 hipError_t launch_gemm_bigwave16(const GemmParams& p, hipStream_t stream) {
   if (!gemm_bigwave16_supports(p)) return hipErrorInvalidValue;
   if (p.splits > 1) {
-    if (p.ws == nullptr || p.ws_ld < (int64_t)p.tiles_n * kBN) return hipErrorInvalidValue;
-    launch_splits16(p, stream);
+    if (p.ws == nullptr || p.ws_ld < (int64_t)p.tiles_n * (p.narrow ? 128 : 256)) return hipErrorInvalidValue;
+    if (p.narrow) launch_one16<kPartials, 256, false, 64>(p, stream);
+    else launch_one16<kPartials, 256>(p, stream);
   }
+  else if (p.narrow) launch_rows16<256, 64>(p, stream);
   else if (p.xr_row0 > 0) launch_one16<kPlain, 256, true>(p, stream);
   else if (p.tile_rows == 192) launch_rows16<192>(p, stream);
   else launch_rows16<256>(p, stream);

@@ -208,13 +208,14 @@ bool launch_tiles16_xr(GemmParams& p, int64_t head, int64_t tn, Ctx& c, hipError
   return true;
 }
 
-// 256 x 128 tiles of the four-wave kernel over all of p (K a multiple of 64).
+// 256 x 128 tiles of the four-wave kernels over all of p (K a multiple of 64): the 16 x 16 x 32
+// kernel's narrow instance where it applies.
 hipError_t launch_narrow(GemmParams& p, Ctx& c) {
   p.tiles_m = (int32_t)cdiv(p.M, gemm_tile_rows());
   p.tiles_n = (int32_t)cdiv(p.N, gemm_bigwave_tile_cols(p.mode, true));
   p.splits = 1;
   p.narrow = 1;
-  return run_bigwave(c, p);
+  return gemm_bigwave16_supports(p) ? run_tiled16(c, p) : run_bigwave(c, p);
 }
 
 // Row cut of one launch into 256-row and 192-row tiles (four-wave kernel, 256 weight columns per
@@ -450,8 +451,8 @@ hipError_t launch_tiles_splitk(GemmParams& p, int64_t splits, bool narrow, Ctx& 
   hipError_t e = workspace(c, (size_t)splits * q.M * q.ws_ld * sizeof(float), &base);
   if (e != hipSuccess) return e;
   q.ws = static_cast<float*>(base);
-  // 256 x 256 tiles on the 16 x 16 x 32 kernel, 256 x 128 tiles on the 32 x 32 x 16 one.
-  if ((e = (!narrow && gemm_bigwave16_supports(q)) ? run_tiled16(c, q) : run_bigwave(c, q)) != hipSuccess) return e;
+  // 256 x 256 or 256 x 128 tiles on the 16 x 16 x 32 kernel (else the 32 x 32 x 16 one).
+  if ((e = gemm_bigwave16_supports(q) ? run_tiled16(c, q) : run_bigwave(c, q)) != hipSuccess) return e;
   GemmParams f = p;
   f.ws = q.ws;
   f.ws_ld = q.ws_ld;

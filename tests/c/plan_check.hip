@@ -23,7 +23,8 @@ bool gemm_bigwave16_supports(const GemmParams& p) {  // the rule of gemm_bigwave
   const bool rows_ok = p.rects > 0 ? (p.tile_rows == 256 || p.tile_rows == 192) : (p.tile_rows == 0 || p.tile_rows == 256);
   const bool splits_ok = p.splits <= 1 || (p.rects == 0 && p.mode == 0 && p.kt_per_split > 0);
   const bool xr_ok = p.xr_row0 == 0 || (p.xr_row0 > 0 && p.mode == 0 && p.rects == 0 && p.splits <= 1);
-  return p.K % 64 == 0 && p.K > 0 && splits_ok && xr_ok && !p.narrow && p.persist == 0 && rows_ok;
+  const bool narrow_ok = !p.narrow || (p.rects == 0 && p.xr_row0 == 0);
+  return p.K % 64 == 0 && p.K > 0 && splits_ok && xr_ok && narrow_ok && p.persist == 0 && rows_ok;
 }
 hipError_t launch_gemm_bigwave16(const GemmParams& p, hipStream_t) { g_launched.push_back(p); g_kernel.push_back(16); return hipSuccess; }
 }  // namespace ttl

@@ -647,6 +647,43 @@ def test_splitk_repeated_launches_reuse_workspace(ttl, gemm_force):
             assert_close(from_gpu(Y[rows]), ref, f"repeated split-K {key}")
 
 
+@pytest.mark.parametrize("layout", ["kn", "nk", "blk"])
+@pytest.mark.parametrize("b,k,I,t,silu", [
+    (300, 256, 344, 1, True),     # ragged rows and act columns, four k-tiles
+    (513, 640, 1024, 2, False),   # ten k-tiles, three row-tiles
+    (257, 128, 1152, 1, False),   # ragged rows, 9 narrow column tiles (4.5 wide ones)
+    (64, 64, 256, 1, True),       # one k-tile
+    (700, 192, 768, 2, True)])    # three k-tiles
+def test_narrow_tiles_16x16(ttl, gemm_force, b, k, I, t, silu, layout):
+    """256 x 128 tiles of 16 x 16 x 32 products (whole, and cut along k): bit-equal to 256 x 256
+    tiles of the same kernel (whole) and to 256 x 256 tiles cut into the same k splits (each output
+    sums the same products in the same k order; the splits cover the same k ranges and are summed in
+    the same order), for every weight storage, and every element against the oracle."""
+    if layout == "blk" and (2 * I if silu else I) % 128:
+        pytest.skip("blocked storage needs a weight whose column count is a multiple of 128")
+    X = wl.random_bf16((b, k), 17 + b)
+    n = 2 * I if silu else I
+    W = wl.random_bf16((k, n), 18 + k, std=0.05)
+    Wd_, lay = _stored3(ttl, W, layout)
+    sp_c = ttl.merged_gate_up_split(I, t) if silu else None
+    sp_np = oracle.merged_gate_up_split(I, t) if silu else oracle.plain_split(I, t)
+    epi = ttl.EPI_SILU_MUL if silu else 0
+    Xd = gpu(X)
+    for r in range(t):
+        out = {}
+        for kern, splits in (("narrow", 0), ("tiled16", 0), ("narrowsplit", 2), ("tilesplit", 2)):
+            gemm_force.set(kernel=kern, splits=splits)
+            out[kern] = ttl.shard_linear_col(Xd, Wd_, t, r, sp_c, epi, w_layout=lay)
+        torch.cuda.synchronize()
+        assert torch.equal(out["narrow"], out["tiled16"]), f"narrow tiles differ from 256 x 256 tiles (rank {r})"
+        assert torch.equal(out["narrowsplit"], out["tilesplit"]), f"narrow k splits differ from 256 x 256 ones (rank {r})"
+        ref = oracle.col_shard(f64(X), f64(W), sp_np, t, r)
+        if silu:
+            ref = oracle.silu_mul(ref)
+        for kern in ("narrow", "narrowsplit"):
+            assert_close(from_gpu(out[kern]), ref, f"{kern} b={b} k={k} I={I} t={t} r={r} silu={silu} {layout}")
+
+
 @pytest.mark.parametrize("b,k,I,t,silu", [
     (300, 256, 344, 1, True),     # ragged rows and act columns, four k-tiles
     (513, 1024, 2048, 4, True),   # several tiles per rank
