@@ -436,15 +436,19 @@ def config_table(ttl, torch, layout, reps=20, warmup=3, only=None, only_op=None,
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / (replays * cycle) * 1e3
 
-    def report(wname, b, t, us, ops, graph_us, lay):
+    def report(wname, b, t, us, ops, graph_us, lay, us_alone=None):
         kern = {}
         for name, _, fl, by, cache in ops:
             u = us[name]
             tf, gbs = fl / (u * 1e6), by / (u * 1e3)
             bound = "mfma" if fl / by > RIDGE_FLOP_PER_BYTE else "hbm"
-            kern[name] = {"us": u, "tflops": tf, "gbs": gbs, "bound": bound,
-                          "frac": tf / PEAK_BF16_TFLOPS if bound == "mfma" else gbs / PEAK_HBM_GBS,
-                          "cache": cache}
+            frac = lambda tf, gbs: tf / PEAK_BF16_TFLOPS if bound == "mfma" else gbs / PEAK_HBM_GBS
+            kern[name] = {"us": u, "tflops": tf, "gbs": gbs, "bound": bound, "frac": frac(tf, gbs), "cache": cache}
+            if us_alone is not None:
+                # the call alone, repeated in a replayed graph: no host launch cost and no events
+                # between launches (the events of the chain's timing add a few us per kernel)
+                ua = us_alone[name]
+                kern[name].update({"us_graph": ua, "frac_graph": frac(fl / (ua * 1e6), by / (ua * 1e3))})
         print(json.dumps({"workload": wname, "tokens": b, "t": t, "weight_storage": names[lay],
                           "step_us": sum(us.values()), "step_us_graph": graph_us, "kernels": kern}),
               flush=True)
@@ -469,7 +473,8 @@ def config_table(ttl, torch, layout, reps=20, warmup=3, only=None, only_op=None,
             if not ops:
                 raise SystemExit(f"{wname}: no kernel named {only_op!r} (one of {[op[0] for op in chain.ops]})")
         us = _time_chain(torch, ops, max(reps, gcycle if gcycle <= 64 else reps), warmup)
-        report(wname, b, t, us, ops, graph_step_us(ops, min(gcycle, 64)) if graph else float("nan"), lay)
+        alone = {op[0]: graph_step_us([op], min(gcycle, 64)) for op in ops} if graph else None
+        report(wname, b, t, us, ops, graph_step_us(ops, min(gcycle, 64)) if graph else float("nan"), lay, alone)
 
     def wanted(w, b):
         if only is None:

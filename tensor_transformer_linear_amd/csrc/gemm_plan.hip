@@ -40,6 +40,7 @@ constexpr int kDefaultCUs = 256;        // MI355X compute units (a whole-chip de
 constexpr int kMinKTilesPerSplit = 4;   // keep each split's copy pipeline full
 constexpr int kTileSplitMinRows = 512;  // 256 x 256 tiles cut along k from this many rows
 constexpr int kMinKTilesPerTileSplit = 16;
+constexpr int kNarrowSplitMinKTiles = 8;  // one row-tile of 129..256 rows: k-tiles per split, at least
 constexpr int kShortK = 2048;           // split-K kernel: k up to this takes its smallest row tiles
 
 struct Workspace {
@@ -547,6 +548,19 @@ hipError_t plan_and_launch(GemmParams& p, Ctx& c) {
         return launch_tiles_splitk(p, nsplits, true, c);
       if (splits >= 2) return launch_tiles_splitk(p, splits, false, c);
     }
+    // One row-tile of 129..256 rows: 256 x 128 tiles cut along k into as many splits as fit one
+    // round, each of at least kNarrowSplitMinKTiles k-tiles, where that makes 4 splits or more
+    // (graph replay, [k][n] / [n][k] weights: 70B TP=8 SiLU·up at 256 tokens 64.2 -> 46.7 / 53.8 ->
+    // 48.5 us, at 192 tokens 56.4 -> 43.4 / 50.0 -> 45.7; 70B row GEMM at 256 tokens 36.3 -> 30.2 /
+    // 31.1 -> 28.4; 8B SiLU·up at 160-256 tokens 9-12 % / 4-5 %; 8B TP=4 qkv at 256 tokens 20.3 ->
+    // 18.3 / 20.0 -> 18.1).  Below: a k too short for 4 such splits (8B row GEMM, k = 1792: the
+    // split-K kernel's 15.1 against 20.0 us) and launches of 128 rows or fewer (half-empty tiles;
+    // the split-K kernel wins at 128, 96 and 64 rows) stay on the split-K kernel.
+    if (p.M > 128 && p.M <= 256 && gemm_bigwave_supports(p)) {
+      const int64_t by_cu = n_cu / narrow_tiles, by_kt = (p.K / 64) / kNarrowSplitMinKTiles;
+      const int64_t ns = by_cu < by_kt ? by_cu : by_kt;
+      if (ns >= 4) return launch_tiles_splitk(p, ns, true, c);
+    }
     return launch_splitk(p, c);
   }
   const int64_t rounds = tiles / n_cu, rem = tiles % n_cu;
@@ -621,7 +635,7 @@ size_t gemm_workspace_bytes(const GemmParams& p) {
   GemmParams q = p;
   Ctx c;
   c.dry = true;
-  plan_and_launch(q, c);
+  (void)plan_and_launch(q, c);  // the dry pass launches nothing and fails only on an invalid plan
   return c.need;
 }
 

@@ -217,6 +217,37 @@ int main() {
             ttl::g_launched[0].tiles_m == 8 && ttl::g_launched[0].tiles_n == 32 && ttl::g_launched[0].splits == 1,
             "2176 x 8192 k=%d (w_nk %d): %zu launches", K, nk, ttl::g_kernel.size());
     }
+  // One row-tile of 129..256 rows with a long k: 256 x 128 tiles cut along k on the 16 x 16 x 32
+  // kernel (8B TP=8 SiLU·up at 256 and 160 tokens: 28 tiles in 8 splits; 70B: 56 tiles in 4 splits;
+  // 70B row GEMM at 256 tokens, k = 3584: 64 tiles in 4 splits); the 8B row GEMM (k = 1792: 3
+  // splits of 8 k-tiles) and launches of at most 128 rows stay on the split-K kernel.
+  {
+    struct Case { int M, N, K, mode, splits; };
+    for (const Case& cs : {Case{256, 1792, 4096, 1, 8}, Case{160, 1792, 4096, 1, 8}, Case{256, 3584, 8192, 1, 4},
+                           Case{192, 3584, 8192, 1, 4}, Case{256, 8192, 3584, 0, 4}, Case{256, 4096, 1792, 0, 0},
+                           Case{128, 3584, 8192, 1, 0}, Case{96, 1792, 4096, 1, 0}}) {
+      GemmParams p = {};
+      p.M = cs.M;
+      p.N = cs.N;
+      p.K = cs.K;
+      p.mode = cs.mode;
+      ttl::g_launched.clear();
+      ttl::g_kernel.clear();
+      const size_t need = ttl::gemm_workspace_bytes(p);
+      CHECK(ttl::launch_gemm_fixed_workspace(p, reinterpret_cast<void*>(uintptr_t{4096}), need, nullptr) == hipSuccess,
+            "M=%d N=%d K=%d", cs.M, cs.N, cs.K);
+      if (cs.splits == 0) {
+        CHECK(ttl::g_launched.empty(), "M=%d N=%d K=%d: %zu tiled launches", cs.M, cs.N, cs.K, ttl::g_launched.size());
+      } else {
+        const int64_t tn = ttl::cdiv(cs.mode == 1 ? 2 * cs.N : cs.N, 128);
+        CHECK(ttl::g_kernel == std::vector<int>({16}) && ttl::g_launched[0].narrow == 1 &&
+              ttl::g_launched[0].splits == cs.splits && ttl::g_launched[0].tiles_n == tn &&
+              need == (size_t)cs.splits * cs.M * tn * 128 * 4,
+              "M=%d N=%d K=%d: %zu launches, splits %d", cs.M, cs.N, cs.K, ttl::g_launched.size(),
+              ttl::g_launched.empty() ? -1 : ttl::g_launched[0].splits);
+      }
+    }
+  }
   // Seeded plain shapes: wherever the planner appends rows, it is the call's only launch, the whole
   // row-tiles end where the appended rows begin, and those (16 per row-tile) reach row M.
   {

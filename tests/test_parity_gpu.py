@@ -648,6 +648,34 @@ def test_splitk_repeated_launches_reuse_workspace(ttl, gemm_force):
 
 
 @pytest.mark.parametrize("layout", ["kn", "nk", "blk"])
+@pytest.mark.parametrize("silu", [False, True])
+def test_auto_narrow_splits(ttl, gemm_force, layout, silu):
+    """One row-tile of 200 rows with k = 4096 (64 k-tiles): the shape-based choice cuts 256 x 128
+    tiles of the 16 x 16 x 32 kernel into 8 k splits (8 k-tiles each).  Bit-equal to the forced launch
+    of that plan, and every element against the oracle."""
+    b, k = 200, 4096
+    I = 896 if silu else 1792  # 14 tiles of 128 weight columns
+    n = 2 * I if silu else I
+    X = wl.random_bf16((b, k), 70 + int(silu))
+    W = wl.random_bf16((k, n), 72 + int(silu), std=0.02)
+    Wd_, lay = _stored3(ttl, W, layout)
+    sp_c = ttl.merged_gate_up_split(I, 1) if silu else None
+    sp_np = oracle.merged_gate_up_split(I, 1) if silu else oracle.plain_split(I, 1)
+    epi = ttl.EPI_SILU_MUL if silu else 0
+    Xd = gpu(X)
+    gemm_force.set(kernel="auto", splits=0)
+    auto = ttl.shard_linear_col(Xd, Wd_, 1, 0, sp_c, epi, w_layout=lay)
+    gemm_force.set(kernel="narrowsplit", splits=8)
+    forced = ttl.shard_linear_col(Xd, Wd_, 1, 0, sp_c, epi, w_layout=lay)
+    torch.cuda.synchronize()
+    assert torch.equal(auto, forced)
+    ref = oracle.col_shard(f64(X), f64(W), sp_np, 1, 0)
+    if silu:
+        ref = oracle.silu_mul(ref)
+    assert_close(from_gpu(auto), ref, f"auto narrow splits silu={silu} {layout}")
+
+
+@pytest.mark.parametrize("layout", ["kn", "nk", "blk"])
 @pytest.mark.parametrize("b,k,I,t,silu", [
     (300, 256, 344, 1, True),     # ragged rows and act columns, four k-tiles
     (513, 640, 1024, 2, False),   # ten k-tiles, three row-tiles
