@@ -99,6 +99,38 @@ def test_mlp_shard_full_size(ttl, w, b, layout):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("b", [192, 256])
+@pytest.mark.parametrize("layout", ["kn", "nk", "blk"])
+def test_mid_batch_70b_tp8(ttl, b, layout):
+    """The Llama-3-70B MLP shard at TP=8 at 192 and 256 tokens, the shapes the planner gives 256 x 128
+    tiles cut along k (SiLU·up: 56 tiles x 4 splits; down at 256 tokens: 64 tiles x 4 splits), for
+    ranks 0 and 7: sampled rows (the first and last of every 64-row block, plus seeded picks) of act
+    and of the down partial against the oracle, each step from the bf16 tensor the previous one
+    stores."""
+    w = wl.LLAMA3_70B_MLP_TP8
+    t, I = w.t, w.intermediate
+    d = wl.mlp_inputs(w, b, seed=3, device="cuda")
+    Wgu_s, lay = _stored(ttl, d["Wgu"], layout)
+    Wd_s, _ = _stored(ttl, d["Wd"], layout)
+    sp = ttl.merged_gate_up_split(I, t)
+    rng = np.random.default_rng(77 + b)
+    rows = sorted({0, b - 1} | {r for r0 in range(0, b, 64) for r in (r0, min(r0 + 63, b - 1))}
+                  | {int(r) for r in rng.choice(b, size=8, replace=False)})
+    Wgu_o, Wd_o = f64(d["Wgu"].cpu()), f64(d["Wd"].cpu())
+    Xs = f64(d["X"][rows].cpu())
+    for r in (0, t - 1):
+        act = ttl.shard_linear_col(d["X"], Wgu_s, t, r, sp, ttl.EPI_SILU_MUL, w_layout=lay)
+        P = ttl.shard_linear_row(act, Wd_s, t, r, True, w_layout=lay)
+        ref_act = oracle.silu_mul(oracle.col_shard(Xs, Wgu_o, oracle.merged_gate_up_split(I, t), t, r))
+        assert_close(from_gpu(act[rows]), ref_act, f"70B b={b} {layout} act r={r}")
+        # each row's partial depends on that row of the stored bf16 act only
+        ref_P = oracle.row_shard(f64(act[rows].cpu()), Wd_o, t, r, x_is_parallel=True)
+        assert_close(from_gpu(P[rows]), ref_P, f"70B b={b} {layout} down partial r={r}")
+    del d, Wgu_s, Wd_s
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
 def test_attn_projections_8b_tp4(ttl):
     w = wl.LLAMA3_8B_ATTN_TP4
     b = w.batches[0]
