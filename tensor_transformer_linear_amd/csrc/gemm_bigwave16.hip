@@ -17,7 +17,8 @@
 // Weights stored [n][k] reach the products with plain 16-byte LDS reads, as the activations do.
 // Weights stored [k][n] (plain or in 64 x 128 blocks) are staged [k][n] and read with
 // ds_read_b64_tr_b16, two transposed half reads per fragment, joined at the product; their products
-// are written out as asm with the accumulator tied in place (see mfma_one).
+// (and, in the instances with appended rows, every storage's) are written out as asm with the
+// accumulator tied in place (see mfma_one).
 //
 // Per k-tile t and wave (order pinned with scheduling barriers):
 //   slice 0: 32 MFMAs, with the LDS reads of slice 2 of tile t (its row blocks and the weight

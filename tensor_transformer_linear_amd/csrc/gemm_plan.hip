@@ -6,11 +6,14 @@
 // k into as many ranges as keep the grid within one workgroup per CU: a CU streams at its full
 // rate with one workgroup, and a grid that does not divide evenly over the CUs leaves a slow tail.
 // A launch of whole rounds of 256 x 256 tiles plus a short last round (e.g. 288 tiles: 2176 rows
-// x 8192 columns) is cut by rows: the whole rounds to the tiled kernel, the last few row-tiles to
-// the split-K kernel.  One whose last round is more than half full (e.g. 448 tiles: 4096 rows x
-// 3584 SiLU·up columns) is cut per column strip into 256-row tiles that fill the whole rounds and
-// 192-row tiles that fill one more round, which then takes three quarters of a round's time.  The
-// 256 x 256 and 192 x 256 tiles run on the 16 x 16 x 32 kernel for every weight storage.
+// x 8192 columns) runs the whole rounds' tiles with the rows below them appended (at most 16 per
+// row-tile, plain columns), or else is cut by rows: the whole rounds to the tiled kernel, the last
+// few row-tiles to the split-K kernel.  One whose last round is more than half full (e.g. 448
+// tiles: 4096 rows x 3584 SiLU·up columns) is cut per column strip into 256-row tiles that fill
+// the whole rounds and 192-row tiles that fill one more round, which then takes three quarters of
+// a round's time.  Launches with few 256 x 256 tiles take 256 x 128 tiles, whole or cut along k
+// (at least 512 rows; or one row-tile of 129..256 rows with a long k).  Every tiled launch runs
+// on the 16 x 16 x 32 kernel, for every weight storage.
 //
 // Workspace: split-K launches with more than one split write fp32 partial tiles that a second
 // kernel reduces.  The library keeps one device buffer per (GPU, stream) for them, allocated (or
@@ -19,7 +22,8 @@
 // recorded after one eager call of the same (or a larger) shape on the capturing stream.
 //
 // Overrides for tests and measurements (ttl_set_gemm_override): a forced kernel family, a forced
-// split count, the CU count the 256-row / 192-row cut is planned for, and a trace of each cut.
+// split count, the CU count the 256-row / 192-row cut is planned for, and a trace of each cut,
+// appended-rows or persistent launch.
 // They are process-wide atomics read once per launch; nothing here reads the environment.
 #include <cstdio>
 #include <cstdlib>

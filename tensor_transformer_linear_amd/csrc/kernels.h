@@ -104,11 +104,12 @@ int gemm_bigwave_tile_cols(int mode, bool narrow);
 // workgroups, each writing its fp32 partial tile; launch_splitk_finalize then sums them.
 hipError_t launch_gemm_bigwave(const GemmParams& p, hipStream_t stream);
 
-// The 256 x 256 tiles of the four-wave kernel fed to 16 x 16 x 32 products (gemm_bigwave16.hip):
-// every weight storage, whole launches of 256-row tiles, tile sets of 256-row or 192-row tiles, or
-// (plain columns) 256-row tiles cut along k into fp32 partials for launch_splitk_finalize (not
-// persistent), or (plain columns) whole launches of 256-row tiles with 16 appended rows (xr_row0),
-// K a multiple of 64.  Same results as launch_gemm_bigwave, bit for bit.
+// The tiles of the four-wave kernel fed to 16 x 16 x 32 products (gemm_bigwave16.hip), every
+// weight storage, K a multiple of 64: whole launches of 256 x 256 tiles, or of 256 x 128 tiles
+// (p.narrow), tile sets of 256-row or 192-row tiles, (plain columns) 256 x 256 or 256 x 128 tiles
+// cut along k into fp32 partials for launch_splitk_finalize (not persistent), or (plain columns)
+// whole launches of 256 x 256 tiles with 16 appended rows (xr_row0).  Same results as
+// launch_gemm_bigwave, bit for bit.
 bool gemm_bigwave16_supports(const GemmParams& p);
 hipError_t launch_gemm_bigwave16(const GemmParams& p, hipStream_t stream);
 
