@@ -22,8 +22,9 @@
 //
 // Per k-tile t and wave (order pinned with scheduling barriers):
 //   slice 0: 32 MFMAs, with the LDS reads of slice 2 of tile t (its row blocks and the weight
-//            fragments of k32 step 1);
-//   slice 1: 32 MFMAs, with the reads of slice 3 (its row blocks, into slice 0's registers);
+//            fragments of k32 step 1), and in the instances whose products are asm also those of
+//            slice 3, so that no read is still in flight at the barrier;
+//   slice 1: 32 MFMAs, with (builtin products) the reads of slice 3 (its row blocks);
 //   barrier: the wave waits for its own copies of tile t+1; the workgroup barrier publishes tile
 //            t+1 and certifies that every wave's reads of tile t have returned;
 //   slice 2: 32 MFMAs, reads of slice 0 of tile t+1 (row-block and weight fragments of its first
@@ -363,13 +364,21 @@ void gemm_bigwave16_kernel(const GemmParams p) {
   auto k_tile = [&](int t, auto next_c, auto copy_c) {
     constexpr bool NEXT = decltype(next_c)::value, COPY = decltype(copy_c)::value;
     // slice 0: reads of slice 2 of tile t (its row blocks and the weight fragments of step 1);
-    // slice 1: reads of slice 3 (row blocks only), into the registers slice 0 has finished with.
+    // slice 1: reads of slice 3 (row blocks only).  With asm products the reads of slice 3 are
+    // issued in slice 0 too: the barrier after slice 1 waits for every read of the wave, and the
+    // last of them no longer trails the slice (70B TP=8 at 4096 tokens, [k][n] weights, medians of
+    // 8 alternating runs: SiLU·up 358.3 -> 355.6 us, row GEMM 179.8 -> 176.6 us; with the builtin
+    // products the longer-lived fragments made the allocator move accumulators: [n][k] 447.7 us).
     constexpr int kR0 = kMB / 2 + kBReads, kR1 = kMB / 2;
+    constexpr int kRS0 = kAsm ? kR0 + kR1 : kR0, kRS1 = kAsm ? 0 : kR1;
 #pragma unroll
     for (int j = 0; j < kMpsl; ++j) {
       mfma_one(0, j);
 #pragma unroll
-      for (int r = j * kR0 / kMpsl; r < (j + 1) * kR0 / kMpsl; ++r) read_one(t, 2, r);
+      for (int r = j * kRS0 / kMpsl; r < (j + 1) * kRS0 / kMpsl; ++r) {
+        if (r < kR0) read_one(t, 2, r);
+        else read_one(t, 3, r - kR0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     slice_x(0);
@@ -377,7 +386,7 @@ void gemm_bigwave16_kernel(const GemmParams p) {
     for (int j = 0; j < kMpsl; ++j) {
       mfma_one(1, j);
 #pragma unroll
-      for (int r = j * kR1 / kMpsl; r < (j + 1) * kR1 / kMpsl; ++r) read_one(t, 3, r);
+      for (int r = j * kRS1 / kMpsl; r < (j + 1) * kRS1 / kMpsl; ++r) read_one(t, 3, r);
       __builtin_amdgcn_sched_barrier(0);
     }
     slice_x(1);
