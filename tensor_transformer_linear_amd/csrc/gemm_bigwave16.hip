@@ -24,12 +24,15 @@
 //   slice 0: 32 MFMAs, with the LDS reads of slice 2 of tile t (its row blocks and the weight
 //            fragments of k32 step 1), and in the instances whose products are asm also those of
 //            slice 3, so that no read is still in flight at the barrier;
-//   slice 1: 32 MFMAs, with (builtin products) the reads of slice 3 (its row blocks);
+//   slice 1: 32 MFMAs, with (builtin products) the reads of slice 3 (its row blocks); with asm
+//            products, a workgroup barrier after the eighth MFMA (every wave's reads of tile t have
+//            returned, so its stage is free) and then the first direct-to-LDS copies of tile t+2;
 //   barrier: the wave waits for its own copies of tile t+1; the workgroup barrier publishes tile
-//            t+1 and certifies that every wave's reads of tile t have returned;
+//            t+1 (and, with builtin products, certifies that every wave's reads of tile t returned);
 //   slice 2: 32 MFMAs, reads of slice 0 of tile t+1 (row-block and weight fragments of its first
-//            k32 step), and half of the direct-to-LDS copies of tile t+2, one after every fourth MFMA;
-//   slice 3: 32 MFMAs, reads of slice 1 of tile t+1, the other half of the copies.
+//            k32 step), and copies of tile t+2: spread evenly from the first barrier to the end of
+//            slice 3 with asm products, otherwise half of them, one after every fourth MFMA;
+//   slice 3: 32 MFMAs, reads of slice 1 of tile t+1, the other copies.
 // Lane layouts (weight fragment as the first operand, so each lane ends with four consecutive
 // output columns of one output row): first operand lane l holds weight column l % 16 of the block
 // and k = 8 (l / 16) .. + 7 of the k32 step; second operand lane l holds activation row l % 16 and
@@ -101,6 +104,20 @@ void gemm_bigwave16_kernel(const GemmParams p) {
   // Products written as asm with the accumulator tied in place (see mfma_one): [k][n] weights, and
   // every storage with appended rows.
   constexpr bool kAsm = !WNK || XR;
+  // Where a k-tile's copies go.  With asm products every read of tile t's stage is issued by the end
+  // of slice 0, so a second barrier, kB1 products into slice 1, frees that stage for tile t+2's
+  // copies, and they spread over the rest of slices 1-3 (about 2.5 % fewer active cycles than in
+  // slices 2-3 alone for the 70B TP=8 [k][n] GEMMs at 4096 tokens; the barrier's position measured
+  // best at 8 of 2-20); otherwise they follow the barrier after slice 1.
+  constexpr bool kSplitBarrier = kAsm;
+  constexpr int kB1 = 8;
+  static_assert(kB1 < kMpsl, "the first barrier sits inside slice 1");
+  constexpr int kCopy0 = kSplitBarrier ? kMpsl + kB1 + 1 : 2 * kMpsl, kCopySpan = 4 * kMpsl - kCopy0;
+  constexpr int kCopiesS1 = [] {
+    int n = 0;
+    for (int c = 0; c < kCopies; ++c) n += kCopy0 + (c + 1) * kCopySpan / kCopies - 1 < 2 * kMpsl;
+    return n;
+  }();
   __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages * kStageElems];
 
   const int tid = threadIdx.x;
@@ -382,27 +399,37 @@ void gemm_bigwave16_kernel(const GemmParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     slice_x(0);
+    // The descriptors of tile t+2's copies are built between slice 1's first products.  Copy c
+    // follows slot kCopy0 + (c + 1) kCopySpan / kCopies - 1 of the k-tile's 4 kMpsl product slots.
+    i32x4_t ad = {0, 0, 0, 0}, bd = {0, 0, 0, 0}, xd = {0, 0, 0, 0};
 #pragma unroll
     for (int j = 0; j < kMpsl; ++j) {
       mfma_one(1, j);
 #pragma unroll
       for (int r = j * kRS1 / kMpsl; r < (j + 1) * kRS1 / kMpsl; ++r) read_one(t, 3, r);
+      if (COPY) {
+        if (j == 0) ad = a_desc(t + kStages);
+        if (j == 1) bd = b_desc(t + kStages);
+        if (XR && j == 2) xd = x_desc(t + kStages);
+        // every read of tile t's stage was issued in slice 0: once all have returned, in every
+        // wave, tile t+2's copies may overwrite it
+        if (kSplitBarrier && j == kB1) lds_barrier();
+#pragma unroll
+        for (int c = 0; c < kCopies; ++c)
+          if (kCopy0 + (c + 1) * kCopySpan / kCopies - 1 == kMpsl + j) copy_one(t + kStages, c, ad, bd);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     slice_x(1);
     if (NEXT) {
-      wait_vmcnt<0>();  // this wave's copies of tile t+1 landed
-      lds_barrier();    // ... everyone's; and every wave's reads of tile t returned
+      // this wave's copies of tile t+1 landed (those of tile t+2 issued in slice 1 are the last
+      // kCopiesS1 copies), then everyone's; and every wave's reads of tile t returned
+      if (COPY) wait_vmcnt<kCopiesS1>();
+      else wait_vmcnt<0>();
+      lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
     }
-    i32x4_t ad = {0, 0, 0, 0}, bd = {0, 0, 0, 0}, xd = {0, 0, 0, 0};
-    if (COPY) {
-      ad = a_desc(t + kStages);
-      bd = b_desc(t + kStages);
-      if (XR) xd = x_desc(t + kStages);
-    }
-    // slice 2: reads of slice 0 of tile t+1; copy c follows MFMA slot (c + 1) 2 kMpsl / kCopies - 1
-    // of slices 2-3 (slots kMpsl.. are slice 3's): after every fourth MFMA for 256-row tiles.
+    // slice 2: reads of slice 0 of tile t+1 and copies
     constexpr int kR2 = kMB / 2 + kBReads;
 #pragma unroll
     for (int j = 0; j < kMpsl; ++j) {
@@ -410,7 +437,7 @@ void gemm_bigwave16_kernel(const GemmParams p) {
       if (COPY) {
 #pragma unroll
         for (int c = 0; c < kCopies; ++c)
-          if ((c + 1) * 2 * kMpsl / kCopies - 1 == j) copy_one(t + kStages, c, ad, bd);
+          if (kCopy0 + (c + 1) * kCopySpan / kCopies - 1 == 2 * kMpsl + j) copy_one(t + kStages, c, ad, bd);
         if (j == kMpsl - 1 && x_copier) copy_x(t + kStages, xd);
       }
       if (NEXT) {
@@ -428,7 +455,7 @@ void gemm_bigwave16_kernel(const GemmParams p) {
       if (COPY) {
 #pragma unroll
         for (int c = 0; c < kCopies; ++c)
-          if ((c + 1) * 2 * kMpsl / kCopies - 1 == kMpsl + j) copy_one(t + kStages, c, ad, bd);
+          if (kCopy0 + (c + 1) * kCopySpan / kCopies - 1 == 3 * kMpsl + j) copy_one(t + kStages, c, ad, bd);
       }
       if (NEXT) {
 #pragma unroll
