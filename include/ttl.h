@@ -352,6 +352,8 @@ const char* ttl_last_error(void);
 #define TTL_GEMM_APPENDED 11    /* 256 x 256 tiles (16 x 16 x 32) over the whole row-tiles, the rows
                                    below them appended to the tiles, at most 16 per row-tile (plain
                                    columns, K % 64 == 0); otherwise the choice by shape */
+#define TTL_GEMM_STREAM_NK 12   /* the split-free kernel for weights stored [n][k] and at most 64
+                                   rows (K % 32 == 0); otherwise the choice by shape */
 ttl_status ttl_set_gemm_override(int32_t kernel, int32_t splits, int32_t plan_cus, int32_t trace);
 
 /* Library version: major * 10000 + minor * 100 + patch. */

@@ -115,6 +115,7 @@ hipError_t run_tileset(Ctx& c, const GemmParams& p) {
 hipError_t run_skinny(Ctx& c, const GemmParams& p, int mb) {
   return c.dry ? hipSuccess : launch_gemm_skinny(p, mb, c.stream);
 }
+hipError_t run_stream_nk(Ctx& c, const GemmParams& p) { return c.dry ? hipSuccess : launch_gemm_stream_nk(p, c.stream); }
 hipError_t run_finalize(Ctx& c, const GemmParams& p) { return c.dry ? hipSuccess : launch_splitk_finalize(p, c.stream); }
 
 // Test and measurement overrides (see ttl_set_gemm_override).
@@ -144,7 +145,8 @@ int64_t device_cus() {
 // k, 7 192 x 256 tiles, 8 the 256-row / 192-row cut planned for the override's CU count, 9 256 x 256
 // tiles by a persistent grid (at most two tiles per workgroup), 10 256 x 256 tiles by the 16 x 16 x 32
 // kernel, 11 the same over the whole row-tiles with the rows below them appended (where those are at
-// most 16 per row-tile; otherwise the choice by shape).
+// most 16 per row-tile; otherwise the choice by shape), 12 the split-free kernel for [n][k] weights
+// and at most 64 rows (otherwise the choice by shape).
 int forced_kernel() { return g_force_kernel.load(std::memory_order_relaxed); }
 int64_t forced_splits() { return g_force_splits.load(std::memory_order_relaxed); }
 
@@ -507,6 +509,7 @@ hipError_t plan_and_launch(GemmParams& p, Ctx& c) {
   const int64_t n_cu = device_cus();
   const int64_t min_tiled = n_cu * 3 / 4;  // 256 x 256 tiles when they occupy >= 3/4 of the CUs
   if (force == 1 || force == 3) return launch_tiles(p, force, c);
+  if (force == 12 && gemm_stream_nk_supports(p)) return run_stream_nk(c, p);
   if (force == 9) return launch_persist(p, c);
   if (force == 10) return launch_tiles16(p, c);
   if (force == 11 && p.M > 256 && p.M % 256 != 0) {
@@ -532,6 +535,13 @@ hipError_t plan_and_launch(GemmParams& p, Ctx& c) {
     const int64_t auto_splits = n_cu / (force == 4 ? tiles : narrow_tiles);
     return launch_tiles_splitk(p, fs > 0 ? fs : (auto_splits > 2 ? auto_splits : 2), force == 6, c);
   }
+  // Decode batches of at most 16 rows with [n][k] weights: the split-free kernel where its workgroups
+  // (one per 32 weight columns) occupy at least 3/4 of the CUs; it writes no fp32 partials and needs
+  // no second kernel (70B TP=8 at 1 token, ranks cycled, graph replay: SiLU·up 32.8 -> 31.0 us, row
+  // GEMM 16.0 -> 14.3 us).  With more rows every workgroup's pass over all of X costs more than
+  // the split-K kernel's partials (at 32 and 64 tokens: SiLU·up 28.4 -> 40.4 and 31-34 -> 54.7 us).
+  if (force == 0 && p.M <= 16 && gemm_stream_nk_supports(p) && gemm_stream_nk_workgroups(p) >= min_tiled)
+    return run_stream_nk(c, p);
   if (tiles < min_tiled) {
     // Few 256 x 256 tiles.  With many rows and a long k, 256 x 256 tiles cut along k into about
     // one workgroup per CU keep the matrix cores busier than the split-K kernel's 128-row tiles;

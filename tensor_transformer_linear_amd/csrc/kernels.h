@@ -120,6 +120,13 @@ constexpr int kSkinnyCols = 128;  // weight columns per tile (64 act columns in 
 constexpr int kSkinnyK = 64;      // k per pipeline stage
 hipError_t launch_gemm_skinny(const GemmParams& p, int mb, hipStream_t stream);
 
+// Split-free GEMM for at most 64 token rows with the weight stored [n][k] (p.w_nk), K a multiple of
+// 32: one workgroup per 32 weight columns over the whole of k (its four waves cut k into quarters
+// and add their sums through LDS), fragments loaded straight into registers; no workspace.
+bool gemm_stream_nk_supports(const GemmParams& p);
+int64_t gemm_stream_nk_workgroups(const GemmParams& p);
+hipError_t launch_gemm_stream_nk(const GemmParams& p, hipStream_t stream);
+
 // Sum of the p.splits fp32 partials in p.ws (ascending split order), then the epilogue of p.mode
 // (SiLU·up: gate at workspace column j, up at column N + j), into p.C.
 hipError_t launch_splitk_finalize(const GemmParams& p, hipStream_t stream);

@@ -438,7 +438,7 @@ ttl_status shard_linear_row(const uint16_t* X, int64_t b, int64_t k, int32_t x_i
 
 ttl_status ttl_set_gemm_override(int32_t kernel, int32_t splits, int32_t plan_cus, int32_t trace) {
   static const char* who = "ttl_set_gemm_override";
-  if (kernel < TTL_GEMM_AUTO || kernel > TTL_GEMM_APPENDED)
+  if (kernel < TTL_GEMM_AUTO || kernel > TTL_GEMM_STREAM_NK)
     return fail(TTL_ERR_UNSUPPORTED, "%s: unknown kernel family %d", who, kernel);
   if (splits < 0 || plan_cus < 0)
     return fail(TTL_ERR_UNSUPPORTED, "%s: splits=%d and plan_cus=%d must be >= 0", who, splits, plan_cus);

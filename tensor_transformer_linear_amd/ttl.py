@@ -40,7 +40,7 @@ EXPORTED = ("shard_linear_col", "shard_linear_col_stored", "shard_linear_col_noa
 # GEMM kernel families ttl_set_gemm_override can force (tests and measurements only)
 GEMM_KERNELS = {"auto": 0, "tiled": 1, "splitk": 2, "eightwave": 3, "tilesplit": 4, "narrow": 5,
                 "narrowsplit": 6, "short": 7, "mixed": 8, "persist": 9, "tiled16": 10,
-                "appended": 11}
+                "appended": 11, "streamnk": 12}
 
 
 class ColSplit(ctypes.Structure):

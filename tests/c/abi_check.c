@@ -54,7 +54,7 @@ int main(void) {
          TTL_ERR_NOT_DIVISIBLE);
   expect("row (stored): blocked with (k/t) % 64", shard_linear_row_stored(X, 16, 1024, 1, W, 256, TTL_W_BLOCKED, 32, 0, Y, NULL),
          TTL_ERR_ALIGN);
-  expect("override: unknown kernel", ttl_set_gemm_override(TTL_GEMM_APPENDED + 1, 0, 0, 0), TTL_ERR_UNSUPPORTED);
+  expect("override: unknown kernel", ttl_set_gemm_override(TTL_GEMM_STREAM_NK + 1, 0, 0, 0), TTL_ERR_UNSUPPORTED);
   expect("reduce: misaligned Y", reduce_partials_rmsnorm(X, 2, 16, 256, NULL, gamma, 1e-5f, Y, Y + 2, NULL),
          TTL_ERR_ALIGN);
   expect("reduce-scatter: b not divisible by t",

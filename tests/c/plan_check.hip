@@ -17,7 +17,7 @@ hipError_t launch_gemm_tiled(const GemmParams&, hipStream_t) { return hipSuccess
 hipError_t launch_gemm_skinny(const GemmParams&, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_splitk_finalize(const GemmParams&, hipStream_t) { return hipSuccess; }
 std::vector<GemmParams> g_launched;
-std::vector<int> g_kernel;  // per launch: 32 (32 x 32 x 16 kernel) or 16 (16 x 16 x 32 kernel)
+std::vector<int> g_kernel;  // per launch: 32 (32 x 32 x 16 kernel), 16 (16 x 16 x 32 kernel), 1 (split-free [n][k] kernel)
 hipError_t launch_gemm_bigwave(const GemmParams& p, hipStream_t) { g_launched.push_back(p); g_kernel.push_back(32); return hipSuccess; }
 bool gemm_bigwave16_supports(const GemmParams& p) {  // the rule of gemm_bigwave16.hip
   const bool rows_ok = p.rects > 0 ? (p.tile_rows == 256 || p.tile_rows == 192) : (p.tile_rows == 0 || p.tile_rows == 256);
@@ -27,6 +27,11 @@ bool gemm_bigwave16_supports(const GemmParams& p) {  // the rule of gemm_bigwave
   return p.K % 64 == 0 && p.K > 0 && splits_ok && xr_ok && narrow_ok && p.persist == 0 && rows_ok;
 }
 hipError_t launch_gemm_bigwave16(const GemmParams& p, hipStream_t) { g_launched.push_back(p); g_kernel.push_back(16); return hipSuccess; }
+bool gemm_stream_nk_supports(const GemmParams& p) {  // the rule of gemm_stream_nk.hip
+  return p.w_nk != 0 && p.M >= 1 && p.M <= 64 && p.K % 32 == 0 && p.K >= 2048 && p.N > 0;
+}
+int64_t gemm_stream_nk_workgroups(const GemmParams& p) { return (p.N + (p.mode == 1 ? 15 : 31)) / (p.mode == 1 ? 16 : 32); }
+hipError_t launch_gemm_stream_nk(const GemmParams& p, hipStream_t) { g_launched.push_back(p); g_kernel.push_back(1); return hipSuccess; }
 }  // namespace ttl
 
 static int failures = 0;
@@ -288,6 +293,34 @@ int main() {
   }
   CHECK(planned > 100, "only %d of the seeded shapes were cut", planned);
   std::printf("%d seeded cuts checked\n", planned);
+  // Decode GEMMs: with [n][k] weights and at most 16 rows the 70B TP=8 rank's gate_up (SiLU·up, 3584
+  // act columns: 224 workgroups of 16) and down (8192 columns, k = 3584: 256 of 32) run on the
+  // split-free kernel, with no workspace; with [k][n] weights, more rows (the 64-token decode), too
+  // few workgroups (8B TP=8 gate_up: 1792 act columns, 112) or a short k (8B row GEMM, k = 1792),
+  // they stay on the split-K kernel.
+  {
+    struct Case { int M, N, K, mode, nk; bool stream; };
+    const Case cases[] = {{16, 3584, 8192, 1, 1, true}, {1, 8192, 3584, 0, 1, true}, {1, 3584, 8192, 1, 0, false},
+                          {1, 8192, 3584, 0, 0, false}, {17, 3584, 8192, 1, 1, false}, {64, 8192, 3584, 0, 1, false},
+                          {1, 1792, 4096, 1, 1, false}, {1, 4096, 1792, 0, 1, false}};
+    for (const Case& k : cases) {
+      GemmParams p = {};
+      p.M = k.M;
+      p.N = k.N;
+      p.K = k.K;
+      p.mode = k.mode;
+      p.w_nk = k.nk;
+      ttl::g_launched.clear();
+      ttl::g_kernel.clear();
+      float fake[4];  // a stand-in workspace for the split-K plans (the stub launchers do not touch it)
+      CHECK(ttl::launch_gemm_fixed_workspace(p, fake, (size_t)1 << 40, nullptr) == hipSuccess, "launch M=%d N=%d K=%d",
+            k.M, k.N, k.K);
+      const bool stream = ttl::g_kernel.size() == 1 && ttl::g_kernel[0] == 1;
+      CHECK(stream == k.stream, "M=%d N=%d K=%d mode %d w_nk %d: split-free kernel %d, expected %d", k.M, k.N, k.K,
+            k.mode, k.nk, (int)stream, (int)k.stream);
+      if (k.stream) CHECK(ttl::gemm_workspace_bytes(p) == 0, "M=%d N=%d K=%d: workspace", k.M, k.N, k.K);
+    }
+  }
   if (failures == 0) std::printf("ALL OK\n");
   return failures == 0 ? 0 : 1;
 }

@@ -159,7 +159,7 @@ def _peers(ptrs=None, t=2, b=16, n=256, row0=0, rows=16, R=B, gamma=D, eps=1e-5,
     (lambda: _colg(k=252), ttl.ERR_ALIGN, "multiples of 8"),
     (lambda: _row(lay=-1), ttl.ERR_UNSUPPORTED, "weight layout"),
     (lambda: _row(lay=ttl.W_KN, P=None), ttl.ERR_NULL, "shard_linear_row_stored"),
-    (lambda: ttl.lib().ttl_set_gemm_override(12, 0, 0, 0), ttl.ERR_UNSUPPORTED, "unknown kernel"),
+    (lambda: ttl.lib().ttl_set_gemm_override(13, 0, 0, 0), ttl.ERR_UNSUPPORTED, "unknown kernel"),
     (lambda: ttl.lib().ttl_set_gemm_override(2, -1, 0, 0), ttl.ERR_UNSUPPORTED, "splits=-1"),
     (lambda: ttl.lib().ttl_set_gemm_override(0, 0, -4, 0), ttl.ERR_UNSUPPORTED, "plan_cus=-4"),
     (lambda: _row(lay=ttl.W_BLOCKED), ttl.ERR_ALIGN, "blocked weight"),          # k % 64 != 0

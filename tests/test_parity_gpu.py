@@ -712,6 +712,76 @@ def test_narrow_tiles_16x16(ttl, gemm_force, b, k, I, t, silu, layout):
             assert_close(from_gpu(out[kern]), ref, f"{kern} b={b} k={k} I={I} t={t} r={r} silu={silu} {layout}")
 
 
+@pytest.mark.parametrize("b,k,n,t,kind", [
+    (1, 2048, 1024, 2, "silu"),     # one token row; the shortest k the kernel takes (16 k32 steps per wave)
+    (17, 2080, 624, 2, "silu"),     # ragged rows, 312 act columns (19.5 workgroups); 65 k32 steps, uneven quarters
+    (64, 4096, 1056, 4, "plain"),   # 64 rows (four row blocks); 264 columns, 8 in the last workgroup
+    (33, 2048, 0, 2, "qkv"),        # three column segments (8 q + 2 kv heads of 32, t = 2)
+    (64, 8192, 520, 4, "row"),      # row-parallel, X the rank's own k slice
+    (40, 8192, 520, 4, "row_full"),  # row-parallel, X full width (the rank's slice read in place)
+])
+def test_stream_nk_split_free(ttl, gemm_force, b, k, n, t, kind):
+    """The split-free kernel for [n][k] weights and up to 64 token rows (forced): every element of
+    every rank against the oracle, and a second launch bit-equal to the first (its four waves' sums
+    are added in a fixed order)."""
+    X = wl.random_bf16((b, k), 500 + b)
+    if kind == "qkv":
+        sp_np, sp_c = oracle.qkv_split(8, 2, 32, t), ttl.qkv_split(8, 2, 32, t)
+        n = sum(sp_np[0])
+    elif kind == "silu":
+        sp_np, sp_c = oracle.merged_gate_up_split(n, t), ttl.merged_gate_up_split(n, t)
+        n = 2 * n
+    else:
+        sp_np, sp_c = oracle.plain_split(n, t), None
+    W = wl.random_bf16((k, n), 501 + b, std=0.05)
+    Xd, Wd = gpu(X), gpu(W.t().contiguous())
+    Xo, Wo = f64(X), f64(W)
+    gemm_force.set(kernel="streamnk", splits=0)
+    for r in range(t):
+        if kind.startswith("row"):
+            w = k // t
+            xin = Xd[:, r * w:(r + 1) * w].contiguous() if kind == "row" else Xd
+            run = lambda: ttl.shard_linear_row(xin, Wd, t, r, kind == "row", w_layout=ttl.W_NK)
+            ref = oracle.row_shard(Xo, Wo, t, r, x_is_parallel=False)
+        else:
+            epi = ttl.EPI_SILU_MUL if kind == "silu" else 0
+            run = lambda: ttl.shard_linear_col(Xd, Wd, t, r, sp_c, epi, w_layout=ttl.W_NK)
+            ref = oracle.col_shard(Xo, Wo, sp_np, t, r)
+            if kind == "silu":
+                ref = oracle.silu_mul(ref)
+        first, second = run(), run()
+        torch.cuda.synchronize()
+        assert torch.equal(first, second), f"split-free kernel not reproducible (rank {r})"
+        assert_close(from_gpu(first), ref, f"split-free [n][k] {kind} b={b} k={k} n={n} t={t} r={r}")
+
+
+@pytest.mark.parametrize("silu", [False, True])
+def test_auto_choice_of_stream_nk(ttl, gemm_force, silu):
+    """Where its workgroups fill at least 3/4 of the CUs (6144 plain columns: 192 workgroups of 32;
+    3072 act columns: 192 of 16), the shape-based choice for [n][k] weights and 8 rows is the
+    split-free kernel (chosen by shape up to 16 rows): bit-equal to the forced launch, and every
+    element against the oracle."""
+    b, k = 8, 2048
+    n_out = 3072 if silu else 6144
+    n = 2 * n_out if silu else n_out
+    X = wl.random_bf16((b, k), 520 + int(silu))
+    W = wl.random_bf16((k, n), 521 + int(silu), std=0.05)
+    Xd, Wd = gpu(X), gpu(W.t().contiguous())
+    sp_c = ttl.merged_gate_up_split(n_out, 1) if silu else None
+    sp_np = oracle.merged_gate_up_split(n_out, 1) if silu else oracle.plain_split(n, 1)
+    epi = ttl.EPI_SILU_MUL if silu else 0
+    gemm_force.set(kernel="auto", splits=0)
+    auto = ttl.shard_linear_col(Xd, Wd, 1, 0, sp_c, epi, w_layout=ttl.W_NK)
+    gemm_force.set(kernel="streamnk", splits=0)
+    forced = ttl.shard_linear_col(Xd, Wd, 1, 0, sp_c, epi, w_layout=ttl.W_NK)
+    torch.cuda.synchronize()
+    assert torch.equal(auto, forced)
+    ref = oracle.col_shard(f64(X), f64(W), sp_np, 1, 0)
+    if silu:
+        ref = oracle.silu_mul(ref)
+    assert_close(from_gpu(auto), ref, f"auto split-free silu={silu}")
+
+
 @pytest.mark.parametrize("b,k,I,t,silu", [
     (300, 256, 344, 1, True),     # ragged rows and act columns, four k-tiles
     (513, 1024, 2048, 4, True),   # several tiles per rank
