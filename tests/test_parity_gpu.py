@@ -4,7 +4,8 @@ Small cases compare every element; they span several 256-wide tiles and ragged t
 GEMM dimensions.  Each GEMM case runs through every kernel the library has, forced with
 the library's test-only override (256 x 256 tiles by the four-wave kernel where K is a multiple of 64, by the
 eight-wave kernel, the four-wave kernel's tiles cut along k, its 256 x 128 tiles, its 192 x 256
-tiles, and the split-K kernel for short M), and through the shape-based choice.  Tolerance, per output tensor: the error beyond the bf16 rounding of each output
+tiles, and the split-K kernel for short M), and through the shape-based choice; the split-free kernel for
+[n][k] weights and few rows has tests of its own.  Tolerance, per output tensor: the error beyond the bf16 rounding of each output
 element is at most 2e-2 * rms(ref), the reference being the oracle's unrounded float64 value (bf16
 inputs, so the device-side error is fp32 accumulation and fp32 elementwise math).  Integer-exact
 special cases (identity and one-hot operands) are compared bit for bit.
